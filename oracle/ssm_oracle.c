@@ -1,0 +1,192 @@
+/*
+ * ssm_oracle.c -- plain, slow, sequential fp64 CPU oracle for the selective
+ * state-space (S6 / Mamba) scan and its single-token decode update.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only tests/, __graft_entry__.smoke() and the
+ * cpu_baseline leg of bench.py may load this library.  It shares no code,
+ * header, table or helper with the HIP library; the GPU path never calls it.
+ *
+ * What it computes (all arithmetic in double precision):
+ *
+ *   for each batch b and channel d, independently, with h[0..N) = 0:
+ *     for t = 0 .. L-1:
+ *       v      = delta[b,t,d] + (delta_bias ? delta_bias[d] : 0)
+ *       dt     = delta_softplus ? softplus(v) : v
+ *       for n:   h[n] = exp(dt * A[d,n]) * h[n] + dt * B[b,t,n] * x[b,t,d]
+ *       y      = sum_n C[b,t,n] * h[n]  +  (D ? D[d] * x[b,t,d] : 0)
+ *       if z:    y = y * silu(z[b,t,d])
+ *       out[b,t,d] = y
+ *     last_state[b,d,:] = h
+ *
+ * Sources (page title, section):
+ *  - "Mamba 论文精读" (youngju.dev), sec. 2.2 "离散化 (Zero-Order Hold)":
+ *    the discretised recurrence h_t = Abar h_{t-1} + Bbar x_t, y_t = C h_t,
+ *    with Abar = exp(delta*A).
+ *  - same page, sec. 3.3 "Hardware-Aware 算法", the simplified selective_scan
+ *    listing: Bbar*x is taken as delta*B*x (not the exact ZOH form), the state
+ *    starts at zero, and the state is updated before y_t is read out, so y_t
+ *    already sees x_t.  Shapes: x, delta (B,L,D); A (D,N); B, C (B,L,N).
+ *  - same page, sec. 3.1: delta = softplus(Linear_delta(x)); sec. 3.4: the
+ *    delta projection carries a bias (added before softplus), D is a per-channel
+ *    skip parameter and the output is gated by SiLU(z).
+ *  - "Mamba的基础知识" (weblog-19d), section on state space models: D is the
+ *    direct input-to-output (skip) term of the observation equation.
+ *
+ * Inputs are read in their storage type (fp32, or bf16 bit patterns) and
+ * widened exactly to double; A, D and delta_bias are fp32.
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+enum { ORACLE_F32 = 0, ORACLE_BF16 = 1, ORACLE_F64 = 2 };
+
+/* Exact widening of one stored element to double.  A bf16 value is the top
+ * 16 bits of the fp32 with the same bit pattern, so shifting it up by 16 bits
+ * gives that fp32 exactly. */
+static double load_elem(const void *p, int dtype, int64_t i) {
+  if (dtype == ORACLE_F64) return ((const double *)p)[i];
+  if (dtype == ORACLE_F32) return (double)((const float *)p)[i];
+  uint32_t bits = (uint32_t)((const uint16_t *)p)[i] << 16;
+  float f;
+  memcpy(&f, &bits, sizeof f);
+  return (double)f;
+}
+
+/* softplus(v) = log(1 + e^v), written in the two overflow-free forms of the
+ * same function; no threshold approximation. */
+static double softplus(double v) {
+  if (v > 0.0) return v + log1p(exp(-v));
+  return log1p(exp(v));
+}
+
+/* SiLU(z) = z * sigmoid(z) = z / (1 + e^-z). */
+static double silu(double z) { return z / (1.0 + exp(-z)); }
+
+/* The definition for one channel (b, d): runs the recurrence over all L steps
+ * from the state h (length N, updated in place) and writes y_t to
+ * y[t * y_stride_t]. */
+static void scan_channel(int64_t L, int64_t Dm, int64_t N, int dtype, const void *x, const void *delta,
+                         const float *A, const void *B, const void *C, const float *Dskip, const void *z,
+                         const float *delta_bias, int delta_softplus, int64_t b, int64_t d, double *h,
+                         double *y, int64_t y_stride_t) {
+  for (int64_t t = 0; t < L; ++t) {
+    const int64_t i_td = (b * L + t) * Dm + d;  /* (b,t,d) */
+    const int64_t i_tn = (b * L + t) * N;       /* (b,t,0) of B and C */
+    double v = load_elem(delta, dtype, i_td) + (delta_bias ? (double)delta_bias[d] : 0.0);
+    double dt = delta_softplus ? softplus(v) : v;
+    double xt = load_elem(x, dtype, i_td);
+    double acc = 0.0;
+    for (int64_t n = 0; n < N; ++n) {
+      double abar = exp(dt * (double)A[d * N + n]);
+      h[n] = abar * h[n] + dt * load_elem(B, dtype, i_tn + n) * xt;
+      acc += load_elem(C, dtype, i_tn + n) * h[n];
+    }
+    double yt = acc + (Dskip ? (double)Dskip[d] * xt : 0.0);
+    if (z) yt *= silu(load_elem(z, dtype, i_td));
+    y[t * y_stride_t] = yt;
+  }
+}
+
+/* Whole scan.  y: (batch, seqlen, dim) doubles.  last_state: (batch, dim,
+ * dstate) doubles or NULL.  h0: optional initial state (batch, dim, dstate);
+ * NULL means zeros.  Returns 0, or -1 on a bad argument. */
+int oracle_scan(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dtype, const void *x,
+                const void *delta, const float *A, const void *B, const void *C, const float *Dskip,
+                const void *z, const float *delta_bias, int delta_softplus, const double *h0, double *y,
+                double *last_state, int nthreads) {
+  if (batch < 0 || seqlen < 0 || dim < 0 || dstate < 1 || dstate > 1024) return -1;
+  if (!x || !delta || !A || !B || !C || !y) return -1;
+  const int64_t nch = batch * dim;
+#ifdef _OPENMP
+  if (nthreads < 1) nthreads = 1;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
+#endif
+  for (int64_t ch = 0; ch < nch; ++ch) {
+    const int64_t b = ch / dim, d = ch % dim;
+    double h[1024];
+    for (int64_t n = 0; n < dstate; ++n) h[n] = h0 ? h0[ch * dstate + n] : 0.0;
+    scan_channel(seqlen, dim, dstate, dtype, x, delta, A, B, C, Dskip, z, delta_bias, delta_softplus, b, d, h,
+                 y + b * seqlen * dim + d, dim);
+    if (last_state)
+      for (int64_t n = 0; n < dstate; ++n) last_state[ch * dstate + n] = h[n];
+  }
+  (void)nthreads;
+  return 0;
+}
+
+/* The same recurrence for a chosen set of channels only (sampling at full
+ * size).  sel_b[k], sel_d[k] name channel k.  y_out: (nsel, seqlen);
+ * state_out: (nsel, dstate) or NULL.  Starts from zero state. */
+int oracle_scan_channels(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dtype, const void *x,
+                         const void *delta, const float *A, const void *B, const void *C, const float *Dskip,
+                         const void *z, const float *delta_bias, int delta_softplus, int64_t nsel,
+                         const int64_t *sel_b, const int64_t *sel_d, double *y_out, double *state_out,
+                         int nthreads) {
+  if (batch < 0 || seqlen < 0 || dim < 0 || dstate < 1 || dstate > 1024 || nsel < 0) return -1;
+  if (!x || !delta || !A || !B || !C || !y_out || (nsel > 0 && (!sel_b || !sel_d))) return -1;
+  for (int64_t k = 0; k < nsel; ++k)
+    if (sel_b[k] < 0 || sel_b[k] >= batch || sel_d[k] < 0 || sel_d[k] >= dim) return -1;
+#ifdef _OPENMP
+  if (nthreads < 1) nthreads = 1;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
+#endif
+  for (int64_t k = 0; k < nsel; ++k) {
+    double h[1024];
+    for (int64_t n = 0; n < dstate; ++n) h[n] = 0.0;
+    scan_channel(seqlen, dim, dstate, dtype, x, delta, A, B, C, Dskip, z, delta_bias, delta_softplus, sel_b[k],
+                 sel_d[k], h, y_out + k * seqlen, 1);
+    if (state_out)
+      for (int64_t n = 0; n < dstate; ++n) state_out[k * dstate + n] = h[n];
+  }
+  (void)nthreads;
+  return 0;
+}
+
+/* One decode step for every channel: the recurrence body at a single time
+ * step, starting from `state` (batch, dim, dstate) doubles, which is updated
+ * in place.  x, delta, z: (batch, dim); B, C: (batch, dstate); y: (batch, dim).
+ * ("Mamba 论文精读" sec. 6: inference costs O(1) per token with a fixed-size
+ * state and no cache of past inputs.) */
+int oracle_state_update(int64_t batch, int64_t dim, int64_t dstate, int dtype, double *state, const void *x,
+                        const void *delta, const float *A, const void *B, const void *C, const float *Dskip,
+                        const void *z, const float *delta_bias, int delta_softplus, double *y) {
+  if (batch < 0 || dim < 0 || dstate < 1 || dstate > 1024) return -1;
+  if (!state || !x || !delta || !A || !B || !C || !y) return -1;
+  for (int64_t b = 0; b < batch; ++b) {
+    for (int64_t d = 0; d < dim; ++d) {
+      const int64_t i_bd = b * dim + d;
+      double v = load_elem(delta, dtype, i_bd) + (delta_bias ? (double)delta_bias[d] : 0.0);
+      double dt = delta_softplus ? softplus(v) : v;
+      double xt = load_elem(x, dtype, i_bd);
+      double *h = state + i_bd * dstate;
+      double acc = 0.0;
+      for (int64_t n = 0; n < dstate; ++n) {
+        double abar = exp(dt * (double)A[d * dstate + n]);
+        h[n] = abar * h[n] + dt * load_elem(B, dtype, b * dstate + n) * xt;
+        acc += load_elem(C, dtype, b * dstate + n) * h[n];
+      }
+      double yt = acc + (Dskip ? (double)Dskip[d] * xt : 0.0);
+      if (z) yt *= silu(load_elem(z, dtype, i_bd));
+      y[i_bd] = yt;
+    }
+  }
+  return 0;
+}
+
+/* Scalar entry points so tests can pin the prologue/epilogue functions. */
+double oracle_softplus(double v) { return softplus(v); }
+double oracle_silu(double z) { return silu(z); }
+double oracle_widen(const void *p, int dtype, int64_t i) { return load_elem(p, dtype, i); }
+
+int oracle_max_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}

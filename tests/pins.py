@@ -1,0 +1,358 @@
+"""Pins for the fp64 oracle: checks against what the pages and the mathematics fix.
+
+Each ``pin_*`` function takes an ``oracle.Oracle`` handle and raises AssertionError
+when the oracle disagrees with the property.  None of them re-types the oracle's
+loop: they use closed forms, an unrolled sum written with cumulative sums, the
+convolution form of a time-invariant SSM, algebraic invariants, hand-derived
+worked examples, and library routines (numpy.logaddexp, scipy.special.expit) for
+softplus and the sigmoid.  ``tests/test_oracle_mutants.py`` shows that planted
+mistakes in the oracle fail at least one pin.
+
+Sources, by page title and section:
+  * "Mamba 论文精读" (youngju.dev): sec. 2.2 recurrence and Abar = exp(delta A);
+    sec. 3.3 selective_scan (Bbar x = delta B x, zero initial state, update then
+    read out); sec. 3.1 softplus; sec. 3.4 bias, D skip, SiLU gate; sec. 6 O(1)
+    decode with a fixed state.
+  * "Mamba的基础知识" (weblog-19d): state space model section (D skip term) and
+    the convolution section (kernel K = (CB, CAB, ..., CA^k B, ...) for a
+    time-invariant SSM).
+  * "mamba->jamba" (blog.csdn.net), sec. 2.3: a small step keeps the state and
+    ignores the input; parallel scan over the linear recurrence.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+from scipy.special import expit
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+# ----------------------------------------------------------------------------------------------
+# helpers (test-side, independent of the oracle's C code)
+# ----------------------------------------------------------------------------------------------
+def _rand_case(seed, batch=2, L=7, dim=3, N=4, softplus=True, bias=True, z=True, D=True):
+    """Small random float64 case with A varying over both d and n (so an index mix-up of A,
+    B or C shows), a per-channel bias and D."""
+    g = np.random.default_rng(seed)
+    case = dict(
+        x=g.normal(size=(batch, L, dim)),
+        delta=g.normal(size=(batch, L, dim)) * 0.5 if softplus else g.uniform(0.05, 0.6, (batch, L, dim)),
+        A=-g.uniform(0.2, 3.0, (dim, N)).astype(np.float32),
+        B=g.normal(size=(batch, L, N)),
+        C=g.normal(size=(batch, L, N)),
+        D=g.normal(size=dim).astype(np.float32) if D else None,
+        z=g.normal(size=(batch, L, dim)) if z else None,
+        delta_bias=g.uniform(-3.0, 0.5, dim).astype(np.float32) if bias else None,
+        delta_softplus=softplus,
+    )
+    return case
+
+
+def _scan(o, c, **over):
+    kw = dict(c)
+    kw.update(over)
+    return o.scan(kw["x"], kw["delta"], kw["A"], kw["B"], kw["C"], D=kw.get("D"), z=kw.get("z"),
+                  delta_bias=kw.get("delta_bias"), delta_softplus=kw.get("delta_softplus", False),
+                  h0=kw.get("h0"))
+
+
+def unrolled(c):
+    """y_t = sum_{s<=t} sum_n C_t[n] exp(A[d,n] (Lam_t - Lam_s)) delta_s B_s[n] x_s + D x_t, then the
+    gate; Lam is the running sum of delta.  This is the recurrence unrolled (the product of the
+    per-step Abar between s and t is the exponential of A times the summed steps).  Returns
+    (y, h_L) in float64."""
+    x, C, B = c["x"], c["C"], c["B"]
+    A = c["A"].astype(np.float64)
+    v = c["delta"] + (0.0 if c.get("delta_bias") is None else c["delta_bias"].astype(np.float64))
+    dt = np.logaddexp(0.0, v) if c.get("delta_softplus") else v
+    batch, L, dim = x.shape
+    N = A.shape[1]
+    lam = np.cumsum(dt, axis=1)
+    y = np.zeros((batch, L, dim))
+    hL = np.zeros((batch, dim, N))
+    for t in range(L):
+        for s in range(t + 1):
+            dec = np.exp(A[None] * (lam[:, t, :] - lam[:, s, :])[:, :, None])          # (b, d, n)
+            contrib = dec * (dt[:, s, :] * x[:, s, :])[:, :, None] * B[:, s, None, :]    # (b, d, n)
+            y[:, t, :] += np.einsum("bdn,bn->bd", contrib, C[:, t, :])
+            if t == L - 1:
+                hL += contrib
+        if c.get("D") is not None:
+            y[:, t, :] += c["D"].astype(np.float64) * x[:, t, :]
+        if c.get("z") is not None:
+            y[:, t, :] *= c["z"][:, t, :] * expit(c["z"][:, t, :])
+    return y, hL
+
+
+def _close(a, b, rtol, what):
+    scale = max(float(np.max(np.abs(b))), 1e-300)
+    err = float(np.max(np.abs(a - b))) if a.size else 0.0
+    assert err <= rtol * scale, f"{what}: max err {err:.3e} > {rtol:.1e} * {scale:.3e}"
+
+
+# ----------------------------------------------------------------------------------------------
+# pins
+# ----------------------------------------------------------------------------------------------
+def pin_worked_examples(o):
+    """Hand-derived examples (tests/golden/*.json); the pages print no numeric example."""
+    for name in sorted(os.listdir(GOLDEN)):
+        if not name.startswith("worked_example"):
+            continue
+        g = json.load(open(os.path.join(GOLDEN, name)))
+        i = g["inputs"]
+        arr = lambda k, dt=np.float64: None if k not in i else np.array(i[k], dt)  # noqa: E731
+        y, st = o.scan(arr("x"), arr("delta"), arr("A", np.float32), arr("B"), arr("C"),
+                       D=arr("D", np.float32), z=arr("z"), delta_bias=arr("delta_bias", np.float32),
+                       delta_softplus=g["delta_softplus"])
+        _close(y, np.array(g["expected"]["y"]), g["rtol"], f"{name} y")
+        _close(st, np.array(g["expected"]["last_state"]), g["rtol"], f"{name} last_state")
+
+
+def pin_unrolled_sum(o):
+    """I-1: brute-force unrolled sum on tiny L, all options on and off."""
+    for seed, opts in enumerate([{}, dict(softplus=False, bias=False), dict(z=False, D=False),
+                                 dict(bias=False), dict(batch=3, L=5, dim=2, N=8)]):
+        c = _rand_case(100 + seed, **opts)
+        y, st = _scan(o, c)
+        yr, hr = unrolled(c)
+        _close(y, yr, 1e-12, f"unrolled y {opts}")
+        _close(st, hr, 1e-12, f"unrolled last_state {opts}")
+
+
+def pin_lti_convolution(o):
+    """I-2: with delta, B, C constant in time (the S4 / LTI case) the scan is a causal convolution
+    of x with K_k = sum_n C_n Abar_n^k Bbar_n, K = (CB, CAB, CA^2B, ...); for x = 1 it has the
+    geometric closed form sum_n C_n Bbar_n (1 - Abar_n^(t+1)) / (1 - Abar_n)."""
+    g = np.random.default_rng(7)
+    batch, L, dim, N = 2, 48, 3, 5
+    dt = g.uniform(0.05, 0.5, (batch, dim))
+    Bc, Cc = g.normal(size=(batch, N)), g.normal(size=(batch, N))
+    A = -g.uniform(0.1, 2.0, (dim, N)).astype(np.float32)
+    x = g.normal(size=(batch, L, dim))
+    delta = np.broadcast_to(dt[:, None, :], (batch, L, dim)).copy()
+    Bt = np.broadcast_to(Bc[:, None, :], (batch, L, N)).copy()
+    Ct = np.broadcast_to(Cc[:, None, :], (batch, L, N)).copy()
+    y, _ = o.scan(x, delta, A, Bt, Ct)
+    k = np.arange(L)
+    for b in range(batch):
+        for d in range(dim):
+            abar = np.exp(dt[b, d] * A[d].astype(np.float64))                      # (N,)
+            K = (Cc[b] * dt[b, d] * Bc[b])[None, :] * abar[None, :] ** k[:, None]  # (L, N)
+            Kk = K.sum(axis=1)
+            ref = np.convolve(x[b, :, d], Kk)[:L]
+            _close(y[b, :, d], ref, 1e-12, f"LTI conv b={b} d={d}")
+    ones = np.ones_like(x)
+    y1, _ = o.scan(ones, delta, A, Bt, Ct)
+    for b in range(batch):
+        for d in range(dim):
+            abar = np.exp(dt[b, d] * A[d].astype(np.float64))
+            ref = np.array([np.sum(Cc[b] * dt[b, d] * Bc[b] * (1 - abar ** (t + 1)) / (1 - abar)) for t in range(L)])
+            _close(y1[b, :, d], ref, 1e-12, f"LTI geometric b={b} d={d}")
+
+
+def pin_linearity(o):
+    """I-3: for fixed delta, B, C, z, D the output is linear in x."""
+    c = _rand_case(11, L=9)
+    g = np.random.default_rng(12)
+    x1, x2 = g.normal(size=c["x"].shape), g.normal(size=c["x"].shape)
+    al, be = 0.7, -1.9
+    y1, s1 = _scan(o, c, x=x1)
+    y2, s2 = _scan(o, c, x=x2)
+    y3, s3 = _scan(o, c, x=al * x1 + be * x2)
+    _close(y3, al * y1 + be * y2, 1e-12, "linearity y")
+    _close(s3, al * s1 + be * s2, 1e-12, "linearity state")
+
+
+def pin_channel_independence(o):
+    """I-4: channels do not interact; a channel permutation permutes the outputs."""
+    c = _rand_case(21, batch=2, L=6, dim=5)
+    y0, s0 = _scan(o, c)
+    x = c["x"].copy()
+    x[:, :, 2] += 3.0
+    y1, s1 = _scan(o, c, x=x)
+    other = [0, 1, 3, 4]
+    assert np.array_equal(y0[:, :, other], y1[:, :, other]), "perturbing channel 2 changed other channels"
+    assert np.array_equal(s0[:, other, :], s1[:, other, :]), "perturbing channel 2 changed other states"
+    assert not np.allclose(y0[:, :, 2], y1[:, :, 2]), "perturbing channel 2 did not change it"
+    p = np.array([3, 0, 4, 1, 2])
+    cp = dict(c, x=c["x"][:, :, p], delta=c["delta"][:, :, p], z=c["z"][:, :, p], A=c["A"][p],
+              D=c["D"][p], delta_bias=c["delta_bias"][p])
+    yp, sp = _scan(o, cp)
+    assert np.array_equal(yp, y0[:, :, p]) and np.array_equal(sp, s0[:, p, :]), "channel permutation"
+    # batches are independent too
+    cb = dict(c, x=c["x"][::-1].copy(), delta=c["delta"][::-1].copy(), z=c["z"][::-1].copy(),
+              B=c["B"][::-1].copy(), C=c["C"][::-1].copy())
+    yb, sb = _scan(o, cb)
+    assert np.array_equal(yb, y0[::-1]) and np.array_equal(sb, s0[::-1]), "batch permutation"
+
+
+def pin_causality(o):
+    """I-5: changing any input at step t0 leaves y_t, t < t0, unchanged."""
+    c = _rand_case(31, L=10)
+    y0, _ = _scan(o, c)
+    t0 = 6
+    for k in ("x", "delta", "B", "C", "z"):
+        a = c[k].copy()
+        a[:, t0:] += 0.5
+        y1, _ = _scan(o, c, **{k: a})
+        assert np.array_equal(y0[:, :t0], y1[:, :t0]), f"changing {k} at t>={t0} changed earlier outputs"
+        assert not np.allclose(y0[:, t0:], y1[:, t0:]), f"changing {k} at t>={t0} had no effect"
+
+
+def pin_zero_step(o):
+    """I-6: delta = 0 gives Abar = I and a vanishing input term, so the state stays 0 and
+    y = D x SiLU(z); a small step moves y away from that by O(delta)."""
+    c = _rand_case(41, softplus=False, bias=False)
+    zero = np.zeros_like(c["delta"])
+    y, st = _scan(o, c, delta=zero)
+    ref = c["D"].astype(np.float64) * c["x"] * c["z"] * expit(c["z"])
+    _close(y, ref, 1e-15, "delta=0 output")
+    assert np.all(st == 0.0), "delta=0 must leave the state at zero"
+    diffs = []
+    for eps in (1e-4, 5e-5, 2.5e-5):
+        ye, _ = _scan(o, c, delta=np.full_like(c["delta"], eps))
+        diffs.append(np.max(np.abs(ye - ref)))
+    assert diffs[0] > 0 and abs(diffs[0] / diffs[1] - 2.0) < 1e-2 and abs(diffs[1] / diffs[2] - 2.0) < 1e-2, \
+        f"y - Dx SiLU(z) is not linear in a small step: {diffs}"
+
+
+def pin_impulse_long_carry(o):
+    """I-7: an impulse at t=0 with delta_0 = 1, then delta = 0: the state is held exactly at
+    delta_0 B_0 x_0, so y_t = (C_t . B_0 + D x_t) SiLU(z_t) for every t, over 2^20 steps."""
+    g = np.random.default_rng(51)
+    L, N = 1 << 20, 16
+    x = g.normal(size=(1, L, 1)).astype(np.float32)
+    x[0, 0, 0] = 1.0
+    delta = np.zeros((1, L, 1), np.float32)
+    delta[0, 0, 0] = 1.0
+    B = g.normal(size=(1, L, N)).astype(np.float32)
+    C = g.normal(size=(1, L, N)).astype(np.float32)
+    z = g.normal(size=(1, L, 1)).astype(np.float32)
+    A = -np.arange(1, N + 1, dtype=np.float32)[None]
+    D = np.array([0.5], np.float32)
+    y, st = o.scan(x, delta, A, B, C, D=D, z=z)
+    h = B[0, 0].astype(np.float64)
+    zz = z[0, :, 0].astype(np.float64)
+    ref = (C[0].astype(np.float64) @ h + 0.5 * x[0, :, 0].astype(np.float64)) * zz * expit(zz)
+    _close(y[0, :, 0], ref, 1e-13, "impulse carry")
+    _close(st[0, 0], h, 1e-15, "impulse state")
+
+
+def pin_decode_equals_scan(o):
+    """I-8: L single-token updates from h=0 reproduce the scan's y_t and h_L; a scan resumed from
+    its own last state equals the scan over the joined sequence."""
+    c = _rand_case(61, batch=2, L=8, dim=3, N=4)
+    y, st = _scan(o, c)
+    h = np.zeros_like(st)
+    for t in range(c["x"].shape[1]):
+        yt, h = o.state_update(h, c["x"][:, t], c["delta"][:, t], c["A"], c["B"][:, t], c["C"][:, t],
+                               D=c["D"], z=c["z"][:, t], delta_bias=c["delta_bias"],
+                               delta_softplus=c["delta_softplus"])
+        _close(yt, y[:, t], 1e-14, f"decode step {t}")
+    _close(h, st, 1e-14, "decode final state")
+    L1 = 5
+    first = {k: (v[:, :L1] if isinstance(v, np.ndarray) and v.ndim == 3 else v) for k, v in c.items()}
+    rest = {k: (v[:, L1:] if isinstance(v, np.ndarray) and v.ndim == 3 else v) for k, v in c.items()}
+    ya, sa = _scan(o, first)
+    yb, sb = _scan(o, rest, h0=sa)
+    _close(np.concatenate([ya, yb], axis=1), y, 1e-14, "scan resumed from last_state")
+    _close(sb, st, 1e-14, "resumed last_state")
+
+
+def _compose(p, q):
+    """The scan operator on (a, b) pairs: (a1, b1) o (a2, b2) = (a1 a2, a2 b1 + b2)."""
+    return (p[0] * q[0], q[0] * p[1] + q[1])
+
+
+def _fold_random_tree(pairs, g):
+    if len(pairs) == 1:
+        return pairs[0]
+    k = int(g.integers(1, len(pairs)))
+    return _compose(_fold_random_tree(pairs[:k], g), _fold_random_tree(pairs[k:], g))
+
+
+def pin_associative_scan(o):
+    """I-9: the last state equals the fold of the per-step pairs (Abar_t, Bbar_t x_t) under the
+    associative operator, for every bracketing (the parallel-scan view of the recurrence)."""
+    c = _rand_case(71, batch=2, L=8, dim=3, N=4)
+    _, st = _scan(o, c)
+    v = c["delta"] + c["delta_bias"].astype(np.float64)
+    dt = np.logaddexp(0.0, v)
+    A = c["A"].astype(np.float64)
+    a = np.exp(dt[..., None] * A[None, None])                          # (b, t, d, n)
+    u = (dt * c["x"])[..., None] * c["B"][:, :, None, :]               # (b, t, d, n)
+    pairs = [(a[:, t], u[:, t]) for t in range(a.shape[1])]
+    g = np.random.default_rng(72)
+    for _ in range(12):
+        tot = _fold_random_tree(pairs, g)
+        _close(tot[1], st, 1e-13, "bracketing of the scan operator")
+        _close(tot[0], np.prod(a, axis=1), 1e-13, "decay product")
+
+
+def pin_special_values(o):
+    """I-10: softplus(0) = ln 2, softplus is log(1+e^v) at both tails, SiLU(0) = 0 and
+    SiLU(1) = 1/(1+e^-1); a zero gate zeroes y; absent D or bias equal zero D or bias."""
+    assert abs(o.softplus(0.0) - math.log(2.0)) <= 1e-16
+    assert o.softplus(800.0) == 800.0 and o.softplus(-800.0) == 0.0
+    for v in (-30.0, -5.0, -0.3, 0.7, 4.0, 25.0):
+        assert abs(o.softplus(v) - float(np.logaddexp(0.0, v))) <= 1e-15 * max(1.0, abs(v)), v
+    assert abs(o.softplus(-30.0) - math.exp(-30.0)) <= 1e-12 * math.exp(-30.0)
+    assert o.silu(0.0) == 0.0
+    assert abs(o.silu(1.0) - 1.0 / (1.0 + math.exp(-1.0))) <= 1e-16
+    for zv in (-40.0, -2.5, 0.3, 9.0):
+        assert abs(o.silu(zv) - zv * float(expit(zv))) <= 1e-15 * max(1.0, abs(zv)), zv
+    c = _rand_case(81)
+    y, _ = _scan(o, c, z=np.zeros_like(c["z"]))
+    assert np.all(y == 0.0), "z = 0 must zero the output"
+    ya, sa = _scan(o, c, D=None)
+    yb, sb = _scan(o, c, D=np.zeros_like(c["D"]))
+    assert np.array_equal(ya, yb) and np.array_equal(sa, sb), "D=None differs from D=0"
+    ya, sa = _scan(o, c, delta_bias=None)
+    yb, sb = _scan(o, c, delta_bias=np.zeros_like(c["delta_bias"]))
+    assert np.array_equal(ya, yb) and np.array_equal(sa, sb), "bias=None differs from bias=0"
+
+
+def pin_storage_widening(o):
+    """I-11: bf16 bit patterns and fp32 values widen exactly; a bf16-stored scan equals the same
+    scan on the widened float64 values."""
+    bits = np.array([0x3F80, 0xC000, 0x0001, 0x7F80, 0xFF80, 0x8000, 0x3F81, 0x0080], np.uint16)
+    ref = np.array([1.0, -2.0, 2.0 ** -133, np.inf, -np.inf, -0.0, 1.0 + 2.0 ** -7, 2.0 ** -126])
+    w = o.widen(bits)
+    assert np.array_equal(w, ref) and np.signbit(w[5]), f"bf16 widening {w}"
+    assert np.isnan(o.widen(np.array([0x7FC0], np.uint16))[0])
+    f = np.array([1.5, -3.25e-39, 3.4028235e38], np.float32)
+    assert np.array_equal(o.widen(f), f.astype(np.float64))
+    g = np.random.default_rng(91)
+    shape = (2, 6, 3)
+    to_bits = lambda a: (np.asarray(a, np.float32).view(np.uint32) >> 16).astype(np.uint16)  # truncation
+    wid = lambda b: (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)           # noqa: E731
+    xb, db, zb = (to_bits(g.normal(size=shape)) for _ in range(3))
+    Bb, Cb = (to_bits(g.normal(size=(2, 6, 4))) for _ in range(2))
+    A = -g.uniform(0.2, 2.0, (3, 4)).astype(np.float32)
+    y1, s1 = o.scan(xb, db, A, Bb, Cb, z=zb, delta_softplus=True)
+    y2, s2 = o.scan(wid(xb), wid(db), A, wid(Bb), wid(Cb), z=wid(zb), delta_softplus=True)
+    assert np.array_equal(y1, y2) and np.array_equal(s1, s2), "bf16 storage path differs"
+    y3, s3 = o.scan(wid(xb).astype(np.float32), wid(db).astype(np.float32), A, wid(Bb).astype(np.float32),
+                    wid(Cb).astype(np.float32), z=wid(zb).astype(np.float32), delta_softplus=True)
+    assert np.array_equal(y1, y3) and np.array_equal(s1, s3), "fp32 storage path differs"
+
+
+def pin_channel_selection(o):
+    """scan_channels (used to sample full-size outputs) equals the full scan on those channels."""
+    c = _rand_case(95, batch=3, L=9, dim=4)
+    y, st = _scan(o, c)
+    sb, sd = np.array([0, 2, 1, 2]), np.array([3, 0, 1, 3])
+    yc, sc = o.scan_channels(c["x"], c["delta"], c["A"], c["B"], c["C"], sb, sd, D=c["D"], z=c["z"],
+                             delta_bias=c["delta_bias"], delta_softplus=True)
+    for k in range(len(sb)):
+        assert np.array_equal(yc[k], y[sb[k], :, sd[k]]) and np.array_equal(sc[k], st[sb[k], sd[k]])
+
+
+ALL_PINS = [pin_worked_examples, pin_unrolled_sum, pin_lti_convolution, pin_linearity,
+            pin_channel_independence, pin_causality, pin_zero_step, pin_impulse_long_carry,
+            pin_decode_equals_scan, pin_associative_scan, pin_special_values, pin_storage_widening,
+            pin_channel_selection]

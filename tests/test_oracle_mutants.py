@@ -1,0 +1,69 @@
+"""Plant plausible mistakes in a copy of the oracle (on the CPU) and check that the pins catch
+every one of them; this is what makes the pins a check on the oracle and not a restatement."""
+import os
+
+import pytest
+
+import oracle
+import pins
+
+# (name, text in ssm_oracle.c, replacement, occurrence to replace (0 = first))
+MUTANTS = [
+    ("bbar_without_delta", "h[n] = abar * h[n] + dt * load_elem(B, dtype, i_tn + n) * xt;",
+     "h[n] = abar * h[n] + load_elem(B, dtype, i_tn + n) * xt;"),
+    ("exp_sign_flipped", "double abar = exp(dt * (double)A[d * N + n]);",
+     "double abar = exp(-dt * (double)A[d * N + n]);"),
+    ("readout_before_update",
+     "      h[n] = abar * h[n] + dt * load_elem(B, dtype, i_tn + n) * xt;\n"
+     "      acc += load_elem(C, dtype, i_tn + n) * h[n];",
+     "      acc += load_elem(C, dtype, i_tn + n) * h[n];\n"
+     "      h[n] = abar * h[n] + dt * load_elem(B, dtype, i_tn + n) * xt;"),
+    ("readout_uses_B", "acc += load_elem(C, dtype, i_tn + n) * h[n];",
+     "acc += load_elem(B, dtype, i_tn + n) * h[n];"),
+    ("skip_dropped", "double yt = acc + (Dskip ? (double)Dskip[d] * xt : 0.0);\n    if (z) yt *= silu(load_elem(z, dtype, i_td));",
+     "double yt = acc;\n    if (z) yt *= silu(load_elem(z, dtype, i_td));"),
+    ("skip_after_gate", "double yt = acc + (Dskip ? (double)Dskip[d] * xt : 0.0);\n    if (z) yt *= silu(load_elem(z, dtype, i_td));",
+     "double yt = acc;\n    if (z) yt *= silu(load_elem(z, dtype, i_td));\n    yt += (Dskip ? (double)Dskip[d] * xt : 0.0);"),
+    ("bias_after_softplus",
+     "    double v = load_elem(delta, dtype, i_td) + (delta_bias ? (double)delta_bias[d] : 0.0);\n"
+     "    double dt = delta_softplus ? softplus(v) : v;",
+     "    double v = load_elem(delta, dtype, i_td);\n"
+     "    double dt = (delta_softplus ? softplus(v) : v) + (delta_bias ? (double)delta_bias[d] : 0.0);"),
+    ("softplus_missing_log", "if (v > 0.0) return v + log1p(exp(-v));\n  return log1p(exp(v));",
+     "if (v > 0.0) return v + exp(-v);\n  return exp(v);"),
+    ("softplus_drops_linear_part", "if (v > 0.0) return v + log1p(exp(-v));", "if (v > 0.0) return log1p(exp(-v));"),
+    ("silu_is_sigmoid", "return z / (1.0 + exp(-z));", "return 1.0 / (1.0 + exp(-z));"),
+    ("B_C_ignore_batch", "const int64_t i_tn = (b * L + t) * N;", "const int64_t i_tn = t * N;"),
+    ("A_transposed", "double abar = exp(dt * (double)A[d * N + n]);", "double abar = exp(dt * (double)A[n * Dm + d]);"),
+    ("decode_bbar_without_delta", "h[n] = abar * h[n] + dt * load_elem(B, dtype, b * dstate + n) * xt;",
+     "h[n] = abar * h[n] + load_elem(B, dtype, b * dstate + n) * xt;"),
+    ("initial_state_ignored", "h[n] = h0 ? h0[ch * dstate + n] : 0.0;", "h[n] = 0.0;"),
+    ("selection_wrong_row", "sel_d[k], h, y_out + k * seqlen, 1);", "sel_d[k], h, y_out + k * seqlen, 0);"),
+]
+
+
+def _run_pins(o):
+    failed = []
+    for pin in pins.ALL_PINS:
+        try:
+            pin(o)
+        except AssertionError as e:
+            failed.append((pin.__name__, str(e)[:80]))
+    return failed
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_planted_mistake_is_caught(tmp_path, name, old, new):
+    src = open(oracle.SOURCE).read()
+    assert src.count(old) >= 1, f"mutation site for {name} not found"
+    mutated = src.replace(old, new, 1)
+    path = os.path.join(tmp_path, "mutant.c")
+    open(path, "w").write(mutated)
+    lib = oracle.build(out_path=os.path.join(tmp_path, f"lib_{name}.so"), src=path)
+    failed = _run_pins(oracle.Oracle(lib))
+    assert failed, f"no pin caught the planted mistake {name}"
+
+
+def test_unmutated_copy_passes(tmp_path):
+    lib = oracle.build(out_path=os.path.join(tmp_path, "lib_clean.so"))
+    assert _run_pins(oracle.Oracle(lib)) == []

@@ -1,0 +1,167 @@
+"""Seeded synthetic inputs for the selective-scan workloads.
+
+This module only draws random tensors.  It holds none of the scan's
+arithmetic, and it is the one piece that both sides of a parity check share:
+the HIP path receives these arrays on the device, the fp64 oracle receives the
+same bytes on the host.
+
+Randomness is numpy's Philox4x64 counter-based generator (Salmon et al., SC'11),
+with one stream per (seed, tensor) pair, so every tensor is reproducible on its
+own regardless of the order in which tensors are drawn.  Values are drawn in
+fp32 and, for bf16 workloads, rounded to bf16 with round-to-nearest-even; the
+bf16 tensors are returned as uint16 bit patterns.
+
+Workload recipes (sizes and value distributions of the pages' workloads; the
+pages' own datasets (the Pile, HG38, YouTubeMix, SC09) are not available and
+these tensors stand in for them):
+
+* ``default`` -- x, B, C, z ~ N(0, 1); raw delta = 0.5 * N(0, 1); A[d, n] =
+  -(n + 1) (the S4D-real style initialisation of A, with A = -exp(A_log));
+  D = 1; the delta bias is chosen per channel so that softplus(bias) is
+  log-uniform in [1e-3, 1e-1], i.e. bias = log(expm1(v)), log10 v ~ U(-3, -1).
+* ``genomics`` -- a one-hot 4-symbol alphabet (s_t ~ U{0..3}) projected by a
+  seeded (4, dim) matrix W ~ N(0, 0.5^2), so x[b, t, :] = W[s_t, :]; delta is
+  passed directly (no softplus, no bias) and is log-uniform in [1e-4, 1e-1];
+  B, C, z ~ N(0, 1); D = 1; A[d, n] = -(n + 1).
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import Dict, Optional
+
+import numpy as np
+
+# Stream ids: one Philox key per (seed, tensor).
+_TENSOR_IDS = {"x": 1, "delta": 2, "B": 3, "C": 4, "z": 5, "bias": 6, "symbols": 7, "W": 8}
+
+_CHUNK = 1 << 24  # elements per draw; bounds temporary memory for the 1M-step workload
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    kind: str                 # "scan" or "decode"
+    batch: int
+    dim: int
+    dstate: int
+    dtype: str                # "f32" or "bf16": storage type of x, delta, B, C, z, y
+    seed: int
+    seqlen: int = 0           # scan length, or number of decode steps
+    recipe: str = "default"
+    delta_softplus: bool = True
+    has_bias: bool = True
+    has_z: bool = True
+    has_D: bool = True
+    note: str = field(default="", compare=False)
+
+
+WORKLOADS: Dict[str, Workload] = {
+    "tiny": Workload("tiny", "scan", batch=1, seqlen=64, dim=16, dstate=4, dtype="f32", seed=61000,
+                     note="tiny fp32 scan; the oracle finishes in milliseconds"),
+    "mamba130m": Workload("mamba130m", "scan", batch=8, seqlen=2048, dim=1536, dstate=16, dtype="bf16",
+                          seed=61001, note="Mamba-130M-shaped layer scan: d_inner = 2 x 768"),
+    "mamba2p8b": Workload("mamba2p8b", "scan", batch=4, seqlen=2048, dim=5120, dstate=16, dtype="bf16",
+                          seed=61002, note="Mamba-2.8B-shaped layer scan: d_inner = 2 x 2560"),
+    "genomics": Workload("genomics", "scan", batch=1, seqlen=1 << 20, dim=256, dstate=16, dtype="f32",
+                         seed=61003, recipe="genomics", delta_softplus=False, has_bias=False,
+                         note="1M-step DNA-shaped fp32 scan"),
+    "decode": Workload("decode", "decode", batch=64, seqlen=256, dim=5120, dstate=16, dtype="bf16",
+                       seed=61004, note="256 single-token decode steps, state (64, 5120, 16) fp32"),
+}
+
+
+def _rng(seed: int, tensor: str) -> np.random.Generator:
+    return np.random.Generator(np.random.Philox(key=(int(seed) << 8) | _TENSOR_IDS[tensor]))
+
+
+def _normal(seed: int, tensor: str, shape, scale: float = 1.0) -> np.ndarray:
+    g = _rng(seed, tensor)
+    n = int(np.prod(shape))
+    out = np.empty(n, np.float32)
+    for s in range(0, n, _CHUNK):
+        e = min(n, s + _CHUNK)
+        out[s:e] = g.standard_normal(e - s, dtype=np.float32)
+        if scale != 1.0:
+            out[s:e] *= np.float32(scale)
+    return out.reshape(shape)
+
+
+def _log_uniform(seed: int, tensor: str, shape, lo_exp: float, hi_exp: float) -> np.ndarray:
+    """10**U(lo_exp, hi_exp), element-wise, fp32."""
+    g = _rng(seed, tensor)
+    n = int(np.prod(shape))
+    out = np.empty(n, np.float32)
+    for s in range(0, n, _CHUNK):
+        e = min(n, s + _CHUNK)
+        u = g.uniform(lo_exp, hi_exp, e - s)
+        out[s:e] = np.power(10.0, u)
+    return out.reshape(shape)
+
+
+def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    """Round fp32 to bf16, round-to-nearest-even; NaN stays a (quiet) NaN.  Returns uint16 bits."""
+    u = np.ascontiguousarray(a, np.float32).view(np.uint32)
+    r = ((u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)).astype(np.uint16)
+    nan = (u & np.uint32(0x7FFFFFFF)) > np.uint32(0x7F800000)
+    if nan.any():
+        r[nan] = ((u[nan] >> np.uint32(16)) | np.uint32(0x0040)).astype(np.uint16)
+    return r
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """Exact widening of bf16 bit patterns to fp32."""
+    return (np.ascontiguousarray(b, np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def _store(a: np.ndarray, dtype: str) -> np.ndarray:
+    return f32_to_bf16_bits(a) if dtype == "bf16" else np.ascontiguousarray(a, np.float32)
+
+
+def params(dim: int, dstate: int, seed: int, has_bias: bool = True, has_D: bool = True):
+    """A (dim, N) fp32, D (dim,) fp32 or None, delta_bias (dim,) fp32 or None."""
+    A = -np.tile(np.arange(1, dstate + 1, dtype=np.float32), (dim, 1))
+    D = np.ones(dim, np.float32) if has_D else None
+    bias = None
+    if has_bias:
+        v = _log_uniform(seed, "bias", (dim,), -3.0, -1.0).astype(np.float64)
+        bias = np.log(np.expm1(v)).astype(np.float32)
+    return A, D, bias
+
+
+def scan_inputs(batch: int, seqlen: int, dim: int, dstate: int, dtype: str = "f32", seed: int = 0,
+                recipe: str = "default", has_bias: bool = True, has_z: bool = True,
+                has_D: bool = True) -> Dict[str, Optional[np.ndarray]]:
+    """Inputs of one scan call: x, delta, z (batch, seqlen, dim); B, C (batch, seqlen, dstate)
+    in the storage type; A (dim, dstate), D (dim,), delta_bias (dim,) in fp32."""
+    shp, shn = (batch, seqlen, dim), (batch, seqlen, dstate)
+    if recipe == "default":
+        x = _normal(seed, "x", shp)
+        delta = _normal(seed, "delta", shp, 0.5)
+    elif recipe == "genomics":
+        g = _rng(seed, "symbols")
+        sym = g.integers(0, 4, size=(batch, seqlen), dtype=np.int8)
+        W = _normal(seed, "W", (4, dim), 0.5)
+        x = W[sym]
+        delta = _log_uniform(seed, "delta", shp, -4.0, -1.0)
+    else:
+        raise ValueError(f"unknown recipe {recipe!r}")
+    B = _normal(seed, "B", shn)
+    C = _normal(seed, "C", shn)
+    z = _normal(seed, "z", shp) if has_z else None
+    A, D, bias = params(dim, dstate, seed, has_bias and recipe == "default", has_D)
+    return {"x": _store(x, dtype), "delta": _store(delta, dtype), "B": _store(B, dtype), "C": _store(C, dtype),
+            "z": None if z is None else _store(z, dtype), "A": A, "D": D, "delta_bias": bias}
+
+
+def workload_inputs(w: Workload) -> Dict[str, Optional[np.ndarray]]:
+    """Inputs of a named workload.  For a decode workload the per-step tensors are drawn like a
+    scan of ``seqlen`` steps and stored step-major: x, delta, z (steps, batch, dim); B, C
+    (steps, batch, dstate); each step is then one contiguous slab."""
+    if w.kind == "scan":
+        return scan_inputs(w.batch, w.seqlen, w.dim, w.dstate, w.dtype, w.seed, w.recipe,
+                           w.has_bias, w.has_z, w.has_D)
+    t = scan_inputs(w.batch, w.seqlen, w.dim, w.dstate, w.dtype, w.seed, w.recipe, w.has_bias, w.has_z, w.has_D)
+    for k in ("x", "delta", "z", "B", "C"):
+        if t[k] is not None:
+            t[k] = np.ascontiguousarray(np.swapaxes(t[k], 0, 1))
+    return t
