@@ -1,0 +1,262 @@
+#!/usr/bin/env python3
+"""Throughput of the selective-scan hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload mamba130m]
+
+One step = one ssm_scan_fwd call over one batch of the workload (the whole fused hot path:
+load + delta prologue + discretise + scan + read-out + gate + store).  Inputs are seeded and
+synthetic (workloads.py) and resident in HBM before the timed region; several copies of the
+input set are rotated so that the 256 MB Infinity Cache cannot hold them between steps.
+
+Prints ONE JSON line.  `value` is B*L*D elements per second for the named workload; the line
+also carries the roofline of the scan kernel (per-launch durations measured with HIP events on
+the stream the kernel runs on), the fp64 CPU oracle timed on this host (cpu_baseline), and as
+context the 2.8B-shaped scan and the batched decode step (updates/s).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0                       # MI355X HBM3E, published
+VALU_LANE_SLOTS = 256 * 4 * 16 * 2.4e9        # CUs x SIMDs x lanes x clock: fp32 VALU issue slots/s (non-packed)
+SLOTS_PER_UPDATE = 6                          # per (t,d,n): 2 mul + 2 fma + v_exp_f32 at half rate (2 slots)
+MALL_BYTES = 256 << 20
+KERNEL_SOURCES = ["selective_state_space_61_amd/csrc/ssm_api.hip", "selective_state_space_61_amd/csrc/scan_fwd.hpp",
+                  "selective_state_space_61_amd/csrc/ssm_device.hpp", "selective_state_space_61_amd/csrc/state_update.hpp"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        h.update(open(os.path.join(ROOT, p), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def scan_bytes(batch, L, dim, N, es, has_z=True):
+    per_td = (4 if has_z else 3) * es          # x, delta, (z), y
+    return batch * L * dim * per_td + 2 * batch * L * N * es + 4 * dim * N + 8 * dim + 4 * batch * dim * N
+
+
+def decode_bytes_per_step(batch, dim, N, es):
+    return 2 * 4 * batch * dim * N + batch * dim * 4 * es + 2 * batch * N * es + 4 * dim * N + 8 * dim
+
+
+def dev_tensor(a, torch, np, device):
+    if a is None:
+        return None
+    if a.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(device).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+
+
+def time_calls(torch, fn, n_calls, warmup):
+    """Runs fn(i) for warmup + n_calls calls back to back on the current stream.  Returns
+    (total ms of the timed calls, list of per-call ms from events around each call)."""
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(n_calls + 1)]
+    ev[0].record()
+    for i in range(n_calls):
+        fn(warmup + i)
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    per = [ev[i].elapsed_time(ev[i + 1]) for i in range(n_calls)]
+    return ev[0].elapsed_time(ev[-1]), per
+
+
+def bench_scan(name, steps, warmup, torch, np, W, ssm, device):
+    w = W.WORKLOADS[name]
+    es = 2 if w.dtype == "bf16" else 4
+    t = W.workload_inputs(w)
+    one = dev_tensor
+    set_bytes = scan_bytes(w.batch, w.seqlen, w.dim, w.dstate, es)
+    copies = max(1, min(4, math.ceil(2 * MALL_BYTES / set_bytes)))
+    sets = []
+    for c in range(copies):
+        d = {k: one(v, torch, np, device) for k, v in t.items()}
+        d["y"] = torch.empty_like(d["x"])
+        d["st"] = torch.empty(w.batch, w.dim, w.dstate, device=device)
+        sets.append(d)
+    del t
+
+    def call(i):
+        d = sets[i % copies]
+        ssm.ssm_scan_fwd(d["x"], d["delta"], d["A"], d["B"], d["C"], D=d["D"], z=d["z"],
+                         delta_bias=d["delta_bias"], delta_softplus=w.delta_softplus, y=d["y"], last_state=d["st"])
+
+    total_ms, per = time_calls(torch, call, steps, warmup)
+    ms_step = total_ms / steps
+    kern_ms = sum(per) / len(per)
+    elems = w.batch * w.seqlen * w.dim
+    updates = elems * w.dstate
+    res = {
+        "workload": name, "batch": w.batch, "seqlen": w.seqlen, "dim": w.dim, "dstate": w.dstate,
+        "io_dtype": w.dtype, "rotated_input_sets": copies, "ms_per_step": ms_step, "kernel_ms": kern_ms,
+        "elems_per_s": elems / (ms_step * 1e-3), "alg_bytes": set_bytes,
+        "hbm_gbps": set_bytes / (kern_ms * 1e-3) / 1e9,
+        "valu_slot_frac": SLOTS_PER_UPDATE * updates / (kern_ms * 1e-3) / VALU_LANE_SLOTS,
+    }
+    res["hbm_frac"] = res["hbm_gbps"] / HBM_PEAK_GBPS
+    del sets
+    torch.cuda.empty_cache()
+    return res
+
+
+def bench_decode(steps_per_rep, torch, np, W, ssm, device, ring):
+    w = W.WORKLOADS["decode"]
+    es = 2 if w.dtype == "bf16" else 4
+    t = W.workload_inputs(w)
+    d = {k: dev_tensor(v, torch, np, device) for k, v in t.items()}
+    del t
+    states = [torch.zeros(w.batch, w.dim, w.dstate, device=device) for _ in range(ring)]
+    ys = torch.empty(w.seqlen, w.batch, w.dim, dtype=d["x"].dtype, device=device)
+
+    def call(i):
+        s = i % w.seqlen
+        ssm.ssm_state_update(states[i % ring], d["x"][s], d["delta"][s], d["A"], d["B"][s], d["C"][s], D=d["D"],
+                             z=d["z"][s], delta_bias=d["delta_bias"], delta_softplus=True, y=ys[s])
+
+    total_ms, per = time_calls(torch, call, steps_per_rep, 8)
+    step_ms = total_ms / steps_per_rep
+    kern_ms = sum(per) / len(per)
+    upd = w.batch * w.dim * w.dstate
+    bpstep = decode_bytes_per_step(w.batch, w.dim, w.dstate, es)
+    out = {"batch": w.batch, "dim": w.dim, "dstate": w.dstate, "steps": steps_per_rep, "state_ring": ring,
+           "ms_per_step": step_ms, "kernel_ms": kern_ms, "updates_per_s": upd / (step_ms * 1e-3),
+           "tokens_per_s": w.batch / (step_ms * 1e-3), "alg_bytes_per_step": bpstep,
+           "hbm_gbps": bpstep / (kern_ms * 1e-3) / 1e9}
+    out["hbm_frac"] = out["hbm_gbps"] / HBM_PEAK_GBPS
+    del states, d
+    torch.cuda.empty_cache()
+    return out
+
+
+def cpu_baseline(name, np, W):
+    import oracle
+    w = W.WORKLOADS[name]
+    t = W.workload_inputs(w)
+    o = oracle.load()
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    cores = max(1, min(cores, int(os.environ.get("OMP_NUM_THREADS", cores))))
+    t0 = time.perf_counter()
+    o.scan(t["x"], t["delta"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"], delta_bias=t["delta_bias"],
+           delta_softplus=w.delta_softplus, nthreads=cores)
+    dt = time.perf_counter() - t0
+    elems = w.batch * w.seqlen * w.dim
+    return {"value": elems / dt, "unit": "elem/s", "cores": cores, "kind": "oracle",
+            "sample": f"the whole {name} workload ({w.batch}x{w.seqlen}x{w.dim}, N={w.dstate}) once, "
+                      f"fp64 sequential recurrence, OpenMP over channels; {dt:.2f} s wall"}
+
+
+def traffic_from_profiles(name, alg_bytes):
+    """HBM bytes per launch measured by rocprofv3 FETCH_SIZE / WRITE_SIZE (profiles/), scaled by the
+    copy-kernel calibration, if the kernels have not changed since they were taken."""
+    p = os.path.join(ROOT, "profiles", f"traffic_{name}.json")
+    if not os.path.exists(p):
+        return None, None
+    rec = json.load(open(p))
+    if rec.get("source_hash") != source_hash():
+        return None, "stale"
+    return rec["hbm_bytes_per_launch"], rec
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="mamba130m", choices=["mamba130m", "mamba2p8b", "genomics"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="skip the context measurements (2.8B scan, decode)")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py: this build measures one GPU only (--gpus {args.gpus}, WORLD_SIZE {world}); "
+              "every (batch, channel) is independent, so N GPUs would each run 1/N of the channels "
+              "with no communication. Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import workloads as W
+    import selective_state_space_61_amd as ssm
+    from selective_state_space_61_amd import build as hip_build
+
+    if not os.path.exists(ssm.LIBRARY):
+        hip_build.build(verbose=True)
+    ssm.load_library()
+    device = torch.device("cuda:0")
+    torch.cuda.set_device(device)
+    log(f"[bench] {torch.cuda.get_device_name(0)}; workload {args.workload}; steps {args.steps}; warmup {args.warmup}")
+
+    main_res = bench_scan(args.workload, args.steps, args.warmup, torch, np, W, ssm, device)
+    log(f"[bench] {args.workload}: {main_res['kernel_ms'] * 1e3:.1f} us/launch, {main_res['hbm_gbps']:.0f} GB/s, "
+        f"VALU slots {main_res['valu_slot_frac']:.3f}")
+
+    extra = {}
+    if not args.no_extra:
+        if args.workload != "mamba2p8b":
+            extra["mamba2p8b"] = bench_scan("mamba2p8b", max(10, args.steps // 2), 3, torch, np, W, ssm, device)
+            log(f"[bench] mamba2p8b: {extra['mamba2p8b']['kernel_ms'] * 1e3:.1f} us/launch")
+        extra["decode_mall_resident"] = bench_decode(256, torch, np, W, ssm, device, ring=1)
+        extra["decode_hbm_ring26"] = bench_decode(256, torch, np, W, ssm, device, ring=26)
+        log(f"[bench] decode: {extra['decode_hbm_ring26']['updates_per_s']:.3e} updates/s (ring of 26 states)")
+
+    hbm_frac = main_res["hbm_frac"]
+    alu_frac = main_res["valu_slot_frac"]
+    traffic, trec = traffic_from_profiles(args.workload, main_res["alg_bytes"])
+    if alu_frac >= hbm_frac:
+        roof = {"bound": "alu", "achieved": SLOTS_PER_UPDATE * main_res["batch"] * main_res["seqlen"] * main_res["dim"]
+                * main_res["dstate"] / (main_res["kernel_ms"] * 1e-3) / 1e12,
+                "peak": VALU_LANE_SLOTS / 1e12, "unit": "TFLOP/s", "frac": alu_frac}
+        roof["note"] = ("fp32 VALU issue slots: 6 per (t,d,n) update (2 mul + 2 fma + v_exp_f32 at half rate); "
+                        "peak = 256 CU x 64 lanes x 2.4 GHz (packed fp32 disabled); HBM side: "
+                        f"{main_res['hbm_gbps']:.0f} GB/s = {hbm_frac:.3f} of 8 TB/s")
+    else:
+        roof = {"bound": "hbm", "achieved": main_res["hbm_gbps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": hbm_frac}
+    roof["traffic"] = traffic
+    roof["hbm_gbps"] = main_res["hbm_gbps"]
+    roof["hbm_frac"] = hbm_frac
+    roof["alg_bytes_per_launch"] = main_res["alg_bytes"]
+    roof["kernel_ms"] = main_res["kernel_ms"]
+
+    line = {
+        "metric": "scan fwd B*L*D elems/s + achieved HBM GB/s (% of peak); decode updates/s",
+        "value": main_res["elems_per_s"], "unit": "elem/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": main_res["ms_per_step"], "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": args.workload, "batch": main_res["batch"], "seqlen": main_res["seqlen"],
+                   "dim": main_res["dim"], "dstate": main_res["dstate"], "io_dtype": main_res["io_dtype"],
+                   "state_dtype": "f32", "delta_softplus": True, "gate": True,
+                   "rotated_input_sets": main_res["rotated_input_sets"]},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(args.workload, np, W)
+        log(f"[bench] cpu oracle: {line['cpu_baseline']['value']:.3e} elem/s on {line['cpu_baseline']['cores']} cores")
+    if extra:
+        line["extra"] = extra
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,169 @@
+/*
+ * ssm.h -- C ABI of the MI355X (gfx950) selective state-space scan library.
+ *
+ * Two operations, both run by hand-written HIP kernels on the caller's stream:
+ *
+ *   ssm_scan_fwd      the selective scan (S6) forward over a whole sequence;
+ *   ssm_state_update  one single-token decode step of the same recurrence.
+ *
+ * What is computed (per batch b and channel d, independently; N = dstate):
+ *
+ *   dt_t  = softplus(delta[b,t,d] + delta_bias[d])   if delta_softplus
+ *         = delta[b,t,d] + delta_bias[d]              otherwise
+ *   h_t   = exp(dt_t * A[d,:]) (.) h_{t-1} + dt_t * B[b,t,:] * x[b,t,d],   h_{-1} = 0
+ *   y_t   = <C[b,t,:], h_t> + D[d] * x[b,t,d]
+ *   y_t  *= silu(z[b,t,d])                            if z is given
+ *
+ * Sources (page title and section):
+ *  - "Mamba 论文精读" (youngju.dev), sec. 2.2: the discretised recurrence
+ *    h_t = Abar h_{t-1} + Bbar x_t, y_t = C h_t with Abar = exp(delta A);
+ *    sec. 3.3: selective_scan(x, delta, A, B, C) with x, delta (B,L,D),
+ *    A (D,N), B and C (B,L,N) shared across channels, Bbar x = delta B x,
+ *    a zero initial state, and the state updated before y_t is read out;
+ *    sec. 3.1: delta = softplus(Linear_delta(x)), whose projection carries a
+ *    bias (sec. 3.4); sec. 3.4: the per-channel skip D and the SiLU(z) gate;
+ *    sec. 6: decoding costs O(1) per token with a fixed-size state.
+ *  - "Mamba的基础知识" (weblog-19d), state space model section: D is the
+ *    direct input-to-output term.
+ *  - "mamba->jamba" (blog.csdn.net), sec. 2.3: discretisation, scan and
+ *    read-out are fused on chip and the (B,L,D,N) intermediates never reach
+ *    HBM; only the final state is written.
+ *
+ * Conventions shared by every call
+ *  - Every tensor argument is a DEVICE pointer to contiguous row-major memory
+ *    in the shape listed beside it (last dimension fastest).  The caller owns
+ *    every buffer; the library keeps no pointer after a call returns.
+ *  - `dtype` is the storage type of x, delta, B, C, z and y.  A, D,
+ *    delta_bias, last_state and state are always fp32.  All arithmetic is
+ *    fp32; bf16 results are rounded to nearest-even.
+ *  - Optional arguments are NULL: D (no skip term), z (no gate), delta_bias
+ *    (zero bias), last_state (not written).
+ *  - Calls are asynchronous: work is enqueued on `stream` (a hipStream_t;
+ *    NULL = the null stream) and the call returns.  A non-OK status means
+ *    nothing was enqueued, except SSM_ERR_HIP, which reports a failed launch
+ *    (work enqueued before it may still run).  Faults inside a kernel
+ *    surface at the caller's next synchronisation.
+ *  - Validation happens on the host before any launch: negative sizes,
+ *    NULL required pointers and overlapping outputs give
+ *    SSM_ERR_INVALID_ARG; a dstate outside {1, 2, 4, 8, 16, 32, 64} or an
+ *    unknown dtype gives SSM_ERR_UNSUPPORTED; a pointer not aligned to its
+ *    element size gives SSM_ERR_MISALIGNED (and for ssm_scan_fwd with bf16
+ *    and an even dstate, B and C must be 4-byte aligned, since they are read
+ *    as bf16 pairs).  Faster paths are used when x, delta, z and y are
+ *    16-byte aligned and dim is a multiple of 8 (bf16) or 4 (fp32); other
+ *    layouts are handled element by element.  A batch, seqlen or dim of 0 is
+ *    valid and enqueues nothing (except that ssm_scan_fwd zero-fills a
+ *    non-empty last_state when seqlen == 0, the state after no steps).
+ *  - No C++ exception crosses the ABI.  The calls are thread-safe; calls
+ *    that write the same buffers must be ordered by the caller.
+ *  - ssm_last_error() gives a thread-local human-readable detail for the
+ *    last non-OK status returned on the calling thread.
+ */
+#ifndef SSM_H_
+#define SSM_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SSM_ABI_VERSION 1
+
+#if defined(__GNUC__)
+#define SSM_API __attribute__((visibility("default")))
+#else
+#define SSM_API
+#endif
+
+typedef enum { SSM_F32 = 0, SSM_BF16 = 1 } ssm_dtype_t;
+
+typedef enum {
+  SSM_OK = 0,
+  SSM_ERR_INVALID_ARG = 1,
+  SSM_ERR_UNSUPPORTED = 2,
+  SSM_ERR_MISALIGNED = 3,
+  SSM_ERR_HIP = 4
+} ssm_status_t;
+
+/*
+ * Selective scan forward over a whole sequence ("Mamba 论文精读" sec. 3.3;
+ * "mamba->jamba" sec. 2.3 for the fused, on-chip evaluation).
+ *
+ *   x, delta, z   (batch, seqlen, dim)    dtype; delta is the raw step
+ *   A             (dim, dstate)           fp32, expected negative (not checked)
+ *   B, C          (batch, seqlen, dstate) dtype, shared by all channels
+ *   D, delta_bias (dim)                   fp32, or NULL
+ *   y             (batch, seqlen, dim)    dtype, written; must not overlap an input
+ *   last_state    (batch, dim, dstate)    fp32 h after the last step, or NULL
+ *
+ * For small batch*dim the sequence is split into segments scanned in
+ * parallel and joined by a carry pass; that needs (segments * batch * dim *
+ * (dstate + 1)) fp32 of device scratch.  The library keeps one such buffer
+ * per (device, stream), allocated with hipMalloc on first need, grown when a
+ * larger call needs it (after synchronising that stream) and kept until the
+ * process ends.  A call that would allocate must not be captured into a HIP
+ * graph; calls on one stream reuse its buffer in stream order, and calls on
+ * different streams never share one.
+ */
+SSM_API ssm_status_t ssm_scan_fwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, ssm_dtype_t dtype,
+                          const void *x, const void *delta, const float *A, const void *B, const void *C,
+                          const float *D, const void *z, const float *delta_bias, int delta_softplus, void *y,
+                          float *last_state, void *stream);
+
+/*
+ * Launch-shape overrides for ssm_scan_fwd.  Every field 0 means "choose
+ * automatically".  The result does not depend on these choices beyond fp32
+ * rounding of the re-associated cross-segment carry; they exist for tuning
+ * and for the invariance tests.
+ *   chains_per_lane  state chains (values of n) per GPU lane: 1, 2, 4, 8 or 16,
+ *                    dividing dstate;
+ *   segments         number of sequence segments scanned in parallel (>= 1).
+ */
+typedef struct {
+  int32_t chains_per_lane;
+  int32_t segments;
+  int32_t reserved[6];
+} ssm_scan_opts_t;
+
+/* ssm_scan_fwd with launch-shape overrides (opts may be NULL). An override
+ * the kernels cannot honour gives SSM_ERR_UNSUPPORTED. */
+SSM_API ssm_status_t ssm_scan_fwd_ex(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, ssm_dtype_t dtype,
+                             const void *x, const void *delta, const float *A, const void *B, const void *C,
+                             const float *D, const void *z, const float *delta_bias, int delta_softplus,
+                             void *y, float *last_state, void *stream, const ssm_scan_opts_t *opts);
+
+/*
+ * One single-token decode step ("Mamba 论文精读" sec. 6: O(1) work per token
+ * with a fixed-size state; sec. 2.2: the recurrence).
+ *
+ *   state         (batch, dim, dstate)    fp32, read and updated in place
+ *   x, delta, z   (batch, dim)            dtype
+ *   A             (dim, dstate)           fp32
+ *   B, C          (batch, dstate)         dtype
+ *   D, delta_bias (dim)                   fp32, or NULL
+ *   y             (batch, dim)            dtype, written; must not overlap state or an input
+ *
+ * Running it for t = 0..L-1 from a zero state gives the same y_t and final
+ * state as ssm_scan_fwd over those L steps.
+ */
+SSM_API ssm_status_t ssm_state_update(int64_t batch, int64_t dim, int64_t dstate, ssm_dtype_t dtype, float *state,
+                              const void *x, const void *delta, const float *A, const void *B, const void *C,
+                              const float *D, const void *z, const float *delta_bias, int delta_softplus, void *y,
+                              void *stream);
+
+/* Static string naming a status code ("SSM_OK", ...); never NULL. */
+SSM_API const char *ssm_status_string(ssm_status_t status);
+
+/* Thread-local detail for the last non-OK status on this thread ("" if none).
+ * Valid until the next library call on the same thread. */
+SSM_API const char *ssm_last_error(void);
+
+/* SSM_ABI_VERSION of the loaded library. */
+SSM_API int ssm_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSM_H_ */

@@ -1,0 +1,188 @@
+"""MI355X (gfx950) selective state-space scan: thin Python binding over the C ABI in include/ssm.h.
+
+Every step of the computation runs in the HIP kernels of ``libssm61.so``.  This module only
+checks shapes and dtypes, allocates outputs with ``torch.empty`` (PyTorch is used for device
+memory and streams), passes ``data_ptr()`` values and the current HIP stream through ctypes, and
+turns a non-OK status into an exception.  If the library has not been built, importing works but
+every call raises: there is no fallback implementation.
+
+    y, last_state = ssm_scan_fwd(x, delta, A, B, C, D=D, z=z, delta_bias=bias, delta_softplus=True)
+    y_t = ssm_state_update(state, x_t, delta_t, A, B_t, C_t, D=D, z=z_t, delta_bias=bias,
+                           delta_softplus=True)
+
+Shapes: x, delta, z (batch, seqlen, dim); A (dim, dstate) fp32; B, C (batch, seqlen, dstate);
+D, delta_bias (dim,) fp32; y like x; last_state / state (batch, dim, dstate) fp32.  x, delta, B, C,
+z and y share one dtype: torch.float32 or torch.bfloat16.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIBRARY = os.path.join(_HERE, "libssm61.so")
+
+SSM_F32, SSM_BF16 = 0, 1
+STATUS_NAMES = {0: "SSM_OK", 1: "SSM_ERR_INVALID_ARG", 2: "SSM_ERR_UNSUPPORTED", 3: "SSM_ERR_MISALIGNED",
+                4: "SSM_ERR_HIP"}
+EXPORTED = ("ssm_scan_fwd", "ssm_scan_fwd_ex", "ssm_state_update", "ssm_status_string", "ssm_last_error",
+            "ssm_abi_version")
+
+
+class SsmError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        self.status = status
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {detail}")
+
+
+class ScanOpts(ctypes.Structure):
+    _fields_ = [("chains_per_lane", ctypes.c_int32), ("segments", ctypes.c_int32),
+                ("reserved", ctypes.c_int32 * 6)]
+
+
+_lib_handle = None
+
+
+def load_library(path: str = LIBRARY) -> ctypes.CDLL:
+    """Load libssm61.so (raises if it is missing: build it with ``__graft_entry__.build()``)."""
+    global _lib_handle
+    if _lib_handle is not None:
+        return _lib_handle
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: the HIP library must be built (there is no fallback)")
+    lib = ctypes.CDLL(path)
+    i64, i32, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
+    lib.ssm_scan_fwd.argtypes = [i64, i64, i64, i64, i32, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp]
+    lib.ssm_scan_fwd.restype = i32
+    lib.ssm_scan_fwd_ex.argtypes = lib.ssm_scan_fwd.argtypes + [ctypes.POINTER(ScanOpts)]
+    lib.ssm_scan_fwd_ex.restype = i32
+    lib.ssm_state_update.argtypes = [i64, i64, i64, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp]
+    lib.ssm_state_update.restype = i32
+    lib.ssm_status_string.argtypes = [i32]
+    lib.ssm_status_string.restype = ctypes.c_char_p
+    lib.ssm_last_error.argtypes = []
+    lib.ssm_last_error.restype = ctypes.c_char_p
+    lib.ssm_abi_version.argtypes = []
+    lib.ssm_abi_version.restype = i32
+    _lib_handle = lib
+    return lib
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        lib = load_library()
+        raise SsmError(status, lib.ssm_last_error().decode(errors="replace"))
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return SSM_F32
+    if t.dtype == torch.bfloat16:
+        return SSM_BF16
+    raise TypeError(f"x, delta, B, C, z must be float32 or bfloat16, got {t.dtype}")
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _need(t: Optional[torch.Tensor], name: str, shape, dtype, device, optional: bool = False) -> None:
+    if t is None:
+        if optional:
+            return
+        raise ValueError(f"{name} is required")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream(device: torch.device, stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream(device).cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def ssm_scan_fwd(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Tensor, C: torch.Tensor,
+                 D: Optional[torch.Tensor] = None, z: Optional[torch.Tensor] = None,
+                 delta_bias: Optional[torch.Tensor] = None, delta_softplus: bool = False, *,
+                 y: Optional[torch.Tensor] = None, last_state: Optional[torch.Tensor] = None,
+                 return_last_state: bool = True, chains_per_lane: int = 0, segments: int = 0,
+                 stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Selective scan forward (include/ssm.h: ssm_scan_fwd).  Returns (y, last_state); last_state
+    is None when return_last_state is False and none was passed in.  chains_per_lane and
+    segments override the launch shape (0 = automatic)."""
+    lib = load_library()
+    if x.dim() != 3 or A.dim() != 2:
+        raise ValueError("x must be (batch, seqlen, dim) and A (dim, dstate)")
+    batch, seqlen, dim = x.shape
+    dstate = A.shape[1]
+    dev, dt = x.device, x.dtype
+    code = _dtype_code(x)
+    _need(x, "x", (batch, seqlen, dim), dt, dev)
+    _need(delta, "delta", (batch, seqlen, dim), dt, dev)
+    _need(A, "A", (dim, dstate), torch.float32, dev)
+    _need(B, "B", (batch, seqlen, dstate), dt, dev)
+    _need(C, "C", (batch, seqlen, dstate), dt, dev)
+    _need(D, "D", (dim,), torch.float32, dev, optional=True)
+    _need(z, "z", (batch, seqlen, dim), dt, dev, optional=True)
+    _need(delta_bias, "delta_bias", (dim,), torch.float32, dev, optional=True)
+    if y is None:
+        y = torch.empty_like(x)
+    _need(y, "y", (batch, seqlen, dim), dt, dev)
+    if last_state is None and return_last_state:
+        last_state = torch.empty((batch, dim, dstate), dtype=torch.float32, device=dev)
+    _need(last_state, "last_state", (batch, dim, dstate), torch.float32, dev, optional=True)
+    opts = ScanOpts(int(chains_per_lane), int(segments))
+    status = lib.ssm_scan_fwd_ex(batch, seqlen, dim, dstate, code, _ptr(x), _ptr(delta), _ptr(A), _ptr(B),
+                                 _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias), int(bool(delta_softplus)), _ptr(y),
+                                 _ptr(last_state), _stream(dev, stream), ctypes.byref(opts))
+    _check(status)
+    return y, last_state
+
+
+def ssm_state_update(state: torch.Tensor, x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor,
+                     B: torch.Tensor, C: torch.Tensor, D: Optional[torch.Tensor] = None,
+                     z: Optional[torch.Tensor] = None, delta_bias: Optional[torch.Tensor] = None,
+                     delta_softplus: bool = False, *, y: Optional[torch.Tensor] = None,
+                     stream=None) -> torch.Tensor:
+    """One decode step (include/ssm.h: ssm_state_update); `state` is updated in place.
+    Returns y (batch, dim)."""
+    lib = load_library()
+    if x.dim() != 2 or A.dim() != 2:
+        raise ValueError("x must be (batch, dim) and A (dim, dstate)")
+    batch, dim = x.shape
+    dstate = A.shape[1]
+    dev, dt = x.device, x.dtype
+    code = _dtype_code(x)
+    _need(state, "state", (batch, dim, dstate), torch.float32, dev)
+    _need(delta, "delta", (batch, dim), dt, dev)
+    _need(A, "A", (dim, dstate), torch.float32, dev)
+    _need(B, "B", (batch, dstate), dt, dev)
+    _need(C, "C", (batch, dstate), dt, dev)
+    _need(D, "D", (dim,), torch.float32, dev, optional=True)
+    _need(z, "z", (batch, dim), dt, dev, optional=True)
+    _need(delta_bias, "delta_bias", (dim,), torch.float32, dev, optional=True)
+    if y is None:
+        y = torch.empty_like(x)
+    _need(y, "y", (batch, dim), dt, dev)
+    status = lib.ssm_state_update(batch, dim, dstate, code, _ptr(state), _ptr(x), _ptr(delta), _ptr(A), _ptr(B),
+                                  _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias), int(bool(delta_softplus)), _ptr(y),
+                                  _stream(dev, stream))
+    _check(status)
+    return y
+
+
+def abi_version() -> int:
+    return load_library().ssm_abi_version()
+
+
+__all__ = ["ssm_scan_fwd", "ssm_state_update", "abi_version", "load_library", "SsmError", "ScanOpts",
+           "LIBRARY", "EXPORTED"]

@@ -1,0 +1,48 @@
+"""Compile the HIP library in-tree for gfx950: selective_state_space_61_amd/libssm61.so."""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+import time
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+LIBRARY = os.path.join(HERE, "libssm61.so")
+SOURCES = [os.path.join(CSRC, "ssm_api.hip")]
+HEADERS = [os.path.join(CSRC, f) for f in ("ssm_device.hpp", "scan_fwd.hpp", "state_update.hpp")] + [
+    os.path.join(os.path.dirname(HERE), "include", "ssm.h")]
+ARCH = "gfx950"
+
+# -packed-fp32-ops: no v_pk_{add,mul,fma}_f32 anywhere (the host pass warns that it does not know
+# the feature; that is harmless).
+FLAGS = ["-O3", "-std=c++17", "-fPIC", "-shared", "-fvisibility=hidden", "-Wall", "-Wno-unused-function",
+         f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+
+
+def build(verbose: bool = False) -> str:
+    """Always recompiles (the caller asked for a build)."""
+    t0 = time.time()
+    cmd = ["hipcc", *FLAGS, "-o", LIBRARY + ".tmp", *SOURCES]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    noise = "is not a recognized feature for this target"
+    err = "\n".join(l for l in (r.stderr or "").splitlines() if noise not in l)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({r.returncode}):\n{' '.join(cmd)}\n{err}")
+    os.replace(LIBRARY + ".tmp", LIBRARY)
+    if verbose:
+        if err.strip():
+            print(err, file=sys.stderr)
+        print(f"built {LIBRARY} in {time.time() - t0:.1f}s")
+    return LIBRARY
+
+
+def is_stale() -> bool:
+    if not os.path.exists(LIBRARY):
+        return True
+    lib_t = os.path.getmtime(LIBRARY)
+    return any(os.path.getmtime(s) > lib_t for s in SOURCES + HEADERS)
+
+
+if __name__ == "__main__":
+    build(verbose=True)

@@ -1,0 +1,369 @@
+// ssm_api.hip -- the C ABI declared in include/ssm.h: host-side validation, launch-shape choice
+// and kernel launches on the caller's stream.  No torch types, no exceptions across the ABI.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <utility>
+
+#include "../../include/ssm.h"
+#include "scan_fwd.hpp"
+#include "state_update.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+ssm_status_t fail(ssm_status_t s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+bool mul_ok(int64_t a, int64_t b, int64_t* out) { return !__builtin_mul_overflow(a, b, out); }
+
+struct Range {
+  const void* p;
+  int64_t bytes;
+};
+
+bool overlap(Range a, Range b) {
+  if (!a.p || !b.p || a.bytes <= 0 || b.bytes <= 0) return false;
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a.p), b0 = reinterpret_cast<uintptr_t>(b.p);
+  return a0 < b0 + static_cast<uintptr_t>(b.bytes) && b0 < a0 + static_cast<uintptr_t>(a.bytes);
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+struct Arg {
+  const void* p;
+  int64_t align;
+  const char* name;
+};
+
+// first non-NULL argument not aligned to its element size, or NULL
+const Arg* misaligned(const Arg* args, size_t n) {
+  for (size_t i = 0; i < n; ++i)
+    if (args[i].p && !aligned(args[i].p, static_cast<uintptr_t>(args[i].align))) return &args[i];
+  return nullptr;
+}
+
+bool dstate_supported(int64_t n) {
+  return n == 1 || n == 2 || n == 4 || n == 8 || n == 16 || n == 32 || n == 64;
+}
+
+// chains per lane the scan kernels are instantiated for, given N (at most 16 waves per workgroup)
+bool npl_supported(int64_t n, int npl) {
+  if (npl != 1 && npl != 2 && npl != 4 && npl != 8 && npl != 16) return false;
+  if (npl > n || (n % npl) != 0) return false;
+  return n / npl <= 16;
+}
+
+int default_npl(int64_t n) {
+  if (n >= 64) return 4;
+  if (n >= 2) return 2;
+  return 1;
+}
+
+// ---- kernel tables -----------------------------------------------------------------------------
+using ScanKernel = void (*)(const ssm::ScanArgs);
+using CarryKernel = void (*)(const ssm::ScanArgs);
+using UpdateKernel = void (*)(const ssm::UpdateArgs);
+
+template <bool BF16, int N, int NPL>
+void register_scan(std::map<std::pair<int, int>, std::pair<ScanKernel, ScanKernel>>& m) {
+  m[{N, NPL}] = {ssm::scan_chunk_kernel<BF16, N, NPL, ssm::MODE_FULL>,
+                 ssm::scan_chunk_kernel<BF16, N, NPL, ssm::MODE_AGG>};
+}
+
+template <bool BF16>
+const std::map<std::pair<int, int>, std::pair<ScanKernel, ScanKernel>>& scan_table() {
+  static const auto table = [] {
+    std::map<std::pair<int, int>, std::pair<ScanKernel, ScanKernel>> m;
+    register_scan<BF16, 1, 1>(m);
+    register_scan<BF16, 2, 1>(m);
+    register_scan<BF16, 2, 2>(m);
+    register_scan<BF16, 4, 1>(m);
+    register_scan<BF16, 4, 2>(m);
+    register_scan<BF16, 4, 4>(m);
+    register_scan<BF16, 8, 1>(m);
+    register_scan<BF16, 8, 2>(m);
+    register_scan<BF16, 8, 4>(m);
+    register_scan<BF16, 8, 8>(m);
+    register_scan<BF16, 16, 1>(m);
+    register_scan<BF16, 16, 2>(m);
+    register_scan<BF16, 16, 4>(m);
+    register_scan<BF16, 16, 8>(m);
+    register_scan<BF16, 16, 16>(m);
+    register_scan<BF16, 32, 2>(m);
+    register_scan<BF16, 32, 4>(m);
+    register_scan<BF16, 32, 8>(m);
+    register_scan<BF16, 32, 16>(m);
+    register_scan<BF16, 64, 4>(m);
+    register_scan<BF16, 64, 8>(m);
+    register_scan<BF16, 64, 16>(m);
+    return m;
+  }();
+  return table;
+}
+
+CarryKernel carry_kernel(int64_t n) {
+  switch (n) {
+    case 1: return ssm::scan_carry_kernel<1>;
+    case 2: return ssm::scan_carry_kernel<2>;
+    case 4: return ssm::scan_carry_kernel<4>;
+    case 8: return ssm::scan_carry_kernel<8>;
+    case 16: return ssm::scan_carry_kernel<16>;
+    case 32: return ssm::scan_carry_kernel<32>;
+    case 64: return ssm::scan_carry_kernel<64>;
+    default: return nullptr;
+  }
+}
+
+template <bool BF16>
+UpdateKernel update_kernel(int64_t n) {
+  switch (n) {
+    case 1: return ssm::state_update_kernel<BF16, 1>;
+    case 2: return ssm::state_update_kernel<BF16, 2>;
+    case 4: return ssm::state_update_kernel<BF16, 4>;
+    case 8: return ssm::state_update_kernel<BF16, 8>;
+    case 16: return ssm::state_update_kernel<BF16, 16>;
+    case 32: return ssm::state_update_kernel<BF16, 32>;
+    case 64: return ssm::state_update_kernel<BF16, 64>;
+    default: return nullptr;
+  }
+}
+
+__global__ void fill_zero_kernel(float* p, int64_t n) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i < n) p[i] = 0.0f;
+}
+
+// ---- segment scratch: one growable device buffer per (device, stream) ----------------------------
+struct Scratch {
+  float* ptr = nullptr;
+  int64_t floats = 0;
+};
+std::mutex g_scratch_mu;
+std::map<std::pair<int, uintptr_t>, Scratch> g_scratch;
+
+ssm_status_t get_scratch(hipStream_t stream, int64_t floats, float** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(SSM_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  Scratch& s = g_scratch[{dev, reinterpret_cast<uintptr_t>(stream)}];
+  if (s.floats < floats) {
+    if (s.ptr) {
+      // earlier work on this stream may still read the old buffer
+      e = hipStreamSynchronize(stream);
+      if (e != hipSuccess) return fail(SSM_ERR_HIP, "hipStreamSynchronize: %s", hipGetErrorString(e));
+      e = hipFree(s.ptr);
+      s.ptr = nullptr;
+      s.floats = 0;
+      if (e != hipSuccess) return fail(SSM_ERR_HIP, "hipFree: %s", hipGetErrorString(e));
+    }
+    void* p = nullptr;
+    e = hipMalloc(&p, static_cast<size_t>(floats) * sizeof(float));
+    if (e != hipSuccess) return fail(SSM_ERR_HIP, "hipMalloc(%lld floats): %s", (long long)floats, hipGetErrorString(e));
+    s.ptr = static_cast<float*>(p);
+    s.floats = floats;
+  }
+  *out = s.ptr;
+  return SSM_OK;
+}
+
+ssm_status_t check_launch(const char* what) {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(SSM_ERR_HIP, "%s launch failed: %s", what, hipGetErrorString(e));
+  return SSM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* ssm_status_string(ssm_status_t s) {
+  switch (s) {
+    case SSM_OK: return "SSM_OK";
+    case SSM_ERR_INVALID_ARG: return "SSM_ERR_INVALID_ARG";
+    case SSM_ERR_UNSUPPORTED: return "SSM_ERR_UNSUPPORTED";
+    case SSM_ERR_MISALIGNED: return "SSM_ERR_MISALIGNED";
+    case SSM_ERR_HIP: return "SSM_ERR_HIP";
+  }
+  return "SSM_ERR_UNKNOWN";
+}
+
+const char* ssm_last_error(void) { return g_err; }
+
+int ssm_abi_version(void) { return SSM_ABI_VERSION; }
+
+ssm_status_t ssm_scan_fwd_ex(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, ssm_dtype_t dtype,
+                             const void* x, const void* delta, const float* A, const void* B, const void* C,
+                             const float* D, const void* z, const float* delta_bias, int delta_softplus,
+                             void* y, float* last_state, void* stream, const ssm_scan_opts_t* opts) {
+  g_err[0] = '\0';
+  if (batch < 0 || seqlen < 0 || dim < 0 || dstate < 0)
+    return fail(SSM_ERR_INVALID_ARG, "negative size (batch=%lld seqlen=%lld dim=%lld dstate=%lld)",
+                (long long)batch, (long long)seqlen, (long long)dim, (long long)dstate);
+  if (dtype != SSM_F32 && dtype != SSM_BF16) return fail(SSM_ERR_UNSUPPORTED, "unknown dtype %d", (int)dtype);
+  if (!dstate_supported(dstate))
+    return fail(SSM_ERR_UNSUPPORTED, "dstate %lld not in {1,2,4,8,16,32,64}", (long long)dstate);
+  const int64_t es = dtype == SSM_BF16 ? 2 : 4;
+  int64_t n_bld, n_bln, n_bdn, n_dn;
+  if (!mul_ok(batch, seqlen, &n_bld) || !mul_ok(n_bld, dim, &n_bld) || !mul_ok(n_bld, es, &n_bld) ||
+      !mul_ok(batch, seqlen, &n_bln) || !mul_ok(n_bln, dstate, &n_bln) || !mul_ok(n_bln, es, &n_bln) ||
+      !mul_ok(batch, dim, &n_bdn) || !mul_ok(n_bdn, dstate * 4, &n_bdn) || !mul_ok(dim, dstate * 4, &n_dn))
+    return fail(SSM_ERR_INVALID_ARG, "tensor size overflows int64");
+  const int64_t nch = batch * dim;
+  if (nch == 0) return SSM_OK;  // nothing to compute, nothing to write
+  if (seqlen > 0) {
+    if (!x || !delta || !A || !B || !C || !y)
+      return fail(SSM_ERR_INVALID_ARG, "NULL required pointer (x, delta, A, B, C and y are required)");
+  }
+  const Arg args[] = {{x, es, "x"}, {delta, es, "delta"}, {A, 4, "A"}, {B, es, "B"}, {C, es, "C"},
+                      {D, 4, "D"}, {z, es, "z"}, {delta_bias, 4, "delta_bias"}, {y, es, "y"},
+                      {last_state, 4, "last_state"}};
+  if (const Arg* bad = misaligned(args, sizeof args / sizeof args[0]))
+    return fail(SSM_ERR_MISALIGNED, "%s (%p) is not aligned to its element size", bad->name, bad->p);
+  if (dtype == SSM_BF16 && (dstate % 2) == 0 && seqlen > 0 && !(aligned(B, 4) && aligned(C, 4)))
+    return fail(SSM_ERR_MISALIGNED, "bf16 B and C must be 4-byte aligned when dstate is even");
+  const Range rx{x, n_bld}, rd{delta, n_bld}, rz{z, n_bld}, rB{B, n_bln}, rC{C, n_bln}, rA{A, n_dn},
+      rD{D, dim * 4}, rb{delta_bias, dim * 4}, ry{seqlen > 0 ? y : nullptr, n_bld}, rs{last_state, n_bdn};
+  for (Range in : {rx, rd, rz, rB, rC, rA, rD, rb})
+    if (overlap(ry, in) || overlap(rs, in)) return fail(SSM_ERR_INVALID_ARG, "an output overlaps an input");
+  if (overlap(ry, rs)) return fail(SSM_ERR_INVALID_ARG, "y overlaps last_state");
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (seqlen == 0) {
+    if (last_state) {
+      const int64_t n = nch * dstate;
+      hipLaunchKernelGGL(fill_zero_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, st,
+                         last_state, n);
+      return check_launch("fill_zero_kernel");
+    }
+    return SSM_OK;
+  }
+
+  // launch shape
+  int npl = default_npl(dstate);
+  if (opts && opts->chains_per_lane) {
+    if (!npl_supported(dstate, opts->chains_per_lane))
+      return fail(SSM_ERR_UNSUPPORTED, "chains_per_lane %d not available for dstate %lld",
+                  (int)opts->chains_per_lane, (long long)dstate);
+    npl = opts->chains_per_lane;
+  }
+  const int G = static_cast<int>(dstate / npl);
+  const int64_t ncb = (dim + 63) / 64;
+  const int64_t base_wgs = ncb * batch;
+  const int64_t max_seg = (seqlen + 4 * ssm::kChunk - 1) / (4 * ssm::kChunk);  // >= 128 steps per segment
+  int64_t nseg = 1;
+  if (opts && opts->segments > 0) {
+    nseg = opts->segments;
+  } else if (base_wgs < 160) {
+    const int64_t target_waves = 4096;
+    nseg = (target_waves + base_wgs * G - 1) / (base_wgs * G);
+  }
+  if (nseg > max_seg) nseg = max_seg;
+  if (nseg < 1) nseg = 1;
+  int64_t seg_len = seqlen;
+  if (nseg > 1) {
+    seg_len = (seqlen + nseg - 1) / nseg;
+    seg_len = (seg_len + ssm::kChunk - 1) / ssm::kChunk * ssm::kChunk;
+    nseg = (seqlen + seg_len - 1) / seg_len;
+  }
+  int64_t grid;
+  if (!mul_ok(base_wgs, nseg, &grid) || grid > 0x7fffffff)
+    return fail(SSM_ERR_UNSUPPORTED, "grid of %lld x %lld workgroups is too large", (long long)base_wgs,
+                (long long)nseg);
+
+  const bool bf16 = dtype == SSM_BF16;
+  const auto& table = bf16 ? scan_table<true>() : scan_table<false>();
+  const auto it = table.find({static_cast<int>(dstate), npl});
+  if (it == table.end()) return fail(SSM_ERR_UNSUPPORTED, "no kernel for dstate %lld chains %d", (long long)dstate, npl);
+
+  ssm::ScanArgs a{};
+  a.x = x; a.delta = delta; a.A = A; a.B = B; a.C = C; a.Dskip = D; a.z = z; a.delta_bias = delta_bias;
+  a.y = y; a.last_state = last_state;
+  a.batch = batch; a.seqlen = seqlen; a.dim = dim; a.seg_len = seg_len;
+  a.nseg = static_cast<int32_t>(nseg);
+  a.ncb = static_cast<int32_t>(ncb);
+  a.softplus = delta_softplus ? 1 : 0;
+  const int64_t vmax = 16 / es;
+  a.vec_ok = (dim % vmax == 0) && aligned(x, 16) && aligned(delta, 16) && aligned(y, 16) && (!z || aligned(z, 16));
+
+  const unsigned threads = static_cast<unsigned>(64 * G);
+  if (nseg > 1) {
+    float* scratch = nullptr;
+    const int64_t floats = nseg * nch * (dstate + 1);
+    ssm_status_t s = get_scratch(st, floats, &scratch);
+    if (s != SSM_OK) return s;
+    a.seg_state = scratch;
+    a.seg_dsum = scratch + nseg * nch * dstate;
+    hipLaunchKernelGGL(it->second.second, dim3(static_cast<unsigned>(base_wgs * (nseg - 1))), dim3(threads), 0, st, a);
+    if ((s = check_launch("scan aggregate")) != SSM_OK) return s;
+    const int64_t per_seg = nch * dstate;
+    hipLaunchKernelGGL(carry_kernel(dstate), dim3(static_cast<unsigned>((per_seg + 255) / 256)), dim3(256), 0, st, a);
+    if ((s = check_launch("scan carry")) != SSM_OK) return s;
+  }
+  hipLaunchKernelGGL(it->second.first, dim3(static_cast<unsigned>(grid)), dim3(threads), 0, st, a);
+  return check_launch("scan");
+}
+
+ssm_status_t ssm_scan_fwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, ssm_dtype_t dtype,
+                          const void* x, const void* delta, const float* A, const void* B, const void* C,
+                          const float* D, const void* z, const float* delta_bias, int delta_softplus, void* y,
+                          float* last_state, void* stream) {
+  return ssm_scan_fwd_ex(batch, seqlen, dim, dstate, dtype, x, delta, A, B, C, D, z, delta_bias, delta_softplus,
+                         y, last_state, stream, nullptr);
+}
+
+ssm_status_t ssm_state_update(int64_t batch, int64_t dim, int64_t dstate, ssm_dtype_t dtype, float* state,
+                              const void* x, const void* delta, const float* A, const void* B, const void* C,
+                              const float* D, const void* z, const float* delta_bias, int delta_softplus, void* y,
+                              void* stream) {
+  g_err[0] = '\0';
+  if (batch < 0 || dim < 0 || dstate < 0)
+    return fail(SSM_ERR_INVALID_ARG, "negative size (batch=%lld dim=%lld dstate=%lld)", (long long)batch,
+                (long long)dim, (long long)dstate);
+  if (dtype != SSM_F32 && dtype != SSM_BF16) return fail(SSM_ERR_UNSUPPORTED, "unknown dtype %d", (int)dtype);
+  if (!dstate_supported(dstate))
+    return fail(SSM_ERR_UNSUPPORTED, "dstate %lld not in {1,2,4,8,16,32,64}", (long long)dstate);
+  const int64_t es = dtype == SSM_BF16 ? 2 : 4;
+  int64_t nch, n_bd, n_bn, n_state;
+  if (!mul_ok(batch, dim, &nch) || !mul_ok(nch, es, &n_bd) || !mul_ok(batch, dstate * es, &n_bn) ||
+      !mul_ok(nch, dstate * 4, &n_state))
+    return fail(SSM_ERR_INVALID_ARG, "tensor size overflows int64");
+  if (nch == 0) return SSM_OK;
+  if (!state || !x || !delta || !A || !B || !C || !y)
+    return fail(SSM_ERR_INVALID_ARG, "NULL required pointer (state, x, delta, A, B, C and y are required)");
+  const Arg args[] = {{state, 4, "state"}, {x, es, "x"}, {delta, es, "delta"}, {A, 4, "A"}, {B, es, "B"},
+                      {C, es, "C"}, {D, 4, "D"}, {z, es, "z"}, {delta_bias, 4, "delta_bias"}, {y, es, "y"}};
+  if (const Arg* bad = misaligned(args, sizeof args / sizeof args[0]))
+    return fail(SSM_ERR_MISALIGNED, "%s (%p) is not aligned to its element size", bad->name, bad->p);
+  const Range rs{state, n_state}, rx{x, n_bd}, rd{delta, n_bd}, rz{z, n_bd}, rB{B, n_bn}, rC{C, n_bn},
+      rA{A, dim * dstate * 4}, rD{D, dim * 4}, rb{delta_bias, dim * 4}, ry{y, n_bd};
+  for (Range in : {rx, rd, rz, rB, rC, rA, rD, rb})
+    if (overlap(ry, in) || overlap(rs, in)) return fail(SSM_ERR_INVALID_ARG, "an output overlaps an input");
+  if (overlap(ry, rs)) return fail(SSM_ERR_INVALID_ARG, "y overlaps state");
+
+  const int64_t spt = dstate < 4 ? dstate : 4;
+  const int64_t threads = nch * (dstate / spt);
+  const int64_t blocks = (threads + 255) / 256;
+  if (blocks > 0x7fffffff) return fail(SSM_ERR_UNSUPPORTED, "grid too large");
+  ssm::UpdateArgs a{};
+  a.state = state; a.x = x; a.delta = delta; a.A = A; a.B = B; a.C = C; a.Dskip = D; a.z = z;
+  a.delta_bias = delta_bias; a.y = y; a.batch = batch; a.dim = dim;
+  a.softplus = delta_softplus ? 1 : 0;
+  a.state_vec_ok = aligned(state, 16) ? 1 : 0;
+  const UpdateKernel k = dtype == SSM_BF16 ? update_kernel<true>(dstate) : update_kernel<false>(dstate);
+  hipLaunchKernelGGL(k, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, static_cast<hipStream_t>(stream), a);
+  return check_launch("state update");
+}
+
+}  // extern "C"

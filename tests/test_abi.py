@@ -1,0 +1,176 @@
+"""The C ABI (include/ssm.h) on the host: the library loads, exports every declared symbol, and its
+argument validation returns the documented statuses.  Every call here fails validation (or has
+nothing to do) before any HIP call, so no GPU is needed; the pointers are never dereferenced."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import selective_state_space_61_amd as ssm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ssm.h")
+
+OK, INVALID, UNSUPPORTED, MISALIGNED = 0, 1, 2, 3
+F32, BF16 = 0, 1
+P = 0x7F0000000000  # a 256-byte aligned fake device address; each tensor gets its own region
+GAP = 1 << 32
+
+
+def fake(i, off=0):
+    return P + i * GAP + off
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from selective_state_space_61_amd import build as b
+    if b.is_stale():
+        b.build()
+    return ssm.load_library()
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"SSM_API\s+[\w\s\*]*?\b(ssm_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    assert declared_symbols() == sorted(ssm.EXPORTED)
+
+
+def test_exports_every_declared_symbol(lib):
+    for name in declared_symbols():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", ssm.LIBRARY], capture_output=True, text=True, check=True)
+    exported = set(re.findall(r"\bT\s+(ssm_\w+)", out.stdout))
+    assert set(declared_symbols()) <= exported
+    # nothing else of ours leaks out of the library
+    assert {s for s in exported if s.startswith("ssm")} == set(declared_symbols())
+
+
+def test_abi_version_and_status_strings(lib):
+    ver = int(re.search(r"#define SSM_ABI_VERSION (\d+)", open(HEADER).read()).group(1))
+    assert lib.ssm_abi_version() == ver
+    names = [lib.ssm_status_string(i).decode() for i in range(5)]
+    assert names == ["SSM_OK", "SSM_ERR_INVALID_ARG", "SSM_ERR_UNSUPPORTED", "SSM_ERR_MISALIGNED", "SSM_ERR_HIP"]
+    assert lib.ssm_status_string(99).decode() == "SSM_ERR_UNKNOWN"
+
+
+def scan(lib, batch=2, seqlen=8, dim=16, dstate=16, dtype=F32, x=fake(0), delta=fake(1), A=fake(2), B=fake(3),
+         C=fake(4), D=fake(5), z=fake(6), bias=fake(7), softplus=1, y=fake(8), state=fake(9), opts=None):
+    if opts is None:
+        return lib.ssm_scan_fwd(batch, seqlen, dim, dstate, dtype, x, delta, A, B, C, D, z, bias, softplus, y, state,
+                                None)
+    return lib.ssm_scan_fwd_ex(batch, seqlen, dim, dstate, dtype, x, delta, A, B, C, D, z, bias, softplus, y, state,
+                               None, ctypes.byref(opts))
+
+
+def update(lib, batch=2, dim=16, dstate=16, dtype=F32, state=fake(0), x=fake(1), delta=fake(2), A=fake(3),
+           B=fake(4), C=fake(5), D=fake(6), z=fake(7), bias=fake(8), softplus=1, y=fake(9)):
+    return lib.ssm_state_update(batch, dim, dstate, dtype, state, x, delta, A, B, C, D, z, bias, softplus, y, None)
+
+
+def err(lib):
+    return lib.ssm_last_error().decode()
+
+
+@pytest.mark.parametrize("kw", [dict(batch=-1), dict(seqlen=-5), dict(dim=-2), dict(dstate=-4)])
+def test_scan_negative_sizes(lib, kw):
+    assert scan(lib, **kw) == INVALID and "negative" in err(lib)
+
+
+@pytest.mark.parametrize("n", [3, 5, 12, 128, 0])
+def test_scan_unsupported_dstate(lib, n):
+    assert scan(lib, dstate=n) == UNSUPPORTED and "dstate" in err(lib)
+
+
+def test_scan_unsupported_dtype(lib):
+    assert scan(lib, dtype=7) == UNSUPPORTED
+
+
+@pytest.mark.parametrize("name", ["x", "delta", "A", "B", "C", "y"])
+def test_scan_null_required(lib, name):
+    assert scan(lib, **{name: None}) == INVALID and "NULL" in err(lib)
+
+
+def test_scan_optional_may_be_null_but_nothing_to_do(lib):
+    # batch == 0 or dim == 0: valid, nothing enqueued, even with NULL tensors
+    assert scan(lib, batch=0, x=None, delta=None, A=None, B=None, C=None, D=None, z=None, bias=None, y=None,
+                state=None) == OK
+    assert scan(lib, dim=0) == OK
+
+
+@pytest.mark.parametrize("name,dtype,off", [("x", F32, 2), ("delta", BF16, 1), ("A", F32, 2), ("y", F32, 1),
+                                            ("state", F32, 2), ("D", F32, 1), ("bias", F32, 3), ("z", BF16, 1)])
+def test_scan_misaligned(lib, name, dtype, off):
+    base = {"x": 0, "delta": 1, "A": 2, "B": 3, "C": 4, "D": 5, "z": 6, "bias": 7, "y": 8, "state": 9}[name]
+    assert scan(lib, dtype=dtype, **{name: fake(base, off)}) == MISALIGNED
+
+
+def test_scan_bf16_bc_pairs_need_4_byte_alignment(lib):
+    assert scan(lib, dtype=BF16, B=fake(3, 2)) == MISALIGNED and "B and C" in err(lib)
+    assert scan(lib, dtype=BF16, C=fake(4, 2)) == MISALIGNED
+    # with an odd dstate the pair path is not used; 2-byte alignment is enough (not launched: dim=0)
+    assert scan(lib, dtype=BF16, dstate=1, B=fake(3, 2), dim=0) == OK
+
+
+@pytest.mark.parametrize("a,b", [("y", "x"), ("y", "delta"), ("y", "z"), ("y", "B"), ("state", "A"),
+                                 ("state", "y"), ("y", "D")])
+def test_scan_output_overlap(lib, a, b):
+    base = {"x": 0, "delta": 1, "A": 2, "B": 3, "C": 4, "D": 5, "z": 6, "bias": 7, "y": 8, "state": 9}
+    assert scan(lib, **{a: fake(base[b], 4)}) == INVALID and "overlap" in err(lib)
+
+
+def test_scan_opts_validation(lib):
+    assert scan(lib, dstate=16, opts=ssm.ScanOpts(3, 0)) == UNSUPPORTED
+    assert scan(lib, dstate=4, opts=ssm.ScanOpts(8, 0)) == UNSUPPORTED     # more chains than states
+    assert scan(lib, dstate=64, opts=ssm.ScanOpts(2, 0)) == UNSUPPORTED    # would need 32 waves
+    assert "chains_per_lane" in err(lib)
+
+
+def test_scan_size_overflow(lib):
+    assert scan(lib, batch=1 << 40, seqlen=1 << 30, dim=1 << 20) == INVALID and "overflow" in err(lib)
+
+
+@pytest.mark.parametrize("kw,code", [(dict(batch=-1), INVALID), (dict(dim=-1), INVALID), (dict(dstate=6), UNSUPPORTED),
+                                     (dict(dtype=3), UNSUPPORTED), (dict(state=None), INVALID), (dict(y=None), INVALID),
+                                     (dict(x=fake(1, 2)), MISALIGNED), (dict(state=fake(0, 2)), MISALIGNED),
+                                     (dict(y=fake(0, 8)), INVALID), (dict(state=fake(1, 0)), INVALID)])
+def test_update_validation(lib, kw, code):
+    assert update(lib, **kw) == code
+    assert err(lib)
+
+
+def test_update_nothing_to_do(lib):
+    assert update(lib, batch=0, state=None, x=None, delta=None, A=None, B=None, C=None, y=None) == OK
+
+
+def test_error_string_is_thread_local(lib):
+    import threading
+    scan(lib, batch=-1)
+    seen = {}
+
+    def other():
+        seen["before"] = err(lib)
+        scan(lib, dstate=3)
+        seen["after"] = err(lib)
+
+    t = threading.Thread(target=other)
+    t.start()
+    t.join()
+    assert seen["before"] == "" and "dstate" in seen["after"]
+    assert "negative" in err(lib)
+
+
+def test_binding_raises_without_library(tmp_path):
+    import importlib
+    mod = importlib.import_module("selective_state_space_61_amd")
+    saved = mod._lib_handle
+    mod._lib_handle = None
+    try:
+        with pytest.raises(RuntimeError, match="no fallback"):
+            mod.load_library(str(tmp_path / "missing.so"))
+    finally:
+        mod._lib_handle = saved

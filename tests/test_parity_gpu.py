@@ -1,0 +1,250 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 oracle, element by element.
+
+Small cases compare every output; the full-size workloads compare sampled channels (block edges,
+the last channel, random ones) over the whole sequence, computed one by one by the oracle, in the
+launch configuration that bench.py times (automatic launch shape)."""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from gpu_util import TOL, assert_close, sample_channels, say, scan_on_gpu, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+THREADS = max(1, min(16, os.cpu_count() or 1))
+
+
+@pytest.fixture(scope="module")
+def o():
+    return oracle.load()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import selective_state_space_61_amd as ssm
+    ssm.load_library()
+    say(f"\n[gpu] {torch.cuda.get_device_name(0)}; library {ssm.LIBRARY}")
+
+
+def run_and_compare(o, t, dtype, softplus, what, **kw):
+    say(f"[case] {what}")
+    y, st, _ = scan_on_gpu(t, softplus, **kw)
+    y_ref, st_ref = o.scan(t["x"], t["delta"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"],
+                           delta_bias=t["delta_bias"], delta_softplus=softplus, nthreads=THREADS)
+    assert_close(to_host(y), y_ref, TOL[dtype], f"{what} y")
+    assert_close(to_host(st), st_ref, TOL[dtype], f"{what} last_state")
+    return y, st
+
+
+def test_tiny_workload(o):
+    w = W.WORKLOADS["tiny"]
+    run_and_compare(o, W.workload_inputs(w), w.dtype, w.delta_softplus, "tiny fp32 (1, 64, 16, N=4)")
+
+
+@pytest.mark.parametrize("variant", ["no_z", "no_D", "no_bias", "softplus_off", "bf16", "bare"])
+def test_tiny_variants(o, variant):
+    dtype = "bf16" if variant == "bf16" else "f32"
+    softplus = variant not in ("softplus_off", "bare")
+    t = W.scan_inputs(1, 64, 16, 4, dtype, seed=61000, has_z=variant not in ("no_z", "bare"),
+                      has_D=variant not in ("no_D", "bare"), has_bias=softplus and variant != "no_bias")
+    if not softplus:
+        # the step is used as given: keep it positive (|raw|), as softplus would
+        t["delta"] = np.abs(t["delta"]) if dtype == "f32" else t["delta"] & np.uint16(0x7FFF)
+    run_and_compare(o, t, dtype, softplus, f"tiny variant {variant}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("shape", [(3, 100, 200, 16), (2, 97, 136, 16), (1, 33, 64, 16), (2, 65, 1, 16),
+                                   (4, 160, 130, 4), (1, 1, 70, 16)])
+def test_tiles_and_ragged_tails(o, dtype, shape):
+    batch, L, dim, N = shape
+    t = W.scan_inputs(batch, L, dim, N, dtype, seed=hash(shape) % 1000)
+    run_and_compare(o, t, dtype, True, f"ragged {shape} {dtype}")
+
+
+CHAIN_CASES = [(n, c) for n in (1, 2, 4, 8, 16, 32, 64) for c in (1, 2, 4, 8, 16) if c <= n and n % c == 0
+               and n // c <= 16]
+
+
+@pytest.mark.parametrize("N,chains", CHAIN_CASES)
+def test_dstate_and_chains_per_lane(o, N, chains):
+    dtype = "bf16" if (N + chains) % 2 else "f32"
+    t = W.scan_inputs(2, 70, 96, N, dtype, seed=N * 31 + chains)
+    run_and_compare(o, t, dtype, True, f"N={N} chains={chains} {dtype}", chains_per_lane=chains)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("segments", [2, 3, 7, 16])
+def test_split_sequence(o, dtype, segments):
+    t = W.scan_inputs(1, 1000, 128, 16, dtype, seed=segments)
+    y, st = run_and_compare(o, t, dtype, True, f"segments={segments} {dtype}", segments=segments)
+    y1, st1, _ = scan_on_gpu(t, True, segments=1)
+    say(f"  max |y(seg={segments}) - y(seg=1)| = {float((y.float() - y1.float()).abs().max()):.3e}")
+
+
+def test_split_sequence_genomics_recipe(o):
+    t = W.scan_inputs(1, 8192, 256, 16, "f32", seed=5, recipe="genomics", has_bias=False)
+    run_and_compare(o, t, "f32", False, "genomics recipe L=8192, automatic segments")
+
+
+def test_empty_and_degenerate(o):
+    import selective_state_space_61_amd as ssm
+    dev = "cuda"
+    for dt in (torch.float32, torch.bfloat16):
+        x = torch.empty(2, 0, 8, dtype=dt, device=dev)
+        A = -torch.ones(8, 4, device=dev)
+        BC = torch.empty(2, 0, 4, dtype=dt, device=dev)
+        st = torch.full((2, 8, 4), 7.0, device=dev)
+        y, st = ssm.ssm_scan_fwd(x, x, A, BC, BC, last_state=st)
+        torch.cuda.synchronize()
+        assert y.numel() == 0 and torch.all(st == 0), "seqlen 0 must give a zero last_state"
+        x0 = torch.empty(0, 5, 8, dtype=dt, device=dev)
+        y0, s0 = ssm.ssm_scan_fwd(x0, x0, A, torch.empty(0, 5, 4, dtype=dt, device=dev),
+                                  torch.empty(0, 5, 4, dtype=dt, device=dev))
+        assert y0.shape == (0, 5, 8) and s0.shape == (0, 8, 4)
+    t = W.scan_inputs(3, 1, 5, 4, "f32", seed=3)
+    run_and_compare(o, t, "f32", True, "seqlen 1")
+
+
+def test_zero_step_keeps_state(o):
+    """delta = 0 (softplus off, no bias): the state stays zero and y = D x SiLU(z)."""
+    t = W.scan_inputs(2, 77, 96, 16, "f32", seed=8, has_bias=False)
+    t["delta"] = np.zeros_like(t["delta"])
+    y, st, _ = scan_on_gpu(t, False)
+    assert torch.all(st == 0)
+    x, z = t["x"].astype(np.float64), t["z"].astype(np.float64)
+    ref = x * z / (1 + np.exp(-z))
+    assert_close(to_host(y), ref, 1e-5, "delta=0 output")
+
+
+def test_unaligned_views(o):
+    """x / delta / z / y not 16-byte aligned: the element-by-element access path."""
+    import selective_state_space_61_amd as ssm
+    t = W.scan_inputs(2, 50, 72, 16, "f32", seed=9)
+    d = {k: to_dev(v) for k, v in t.items()}
+
+    def shifted(a):
+        buf = torch.empty(a.numel() + 1, dtype=a.dtype, device=a.device)
+        v = buf[1:].view(a.shape)
+        v.copy_(a)
+        return v
+    y = shifted(torch.zeros_like(d["x"]))
+    yy, st = ssm.ssm_scan_fwd(shifted(d["x"]), shifted(d["delta"]), d["A"], d["B"], d["C"], D=d["D"],
+                              z=shifted(d["z"]), delta_bias=d["delta_bias"], delta_softplus=True, y=y)
+    torch.cuda.synchronize()
+    assert yy.data_ptr() % 16 != 0
+    y_ref, st_ref = o.scan(t["x"], t["delta"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"],
+                           delta_bias=t["delta_bias"], delta_softplus=True)
+    assert_close(to_host(yy), y_ref, TOL["f32"], "unaligned y")
+    assert_close(to_host(st), st_ref, TOL["f32"], "unaligned state")
+
+
+def test_bitwise_deterministic():
+    t = W.scan_inputs(2, 300, 192, 16, "bf16", seed=12)
+    y1, s1, _ = scan_on_gpu(t, True)
+    y2, s2, _ = scan_on_gpu(t, True)
+    assert torch.equal(y1, y2) and torch.equal(s1, s2)
+    y3, s3, _ = scan_on_gpu(t, True, segments=4)
+    y4, s4, _ = scan_on_gpu(t, True, segments=4)
+    assert torch.equal(y3, y4) and torch.equal(s3, s4)
+
+
+# ---------------------------------------------------------------------------------------------------
+# full-size workloads, sampled channels
+# ---------------------------------------------------------------------------------------------------
+def full_size(o, name, nsample):
+    w = W.WORKLOADS[name]
+    say(f"[case] full size {name}: batch={w.batch} L={w.seqlen} dim={w.dim} N={w.dstate} {w.dtype}")
+    t = W.workload_inputs(w)
+    y, st, _ = scan_on_gpu(t, w.delta_softplus)
+    sb, sd = sample_channels(w.batch, w.dim, nsample, seed=w.seed)
+    y_ref, st_ref = o.scan_channels(t["x"], t["delta"], t["A"], t["B"], t["C"], sb, sd, D=t["D"], z=t["z"],
+                                    delta_bias=t["delta_bias"], delta_softplus=w.delta_softplus, nthreads=THREADS)
+    yg = to_host(y[torch.as_tensor(sb), :, torch.as_tensor(sd)])      # (nsel, L)
+    sg = to_host(st[torch.as_tensor(sb), torch.as_tensor(sd), :])     # (nsel, N)
+    assert_close(yg, y_ref, TOL[w.dtype], f"{name} y (sampled {len(sb)} channels)")
+    assert_close(sg, st_ref, TOL[w.dtype], f"{name} last_state (sampled)")
+    return t, y, st
+
+
+def test_full_mamba130m(o):
+    full_size(o, "mamba130m", 64)
+
+
+def test_full_mamba2p8b(o):
+    full_size(o, "mamba2p8b", 64)
+
+
+def test_full_genomics(o):
+    full_size(o, "genomics", 24)
+
+
+def test_full_genomics_impulse_carry(o):
+    """Impulse at t = 0 with delta_0 = 1, then delta = 0 for 2^20 - 1 steps: the state is held
+    exactly, so y_t = (C_t . B_0 + D x_t) SiLU(z_t) for every t; catches any carry error across
+    chunks and segments."""
+    w = W.WORKLOADS["genomics"]
+    t = W.workload_inputs(w)
+    t["delta"] = np.zeros_like(t["delta"])
+    t["delta"][:, 0, :] = 1.0
+    y, st, _ = scan_on_gpu(t, False)
+    sb, sd = sample_channels(w.batch, w.dim, 12, seed=3)
+    y_ref, st_ref = o.scan_channels(t["x"], t["delta"], t["A"], t["B"], t["C"], sb, sd, D=t["D"], z=t["z"],
+                                    delta_softplus=False, nthreads=THREADS)
+    yg = to_host(y[torch.as_tensor(sb), :, torch.as_tensor(sd)])
+    assert_close(yg, y_ref, TOL["f32"], "impulse carry y (sampled)")
+    assert_close(to_host(st[torch.as_tensor(sb), torch.as_tensor(sd), :]), st_ref, TOL["f32"], "impulse state")
+
+
+# ---------------------------------------------------------------------------------------------------
+# decode
+# ---------------------------------------------------------------------------------------------------
+def decode_steps(t, batch, dim, N, steps, softplus, device="cuda"):
+    import selective_state_space_61_amd as ssm
+    d = {k: to_dev(v, device) for k, v in t.items()}
+    state = torch.zeros(batch, dim, N, device=device)
+    ys = []
+    for s in range(steps):
+        ys.append(ssm.ssm_state_update(state, d["x"][s], d["delta"][s], d["A"], d["B"][s], d["C"][s], D=d["D"],
+                                       z=None if d["z"] is None else d["z"][s], delta_bias=d["delta_bias"],
+                                       delta_softplus=softplus))
+    torch.cuda.synchronize()
+    return torch.stack(ys), state
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("N", [1, 2, 4, 8, 16, 32, 64])
+def test_decode_matches_scan_oracle(o, dtype, N):
+    batch, dim, steps = 3, 70, 12
+    w = W.Workload("dec", "decode", batch=batch, seqlen=steps, dim=dim, dstate=N, dtype=dtype, seed=N)
+    t = W.workload_inputs(w)
+    say(f"[case] decode N={N} {dtype}")
+    ys, state = decode_steps(t, batch, dim, N, steps, True)
+    sc = {k: (np.ascontiguousarray(np.swapaxes(v, 0, 1)) if k in ("x", "delta", "z", "B", "C") else v)
+          for k, v in t.items()}
+    y_ref, st_ref = o.scan(sc["x"], sc["delta"], sc["A"], sc["B"], sc["C"], D=sc["D"], z=sc["z"],
+                           delta_bias=sc["delta_bias"], delta_softplus=True)
+    assert_close(to_host(ys), np.swapaxes(y_ref, 0, 1), TOL[dtype], "decode y")
+    assert_close(to_host(state), st_ref, TOL[dtype], "decode state")
+
+
+def test_decode_full_workload(o):
+    w = W.WORKLOADS["decode"]
+    say(f"[case] full decode: batch={w.batch} dim={w.dim} N={w.dstate} steps={w.seqlen}")
+    t = W.workload_inputs(w)
+    ys, state = decode_steps(t, w.batch, w.dim, w.dstate, w.seqlen, w.delta_softplus)
+    sc = {k: (np.ascontiguousarray(np.swapaxes(v, 0, 1)) if k in ("x", "delta", "z", "B", "C") else v)
+          for k, v in t.items()}
+    sb, sd = sample_channels(w.batch, w.dim, 96, seed=4)
+    y_ref, st_ref = o.scan_channels(sc["x"], sc["delta"], sc["A"], sc["B"], sc["C"], sb, sd, D=sc["D"], z=sc["z"],
+                                    delta_bias=sc["delta_bias"], delta_softplus=True, nthreads=THREADS)
+    yg = to_host(ys[:, torch.as_tensor(sb), torch.as_tensor(sd)]).T       # (nsel, steps)
+    assert_close(yg, y_ref, TOL[w.dtype], "decode y over 256 steps (sampled)")
+    assert_close(to_host(state[torch.as_tensor(sb), torch.as_tensor(sd), :]), st_ref, TOL[w.dtype],
+                 "decode final state (sampled)")
