@@ -9,16 +9,21 @@
 // optionally x one segment of the sequence):
 //   * wave g of the workgroup owns state indices n in [g*NPL, (g+1)*NPL) of all 64 channels;
 //     lane = channel.  Its NPL states live in VGPRs for the whole sequence (never in HBM).
-//     B_t[n] and C_t[n] are the same for all 64 lanes, so they are read through the scalar
-//     cache into SGPRs.
+//     B_t[n] and C_t[n] are the same for all 64 lanes: lane k of every 16-lane row loads step
+//     k of each 16-step half of the chunk, and each step takes its values with DPP row
+//     broadcasts that are operands of the multiply (B_t * w) and of the read-out multiply-adds
+//     (C_t * h) -- no memory access and no LDS traffic for B and C.  Each step is one fused,
+//     hazard-ordered instruction block that also reads out the previous step.
 //   * per chunk of CHUNK time steps, all threads of the workgroup load the x / delta / z tile
 //     with coalesced vector loads (a chunk ahead, into registers), compute the per-(t, d)
 //     prologue once (softplus, dt * x) into LDS, every wave runs its CHUNK steps of the
 //     recurrence reading (dt, w) from LDS, writes its partial read-out sum_{n in group} C h
 //     to LDS, and the same threads that loaded the tile sum the G partials, add D x, apply
 //     the gate and store y with vector stores.
-//   * rows past the end of the sequence and channels past `dim` are carried with dt = w = 0
-//     and never stored.
+//   * rows past the end of the sequence and channels past `dim` are carried with
+//     dt = w = B = C = 0, which makes those steps exact identities on the state (A is clamped
+//     to a finite value, so exp2(0 * A) = 1); their outputs are never stored.  Every chunk
+//     therefore runs all CHUNK steps, fully unrolled.
 //
 // Split sequence (few channels, long L): the sequence is cut into `nseg` segments of seg_len
 // steps (a multiple of CHUNK).  Phase 1 (MODE_AGG) runs the recurrence of segments
@@ -107,7 +112,8 @@ __global__ __launch_bounds__(64 * (N / NPL)) void scan_chunk_kernel(const ScanAr
   float A2[NPL], h[NPL];
 #pragma unroll
   for (int j = 0; j < NPL; ++j) {
-    A2[j] = lane_ok ? p.A[d_lane * N + n0 + j] * kLog2e : 0.0f;
+    // log2(e) * A, clamped to a finite value: a padded step (dt = 0) must give exp2(0) = 1
+    A2[j] = lane_ok ? fmaxf(p.A[d_lane * N + n0 + j] * kLog2e, -3.0e38f) : 0.0f;
     h[j] = 0.0f;
   }
   if (kFull && p.nseg > 1 && lane_ok) {
@@ -133,6 +139,9 @@ __global__ __launch_bounds__(64 * (N / NPL)) void scan_chunk_kernel(const ScanAr
   const int64_t row_base = b * p.seqlen;  // (b, t) row index = row_base + t
 
   RawVec<BF16, VEC> nx[ITEMS], nd[ITEMS], nz[ITEMS];
+  constexpr int kHalves = kChunk / 16;
+  const int bc_k = lane & 15;
+  BcRow<BF16, NPL> nb[kHalves], nc[kHalves];
   auto load_tile = [&](int64_t t0) {
 #pragma unroll
     for (int i = 0; i < ITEMS; ++i) {
@@ -143,88 +152,136 @@ __global__ __launch_bounds__(64 * (N / NPL)) void scan_chunk_kernel(const ScanAr
       nd[i].load(p.delta, idx, nv, vec_ok);
       if (has_z) nz[i].load(p.z, idx, nv, vec_ok);
     }
+#pragma unroll
+    for (int hf = 0; hf < kHalves; ++hf) {
+      const int64_t t = t0 + hf * 16 + bc_k;
+      const int64_t e = (row_base + t) * N + n0;
+      nb[hf].load(p.B, e, t < t_end);
+      if constexpr (kFull) nc[hf].load(p.C, e, t < t_end);
+    }
   };
   if (t_begin < t_end) load_tile(t_begin);
 
+  // whole 64-channel block valid with vector access: chunks away from the sequence end need no
+  // per-element masking
+  const bool full_cols = vec_ok && (static_cast<int64_t>(cb) * 64 + 64 <= p.dim);
+
   for (int64_t t0 = t_begin; t0 < t_end; t0 += kChunk) {
+    const bool full = full_cols && (t0 + kChunk <= t_end);
+
     // 1. prologue of this chunk: (dt, dt * x) into LDS; keep x and z for the epilogue
     RawVec<BF16, VEC> cx[ITEMS], cz[ITEMS];
-    float dts[ITEMS][VEC];
+    float dts[ITEMS][VEC], xs[ITEMS][VEC];
 #pragma unroll
     for (int i = 0; i < ITEMS; ++i)
 #pragma unroll
-      for (int v = 0; v < VEC; ++v) dts[i][v] = nd[i].get(v) + bias[v];
+      for (int v = 0; v < VEC; ++v) {
+        dts[i][v] = nd[i].get(v) + bias[v];
+        xs[i][v] = nx[i].get(v);
+      }
     if (p.softplus) {
 #pragma unroll
       for (int i = 0; i < ITEMS; ++i)
 #pragma unroll
         for (int v = 0; v < VEC; ++v) dts[i][v] = softplus_f32(dts[i][v]);
     }
+    if (!full) {  // rows past the end and channels past dim become identity steps
+#pragma unroll
+      for (int i = 0; i < ITEMS; ++i) {
+        const bool row_ok = (t0 + row0 + i * RSTEP) < t_end;
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) {
+          const bool ok = row_ok && (v < nvalid_col);
+          dts[i][v] = ok ? dts[i][v] : 0.0f;
+          xs[i][v] = ok ? xs[i][v] : 0.0f;
+        }
+      }
+    }
 #pragma unroll
     for (int i = 0; i < ITEMS; ++i) {
       const int row = row0 + i * RSTEP;
-      const bool row_ok = (t0 + row) < t_end;
 #pragma unroll
-      for (int v = 0; v < VEC; ++v) {
-        const bool ok = row_ok && (v < nvalid_col);
-        const float dt = ok ? dts[i][v] : 0.0f;
-        s_dw[row][col + v] = make_float2(dt, ok ? dt * nx[i].get(v) : 0.0f);
-      }
+      for (int v = 0; v < VEC; ++v) s_dw[row][col + v] = make_float2(dts[i][v], dts[i][v] * xs[i][v]);
       cx[i] = nx[i];
       if (has_z) cz[i] = nz[i];
     }
+    float Bv[kHalves][NPL], Cv[kHalves][NPL];
+#pragma unroll
+    for (int hf = 0; hf < kHalves; ++hf)
+#pragma unroll
+      for (int j = 0; j < NPL; ++j) {
+        Bv[hf][j] = nb[hf].get(j);
+        Cv[hf][j] = kFull ? nc[hf].get(j) : 0.0f;
+      }
     // 2. prefetch the next chunk's tile into registers
     if (t0 + kChunk < t_end) load_tile(t0 + kChunk);
     __syncthreads();
 
-    // 3. the recurrence over this chunk, NPL chains per lane, B and C from SGPRs
-    const int64_t nsteps64 = t_end - t0;
-    const int nsteps = nsteps64 < kChunk ? static_cast<int>(nsteps64) : kChunk;
-    const int64_t e0 = (row_base + t0) * N + n0;
-    const BcChunk<BF16, N, NPL> Bc(p.B, e0);
-    const BcChunk<BF16, N, NPL> Cc(p.C, e0);
-    auto step = [&](int t) {
-      const float2 dw = s_dw[t][lane];
-      float yp = 0.0f;
+    // 3. the recurrence over this chunk: NPL chains per lane, all kChunk steps unrolled, the
+    //    (dt, w) pairs of kBatch steps read from LDS ahead of their use.  In FULL mode each step
+    //    t >= 1 is one fused block that also reads out step t - 1; step 31 is read out after the
+    //    loop.
+    constexpr int kBatch = 8;
+    static_for<kChunk / kBatch>([&](auto Q) {
+      constexpr int q = decltype(Q)::value;
+      float2 dw[kBatch];
+      static_for<kBatch>([&](auto K) { dw[decltype(K)::value] = s_dw[q * kBatch + decltype(K)::value][lane]; });
+      static_for<kBatch>([&](auto K) {
+        constexpr int k = decltype(K)::value;
+        constexpr int t = q * kBatch + k;
+        if constexpr (kFull && t > 0) {
+          s_yp[wave][t - 1][lane] =
+              step_readout<NPL, t % 16, (t - 1) % 16>(dw[k].x, dw[k].y, A2, Bv[t / 16], Cv[(t - 1) / 16], h);
+        } else {
 #pragma unroll
-      for (int j = 0; j < NPL; ++j) {
-        const float a = hw_exp2(dw.x * A2[j]);
-        h[j] = fmaf(a, h[j], dw.y * Bc.get(t, j));
-        if constexpr (kFull) yp = fmaf(Cc.get(t, j), h[j], yp);
-      }
-      if constexpr (kFull) s_yp[wave][t][lane] = yp;
-      else dsum += dw.x;
-    };
-    if (nsteps == kChunk) {
+          for (int j = 0; j < NPL; ++j)
+            h[j] = fmaf(hw_exp2(dw[k].x * A2[j]), h[j], row_bcast<t % 16>(Bv[t / 16][j]) * dw[k].y);
+          if constexpr (!kFull) dsum += dw[k].x;
+        }
+      });
+    });
+    if constexpr (kFull) {
+      float yp = row_bcast<15>(Cv[kHalves - 1][0]) * h[0];
 #pragma unroll
-      for (int t = 0; t < kChunk; ++t) step(t);
-    } else {
-      for (int t = 0; t < nsteps; ++t) step(t);
+      for (int j = 1; j < NPL; ++j) yp = fmaf(row_bcast<15>(Cv[kHalves - 1][j]), h[j], yp);
+      s_yp[wave][kChunk - 1][lane] = yp;
     }
 
     // 4. one barrier: every wave is done with s_dw (the next prologue may overwrite it) and
-    //    s_yp is complete.  The next chunk's first barrier orders this epilogue's reads of
-    //    s_yp before the next scan's writes.
+    //    s_yp is complete.  The next chunk's first barrier orders this epilogue's
+    //    reads of s_yp before the next scan's writes.
     __syncthreads();
 
     // 5. epilogue: y = sum of partials + D x, gated, stored with vector stores
     if constexpr (kFull) {
+      float out[ITEMS][VEC];
 #pragma unroll
       for (int i = 0; i < ITEMS; ++i) {
         const int row = row0 + i * RSTEP;
-        const int64_t t = t0 + row;
-        const int nv = (t < t_end) ? nvalid_col : 0;
-        float out[VEC];
 #pragma unroll
         for (int v = 0; v < VEC; ++v) {
-          float acc = 0.0f;
+          float acc = s_yp[0][row][col + v];
 #pragma unroll
-          for (int g = 0; g < G; ++g) acc += s_yp[g][row][col + v];
-          float yv = fmaf(dsk[v], cx[i].get(v), acc);
-          if (has_z) yv *= silu_f32(cz[i].get(v));
-          out[v] = yv;
+          for (int g = 1; g < G; ++g) acc += s_yp[g][row][col + v];
+          out[i][v] = fmaf(dsk[v], cx[i].get(v), acc);
         }
-        if (nv > 0) store_vec<BF16, VEC>(p.y, (row_base + t) * p.dim + d_col, out, nv, vec_ok);
+      }
+      if (has_z) {
+#pragma unroll
+        for (int i = 0; i < ITEMS; ++i)
+#pragma unroll
+          for (int v = 0; v < VEC; ++v) out[i][v] *= silu_f32(cz[i].get(v));
+      }
+#pragma unroll
+      for (int i = 0; i < ITEMS; ++i) {
+        const int64_t t = t0 + row0 + i * RSTEP;
+        const int64_t idx = (row_base + t) * p.dim + d_col;
+        if (full) {
+          store_vec<BF16, VEC>(p.y, idx, out[i], VEC, true);
+        } else {
+          const int nv = (t < t_end) ? nvalid_col : 0;
+          if (nv > 0) store_vec<BF16, VEC>(p.y, idx, out[i], nv, vec_ok);
+        }
       }
     }
   }

@@ -57,15 +57,20 @@ bool dstate_supported(int64_t n) {
   return n == 1 || n == 2 || n == 4 || n == 8 || n == 16 || n == 32 || n == 64;
 }
 
-// chains per lane the scan kernels are instantiated for, given N (at most 16 waves per workgroup)
+// chains per lane the scan kernels are instantiated for, given N: at most 16 waves per
+// workgroup, and N = 64 needs at least 8 chains per lane (16 waves would not fit the LDS)
 bool npl_supported(int64_t n, int npl) {
   if (npl != 1 && npl != 2 && npl != 4 && npl != 8 && npl != 16) return false;
   if (npl > n || (n % npl) != 0) return false;
+  if (n == 64 && npl < 8) return false;
   return n / npl <= 16;
 }
 
-int default_npl(int64_t n) {
-  if (n >= 64) return 4;
+// Measured on MI355X (dstate 16): with fewer workgroups than CUs, 2 chains per lane (8 waves
+// per workgroup) hides latency best; with more, 4 chains per lane (4 waves) does less work.
+int default_npl(int64_t n, int64_t workgroups) {
+  if (n >= 64) return 8;
+  if (n >= 4 && workgroups >= 256) return 4;
   if (n >= 2) return 2;
   return 1;
 }
@@ -104,7 +109,6 @@ const std::map<std::pair<int, int>, std::pair<ScanKernel, ScanKernel>>& scan_tab
     register_scan<BF16, 32, 4>(m);
     register_scan<BF16, 32, 8>(m);
     register_scan<BF16, 32, 16>(m);
-    register_scan<BF16, 64, 4>(m);
     register_scan<BF16, 64, 8>(m);
     register_scan<BF16, 64, 16>(m);
     return m;
@@ -251,7 +255,10 @@ ssm_status_t ssm_scan_fwd_ex(int64_t batch, int64_t seqlen, int64_t dim, int64_t
   }
 
   // launch shape
-  int npl = default_npl(dstate);
+  const int64_t ncb = (dim + 63) / 64;
+  const int64_t base_wgs = ncb * batch;
+  const bool split_auto = !(opts && opts->segments > 0) && base_wgs < 160;
+  int npl = default_npl(dstate, split_auto ? 1024 : base_wgs);
   if (opts && opts->chains_per_lane) {
     if (!npl_supported(dstate, opts->chains_per_lane))
       return fail(SSM_ERR_UNSUPPORTED, "chains_per_lane %d not available for dstate %lld",
@@ -259,13 +266,11 @@ ssm_status_t ssm_scan_fwd_ex(int64_t batch, int64_t seqlen, int64_t dim, int64_t
     npl = opts->chains_per_lane;
   }
   const int G = static_cast<int>(dstate / npl);
-  const int64_t ncb = (dim + 63) / 64;
-  const int64_t base_wgs = ncb * batch;
   const int64_t max_seg = (seqlen + 4 * ssm::kChunk - 1) / (4 * ssm::kChunk);  // >= 128 steps per segment
   int64_t nseg = 1;
   if (opts && opts->segments > 0) {
     nseg = opts->segments;
-  } else if (base_wgs < 160) {
+  } else if (split_auto) {
     const int64_t target_waves = 4096;
     nseg = (target_waves + base_wgs * G - 1) / (base_wgs * G);
   }

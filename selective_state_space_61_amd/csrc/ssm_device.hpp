@@ -6,25 +6,23 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+#include <utility>
+
 namespace ssm {
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.69314718055994531f;
 
-// Scalar-cache loads: a pointer in the constant address space whose address is
-// wave-uniform is read with s_load into SGPRs.
-typedef __attribute__((address_space(4))) const uint32_t* const_u32_ptr;
-typedef __attribute__((address_space(4))) const float* const_f32_ptr;
-
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
 
-// fp32 -> bf16, round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
+// fp32 -> bf16, round to nearest even: one v_cvt_pk_bf16_f32 per pair on gfx950.
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  const __bf16 a = static_cast<__bf16>(lo);
-  const __bf16 b = static_cast<__bf16>(hi);
-  return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, a)) |
-         (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, b)) << 16);
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 __device__ __forceinline__ uint16_t to_bf16(float v) {
   return __builtin_bit_cast(uint16_t, static_cast<__bf16>(v));
@@ -35,17 +33,17 @@ __device__ __forceinline__ float hw_exp2(float x) { return __builtin_amdgcn_exp2
 __device__ __forceinline__ float hw_log2(float x) { return __builtin_amdgcn_logf(x); }
 __device__ __forceinline__ float hw_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
 
-// softplus(v) = log(1 + e^v).  Above 20 the correction log1p(e^-v) < 2.1e-9 is
-// below fp32 resolution of v and v is returned.  Otherwise, with u = e^v and
-// w = fl(1 + u), log1p(u) = log(w) * u / (w - 1) (Goldberg's correction for
-// the rounding of 1 + u; exact when w == 1, where the result is u), which
-// keeps small steps (delta ~ 1e-4) accurate to a few ulp.
+// softplus(v) = log(1 + e^v).  Above 20 the correction log1p(e^-v) < 2.1e-9 is below the fp32
+// resolution of v and v is returned.  Otherwise u = e^v, w = fl(1 + u) and
+//   log1p(u) = log(w) + log(1 + e / w),  e = u - (w - 1)  (the exact rounding error of 1 + u;
+// w - 1 is exact),  and log(1 + e/w) is replaced by e: |e| <= 2^-24 w, so the dropped terms are
+// below 2^-24 * u * |e| + e^2, far under one ulp of the result.  For u < 2^-24, w = 1 and the
+// result is u exactly.  Small steps (delta ~ 1e-4) stay accurate to about an ulp.
 __device__ __forceinline__ float softplus_f32(float v) {
   const float u = hw_exp2(v * kLog2e);
   const float w = 1.0f + u;
-  const float wm1 = w - 1.0f;
-  const float lg = hw_log2(w) * kLn2;
-  const float r = (wm1 == 0.0f) ? u : lg * (u * hw_rcp(wm1));
+  const float e = u - (w - 1.0f);
+  const float r = fmaf(hw_log2(w), kLn2, e);
   return v > 20.0f ? v : r;
 }
 
@@ -142,54 +140,163 @@ __device__ __forceinline__ void store_vec(void* __restrict__ base, int64_t idx, 
   }
 }
 
-// Element `idx` of a B or C row read through the scalar cache (wave-uniform idx).  A bf16
-// element is taken from the aligned dword that holds it (that dword never leaves the memory
-// page of the element itself).  Generic path; the scan kernels use BcChunk below when they can.
-template <bool BF16>
-__device__ __forceinline__ float load_uniform(const void* base, int64_t idx) {
-  if constexpr (BF16) {
-    const uintptr_t addr = reinterpret_cast<uintptr_t>(base) + static_cast<uintptr_t>(idx) * 2u;
-    const uint32_t w = *reinterpret_cast<const_u32_ptr>(addr & ~static_cast<uintptr_t>(3));
-    return (addr & 2u) ? bf16_hi(w) : bf16_lo(w);
+// ---------------------------------------------------------------------------------------------
+// Row broadcasts (DPP row_newbcast:K, gfx90a and later): every lane of a 16-lane row reads lane K
+// of that row.  A register whose lane (row r, k) holds the value for step k (the same in every
+// row) hands step K's value to all 64 lanes without a memory access.
+// ---------------------------------------------------------------------------------------------
+template <int K>
+__device__ __forceinline__ float row_bcast(float v) {
+  static_assert(K >= 0 && K < 16, "row_newbcast selects one of 16 lanes");
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x150 + K, 0xF, 0xF,
+                                                               false));
+}
+
+// ---------------------------------------------------------------------------------------------
+// One step of the recurrence for a lane's chains, fused with the read-out of the PREVIOUS step:
+//   read-out (step t-1):  yp = sum_j C_{t-1}[j] * h[j]           (h still holds h_{t-1})
+//   update   (step t):    h[j] = exp2(dt * a2[j]) * h[j] + B_t[j] * w
+// B_t and C_{t-1} come from DPP row broadcasts (lanes KB and KC of each 16-lane row).  The
+// compiler does not fold a broadcast into a multiply-accumulate, so the step is written as one
+// instruction sequence.  Its order obeys the gfx9 VALU hazards, which the compiler cannot enforce
+// inside an asm statement:
+//   * a DPP instruction reads each VGPR operand at least two instructions after the VALU write
+//     of it (inside the block), and its first DPP instruction comes late enough that any write
+//     made just before the block is two or more instructions old;
+//   * no instruction reads a v_exp_f32 result sooner than two instructions after it.
+// The block has only VALU instructions: no memory access, no EXEC change.
+// ---------------------------------------------------------------------------------------------
+#define SSM_DPP_KB "row_newbcast:%[kb] row_mask:0xf bank_mask:0xf"
+#define SSM_DPP_KC "row_newbcast:%[kc] row_mask:0xf bank_mask:0xf"
+
+template <int KB, int KC>
+__device__ __forceinline__ float step_readout1(float dt, float w, float a2, float b, float c, float& h) {
+  float t0, u0, yp;
+  asm("v_mul_f32 %[t0], %[dt], %[a0]\n\t"
+      "v_exp_f32 %[t0], %[t0]\n\t"
+      "v_mul_f32_dpp %[u0], %[b0], %[w] " SSM_DPP_KB "\n\t"
+      "v_mul_f32_dpp %[yp], %[c0], %[h0] " SSM_DPP_KC "\n\t"
+      "v_fma_f32 %[h0], %[t0], %[h0], %[u0]"
+      : [t0] "=&v"(t0), [u0] "=&v"(u0), [yp] "=&v"(yp), [h0] "+v"(h)
+      : [dt] "v"(dt), [w] "v"(w), [a0] "v"(a2), [b0] "v"(b), [c0] "v"(c), [kb] "i"(KB), [kc] "i"(KC));
+  return yp;
+}
+
+template <int KB, int KC>
+__device__ __forceinline__ float step_readout2(float dt, float w, const float* a2, const float* b, const float* c,
+                                               float* h) {
+  float t0, t1, u0, u1, ya;
+  asm("v_mul_f32 %[t0], %[dt], %[a0]\n\t"
+      "v_mul_f32 %[t1], %[dt], %[a1]\n\t"
+      "v_exp_f32 %[t0], %[t0]\n\t"
+      "v_exp_f32 %[t1], %[t1]\n\t"
+      "v_mul_f32_dpp %[u0], %[b0], %[w] " SSM_DPP_KB "\n\t"
+      "v_mul_f32_dpp %[ya], %[c0], %[h0] " SSM_DPP_KC "\n\t"
+      "v_mul_f32_dpp %[u1], %[b1], %[w] " SSM_DPP_KB "\n\t"
+      "v_fma_f32 %[h0], %[t0], %[h0], %[u0]\n\t"
+      "v_fmac_f32_dpp %[ya], %[c1], %[h1] " SSM_DPP_KC "\n\t"
+      "v_fma_f32 %[h1], %[t1], %[h1], %[u1]"
+      : [t0] "=&v"(t0), [t1] "=&v"(t1), [u0] "=&v"(u0), [u1] "=&v"(u1), [ya] "=&v"(ya), [h0] "+v"(h[0]),
+        [h1] "+v"(h[1])
+      : [dt] "v"(dt), [w] "v"(w), [a0] "v"(a2[0]), [a1] "v"(a2[1]), [b0] "v"(b[0]), [b1] "v"(b[1]),
+        [c0] "v"(c[0]), [c1] "v"(c[1]), [kb] "i"(KB), [kc] "i"(KC));
+  return ya;
+}
+
+template <int KB, int KC>
+__device__ __forceinline__ float step_readout4(float dt, float w, const float* a2, const float* b, const float* c,
+                                               float* h) {
+  float t0, t1, t2, t3, u0, u1, u2, u3, ya, yb, yp;
+  asm("v_mul_f32 %[t0], %[dt], %[a0]\n\t"
+      "v_mul_f32 %[t1], %[dt], %[a1]\n\t"
+      "v_mul_f32 %[t2], %[dt], %[a2]\n\t"
+      "v_mul_f32 %[t3], %[dt], %[a3]\n\t"
+      "v_exp_f32 %[t0], %[t0]\n\t"
+      "v_exp_f32 %[t1], %[t1]\n\t"
+      "v_exp_f32 %[t2], %[t2]\n\t"
+      "v_exp_f32 %[t3], %[t3]\n\t"
+      "v_mul_f32_dpp %[u0], %[b0], %[w] " SSM_DPP_KB "\n\t"
+      "v_mul_f32_dpp %[ya], %[c0], %[h0] " SSM_DPP_KC "\n\t"
+      "v_mul_f32_dpp %[u1], %[b1], %[w] " SSM_DPP_KB "\n\t"
+      "v_mul_f32_dpp %[yb], %[c1], %[h1] " SSM_DPP_KC "\n\t"
+      "v_fma_f32 %[h0], %[t0], %[h0], %[u0]\n\t"
+      "v_fmac_f32_dpp %[ya], %[c2], %[h2] " SSM_DPP_KC "\n\t"
+      "v_mul_f32_dpp %[u2], %[b2], %[w] " SSM_DPP_KB "\n\t"
+      "v_fma_f32 %[h1], %[t1], %[h1], %[u1]\n\t"
+      "v_fmac_f32_dpp %[yb], %[c3], %[h3] " SSM_DPP_KC "\n\t"
+      "v_mul_f32_dpp %[u3], %[b3], %[w] " SSM_DPP_KB "\n\t"
+      "v_fma_f32 %[h2], %[t2], %[h2], %[u2]\n\t"
+      "v_fma_f32 %[h3], %[t3], %[h3], %[u3]\n\t"
+      "v_add_f32 %[yp], %[ya], %[yb]"
+      : [t0] "=&v"(t0), [t1] "=&v"(t1), [t2] "=&v"(t2), [t3] "=&v"(t3), [u0] "=&v"(u0), [u1] "=&v"(u1),
+        [u2] "=&v"(u2), [u3] "=&v"(u3), [ya] "=&v"(ya), [yb] "=&v"(yb), [yp] "=&v"(yp), [h0] "+v"(h[0]),
+        [h1] "+v"(h[1]), [h2] "+v"(h[2]), [h3] "+v"(h[3])
+      : [dt] "v"(dt), [w] "v"(w), [a0] "v"(a2[0]), [a1] "v"(a2[1]), [a2] "v"(a2[2]), [a3] "v"(a2[3]),
+        [b0] "v"(b[0]), [b1] "v"(b[1]), [b2] "v"(b[2]), [b3] "v"(b[3]), [c0] "v"(c[0]), [c1] "v"(c[1]),
+        [c2] "v"(c[2]), [c3] "v"(c[3]), [kb] "i"(KB), [kc] "i"(KC));
+  return yp;
+}
+
+// NPL chains: blocks of 4 (or the 1 / 2 forms); each block is hazard-safe on its own, so blocks
+// can follow one another in any order.
+template <int NPL, int KB, int KC>
+__device__ __forceinline__ float step_readout(float dt, float w, const float* a2, const float* b, const float* c,
+                                              float* h) {
+  if constexpr (NPL == 1) {
+    return step_readout1<KB, KC>(dt, w, a2[0], b[0], c[0], h[0]);
+  } else if constexpr (NPL == 2) {
+    return step_readout2<KB, KC>(dt, w, a2, b, c, h);
   } else {
-    return *reinterpret_cast<const_f32_ptr>(reinterpret_cast<uintptr_t>(base) + static_cast<uintptr_t>(idx) * 4u);
+    static_assert(NPL % 4 == 0, "chains per lane: 1, 2 or a multiple of 4");
+    float yp = step_readout4<KB, KC>(dt, w, a2, b, c, h);
+#pragma unroll
+    for (int g = 1; g < NPL / 4; ++g) yp += step_readout4<KB, KC>(dt, w, a2 + 4 * g, b + 4 * g, c + 4 * g, h + 4 * g);
+    return yp;
   }
 }
 
-// B_t[n0 + j] and C_t[n0 + j] for the steps t = 0.. of one chunk, read through the scalar cache
-// from a per-chunk base pointer so that every load has a compile-time offset.  `e0` is the
-// element index of (b, t0, n0).  For bf16 with even N the host guarantees 4-byte aligned B and
-// C, so element e0 + t*N + j lies in dword (e0 + t*N + j) / 2 of the tensor, in the high half
-// when that index is odd; with NPL even (so e0 even) the half is known at compile time.
-template <bool BF16, int N, int NPL>
-struct BcChunk {
-  static constexpr bool kPairs = BF16 && (N % 2 == 0);
-  const void* base;
-  int64_t e0;
-  int par;  // (e0 & 1) for the bf16 pair path
+#undef SSM_DPP_KB
+#undef SSM_DPP_KC
 
-  __device__ __forceinline__ BcChunk(const void* tensor, int64_t elem0) : base(tensor), e0(elem0) {
-    par = static_cast<int>(elem0 & 1);
-    if constexpr (kPairs) base = static_cast<const uint32_t*>(tensor) + (elem0 >> 1);
-    else if constexpr (!BF16) base = static_cast<const float*>(tensor) + elem0;
-  }
+// NPL consecutive elements of one B or C row (state indices n0 .. n0+NPL-1 of step t), loaded by
+// one lane as raw words and widened to fp32.  For bf16 with even NPL the elements come in
+// 4-byte-aligned pairs (the host requires 4-byte aligned B and C for an even dstate).
+template <bool BF16, int NPL>
+struct BcRow {
+  static constexpr int kWords = BF16 ? (NPL + 1) / 2 : NPL;
+  uint32_t w[kWords];
 
-  __device__ __forceinline__ float get(int t, int j) const {
-    if constexpr (kPairs) {
-      const const_u32_ptr w = reinterpret_cast<const_u32_ptr>(reinterpret_cast<uintptr_t>(base));
-      if constexpr (NPL % 2 == 0) {
-        const uint32_t v = w[(t * N + j) >> 1];
-        return (j & 1) ? bf16_hi(v) : bf16_lo(v);
-      } else {
-        const uint32_t v = w[(t * N + j + par) >> 1];
-        return ((j + par) & 1) ? bf16_hi(v) : bf16_lo(v);
-      }
-    } else if constexpr (!BF16) {
-      return reinterpret_cast<const_f32_ptr>(reinterpret_cast<uintptr_t>(base))[t * N + j];
+  __device__ __forceinline__ void load(const void* __restrict__ tensor, int64_t e, bool valid) {
+#pragma unroll
+    for (int i = 0; i < kWords; ++i) w[i] = 0u;
+    if (!valid) return;
+    if constexpr (BF16 && NPL == 1) {
+      w[0] = static_cast<const uint16_t*>(tensor)[e];
+    } else if constexpr (BF16) {
+      const uint32_t* p = reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(tensor) + e);
+#pragma unroll
+      for (int i = 0; i < kWords; ++i) w[i] = p[i];
     } else {
-      return load_uniform<true>(base, e0 + static_cast<int64_t>(t) * N + j);
+      const uint32_t* p = static_cast<const uint32_t*>(tensor) + e;
+#pragma unroll
+      for (int i = 0; i < kWords; ++i) w[i] = p[i];
     }
   }
+
+  __device__ __forceinline__ float get(int j) const {
+    if constexpr (BF16) return (j & 1) ? bf16_hi(w[j >> 1]) : bf16_lo(w[j >> 1]);
+    else return __builtin_bit_cast(float, w[j]);
+  }
 };
+
+// compile-time loop: f(std::integral_constant<int, I>) for I = 0 .. N-1
+template <typename F, int... Is>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, Is...>) {
+  (f(std::integral_constant<int, Is>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
 
 }  // namespace ssm

@@ -127,6 +127,7 @@ def test_scan_opts_validation(lib):
     assert scan(lib, dstate=16, opts=ssm.ScanOpts(3, 0)) == UNSUPPORTED
     assert scan(lib, dstate=4, opts=ssm.ScanOpts(8, 0)) == UNSUPPORTED     # more chains than states
     assert scan(lib, dstate=64, opts=ssm.ScanOpts(2, 0)) == UNSUPPORTED    # would need 32 waves
+    assert scan(lib, dstate=64, opts=ssm.ScanOpts(4, 0)) == UNSUPPORTED    # 16 waves: LDS too small
     assert "chains_per_lane" in err(lib)
 
 
