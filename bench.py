@@ -177,6 +177,66 @@ def traffic_from_profiles(name, alg_bytes):
     return rec["hbm_bytes_per_launch"], rec
 
 
+CALIB_BYTES = 512 << 20
+
+
+def profile_mode(args):
+    """For rocprofv3: one device-to-device copy of CALIB_BYTES (the calibration kernel for the
+    FETCH_SIZE / WRITE_SIZE counters), then warmup + steps launches of the workload's scan."""
+    import numpy as np
+    import torch
+
+    import workloads as W
+    import selective_state_space_61_amd as ssm
+
+    ssm.load_library()
+    src = torch.ones(CALIB_BYTES // 4, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    res = bench_scan(args.workload, args.steps, args.warmup, torch, np, W, ssm, torch.device("cuda:0"))
+    log(f"[profile] {args.workload}: {res['kernel_ms'] * 1e3:.1f} us/launch over {args.steps} launches")
+
+
+def summarize_traffic(fetch_csv, write_csv, workload):
+    """Turns the two rocprofv3 --pmc CSVs (FETCH_SIZE, WRITE_SIZE; KiB per dispatch) into HBM bytes
+    per scan launch, scaled by what the counters read for the calibration copy, and writes
+    profiles/traffic_<workload>.json."""
+    import csv
+    import workloads as W
+
+    def per_kernel(path, counter):
+        vals = {}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] == counter:
+                vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return vals
+
+    fetch, write = per_kernel(fetch_csv, "FETCH_SIZE"), per_kernel(write_csv, "WRITE_SIZE")
+    calib = [k for k in fetch if "copy" in k.lower()]
+    scan = [k for k in fetch if "scan_chunk_kernel" in k]
+    if not calib or not scan:
+        raise SystemExit(f"calibration or scan kernel missing in {fetch_csv}: {list(fetch)}")
+    ck, sk = calib[0], scan[0]
+    kib = CALIB_BYTES / 1024
+    f_scale = kib / max(fetch[ck]), kib / max(write[ck])  # the copy reads and writes CALIB_BYTES
+    f_kib = sorted(fetch[sk])[len(fetch[sk]) // 2]
+    w_kib = sorted(write[sk])[len(write[sk]) // 2]
+    w = W.WORKLOADS[workload]
+    es = 2 if w.dtype == "bf16" else 4
+    alg = scan_bytes(w.batch, w.seqlen, w.dim, w.dstate, es)
+    hbm = f_kib * 1024 * f_scale[0] + w_kib * 1024 * f_scale[1]
+    rec = {"workload": workload, "kernel": sk, "source_hash": source_hash(),
+           "fetch_kib_per_launch": f_kib, "write_kib_per_launch": w_kib,
+           "calibration_kernel": ck, "calibration_bytes": CALIB_BYTES,
+           "calibration_fetch_kib": max(fetch[ck]), "calibration_write_kib": max(write[ck]),
+           "fetch_scale": f_scale[0], "write_scale": f_scale[1],
+           "hbm_bytes_per_launch": hbm, "alg_bytes_per_launch": alg, "ratio_to_algorithmic": hbm / alg}
+    out = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    json.dump(rec, open(out, "w"), indent=2)
+    print(json.dumps(rec, indent=2))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -185,7 +245,17 @@ def main():
     ap.add_argument("--workload", default="mamba130m", choices=["mamba130m", "mamba2p8b", "genomics"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the context measurements (2.8B scan, decode)")
+    ap.add_argument("--profile-mode", action="store_true",
+                    help="calibration copy + scan launches only (run under rocprofv3)")
+    ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/traffic_<workload>.json from two rocprofv3 --pmc runs")
     args = ap.parse_args()
+    if args.summarize_traffic:
+        summarize_traffic(args.summarize_traffic[0], args.summarize_traffic[1], args.workload)
+        return
+    if args.profile_mode:
+        profile_mode(args)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py: this build measures one GPU only (--gpus {args.gpus}, WORLD_SIZE {world}); "
