@@ -142,7 +142,25 @@ __global__ __launch_bounds__(64 * (N / NPL)) void scan_chunk_kernel(const ScanAr
   constexpr int kHalves = kChunk / 16;
   const int bc_k = lane & 15;
   BcRow<BF16, NPL> nb[kHalves], nc[kHalves];
-  auto load_tile = [&](int64_t t0) {
+  // loads the x / delta / z tile and the B / C rows of the chunk starting at t0 into registers;
+  // `full` (uniform): every row of the chunk exists and the channel block is whole
+  auto load_tile = [&](int64_t t0, bool full) {
+    if (full) {
+#pragma unroll
+      for (int i = 0; i < ITEMS; ++i) {
+        const int64_t idx = (row_base + t0 + row0 + i * RSTEP) * p.dim + d_col;
+        nx[i].load(p.x, idx, VEC, true);
+        nd[i].load(p.delta, idx, VEC, true);
+        if (has_z) nz[i].load(p.z, idx, VEC, true);
+      }
+#pragma unroll
+      for (int hf = 0; hf < kHalves; ++hf) {
+        const int64_t e = (row_base + t0 + hf * 16 + bc_k) * N + n0;
+        nb[hf].load(p.B, e, true);
+        if constexpr (kFull) nc[hf].load(p.C, e, true);
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < ITEMS; ++i) {
       const int64_t t = t0 + row0 + i * RSTEP;
@@ -160,11 +178,11 @@ __global__ __launch_bounds__(64 * (N / NPL)) void scan_chunk_kernel(const ScanAr
       if constexpr (kFull) nc[hf].load(p.C, e, t < t_end);
     }
   };
-  if (t_begin < t_end) load_tile(t_begin);
 
   // whole 64-channel block valid with vector access: chunks away from the sequence end need no
   // per-element masking
   const bool full_cols = vec_ok && (static_cast<int64_t>(cb) * 64 + 64 <= p.dim);
+  if (t_begin < t_end) load_tile(t_begin, full_cols && t_begin + kChunk <= t_end);
 
   for (int64_t t0 = t_begin; t0 < t_end; t0 += kChunk) {
     const bool full = full_cols && (t0 + kChunk <= t_end);
@@ -214,7 +232,7 @@ __global__ __launch_bounds__(64 * (N / NPL)) void scan_chunk_kernel(const ScanAr
         Cv[hf][j] = kFull ? nc[hf].get(j) : 0.0f;
       }
     // 2. prefetch the next chunk's tile into registers
-    if (t0 + kChunk < t_end) load_tile(t0 + kChunk);
+    if (t0 + kChunk < t_end) load_tile(t0 + kChunk, full_cols && t0 + 2 * kChunk <= t_end);
     __syncthreads();
 
     // 3. the recurrence over this chunk: NPL chains per lane, all kChunk steps unrolled, the

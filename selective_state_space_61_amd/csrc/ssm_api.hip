@@ -358,16 +358,19 @@ ssm_status_t ssm_state_update(int64_t batch, int64_t dim, int64_t dstate, ssm_dt
   if (overlap(ry, rs)) return fail(SSM_ERR_INVALID_ARG, "y overlaps state");
 
   const int64_t spt = dstate < 4 ? dstate : 4;
-  const int64_t threads = nch * (dstate / spt);
-  const int64_t blocks = (threads + 255) / 256;
+  const int64_t quads = nch * (dstate / spt);
+  const int64_t per_block = static_cast<int64_t>(ssm::kUpdateThreads) * ssm::kQuadsPerThread;
+  const int64_t blocks = (quads + per_block - 1) / per_block;
   if (blocks > 0x7fffffff) return fail(SSM_ERR_UNSUPPORTED, "grid too large");
   ssm::UpdateArgs a{};
   a.state = state; a.x = x; a.delta = delta; a.A = A; a.B = B; a.C = C; a.Dskip = D; a.z = z;
   a.delta_bias = delta_bias; a.y = y; a.batch = batch; a.dim = dim;
   a.softplus = delta_softplus ? 1 : 0;
   a.state_vec_ok = aligned(state, 16) ? 1 : 0;
+  a.a_vec_ok = aligned(A, 16) ? 1 : 0;
   const UpdateKernel k = dtype == SSM_BF16 ? update_kernel<true>(dstate) : update_kernel<false>(dstate);
-  hipLaunchKernelGGL(k, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, static_cast<hipStream_t>(stream), a);
+  hipLaunchKernelGGL(k, dim3(static_cast<unsigned>(blocks)), dim3(ssm::kUpdateThreads), 0,
+                     static_cast<hipStream_t>(stream), a);
   return check_launch("state update");
 }
 

@@ -31,6 +31,7 @@ struct UpdateArgs {
   int64_t dim;
   int32_t softplus;
   int32_t state_vec_ok;  // state rows allow 16-byte access
+  int32_t a_vec_ok;      // rows of A allow 16-byte access
 };
 
 template <bool BF16>
@@ -39,71 +40,118 @@ __device__ __forceinline__ float load_elem(const void* base, int64_t idx) {
   else return static_cast<const float*>(base)[idx];
 }
 
+// Quads (SPT consecutive states of one channel) handled per thread: all their loads are issued
+// before any arithmetic, so each wave keeps several 1 KB state reads in flight.
+constexpr int kQuadsPerThread = 1;
+constexpr int kUpdateThreads = 256;
+
 template <bool BF16, int N>
-__global__ __launch_bounds__(256) void state_update_kernel(const UpdateArgs p) {
+__global__ __launch_bounds__(kUpdateThreads) void state_update_kernel(const UpdateArgs p) {
   constexpr int SPT = N < 4 ? N : 4;
   constexpr int TPC = N / SPT;
+  constexpr int Q = kQuadsPerThread;
   static_assert(TPC <= 64 && (64 % TPC) == 0, "a channel's lanes must share one wave");
-  const int64_t gid = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  const int64_t ch = gid / TPC;
-  const int sub = static_cast<int>(gid % TPC);
-  const bool ok = ch < p.batch * p.dim;
+  const int64_t nquads = p.batch * p.dim * TPC;
+  // quad of slice k: consecutive threads take consecutive quads (coalesced 16-byte accesses)
+  const int64_t base = static_cast<int64_t>(blockIdx.x) * (kUpdateThreads * Q) + threadIdx.x;
 
-  float yp = 0.0f;
-  float xv = 0.0f, zv = 0.0f;
-  if (ok) {
-    const int64_t b = ch / p.dim;
-    const int64_t d = ch % p.dim;
-    const int n0 = sub * SPT;
-    xv = load_elem<BF16>(p.x, ch);
-    const float vb = load_elem<BF16>(p.delta, ch) + (p.delta_bias ? p.delta_bias[d] : 0.0f);
-    const float dt = p.softplus ? softplus_f32(vb) : vb;
-    const float w = dt * xv;
-    if (p.z) zv = load_elem<BF16>(p.z, ch);
+  // optional tensors are read from an always-valid stand-in when absent and zeroed afterwards,
+  // so that no load is behind a branch
+  const void* zsrc = p.z ? p.z : p.x;
+  const float* bsrc = p.delta_bias ? p.delta_bias : p.A;
+  const float* dsrc = p.Dskip ? p.Dskip : p.A;
+  const float bias_on = p.delta_bias ? 1.0f : 0.0f, d_on = p.Dskip ? 1.0f : 0.0f;
 
-    float hs[SPT];
-    float* st = p.state + ch * N + n0;
+  float hs[Q][SPT], a2[Q][SPT], bv[Q][SPT], cv[Q][SPT];
+  float xv[Q], dv[Q], zv[Q], bias[Q], dsk[Q];
+  bool ok[Q];
+  // 1. loads, all unconditional: a quad past the end reads channel 0 (always in bounds) and its
+  //    results are never stored, so no load sits behind a branch and all stay in flight together
+#pragma unroll
+  for (int k = 0; k < Q; ++k) {
+    const int64_t q = base + k * kUpdateThreads;
+    ok[k] = q < nquads;
+    const int64_t ch = ok[k] ? q / TPC : 0;
+    const int n0 = static_cast<int>(q % TPC) * SPT;
+    const int64_t b = ch / p.dim, d = ch % p.dim;
+    const float* st = p.state + ch * N + n0;
     if constexpr (SPT == 4) {
       if (p.state_vec_ok) {
         const float4 v = *reinterpret_cast<const float4*>(st);
-        hs[0] = v.x; hs[1] = v.y; hs[2] = v.z; hs[3] = v.w;
+        hs[k][0] = v.x; hs[k][1] = v.y; hs[k][2] = v.z; hs[k][3] = v.w;
       } else {
 #pragma unroll
-        for (int j = 0; j < SPT; ++j) hs[j] = st[j];
+        for (int j = 0; j < SPT; ++j) hs[k][j] = st[j];
+      }
+      if (p.a_vec_ok) {
+        const float4 av = *reinterpret_cast<const float4*>(p.A + d * N + n0);
+        a2[k][0] = av.x; a2[k][1] = av.y; a2[k][2] = av.z; a2[k][3] = av.w;
+      } else {
+#pragma unroll
+        for (int j = 0; j < SPT; ++j) a2[k][j] = p.A[d * N + n0 + j];
       }
     } else {
 #pragma unroll
-      for (int j = 0; j < SPT; ++j) hs[j] = st[j];
+      for (int j = 0; j < SPT; ++j) {
+        hs[k][j] = st[j];
+        a2[k][j] = p.A[d * N + n0 + j];
+      }
     }
 #pragma unroll
     for (int j = 0; j < SPT; ++j) {
-      const float a = hw_exp2(dt * (p.A[d * N + n0 + j] * kLog2e));
-      const float bv = load_elem<BF16>(p.B, b * N + n0 + j);
-      const float cv = load_elem<BF16>(p.C, b * N + n0 + j);
-      hs[j] = fmaf(a, hs[j], w * bv);
-      yp = fmaf(cv, hs[j], yp);
+      bv[k][j] = load_elem<BF16>(p.B, b * N + n0 + j);
+      cv[k][j] = load_elem<BF16>(p.C, b * N + n0 + j);
     }
-    if constexpr (SPT == 4) {
-      if (p.state_vec_ok) {
-        *reinterpret_cast<float4*>(st) = make_float4(hs[0], hs[1], hs[2], hs[3]);
-      } else {
+    xv[k] = load_elem<BF16>(p.x, ch);
+    dv[k] = load_elem<BF16>(p.delta, ch);
+    zv[k] = load_elem<BF16>(zsrc, ch);
+    bias[k] = bias_on * bsrc[d];
+    dsk[k] = d_on * dsrc[d];
+  }
+  // 2. arithmetic
+  float yp[Q];
 #pragma unroll
-        for (int j = 0; j < SPT; ++j) st[j] = hs[j];
-      }
-    } else {
+  for (int k = 0; k < Q; ++k) {
+    const float vb = dv[k] + bias[k];
+    const float dt = p.softplus ? softplus_f32(vb) : vb;
+    const float w = dt * xv[k];
+    yp[k] = 0.0f;
 #pragma unroll
-      for (int j = 0; j < SPT; ++j) st[j] = hs[j];
+    for (int j = 0; j < SPT; ++j) {
+      const float a = hw_exp2(dt * (a2[k][j] * kLog2e));
+      hs[k][j] = fmaf(a, hs[k][j], w * bv[k][j]);
+      yp[k] = fmaf(cv[k][j], hs[k][j], yp[k]);
     }
   }
-  // combine the TPC partial read-outs of a channel (its lanes are adjacent in one wave)
+  // 3. stores: the state, then y from the first lane of each channel after the cross-lane sum
 #pragma unroll
-  for (int off = 1; off < TPC; off <<= 1) yp += __shfl_xor(yp, off, 64);
-  if (ok && sub == 0) {
-    const int64_t d = ch % p.dim;
-    float yv = fmaf(p.Dskip ? p.Dskip[d] : 0.0f, xv, yp);
-    if (p.z) yv *= silu_f32(zv);
-    if constexpr (BF16) static_cast<uint16_t*>(p.y)[ch] = to_bf16(yv);
-    else static_cast<float*>(p.y)[ch] = yv;
+  for (int k = 0; k < Q; ++k) {
+    const int64_t q = base + k * kUpdateThreads;
+    const int64_t ch = ok[k] ? q / TPC : 0;
+    const int n0 = static_cast<int>(q % TPC) * SPT;
+    float* st = p.state + ch * N + n0;
+    if (ok[k]) {
+      if constexpr (SPT == 4) {
+        if (p.state_vec_ok) {
+          *reinterpret_cast<float4*>(st) = make_float4(hs[k][0], hs[k][1], hs[k][2], hs[k][3]);
+        } else {
+#pragma unroll
+          for (int j = 0; j < SPT; ++j) st[j] = hs[k][j];
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < SPT; ++j) st[j] = hs[k][j];
+      }
+    }
+    float y = yp[k];
+#pragma unroll
+    for (int off = 1; off < TPC; off <<= 1) y += __shfl_xor(y, off, 64);
+    if (ok[k] && n0 == 0) {
+      float yv = fmaf(dsk[k], xv[k], y);
+      if (p.z) yv *= silu_f32(zv[k]);
+      if constexpr (BF16) static_cast<uint16_t*>(p.y)[ch] = to_bf16(yv);
+      else static_cast<float*>(p.y)[ch] = yv;
+    }
   }
 }
 
