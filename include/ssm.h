@@ -118,12 +118,16 @@ SSM_API ssm_status_t ssm_scan_fwd(int64_t batch, int64_t seqlen, int64_t dim, in
  * and for the invariance tests.
  *   chains_per_lane  state chains (values of n) per GPU lane: 1, 2, 4, 8 or 16,
  *                    dividing dstate;
- *   segments         number of sequence segments scanned in parallel (>= 1).
+ *   segments         number of sequence segments scanned in parallel (>= 1);
+ *   chunk_steps      time steps staged per LDS tile: 16 or 32 (32 needs at most
+ *                    4 scan waves, i.e. dstate / chains_per_lane <= 4).
+ * reserved must be zero.
  */
 typedef struct {
   int32_t chains_per_lane;
   int32_t segments;
-  int32_t reserved[6];
+  int32_t chunk_steps;
+  int32_t reserved[5];
 } ssm_scan_opts_t;
 
 /* ssm_scan_fwd with launch-shape overrides (opts may be NULL). An override

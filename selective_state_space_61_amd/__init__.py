@@ -40,7 +40,7 @@ class SsmError(RuntimeError):
 
 class ScanOpts(ctypes.Structure):
     _fields_ = [("chains_per_lane", ctypes.c_int32), ("segments", ctypes.c_int32),
-                ("reserved", ctypes.c_int32 * 6)]
+                ("chunk_steps", ctypes.c_int32), ("reserved", ctypes.c_int32 * 5)]
 
 
 _lib_handle = None
@@ -115,10 +115,10 @@ def ssm_scan_fwd(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch
                  delta_bias: Optional[torch.Tensor] = None, delta_softplus: bool = False, *,
                  y: Optional[torch.Tensor] = None, last_state: Optional[torch.Tensor] = None,
                  return_last_state: bool = True, chains_per_lane: int = 0, segments: int = 0,
-                 stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+                 chunk_steps: int = 0, stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Selective scan forward (include/ssm.h: ssm_scan_fwd).  Returns (y, last_state); last_state
-    is None when return_last_state is False and none was passed in.  chains_per_lane and
-    segments override the launch shape (0 = automatic)."""
+    is None when return_last_state is False and none was passed in.  chains_per_lane, segments
+    and chunk_steps override the launch shape (0 = automatic)."""
     lib = load_library()
     if x.dim() != 3 or A.dim() != 2:
         raise ValueError("x must be (batch, seqlen, dim) and A (dim, dstate)")
@@ -140,7 +140,7 @@ def ssm_scan_fwd(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch
     if last_state is None and return_last_state:
         last_state = torch.empty((batch, dim, dstate), dtype=torch.float32, device=dev)
     _need(last_state, "last_state", (batch, dim, dstate), torch.float32, dev, optional=True)
-    opts = ScanOpts(int(chains_per_lane), int(segments))
+    opts = ScanOpts(int(chains_per_lane), int(segments), int(chunk_steps))
     status = lib.ssm_scan_fwd_ex(batch, seqlen, dim, dstate, code, _ptr(x), _ptr(delta), _ptr(A), _ptr(B),
                                  _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias), int(bool(delta_softplus)), _ptr(y),
                                  _ptr(last_state), _stream(dev, stream), ctypes.byref(opts))

@@ -9,29 +9,41 @@ import time
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIBRARY = os.path.join(HERE, "libssm61.so")
-SOURCES = [os.path.join(CSRC, "ssm_api.hip")]
-HEADERS = [os.path.join(CSRC, f) for f in ("ssm_device.hpp", "scan_fwd.hpp", "state_update.hpp")] + [
+SOURCES = [os.path.join(CSRC, f) for f in ("ssm_api.hip", "scan_f32.hip", "scan_bf16.hip")]
+HEADERS = [os.path.join(CSRC, f) for f in ("ssm_device.hpp", "scan_fwd.hpp", "scan_table.hpp", "state_update.hpp")] + [
     os.path.join(os.path.dirname(HERE), "include", "ssm.h")]
+OBJDIR = os.path.join(HERE, "_build")
 ARCH = "gfx950"
 
 # -packed-fp32-ops: no v_pk_{add,mul,fma}_f32 anywhere (the host pass warns that it does not know
 # the feature; that is harmless).
-FLAGS = ["-O3", "-std=c++17", "-fPIC", "-shared", "-fvisibility=hidden", "-Wall", "-Wno-unused-function",
+FLAGS = ["-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", "-Wall", "-Wno-unused-function",
          f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+NOISE = "is not a recognized feature for this target"
+
+
+def _run(cmd):
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    err = "\n".join(l for l in (r.stderr or "").splitlines() if NOISE not in l)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({r.returncode}):\n{' '.join(cmd)}\n{err}")
+    return err
 
 
 def build(verbose: bool = False) -> str:
-    """Always recompiles (the caller asked for a build)."""
+    """Always recompiles (the caller asked for a build): one object per source, compiled in
+    parallel, then linked into the shared library."""
+    from concurrent.futures import ThreadPoolExecutor
     t0 = time.time()
-    cmd = ["hipcc", *FLAGS, "-o", LIBRARY + ".tmp", *SOURCES]
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    noise = "is not a recognized feature for this target"
-    err = "\n".join(l for l in (r.stderr or "").splitlines() if noise not in l)
-    if r.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({r.returncode}):\n{' '.join(cmd)}\n{err}")
+    os.makedirs(OBJDIR, exist_ok=True)
+    objs = [os.path.join(OBJDIR, os.path.basename(s) + ".o") for s in SOURCES]
+    with ThreadPoolExecutor(len(SOURCES)) as ex:
+        errs = list(ex.map(lambda so: _run(["hipcc", *FLAGS, "-c", "-o", so[1], so[0]]), zip(SOURCES, objs)))
+    errs.append(_run(["hipcc", "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", LIBRARY + ".tmp", *objs]))
     os.replace(LIBRARY + ".tmp", LIBRARY)
     if verbose:
-        if err.strip():
+        err = "\n".join(e for e in errs if e.strip())
+        if err:
             print(err, file=sys.stderr)
         print(f"built {LIBRARY} in {time.time() - t0:.1f}s")
     return LIBRARY

@@ -63,34 +63,37 @@ struct ScanArgs {
   int32_t vec_ok;    // x / delta / z / y rows allow aligned vector access
 };
 
-constexpr int kChunk = 32;
+constexpr int kChunk = 32;  // segment lengths are multiples of this (and so of every chunk size)
+constexpr int kIoWaves = 4; // waves per workgroup that load, prologue, epilogue and store
 constexpr int kDwPad = 2;   // float2 padding per LDS row of (dt, w)
 constexpr int kYpPad = 4;   // float padding per LDS row of partial read-outs
 
-template <int N, int NPL>
-struct ScanShape {
-  static constexpr int G = N / NPL;           // waves per workgroup
-  static constexpr int NT = 64 * G;           // threads per workgroup
-  static constexpr int EPT = kChunk * 64 / NT;  // tile elements per thread
-};
+// LDS bytes of one workgroup: double-buffered (dt, dt x) tiles, plus (full scan only) the
+// double-buffered partial read-outs of the G scan waves.
+constexpr int scan_lds_bytes(int G, bool full, int ch) {
+  return ch * (2 * (64 + kDwPad) * 8 + (full ? 2 * G * (64 + kYpPad) * 4 : 0));
+}
+constexpr int kLdsBudget = 160 * 1024;
 
-template <bool BF16, int N, int NPL, int MODE>
-__global__ __launch_bounds__(64 * (N / NPL)) void scan_chunk_kernel(const ScanArgs p) {
-  using Shape = ScanShape<N, NPL>;
-  constexpr int G = Shape::G;
-  constexpr int NT = Shape::NT;
-  constexpr int EPT = Shape::EPT;
-  static_assert(EPT >= 1, "chunk too small for this workgroup");
-  constexpr int kMaxVec = BF16 ? 8 : 4;       // 16-byte accesses
+template <bool BF16, int N, int NPL, int MODE, int CH>
+__global__ __launch_bounds__(64 * (N / NPL + kIoWaves)) void scan_chunk_kernel(const ScanArgs p) {
+  constexpr int G = N / NPL;                   // scan waves
+  constexpr bool kFull = (MODE == MODE_FULL);
+  static_assert(CH == 16 || CH == 32, "chunks of 16 or 32 steps");
+  static_assert(scan_lds_bytes(G, kFull, CH) <= kLdsBudget, "LDS tiles exceed a workgroup's share");
+  constexpr int kHalves = CH / 16;
+  constexpr int IOT = 64 * kIoWaves;           // IO threads
+  constexpr int EPT = CH * 64 / IOT;           // tile elements per IO thread
+  constexpr int kMaxVec = BF16 ? 8 : 4;        // 16-byte accesses
   constexpr int VEC = EPT < kMaxVec ? EPT : kMaxVec;
   constexpr int ITEMS = EPT / VEC;
-  constexpr int TPR = 64 / VEC;               // threads per tile row
-  constexpr int RSTEP = NT / TPR;             // tile rows covered per pass
-  static_assert(ITEMS * RSTEP == kChunk, "tile mapping must cover the chunk exactly");
-  constexpr bool kFull = (MODE == MODE_FULL);
+  constexpr int TPR = 64 / VEC;                // IO threads per tile row
+  constexpr int RSTEP = IOT / TPR;             // tile rows covered per pass
+  static_assert(EPT >= 1 && ITEMS * RSTEP == CH, "tile mapping must cover the chunk exactly");
 
-  __shared__ float2 s_dw[kChunk][64 + kDwPad];
-  __shared__ float s_yp[kFull ? G : 1][kChunk][64 + kYpPad];
+  // double buffers: chunk c uses s_dw[c & 1] and s_yp[c & 1]
+  __shared__ float2 s_dw[2][CH][64 + kDwPad];
+  __shared__ float s_yp[kFull ? 2 : 1][kFull ? G : 1][CH][64 + kYpPad];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -104,31 +107,122 @@ __global__ __launch_bounds__(64 * (N / NPL)) void scan_chunk_kernel(const ScanAr
   const int seg = static_cast<int>(rest / p.batch);
   const int64_t t_begin = static_cast<int64_t>(seg) * p.seg_len;
   const int64_t t_end = (t_begin + p.seg_len < p.seqlen) ? (t_begin + p.seg_len) : p.seqlen;
+  const int64_t nchunks = (t_end - t_begin + CH - 1) / CH;
+  const int64_t row_base = b * p.seqlen;  // (b, t) row index = row_base + t
+  const bool vec_ok = p.vec_ok != 0;
+  // whole 64-channel block valid with vector access, and chunk c entirely inside the sequence
+  const bool full_cols = vec_ok && (static_cast<int64_t>(cb) * 64 + 64 <= p.dim);
+  auto chunk_full = [&](int64_t c) { return full_cols && t_begin + (c + 1) * CH <= t_end; };
 
-  // ---- scan-side state: lane = channel, NPL chains -------------------------------------------
-  const int64_t d_lane = static_cast<int64_t>(cb) * 64 + lane;
-  const bool lane_ok = d_lane < p.dim;
-  const int n0 = wave * NPL;
-  float A2[NPL], h[NPL];
+  // Both roles run nchunks + 2 iterations (j = -1 .. nchunks) with one barrier each:
+  //   IO waves:   epilogue of chunk j-1 <- s_yp[(j-1) & 1];  prologue of chunk j+1 -> s_dw[(j+1) & 1]
+  //   scan waves: recurrence of chunk j:  s_dw[j & 1] -> s_yp[j & 1]
+  // Every buffer is written in one iteration, read in the next and rewritten in the one after,
+  // each time across a barrier.
+  if (wave < G) {
+    // ================================ scan role ================================================
+    const int64_t d_lane = static_cast<int64_t>(cb) * 64 + lane;
+    const bool lane_ok = d_lane < p.dim;
+    const int n0 = wave * NPL;
+    float A2[NPL], h[NPL];
 #pragma unroll
-  for (int j = 0; j < NPL; ++j) {
-    // log2(e) * A, clamped to a finite value: a padded step (dt = 0) must give exp2(0) = 1
-    A2[j] = lane_ok ? fmaxf(p.A[d_lane * N + n0 + j] * kLog2e, -3.0e38f) : 0.0f;
-    h[j] = 0.0f;
-  }
-  if (kFull && p.nseg > 1 && lane_ok) {
-    const float* hin = p.seg_state + ((static_cast<int64_t>(seg) * p.batch + b) * p.dim + d_lane) * N + n0;
+    for (int j = 0; j < NPL; ++j) {
+      // log2(e) * A, clamped to a finite value: a padded step (dt = 0) must give exp2(0) = 1
+      A2[j] = lane_ok ? fmaxf(p.A[d_lane * N + n0 + j] * kLog2e, -3.0e38f) : 0.0f;
+      h[j] = 0.0f;
+    }
+    if (kFull && p.nseg > 1 && lane_ok) {
+      const float* hin = p.seg_state + ((static_cast<int64_t>(seg) * p.batch + b) * p.dim + d_lane) * N + n0;
 #pragma unroll
-    for (int j = 0; j < NPL; ++j) h[j] = hin[j];
-  }
-  float dsum = 0.0f;
+      for (int j = 0; j < NPL; ++j) h[j] = hin[j];
+    }
+    float dsum = 0.0f;
 
-  // ---- tile-side mapping: (row, VEC channels) items ------------------------------------------
-  const int col = (tid % TPR) * VEC;
-  const int row0 = tid / TPR;
+    // B / C rows: lane k of each 16-lane row holds step k of each 16-step half of a chunk
+    const int bc_k = lane & 15;
+    BcRow<BF16, NPL> nb[kHalves], nc[kHalves];
+    auto load_bc = [&](int64_t c) {
+#pragma unroll
+      for (int hf = 0; hf < kHalves; ++hf) {
+        const int64_t t = t_begin + c * CH + hf * 16 + bc_k;
+        const int64_t e = (row_base + t) * N + n0;
+        nb[hf].load(p.B, e, t < t_end);
+        if constexpr (kFull) nc[hf].load(p.C, e, t < t_end);
+      }
+    };
+    if (nchunks > 0) load_bc(0);
+
+    for (int64_t j = -1; j <= nchunks; ++j) {
+      if (j >= 0 && j < nchunks) {
+        const int sb = static_cast<int>(j & 1);
+        float Bv[kHalves][NPL], Cv[kHalves][NPL];
+#pragma unroll
+        for (int hf = 0; hf < kHalves; ++hf)
+#pragma unroll
+          for (int jj = 0; jj < NPL; ++jj) {
+            Bv[hf][jj] = nb[hf].get(jj);
+            Cv[hf][jj] = kFull ? nc[hf].get(jj) : 0.0f;
+          }
+        if (j + 1 < nchunks) load_bc(j + 1);
+        // CH steps unrolled; each step t >= 1 is one fused block that also reads out step t-1,
+        // step CH-1 is read out at the end
+        // (dt, w) of the next batch of steps is read from LDS while the current batch computes
+        constexpr int kBatch = 8;
+        float2 dwq[2][kBatch];
+        static_for<kBatch>([&](auto K) { dwq[0][decltype(K)::value] = s_dw[sb][decltype(K)::value][lane]; });
+        static_for<CH / kBatch>([&](auto Q) {
+          constexpr int q = decltype(Q)::value;
+          if constexpr (q + 1 < CH / kBatch)
+            static_for<kBatch>([&](auto K) {
+              dwq[(q + 1) & 1][decltype(K)::value] = s_dw[sb][(q + 1) * kBatch + decltype(K)::value][lane];
+            });
+          float2* dw = dwq[q & 1];
+          static_for<kBatch>([&](auto K) {
+            constexpr int k = decltype(K)::value;
+            constexpr int t = q * kBatch + k;
+            if constexpr (kFull && t > 0) {
+              s_yp[sb][wave][t - 1][lane] =
+                  step_readout<NPL, t % 16, (t - 1) % 16>(dw[k].x, dw[k].y, A2, Bv[t / 16], Cv[(t - 1) / 16], h);
+            } else {
+#pragma unroll
+              for (int jj = 0; jj < NPL; ++jj)
+                h[jj] = fmaf(hw_exp2(dw[k].x * A2[jj]), h[jj], row_bcast<t % 16>(Bv[t / 16][jj]) * dw[k].y);
+              if constexpr (!kFull) dsum += dw[k].x;
+            }
+          });
+        });
+        if constexpr (kFull) {
+          float yp = row_bcast<15>(Cv[kHalves - 1][0]) * h[0];
+#pragma unroll
+          for (int jj = 1; jj < NPL; ++jj) yp = fmaf(row_bcast<15>(Cv[kHalves - 1][jj]), h[jj], yp);
+          s_yp[sb][wave][CH - 1][lane] = yp;
+        }
+      }
+      __syncthreads();
+    }
+
+    if (!lane_ok) return;
+    if constexpr (kFull) {
+      if (p.last_state && seg == p.nseg - 1) {
+        float* dst = p.last_state + (b * p.dim + d_lane) * N + n0;
+#pragma unroll
+        for (int j = 0; j < NPL; ++j) dst[j] = h[j];
+      }
+    } else {
+      float* dst = p.seg_state + ((static_cast<int64_t>(seg) * p.batch + b) * p.dim + d_lane) * N + n0;
+#pragma unroll
+      for (int j = 0; j < NPL; ++j) dst[j] = h[j];
+      if (wave == 0) p.seg_dsum[(static_cast<int64_t>(seg) * p.batch + b) * p.dim + d_lane] = dsum;
+    }
+    return;
+  }
+
+  // ================================== IO role ===================================================
+  const int iot = tid - 64 * G;
+  const int col = (iot % TPR) * VEC;
+  const int row0 = iot / TPR;
   const int64_t d_col = static_cast<int64_t>(cb) * 64 + col;
   const int nvalid_col = d_col >= p.dim ? 0 : static_cast<int>((p.dim - d_col) < VEC ? (p.dim - d_col) : VEC);
-  const bool vec_ok = p.vec_ok != 0;
   float bias[VEC], dsk[VEC];
 #pragma unroll
   for (int v = 0; v < VEC; ++v) {
@@ -136,28 +230,18 @@ __global__ __launch_bounds__(64 * (N / NPL)) void scan_chunk_kernel(const ScanAr
     dsk[v] = (p.Dskip && v < nvalid_col) ? p.Dskip[d_col + v] : 0.0f;
   }
   const bool has_z = kFull && p.z != nullptr;
-  const int64_t row_base = b * p.seqlen;  // (b, t) row index = row_base + t
 
-  RawVec<BF16, VEC> nx[ITEMS], nd[ITEMS], nz[ITEMS];
-  constexpr int kHalves = kChunk / 16;
-  const int bc_k = lane & 15;
-  BcRow<BF16, NPL> nb[kHalves], nc[kHalves];
-  // loads the x / delta / z tile and the B / C rows of the chunk starting at t0 into registers;
-  // `full` (uniform): every row of the chunk exists and the channel block is whole
-  auto load_tile = [&](int64_t t0, bool full) {
-    if (full) {
+  RawVec<BF16, VEC> nx[ITEMS], nd[ITEMS], nz[ITEMS];  // tile of the next chunk to enter the prologue
+  // loads the x / delta / z tile of chunk c into registers
+  auto load_tile = [&](int64_t c) {
+    const int64_t t0 = t_begin + c * CH;
+    if (chunk_full(c)) {
 #pragma unroll
       for (int i = 0; i < ITEMS; ++i) {
         const int64_t idx = (row_base + t0 + row0 + i * RSTEP) * p.dim + d_col;
         nx[i].load(p.x, idx, VEC, true);
         nd[i].load(p.delta, idx, VEC, true);
         if (has_z) nz[i].load(p.z, idx, VEC, true);
-      }
-#pragma unroll
-      for (int hf = 0; hf < kHalves; ++hf) {
-        const int64_t e = (row_base + t0 + hf * 16 + bc_k) * N + n0;
-        nb[hf].load(p.B, e, true);
-        if constexpr (kFull) nc[hf].load(p.C, e, true);
       }
       return;
     }
@@ -170,153 +254,104 @@ __global__ __launch_bounds__(64 * (N / NPL)) void scan_chunk_kernel(const ScanAr
       nd[i].load(p.delta, idx, nv, vec_ok);
       if (has_z) nz[i].load(p.z, idx, nv, vec_ok);
     }
-#pragma unroll
-    for (int hf = 0; hf < kHalves; ++hf) {
-      const int64_t t = t0 + hf * 16 + bc_k;
-      const int64_t e = (row_base + t) * N + n0;
-      nb[hf].load(p.B, e, t < t_end);
-      if constexpr (kFull) nc[hf].load(p.C, e, t < t_end);
-    }
   };
+  if (nchunks > 0) load_tile(0);
 
-  // whole 64-channel block valid with vector access: chunks away from the sequence end need no
-  // per-element masking
-  const bool full_cols = vec_ok && (static_cast<int64_t>(cb) * 64 + 64 <= p.dim);
-  if (t_begin < t_end) load_tile(t_begin, full_cols && t_begin + kChunk <= t_end);
-
-  for (int64_t t0 = t_begin; t0 < t_end; t0 += kChunk) {
-    const bool full = full_cols && (t0 + kChunk <= t_end);
-
-    // 1. prologue of this chunk: (dt, dt * x) into LDS; keep x and z for the epilogue
-    RawVec<BF16, VEC> cx[ITEMS], cz[ITEMS];
-    float dts[ITEMS][VEC], xs[ITEMS][VEC];
+  // x and z of the chunks between prologue and epilogue: at the top of iteration j, [0] holds
+  // chunk j (prologued in iteration j-1) and [1] chunk j-1 (its epilogue runs now)
+  RawVec<BF16, VEC> ex[2][ITEMS], ez[2][ITEMS];
+  for (int64_t j = -1; j <= nchunks; ++j) {
+    // ---- epilogue of chunk j-1: y = sum of partials + D x, gated, stored with vector stores ----
+    if constexpr (kFull) {
+      const int64_t e = j - 1;
+      if (e >= 0) {
+        const int eb = static_cast<int>(e & 1);
+        const int64_t t0 = t_begin + e * CH;
+        float out[ITEMS][VEC];
 #pragma unroll
-    for (int i = 0; i < ITEMS; ++i)
+        for (int i = 0; i < ITEMS; ++i) {
+          const int row = row0 + i * RSTEP;
 #pragma unroll
-      for (int v = 0; v < VEC; ++v) {
-        dts[i][v] = nd[i].get(v) + bias[v];
-        xs[i][v] = nx[i].get(v);
+          for (int v = 0; v < VEC; ++v) {
+            float acc = s_yp[eb][0][row][col + v];
+#pragma unroll
+            for (int g = 1; g < G; ++g) acc += s_yp[eb][g][row][col + v];
+            out[i][v] = fmaf(dsk[v], ex[1][i].get(v), acc);
+          }
+        }
+        if (has_z) {
+#pragma unroll
+          for (int i = 0; i < ITEMS; ++i)
+#pragma unroll
+            for (int v = 0; v < VEC; ++v) out[i][v] *= silu_f32(ez[1][i].get(v));
+        }
+        const bool full = chunk_full(e);
+#pragma unroll
+        for (int i = 0; i < ITEMS; ++i) {
+          const int64_t t = t0 + row0 + i * RSTEP;
+          const int64_t idx = (row_base + t) * p.dim + d_col;
+          if (full) {
+            store_vec<BF16, VEC>(p.y, idx, out[i], VEC, true);
+          } else {
+            const int nv = (t < t_end) ? nvalid_col : 0;
+            if (nv > 0) store_vec<BF16, VEC>(p.y, idx, out[i], nv, vec_ok);
+          }
+        }
       }
-    if (p.softplus) {
+    }
+    // ---- prologue of chunk j+1 ----------------------------------------------------------------
+    const int64_t c = j + 1;
+    if (c < nchunks) {
+      const int pb = static_cast<int>(c & 1);
+      const int64_t t0 = t_begin + c * CH;
+      float dts[ITEMS][VEC], xs[ITEMS][VEC];
 #pragma unroll
       for (int i = 0; i < ITEMS; ++i)
 #pragma unroll
-        for (int v = 0; v < VEC; ++v) dts[i][v] = softplus_f32(dts[i][v]);
-    }
-    if (!full) {  // rows past the end and channels past dim become identity steps
-#pragma unroll
-      for (int i = 0; i < ITEMS; ++i) {
-        const bool row_ok = (t0 + row0 + i * RSTEP) < t_end;
-#pragma unroll
         for (int v = 0; v < VEC; ++v) {
-          const bool ok = row_ok && (v < nvalid_col);
-          dts[i][v] = ok ? dts[i][v] : 0.0f;
-          xs[i][v] = ok ? xs[i][v] : 0.0f;
+          dts[i][v] = nd[i].get(v) + bias[v];
+          xs[i][v] = nx[i].get(v);
+        }
+      if (p.softplus) {
+#pragma unroll
+        for (int i = 0; i < ITEMS; ++i)
+#pragma unroll
+          for (int v = 0; v < VEC; ++v) dts[i][v] = softplus_f32(dts[i][v]);
+      }
+      if (!chunk_full(c)) {  // rows past the end and channels past dim become identity steps
+#pragma unroll
+        for (int i = 0; i < ITEMS; ++i) {
+          const bool row_ok = (t0 + row0 + i * RSTEP) < t_end;
+#pragma unroll
+          for (int v = 0; v < VEC; ++v) {
+            const bool ok = row_ok && (v < nvalid_col);
+            dts[i][v] = ok ? dts[i][v] : 0.0f;
+            xs[i][v] = ok ? xs[i][v] : 0.0f;
+          }
         }
       }
-    }
-#pragma unroll
-    for (int i = 0; i < ITEMS; ++i) {
-      const int row = row0 + i * RSTEP;
-#pragma unroll
-      for (int v = 0; v < VEC; ++v) s_dw[row][col + v] = make_float2(dts[i][v], dts[i][v] * xs[i][v]);
-      cx[i] = nx[i];
-      if (has_z) cz[i] = nz[i];
-    }
-    float Bv[kHalves][NPL], Cv[kHalves][NPL];
-#pragma unroll
-    for (int hf = 0; hf < kHalves; ++hf)
-#pragma unroll
-      for (int j = 0; j < NPL; ++j) {
-        Bv[hf][j] = nb[hf].get(j);
-        Cv[hf][j] = kFull ? nc[hf].get(j) : 0.0f;
-      }
-    // 2. prefetch the next chunk's tile into registers
-    if (t0 + kChunk < t_end) load_tile(t0 + kChunk, full_cols && t0 + 2 * kChunk <= t_end);
-    __syncthreads();
-
-    // 3. the recurrence over this chunk: NPL chains per lane, all kChunk steps unrolled, the
-    //    (dt, w) pairs of kBatch steps read from LDS ahead of their use.  In FULL mode each step
-    //    t >= 1 is one fused block that also reads out step t - 1; step 31 is read out after the
-    //    loop.
-    constexpr int kBatch = 8;
-    static_for<kChunk / kBatch>([&](auto Q) {
-      constexpr int q = decltype(Q)::value;
-      float2 dw[kBatch];
-      static_for<kBatch>([&](auto K) { dw[decltype(K)::value] = s_dw[q * kBatch + decltype(K)::value][lane]; });
-      static_for<kBatch>([&](auto K) {
-        constexpr int k = decltype(K)::value;
-        constexpr int t = q * kBatch + k;
-        if constexpr (kFull && t > 0) {
-          s_yp[wave][t - 1][lane] =
-              step_readout<NPL, t % 16, (t - 1) % 16>(dw[k].x, dw[k].y, A2, Bv[t / 16], Cv[(t - 1) / 16], h);
-        } else {
-#pragma unroll
-          for (int j = 0; j < NPL; ++j)
-            h[j] = fmaf(hw_exp2(dw[k].x * A2[j]), h[j], row_bcast<t % 16>(Bv[t / 16][j]) * dw[k].y);
-          if constexpr (!kFull) dsum += dw[k].x;
-        }
-      });
-    });
-    if constexpr (kFull) {
-      float yp = row_bcast<15>(Cv[kHalves - 1][0]) * h[0];
-#pragma unroll
-      for (int j = 1; j < NPL; ++j) yp = fmaf(row_bcast<15>(Cv[kHalves - 1][j]), h[j], yp);
-      s_yp[wave][kChunk - 1][lane] = yp;
-    }
-
-    // 4. one barrier: every wave is done with s_dw (the next prologue may overwrite it) and
-    //    s_yp is complete.  The next chunk's first barrier orders this epilogue's
-    //    reads of s_yp before the next scan's writes.
-    __syncthreads();
-
-    // 5. epilogue: y = sum of partials + D x, gated, stored with vector stores
-    if constexpr (kFull) {
-      float out[ITEMS][VEC];
 #pragma unroll
       for (int i = 0; i < ITEMS; ++i) {
         const int row = row0 + i * RSTEP;
 #pragma unroll
-        for (int v = 0; v < VEC; ++v) {
-          float acc = s_yp[0][row][col + v];
-#pragma unroll
-          for (int g = 1; g < G; ++g) acc += s_yp[g][row][col + v];
-          out[i][v] = fmaf(dsk[v], cx[i].get(v), acc);
+        for (int v = 0; v < VEC; ++v) s_dw[pb][row][col + v] = make_float2(dts[i][v], dts[i][v] * xs[i][v]);
+        ex[1][i] = ex[0][i];
+        ex[0][i] = nx[i];
+        if (has_z) {
+          ez[1][i] = ez[0][i];
+          ez[0][i] = nz[i];
         }
       }
-      if (has_z) {
-#pragma unroll
-        for (int i = 0; i < ITEMS; ++i)
-#pragma unroll
-          for (int v = 0; v < VEC; ++v) out[i][v] *= silu_f32(cz[i].get(v));
-      }
+      if (c + 1 < nchunks) load_tile(c + 1);
+    } else {
 #pragma unroll
       for (int i = 0; i < ITEMS; ++i) {
-        const int64_t t = t0 + row0 + i * RSTEP;
-        const int64_t idx = (row_base + t) * p.dim + d_col;
-        if (full) {
-          store_vec<BF16, VEC>(p.y, idx, out[i], VEC, true);
-        } else {
-          const int nv = (t < t_end) ? nvalid_col : 0;
-          if (nv > 0) store_vec<BF16, VEC>(p.y, idx, out[i], nv, vec_ok);
-        }
+        ex[1][i] = ex[0][i];
+        if (has_z) ez[1][i] = ez[0][i];
       }
     }
-  }
 
-  // ---- results --------------------------------------------------------------------------------
-  if (!lane_ok) return;
-  if constexpr (kFull) {
-    if (p.last_state && seg == p.nseg - 1) {
-      float* dst = p.last_state + (b * p.dim + d_lane) * N + n0;
-#pragma unroll
-      for (int j = 0; j < NPL; ++j) dst[j] = h[j];
-    }
-  } else {
-    float* dst = p.seg_state + ((static_cast<int64_t>(seg) * p.batch + b) * p.dim + d_lane) * N + n0;
-#pragma unroll
-    for (int j = 0; j < NPL; ++j) dst[j] = h[j];
-    if (wave == 0) p.seg_dsum[(static_cast<int64_t>(seg) * p.batch + b) * p.dim + d_lane] = dsum;
+    __syncthreads();
   }
 }
 

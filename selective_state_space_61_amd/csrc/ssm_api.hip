@@ -10,7 +10,7 @@
 #include <utility>
 
 #include "../../include/ssm.h"
-#include "scan_fwd.hpp"
+#include "scan_table.hpp"
 #include "state_update.hpp"
 
 namespace {
@@ -57,64 +57,39 @@ bool dstate_supported(int64_t n) {
   return n == 1 || n == 2 || n == 4 || n == 8 || n == 16 || n == 32 || n == 64;
 }
 
-// chains per lane the scan kernels are instantiated for, given N: at most 16 waves per
-// workgroup, and N = 64 needs at least 8 chains per lane (16 waves would not fit the LDS)
+// chains per lane the scan kernels are instantiated for, given N: at most 8 scan waves per
+// workgroup (next to the IO waves, within 1024 threads)
 bool npl_supported(int64_t n, int npl) {
   if (npl != 1 && npl != 2 && npl != 4 && npl != 8 && npl != 16) return false;
   if (npl > n || (n % npl) != 0) return false;
-  if (n == 64 && npl < 8) return false;
-  return n / npl <= 16;
+  return n / npl <= 8;
 }
 
-// Measured on MI355X (dstate 16): with fewer workgroups than CUs, 2 chains per lane (8 waves
-// per workgroup) hides latency best; with more, 4 chains per lane (4 waves) does less work.
+// Measured on MI355X (dstate 16): 4 chains per lane (4 scan waves next to the 4 IO waves) is
+// fastest for both the 130M- and 2.8B-shaped workloads.
 int default_npl(int64_t n, int64_t workgroups) {
-  if (n >= 64) return 8;
-  if (n >= 4 && workgroups >= 256) return 4;
-  if (n >= 2) return 2;
-  return 1;
+  (void)workgroups;
+  int npl = n >= 4 ? 4 : static_cast<int>(n);
+  while (n / npl > 8) npl *= 2;  // at most 8 scan waves per workgroup
+  return npl;
+}
+
+// compute units of the current device, cached per device
+int device_cus() {
+  static int cache[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int cus = __atomic_load_n(&cache[dev], __ATOMIC_RELAXED);
+  if (cus == 0) {
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+    __atomic_store_n(&cache[dev], cus, __ATOMIC_RELAXED);
+  }
+  return cus;
 }
 
 // ---- kernel tables -----------------------------------------------------------------------------
-using ScanKernel = void (*)(const ssm::ScanArgs);
 using CarryKernel = void (*)(const ssm::ScanArgs);
 using UpdateKernel = void (*)(const ssm::UpdateArgs);
-
-template <bool BF16, int N, int NPL>
-void register_scan(std::map<std::pair<int, int>, std::pair<ScanKernel, ScanKernel>>& m) {
-  m[{N, NPL}] = {ssm::scan_chunk_kernel<BF16, N, NPL, ssm::MODE_FULL>,
-                 ssm::scan_chunk_kernel<BF16, N, NPL, ssm::MODE_AGG>};
-}
-
-template <bool BF16>
-const std::map<std::pair<int, int>, std::pair<ScanKernel, ScanKernel>>& scan_table() {
-  static const auto table = [] {
-    std::map<std::pair<int, int>, std::pair<ScanKernel, ScanKernel>> m;
-    register_scan<BF16, 1, 1>(m);
-    register_scan<BF16, 2, 1>(m);
-    register_scan<BF16, 2, 2>(m);
-    register_scan<BF16, 4, 1>(m);
-    register_scan<BF16, 4, 2>(m);
-    register_scan<BF16, 4, 4>(m);
-    register_scan<BF16, 8, 1>(m);
-    register_scan<BF16, 8, 2>(m);
-    register_scan<BF16, 8, 4>(m);
-    register_scan<BF16, 8, 8>(m);
-    register_scan<BF16, 16, 1>(m);
-    register_scan<BF16, 16, 2>(m);
-    register_scan<BF16, 16, 4>(m);
-    register_scan<BF16, 16, 8>(m);
-    register_scan<BF16, 16, 16>(m);
-    register_scan<BF16, 32, 2>(m);
-    register_scan<BF16, 32, 4>(m);
-    register_scan<BF16, 32, 8>(m);
-    register_scan<BF16, 32, 16>(m);
-    register_scan<BF16, 64, 8>(m);
-    register_scan<BF16, 64, 16>(m);
-    return m;
-  }();
-  return table;
-}
 
 CarryKernel carry_kernel(int64_t n) {
   switch (n) {
@@ -257,6 +232,12 @@ ssm_status_t ssm_scan_fwd_ex(int64_t batch, int64_t seqlen, int64_t dim, int64_t
   // launch shape
   const int64_t ncb = (dim + 63) / 64;
   const int64_t base_wgs = ncb * batch;
+  if (opts) {
+    if (opts->segments < 0 || opts->chains_per_lane < 0)
+      return fail(SSM_ERR_INVALID_ARG, "negative launch-shape override");
+    for (int32_t r : opts->reserved)
+      if (r != 0) return fail(SSM_ERR_INVALID_ARG, "ssm_scan_opts_t.reserved must be zero");
+  }
   const bool split_auto = !(opts && opts->segments > 0) && base_wgs < 160;
   int npl = default_npl(dstate, split_auto ? 1024 : base_wgs);
   if (opts && opts->chains_per_lane) {
@@ -288,9 +269,30 @@ ssm_status_t ssm_scan_fwd_ex(int64_t batch, int64_t seqlen, int64_t dim, int64_t
                 (long long)nseg);
 
   const bool bf16 = dtype == SSM_BF16;
-  const auto& table = bf16 ? scan_table<true>() : scan_table<false>();
+  const ssm::ScanTable& table = bf16 ? ssm::scan_table_bf16() : ssm::scan_table_f32();
   const auto it = table.find({static_cast<int>(dstate), npl});
   if (it == table.end()) return fail(SSM_ERR_UNSUPPORTED, "no kernel for dstate %lld chains %d", (long long)dstate, npl);
+  // Chunk length: 32-step tiles halve the barriers per step but take twice the LDS, which with
+  // 4 scan waves leaves room for one workgroup per CU; measured on MI355X they win while the
+  // grid fits in one workgroup per CU, and 16-step tiles (several workgroups per CU) win beyond.
+  const int chunk_opt = opts ? opts->chunk_steps : 0;
+  if (chunk_opt != 0 && chunk_opt != 16 && chunk_opt != 32)
+    return fail(SSM_ERR_UNSUPPORTED, "chunk_steps %d is not 16 or 32", chunk_opt);
+  ssm::ScanKernel k_full, k_agg;
+  if (chunk_opt == 32) {
+    k_full = it->second.full[1];
+    k_agg = it->second.agg[1];
+    if (!k_full || !k_agg)
+      return fail(SSM_ERR_UNSUPPORTED, "chunk_steps 32 not available for dstate %lld chains %d", (long long)dstate,
+                  npl);
+  } else if (chunk_opt == 16) {
+    k_full = it->second.full[0];
+    k_agg = it->second.agg[0];
+  } else {
+    const bool one_round = grid <= device_cus();
+    k_full = (one_round && it->second.full[1]) ? it->second.full[1] : it->second.full[0];
+    k_agg = it->second.agg[0];
+  }
 
   ssm::ScanArgs a{};
   a.x = x; a.delta = delta; a.A = A; a.B = B; a.C = C; a.Dskip = D; a.z = z; a.delta_bias = delta_bias;
@@ -302,7 +304,7 @@ ssm_status_t ssm_scan_fwd_ex(int64_t batch, int64_t seqlen, int64_t dim, int64_t
   const int64_t vmax = 16 / es;
   a.vec_ok = (dim % vmax == 0) && aligned(x, 16) && aligned(delta, 16) && aligned(y, 16) && (!z || aligned(z, 16));
 
-  const unsigned threads = static_cast<unsigned>(64 * G);
+  const unsigned threads = static_cast<unsigned>(64 * (G + ssm::kIoWaves));
   if (nseg > 1) {
     float* scratch = nullptr;
     const int64_t floats = nseg * nch * (dstate + 1);
@@ -310,13 +312,13 @@ ssm_status_t ssm_scan_fwd_ex(int64_t batch, int64_t seqlen, int64_t dim, int64_t
     if (s != SSM_OK) return s;
     a.seg_state = scratch;
     a.seg_dsum = scratch + nseg * nch * dstate;
-    hipLaunchKernelGGL(it->second.second, dim3(static_cast<unsigned>(base_wgs * (nseg - 1))), dim3(threads), 0, st, a);
+    hipLaunchKernelGGL(k_agg, dim3(static_cast<unsigned>(base_wgs * (nseg - 1))), dim3(threads), 0, st, a);
     if ((s = check_launch("scan aggregate")) != SSM_OK) return s;
     const int64_t per_seg = nch * dstate;
     hipLaunchKernelGGL(carry_kernel(dstate), dim3(static_cast<unsigned>((per_seg + 255) / 256)), dim3(256), 0, st, a);
     if ((s = check_launch("scan carry")) != SSM_OK) return s;
   }
-  hipLaunchKernelGGL(it->second.first, dim3(static_cast<unsigned>(grid)), dim3(threads), 0, st, a);
+  hipLaunchKernelGGL(k_full, dim3(static_cast<unsigned>(grid)), dim3(threads), 0, st, a);
   return check_launch("scan");
 }
 

@@ -126,9 +126,15 @@ def test_scan_output_overlap(lib, a, b):
 def test_scan_opts_validation(lib):
     assert scan(lib, dstate=16, opts=ssm.ScanOpts(3, 0)) == UNSUPPORTED
     assert scan(lib, dstate=4, opts=ssm.ScanOpts(8, 0)) == UNSUPPORTED     # more chains than states
-    assert scan(lib, dstate=64, opts=ssm.ScanOpts(2, 0)) == UNSUPPORTED    # would need 32 waves
-    assert scan(lib, dstate=64, opts=ssm.ScanOpts(4, 0)) == UNSUPPORTED    # 16 waves: LDS too small
+    assert scan(lib, dstate=64, opts=ssm.ScanOpts(4, 0)) == UNSUPPORTED    # 16 scan waves: too many
+    assert scan(lib, dstate=16, opts=ssm.ScanOpts(1, 0)) == UNSUPPORTED    # 16 scan waves: too many
     assert "chains_per_lane" in err(lib)
+    assert scan(lib, dstate=16, opts=ssm.ScanOpts(4, 0, 24)) == UNSUPPORTED and "chunk_steps" in err(lib)
+    assert scan(lib, dstate=16, opts=ssm.ScanOpts(2, 0, 32)) == UNSUPPORTED  # 8 scan waves: 32-step tiles too big
+    assert scan(lib, dstate=16, opts=ssm.ScanOpts(0, -1, 0)) == INVALID
+    bad = ssm.ScanOpts(0, 0, 0)
+    bad.reserved[2] = 1
+    assert scan(lib, dstate=16, opts=bad) == INVALID and "reserved" in err(lib)
 
 
 def test_scan_size_overflow(lib):

@@ -69,14 +69,27 @@ def test_tiles_and_ragged_tails(o, dtype, shape):
 
 
 CHAIN_CASES = [(n, c) for n in (1, 2, 4, 8, 16, 32, 64) for c in (1, 2, 4, 8, 16) if c <= n and n % c == 0
-               and n // c <= 16 and not (n == 64 and c < 8)]
+               and n // c <= 8]
 
 
 @pytest.mark.parametrize("N,chains", CHAIN_CASES)
 def test_dstate_and_chains_per_lane(o, N, chains):
     dtype = "bf16" if (N + chains) % 2 else "f32"
     t = W.scan_inputs(2, 70, 96, N, dtype, seed=N * 31 + chains)
-    run_and_compare(o, t, dtype, True, f"N={N} chains={chains} {dtype}", chains_per_lane=chains)
+    for chunk in ((16, 32) if N // chains <= 4 else (16,)):
+        run_and_compare(o, t, dtype, True, f"N={N} chains={chains} chunk={chunk} {dtype}", chains_per_lane=chains,
+                        chunk_steps=chunk)
+
+
+@pytest.mark.parametrize("chunk", [16, 32])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("shape,segments", [((3, 100, 200, 16), 1), ((2, 47, 136, 16), 1), ((1, 1000, 72, 16), 5),
+                                            ((2, 333, 64, 8), 3)])
+def test_chunk_lengths(o, chunk, dtype, shape, segments):
+    batch, L, dim, N = shape
+    t = W.scan_inputs(batch, L, dim, N, dtype, seed=L + chunk)
+    run_and_compare(o, t, dtype, True, f"chunk={chunk} {shape} segments={segments} {dtype}", chunk_steps=chunk,
+                    segments=segments)
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
