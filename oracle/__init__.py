@@ -81,6 +81,10 @@ class Oracle:
         lib.oracle_widen.argtypes = [vp, i32, i64]
         lib.oracle_widen.restype = dp
         lib.oracle_max_threads.restype = i32
+        lib.oracle_causal_conv1d.argtypes = [i64, i64, i64, i64, i32, vp, vp, vp, vp, i32, vp, vp]
+        lib.oracle_causal_conv1d.restype = i32
+        lib.oracle_conv1d_update.argtypes = [i64, i64, i64, i32, vp, vp, vp, vp, i32, vp]
+        lib.oracle_conv1d_update.restype = i32
         self._lib = lib
 
     # -- scalar helpers -------------------------------------------------------------------------
@@ -170,6 +174,49 @@ class Oracle:
                                            int(bool(delta_softplus)), _ptr(y))
         if rc != 0:
             raise ValueError("oracle_state_update rejected its arguments")
+        return y, st
+
+
+    # -- the causal convolution before the scan ------------------------------------------------
+    def causal_conv1d(self, x, weight, bias=None, init_state=None, silu=True) -> Tuple[np.ndarray, np.ndarray]:
+        """Depthwise causal convolution.  x: (batch, L, dim) (float32 / float64 / bf16 bits);
+        weight: (dim, K) fp32; bias: (dim,) fp32; init_state: (batch, dim, K-1) in x's storage
+        type.  Returns y (batch, L, dim) and final_state (batch, dim, K-1), both float64."""
+        x, init_state = _c(x), _c(init_state)
+        code = _dtype_code(x)
+        if init_state is not None and _dtype_code(init_state) != code:
+            raise TypeError("init_state must share x's storage type")
+        weight = _c(weight, np.float32)
+        bias = _c(bias, np.float32)
+        batch, L, dim = x.shape
+        K = weight.shape[1]
+        assert weight.shape == (dim, K)
+        assert bias is None or bias.shape == (dim,)
+        assert init_state is None or init_state.shape == (batch, dim, K - 1)
+        y = np.empty((batch, L, dim), np.float64)
+        fin = np.empty((batch, dim, K - 1), np.float64)
+        rc = self._lib.oracle_causal_conv1d(batch, L, dim, K, code, _ptr(x), _ptr(weight), _ptr(bias),
+                                            _ptr(init_state), int(bool(silu)), _ptr(y), _ptr(fin))
+        if rc != 0:
+            raise ValueError("oracle_causal_conv1d rejected its arguments")
+        return y, fin
+
+    def conv1d_update(self, state, x, weight, bias=None, silu=True) -> Tuple[np.ndarray, np.ndarray]:
+        """One decode step of the convolution.  state: (batch, dim, K-1) (not modified; a float64
+        copy is updated and returned); x: (batch, dim).  Returns (y, new_state)."""
+        x = _c(x)
+        code = _dtype_code(x)
+        weight = _c(weight, np.float32)
+        bias = _c(bias, np.float32)
+        st = np.array(state, np.float64, copy=True, order="C")
+        batch, dim = x.shape
+        K = weight.shape[1]
+        assert st.shape == (batch, dim, K - 1) and weight.shape == (dim, K)
+        y = np.empty((batch, dim), np.float64)
+        rc = self._lib.oracle_conv1d_update(batch, dim, K, code, _ptr(st), _ptr(x), _ptr(weight), _ptr(bias),
+                                            int(bool(silu)), _ptr(y))
+        if rc != 0:
+            raise ValueError("oracle_conv1d_update rejected its arguments")
         return y, st
 
 

@@ -34,6 +34,10 @@
  *
  * Inputs are read in their storage type (fp32, or bf16 bit patterns) and
  * widened exactly to double; A, D and delta_bias are fp32.
+ *
+ * The file also holds the depthwise causal convolution that precedes the scan
+ * in the Mamba block, and its one-token form (oracle_causal_conv1d,
+ * oracle_conv1d_update, below).
  */
 #include <math.h>
 #include <stddef.h>
@@ -173,6 +177,86 @@ int oracle_state_update(int64_t batch, int64_t dim, int64_t dstate, int dtype, d
       double yt = acc + (Dskip ? (double)Dskip[d] * xt : 0.0);
       if (z) yt *= silu(load_elem(z, dtype, i_bd));
       y[i_bd] = yt;
+    }
+  }
+  return 0;
+}
+
+/* ---------------------------------------------------------------------------
+ * Depthwise causal convolution that feeds the scan in the Mamba block
+ * ("Mamba 论文精读" (youngju.dev), sec. 3.4 "Mamba Block 架构", the MambaBlock
+ * listing): a Conv1d with one group per channel, kernel width K and K-1
+ * zeros of padding, cut back to the first L outputs, then SiLU.  PyTorch's
+ * Conv1d is a cross-correlation, so for channel d of batch row b:
+ *
+ *   y[t]  = bias[d] + sum_{k=0..K-1} w[d,k] * xin[t - (K-1) + k]
+ *   xin[s] = x[b,s,d] for s >= 0; for -(K-1) <= s < 0 it is the initial
+ *            state init[b,d,(K-1)+s] (zero without one: the padding)
+ *   out[b,t,d]   = silu ? silu(y[t]) : y[t]
+ *   final[b,d,j] = xin[L-(K-1)+j], j = 0..K-2  (the last K-1 inputs, oldest first)
+ *
+ * x, out: (batch, L, dim); w: (dim, K) fp32; bias: (dim) fp32 or NULL;
+ * init, final: (batch, dim, K-1) (init in the storage type of x, or NULL;
+ * final as doubles, or NULL).  The state layout is a reading: the pages
+ * define no convolution state.
+ * ------------------------------------------------------------------------- */
+int oracle_causal_conv1d(int64_t batch, int64_t seqlen, int64_t dim, int64_t width, int dtype, const void *x,
+                         const float *w, const float *bias, const void *init, int apply_silu, double *out,
+                         double *final_state) {
+  if (batch < 0 || seqlen < 0 || dim < 0 || width < 1 || width > 64) return -1;
+  if (!x || !w || !out) return -1;
+  const int64_t K = width;
+  for (int64_t b = 0; b < batch; ++b) {
+    for (int64_t d = 0; d < dim; ++d) {
+      /* xin[s] for s in [-(K-1), L) */
+      for (int64_t t = 0; t < seqlen; ++t) {
+        double acc = bias ? (double)bias[d] : 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+          const int64_t s = t - (K - 1) + k;
+          double v;
+          if (s >= 0)
+            v = load_elem(x, dtype, (b * seqlen + s) * dim + d);
+          else
+            v = init ? load_elem(init, dtype, (b * dim + d) * (K - 1) + (K - 1) + s) : 0.0;
+          acc += (double)w[d * K + k] * v;
+        }
+        out[(b * seqlen + t) * dim + d] = apply_silu ? silu(acc) : acc;
+      }
+      if (final_state) {
+        for (int64_t j = 0; j < K - 1; ++j) {
+          const int64_t s = seqlen - (K - 1) + j;
+          double v;
+          if (s >= 0)
+            v = load_elem(x, dtype, (b * seqlen + s) * dim + d);
+          else
+            v = init ? load_elem(init, dtype, (b * dim + d) * (K - 1) + (K - 1) + s) : 0.0;
+          final_state[(b * dim + d) * (K - 1) + j] = v;
+        }
+      }
+    }
+  }
+  return 0;
+}
+
+/* One decode step of the same convolution: the window is the K-1 stored
+ * inputs (oldest first) followed by the new input x[b,d]; then the state
+ * drops its oldest input and appends x.  state: (batch, dim, K-1) doubles,
+ * updated in place; x, out: (batch, dim). */
+int oracle_conv1d_update(int64_t batch, int64_t dim, int64_t width, int dtype, double *state, const void *x,
+                         const float *w, const float *bias, int apply_silu, double *out) {
+  if (batch < 0 || dim < 0 || width < 1 || width > 64) return -1;
+  if (!state || !x || !w || !out) return -1;
+  const int64_t K = width;
+  for (int64_t b = 0; b < batch; ++b) {
+    for (int64_t d = 0; d < dim; ++d) {
+      double *st = state + (b * dim + d) * (K - 1);
+      const double xt = load_elem(x, dtype, b * dim + d);
+      double acc = bias ? (double)bias[d] : 0.0;
+      for (int64_t k = 0; k < K - 1; ++k) acc += (double)w[d * K + k] * st[k];
+      acc += (double)w[d * K + K - 1] * xt;
+      for (int64_t k = 0; k + 1 < K - 1; ++k) st[k] = st[k + 1];
+      if (K > 1) st[K - 2] = xt;
+      out[b * dim + d] = apply_silu ? silu(acc) : acc;
     }
   }
   return 0;

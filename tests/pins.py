@@ -352,7 +352,96 @@ def pin_channel_selection(o):
         assert np.array_equal(yc[k], y[sb[k], :, sd[k]]) and np.array_equal(sc[k], st[sb[k], sd[k]])
 
 
+# ----------------------------------------------------------------------------------------------
+# the depthwise causal convolution before the scan ("Mamba 论文精读" sec. 3.4, MambaBlock listing:
+# Conv1d with groups = channels, padding K-1, first L outputs kept, then SiLU)
+# ----------------------------------------------------------------------------------------------
+def _conv_case(seed, batch=2, L=11, dim=5, K=4):
+    g = np.random.default_rng(seed)
+    return (g.normal(size=(batch, L, dim)), g.normal(size=(dim, K)).astype(np.float32),
+            g.normal(size=dim).astype(np.float32))
+
+
+def pin_conv_library_convolution(o):
+    """Without SiLU and initial state, each channel is numpy.convolve of the input with the
+    reversed kernel (Conv1d is a cross-correlation), cut to the first L outputs, plus the bias."""
+    for K in (1, 2, 3, 4):
+        x, w, bias = _conv_case(100 + K, K=K)
+        y, _ = o.causal_conv1d(x, w, bias, silu=False)
+        for b in range(x.shape[0]):
+            for d in range(x.shape[2]):
+                ref = np.convolve(x[b, :, d], w[d, ::-1].astype(np.float64))[: x.shape[1]] + float(bias[d])
+                _close(y[b, :, d], ref, 1e-13, f"conv K={K} b={b} d={d}")
+
+
+def pin_conv_impulse(o):
+    """A unit impulse at t0 gives y[t0 + j] = bias + w[K-1-j] for j < K and bias elsewhere."""
+    K, L, t0 = 4, 12, 5
+    x = np.zeros((1, L, 2))
+    x[0, t0, 1] = 1.0
+    w = np.array([[1.0, 2.0, 3.0, 4.0], [0.5, -1.5, 2.5, -3.5]], np.float32)
+    bias = np.array([0.0, 0.25], np.float32)
+    y, fin = o.causal_conv1d(x, w, bias, silu=False)
+    ref = np.full(L, 0.25)
+    for j in range(K):
+        ref[t0 + j] += float(w[1, K - 1 - j])
+    _close(y[0, :, 1], ref, 0.0, "impulse response")
+    _close(y[0, :, 0], np.zeros(L), 0.0, "silent channel")
+    _close(fin[0, 1], x[0, L - 3:, 1], 0.0, "final state = last K-1 inputs")
+
+
+def pin_conv_silu(o):
+    """SiLU on the output is y * sigmoid(y) of the output without it (scipy.special.expit)."""
+    x, w, bias = _conv_case(7)
+    y0, _ = o.causal_conv1d(x, w, bias, silu=False)
+    y1, _ = o.causal_conv1d(x, w, bias, silu=True)
+    _close(y1, y0 * expit(y0), 1e-13, "silu(conv)")
+
+
+def pin_conv_chaining(o):
+    """Splitting the sequence and passing the final state of the first part as the initial
+    state of the second gives the unsplit result; for L < K-1 the final state keeps the tail
+    of the initial state."""
+    x, w, bias = _conv_case(9, L=13, K=4)
+    y, fin = o.causal_conv1d(x, w, bias, silu=True)
+    for cut in (1, 2, 3, 7):
+        y1, f1 = o.causal_conv1d(x[:, :cut], w, bias, silu=True)
+        y2, f2 = o.causal_conv1d(x[:, cut:], w, bias, init_state=f1, silu=True)
+        _close(np.concatenate([y1, y2], axis=1), y, 1e-13, f"chained at {cut}")
+        _close(f2, fin, 0.0, f"final state chained at {cut}")
+    init = np.random.default_rng(3).normal(size=(2, 5, 3))
+    _, fs = o.causal_conv1d(x[:, :1], w, bias, init_state=init, silu=False)
+    _close(fs[:, :, :2], init[:, :, 1:], 0.0, "short sequence keeps the initial state's tail")
+    _close(fs[:, :, 2], x[:, 0, :], 0.0, "short sequence appends the input")
+
+
+def pin_conv_decode_equals_fwd(o):
+    """Feeding the tokens one by one through the decode update reproduces the full convolution
+    (outputs and final state), from zeros and from a given initial state."""
+    x, w, bias = _conv_case(11, L=9, K=4)
+    init = np.random.default_rng(4).normal(size=(2, 5, 3))
+    for st0 in (None, init):
+        y, fin = o.causal_conv1d(x, w, bias, init_state=st0, silu=True)
+        st = np.zeros((2, 5, 3)) if st0 is None else st0.copy()
+        for t in range(x.shape[1]):
+            yt, st = o.conv1d_update(st, x[:, t], w, bias, silu=True)
+            _close(yt, y[:, t], 1e-13, f"decode step {t}")
+        _close(st, fin, 0.0, "decode final state")
+
+
+def pin_conv_causality(o):
+    """Changing the input at t changes no output before t."""
+    x, w, bias = _conv_case(13, L=10)
+    y, _ = o.causal_conv1d(x, w, bias, silu=True)
+    x2 = x.copy()
+    x2[:, 6] += 3.0
+    y2, _ = o.causal_conv1d(x2, w, bias, silu=True)
+    _close(y2[:, :6], y[:, :6], 0.0, "outputs before the change")
+    assert np.all(np.abs(y2[:, 6] - y[:, 6]) > 0), "the changed step must move its own output"
+
+
 ALL_PINS = [pin_worked_examples, pin_unrolled_sum, pin_lti_convolution, pin_linearity,
             pin_channel_independence, pin_causality, pin_zero_step, pin_impulse_long_carry,
             pin_decode_equals_scan, pin_associative_scan, pin_special_values, pin_storage_widening,
-            pin_channel_selection]
+            pin_channel_selection, pin_conv_library_convolution, pin_conv_impulse, pin_conv_silu,
+            pin_conv_chaining, pin_conv_decode_equals_fwd, pin_conv_causality]

@@ -39,6 +39,17 @@ MUTANTS = [
      "h[n] = abar * h[n] + load_elem(B, dtype, b * dstate + n) * xt;"),
     ("initial_state_ignored", "h[n] = h0 ? h0[ch * dstate + n] : 0.0;", "h[n] = 0.0;"),
     ("selection_wrong_row", "sel_d[k], h, y_out + k * seqlen, 1);", "sel_d[k], h, y_out + k * seqlen, 0);"),
+    ("conv_taps_reversed", "acc += (double)w[d * K + k] * v;", "acc += (double)w[d * K + (K - 1 - k)] * v;"),
+    ("conv_window_off_by_one", "const int64_t s = t - (K - 1) + k;", "const int64_t s = t - K + k;"),
+    ("conv_bias_dropped", "double acc = bias ? (double)bias[d] : 0.0;\n        for (int64_t k = 0; k < K; ++k) {",
+     "double acc = 0.0;\n        for (int64_t k = 0; k < K; ++k) {"),
+    ("conv_init_state_ignored", "v = init ? load_elem(init, dtype, (b * dim + d) * (K - 1) + (K - 1) + s) : 0.0;\n"
+     "          acc +=", "v = 0.0;\n          acc +="),
+    ("conv_final_state_first_inputs", "const int64_t s = seqlen - (K - 1) + j;", "const int64_t s = j;"),
+    ("conv_update_newest_first", "acc += (double)w[d * K + k] * st[k];", "acc += (double)w[d * K + k] * st[K - 2 - k];"),
+    ("conv_update_no_shift", "for (int64_t k = 0; k + 1 < K - 1; ++k) st[k] = st[k + 1];", ""),
+    ("conv_silu_skipped", "out[(b * seqlen + t) * dim + d] = apply_silu ? silu(acc) : acc;",
+     "out[(b * seqlen + t) * dim + d] = acc;"),
 ]
 
 
