@@ -158,28 +158,112 @@ def bench_decode(steps_per_rep, torch, np, W, ssm, device, ring):
     graph_ms = e0.elapsed_time(e1) / (reps * steps_per_rep)
     upd = w.batch * w.dim * w.dstate
     bpstep = decode_bytes_per_step(w.batch, w.dim, w.dstate, es)
-    # copy ceiling: read and write the state's byte count once
-    src = torch.empty(w.batch * w.dim * w.dstate, device=device)
-    dst = torch.empty_like(src)
-    for _ in range(3):
-        dst.copy_(src)
+    # ceiling: an in-place elementwise pass over the same ring of states (each state read and
+    # written once per step, as the update does), timed the same way
+    for i in range(3):
+        states[i % ring].mul_(1.0)
     torch.cuda.synchronize()
+    n_copy = 2 * ring if ring > 1 else 20
     e0.record()
-    for _ in range(20):
-        dst.copy_(src)
+    for i in range(n_copy):
+        states[i % ring].mul_(1.0)
     e1.record()
     torch.cuda.synchronize()
-    copy_ms = e0.elapsed_time(e1) / 20
+    copy_ms = e0.elapsed_time(e1) / n_copy
     out = {"batch": w.batch, "dim": w.dim, "dstate": w.dstate, "steps": steps_per_rep, "state_ring": ring,
            "ms_per_step": graph_ms, "ms_per_step_eager_python": eager_ms,
            "updates_per_s": upd / (graph_ms * 1e-3), "tokens_per_s": w.batch / (graph_ms * 1e-3),
            "alg_bytes_per_step": bpstep, "hbm_gbps": bpstep / (graph_ms * 1e-3) / 1e9,
-           "same_size_copy_gbps": 2 * src.numel() * 4 / (copy_ms * 1e-3) / 1e9,
+           "same_size_inplace_pass_gbps": 2 * states[0].numel() * 4 / (copy_ms * 1e-3) / 1e9,
            "kernel_ms": graph_ms}
     out["hbm_frac"] = out["hbm_gbps"] / HBM_PEAK_GBPS
     del states, d, graph
     torch.cuda.empty_cache()
     return out
+
+
+CONV_SHAPE = dict(batch=8, seqlen=2048, dim=1536, width=4, dtype="bf16", seed=61001)
+
+
+def conv_bytes(batch, seqlen, dim, width, es):
+    """Algorithmic bytes of one causal conv1d call: x read and y written once, the weights and
+    bias, and the final state (width-1 inputs per channel) written."""
+    return 2 * batch * seqlen * dim * es + dim * (width + 1) * 4 + batch * dim * (width - 1) * es
+
+
+def bench_conv(steps, warmup, torch, np, W, ssm, device):
+    """The depthwise causal convolution before the scan on the 130M-shaped layer input
+    (8 x 2048 x 1536, bf16, width 4), input sets rotated to defeat the Infinity Cache."""
+    c = CONV_SHAPE
+    es = 2
+    t = W.conv_inputs(c["batch"], c["seqlen"], c["dim"], c["width"], c["dtype"], c["seed"])
+    set_bytes = conv_bytes(c["batch"], c["seqlen"], c["dim"], c["width"], es)
+    copies = max(1, min(6, math.ceil(2 * MALL_BYTES / set_bytes)))
+    sets = []
+    for _ in range(copies):
+        d = {k: dev_tensor(v, torch, np, device) for k, v in t.items() if v is not None}
+        d["y"] = torch.empty_like(d["x"])
+        d["fin"] = torch.empty(c["batch"], c["dim"], c["width"] - 1, dtype=d["x"].dtype, device=device)
+        sets.append(d)
+
+    def call(i):
+        d = sets[i % copies]
+        ssm.ssm_causal_conv1d_fwd(d["x"], d["weight"], d["bias"], None, True, y=d["y"], final_state=d["fin"])
+
+    total_ms, per = time_calls(torch, call, steps, warmup)
+    kern_ms = sum(per) / len(per)
+    res = {"batch": c["batch"], "seqlen": c["seqlen"], "dim": c["dim"], "width": c["width"], "io_dtype": c["dtype"],
+           "rotated_input_sets": copies, "kernel_ms": kern_ms, "ms_per_step": total_ms / steps,
+           "elems_per_s": c["batch"] * c["seqlen"] * c["dim"] / (kern_ms * 1e-3), "alg_bytes": set_bytes,
+           "hbm_gbps": set_bytes / (kern_ms * 1e-3) / 1e9}
+    res["hbm_frac"] = res["hbm_gbps"] / HBM_PEAK_GBPS
+    del sets
+    torch.cuda.empty_cache()
+    return res
+
+
+def bench_conv_update(steps, torch, np, W, ssm, device):
+    """The one-token convolution on the decode shape (64 x 5120, width 4, bf16), one call per
+    step on a ring of 26 conv states, captured as one HIP graph and replayed."""
+    batch, dim, width = 64, 5120, 4
+    t = W.conv_inputs(batch, steps, dim, width, "bf16", seed=61004, has_init=True)
+    x = dev_tensor(np.ascontiguousarray(np.swapaxes(t["x"], 0, 1)), torch, np, device)  # step-major
+    wgt, bias = dev_tensor(t["weight"], torch, np, device), dev_tensor(t["bias"], torch, np, device)
+    ring = 26
+    states = [dev_tensor(t["init"], torch, np, device) for _ in range(ring)]
+    ys = torch.empty_like(x)
+
+    def call(i):
+        s = i % steps
+        ssm.ssm_causal_conv1d_update(states[i % ring], x[s], wgt, bias, True, y=ys[s])
+
+    for i in range(4):
+        call(i)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream(device)
+    side.wait_stream(torch.cuda.current_stream(device))
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            for i in range(steps):
+                call(i)
+    torch.cuda.synchronize()
+    graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 4
+    e0.record()
+    for _ in range(reps):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / (reps * steps)
+    step_bytes = 2 * batch * dim * 2 + 2 * batch * dim * (width - 1) * 2 + dim * (width + 1) * 4
+    del graph, states
+    torch.cuda.empty_cache()
+    return {"batch": batch, "dim": dim, "width": width, "io_dtype": "bf16", "steps": steps, "state_ring": ring,
+            "ms_per_step": ms, "tokens_per_s": batch / (ms * 1e-3), "alg_bytes_per_step": step_bytes,
+            "hbm_gbps": step_bytes / (ms * 1e-3) / 1e9}
 
 
 def cpu_baseline(name, np, W):
@@ -233,6 +317,8 @@ def profile_mode(args):
     torch.cuda.synchronize()
     if args.workload == "decode":
         res = bench_decode(args.steps, torch, np, W, ssm, torch.device("cuda:0"), ring=26)
+    elif args.workload == "conv":
+        res = bench_conv(args.steps, args.warmup, torch, np, W, ssm, torch.device("cuda:0"))
     else:
         res = bench_scan(args.workload, args.steps, args.warmup, torch, np, W, ssm, torch.device("cuda:0"))
     log(f"[profile] {args.workload}: {res['kernel_ms'] * 1e3:.1f} us/launch over {args.steps} launches")
@@ -282,7 +368,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="mamba130m", choices=["mamba130m", "mamba2p8b", "genomics", "decode"])
+    ap.add_argument("--workload", default="mamba130m",
+                    choices=["mamba130m", "mamba2p8b", "genomics", "decode", "conv"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the context measurements (2.8B scan, decode)")
     ap.add_argument("--profile-mode", action="store_true",
@@ -310,8 +397,8 @@ def main():
     import selective_state_space_61_amd as ssm
     from selective_state_space_61_amd import build as hip_build
 
-    if args.workload == "decode":
-        raise SystemExit("decode is measured as context next to a scan workload; use --profile-mode for it alone")
+    if args.workload in ("decode", "conv"):
+        raise SystemExit(f"{args.workload} is measured as context next to a scan workload; use --profile-mode for it alone")
     if not os.path.exists(ssm.LIBRARY):
         hip_build.build(verbose=True)
     ssm.load_library()
@@ -331,6 +418,11 @@ def main():
         extra["decode_mall_resident"] = bench_decode(256, torch, np, W, ssm, device, ring=1)
         extra["decode_hbm_ring26"] = bench_decode(256, torch, np, W, ssm, device, ring=26)
         log(f"[bench] decode: {extra['decode_hbm_ring26']['updates_per_s']:.3e} updates/s (ring of 26 states)")
+        extra["causal_conv1d"] = bench_conv(max(10, args.steps // 2), 3, torch, np, W, ssm, device)
+        log(f"[bench] causal conv1d: {extra['causal_conv1d']['kernel_ms'] * 1e3:.1f} us/launch, "
+            f"{extra['causal_conv1d']['hbm_gbps']:.0f} GB/s")
+        extra["causal_conv1d_update"] = bench_conv_update(256, torch, np, W, ssm, device)
+        log(f"[bench] conv update: {extra['causal_conv1d_update']['ms_per_step'] * 1e3:.2f} us/step")
 
     hbm_frac = main_res["hbm_frac"]
     alu_frac = main_res["valu_slot_frac"]

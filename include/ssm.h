@@ -156,6 +156,50 @@ SSM_API ssm_status_t ssm_state_update(int64_t batch, int64_t dim, int64_t dstate
                               const float *D, const void *z, const float *delta_bias, int delta_softplus, void *y,
                               void *stream);
 
+/*
+ * Depthwise causal convolution that feeds the scan in the Mamba block
+ * ("Mamba 论文精读" sec. 3.4, MambaBlock: Conv1d with one group per channel,
+ * kernel width K and K-1 zeros of padding, the first L outputs kept, then
+ * SiLU).  For each batch row b and channel d:
+ *
+ *   y[b,t,d] = bias[d] + sum_{k<K} weight[d,k] * xin[t-(K-1)+k]
+ *   xin[s]   = x[b,s,d] for s >= 0, initial_state[b,d,(K-1)+s] for s < 0
+ *              (zeros when initial_state is NULL)
+ *   y        = silu(y) when silu != 0
+ *   final_state[b,d,j] = xin[L-(K-1)+j], j = 0..K-2 (the last K-1 inputs,
+ *              oldest first): pass it as the next call's initial_state, or
+ *              as the conv_state of ssm_causal_conv1d_update.
+ *
+ *   x, y          (batch, seqlen, dim)  dtype (the scan's x layout)
+ *   weight        (dim, width)          fp32, width in 1..4
+ *   bias          (dim)                 fp32, or NULL
+ *   initial_state (batch, dim, width-1) dtype, or NULL
+ *   final_state   (batch, dim, width-1) dtype, or NULL; written
+ *
+ * Outputs must not overlap an input or each other.  The kernel is
+ * bandwidth-bound: x is read once and y written once.
+ */
+SSM_API ssm_status_t ssm_causal_conv1d_fwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t width,
+                                           ssm_dtype_t dtype, const void *x, const float *weight, const float *bias,
+                                           const void *initial_state, int silu, void *y, void *final_state,
+                                           void *stream);
+
+/*
+ * One token of the same convolution: the window is conv_state[b,d,0..K-2]
+ * followed by x[b,d]; y = bias + sum weight * window (then SiLU when asked);
+ * conv_state then drops its oldest input and appends x (in place).
+ *
+ *   conv_state (batch, dim, width-1) dtype, read and updated (may be NULL when width == 1)
+ *   x, y       (batch, dim)          dtype
+ *   weight     (dim, width) fp32; bias (dim) fp32 or NULL
+ *
+ * Running it over x[:, t] for t = 0..L-1 gives ssm_causal_conv1d_fwd's
+ * outputs and final state for the same initial state.
+ */
+SSM_API ssm_status_t ssm_causal_conv1d_update(int64_t batch, int64_t dim, int64_t width, ssm_dtype_t dtype,
+                                              void *conv_state, const void *x, const float *weight,
+                                              const float *bias, int silu, void *y, void *stream);
+
 /* Static string naming a status code ("SSM_OK", ...); never NULL. */
 SSM_API const char *ssm_status_string(ssm_status_t status);
 

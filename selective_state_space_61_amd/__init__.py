@@ -28,8 +28,8 @@ LIBRARY = os.path.join(_HERE, "libssm61.so")
 SSM_F32, SSM_BF16 = 0, 1
 STATUS_NAMES = {0: "SSM_OK", 1: "SSM_ERR_INVALID_ARG", 2: "SSM_ERR_UNSUPPORTED", 3: "SSM_ERR_MISALIGNED",
                 4: "SSM_ERR_HIP"}
-EXPORTED = ("ssm_scan_fwd", "ssm_scan_fwd_ex", "ssm_state_update", "ssm_status_string", "ssm_last_error",
-            "ssm_abi_version")
+EXPORTED = ("ssm_scan_fwd", "ssm_scan_fwd_ex", "ssm_state_update", "ssm_causal_conv1d_fwd",
+            "ssm_causal_conv1d_update", "ssm_status_string", "ssm_last_error", "ssm_abi_version")
 
 
 class SsmError(RuntimeError):
@@ -61,6 +61,10 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
     lib.ssm_scan_fwd_ex.restype = i32
     lib.ssm_state_update.argtypes = [i64, i64, i64, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp]
     lib.ssm_state_update.restype = i32
+    lib.ssm_causal_conv1d_fwd.argtypes = [i64, i64, i64, i64, i32, vp, vp, vp, vp, i32, vp, vp, vp]
+    lib.ssm_causal_conv1d_fwd.restype = i32
+    lib.ssm_causal_conv1d_update.argtypes = [i64, i64, i64, i32, vp, vp, vp, vp, i32, vp, vp]
+    lib.ssm_causal_conv1d_update.restype = i32
     lib.ssm_status_string.argtypes = [i32]
     lib.ssm_status_string.restype = ctypes.c_char_p
     lib.ssm_last_error.argtypes = []
@@ -180,9 +184,65 @@ def ssm_state_update(state: torch.Tensor, x: torch.Tensor, delta: torch.Tensor, 
     return y
 
 
+def ssm_causal_conv1d_fwd(x: torch.Tensor, weight: torch.Tensor, bias: Optional[torch.Tensor] = None,
+                          initial_state: Optional[torch.Tensor] = None, silu: bool = True, *,
+                          y: Optional[torch.Tensor] = None, final_state: Optional[torch.Tensor] = None,
+                          return_final_state: bool = False,
+                          stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Depthwise causal convolution before the scan (include/ssm.h: ssm_causal_conv1d_fwd).
+    x: (batch, seqlen, dim); weight: (dim, width) fp32; bias: (dim,) fp32; initial_state /
+    final_state: (batch, dim, width-1) in x's dtype.  Returns (y, final_state); final_state is
+    None unless one was passed in or return_final_state is True."""
+    lib = load_library()
+    if x.dim() != 3 or weight.dim() != 2:
+        raise ValueError("x must be (batch, seqlen, dim) and weight (dim, width)")
+    batch, seqlen, dim = x.shape
+    width = weight.shape[1]
+    dev, dt = x.device, x.dtype
+    code = _dtype_code(x)
+    _need(weight, "weight", (dim, width), torch.float32, dev)
+    _need(bias, "bias", (dim,), torch.float32, dev, optional=True)
+    _need(initial_state, "initial_state", (batch, dim, width - 1), dt, dev, optional=True)
+    if y is None:
+        y = torch.empty_like(x)
+    _need(y, "y", (batch, seqlen, dim), dt, dev)
+    if final_state is None and return_final_state:
+        final_state = torch.empty((batch, dim, width - 1), dtype=dt, device=dev)
+    _need(final_state, "final_state", (batch, dim, width - 1), dt, dev, optional=True)
+    status = lib.ssm_causal_conv1d_fwd(batch, seqlen, dim, width, code, _ptr(x), _ptr(weight), _ptr(bias),
+                                       _ptr(initial_state), int(bool(silu)), _ptr(y), _ptr(final_state),
+                                       _stream(dev, stream))
+    _check(status)
+    return y, final_state
+
+
+def ssm_causal_conv1d_update(conv_state: Optional[torch.Tensor], x: torch.Tensor, weight: torch.Tensor,
+                             bias: Optional[torch.Tensor] = None, silu: bool = True, *,
+                             y: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """One token of the convolution (include/ssm.h: ssm_causal_conv1d_update); conv_state
+    (batch, dim, width-1) in x's dtype is updated in place.  Returns y (batch, dim)."""
+    lib = load_library()
+    if x.dim() != 2 or weight.dim() != 2:
+        raise ValueError("x must be (batch, dim) and weight (dim, width)")
+    batch, dim = x.shape
+    width = weight.shape[1]
+    dev, dt = x.device, x.dtype
+    code = _dtype_code(x)
+    _need(weight, "weight", (dim, width), torch.float32, dev)
+    _need(bias, "bias", (dim,), torch.float32, dev, optional=True)
+    _need(conv_state, "conv_state", (batch, dim, width - 1), dt, dev, optional=width == 1)
+    if y is None:
+        y = torch.empty_like(x)
+    _need(y, "y", (batch, dim), dt, dev)
+    status = lib.ssm_causal_conv1d_update(batch, dim, width, code, _ptr(conv_state), _ptr(x), _ptr(weight),
+                                          _ptr(bias), int(bool(silu)), _ptr(y), _stream(dev, stream))
+    _check(status)
+    return y
+
+
 def abi_version() -> int:
     return load_library().ssm_abi_version()
 
 
-__all__ = ["ssm_scan_fwd", "ssm_state_update", "abi_version", "load_library", "SsmError", "ScanOpts",
+__all__ = ["ssm_scan_fwd", "ssm_state_update", "ssm_causal_conv1d_fwd", "ssm_causal_conv1d_update", "abi_version", "load_library", "SsmError", "ScanOpts",
            "LIBRARY", "EXPORTED"]

@@ -12,6 +12,7 @@
 #include "../../include/ssm.h"
 #include "scan_table.hpp"
 #include "state_update.hpp"
+#include "conv1d.hpp"
 
 namespace {
 
@@ -100,6 +101,31 @@ CarryKernel carry_kernel(int64_t n) {
     case 16: return ssm::scan_carry_kernel<16>;
     case 32: return ssm::scan_carry_kernel<32>;
     case 64: return ssm::scan_carry_kernel<64>;
+    default: return nullptr;
+  }
+}
+
+using ConvKernel = void (*)(const ssm::ConvArgs);
+using ConvUpdateKernel = void (*)(const ssm::ConvUpdateArgs);
+
+template <bool BF16>
+ConvKernel conv_kernel(int64_t width) {
+  switch (width) {
+    case 1: return ssm::causal_conv1d_kernel<BF16, 1>;
+    case 2: return ssm::causal_conv1d_kernel<BF16, 2>;
+    case 3: return ssm::causal_conv1d_kernel<BF16, 3>;
+    case 4: return ssm::causal_conv1d_kernel<BF16, 4>;
+    default: return nullptr;
+  }
+}
+
+template <bool BF16>
+ConvUpdateKernel conv_update_kernel(int64_t width) {
+  switch (width) {
+    case 1: return ssm::conv1d_update_kernel<BF16, 1>;
+    case 2: return ssm::conv1d_update_kernel<BF16, 2>;
+    case 3: return ssm::conv1d_update_kernel<BF16, 3>;
+    case 4: return ssm::conv1d_update_kernel<BF16, 4>;
     default: return nullptr;
   }
 }
@@ -374,6 +400,90 @@ ssm_status_t ssm_state_update(int64_t batch, int64_t dim, int64_t dstate, ssm_dt
   hipLaunchKernelGGL(k, dim3(static_cast<unsigned>(blocks)), dim3(ssm::kUpdateThreads), 0,
                      static_cast<hipStream_t>(stream), a);
   return check_launch("state update");
+}
+
+ssm_status_t ssm_causal_conv1d_fwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t width, ssm_dtype_t dtype,
+                                   const void* x, const float* weight, const float* bias, const void* initial_state,
+                                   int silu, void* y, void* final_state, void* stream) {
+  g_err[0] = '\0';
+  if (batch < 0 || seqlen < 0 || dim < 0 || width < 0)
+    return fail(SSM_ERR_INVALID_ARG, "negative size (batch=%lld seqlen=%lld dim=%lld width=%lld)", (long long)batch,
+                (long long)seqlen, (long long)dim, (long long)width);
+  if (dtype != SSM_F32 && dtype != SSM_BF16) return fail(SSM_ERR_UNSUPPORTED, "unknown dtype %d", (int)dtype);
+  if (width < 1 || width > 4) return fail(SSM_ERR_UNSUPPORTED, "width %lld not in 1..4", (long long)width);
+  const int64_t es = dtype == SSM_BF16 ? 2 : 4;
+  int64_t nch, n_bl, n_bld, n_st, n_w;
+  if (!mul_ok(batch, dim, &nch) || !mul_ok(batch, seqlen, &n_bl) || !mul_ok(n_bl, dim * es, &n_bld) ||
+      !mul_ok(nch, (width - 1) * es, &n_st) || !mul_ok(dim, width * 4, &n_w))
+    return fail(SSM_ERR_INVALID_ARG, "tensor size overflows int64");
+  if (nch == 0) return SSM_OK;
+  if (seqlen == 0 && !final_state) return SSM_OK;
+  if (!weight || (seqlen > 0 && (!x || !y)))
+    return fail(SSM_ERR_INVALID_ARG, "NULL required pointer (weight, and x and y when seqlen > 0)");
+  const Arg args[] = {{x, es, "x"}, {weight, 4, "weight"}, {bias, 4, "bias"}, {initial_state, es, "initial_state"},
+                      {y, es, "y"}, {final_state, es, "final_state"}};
+  if (const Arg* bad = misaligned(args, sizeof args / sizeof args[0]))
+    return fail(SSM_ERR_MISALIGNED, "%s (%p) is not aligned to its element size", bad->name, bad->p);
+  const Range rx{x, n_bld}, rw{weight, n_w}, rb{bias, dim * 4}, ri{initial_state, n_st},
+      ry{seqlen > 0 ? y : nullptr, n_bld}, rf{final_state, n_st};
+  for (Range in : {rx, rw, rb, ri})
+    if (overlap(ry, in) || overlap(rf, in)) return fail(SSM_ERR_INVALID_ARG, "an output overlaps an input");
+  if (overlap(ry, rf)) return fail(SSM_ERR_INVALID_ARG, "y overlaps final_state");
+
+  const int64_t vec = dtype == SSM_BF16 ? ssm::kConvVec<true> : ssm::kConvVec<false>;
+  ssm::ConvArgs a{};
+  a.x = x; a.weight = weight; a.bias = bias; a.init = initial_state; a.y = y; a.final_state = final_state;
+  a.batch = batch; a.seqlen = seqlen; a.dim = dim;
+  a.ncv = (dim + vec - 1) / vec;
+  a.ntiles = seqlen > 0 ? (seqlen + ssm::kConvTile - 1) / ssm::kConvTile : 1;
+  a.silu = silu ? 1 : 0;
+  a.vec_ok = (dim % vec == 0) && aligned(x, ssm::kConvVecBytes) && aligned(y, ssm::kConvVecBytes);
+  int64_t threads;
+  if (!mul_ok(a.ncv * a.ntiles, batch, &threads)) return fail(SSM_ERR_INVALID_ARG, "tensor size overflows int64");
+  const int64_t blocks = (threads + ssm::kConvThreads - 1) / ssm::kConvThreads;
+  if (blocks > 0x7fffffff) return fail(SSM_ERR_UNSUPPORTED, "grid too large");
+  const ConvKernel k = dtype == SSM_BF16 ? conv_kernel<true>(width) : conv_kernel<false>(width);
+  hipLaunchKernelGGL(k, dim3(static_cast<unsigned>(blocks)), dim3(ssm::kConvThreads), 0,
+                     static_cast<hipStream_t>(stream), a);
+  return check_launch("causal conv1d");
+}
+
+ssm_status_t ssm_causal_conv1d_update(int64_t batch, int64_t dim, int64_t width, ssm_dtype_t dtype, void* conv_state,
+                                      const void* x, const float* weight, const float* bias, int silu, void* y,
+                                      void* stream) {
+  g_err[0] = '\0';
+  if (batch < 0 || dim < 0 || width < 0)
+    return fail(SSM_ERR_INVALID_ARG, "negative size (batch=%lld dim=%lld width=%lld)", (long long)batch,
+                (long long)dim, (long long)width);
+  if (dtype != SSM_F32 && dtype != SSM_BF16) return fail(SSM_ERR_UNSUPPORTED, "unknown dtype %d", (int)dtype);
+  if (width < 1 || width > 4) return fail(SSM_ERR_UNSUPPORTED, "width %lld not in 1..4", (long long)width);
+  const int64_t es = dtype == SSM_BF16 ? 2 : 4;
+  int64_t nch, n_bd, n_st, n_w;
+  if (!mul_ok(batch, dim, &nch) || !mul_ok(nch, es, &n_bd) || !mul_ok(nch, (width - 1) * es, &n_st) ||
+      !mul_ok(dim, width * 4, &n_w))
+    return fail(SSM_ERR_INVALID_ARG, "tensor size overflows int64");
+  if (nch == 0) return SSM_OK;
+  if (!x || !weight || !y || (width > 1 && !conv_state))
+    return fail(SSM_ERR_INVALID_ARG, "NULL required pointer (x, weight, y, and conv_state when width > 1)");
+  const Arg args[] = {{conv_state, es, "conv_state"}, {x, es, "x"}, {weight, 4, "weight"}, {bias, 4, "bias"},
+                      {y, es, "y"}};
+  if (const Arg* bad = misaligned(args, sizeof args / sizeof args[0]))
+    return fail(SSM_ERR_MISALIGNED, "%s (%p) is not aligned to its element size", bad->name, bad->p);
+  const Range rs{width > 1 ? conv_state : nullptr, n_st}, rx{x, n_bd}, rw{weight, n_w}, rb{bias, dim * 4},
+      ry{y, n_bd};
+  for (Range in : {rx, rw, rb})
+    if (overlap(ry, in) || overlap(rs, in)) return fail(SSM_ERR_INVALID_ARG, "an output overlaps an input");
+  if (overlap(ry, rs)) return fail(SSM_ERR_INVALID_ARG, "y overlaps conv_state");
+
+  ssm::ConvUpdateArgs a{};
+  a.state = conv_state; a.x = x; a.weight = weight; a.bias = bias; a.y = y;
+  a.batch = batch; a.dim = dim; a.silu = silu ? 1 : 0;
+  const int64_t blocks = (nch + ssm::kConvThreads - 1) / ssm::kConvThreads;
+  if (blocks > 0x7fffffff) return fail(SSM_ERR_UNSUPPORTED, "grid too large");
+  const ConvUpdateKernel k = dtype == SSM_BF16 ? conv_update_kernel<true>(width) : conv_update_kernel<false>(width);
+  hipLaunchKernelGGL(k, dim3(static_cast<unsigned>(blocks)), dim3(ssm::kConvThreads), 0,
+                     static_cast<hipStream_t>(stream), a);
+  return check_launch("causal conv1d update");
 }
 
 }  // extern "C"

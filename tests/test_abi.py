@@ -181,3 +181,38 @@ def test_binding_raises_without_library(tmp_path):
             mod.load_library(str(tmp_path / "missing.so"))
     finally:
         mod._lib_handle = saved
+
+
+def conv(lib, batch=2, seqlen=8, dim=16, width=4, dtype=F32, x=fake(0), w=fake(1), bias=fake(2), init=fake(3),
+         silu=1, y=fake(4), fin=fake(5)):
+    return lib.ssm_causal_conv1d_fwd(batch, seqlen, dim, width, dtype, x, w, bias, init, silu, y, fin, None)
+
+
+def conv_update(lib, batch=2, dim=16, width=4, dtype=F32, state=fake(0), x=fake(1), w=fake(2), bias=fake(3),
+                silu=1, y=fake(4)):
+    return lib.ssm_causal_conv1d_update(batch, dim, width, dtype, state, x, w, bias, silu, y, None)
+
+
+@pytest.mark.parametrize("kw,code", [(dict(batch=-1), INVALID), (dict(seqlen=-1), INVALID), (dict(width=0), UNSUPPORTED),
+                                     (dict(width=5), UNSUPPORTED), (dict(dtype=4), UNSUPPORTED),
+                                     (dict(x=None), INVALID), (dict(w=None), INVALID), (dict(y=None), INVALID),
+                                     (dict(x=fake(0, 2)), MISALIGNED), (dict(fin=fake(5, 2)), MISALIGNED),
+                                     (dict(w=fake(1, 2)), MISALIGNED), (dict(y=fake(0, 4)), INVALID),
+                                     (dict(fin=fake(3, 0)), INVALID), (dict(fin=fake(4, 0)), INVALID)])
+def test_conv_validation(lib, kw, code):
+    assert conv(lib, **kw) == code
+    assert err(lib)
+
+
+def test_conv_nothing_to_do(lib):
+    assert conv(lib, batch=0, x=None, w=None, y=None) == OK
+    # seqlen == 0 without a final state: nothing to write
+    assert conv(lib, seqlen=0, x=None, y=None, fin=None) == OK
+
+
+@pytest.mark.parametrize("kw,code", [(dict(dim=-1), INVALID), (dict(width=7), UNSUPPORTED), (dict(state=None), INVALID),
+                                     (dict(y=None), INVALID), (dict(state=fake(0, 2)), MISALIGNED),
+                                     (dict(y=fake(1, 0)), INVALID), (dict(state=fake(2, 0)), INVALID)])
+def test_conv_update_validation(lib, kw, code):
+    assert conv_update(lib, **kw) == code
+    assert err(lib)

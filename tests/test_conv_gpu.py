@@ -1,0 +1,150 @@
+"""Parity of the HIP depthwise causal convolution (through the C ABI) with the fp64 oracle.
+
+Outputs are compared element by element under the same tolerance rule as the scan
+(max |y - y_ref| <= tol * max |y_ref|, tol 1e-4 for fp32 and 2e-2 for bf16 storage).  The final
+state holds copies of inputs, so it must match bit for bit."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from gpu_util import TOL, assert_close, say, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def o():
+    return oracle.load()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import selective_state_space_61_amd as ssm
+    ssm.load_library()
+    say(f"\n[gpu] {torch.cuda.get_device_name(0)}; library {ssm.LIBRARY}")
+
+
+def conv_gpu(t, silu, **kw):
+    import selective_state_space_61_amd as ssm
+    d = {k: to_dev(v) for k, v in t.items()}
+    y, fin = ssm.ssm_causal_conv1d_fwd(d["x"], d["weight"], d["bias"], d["init"], silu, return_final_state=True,
+                                       **kw)
+    torch.cuda.synchronize()
+    return y, fin
+
+
+def exact(got, ref_f64, what):
+    """A state that copies inputs must equal the oracle's value bit for bit (after widening)."""
+    g = to_host(got)
+    assert np.array_equal(g, ref_f64), f"{what}: max diff {np.max(np.abs(g - ref_f64)) if g.size else 0}"
+
+
+def compare(o, t, dtype, silu, what):
+    say(f"[case] {what}")
+    y, fin = conv_gpu(t, silu)
+    y_ref, fin_ref = o.causal_conv1d(t["x"], t["weight"], t["bias"], t["init"], silu=silu)
+    assert_close(to_host(y), y_ref, TOL[dtype], f"{what} y")
+    exact(fin, fin_ref, f"{what} final_state")
+    return y, fin
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("width", [1, 2, 3, 4])
+def test_widths(o, dtype, width):
+    t = W.conv_inputs(2, 100, 200, width, dtype, seed=width, has_init=width > 1)
+    compare(o, t, dtype, True, f"width={width} {dtype}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("shape", [(3, 77, 13), (1, 1, 64), (2, 2, 9), (1, 3, 8), (4, 33, 1), (2, 64, 520),
+                                   (1, 31, 24)])
+def test_ragged_shapes(o, dtype, shape):
+    batch, L, dim = shape
+    t = W.conv_inputs(batch, L, dim, 4, dtype, seed=L * 7 + dim, has_init=(L % 2 == 1))
+    compare(o, t, dtype, True, f"ragged {shape} {dtype}")
+
+
+@pytest.mark.parametrize("variant", ["no_bias", "no_silu", "no_init"])
+def test_variants(o, variant):
+    t = W.conv_inputs(2, 70, 48, 4, "bf16", seed=5, has_bias=variant != "no_bias", has_init=variant != "no_init")
+    compare(o, t, "bf16", variant != "no_silu", f"variant {variant}")
+
+
+def test_empty_sequence_passes_state_through(o):
+    import selective_state_space_61_amd as ssm
+    t = W.conv_inputs(2, 0, 24, 4, "f32", seed=3, has_init=True)
+    d = {k: to_dev(v) for k, v in t.items()}
+    y, fin = ssm.ssm_causal_conv1d_fwd(d["x"], d["weight"], d["bias"], d["init"], True, return_final_state=True)
+    torch.cuda.synchronize()
+    assert y.numel() == 0
+    _, fin_ref = o.causal_conv1d(t["x"], t["weight"], t["bias"], t["init"], silu=True)
+    exact(fin, fin_ref, "passthrough")
+    # without an initial state the final state is the zero padding
+    _, fin0 = ssm.ssm_causal_conv1d_fwd(d["x"], d["weight"], d["bias"], None, True, return_final_state=True)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(fin0).item() == 0
+
+
+def test_unaligned_views(o):
+    """Views one element off 16-byte alignment take the element-wise path."""
+    import selective_state_space_61_amd as ssm
+    t = W.conv_inputs(2, 50, 64, 4, "bf16", seed=9)
+    x = to_dev(t["x"])
+    buf = torch.empty(x.numel() + 1, dtype=x.dtype, device=x.device)
+    xv = buf[1:].view(x.shape)
+    xv.copy_(x)
+    ybuf = torch.empty_like(buf)
+    yv = ybuf[1:].view(x.shape)
+    ssm.ssm_causal_conv1d_fwd(xv, to_dev(t["weight"]), to_dev(t["bias"]), None, True, y=yv)
+    torch.cuda.synchronize()
+    y_ref, _ = o.causal_conv1d(t["x"], t["weight"], t["bias"], None, silu=True)
+    assert_close(to_host(yv), y_ref, TOL["bf16"], "unaligned y")
+
+
+def test_chaining_equals_one_call(o):
+    import selective_state_space_61_amd as ssm
+    t = W.conv_inputs(2, 200, 136, 4, "bf16", seed=21, has_init=True)
+    d = {k: to_dev(v) for k, v in t.items()}
+    y_all, fin_all = ssm.ssm_causal_conv1d_fwd(d["x"], d["weight"], d["bias"], d["init"], True,
+                                               return_final_state=True)
+    cut = 77
+    x1, x2 = d["x"][:, :cut].contiguous(), d["x"][:, cut:].contiguous()
+    y1, f1 = ssm.ssm_causal_conv1d_fwd(x1, d["weight"], d["bias"], d["init"], True, return_final_state=True)
+    y2, f2 = ssm.ssm_causal_conv1d_fwd(x2, d["weight"], d["bias"], f1, True, return_final_state=True)
+    torch.cuda.synchronize()
+    assert torch.equal(torch.cat([y1, y2], dim=1), y_all), "chained outputs differ from one call"
+    assert torch.equal(f2, fin_all)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("width", [1, 2, 4])
+def test_update_matches_oracle_and_fwd(o, dtype, width):
+    """Token-by-token updates reproduce the oracle's convolution and the GPU's full call."""
+    import selective_state_space_61_amd as ssm
+    batch, L, dim = 3, 12, 40
+    t = W.conv_inputs(batch, L, dim, width, dtype, seed=width + 30, has_init=width > 1)
+    d = {k: to_dev(v) for k, v in t.items()}
+    y_ref, fin_ref = o.causal_conv1d(t["x"], t["weight"], t["bias"], t["init"], silu=True)
+    y_fwd, fin_fwd = ssm.ssm_causal_conv1d_fwd(d["x"], d["weight"], d["bias"], d["init"], True,
+                                               return_final_state=True)
+    state = d["init"].clone() if d["init"] is not None else None
+    ys = []
+    for s in range(L):
+        ys.append(ssm.ssm_causal_conv1d_update(state, d["x"][:, s].contiguous(), d["weight"], d["bias"], True))
+    torch.cuda.synchronize()
+    y_dec = torch.stack(ys, dim=1)
+    assert_close(to_host(y_dec), y_ref, TOL[dtype], f"update width={width} {dtype}")
+    if width > 1:
+        exact(state, fin_ref, "update final state")
+    assert torch.equal(y_dec, y_fwd), "update and full call must give the same bits"
+
+
+def test_full_mamba130m_shape(o):
+    """The 130M-shaped layer input (8 x 2048 x 1536, bf16, width 4) against the oracle, every
+    element, in the launch configuration the benchmark times."""
+    t = W.conv_inputs(8, 2048, 1536, 4, "bf16", seed=61001)
+    compare(o, t, "bf16", True, "mamba130m-shaped conv")

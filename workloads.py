@@ -19,6 +19,9 @@ these tensors stand in for them):
   -(n + 1) (the S4D-real style initialisation of A, with A = -exp(A_log));
   D = 1; the delta bias is chosen per channel so that softplus(bias) is
   log-uniform in [1e-3, 1e-1], i.e. bias = log(expm1(v)), log10 v ~ U(-3, -1).
+* ``conv`` (the depthwise convolution before the scan) -- x ~ N(0, 1) as above; weight and bias
+  ~ U(-1/sqrt(K), 1/sqrt(K)), the default initialisation range of a depthwise Conv1d whose
+  fan-in is the kernel width K; an initial state, when asked for, ~ N(0, 1).
 * ``genomics`` -- a one-hot 4-symbol alphabet (s_t ~ U{0..3}) projected by a
   seeded (4, dim) matrix W ~ N(0, 0.5^2), so x[b, t, :] = W[s_t, :]; delta is
   passed directly (no softplus, no bias) and is log-uniform in [1e-4, 1e-1];
@@ -32,7 +35,8 @@ from typing import Dict, Optional
 import numpy as np
 
 # Stream ids: one Philox key per (seed, tensor).
-_TENSOR_IDS = {"x": 1, "delta": 2, "B": 3, "C": 4, "z": 5, "bias": 6, "symbols": 7, "W": 8}
+_TENSOR_IDS = {"x": 1, "delta": 2, "B": 3, "C": 4, "z": 5, "bias": 6, "symbols": 7, "W": 8, "conv_w": 9,
+               "conv_b": 10, "conv_state": 11}
 
 _CHUNK = 1 << 24  # elements per draw; bounds temporary memory for the 1M-step workload
 
@@ -151,6 +155,23 @@ def scan_inputs(batch: int, seqlen: int, dim: int, dstate: int, dtype: str = "f3
     A, D, bias = params(dim, dstate, seed, has_bias and recipe == "default", has_D)
     return {"x": _store(x, dtype), "delta": _store(delta, dtype), "B": _store(B, dtype), "C": _store(C, dtype),
             "z": None if z is None else _store(z, dtype), "A": A, "D": D, "delta_bias": bias}
+
+
+def _uniform(seed: int, tensor: str, shape, lo: float, hi: float) -> np.ndarray:
+    return _rng(seed, tensor).uniform(lo, hi, int(np.prod(shape))).astype(np.float32).reshape(shape)
+
+
+def conv_inputs(batch: int, seqlen: int, dim: int, width: int, dtype: str = "f32", seed: int = 0,
+                has_bias: bool = True, has_init: bool = False) -> Dict[str, Optional[np.ndarray]]:
+    """Inputs of one depthwise causal convolution: x (batch, seqlen, dim) in the storage type;
+    weight (dim, width) and bias (dim,) in fp32; init (batch, dim, width-1) in the storage type
+    or None."""
+    bound = 1.0 / np.sqrt(width)
+    x = _normal(seed, "x", (batch, seqlen, dim))
+    w = _uniform(seed, "conv_w", (dim, width), -bound, bound)
+    b = _uniform(seed, "conv_b", (dim,), -bound, bound) if has_bias else None
+    init = _normal(seed, "conv_state", (batch, dim, width - 1)) if has_init else None
+    return {"x": _store(x, dtype), "weight": w, "bias": b, "init": None if init is None else _store(init, dtype)}
 
 
 def workload_inputs(w: Workload) -> Dict[str, Optional[np.ndarray]]:
