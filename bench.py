@@ -30,17 +30,22 @@ HBM_PEAK_GBPS = 8000.0                       # MI355X HBM3E, published
 VALU_LANE_SLOTS = 256 * 4 * 16 * 2.4e9        # CUs x SIMDs x lanes x clock: fp32 VALU issue slots/s (non-packed)
 SLOTS_PER_UPDATE = 6                          # per (t,d,n): 2 mul + 2 fma + v_exp_f32 at half rate (2 slots)
 MALL_BYTES = 256 << 20
-KERNEL_SOURCES = ["selective_state_space_61_amd/csrc/ssm_api.hip", "selective_state_space_61_amd/csrc/scan_fwd.hpp",
-                  "selective_state_space_61_amd/csrc/ssm_device.hpp", "selective_state_space_61_amd/csrc/state_update.hpp"]
+_CSRC = "selective_state_space_61_amd/csrc/"
+# the sources each measured kernel is compiled from; a traffic record is used only while they are
+# unchanged (launch shapes live in ssm_api.hip and are re-measured whenever they change)
+KERNEL_SOURCES = {
+    "scan": [_CSRC + f for f in ("scan_fwd.hpp", "scan_table.hpp", "scan_bf16.hip", "scan_f32.hip", "ssm_device.hpp")],
+    "conv": [_CSRC + f for f in ("conv1d.hpp", "ssm_device.hpp")],
+}
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def source_hash() -> str:
+def source_hash(family: str = "scan") -> str:
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in KERNEL_SOURCES[family]:
         h.update(open(os.path.join(ROOT, p), "rb").read())
     return h.hexdigest()[:16]
 
@@ -210,8 +215,29 @@ def bench_conv(steps, warmup, torch, np, W, ssm, device):
         d = sets[i % copies]
         ssm.ssm_causal_conv1d_fwd(d["x"], d["weight"], d["bias"], None, True, y=d["y"], final_state=d["fin"])
 
-    total_ms, per = time_calls(torch, call, steps, warmup)
-    kern_ms = sum(per) / len(per)
+    # a call takes ~25 us, less than the Python launch path, so the calls are captured once as a
+    # HIP graph and replayed: the timing then holds the kernels and not host gaps between them
+    for i in range(warmup):
+        call(i)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream(device)
+    side.wait_stream(torch.cuda.current_stream(device))
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            for i in range(steps):
+                call(i)
+    torch.cuda.synchronize()
+    graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    total_ms = e0.elapsed_time(e1)
+    kern_ms = total_ms / steps
+    del graph
     res = {"batch": c["batch"], "seqlen": c["seqlen"], "dim": c["dim"], "width": c["width"], "io_dtype": c["dtype"],
            "rotated_input_sets": copies, "kernel_ms": kern_ms, "ms_per_step": total_ms / steps,
            "elems_per_s": c["batch"] * c["seqlen"] * c["dim"] / (kern_ms * 1e-3), "alg_bytes": set_bytes,
@@ -293,7 +319,7 @@ def traffic_from_profiles(name, alg_bytes):
     if not os.path.exists(p):
         return None, None
     rec = json.load(open(p))
-    if rec.get("source_hash") != source_hash():
+    if rec.get("source_hash") != source_hash(rec.get("family", "scan")):
         return None, "stale"
     return rec["hbm_bytes_per_launch"], rec
 
@@ -339,20 +365,26 @@ def summarize_traffic(fetch_csv, write_csv, workload):
         return vals
 
     fetch, write = per_kernel(fetch_csv, "FETCH_SIZE"), per_kernel(write_csv, "WRITE_SIZE")
+    family = "conv" if workload == "conv" else "scan"
     calib = [k for k in fetch if "copy" in k.lower()]
-    scan = [k for k in fetch if "scan_chunk_kernel" in k]
+    scan = [k for k in fetch if ("causal_conv1d_kernel" if family == "conv" else "scan_chunk_kernel") in k]
     if not calib or not scan:
-        raise SystemExit(f"calibration or scan kernel missing in {fetch_csv}: {list(fetch)}")
+        raise SystemExit(f"calibration or measured kernel missing in {fetch_csv}: {list(fetch)}")
     ck, sk = calib[0], scan[0]
     kib = CALIB_BYTES / 1024
     f_scale = kib / max(fetch[ck]), kib / max(write[ck])  # the copy reads and writes CALIB_BYTES
     f_kib = sorted(fetch[sk])[len(fetch[sk]) // 2]
     w_kib = sorted(write[sk])[len(write[sk]) // 2]
-    w = W.WORKLOADS[workload]
-    es = 2 if w.dtype == "bf16" else 4
-    alg = scan_bytes(w.batch, w.seqlen, w.dim, w.dstate, es)
+    if family == "conv":
+        c = CONV_SHAPE
+        alg = conv_bytes(c["batch"], c["seqlen"], c["dim"], c["width"], 2)
+    else:
+        w = W.WORKLOADS[workload]
+        es = 2 if w.dtype == "bf16" else 4
+        alg = scan_bytes(w.batch, w.seqlen, w.dim, w.dstate, es)
     hbm = f_kib * 1024 * f_scale[0] + w_kib * 1024 * f_scale[1]
-    rec = {"workload": workload, "kernel": sk, "source_hash": source_hash(),
+    rec = {"workload": workload, "family": family, "kernel": sk, "sources": KERNEL_SOURCES[family],
+           "source_hash": source_hash(family),
            "fetch_kib_per_launch": f_kib, "write_kib_per_launch": w_kib,
            "calibration_kernel": ck, "calibration_bytes": CALIB_BYTES,
            "calibration_fetch_kib": max(fetch[ck]), "calibration_write_kib": max(write[ck]),
@@ -419,6 +451,7 @@ def main():
         extra["decode_hbm_ring26"] = bench_decode(256, torch, np, W, ssm, device, ring=26)
         log(f"[bench] decode: {extra['decode_hbm_ring26']['updates_per_s']:.3e} updates/s (ring of 26 states)")
         extra["causal_conv1d"] = bench_conv(max(10, args.steps // 2), 3, torch, np, W, ssm, device)
+        extra["causal_conv1d"]["traffic"] = traffic_from_profiles("conv", extra["causal_conv1d"]["alg_bytes"])[0]
         log(f"[bench] causal conv1d: {extra['causal_conv1d']['kernel_ms'] * 1e3:.1f} us/launch, "
             f"{extra['causal_conv1d']['hbm_gbps']:.0f} GB/s")
         extra["causal_conv1d_update"] = bench_conv_update(256, torch, np, W, ssm, device)
