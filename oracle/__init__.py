@@ -81,6 +81,9 @@ class Oracle:
         lib.oracle_widen.argtypes = [vp, i32, i64]
         lib.oracle_widen.restype = dp
         lib.oracle_max_threads.restype = i32
+        lib.oracle_scan_bwd.argtypes = [i64, i64, i64, i64, i32, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp,
+                                        vp, vp, vp, vp, vp, vp]
+        lib.oracle_scan_bwd.restype = i32
         lib.oracle_causal_conv1d.argtypes = [i64, i64, i64, i64, i32, vp, vp, vp, vp, i32, vp, vp]
         lib.oracle_causal_conv1d.restype = i32
         lib.oracle_conv1d_update.argtypes = [i64, i64, i64, i32, vp, vp, vp, vp, i32, vp]
@@ -176,6 +179,33 @@ class Oracle:
             raise ValueError("oracle_state_update rejected its arguments")
         return y, st
 
+
+    def scan_bwd(self, x, delta, A, B, C, dy, D=None, z=None, delta_bias=None, delta_softplus=False):
+        """Gradients of sum(dy * y) for the scan from a zero state.  Returns a dict of float64
+        arrays: dx, ddelta (batch, L, dim); dA (dim, N); dB, dC (batch, L, N); dD, ddelta_bias
+        (dim,) when D / delta_bias are given; dz (batch, L, dim) when z is given."""
+        x, delta, B, C, z = _c(x), _c(delta), _c(B), _c(C), _c(z)
+        code = _dtype_code(x)
+        A = _c(A, np.float32)
+        D = _c(D, np.float32)
+        delta_bias = _c(delta_bias, np.float32)
+        dy = _c(dy, np.float64)
+        batch, L, dim = x.shape
+        N = A.shape[1]
+        assert dy.shape == x.shape
+        out = {"dx": np.empty((batch, L, dim)), "ddelta": np.empty((batch, L, dim)), "dA": np.empty((dim, N)),
+               "dB": np.empty((batch, L, N)), "dC": np.empty((batch, L, N))}
+        out["dD"] = np.empty(dim) if D is not None else None
+        out["ddelta_bias"] = np.empty(dim) if delta_bias is not None else None
+        out["dz"] = np.empty((batch, L, dim)) if z is not None else None
+        rc = self._lib.oracle_scan_bwd(batch, L, dim, N, code, _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C),
+                                       _ptr(D), _ptr(z), _ptr(delta_bias), int(bool(delta_softplus)), _ptr(dy),
+                                       _ptr(out["dx"]), _ptr(out["ddelta"]), _ptr(out["dA"]), _ptr(out["dB"]),
+                                       _ptr(out["dC"]), _ptr(out["dD"]), _ptr(out["dz"]),
+                                       _ptr(out["ddelta_bias"]))
+        if rc != 0:
+            raise ValueError("oracle_scan_bwd rejected its arguments")
+        return out
 
     # -- the causal convolution before the scan ------------------------------------------------
     def causal_conv1d(self, x, weight, bias=None, init_state=None, silu=True) -> Tuple[np.ndarray, np.ndarray]:

@@ -42,6 +42,7 @@
 #include <math.h>
 #include <stddef.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 #ifdef _OPENMP
 #include <omp.h>
@@ -179,6 +180,100 @@ int oracle_state_update(int64_t batch, int64_t dim, int64_t dstate, int dtype, d
       y[i_bd] = yt;
     }
   }
+  return 0;
+}
+
+/* ---------------------------------------------------------------------------
+ * Backward pass of the scan: the gradients of L = sum_{b,t,d} dy[b,t,d] *
+ * y[b,t,d] with respect to every input, by the adjoint of the recurrence.
+ * The forward states are recomputed (the pages' backward recomputes Abar and
+ * Bbar instead of storing the O(BLDN) intermediates: "mamba->jamba" sec. 2.3,
+ * hardware-aware algorithm).  For one channel, with g_t = dL/dh_t:
+ *
+ *   y0_t = sum_n C_t[n] h_t[n] + D x_t,  y_t = y0_t * silu(z_t)
+ *   dy0_t = dy_t * silu(z_t);   dz_t = dy_t * y0_t * silu'(z_t)
+ *   g_t[n] = dy0_t C_t[n] + abar_{t+1}[n] g_{t+1}[n]      (g_L = 0)
+ *   dC_t[n] += dy0_t h_t[n];  dD += dy0_t x_t
+ *   dB_t[n] += g_t[n] dt_t x_t
+ *   dx_t    = dy0_t D + sum_n g_t[n] dt_t B_t[n]
+ *   ddt_t   = sum_n g_t[n] (B_t[n] x_t + A[n] abar_t[n] h_{t-1}[n])
+ *   dA[n]  += g_t[n] dt_t abar_t[n] h_{t-1}[n]
+ *   ddelta_t = ddt_t * (softplus ? sigmoid(delta_t + bias) : 1);  dbias += ddelta_t
+ *
+ * dy: (batch, L, dim) doubles.  Outputs (doubles, all written): dx, ddelta,
+ * dz (batch, L, dim) (dz only when z is given); dB, dC (batch, L, dstate);
+ * dA (dim, dstate); dD, ddelta_bias (dim) (only when D / delta_bias are
+ * given).  The state starts at zero; last_state is not differentiated.
+ * ------------------------------------------------------------------------- */
+static double sigmoid(double v) { return 1.0 / (1.0 + exp(-v)); }
+
+int oracle_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dtype, const void *x,
+                    const void *delta, const float *A, const void *B, const void *C, const float *Dskip,
+                    const void *z, const float *delta_bias, int delta_softplus, const double *dy, double *dx,
+                    double *ddelta, double *dA, double *dB, double *dC, double *dD, double *dz,
+                    double *ddelta_bias) {
+  if (batch < 0 || seqlen < 0 || dim < 0 || dstate < 1 || dstate > 1024) return -1;
+  if (!x || !delta || !A || !B || !C || !dy || !dx || !ddelta || !dA || !dB || !dC) return -1;
+  const int64_t L = seqlen, N = dstate;
+  for (int64_t i = 0; i < dim * N; ++i) dA[i] = 0.0;
+  for (int64_t i = 0; i < batch * L * N; ++i) dB[i] = dC[i] = 0.0;
+  if (dD) for (int64_t d = 0; d < dim; ++d) dD[d] = 0.0;
+  if (ddelta_bias) for (int64_t d = 0; d < dim; ++d) ddelta_bias[d] = 0.0;
+  double *hs = (double *)malloc(sizeof(double) * (size_t)(L + 1) * (size_t)N);  /* h_{-1}=0 .. h_{L-1} */
+  double *g = (double *)malloc(sizeof(double) * (size_t)N);
+  if (!hs || !g) { free(hs); free(g); return -1; }
+  for (int64_t b = 0; b < batch; ++b) {
+    for (int64_t d = 0; d < dim; ++d) {
+      /* forward: every state, h_t at hs[(t+1)*N] */
+      for (int64_t n = 0; n < N; ++n) hs[n] = 0.0;
+      for (int64_t t = 0; t < L; ++t) {
+        const int64_t i_td = (b * L + t) * dim + d, i_tn = (b * L + t) * N;
+        double v = load_elem(delta, dtype, i_td) + (delta_bias ? (double)delta_bias[d] : 0.0);
+        double dt = delta_softplus ? softplus(v) : v;
+        double xt = load_elem(x, dtype, i_td);
+        for (int64_t n = 0; n < N; ++n)
+          hs[(t + 1) * N + n] = exp(dt * (double)A[d * N + n]) * hs[t * N + n] +
+                                dt * load_elem(B, dtype, i_tn + n) * xt;
+      }
+      /* backward */
+      for (int64_t n = 0; n < N; ++n) g[n] = 0.0;
+      for (int64_t t = L - 1; t >= 0; --t) {
+        const int64_t i_td = (b * L + t) * dim + d, i_tn = (b * L + t) * N;
+        double v = load_elem(delta, dtype, i_td) + (delta_bias ? (double)delta_bias[d] : 0.0);
+        double dt = delta_softplus ? softplus(v) : v;
+        double xt = load_elem(x, dtype, i_td);
+        const double *h = hs + (t + 1) * N, *hp = hs + t * N;
+        double y0 = Dskip ? (double)Dskip[d] * xt : 0.0;
+        for (int64_t n = 0; n < N; ++n) y0 += load_elem(C, dtype, i_tn + n) * h[n];
+        double dy0 = dy[i_td];
+        if (z) {
+          double zt = load_elem(z, dtype, i_td), sg = sigmoid(zt);
+          dz[i_td] = dy[i_td] * y0 * (sg + zt * sg * (1.0 - sg));
+          dy0 = dy[i_td] * zt * sg;
+        }
+        double dxt = Dskip ? dy0 * (double)Dskip[d] : 0.0, ddt = 0.0;
+        if (dD) dD[d] += dy0 * xt;
+        for (int64_t n = 0; n < N; ++n) {
+          /* g holds g_{t+1} * abar_{t+1} from the step after; add this step's read-out */
+          const double Bn = load_elem(B, dtype, i_tn + n), Cn = load_elem(C, dtype, i_tn + n);
+          const double an = (double)A[d * N + n], abar = exp(dt * an);
+          g[n] += dy0 * Cn;
+          dC[i_tn + n] += dy0 * h[n];
+          dB[i_tn + n] += g[n] * dt * xt;
+          dxt += g[n] * dt * Bn;
+          ddt += g[n] * (Bn * xt + an * abar * hp[n]);
+          dA[d * N + n] += g[n] * dt * abar * hp[n];
+          g[n] *= abar; /* carried to step t-1 */
+        }
+        dx[i_td] = dxt;
+        const double dd = delta_softplus ? ddt * sigmoid(v) : ddt;
+        ddelta[i_td] = dd;
+        if (ddelta_bias) ddelta_bias[d] += dd;
+      }
+    }
+  }
+  free(hs);
+  free(g);
   return 0;
 }
 

@@ -440,8 +440,64 @@ def pin_conv_causality(o):
     assert np.all(np.abs(y2[:, 6] - y[:, 6]) > 0), "the changed step must move its own output"
 
 
+# ----------------------------------------------------------------------------------------------
+# the backward pass: central finite differences of sum(dy * y) through the (pinned) forward
+# ----------------------------------------------------------------------------------------------
+def _fd_grad(o, c, dy, name, eps):
+    """Central differences of sum(dy * y) w.r.t. every element of c[name]."""
+    base = c[name]
+    grad = np.zeros(base.shape)
+    flat = grad.reshape(-1)
+    for i in range(base.size):
+        up, dn = base.copy(), base.copy()
+        up.reshape(-1)[i] += eps
+        dn.reshape(-1)[i] -= eps
+        # parameters are stored in fp32: use the perturbation the storage actually holds
+        h = float(up.reshape(-1)[i]) - float(dn.reshape(-1)[i])
+        yu, _ = _scan(o, c, **{name: up})
+        yd, _ = _scan(o, c, **{name: dn})
+        flat[i] = float(np.sum(dy * (yu - yd))) / h
+    return grad
+
+
+def pin_backward_finite_differences(o):
+    """Every gradient of the adjoint oracle matches central finite differences of the forward
+    oracle (fp64 for the activations, the fp32-representable step for A, D and the bias)."""
+    for seed, softplus, z, D, bias in ((21, True, True, True, True), (22, False, False, True, False),
+                                        (23, True, True, False, False)):
+        c = _rand_case(seed, batch=2, L=5, dim=3, N=3, softplus=softplus, bias=bias, z=z, D=D)
+        dy = np.random.default_rng(seed + 100).normal(size=c["x"].shape)
+        g = o.scan_bwd(c["x"], c["delta"], c["A"], c["B"], c["C"], dy, D=c["D"], z=c["z"],
+                       delta_bias=c["delta_bias"], delta_softplus=softplus)
+        checks = [("x", "dx", 1e-6, 1e-6), ("delta", "ddelta", 1e-6, 1e-6), ("B", "dB", 1e-6, 1e-6),
+                  ("C", "dC", 1e-6, 1e-6), ("A", "dA", 1e-3, 1e-5)]
+        if z:
+            checks.append(("z", "dz", 1e-6, 1e-6))
+        if D:
+            checks.append(("D", "dD", 1e-3, 1e-5))
+        if bias:
+            checks.append(("delta_bias", "ddelta_bias", 1e-3, 1e-5))
+        for name, gname, eps, rtol in checks:
+            fd = _fd_grad(o, c, dy, name, eps)
+            _close(g[gname], fd, rtol, f"d{name} (seed {seed})")
+
+
+def pin_backward_linear_in_dy(o):
+    """The gradients are linear in dy."""
+    c = _rand_case(31, batch=1, L=6, dim=2, N=3)
+    g = np.random.default_rng(32)
+    dy1, dy2 = g.normal(size=c["x"].shape), g.normal(size=c["x"].shape)
+    kw = dict(D=c["D"], z=c["z"], delta_bias=c["delta_bias"], delta_softplus=True)
+    r1 = o.scan_bwd(c["x"], c["delta"], c["A"], c["B"], c["C"], dy1, **kw)
+    r2 = o.scan_bwd(c["x"], c["delta"], c["A"], c["B"], c["C"], dy2, **kw)
+    r3 = o.scan_bwd(c["x"], c["delta"], c["A"], c["B"], c["C"], 2.0 * dy1 - 3.0 * dy2, **kw)
+    for k in r1:
+        _close(r3[k], 2.0 * r1[k] - 3.0 * r2[k], 1e-12, f"linearity of {k}")
+
+
 ALL_PINS = [pin_worked_examples, pin_unrolled_sum, pin_lti_convolution, pin_linearity,
             pin_channel_independence, pin_causality, pin_zero_step, pin_impulse_long_carry,
             pin_decode_equals_scan, pin_associative_scan, pin_special_values, pin_storage_widening,
             pin_channel_selection, pin_conv_library_convolution, pin_conv_impulse, pin_conv_silu,
-            pin_conv_chaining, pin_conv_decode_equals_fwd, pin_conv_causality]
+            pin_conv_chaining, pin_conv_decode_equals_fwd, pin_conv_causality, pin_backward_finite_differences,
+            pin_backward_linear_in_dy]

@@ -48,6 +48,14 @@ MUTANTS = [
     ("conv_final_state_first_inputs", "const int64_t s = seqlen - (K - 1) + j;", "const int64_t s = j;"),
     ("conv_update_newest_first", "acc += (double)w[d * K + k] * st[k];", "acc += (double)w[d * K + k] * st[K - 2 - k];"),
     ("conv_update_no_shift", "for (int64_t k = 0; k + 1 < K - 1; ++k) st[k] = st[k + 1];", ""),
+    ("bwd_adjoint_not_decayed", "          g[n] *= abar; /* carried to step t-1 */", ""),
+    ("bwd_dA_without_dt", "dA[d * N + n] += g[n] * dt * abar * hp[n];", "dA[d * N + n] += g[n] * abar * hp[n];"),
+    ("bwd_ddt_uses_new_state", "ddt += g[n] * (Bn * xt + an * abar * hp[n]);", "ddt += g[n] * (Bn * xt + an * abar * h[n]);"),
+    ("bwd_dz_without_silu_slope", "dz[i_td] = dy[i_td] * y0 * (sg + zt * sg * (1.0 - sg));", "dz[i_td] = dy[i_td] * y0 * sg;"),
+    ("bwd_dx_without_skip", "double dxt = Dskip ? dy0 * (double)Dskip[d] : 0.0, ddt = 0.0;", "double dxt = 0.0, ddt = 0.0;"),
+    ("bwd_no_softplus_slope", "const double dd = delta_softplus ? ddt * sigmoid(v) : ddt;", "const double dd = ddt;"),
+    ("bwd_dB_without_dt", "dB[i_tn + n] += g[n] * dt * xt;", "dB[i_tn + n] += g[n] * xt;"),
+    ("bwd_dC_uses_old_state", "dC[i_tn + n] += dy0 * h[n];", "dC[i_tn + n] += dy0 * hp[n];"),
     ("conv_silu_skipped", "out[(b * seqlen + t) * dim + d] = apply_silu ? silu(acc) : acc;",
      "out[(b * seqlen + t) * dim + d] = acc;"),
 ]
