@@ -157,6 +157,32 @@ SSM_API ssm_status_t ssm_state_update(int64_t batch, int64_t dim, int64_t dstate
                               void *stream);
 
 /*
+ * Backward pass of ssm_scan_fwd (zero initial state): the gradients of
+ * sum(dy * y) with respect to every input.  The forward states are
+ * recomputed, never stored per step ("mamba->jamba" sec. 2.3: the backward
+ * recomputes Abar and Bbar, as FlashAttention recomputes its scores).
+ *
+ *   inputs: as ssm_scan_fwd, plus dy (batch, seqlen, dim) dtype
+ *   dx, ddelta, dz (batch, seqlen, dim) dtype;  dB, dC (batch, seqlen, dstate) dtype
+ *   dA (dim, dstate), dD (dim), ddelta_bias (dim) fp32
+ *   dz is required when z is given (else ignored), dD when D is given,
+ *   ddelta_bias when delta_bias is given; ddelta is the gradient with respect
+ *   to the raw delta (before bias and softplus).
+ *
+ * dstate must be 1, 2, 4, 8 or 16.  last_state is not differentiated.  The
+ * channel sums of dB / dC and the batch sums of dA / dD / ddelta_bias are
+ * taken in a fixed order, so the result does not vary from run to run.
+ * Scratch: batch*ceil(seqlen/16)*dstate*dim + 2*ceil(dim/64)*batch*seqlen*dstate
+ * + batch*dstate*dim + 32*batch*dim fp32, in the same per-(device, stream)
+ * buffer as the split-sequence scan (same rules as ssm_scan_fwd).
+ */
+SSM_API ssm_status_t ssm_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, ssm_dtype_t dtype,
+                                  const void *x, const void *delta, const float *A, const void *B, const void *C,
+                                  const float *D, const void *z, const float *delta_bias, int delta_softplus,
+                                  const void *dy, void *dx, void *ddelta, float *dA, void *dB, void *dC, float *dD,
+                                  void *dz, float *ddelta_bias, void *stream);
+
+/*
  * Depthwise causal convolution that feeds the scan in the Mamba block
  * ("Mamba 论文精读" sec. 3.4, MambaBlock: Conv1d with one group per channel,
  * kernel width K and K-1 zeros of padding, the first L outputs kept, then

@@ -28,7 +28,7 @@ LIBRARY = os.path.join(_HERE, "libssm61.so")
 SSM_F32, SSM_BF16 = 0, 1
 STATUS_NAMES = {0: "SSM_OK", 1: "SSM_ERR_INVALID_ARG", 2: "SSM_ERR_UNSUPPORTED", 3: "SSM_ERR_MISALIGNED",
                 4: "SSM_ERR_HIP"}
-EXPORTED = ("ssm_scan_fwd", "ssm_scan_fwd_ex", "ssm_state_update", "ssm_causal_conv1d_fwd",
+EXPORTED = ("ssm_scan_fwd", "ssm_scan_fwd_ex", "ssm_scan_bwd", "ssm_state_update", "ssm_causal_conv1d_fwd",
             "ssm_causal_conv1d_update", "ssm_status_string", "ssm_last_error", "ssm_abi_version")
 
 
@@ -61,6 +61,9 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
     lib.ssm_scan_fwd_ex.restype = i32
     lib.ssm_state_update.argtypes = [i64, i64, i64, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp]
     lib.ssm_state_update.restype = i32
+    lib.ssm_scan_bwd.argtypes = [i64, i64, i64, i64, i32, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp,
+                                 vp, vp, vp, vp]
+    lib.ssm_scan_bwd.restype = i32
     lib.ssm_causal_conv1d_fwd.argtypes = [i64, i64, i64, i64, i32, vp, vp, vp, vp, i32, vp, vp, vp]
     lib.ssm_causal_conv1d_fwd.restype = i32
     lib.ssm_causal_conv1d_update.argtypes = [i64, i64, i64, i32, vp, vp, vp, vp, i32, vp, vp]
@@ -184,6 +187,42 @@ def ssm_state_update(state: torch.Tensor, x: torch.Tensor, delta: torch.Tensor, 
     return y
 
 
+def ssm_scan_bwd(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Tensor, C: torch.Tensor,
+                 dy: torch.Tensor, D: Optional[torch.Tensor] = None, z: Optional[torch.Tensor] = None,
+                 delta_bias: Optional[torch.Tensor] = None, delta_softplus: bool = False,
+                 stream=None) -> dict:
+    """Backward of ssm_scan_fwd (include/ssm.h: ssm_scan_bwd): gradients of sum(dy * y).
+    Returns a dict with dx, ddelta, dB, dC (x's dtype), dA (fp32), and dz / dD / ddelta_bias
+    (None unless z / D / delta_bias were given)."""
+    lib = load_library()
+    if x.dim() != 3 or A.dim() != 2:
+        raise ValueError("x must be (batch, seqlen, dim) and A (dim, dstate)")
+    batch, seqlen, dim = x.shape
+    dstate = A.shape[1]
+    dev, dt = x.device, x.dtype
+    code = _dtype_code(x)
+    _need(delta, "delta", (batch, seqlen, dim), dt, dev)
+    _need(A, "A", (dim, dstate), torch.float32, dev)
+    _need(B, "B", (batch, seqlen, dstate), dt, dev)
+    _need(C, "C", (batch, seqlen, dstate), dt, dev)
+    _need(dy, "dy", (batch, seqlen, dim), dt, dev)
+    _need(D, "D", (dim,), torch.float32, dev, optional=True)
+    _need(z, "z", (batch, seqlen, dim), dt, dev, optional=True)
+    _need(delta_bias, "delta_bias", (dim,), torch.float32, dev, optional=True)
+    out = {"dx": torch.empty_like(x), "ddelta": torch.empty_like(x), "dB": torch.empty_like(B),
+           "dC": torch.empty_like(C), "dA": torch.empty((dim, dstate), dtype=torch.float32, device=dev),
+           "dz": torch.empty_like(x) if z is not None else None,
+           "dD": torch.empty((dim,), dtype=torch.float32, device=dev) if D is not None else None,
+           "ddelta_bias": torch.empty((dim,), dtype=torch.float32, device=dev) if delta_bias is not None else None}
+    status = lib.ssm_scan_bwd(batch, seqlen, dim, dstate, code, _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C),
+                              _ptr(D), _ptr(z), _ptr(delta_bias), int(bool(delta_softplus)), _ptr(dy),
+                              _ptr(out["dx"]), _ptr(out["ddelta"]), _ptr(out["dA"]), _ptr(out["dB"]),
+                              _ptr(out["dC"]), _ptr(out["dD"]), _ptr(out["dz"]), _ptr(out["ddelta_bias"]),
+                              _stream(dev, stream))
+    _check(status)
+    return out
+
+
 def ssm_causal_conv1d_fwd(x: torch.Tensor, weight: torch.Tensor, bias: Optional[torch.Tensor] = None,
                           initial_state: Optional[torch.Tensor] = None, silu: bool = True, *,
                           y: Optional[torch.Tensor] = None, final_state: Optional[torch.Tensor] = None,
@@ -244,5 +283,5 @@ def abi_version() -> int:
     return load_library().ssm_abi_version()
 
 
-__all__ = ["ssm_scan_fwd", "ssm_state_update", "ssm_causal_conv1d_fwd", "ssm_causal_conv1d_update", "abi_version", "load_library", "SsmError", "ScanOpts",
+__all__ = ["ssm_scan_fwd", "ssm_scan_bwd", "ssm_state_update", "ssm_causal_conv1d_fwd", "ssm_causal_conv1d_update", "abi_version", "load_library", "SsmError", "ScanOpts",
            "LIBRARY", "EXPORTED"]

@@ -11,7 +11,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIBRARY = os.path.join(HERE, "libssm61.so")
 SOURCES = [os.path.join(CSRC, f) for f in ("ssm_api.hip", "scan_f32.hip", "scan_bf16.hip")]
 HEADERS = [os.path.join(CSRC, f) for f in ("ssm_device.hpp", "scan_fwd.hpp", "scan_table.hpp", "state_update.hpp",
-                                                  "conv1d.hpp")] + [
+                                                  "conv1d.hpp", "scan_bwd.hpp")] + [
     os.path.join(os.path.dirname(HERE), "include", "ssm.h")]
 OBJDIR = os.path.join(HERE, "_build")
 ARCH = "gfx950"

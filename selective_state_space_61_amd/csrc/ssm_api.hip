@@ -13,6 +13,7 @@
 #include "scan_table.hpp"
 #include "state_update.hpp"
 #include "conv1d.hpp"
+#include "scan_bwd.hpp"
 
 namespace {
 
@@ -101,6 +102,22 @@ CarryKernel carry_kernel(int64_t n) {
     case 16: return ssm::scan_carry_kernel<16>;
     case 32: return ssm::scan_carry_kernel<32>;
     case 64: return ssm::scan_carry_kernel<64>;
+    default: return nullptr;
+  }
+}
+
+using BwdKernel = void (*)(const ssm::BwdArgs);
+using BwdReduceKernel = void (*)(const ssm::BwdReduceArgs);
+
+// backward instantiations: chains per lane min(N, 4), so at most 4 scan waves for N <= 16
+template <bool BF16>
+BwdKernel bwd_kernel(int64_t n) {
+  switch (n) {
+    case 1: return ssm::scan_bwd_kernel<BF16, 1, 1>;
+    case 2: return ssm::scan_bwd_kernel<BF16, 2, 2>;
+    case 4: return ssm::scan_bwd_kernel<BF16, 4, 4>;
+    case 8: return ssm::scan_bwd_kernel<BF16, 8, 4>;
+    case 16: return ssm::scan_bwd_kernel<BF16, 16, 4>;
     default: return nullptr;
   }
 }
@@ -400,6 +417,99 @@ ssm_status_t ssm_state_update(int64_t batch, int64_t dim, int64_t dstate, ssm_dt
   hipLaunchKernelGGL(k, dim3(static_cast<unsigned>(blocks)), dim3(ssm::kUpdateThreads), 0,
                      static_cast<hipStream_t>(stream), a);
   return check_launch("state update");
+}
+
+ssm_status_t ssm_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, ssm_dtype_t dtype,
+                          const void* x, const void* delta, const float* A, const void* B, const void* C,
+                          const float* D, const void* z, const float* delta_bias, int delta_softplus,
+                          const void* dy, void* dx, void* ddelta, float* dA, void* dB, void* dC, float* dD,
+                          void* dz, float* ddelta_bias, void* stream) {
+  g_err[0] = '\0';
+  if (batch < 0 || seqlen < 0 || dim < 0 || dstate < 0)
+    return fail(SSM_ERR_INVALID_ARG, "negative size (batch=%lld seqlen=%lld dim=%lld dstate=%lld)",
+                (long long)batch, (long long)seqlen, (long long)dim, (long long)dstate);
+  if (dtype != SSM_F32 && dtype != SSM_BF16) return fail(SSM_ERR_UNSUPPORTED, "unknown dtype %d", (int)dtype);
+  if (dstate != 1 && dstate != 2 && dstate != 4 && dstate != 8 && dstate != 16)
+    return fail(SSM_ERR_UNSUPPORTED, "dstate %lld not in {1,2,4,8,16} for the backward pass", (long long)dstate);
+  const int64_t es = dtype == SSM_BF16 ? 2 : 4;
+  int64_t nch, n_bl, n_bld, n_bln;
+  if (!mul_ok(batch, dim, &nch) || !mul_ok(batch, seqlen, &n_bl) || !mul_ok(n_bl, dim * es, &n_bld) ||
+      !mul_ok(n_bl, dstate * es, &n_bln) || n_bld > (int64_t{1} << 46))
+    return fail(SSM_ERR_INVALID_ARG, "tensor size overflows int64");
+  if (dim == 0 || dstate == 0) return SSM_OK;
+  if (!dA || (D && !dD) || (delta_bias && !ddelta_bias))
+    return fail(SSM_ERR_INVALID_ARG, "NULL gradient for a given parameter (dA; dD when D; ddelta_bias when delta_bias)");
+  const bool empty = batch == 0 || seqlen == 0;
+  if (!empty && (!x || !delta || !A || !B || !C || !dy || !dx || !ddelta || !dB || !dC || (z && !dz)))
+    return fail(SSM_ERR_INVALID_ARG, "NULL required pointer (x, delta, A, B, C, dy, dx, ddelta, dB, dC; dz when z)");
+  const Arg args[] = {{x, es, "x"}, {delta, es, "delta"}, {A, 4, "A"}, {B, es, "B"}, {C, es, "C"}, {D, 4, "D"},
+                      {z, es, "z"}, {delta_bias, 4, "delta_bias"}, {dy, es, "dy"}, {dx, es, "dx"},
+                      {ddelta, es, "ddelta"}, {dA, 4, "dA"}, {dB, es, "dB"}, {dC, es, "dC"}, {dD, 4, "dD"},
+                      {dz, es, "dz"}, {ddelta_bias, 4, "ddelta_bias"}};
+  if (const Arg* bad = misaligned(args, sizeof args / sizeof args[0]))
+    return fail(SSM_ERR_MISALIGNED, "%s (%p) is not aligned to its element size", bad->name, bad->p);
+  if (dtype == SSM_BF16 && !empty && !(aligned(B, 4) && aligned(C, 4)))
+    return fail(SSM_ERR_MISALIGNED, "bf16 B and C must be 4-byte aligned");
+  const Range ins[] = {{x, n_bld}, {delta, n_bld}, {z, n_bld}, {dy, n_bld}, {B, n_bln}, {C, n_bln},
+                       {A, dim * dstate * 4}, {D, dim * 4}, {delta_bias, dim * 4}};
+  const Range outs[] = {{dx, n_bld}, {ddelta, n_bld}, {dz, n_bld}, {dB, n_bln}, {dC, n_bln},
+                        {dA, dim * dstate * 4}, {dD, dim * 4}, {ddelta_bias, dim * 4}};
+  for (const Range& o : outs) {
+    for (const Range& i : ins)
+      if (overlap(o, i)) return fail(SSM_ERR_INVALID_ARG, "an output overlaps an input");
+    for (const Range& o2 : outs)
+      if (&o2 != &o && overlap(o, o2)) return fail(SSM_ERR_INVALID_ARG, "two outputs overlap");
+  }
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int64_t T = ssm::kBwdChunk;
+  const int64_t nc = empty ? 0 : (seqlen + T - 1) / T;
+  const int64_t ncb = (dim + 63) / 64;
+  // scratch: chunk-start states, dB/dC channel-block partials, dA / dD / dbias batch partials
+  const int64_t n_h = batch * nc * dstate * dim;
+  const int64_t n_bc = 2 * ncb * batch * seqlen * dstate;
+  const int64_t n_a = batch * dstate * dim;
+  const int64_t n_d = batch * T * dim;
+  float* scratch = nullptr;
+  ssm_status_t s = get_scratch(st, n_h + n_bc + n_a + 2 * n_d + 1, &scratch);
+  if (s != SSM_OK) return s;
+  ssm::BwdArgs a{};
+  a.x = x; a.delta = delta; a.A = A; a.B = B; a.C = C; a.Dskip = D; a.z = z; a.delta_bias = delta_bias; a.dy = dy;
+  a.dx = dx; a.ddelta = ddelta; a.dz = dz;
+  a.hstart = scratch;
+  a.part_bc = scratch + n_h;
+  a.part_a = a.part_bc + n_bc;
+  a.part_d = a.part_a + n_a;
+  a.part_bias = a.part_d + n_d;
+  a.batch = batch; a.seqlen = seqlen; a.dim = dim; a.nc = nc;
+  a.ncb = static_cast<int32_t>(ncb);
+  a.softplus = delta_softplus ? 1 : 0;
+  const int64_t vbytes = 4 * es;  // the IO waves move 4 channels per access
+  a.vec_ok = (dim % 4 == 0) && aligned(x, vbytes) && aligned(delta, vbytes) && aligned(dy, vbytes) &&
+             aligned(dx, vbytes) && aligned(ddelta, vbytes) && (!z || (aligned(z, vbytes) && aligned(dz, vbytes)));
+  const int npl = dstate < 4 ? static_cast<int>(dstate) : 4;
+  const unsigned threads = static_cast<unsigned>(64 * (dstate / npl + ssm::kBwdIoWaves));
+  if (!empty) {
+    if (batch * ncb > 0x7fffffff) return fail(SSM_ERR_UNSUPPORTED, "grid too large");
+    const BwdKernel k = dtype == SSM_BF16 ? bwd_kernel<true>(dstate) : bwd_kernel<false>(dstate);
+    hipLaunchKernelGGL(k, dim3(static_cast<unsigned>(batch * ncb)), dim3(threads), 0, st, a);
+    if ((s = check_launch("scan backward")) != SSM_OK) return s;
+  } else if (n_a + 2 * n_d > 0) {
+    // nothing flows back: the parameter gradients are zero
+    hipLaunchKernelGGL(fill_zero_kernel, dim3(static_cast<unsigned>((n_a + 2 * n_d + 255) / 256)), dim3(256), 0,
+                       st, a.part_a, n_a + 2 * n_d);
+    if ((s = check_launch("fill_zero_kernel")) != SSM_OK) return s;
+  }
+  ssm::BwdReduceArgs r{};
+  r.part_bc = a.part_bc; r.part_a = a.part_a; r.part_d = a.part_d; r.part_bias = a.part_bias;
+  r.dB = dB; r.dC = dC; r.dA = dA; r.dD = dD; r.dbias = ddelta_bias;
+  r.batch = batch; r.seqlen = seqlen; r.dim = dim; r.N = static_cast<int32_t>(dstate);
+  r.ncb = static_cast<int32_t>(ncb);
+  const int64_t nred = 2 * batch * seqlen * dstate + dim * dstate + dim;
+  const BwdReduceKernel rk =
+      dtype == SSM_BF16 ? ssm::scan_bwd_reduce_kernel<true> : ssm::scan_bwd_reduce_kernel<false>;
+  hipLaunchKernelGGL(rk, dim3(static_cast<unsigned>((nred + 255) / 256)), dim3(256), 0, st, r);
+  return check_launch("scan backward reduce");
 }
 
 ssm_status_t ssm_causal_conv1d_fwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t width, ssm_dtype_t dtype,
