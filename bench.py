@@ -248,6 +248,37 @@ def bench_conv(steps, warmup, torch, np, W, ssm, device):
     return res
 
 
+def bench_scan_bwd(steps, warmup, torch, np, W, ssm, device):
+    """The backward scan on the 130M-shaped layer (inputs, dy and gradients resident in HBM;
+    two input sets rotated).  Reports the time per call of the whole backward (both kernels)."""
+    w = W.WORKLOADS["mamba130m"]
+    t = W.workload_inputs(w)
+    g = np.random.default_rng(61)
+    dy = W.f32_to_bf16_bits(g.standard_normal((w.batch, w.seqlen, w.dim)).astype(np.float32))
+    sets = []
+    for _ in range(2):
+        d = {k: dev_tensor(v, torch, np, device) for k, v in t.items()}
+        d["dy"] = dev_tensor(dy, torch, np, device)
+        sets.append(d)
+
+    def call(i):
+        d = sets[i % 2]
+        ssm.ssm_scan_bwd(d["x"], d["delta"], d["A"], d["B"], d["C"], d["dy"], D=d["D"], z=d["z"],
+                         delta_bias=d["delta_bias"], delta_softplus=True)
+
+    total_ms, per = time_calls(torch, call, steps, warmup)
+    ms = sum(per) / len(per)
+    elems = w.batch * w.seqlen * w.dim
+    updates = elems * w.dstate
+    # algorithmic bytes: x, delta, z, dy read; dx, ddelta, dz written; B, C read, dB, dC written
+    alg = elems * 2 * 7 + 4 * w.batch * w.seqlen * w.dstate * 2 + 4 * w.dim * w.dstate * 2
+    del sets
+    torch.cuda.empty_cache()
+    return {"workload": "mamba130m", "ms_per_call": ms, "elems_per_s": elems / (ms * 1e-3),
+            "updates_per_s": updates / (ms * 1e-3), "alg_bytes": alg, "hbm_gbps": alg / (ms * 1e-3) / 1e9,
+            "fwd_equiv": None}
+
+
 def bench_conv_update(steps, torch, np, W, ssm, device):
     """The one-token convolution on the decode shape (64 x 5120, width 4, bf16), one call per
     step on a ring of 26 conv states, captured as one HIP graph and replayed."""
@@ -345,6 +376,9 @@ def profile_mode(args):
         res = bench_decode(args.steps, torch, np, W, ssm, torch.device("cuda:0"), ring=26)
     elif args.workload == "conv":
         res = bench_conv(args.steps, args.warmup, torch, np, W, ssm, torch.device("cuda:0"))
+    elif args.workload == "bwd":
+        res = bench_scan_bwd(args.steps, args.warmup, torch, np, W, ssm, torch.device("cuda:0"))
+        res["kernel_ms"] = res["ms_per_call"]
     else:
         res = bench_scan(args.workload, args.steps, args.warmup, torch, np, W, ssm, torch.device("cuda:0"))
     log(f"[profile] {args.workload}: {res['kernel_ms'] * 1e3:.1f} us/launch over {args.steps} launches")
@@ -401,7 +435,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="mamba130m",
-                    choices=["mamba130m", "mamba2p8b", "genomics", "decode", "conv"])
+                    choices=["mamba130m", "mamba2p8b", "genomics", "decode", "conv", "bwd"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the context measurements (2.8B scan, decode)")
     ap.add_argument("--profile-mode", action="store_true",
@@ -429,7 +463,7 @@ def main():
     import selective_state_space_61_amd as ssm
     from selective_state_space_61_amd import build as hip_build
 
-    if args.workload in ("decode", "conv"):
+    if args.workload in ("decode", "conv", "bwd"):
         raise SystemExit(f"{args.workload} is measured as context next to a scan workload; use --profile-mode for it alone")
     if not os.path.exists(ssm.LIBRARY):
         hip_build.build(verbose=True)
@@ -450,6 +484,10 @@ def main():
         extra["decode_mall_resident"] = bench_decode(256, torch, np, W, ssm, device, ring=1)
         extra["decode_hbm_ring26"] = bench_decode(256, torch, np, W, ssm, device, ring=26)
         log(f"[bench] decode: {extra['decode_hbm_ring26']['updates_per_s']:.3e} updates/s (ring of 26 states)")
+        extra["scan_bwd"] = bench_scan_bwd(max(6, args.steps // 5), 2, torch, np, W, ssm, device)
+        extra["scan_bwd"]["fwd_equiv"] = extra["scan_bwd"]["ms_per_call"] / main_res["kernel_ms"]
+        log(f"[bench] scan backward (130M shape): {extra['scan_bwd']['ms_per_call'] * 1e3:.1f} us/call "
+            f"({extra['scan_bwd']['fwd_equiv']:.2f}x the forward)")
         extra["causal_conv1d"] = bench_conv(max(10, args.steps // 2), 3, torch, np, W, ssm, device)
         extra["causal_conv1d"]["traffic"] = traffic_from_profiles("conv", extra["causal_conv1d"]["alg_bytes"])[0]
         log(f"[bench] causal conv1d: {extra['causal_conv1d']['kernel_ms'] * 1e3:.1f} us/launch, "

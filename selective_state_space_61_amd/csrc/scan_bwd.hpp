@@ -61,7 +61,7 @@ struct BwdArgs {
 
 constexpr int kBwdChunk = 16;
 constexpr int kBwdIoWaves = 4;
-// steps per dB / dC reduction round: 2 NPL values per step and lane, one column per lane
+// steps per dB / dC reduction round: 2 NPL values per step and lane, at most 64 rows per round
 template <int NPL>
 constexpr int kBwdHalf = 32 / NPL < kBwdChunk ? 32 / NPL : kBwdChunk;
 
@@ -83,13 +83,13 @@ __global__ __launch_bounds__(64 * (N / NPL + kBwdIoWaves)) void scan_bwd_kernel(
   static_assert(TPR * T == IOT, "IO threads cover the chunk tile exactly once");
   constexpr int H = kBwdHalf<NPL>;
   constexpr int RED = 2 * NPL * H;  // dB and dC values per lane per reduction round
-  static_assert(RED <= 64 && T % H == 0, "one reduction column per lane, whole rounds per chunk");
+  static_assert(RED <= 64 && T % H == 0, "one reduction row per lane, whole rounds per chunk");
 
-  __shared__ float2 s_dw[T][64 + 2];        // (dt, dt x)
-  __shared__ float s_yp[G][T][64 + 4];      // read-out partials
-  __shared__ float s_dy0[T][64 + 2];        // dy * silu(z)
-  __shared__ float2 s_part[G][T][64 + 2];   // (dx, ddt) partials
-  __shared__ float s_red[G][64][RED + 1];   // per-wave transpose for the dB / dC channel sums
+  __shared__ float2 s_dw[2][T][64 + 2];               // (dt, dt x); phase 0 double-buffers
+  __shared__ float s_dy0[T][64 + 2];                  // dy * silu(z)
+  __shared__ float s_yp[G][T][64 + 4];                // read-out partials C_t.h_t
+  __shared__ float2 s_part[G][T][64 + 2];             // (sum_j g_j B_j, sum_j g_j A_j abar_j h_{t-1,j})
+  __shared__ __align__(16) float s_red[G][RED][64 + 4];  // per-wave transpose for dB / dC sums
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -103,6 +103,8 @@ __global__ __launch_bounds__(64 * (N / NPL + kBwdIoWaves)) void scan_bwd_kernel(
   const bool full_cols = p.vec_ok && (static_cast<int64_t>(cb) * 64 + 64 <= p.dim);
   auto chunk_full = [&](int64_t c) { return full_cols && (c + 1) * T <= L; };
 
+  // Barriers: phase 0 runs nc + 1 iterations with one barrier each; phase 1 runs nc chunks with
+  // two barriers each (after the IO staging, after the scan).  Both roles follow that count.
   if (wave < G) {
     // ===================================== scan role ==========================================
     const int64_t d_lane = static_cast<int64_t>(cb) * 64 + lane;
@@ -127,111 +129,115 @@ __global__ __launch_bounds__(64 * (N / NPL + kBwdIoWaves)) void scan_bwd_kernel(
       return p.hstart + ((b * nc + c) * N + n0 + j) * p.dim + d_lane;
     };
 
-    // ---- phase 0: forward, storing every chunk-start state ----------------------------------
-    for (int64_t c = 0; c < nc; ++c) {
-      if (lane_ok) {
+    // ---- phase 0: forward over chunk j-1 while the IO waves stage chunk j --------------------
+    BcRow<BF16, NPL> rb0, rc0;
+    if (nc > 0) load_bc(0, rb0, rc0);
+    for (int64_t j = 0; j <= nc; ++j) {
+      if (j >= 1) {
+        const int64_t c = j - 1;
+        const int sb = static_cast<int>(c & 1);
+        if (lane_ok) {
 #pragma unroll
-        for (int j = 0; j < NPL; ++j) *hstart(c, j) = h[j];
+          for (int q = 0; q < NPL; ++q) *hstart(c, q) = h[q];
+        }
+        float Bv[NPL];
+#pragma unroll
+        for (int q = 0; q < NPL; ++q) Bv[q] = rb0.get(q);
+        if (c + 1 < nc) load_bc(c + 1, rb0, rc0);
+        static_for<T>([&](auto K) {
+          constexpr int k = decltype(K)::value;
+          const float2 dw = s_dw[sb][k][lane];
+#pragma unroll
+          for (int q = 0; q < NPL; ++q)
+            h[q] = fmaf(hw_exp2(dw.x * A2[q]), h[q], row_bcast<k>(Bv[q]) * dw.y);
+        });
       }
-      BcRow<BF16, NPL> rb, rc;
-      load_bc(c, rb, rc);
-      __syncthreads();  // s_dw of chunk c is ready
-      float Bv[NPL];
-#pragma unroll
-      for (int j = 0; j < NPL; ++j) Bv[j] = rb.get(j);
-      static_for<T>([&](auto K) {
-        constexpr int k = decltype(K)::value;
-        const float2 dw = s_dw[k][lane];
-#pragma unroll
-        for (int j = 0; j < NPL; ++j) h[j] = fmaf(hw_exp2(dw.x * A2[j]), h[j], row_bcast<k>(Bv[j]) * dw.y);
-      });
-      __syncthreads();  // s_dw may be rewritten
+      __syncthreads();
     }
 
     // ---- phase 1: reverse ---------------------------------------------------------------------
     float g[NPL], an[NPL], dA[NPL];  // adjoint, abar of the step after, dA accumulator
 #pragma unroll
-    for (int j = 0; j < NPL; ++j) {
-      g[j] = 0.0f;
-      an[j] = 0.0f;
-      dA[j] = 0.0f;
+    for (int q = 0; q < NPL; ++q) {
+      g[q] = 0.0f;
+      an[q] = 0.0f;
+      dA[q] = 0.0f;
     }
     float* const red = &s_red[wave][0][0];
     for (int64_t c = nc - 1; c >= 0; --c) {
       BcRow<BF16, NPL> rb, rc;
       load_bc(c, rb, rc);
-      float Bv[NPL], Cv[NPL];
-#pragma unroll
-      for (int j = 0; j < NPL; ++j) {
-        Bv[j] = rb.get(j);
-        Cv[j] = rc.get(j);
-      }
       float hs[T + 1][NPL];  // hs[k] = state before step k of the chunk; hs[T] after its last step
 #pragma unroll
-      for (int j = 0; j < NPL; ++j) hs[0][j] = lane_ok ? *hstart(c, j) : 0.0f;
-      __syncthreads();  // (A) s_dw of chunk c is ready
-      // ---- B: recompute the chunk, read-out partials ----
+      for (int q = 0; q < NPL; ++q) hs[0][q] = lane_ok ? *hstart(c, q) : 0.0f;
+      __syncthreads();  // (1) the chunk's (dt, dt x) and dy0 are staged
+      float Bv[NPL], Cv[NPL];
+#pragma unroll
+      for (int q = 0; q < NPL; ++q) {
+        Bv[q] = rb.get(q);
+        Cv[q] = rc.get(q);
+      }
+      // recompute the chunk's states and read-out partials
       static_for<T>([&](auto K) {
         constexpr int k = decltype(K)::value;
-        const float2 dw = s_dw[k][lane];
+        const float2 dw = s_dw[0][k][lane];
         float yp = 0.0f;
 #pragma unroll
-        for (int j = 0; j < NPL; ++j) {
-          hs[k + 1][j] = fmaf(hw_exp2(dw.x * A2[j]), hs[k][j], row_bcast<k>(Bv[j]) * dw.y);
-          yp = fmaf(row_bcast<k>(Cv[j]), hs[k + 1][j], yp);
+        for (int q = 0; q < NPL; ++q) {
+          hs[k + 1][q] = fmaf(hw_exp2(dw.x * A2[q]), hs[k][q], row_bcast<k>(Bv[q]) * dw.y);
+          yp = fmaf(row_bcast<k>(Cv[q]), hs[k + 1][q], yp);
         }
         s_yp[wave][k][lane] = yp;
       });
-      __syncthreads();  // (B) partials ready
-      __syncthreads();  // (C) s_dy0 ready
-      // ---- D: reverse the chunk ----
+      // reverse the chunk, in rounds of H steps for the dB / dC channel sums
       static_for<T / H>([&](auto R) {
         constexpr int hf = T / H - 1 - decltype(R)::value;  // rounds in reverse
         static_for<H>([&](auto K) {
           constexpr int k = hf * H + H - 1 - decltype(K)::value;  // steps in reverse
-          constexpr int r = k - hf * H;                                   // row in the round
-          const float2 dw = s_dw[k][lane];
+          constexpr int r = k - hf * H;                             // step within the round
+          const float2 dw = s_dw[0][k][lane];
           const float dt = dw.x, w = dw.y;
           const float dy0 = s_dy0[k][lane];
-          float gB = 0.0f, pdt = 0.0f;  // sum_j g_j B_j; sum_j g_j A_j abar_j h_{t-1,j}
+          float gB = 0.0f, pdt = 0.0f;
 #pragma unroll
-          for (int j = 0; j < NPL; ++j) {
-            const float Bk = row_bcast<k>(Bv[j]), Ck = row_bcast<k>(Cv[j]);
-            const float a = hw_exp2(dt * A2[j]);  // abar_t
-            g[j] = fmaf(an[j], g[j], dy0 * Ck);    // g_t = dy0 C_t + abar_{t+1} g_{t+1}
-            const float ah = a * hs[k][j];         // abar_t h_{t-1}
-            red[lane * (RED + 1) + r * 2 * NPL + j] = g[j] * w;                  // dB: g dt x
-            red[lane * (RED + 1) + r * 2 * NPL + NPL + j] = dy0 * hs[k + 1][j];  // dC: dy0 h_t
-            gB = fmaf(g[j], Bk, gB);
-            pdt = fmaf(g[j] * Araw[j], ah, pdt);
-            dA[j] = fmaf(g[j] * dt, ah, dA[j]);
-            an[j] = a;
+          for (int q = 0; q < NPL; ++q) {
+            g[q] = fmaf(an[q], g[q], dy0 * row_bcast<k>(Cv[q]));  // g_t = dy0 C_t + abar_{t+1} g_{t+1}
+            const float a = hw_exp2(dt * A2[q]);                   // abar_t (recomputed)
+            const float ah = a * hs[k][q];                         // abar_t h_{t-1}
+            red[(r * 2 * NPL + q) * (64 + 4) + lane] = g[q] * w;                   // dB: g dt x
+            red[(r * 2 * NPL + NPL + q) * (64 + 4) + lane] = dy0 * hs[k + 1][q];  // dC: dy0 h_t
+            gB = fmaf(g[q], row_bcast<k>(Bv[q]), gB);
+            const float gah = g[q] * ah;
+            pdt = fmaf(gah, Araw[q], pdt);
+            dA[q] = fmaf(gah, dt, dA[q]);
+            an[q] = a;
           }
-          // dx partial = dt sum_j g_j B_j; ddt partial = sum_j g_j A_j abar_j h_{t-1,j}.  The
-          // x sum_j g_j B_j part of ddt is added by the IO waves, which hold x.
-          s_part[wave][k][lane] = make_float2(gB * dt, pdt);
-          s_yp[wave][k][lane] = gB;
+          s_part[wave][k][lane] = make_float2(gB, pdt);
         });
-        // channel sums of this round's dB / dC partials: lane l adds column l over the 64 lanes
+        // channel sums of this round's dB / dC values: lane q adds row q of the transpose
         wave_sync();
         if (lane < RED) {
-          float s = 0.0f;
-          for (int l = 0; l < 64; ++l) s += red[l * (RED + 1) + lane];
-          const int r = lane / (2 * NPL), q = lane % (2 * NPL);
+          const float4* rowp = reinterpret_cast<const float4*>(red + lane * (64 + 4));
+          float4 acc = rowp[0];
+#pragma unroll
+          for (int i = 1; i < 16; ++i) {
+            const float4 v = rowp[i];
+            acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+          }
+          const float sum = (acc.x + acc.y) + (acc.z + acc.w);
+          const int r = lane / (2 * NPL), qq = lane % (2 * NPL);
           const int64_t t = c * T + hf * H + r;
-          const int which = q < NPL ? 0 : 1;  // 0: dB, 1: dC
-          const int n = n0 + (q % NPL);
-          if (t < L)
-            p.part_bc[((((int64_t)which * p.ncb + cb) * p.batch + b) * L + t) * N + n] = s;
+          const int which = qq < NPL ? 0 : 1;  // 0: dB, 1: dC
+          const int n = n0 + (qq % NPL);
+          if (t < L) p.part_bc[((((int64_t)which * p.ncb + cb) * p.batch + b) * L + t) * N + n] = sum;
         }
         wave_sync();  // the next round rewrites the transpose buffer
       });
-      __syncthreads();  // (D) partials ready
-      __syncthreads();  // (E) IO done with s_dw, s_part
+      __syncthreads();  // (2) read-out and adjoint partials are ready
     }
     if (lane_ok) {
 #pragma unroll
-      for (int j = 0; j < NPL; ++j) p.part_a[(b * N + n0 + j) * p.dim + d_lane] = dA[j];
+      for (int q = 0; q < NPL; ++q) p.part_a[(b * N + n0 + q) * p.dim + d_lane] = dA[q];
     }
     return;
   }
@@ -249,98 +255,103 @@ __global__ __launch_bounds__(64 * (N / NPL + kBwdIoWaves)) void scan_bwd_kernel(
     dsk[v] = (p.Dskip && v < nvalid_col) ? p.Dskip[d_col + v] : 0.0f;
   }
   const bool has_z = p.z != nullptr;
-  // stages (dt, dt x) of chunk c into s_dw; returns the values it needs later
-  auto stage = [&](int64_t c, float (&xs)[VEC], float (&vs)[VEC], float (&dts)[VEC], bool& row_ok) {
+  // Raw tiles are loaded one chunk ahead of their use, so the global-load latency overlaps the
+  // scan waves' work on the current chunk.
+  struct Raw {
+    RawVec<BF16, VEC> x, d, z, dy;
+    int nv;
+  };
+  auto fetch = [&](int64_t c, Raw& r, bool grads) {
     const int64_t t = c * T + row;
-    row_ok = t < L;
-    const int nv = row_ok ? nvalid_col : 0;
+    r.nv = t < L ? nvalid_col : 0;
     const int64_t idx = (row_base + t) * p.dim + d_col;
     const bool vec = chunk_full(c);
-    RawVec<BF16, VEC> rx, rd;
-    rx.load(p.x, idx, nv, vec);
-    rd.load(p.delta, idx, nv, vec);
+    r.x.load(p.x, idx, r.nv, vec);
+    r.d.load(p.delta, idx, r.nv, vec);
+    if (grads) {
+      if (has_z) r.z.load(p.z, idx, r.nv, vec);
+      r.dy.load(p.dy, idx, r.nv, vec);
+    }
+  };
+  // (dt, dt x) of a fetched tile into s_dw[sb]; x and the pre-softplus value kept
+  auto stage = [&](const Raw& r, int sb, float (&xs)[VEC], float (&vs)[VEC]) {
 #pragma unroll
     for (int v = 0; v < VEC; ++v) {
-      const bool ok = v < nv;
-      xs[v] = ok ? rx.get(v) : 0.0f;
-      vs[v] = rd.get(v) + bias[v];
-      const float dt = p.softplus ? softplus_f32(vs[v]) : vs[v];
-      dts[v] = ok ? dt : 0.0f;
-      s_dw[row][col + v] = make_float2(dts[v], dts[v] * xs[v]);
+      const bool ok = v < r.nv;
+      xs[v] = ok ? r.x.get(v) : 0.0f;
+      vs[v] = r.d.get(v) + bias[v];
+      const float dt = ok ? (p.softplus ? softplus_f32(vs[v]) : vs[v]) : 0.0f;
+      s_dw[sb][row][col + v] = make_float2(dt, dt * xs[v]);
     }
   };
 
   // ---- phase 0 ----
-  for (int64_t c = 0; c < nc; ++c) {
-    float xs[VEC], vs[VEC], dts[VEC];
-    bool row_ok;
-    stage(c, xs, vs, dts, row_ok);
-    __syncthreads();
-    __syncthreads();
+  {
+    Raw cur;
+    if (nc > 0) fetch(0, cur, false);
+    for (int64_t j = 0; j <= nc; ++j) {
+      if (j < nc) {
+        float xs[VEC], vs[VEC];
+        stage(cur, static_cast<int>(j & 1), xs, vs);
+        if (j + 1 < nc) fetch(j + 1, cur, false);
+      }
+      __syncthreads();
+    }
   }
   // ---- phase 1 ----
   float accD[VEC], accBias[VEC];
 #pragma unroll
   for (int v = 0; v < VEC; ++v) accD[v] = accBias[v] = 0.0f;
+  Raw nxt;
+  if (nc > 0) fetch(nc - 1, nxt, true);
   for (int64_t c = nc - 1; c >= 0; --c) {
-    float xs[VEC], vs[VEC], dts[VEC];
-    bool row_ok;
-    stage(c, xs, vs, dts, row_ok);  // (A)
-    const int64_t t = c * T + row;
-    const int nv = row_ok ? nvalid_col : 0;
-    const int64_t idx = (row_base + t) * p.dim + d_col;
+    const Raw cur = nxt;
+    float xs[VEC], vs[VEC];
+    stage(cur, 0, xs, vs);
+    const int nv = cur.nv;
+    const int64_t idx = (row_base + c * T + row) * p.dim + d_col;
     const bool vec = chunk_full(c);
-    RawVec<BF16, VEC> rz, rdy;
-    if (has_z) rz.load(p.z, idx, nv, vec);
-    rdy.load(p.dy, idx, nv, vec);
-    __syncthreads();  // (A)
-    __syncthreads();  // (B) read-out partials ready
-    // ---- C ----
-    float dy0[VEC], dzv[VEC];
+    float dyv[VEC], zv[VEC], sg[VEC], dy0[VEC];
 #pragma unroll
     for (int v = 0; v < VEC; ++v) {
-      float y0 = fmaf(dsk[v], xs[v], s_yp[0][row][col + v]);
-#pragma unroll
-      for (int gw = 1; gw < G; ++gw) y0 += s_yp[gw][row][col + v];
-      const float dyv = v < nv ? rdy.get(v) : 0.0f;
+      dyv[v] = v < nv ? cur.dy.get(v) : 0.0f;
       if (has_z) {
-        const float zv = rz.get(v);
-        const float sg = hw_rcp(1.0f + hw_exp2(-zv * kLog2e));
-        dzv[v] = dyv * y0 * fmaf(zv * sg, 1.0f - sg, sg);
-        dy0[v] = dyv * zv * sg;
+        zv[v] = cur.z.get(v);
+        sg[v] = hw_rcp(1.0f + hw_exp2(-zv[v] * kLog2e));
+        dy0[v] = dyv[v] * zv[v] * sg[v];
       } else {
-        dzv[v] = 0.0f;
-        dy0[v] = dyv;
+        zv[v] = sg[v] = 0.0f;
+        dy0[v] = dyv[v];
       }
       accD[v] = fmaf(dy0[v], xs[v], accD[v]);
       s_dy0[row][col + v] = dy0[v];
     }
-    __syncthreads();  // (C)
-    __syncthreads();  // (D) partials ready
-    // ---- E ----
-    float dxo[VEC], ddo[VEC];
+    if (c > 0) fetch(c - 1, nxt, true);
+    __syncthreads();  // (1)
+    __syncthreads();  // (2) the scan waves' partials are ready
+    float dxo[VEC], ddo[VEC], dzo[VEC];
 #pragma unroll
     for (int v = 0; v < VEC; ++v) {
-      float dxv = dy0[v] * dsk[v], ddt = 0.0f, gB = 0.0f;
+      float y0 = dsk[v] * xs[v], gB = 0.0f, pdt = 0.0f;
 #pragma unroll
       for (int gw = 0; gw < G; ++gw) {
+        y0 += s_yp[gw][row][col + v];
         const float2 pr = s_part[gw][row][col + v];
-        dxv += pr.x;
-        ddt += pr.y;
-        gB += s_yp[gw][row][col + v];
+        gB += pr.x;
+        pdt += pr.y;
       }
-      ddt = fmaf(gB, xs[v], ddt);  // the B x term of ddt
-      const float dd = p.softplus ? ddt * hw_rcp(1.0f + hw_exp2(-vs[v] * kLog2e)) : ddt;
-      dxo[v] = dxv;
-      ddo[v] = dd;
-      if (v < nv) accBias[v] += dd;
+      const float dt = s_dw[0][row][col + v].x;
+      dzo[v] = has_z ? dyv[v] * y0 * fmaf(zv[v] * sg[v], 1.0f - sg[v], sg[v]) : 0.0f;
+      dxo[v] = fmaf(dy0[v], dsk[v], dt * gB);
+      const float ddt = fmaf(gB, xs[v], pdt);
+      ddo[v] = p.softplus ? ddt * hw_rcp(1.0f + hw_exp2(-vs[v] * kLog2e)) : ddt;
+      if (v < nv) accBias[v] += ddo[v];
     }
     if (nv > 0) {
       store_vec<BF16, VEC>(p.dx, idx, dxo, nv, vec);
       store_vec<BF16, VEC>(p.ddelta, idx, ddo, nv, vec);
-      if (has_z) store_vec<BF16, VEC>(p.dz, idx, dzv, nv, vec);
+      if (has_z) store_vec<BF16, VEC>(p.dz, idx, dzo, nv, vec);
     }
-    __syncthreads();  // (E)
   }
   // per-(batch row, tile row) partials of dD and dbias, summed by the reduce kernel
   if (nvalid_col > 0) {

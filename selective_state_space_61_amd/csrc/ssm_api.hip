@@ -110,6 +110,7 @@ using BwdKernel = void (*)(const ssm::BwdArgs);
 using BwdReduceKernel = void (*)(const ssm::BwdReduceArgs);
 
 // backward instantiations: chains per lane min(N, 4), so at most 4 scan waves for N <= 16
+// (measured on MI355X: 2 chains per lane with 8 scan waves was 13% slower on the 130M shape)
 template <bool BF16>
 BwdKernel bwd_kernel(int64_t n) {
   switch (n) {
