@@ -69,6 +69,11 @@ class Oracle:
         i64, i32, vp, dp = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_double
         lib.oracle_scan.argtypes = [i64, i64, i64, i64, i32, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, i32]
         lib.oracle_scan.restype = i32
+        lib.oracle_scan_ex.argtypes = [i64, i64, i64, i64, i32, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, vp, vp, vp,
+                                       i32]
+        lib.oracle_scan_ex.restype = i32
+        lib.oracle_state_update_ex.argtypes = [i64, i64, i64, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, vp]
+        lib.oracle_state_update_ex.restype = i32
         lib.oracle_scan_channels.argtypes = [i64, i64, i64, i64, i32, vp, vp, vp, vp, vp, vp, vp, vp, i32, i64,
                                              vp, vp, vp, vp, i32]
         lib.oracle_scan_channels.restype = i32
@@ -107,7 +112,7 @@ class Oracle:
 
     # -- the scan -------------------------------------------------------------------------------
     def scan(self, x, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=False,
-             h0=None, nthreads: int = 1) -> Tuple[np.ndarray, np.ndarray]:
+             h0=None, nthreads: int = 1, zoh: bool = False) -> Tuple[np.ndarray, np.ndarray]:
         """Full scan.  x, delta, z: (batch, L, dim); B, C: (batch, L, N); A: (dim, N) fp32;
         D, delta_bias: (dim,) fp32.  Returns y (batch, L, dim) and last_state (batch, dim, N),
         both float64."""
@@ -128,9 +133,14 @@ class Oracle:
         assert h0 is None or h0.shape == (batch, dim, N)
         y = np.empty((batch, L, dim), np.float64)
         st = np.empty((batch, dim, N), np.float64)
-        rc = self._lib.oracle_scan(batch, L, dim, N, code, _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C),
-                                   _ptr(D), _ptr(z), _ptr(delta_bias), int(bool(delta_softplus)), _ptr(h0),
-                                   _ptr(y), _ptr(st), int(nthreads))
+        if zoh:
+            rc = self._lib.oracle_scan_ex(batch, L, dim, N, code, _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C),
+                                          _ptr(D), _ptr(z), _ptr(delta_bias), int(bool(delta_softplus)), 1,
+                                          _ptr(h0), _ptr(y), _ptr(st), int(nthreads))
+        else:
+            rc = self._lib.oracle_scan(batch, L, dim, N, code, _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C),
+                                       _ptr(D), _ptr(z), _ptr(delta_bias), int(bool(delta_softplus)), _ptr(h0),
+                                       _ptr(y), _ptr(st), int(nthreads))
         if rc != 0:
             raise ValueError("oracle_scan rejected its arguments")
         return y, st
@@ -159,7 +169,7 @@ class Oracle:
         return y, st
 
     def state_update(self, state, x, delta, A, B, C, D=None, z=None, delta_bias=None,
-                     delta_softplus=False) -> Tuple[np.ndarray, np.ndarray]:
+                     delta_softplus=False, zoh: bool = False) -> Tuple[np.ndarray, np.ndarray]:
         """One decode step.  state: (batch, dim, N) (not modified; a float64 copy is updated
         and returned); x, delta, z: (batch, dim); B, C: (batch, N).  Returns (y, new_state)."""
         x, delta, B, C, z = _c(x), _c(delta), _c(B), _c(C), _c(z)
@@ -172,9 +182,9 @@ class Oracle:
         N = A.shape[1]
         assert st.shape == (batch, dim, N) and B.shape == (batch, N) and C.shape == (batch, N)
         y = np.empty((batch, dim), np.float64)
-        rc = self._lib.oracle_state_update(batch, dim, N, code, _ptr(st), _ptr(x), _ptr(delta), _ptr(A),
-                                           _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
-                                           int(bool(delta_softplus)), _ptr(y))
+        rc = self._lib.oracle_state_update_ex(batch, dim, N, code, _ptr(st), _ptr(x), _ptr(delta), _ptr(A),
+                                              _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
+                                              int(bool(delta_softplus)), int(bool(zoh)), _ptr(y))
         if rc != 0:
             raise ValueError("oracle_state_update rejected its arguments")
         return y, st

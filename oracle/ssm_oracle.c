@@ -75,9 +75,18 @@ static double silu(double z) { return z / (1.0 + exp(-z)); }
 /* The definition for one channel (b, d): runs the recurrence over all L steps
  * from the state h (length N, updated in place) and writes y_t to
  * y[t * y_stride_t]. */
+/* Bbar for one (d, n), times x: the Delta*B form of the simplified selective_scan
+ * ("Mamba 论文精读" sec. 3.3), or the exact zero-order hold of sec. 2.2,
+ * Bbar = (Delta A)^-1 (exp(Delta A) - 1) Delta B, which for a diagonal A is
+ * expm1(Delta A_n) / A_n * B_n (and Delta B_n in the limit A_n = 0). */
+static double bbar_x(int zoh, double dt, double a, double bv, double xt) {
+  if (!zoh || a == 0.0) return dt * bv * xt;
+  return expm1(dt * a) / a * bv * xt;
+}
+
 static void scan_channel(int64_t L, int64_t Dm, int64_t N, int dtype, const void *x, const void *delta,
                          const float *A, const void *B, const void *C, const float *Dskip, const void *z,
-                         const float *delta_bias, int delta_softplus, int64_t b, int64_t d, double *h,
+                         const float *delta_bias, int delta_softplus, int zoh, int64_t b, int64_t d, double *h,
                          double *y, int64_t y_stride_t) {
   for (int64_t t = 0; t < L; ++t) {
     const int64_t i_td = (b * L + t) * Dm + d;  /* (b,t,d) */
@@ -88,7 +97,10 @@ static void scan_channel(int64_t L, int64_t Dm, int64_t N, int dtype, const void
     double acc = 0.0;
     for (int64_t n = 0; n < N; ++n) {
       double abar = exp(dt * (double)A[d * N + n]);
-      h[n] = abar * h[n] + dt * load_elem(B, dtype, i_tn + n) * xt;
+      if (zoh)
+        h[n] = abar * h[n] + bbar_x(1, dt, (double)A[d * N + n], load_elem(B, dtype, i_tn + n), xt);
+      else
+        h[n] = abar * h[n] + dt * load_elem(B, dtype, i_tn + n) * xt;
       acc += load_elem(C, dtype, i_tn + n) * h[n];
     }
     double yt = acc + (Dskip ? (double)Dskip[d] * xt : 0.0);
@@ -100,10 +112,24 @@ static void scan_channel(int64_t L, int64_t Dm, int64_t N, int dtype, const void
 /* Whole scan.  y: (batch, seqlen, dim) doubles.  last_state: (batch, dim,
  * dstate) doubles or NULL.  h0: optional initial state (batch, dim, dstate);
  * NULL means zeros.  Returns 0, or -1 on a bad argument. */
+int oracle_scan_ex(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dtype, const void *x,
+                   const void *delta, const float *A, const void *B, const void *C, const float *Dskip,
+                   const void *z, const float *delta_bias, int delta_softplus, int zoh, const double *h0, double *y,
+                   double *last_state, int nthreads);
+
 int oracle_scan(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dtype, const void *x,
                 const void *delta, const float *A, const void *B, const void *C, const float *Dskip,
                 const void *z, const float *delta_bias, int delta_softplus, const double *h0, double *y,
                 double *last_state, int nthreads) {
+  return oracle_scan_ex(batch, seqlen, dim, dstate, dtype, x, delta, A, B, C, Dskip, z, delta_bias, delta_softplus,
+                        0, h0, y, last_state, nthreads);
+}
+
+/* oracle_scan with the choice of Bbar: zoh = 0 for Delta*B, 1 for the exact zero-order hold. */
+int oracle_scan_ex(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dtype, const void *x,
+                   const void *delta, const float *A, const void *B, const void *C, const float *Dskip,
+                   const void *z, const float *delta_bias, int delta_softplus, int zoh, const double *h0, double *y,
+                   double *last_state, int nthreads) {
   if (batch < 0 || seqlen < 0 || dim < 0 || dstate < 1 || dstate > 1024) return -1;
   if (!x || !delta || !A || !B || !C || !y) return -1;
   const int64_t nch = batch * dim;
@@ -115,8 +141,8 @@ int oracle_scan(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int 
     const int64_t b = ch / dim, d = ch % dim;
     double h[1024];
     for (int64_t n = 0; n < dstate; ++n) h[n] = h0 ? h0[ch * dstate + n] : 0.0;
-    scan_channel(seqlen, dim, dstate, dtype, x, delta, A, B, C, Dskip, z, delta_bias, delta_softplus, b, d, h,
-                 y + b * seqlen * dim + d, dim);
+    scan_channel(seqlen, dim, dstate, dtype, x, delta, A, B, C, Dskip, z, delta_bias, delta_softplus, zoh, b, d,
+                 h, y + b * seqlen * dim + d, dim);
     if (last_state)
       for (int64_t n = 0; n < dstate; ++n) last_state[ch * dstate + n] = h[n];
   }
@@ -143,7 +169,7 @@ int oracle_scan_channels(int64_t batch, int64_t seqlen, int64_t dim, int64_t dst
   for (int64_t k = 0; k < nsel; ++k) {
     double h[1024];
     for (int64_t n = 0; n < dstate; ++n) h[n] = 0.0;
-    scan_channel(seqlen, dim, dstate, dtype, x, delta, A, B, C, Dskip, z, delta_bias, delta_softplus, sel_b[k],
+    scan_channel(seqlen, dim, dstate, dtype, x, delta, A, B, C, Dskip, z, delta_bias, delta_softplus, 0, sel_b[k],
                  sel_d[k], h, y_out + k * seqlen, 1);
     if (state_out)
       for (int64_t n = 0; n < dstate; ++n) state_out[k * dstate + n] = h[n];
@@ -157,9 +183,21 @@ int oracle_scan_channels(int64_t batch, int64_t seqlen, int64_t dim, int64_t dst
  * in place.  x, delta, z: (batch, dim); B, C: (batch, dstate); y: (batch, dim).
  * ("Mamba 论文精读" sec. 6: inference costs O(1) per token with a fixed-size
  * state and no cache of past inputs.) */
+int oracle_state_update_ex(int64_t batch, int64_t dim, int64_t dstate, int dtype, double *state, const void *x,
+                           const void *delta, const float *A, const void *B, const void *C, const float *Dskip,
+                           const void *z, const float *delta_bias, int delta_softplus, int zoh, double *y);
+
 int oracle_state_update(int64_t batch, int64_t dim, int64_t dstate, int dtype, double *state, const void *x,
                         const void *delta, const float *A, const void *B, const void *C, const float *Dskip,
                         const void *z, const float *delta_bias, int delta_softplus, double *y) {
+  return oracle_state_update_ex(batch, dim, dstate, dtype, state, x, delta, A, B, C, Dskip, z, delta_bias,
+                                delta_softplus, 0, y);
+}
+
+/* oracle_state_update with the choice of Bbar (zoh as in oracle_scan_ex). */
+int oracle_state_update_ex(int64_t batch, int64_t dim, int64_t dstate, int dtype, double *state, const void *x,
+                           const void *delta, const float *A, const void *B, const void *C, const float *Dskip,
+                           const void *z, const float *delta_bias, int delta_softplus, int zoh, double *y) {
   if (batch < 0 || dim < 0 || dstate < 1 || dstate > 1024) return -1;
   if (!state || !x || !delta || !A || !B || !C || !y) return -1;
   for (int64_t b = 0; b < batch; ++b) {
@@ -172,7 +210,10 @@ int oracle_state_update(int64_t batch, int64_t dim, int64_t dstate, int dtype, d
       double acc = 0.0;
       for (int64_t n = 0; n < dstate; ++n) {
         double abar = exp(dt * (double)A[d * dstate + n]);
-        h[n] = abar * h[n] + dt * load_elem(B, dtype, b * dstate + n) * xt;
+        if (zoh)
+          h[n] = abar * h[n] + bbar_x(1, dt, (double)A[d * dstate + n], load_elem(B, dtype, b * dstate + n), xt);
+        else
+          h[n] = abar * h[n] + dt * load_elem(B, dtype, b * dstate + n) * xt;
         acc += load_elem(C, dtype, b * dstate + n) * h[n];
       }
       double yt = acc + (Dskip ? (double)Dskip[d] * xt : 0.0);

@@ -495,9 +495,75 @@ def pin_backward_linear_in_dy(o):
         _close(r3[k], 2.0 * r1[k] - 3.0 * r2[k], 1e-12, f"linearity of {k}")
 
 
+# ----------------------------------------------------------------------------------------------
+# the exact zero-order hold ("Mamba 论文精读" sec. 2.2: Bbar = (Delta A)^-1 (exp(Delta A) - I) Delta B)
+# ----------------------------------------------------------------------------------------------
+def _lti_zoh(o, x, dt, A, Bv, Cv):
+    """One channel, constant Delta / B / C, as a (1, L, 1) scan with the ZOH flag."""
+    L, N = x.size, A.size
+    return o.scan(x.reshape(1, L, 1), np.full((1, L, 1), dt), A.reshape(1, N).astype(np.float32),
+                  np.tile(Bv, (1, L, 1)), np.tile(Cv, (1, L, 1)), zoh=True)
+
+
+def pin_zoh_steady_state(o):
+    """Under a constant input x = 1 the exact ZOH state tends to the continuous fixed point
+    -B/A, whatever the step (the Delta B form tends to Delta B / (1 - e^{Delta A}) instead)."""
+    A = np.array([-0.5, -1.0, -2.0, -4.0])
+    Bv = np.array([1.0, -2.0, 0.5, 3.0])
+    Cv = np.ones(4)
+    for dt in (0.01, 0.3, 2.0):
+        L = int(60.0 / (dt * 0.5)) + 1
+        _, st = _lti_zoh(o, np.ones(L), dt, A, Bv, Cv)
+        _close(st[0, 0], -Bv / A, 1e-9, f"ZOH fixed point, dt={dt}")
+
+
+def pin_zoh_semigroup(o):
+    """ZOH is exact for piecewise-constant input: one step of 2 Delta equals two steps of Delta
+    with the same input held."""
+    A = np.array([-0.3, -1.7, -5.0])
+    Bv, Cv = np.array([0.7, -1.1, 2.0]), np.array([1.0, 0.5, -2.0])
+    for dt in (0.05, 0.8):
+        _, one = _lti_zoh(o, np.array([1.3]), 2 * dt, A, Bv, Cv)
+        _, two = _lti_zoh(o, np.array([1.3, 1.3]), dt, A, Bv, Cv)
+        _close(one, two, 1e-12, f"ZOH semigroup, dt={dt}")
+
+
+def pin_zoh_small_step_limit(o):
+    """As Delta -> 0 the exact ZOH input term agrees with Delta B to first order: the states of
+    the two forms differ by O(Delta^2 A) after one step."""
+    A = np.array([-1.0, -3.0])
+    Bv, Cv = np.array([2.0, -1.0]), np.array([1.0, 1.0])
+    prev = None
+    for dt in (1e-2, 1e-3, 1e-4):
+        _, zoh = _lti_zoh(o, np.array([1.0]), dt, A, Bv, Cv)
+        plain, _ = o.scan(np.ones((1, 1, 1)), np.full((1, 1, 1), dt), A.reshape(1, 2).astype(np.float32),
+                          Bv.reshape(1, 1, 2), Cv.reshape(1, 1, 2))
+        diff = float(np.max(np.abs(zoh[0, 0] - dt * Bv)))
+        # expm1(dt a)/a - dt = dt^2 a / 2 + O(dt^3)
+        ref = float(np.max(np.abs(dt * dt * A / 2 * Bv)))
+        assert abs(diff - ref) <= 0.02 * ref, f"ZOH vs Delta B at dt={dt}: {diff} vs {ref}"
+        if prev is not None:
+            assert diff < prev / 50, "the ZOH / Delta B difference must shrink like Delta^2"
+        prev = diff
+
+
+def pin_zoh_decode_equals_scan(o):
+    """The ZOH decode step run token by token equals the ZOH scan."""
+    c = _rand_case(41, batch=2, L=6, dim=3, N=4)
+    y, st = o.scan(c["x"], c["delta"], c["A"], c["B"], c["C"], D=c["D"], z=c["z"], delta_bias=c["delta_bias"],
+                   delta_softplus=True, zoh=True)
+    s = np.zeros((2, 3, 4))
+    for t in range(6):
+        yt, s = o.state_update(s, c["x"][:, t], c["delta"][:, t], c["A"], c["B"][:, t], c["C"][:, t], D=c["D"],
+                               z=c["z"][:, t], delta_bias=c["delta_bias"], delta_softplus=True, zoh=True)
+        _close(yt, y[:, t], 1e-12, f"ZOH decode step {t}")
+    _close(s, st, 1e-12, "ZOH decode state")
+
+
 ALL_PINS = [pin_worked_examples, pin_unrolled_sum, pin_lti_convolution, pin_linearity,
             pin_channel_independence, pin_causality, pin_zero_step, pin_impulse_long_carry,
             pin_decode_equals_scan, pin_associative_scan, pin_special_values, pin_storage_widening,
             pin_channel_selection, pin_conv_library_convolution, pin_conv_impulse, pin_conv_silu,
             pin_conv_chaining, pin_conv_decode_equals_fwd, pin_conv_causality, pin_backward_finite_differences,
-            pin_backward_linear_in_dy]
+            pin_backward_linear_in_dy, pin_zoh_steady_state, pin_zoh_semigroup, pin_zoh_small_step_limit,
+            pin_zoh_decode_equals_scan]

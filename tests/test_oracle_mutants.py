@@ -56,6 +56,9 @@ MUTANTS = [
     ("bwd_no_softplus_slope", "const double dd = delta_softplus ? ddt * sigmoid(v) : ddt;", "const double dd = ddt;"),
     ("bwd_dB_without_dt", "dB[i_tn + n] += g[n] * dt * xt;", "dB[i_tn + n] += g[n] * xt;"),
     ("bwd_dC_uses_old_state", "dC[i_tn + n] += dy0 * h[n];", "dC[i_tn + n] += dy0 * hp[n];"),
+    ("zoh_missing_division", "return expm1(dt * a) / a * bv * xt;", "return expm1(dt * a) * bv * xt;"),
+    ("zoh_plain_exp", "return expm1(dt * a) / a * bv * xt;", "return exp(dt * a) / a * bv * xt;"),
+    ("zoh_keeps_delta", "return expm1(dt * a) / a * bv * xt;", "return dt * expm1(dt * a) / a * bv * xt;"),
     ("conv_silu_skipped", "out[(b * seqlen + t) * dim + d] = apply_silu ? silu(acc) : acc;",
      "out[(b * seqlen + t) * dim + d] = acc;"),
 ]
