@@ -83,7 +83,7 @@ def time_calls(torch, fn, n_calls, warmup):
     return ev[0].elapsed_time(ev[-1]), per
 
 
-def bench_scan(name, steps, warmup, torch, np, W, ssm, device):
+def bench_scan(name, steps, warmup, torch, np, W, ssm, device, zoh=False):
     w = W.WORKLOADS[name]
     es = 2 if w.dtype == "bf16" else 4
     t = W.workload_inputs(w)
@@ -101,7 +101,8 @@ def bench_scan(name, steps, warmup, torch, np, W, ssm, device):
     def call(i):
         d = sets[i % copies]
         ssm.ssm_scan_fwd(d["x"], d["delta"], d["A"], d["B"], d["C"], D=d["D"], z=d["z"],
-                         delta_bias=d["delta_bias"], delta_softplus=w.delta_softplus, y=d["y"], last_state=d["st"])
+                         delta_bias=d["delta_bias"], delta_softplus=w.delta_softplus, y=d["y"], last_state=d["st"],
+                         zoh=zoh)
 
     total_ms, per = time_calls(torch, call, steps, warmup)
     ms_step = total_ms / steps
@@ -484,6 +485,10 @@ def main():
         extra["decode_mall_resident"] = bench_decode(256, torch, np, W, ssm, device, ring=1)
         extra["decode_hbm_ring26"] = bench_decode(256, torch, np, W, ssm, device, ring=26)
         log(f"[bench] decode: {extra['decode_hbm_ring26']['updates_per_s']:.3e} updates/s (ring of 26 states)")
+        zres = bench_scan(args.workload, max(10, args.steps // 2), 3, torch, np, W, ssm, device, zoh=True)
+        extra["scan_fwd_exact_zoh"] = {"kernel_ms": zres["kernel_ms"], "elems_per_s": zres["elems_per_s"],
+                                       "vs_delta_b": zres["kernel_ms"] / main_res["kernel_ms"]}
+        log(f"[bench] {args.workload} with exact ZOH Bbar: {zres['kernel_ms'] * 1e3:.1f} us/launch")
         extra["scan_bwd"] = bench_scan_bwd(max(6, args.steps // 5), 2, torch, np, W, ssm, device)
         extra["scan_bwd"]["fwd_equiv"] = extra["scan_bwd"]["ms_per_call"] / main_res["kernel_ms"]
         log(f"[bench] scan backward (130M shape): {extra['scan_bwd']['ms_per_call'] * 1e3:.1f} us/call "

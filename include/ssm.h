@@ -112,6 +112,19 @@ SSM_API ssm_status_t ssm_scan_fwd(int64_t batch, int64_t seqlen, int64_t dim, in
                           float *last_state, void *stream);
 
 /*
+ * The discretised input term Bbar x.
+ *   SSM_BBAR_DELTA_B  Bbar = Delta B (the default; the simplified
+ *                     selective_scan of "Mamba 论文精读" sec. 3.3)
+ *   SSM_BBAR_ZOH      the exact zero-order hold of sec. 2.2,
+ *                     Bbar = (Delta A)^-1 (exp(Delta A) - I) Delta B, i.e.
+ *                     (exp(Delta A_n) - 1) / A_n B_n for the diagonal A
+ *                     (Delta B_n where A_n = 0).  About 2.5x the arithmetic
+ *                     of the default; the backward pass supports only the
+ *                     default.
+ */
+typedef enum { SSM_BBAR_DELTA_B = 0, SSM_BBAR_ZOH = 1 } ssm_bbar_mode_t;
+
+/*
  * Launch-shape overrides for ssm_scan_fwd.  Every field 0 means "choose
  * automatically".  The result does not depend on these choices beyond fp32
  * rounding of the re-associated cross-segment carry; they exist for tuning
@@ -120,14 +133,18 @@ SSM_API ssm_status_t ssm_scan_fwd(int64_t batch, int64_t seqlen, int64_t dim, in
  *                    dividing dstate;
  *   segments         number of sequence segments scanned in parallel (>= 1);
  *   chunk_steps      time steps staged per LDS tile: 16 or 32 (32 needs at most
- *                    4 scan waves, i.e. dstate / chains_per_lane <= 4).
+ *                    4 scan waves, i.e. dstate / chains_per_lane <= 4, and
+ *                    bbar_mode SSM_BBAR_DELTA_B).
+ *   bbar_mode        the discretised input term (not a launch-shape choice:
+ *                    it changes the result), see ssm_bbar_mode_t.
  * reserved must be zero.
  */
 typedef struct {
   int32_t chains_per_lane;
   int32_t segments;
   int32_t chunk_steps;
-  int32_t reserved[5];
+  int32_t bbar_mode;
+  int32_t reserved[4];
 } ssm_scan_opts_t;
 
 /* ssm_scan_fwd with launch-shape overrides (opts may be NULL). An override
@@ -225,6 +242,19 @@ SSM_API ssm_status_t ssm_causal_conv1d_fwd(int64_t batch, int64_t seqlen, int64_
 SSM_API ssm_status_t ssm_causal_conv1d_update(int64_t batch, int64_t dim, int64_t width, ssm_dtype_t dtype,
                                               void *conv_state, const void *x, const float *weight,
                                               const float *bias, int silu, void *y, void *stream);
+
+/* Options of ssm_state_update_ex: bbar_mode as in ssm_scan_opts_t; reserved
+ * must be zero. */
+typedef struct {
+  int32_t bbar_mode;
+  int32_t reserved[7];
+} ssm_update_opts_t;
+
+/* ssm_state_update with options (opts may be NULL: the defaults). */
+SSM_API ssm_status_t ssm_state_update_ex(int64_t batch, int64_t dim, int64_t dstate, ssm_dtype_t dtype, float *state,
+                                         const void *x, const void *delta, const float *A, const void *B,
+                                         const void *C, const float *D, const void *z, const float *delta_bias,
+                                         int delta_softplus, void *y, void *stream, const ssm_update_opts_t *opts);
 
 /* Static string naming a status code ("SSM_OK", ...); never NULL. */
 SSM_API const char *ssm_status_string(ssm_status_t status);

@@ -28,7 +28,8 @@ LIBRARY = os.path.join(_HERE, "libssm61.so")
 SSM_F32, SSM_BF16 = 0, 1
 STATUS_NAMES = {0: "SSM_OK", 1: "SSM_ERR_INVALID_ARG", 2: "SSM_ERR_UNSUPPORTED", 3: "SSM_ERR_MISALIGNED",
                 4: "SSM_ERR_HIP"}
-EXPORTED = ("ssm_scan_fwd", "ssm_scan_fwd_ex", "ssm_scan_bwd", "ssm_state_update", "ssm_causal_conv1d_fwd",
+EXPORTED = ("ssm_scan_fwd", "ssm_scan_fwd_ex", "ssm_scan_bwd", "ssm_state_update", "ssm_state_update_ex",
+            "ssm_causal_conv1d_fwd",
             "ssm_causal_conv1d_update", "ssm_status_string", "ssm_last_error", "ssm_abi_version")
 
 
@@ -40,7 +41,14 @@ class SsmError(RuntimeError):
 
 class ScanOpts(ctypes.Structure):
     _fields_ = [("chains_per_lane", ctypes.c_int32), ("segments", ctypes.c_int32),
-                ("chunk_steps", ctypes.c_int32), ("reserved", ctypes.c_int32 * 5)]
+                ("chunk_steps", ctypes.c_int32), ("bbar_mode", ctypes.c_int32), ("reserved", ctypes.c_int32 * 4)]
+
+
+class UpdateOpts(ctypes.Structure):
+    _fields_ = [("bbar_mode", ctypes.c_int32), ("reserved", ctypes.c_int32 * 7)]
+
+
+SSM_BBAR_DELTA_B, SSM_BBAR_ZOH = 0, 1
 
 
 _lib_handle = None
@@ -61,6 +69,8 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
     lib.ssm_scan_fwd_ex.restype = i32
     lib.ssm_state_update.argtypes = [i64, i64, i64, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp]
     lib.ssm_state_update.restype = i32
+    lib.ssm_state_update_ex.argtypes = lib.ssm_state_update.argtypes + [ctypes.POINTER(UpdateOpts)]
+    lib.ssm_state_update_ex.restype = i32
     lib.ssm_scan_bwd.argtypes = [i64, i64, i64, i64, i32, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp,
                                  vp, vp, vp, vp]
     lib.ssm_scan_bwd.restype = i32
@@ -122,10 +132,11 @@ def ssm_scan_fwd(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch
                  delta_bias: Optional[torch.Tensor] = None, delta_softplus: bool = False, *,
                  y: Optional[torch.Tensor] = None, last_state: Optional[torch.Tensor] = None,
                  return_last_state: bool = True, chains_per_lane: int = 0, segments: int = 0,
-                 chunk_steps: int = 0, stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+                 chunk_steps: int = 0, zoh: bool = False, stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Selective scan forward (include/ssm.h: ssm_scan_fwd).  Returns (y, last_state); last_state
     is None when return_last_state is False and none was passed in.  chains_per_lane, segments
-    and chunk_steps override the launch shape (0 = automatic)."""
+    and chunk_steps override the launch shape (0 = automatic); zoh selects the exact
+    zero-order-hold input term (SSM_BBAR_ZOH) instead of Delta B."""
     lib = load_library()
     if x.dim() != 3 or A.dim() != 2:
         raise ValueError("x must be (batch, seqlen, dim) and A (dim, dstate)")
@@ -147,7 +158,8 @@ def ssm_scan_fwd(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch
     if last_state is None and return_last_state:
         last_state = torch.empty((batch, dim, dstate), dtype=torch.float32, device=dev)
     _need(last_state, "last_state", (batch, dim, dstate), torch.float32, dev, optional=True)
-    opts = ScanOpts(int(chains_per_lane), int(segments), int(chunk_steps))
+    opts = ScanOpts(int(chains_per_lane), int(segments), int(chunk_steps),
+                    SSM_BBAR_ZOH if zoh else SSM_BBAR_DELTA_B)
     status = lib.ssm_scan_fwd_ex(batch, seqlen, dim, dstate, code, _ptr(x), _ptr(delta), _ptr(A), _ptr(B),
                                  _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias), int(bool(delta_softplus)), _ptr(y),
                                  _ptr(last_state), _stream(dev, stream), ctypes.byref(opts))
@@ -158,10 +170,10 @@ def ssm_scan_fwd(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch
 def ssm_state_update(state: torch.Tensor, x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor,
                      B: torch.Tensor, C: torch.Tensor, D: Optional[torch.Tensor] = None,
                      z: Optional[torch.Tensor] = None, delta_bias: Optional[torch.Tensor] = None,
-                     delta_softplus: bool = False, *, y: Optional[torch.Tensor] = None,
+                     delta_softplus: bool = False, *, y: Optional[torch.Tensor] = None, zoh: bool = False,
                      stream=None) -> torch.Tensor:
-    """One decode step (include/ssm.h: ssm_state_update); `state` is updated in place.
-    Returns y (batch, dim)."""
+    """One decode step (include/ssm.h: ssm_state_update_ex); `state` is updated in place.
+    Returns y (batch, dim).  zoh selects the exact zero-order-hold input term."""
     lib = load_library()
     if x.dim() != 2 or A.dim() != 2:
         raise ValueError("x must be (batch, dim) and A (dim, dstate)")
@@ -180,9 +192,10 @@ def ssm_state_update(state: torch.Tensor, x: torch.Tensor, delta: torch.Tensor, 
     if y is None:
         y = torch.empty_like(x)
     _need(y, "y", (batch, dim), dt, dev)
-    status = lib.ssm_state_update(batch, dim, dstate, code, _ptr(state), _ptr(x), _ptr(delta), _ptr(A), _ptr(B),
-                                  _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias), int(bool(delta_softplus)), _ptr(y),
-                                  _stream(dev, stream))
+    opts = UpdateOpts(SSM_BBAR_ZOH if zoh else SSM_BBAR_DELTA_B)
+    status = lib.ssm_state_update_ex(batch, dim, dstate, code, _ptr(state), _ptr(x), _ptr(delta), _ptr(A), _ptr(B),
+                                     _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias), int(bool(delta_softplus)),
+                                     _ptr(y), _stream(dev, stream), ctypes.byref(opts))
     _check(status)
     return y
 
@@ -283,5 +296,5 @@ def abi_version() -> int:
     return load_library().ssm_abi_version()
 
 
-__all__ = ["ssm_scan_fwd", "ssm_scan_bwd", "ssm_state_update", "ssm_causal_conv1d_fwd", "ssm_causal_conv1d_update", "abi_version", "load_library", "SsmError", "ScanOpts",
+__all__ = ["ssm_scan_fwd", "ssm_scan_bwd", "ssm_state_update", "ssm_causal_conv1d_fwd", "ssm_causal_conv1d_update", "abi_version", "load_library", "SsmError", "ScanOpts", "UpdateOpts",
            "LIBRARY", "EXPORTED"]

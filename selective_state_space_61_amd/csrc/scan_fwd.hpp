@@ -75,7 +75,9 @@ constexpr int scan_lds_bytes(int G, bool full, int ch) {
 }
 constexpr int kLdsBudget = 160 * 1024;
 
-template <bool BF16, int N, int NPL, int MODE, int CH>
+// ZOH: exact zero-order-hold input term (zoh_factor) instead of Delta B.  That form runs as
+// compiler-scheduled code and reads out each step in the step itself.
+template <bool BF16, int N, int NPL, int MODE, int CH, bool ZOH = false>
 __global__ __launch_bounds__(64 * (N / NPL + kIoWaves)) void scan_chunk_kernel(const ScanArgs p) {
   constexpr int G = N / NPL;                   // scan waves
   constexpr bool kFull = (MODE == MODE_FULL);
@@ -180,7 +182,18 @@ __global__ __launch_bounds__(64 * (N / NPL + kIoWaves)) void scan_chunk_kernel(c
           static_for<kBatch>([&](auto K) {
             constexpr int k = decltype(K)::value;
             constexpr int t = q * kBatch + k;
-            if constexpr (kFull && t > 0) {
+            if constexpr (ZOH) {
+              float yp = 0.0f;
+#pragma unroll
+              for (int jj = 0; jj < NPL; ++jj) {
+                const float tt = dw[k].x * A2[jj];
+                const float a = hw_exp2(tt);
+                h[jj] = fmaf(a, h[jj], row_bcast<t % 16>(Bv[t / 16][jj]) * (dw[k].y * zoh_factor(tt, a)));
+                if constexpr (kFull) yp = fmaf(row_bcast<t % 16>(Cv[t / 16][jj]), h[jj], yp);
+              }
+              if constexpr (kFull) s_yp[sb][wave][t][lane] = yp;
+              else dsum += dw[k].x;
+            } else if constexpr (kFull && t > 0) {
               s_yp[sb][wave][t - 1][lane] =
                   step_readout<NPL, t % 16, (t - 1) % 16>(dw[k].x, dw[k].y, A2, Bv[t / 16], Cv[(t - 1) / 16], h);
             } else {
@@ -191,7 +204,7 @@ __global__ __launch_bounds__(64 * (N / NPL + kIoWaves)) void scan_chunk_kernel(c
             }
           });
         });
-        if constexpr (kFull) {
+        if constexpr (kFull && !ZOH) {
           float yp = row_bcast<15>(Cv[kHalves - 1][0]) * h[0];
 #pragma unroll
           for (int jj = 1; jj < NPL; ++jj) yp = fmaf(row_bcast<15>(Cv[kHalves - 1][jj]), h[jj], yp);
@@ -334,7 +347,8 @@ __global__ __launch_bounds__(64 * (N / NPL + kIoWaves)) void scan_chunk_kernel(c
       for (int i = 0; i < ITEMS; ++i) {
         const int row = row0 + i * RSTEP;
 #pragma unroll
-        for (int v = 0; v < VEC; ++v) s_dw[pb][row][col + v] = make_float2(dts[i][v], dts[i][v] * xs[i][v]);
+        for (int v = 0; v < VEC; ++v)  // ZOH: the scan multiplies by ln2 phi, so w carries log2(e)
+          s_dw[pb][row][col + v] = make_float2(dts[i][v], dts[i][v] * (ZOH ? xs[i][v] * kLog2e : xs[i][v]));
         ex[1][i] = ex[0][i];
         ex[0][i] = nx[i];
         if (has_z) {

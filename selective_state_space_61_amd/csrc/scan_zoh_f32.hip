@@ -1,0 +1,11 @@
+// scan_zoh_f32.hip -- scan kernels with the exact zero-order-hold input term, f32 x / delta / B / C / z / y.
+#include <hip/hip_runtime.h>
+#define SSM_SCAN_TABLE_DEFINE
+#include "scan_table.hpp"
+
+namespace ssm {
+const ScanTable& scan_table_zoh_f32() {
+  static const ScanTable t = make_table<false, true>();
+  return t;
+}
+}  // namespace ssm

@@ -148,16 +148,16 @@ ConvUpdateKernel conv_update_kernel(int64_t width) {
   }
 }
 
-template <bool BF16>
+template <bool BF16, bool ZOH>
 UpdateKernel update_kernel(int64_t n) {
   switch (n) {
-    case 1: return ssm::state_update_kernel<BF16, 1>;
-    case 2: return ssm::state_update_kernel<BF16, 2>;
-    case 4: return ssm::state_update_kernel<BF16, 4>;
-    case 8: return ssm::state_update_kernel<BF16, 8>;
-    case 16: return ssm::state_update_kernel<BF16, 16>;
-    case 32: return ssm::state_update_kernel<BF16, 32>;
-    case 64: return ssm::state_update_kernel<BF16, 64>;
+    case 1: return ssm::state_update_kernel<BF16, 1, ZOH>;
+    case 2: return ssm::state_update_kernel<BF16, 2, ZOH>;
+    case 4: return ssm::state_update_kernel<BF16, 4, ZOH>;
+    case 8: return ssm::state_update_kernel<BF16, 8, ZOH>;
+    case 16: return ssm::state_update_kernel<BF16, 16, ZOH>;
+    case 32: return ssm::state_update_kernel<BF16, 32, ZOH>;
+    case 64: return ssm::state_update_kernel<BF16, 64, ZOH>;
     default: return nullptr;
   }
 }
@@ -279,6 +279,8 @@ ssm_status_t ssm_scan_fwd_ex(int64_t batch, int64_t seqlen, int64_t dim, int64_t
   if (opts) {
     if (opts->segments < 0 || opts->chains_per_lane < 0)
       return fail(SSM_ERR_INVALID_ARG, "negative launch-shape override");
+    if (opts->bbar_mode != SSM_BBAR_DELTA_B && opts->bbar_mode != SSM_BBAR_ZOH)
+      return fail(SSM_ERR_UNSUPPORTED, "bbar_mode %d is not SSM_BBAR_DELTA_B or SSM_BBAR_ZOH", (int)opts->bbar_mode);
     for (int32_t r : opts->reserved)
       if (r != 0) return fail(SSM_ERR_INVALID_ARG, "ssm_scan_opts_t.reserved must be zero");
   }
@@ -313,7 +315,9 @@ ssm_status_t ssm_scan_fwd_ex(int64_t batch, int64_t seqlen, int64_t dim, int64_t
                 (long long)nseg);
 
   const bool bf16 = dtype == SSM_BF16;
-  const ssm::ScanTable& table = bf16 ? ssm::scan_table_bf16() : ssm::scan_table_f32();
+  const bool zoh = opts && opts->bbar_mode == SSM_BBAR_ZOH;
+  const ssm::ScanTable& table = zoh ? (bf16 ? ssm::scan_table_zoh_bf16() : ssm::scan_table_zoh_f32())
+                                    : (bf16 ? ssm::scan_table_bf16() : ssm::scan_table_f32());
   const auto it = table.find({static_cast<int>(dstate), npl});
   if (it == table.end()) return fail(SSM_ERR_UNSUPPORTED, "no kernel for dstate %lld chains %d", (long long)dstate, npl);
   // Chunk length: 32-step tiles halve the barriers per step but take twice the LDS, which with
@@ -327,8 +331,8 @@ ssm_status_t ssm_scan_fwd_ex(int64_t batch, int64_t seqlen, int64_t dim, int64_t
     k_full = it->second.full[1];
     k_agg = it->second.agg[1];
     if (!k_full || !k_agg)
-      return fail(SSM_ERR_UNSUPPORTED, "chunk_steps 32 not available for dstate %lld chains %d", (long long)dstate,
-                  npl);
+      return fail(SSM_ERR_UNSUPPORTED, "chunk_steps 32 not available for dstate %lld chains %d%s", (long long)dstate,
+                  npl, zoh ? " with SSM_BBAR_ZOH" : "");
   } else if (chunk_opt == 16) {
     k_full = it->second.full[0];
     k_agg = it->second.agg[0];
@@ -337,6 +341,7 @@ ssm_status_t ssm_scan_fwd_ex(int64_t batch, int64_t seqlen, int64_t dim, int64_t
     k_full = (one_round && it->second.full[1]) ? it->second.full[1] : it->second.full[0];
     k_agg = it->second.agg[0];
   }
+  if (!k_full || !k_agg) return fail(SSM_ERR_UNSUPPORTED, "no kernel for this chunk length and bbar_mode");
 
   ssm::ScanArgs a{};
   a.x = x; a.delta = delta; a.A = A; a.B = B; a.C = C; a.Dskip = D; a.z = z; a.delta_bias = delta_bias;
@@ -378,7 +383,22 @@ ssm_status_t ssm_state_update(int64_t batch, int64_t dim, int64_t dstate, ssm_dt
                               const void* x, const void* delta, const float* A, const void* B, const void* C,
                               const float* D, const void* z, const float* delta_bias, int delta_softplus, void* y,
                               void* stream) {
+  return ssm_state_update_ex(batch, dim, dstate, dtype, state, x, delta, A, B, C, D, z, delta_bias, delta_softplus,
+                             y, stream, nullptr);
+}
+
+ssm_status_t ssm_state_update_ex(int64_t batch, int64_t dim, int64_t dstate, ssm_dtype_t dtype, float* state,
+                                 const void* x, const void* delta, const float* A, const void* B, const void* C,
+                                 const float* D, const void* z, const float* delta_bias, int delta_softplus, void* y,
+                                 void* stream, const ssm_update_opts_t* opts) {
   g_err[0] = '\0';
+  if (opts) {
+    if (opts->bbar_mode != SSM_BBAR_DELTA_B && opts->bbar_mode != SSM_BBAR_ZOH)
+      return fail(SSM_ERR_UNSUPPORTED, "bbar_mode %d is not SSM_BBAR_DELTA_B or SSM_BBAR_ZOH", (int)opts->bbar_mode);
+    for (int32_t r : opts->reserved)
+      if (r != 0) return fail(SSM_ERR_INVALID_ARG, "ssm_update_opts_t.reserved must be zero");
+  }
+  const bool zoh = opts && opts->bbar_mode == SSM_BBAR_ZOH;
   if (batch < 0 || dim < 0 || dstate < 0)
     return fail(SSM_ERR_INVALID_ARG, "negative size (batch=%lld dim=%lld dstate=%lld)", (long long)batch,
                 (long long)dim, (long long)dstate);
@@ -414,7 +434,8 @@ ssm_status_t ssm_state_update(int64_t batch, int64_t dim, int64_t dstate, ssm_dt
   a.softplus = delta_softplus ? 1 : 0;
   a.state_vec_ok = aligned(state, 16) ? 1 : 0;
   a.a_vec_ok = aligned(A, 16) ? 1 : 0;
-  const UpdateKernel k = dtype == SSM_BF16 ? update_kernel<true>(dstate) : update_kernel<false>(dstate);
+  const UpdateKernel k = dtype == SSM_BF16 ? (zoh ? update_kernel<true, true>(dstate) : update_kernel<true, false>(dstate))
+                                            : (zoh ? update_kernel<false, true>(dstate) : update_kernel<false, false>(dstate));
   hipLaunchKernelGGL(k, dim3(static_cast<unsigned>(blocks)), dim3(ssm::kUpdateThreads), 0,
                      static_cast<hipStream_t>(stream), a);
   return check_launch("state update");

@@ -289,6 +289,18 @@ struct BcRow {
   }
 };
 
+// Factor of the exact zero-order-hold input term.  With tt = Delta A log2(e) and a = 2^tt =
+// e^(Delta A), the ZOH input matrix is Bbar = (e^(Delta A) - 1) / A B = Delta B phi(Delta A),
+// phi(z) = (e^z - 1) / z ("Mamba 论文精读" sec. 2.2).  This returns m = (a - 1) / tt = ln2 phi, so
+// that Bbar x = B (Delta x log2 e) m.  For |tt| < 1 the division uses log2(a) in place of tt
+// (Kahan's expm1 device: the rounding of a cancels between numerator and denominator, so no
+// precision is lost to a - 1 when a is near 1); elsewhere a - 1 does not cancel, and tt itself is
+// used, which stays right when a underflows.  a == 1 gives the limit ln2.
+__device__ __forceinline__ float zoh_factor(float tt, float a) {
+  const float l = fabsf(tt) < 1.0f ? hw_log2(a) : tt;
+  return a == 1.0f ? kLn2 : (a - 1.0f) * hw_rcp(l);
+}
+
 // compile-time loop: f(std::integral_constant<int, I>) for I = 0 .. N-1
 template <typename F, int... Is>
 __device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, Is...>) {

@@ -45,7 +45,8 @@ __device__ __forceinline__ float load_elem(const void* base, int64_t idx) {
 constexpr int kQuadsPerThread = 1;
 constexpr int kUpdateThreads = 256;
 
-template <bool BF16, int N>
+// ZOH: exact zero-order-hold input term (zoh_factor) instead of Delta B
+template <bool BF16, int N, bool ZOH = false>
 __global__ __launch_bounds__(kUpdateThreads) void state_update_kernel(const UpdateArgs p) {
   constexpr int SPT = N < 4 ? N : 4;
   constexpr int TPC = N / SPT;
@@ -118,8 +119,10 @@ __global__ __launch_bounds__(kUpdateThreads) void state_update_kernel(const Upda
     yp[k] = 0.0f;
 #pragma unroll
     for (int j = 0; j < SPT; ++j) {
-      const float a = hw_exp2(dt * (a2[k][j] * kLog2e));
-      hs[k][j] = fmaf(a, hs[k][j], w * bv[k][j]);
+      const float tt = dt * (a2[k][j] * kLog2e);
+      const float a = hw_exp2(tt);
+      const float u = ZOH ? (w * kLog2e) * zoh_factor(tt, a) * bv[k][j] : w * bv[k][j];
+      hs[k][j] = fmaf(a, hs[k][j], u);
       yp[k] = fmaf(cv[k][j], hs[k][j], yp[k]);
     }
   }

@@ -135,6 +135,18 @@ def test_scan_opts_validation(lib):
     bad = ssm.ScanOpts(0, 0, 0)
     bad.reserved[2] = 1
     assert scan(lib, dstate=16, opts=bad) == INVALID and "reserved" in err(lib)
+    assert scan(lib, dstate=16, opts=ssm.ScanOpts(0, 0, 0, 2)) == UNSUPPORTED and "bbar_mode" in err(lib)
+    assert scan(lib, dstate=16, opts=ssm.ScanOpts(4, 0, 32, ssm.SSM_BBAR_ZOH)) == UNSUPPORTED  # ZOH: 16-step tiles
+
+
+def test_update_opts_validation(lib):
+    def upd(opts):
+        return lib.ssm_state_update_ex(2, 16, 16, F32, fake(0), fake(1), fake(2), fake(3), fake(4), fake(5), fake(6),
+                                       fake(7), fake(8), 1, fake(9), None, ctypes.byref(opts))
+    assert upd(ssm.UpdateOpts(5)) == UNSUPPORTED and "bbar_mode" in err(lib)
+    bad = ssm.UpdateOpts(0)
+    bad.reserved[0] = 3
+    assert upd(bad) == INVALID and "reserved" in err(lib)
 
 
 def test_scan_size_overflow(lib):
