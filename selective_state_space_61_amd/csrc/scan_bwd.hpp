@@ -385,6 +385,19 @@ struct BwdReduceArgs {
   int32_t ncb;
 };
 
+// Sum of n values base[i * stride], i = 0 .. n-1, with 8 independent accumulators so that the
+// loads overlap; the order of the additions is fixed, so the result is reproducible.
+__device__ __forceinline__ float strided_sum(const float* base, int64_t n, int64_t stride) {
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  int64_t i = 0;
+  for (; i + 8 <= n; i += 8) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc[u] += base[(i + u) * stride];
+  }
+  for (int u = 0; i < n; ++i, ++u) acc[u] += base[i * stride];
+  return ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
+}
+
 template <bool BF16>
 __global__ __launch_bounds__(256) void scan_bwd_reduce_kernel(const BwdReduceArgs p) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
@@ -393,8 +406,7 @@ __global__ __launch_bounds__(256) void scan_bwd_reduce_kernel(const BwdReduceArg
   if (i < 2 * nbln) {
     const int which = i < nbln ? 0 : 1;
     const int64_t e = i - which * nbln;  // (b, t, n)
-    float s = 0.0f;
-    for (int k = 0; k < p.ncb; ++k) s += p.part_bc[(static_cast<int64_t>(which) * p.ncb + k) * nbln + e];
+    const float s = strided_sum(p.part_bc + static_cast<int64_t>(which) * p.ncb * nbln + e, p.ncb, nbln);
     void* out = which == 0 ? p.dB : p.dC;
     if constexpr (BF16) static_cast<uint16_t*>(out)[e] = to_bf16(s);
     else static_cast<float*>(out)[e] = s;
@@ -403,18 +415,13 @@ __global__ __launch_bounds__(256) void scan_bwd_reduce_kernel(const BwdReduceArg
   const int64_t j = i - 2 * nbln;
   if (j < ndn) {  // dA[d, n] = sum_b part_a[b, n, d]
     const int64_t d = j / p.N, n = j % p.N;
-    float s = 0.0f;
-    for (int64_t bb = 0; bb < p.batch; ++bb) s += p.part_a[(bb * p.N + n) * p.dim + d];
-    p.dA[j] = s;
+    p.dA[j] = strided_sum(p.part_a + n * p.dim + d, p.batch, static_cast<int64_t>(p.N) * p.dim);
     return;
   }
   const int64_t k = j - ndn;
   if (k < p.dim) {
-    float sd = 0.0f, sb = 0.0f;
-    for (int64_t r = 0; r < p.batch * kBwdChunk; ++r) {
-      sd += p.part_d[r * p.dim + k];
-      sb += p.part_bias[r * p.dim + k];
-    }
+    const float sd = strided_sum(p.part_d + k, p.batch * kBwdChunk, p.dim);
+    const float sb = strided_sum(p.part_bias + k, p.batch * kBwdChunk, p.dim);
     if (p.dD) p.dD[k] = sd;
     if (p.dbias) p.dbias[k] = sb;
   }
