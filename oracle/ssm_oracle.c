@@ -37,7 +37,9 @@
  *
  * The file also holds the depthwise causal convolution that precedes the scan
  * in the Mamba block, and its one-token form (oracle_causal_conv1d,
- * oracle_conv1d_update, below).
+ * oracle_conv1d_update, below), the backward scan (oracle_scan_bwd), and the
+ * Mamba-2 state space dual layer with one scalar A per head and B, C shared by
+ * a group of heads (oracle_ssd, "Mamba 论文精读" sec. 4 and 5.2).
  */
 #include <math.h>
 #include <stddef.h>
@@ -315,6 +317,61 @@ int oracle_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, 
   }
   free(hs);
   free(g);
+  return 0;
+}
+
+/* ---------------------------------------------------------------------------
+ * Mamba-2 state space dual (SSD) layer ("Mamba 论文精读" sec. 4.1: the recurrence
+ * h_t = A_t h_{t-1} + B_t x_t, y_t = C_t h_t, dual to a masked structured
+ * matrix; sec. 4.2: multi-head; sec. 5.2: the Mamba2 layer with headdim and
+ * d_state).  A is one scalar per head, B and C are shared by the heads of a
+ * group, and Bbar = dt B as in the selective scan.  For batch b, head h
+ * (group g = h / (nheads / ngroups)) and head channel p, from S = 0:
+ *   dt = softplus(dt[b,t,h] + dt_bias[h])  (or without softplus)
+ *   S[p,n] = exp(dt A[h]) S[p,n] + dt x[b,t,h,p] B[b,t,g,n]
+ *   y[b,t,h,p] = sum_n C[b,t,g,n] S[p,n] + D[h] x[b,t,h,p];  y *= silu(z[b,t,h,p]) if z
+ *   final_state[b,h,p,n] = S
+ * x, z, y: (batch, L, nheads, headdim); dt: (batch, L, nheads); B, C: (batch,
+ * L, ngroups, dstate); A, D, dt_bias: (nheads) fp32.
+ * ------------------------------------------------------------------------- */
+int oracle_ssd(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, int64_t dstate, int64_t ngroups,
+               int dtype, const void *x, const void *dt, const float *A, const void *B, const void *C,
+               const float *Dskip, const void *z, const float *dt_bias, int dt_softplus, double *y,
+               double *final_state, int nthreads) {
+  if (batch < 0 || seqlen < 0 || nheads < 1 || headdim < 1 || dstate < 1 || ngroups < 1) return -1;
+  if (nheads % ngroups != 0 || !x || !dt || !A || !B || !C || !y) return -1;
+  const int64_t H = nheads, P = headdim, N = dstate, G = ngroups, hpg = H / G;
+#ifdef _OPENMP
+  if (nthreads < 1) nthreads = 1;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
+#endif
+  for (int64_t bh = 0; bh < batch * H; ++bh) {
+    const int64_t b = bh / H, h = bh % H, g = h / hpg;
+    double *S = (double *)calloc((size_t)(P * N), sizeof(double));
+    if (!S) continue;
+    for (int64_t t = 0; t < seqlen; ++t) {
+      const double v = load_elem(dt, dtype, (b * seqlen + t) * H + h) + (dt_bias ? (double)dt_bias[h] : 0.0);
+      const double d = dt_softplus ? softplus(v) : v;
+      const double a = exp(d * (double)A[h]);
+      const int64_t ibc = ((b * seqlen + t) * G + g) * N;
+      for (int64_t p = 0; p < P; ++p) {
+        const int64_t ix = ((b * seqlen + t) * H + h) * P + p;
+        const double xv = load_elem(x, dtype, ix);
+        double acc = 0.0;
+        for (int64_t n = 0; n < N; ++n) {
+          S[p * N + n] = a * S[p * N + n] + d * xv * load_elem(B, dtype, ibc + n);
+          acc += load_elem(C, dtype, ibc + n) * S[p * N + n];
+        }
+        double yv = acc + (Dskip ? (double)Dskip[h] * xv : 0.0);
+        if (z) yv *= silu(load_elem(z, dtype, ix));
+        y[ix] = yv;
+      }
+    }
+    if (final_state)
+      for (int64_t i = 0; i < P * N; ++i) final_state[bh * P * N + i] = S[i];
+    free(S);
+  }
+  (void)nthreads;
   return 0;
 }
 

@@ -560,10 +560,67 @@ def pin_zoh_decode_equals_scan(o):
     _close(s, st, 1e-12, "ZOH decode state")
 
 
+# ----------------------------------------------------------------------------------------------
+# Mamba-2 SSD ("Mamba 论文精读" sec. 4.1-4.2, 5.2)
+# ----------------------------------------------------------------------------------------------
+def _ssd_case(seed, batch=2, L=9, H=4, P=3, N=5, G=2, softplus=True):
+    g = np.random.default_rng(seed)
+    return dict(x=g.normal(size=(batch, L, H, P)), dt=g.normal(size=(batch, L, H)) * 0.5,
+                A=-g.uniform(0.3, 3.0, H).astype(np.float32), B=g.normal(size=(batch, L, G, N)),
+                C=g.normal(size=(batch, L, G, N)), D=g.normal(size=H).astype(np.float32),
+                z=g.normal(size=(batch, L, H, P)), dt_bias=g.uniform(-2.0, 0.5, H).astype(np.float32),
+                dt_softplus=softplus)
+
+
+def pin_ssd_equals_selective_scan(o):
+    """A Mamba-2 head is a selective scan whose channels share one dt, one scalar A and their
+    group's B and C: mapping every head to headdim channels of the (pinned) scan oracle gives
+    the same y and states."""
+    c = _ssd_case(51)
+    y, fin = o.ssd(c["x"], c["dt"], c["A"], c["B"], c["C"], D=c["D"], z=c["z"], dt_bias=c["dt_bias"],
+                   dt_softplus=True)
+    batch, L, H, P = c["x"].shape
+    G, N = c["B"].shape[2:]
+    hpg = H // G
+    for g in range(G):
+        heads = range(g * hpg, (g + 1) * hpg)
+        x1 = np.concatenate([c["x"][:, :, h, :] for h in heads], axis=2)
+        d1 = np.concatenate([np.repeat(c["dt"][:, :, h:h + 1], P, axis=2) for h in heads], axis=2)
+        z1 = np.concatenate([c["z"][:, :, h, :] for h in heads], axis=2)
+        A1 = np.concatenate([np.full((P, N), c["A"][h], np.float32) for h in heads], axis=0)
+        D1 = np.concatenate([np.full(P, c["D"][h], np.float32) for h in heads])
+        b1 = np.concatenate([np.full(P, c["dt_bias"][h], np.float32) for h in heads])
+        y1, st1 = o.scan(x1, d1, A1, c["B"][:, :, g, :], c["C"][:, :, g, :], D=D1, z=z1, delta_bias=b1,
+                         delta_softplus=True)
+        for i, h in enumerate(heads):
+            _close(y[:, :, h, :], y1[:, :, i * P:(i + 1) * P], 1e-13, f"SSD head {h} vs selective scan")
+            _close(fin[:, h], st1[:, i * P:(i + 1) * P, :], 1e-13, f"SSD state {h}")
+
+
+def pin_ssd_dual_matrix_form(o):
+    """The duality of sec. 4.1: without gate and skip, y = (L o C B^T)(dt x) per head, where
+    L[i, j] = exp(sum_{k=j+1..i} dt_k A) for j <= i and 0 above the diagonal (a masked,
+    semi-separable matrix), computed with numpy matmuls."""
+    c = _ssd_case(52, L=11, softplus=False)
+    c["dt"] = np.abs(c["dt"])
+    y, _ = o.ssd(c["x"], c["dt"], c["A"], c["B"], c["C"])
+    batch, L, H, P = c["x"].shape
+    G = c["B"].shape[2]
+    for b in range(batch):
+        for h in range(H):
+            g = h // (H // G)
+            dt = c["dt"][b, :, h]
+            cum = np.cumsum(dt * float(c["A"][h]))
+            mask = np.tril(np.exp(cum[:, None] - cum[None, :]))
+            M = mask * (c["C"][b, :, g, :] @ c["B"][b, :, g, :].T)
+            ref = M @ (dt[:, None] * c["x"][b, :, h, :])
+            _close(y[b, :, h, :], ref, 1e-12, f"SSD dual form b={b} h={h}")
+
+
 ALL_PINS = [pin_worked_examples, pin_unrolled_sum, pin_lti_convolution, pin_linearity,
             pin_channel_independence, pin_causality, pin_zero_step, pin_impulse_long_carry,
             pin_decode_equals_scan, pin_associative_scan, pin_special_values, pin_storage_widening,
             pin_channel_selection, pin_conv_library_convolution, pin_conv_impulse, pin_conv_silu,
             pin_conv_chaining, pin_conv_decode_equals_fwd, pin_conv_causality, pin_backward_finite_differences,
             pin_backward_linear_in_dy, pin_zoh_steady_state, pin_zoh_semigroup, pin_zoh_small_step_limit,
-            pin_zoh_decode_equals_scan]
+            pin_zoh_decode_equals_scan, pin_ssd_equals_selective_scan, pin_ssd_dual_matrix_form]

@@ -59,6 +59,10 @@ MUTANTS = [
     ("zoh_missing_division", "return expm1(dt * a) / a * bv * xt;", "return expm1(dt * a) * bv * xt;"),
     ("zoh_plain_exp", "return expm1(dt * a) / a * bv * xt;", "return exp(dt * a) / a * bv * xt;"),
     ("zoh_keeps_delta", "return expm1(dt * a) / a * bv * xt;", "return dt * expm1(dt * a) / a * bv * xt;"),
+    ("ssd_group_ignored", "const int64_t b = bh / H, h = bh % H, g = h / hpg;", "const int64_t b = bh / H, h = bh % H, g = 0;"),
+    ("ssd_no_dt_on_input", "S[p * N + n] = a * S[p * N + n] + d * xv * load_elem(B, dtype, ibc + n);",
+     "S[p * N + n] = a * S[p * N + n] + xv * load_elem(B, dtype, ibc + n);"),
+    ("ssd_readout_uses_B", "acc += load_elem(C, dtype, ibc + n) * S[p * N + n];", "acc += load_elem(B, dtype, ibc + n) * S[p * N + n];"),
     ("conv_silu_skipped", "out[(b * seqlen + t) * dim + d] = apply_silu ? silu(acc) : acc;",
      "out[(b * seqlen + t) * dim + d] = acc;"),
 ]
