@@ -256,6 +256,49 @@ SSM_API ssm_status_t ssm_state_update_ex(int64_t batch, int64_t dim, int64_t dst
                                          const void *C, const float *D, const void *z, const float *delta_bias,
                                          int delta_softplus, void *y, void *stream, const ssm_update_opts_t *opts);
 
+/* Options of ssm_ssd_fwd.  head_slice: head channels per workgroup (16, 32
+ * or 64, dividing headdim), or 0 to let the library choose from the grid
+ * size; reserved must be zero. */
+typedef struct {
+  int32_t head_slice;
+  int32_t reserved[7];
+} ssm_ssd_opts_t;
+
+/*
+ * Mamba-2 state space dual (SSD) layer, forward ("Mamba 论文精读" sec. 4.1:
+ * the recurrence h_t = A_t h_{t-1} + B_t x_t, y_t = C_t h_t and its dual, a
+ * product with a causal semi-separable matrix; sec. 4.2: multiple heads and
+ * larger states; sec. 5.2: the Mamba2 layer with headdim and d_state).  A is
+ * one scalar per head, Bbar = dt B as in ssm_scan_fwd, and the heads of a
+ * group (nheads / ngroups consecutive heads) share B and C.  For batch row
+ * b, head h in group g and head channel p, from a zero state S (dstate):
+ *
+ *   dt_t = softplus(dt[b,t,h] + dt_bias[h])   (no softplus when dt_softplus == 0)
+ *   S    = exp(dt_t A[h]) S + dt_t x[b,t,h,p] B[b,t,g,:]
+ *   y[b,t,h,p] = (C[b,t,g,:] . S + D[h] x[b,t,h,p]) * silu(z[b,t,h,p])
+ *   final_state[b,h,p,:] = S after the last step
+ *
+ *   x, z, y        (batch, seqlen, nheads, headdim)  bf16; z may be NULL
+ *   dt             (batch, seqlen, nheads)           bf16
+ *   B, C           (batch, seqlen, ngroups, dstate)  bf16
+ *   A              (nheads) fp32;  D, dt_bias (nheads) fp32 or NULL
+ *   final_state    (batch, nheads, headdim, dstate)  fp32, or NULL
+ *
+ * The sequence is taken in chunks of 64 steps whose products run on bf16
+ * matrix cores with fp32 accumulation; the state carried between chunks is
+ * fp32 and is rounded to bf16 only as an operand of the chunk's read-out.
+ * Storage must be bf16 (SSM_F32 gives SSM_ERR_UNSUPPORTED).  dstate must be
+ * 32, 64, 128 or 256 and headdim a multiple of 16 (else SSM_ERR_UNSUPPORTED).
+ * x, z, y, B, C and final_state must be 16-byte aligned (else
+ * SSM_ERR_MISALIGNED).  Outputs must not overlap an input or each other.
+ * opts may be NULL.
+ */
+SSM_API ssm_status_t ssm_ssd_fwd(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, int64_t dstate,
+                                 int64_t ngroups, ssm_dtype_t dtype, const void *x, const void *dt, const float *A,
+                                 const void *B, const void *C, const float *D, const void *z,
+                                 const float *dt_bias, int dt_softplus, void *y, float *final_state, void *stream,
+                                 const ssm_ssd_opts_t *opts);
+
 /* Static string naming a status code ("SSM_OK", ...); never NULL. */
 SSM_API const char *ssm_status_string(ssm_status_t status);
 

@@ -30,7 +30,7 @@ STATUS_NAMES = {0: "SSM_OK", 1: "SSM_ERR_INVALID_ARG", 2: "SSM_ERR_UNSUPPORTED",
                 4: "SSM_ERR_HIP"}
 EXPORTED = ("ssm_scan_fwd", "ssm_scan_fwd_ex", "ssm_scan_bwd", "ssm_state_update", "ssm_state_update_ex",
             "ssm_causal_conv1d_fwd",
-            "ssm_causal_conv1d_update", "ssm_status_string", "ssm_last_error", "ssm_abi_version")
+            "ssm_causal_conv1d_update", "ssm_ssd_fwd", "ssm_status_string", "ssm_last_error", "ssm_abi_version")
 
 
 class SsmError(RuntimeError):
@@ -46,6 +46,10 @@ class ScanOpts(ctypes.Structure):
 
 class UpdateOpts(ctypes.Structure):
     _fields_ = [("bbar_mode", ctypes.c_int32), ("reserved", ctypes.c_int32 * 7)]
+
+
+class SsdOpts(ctypes.Structure):
+    _fields_ = [("head_slice", ctypes.c_int32), ("reserved", ctypes.c_int32 * 7)]
 
 
 SSM_BBAR_DELTA_B, SSM_BBAR_ZOH = 0, 1
@@ -78,6 +82,9 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
     lib.ssm_causal_conv1d_fwd.restype = i32
     lib.ssm_causal_conv1d_update.argtypes = [i64, i64, i64, i32, vp, vp, vp, vp, i32, vp, vp]
     lib.ssm_causal_conv1d_update.restype = i32
+    lib.ssm_ssd_fwd.argtypes = [i64, i64, i64, i64, i64, i64, i32, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp,
+                                ctypes.POINTER(SsdOpts)]
+    lib.ssm_ssd_fwd.restype = i32
     lib.ssm_status_string.argtypes = [i32]
     lib.ssm_status_string.restype = ctypes.c_char_p
     lib.ssm_last_error.argtypes = []
@@ -292,9 +299,48 @@ def ssm_causal_conv1d_update(conv_state: Optional[torch.Tensor], x: torch.Tensor
     return y
 
 
+def ssm_ssd_fwd(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, B: torch.Tensor, C: torch.Tensor,
+                D: Optional[torch.Tensor] = None, z: Optional[torch.Tensor] = None,
+                dt_bias: Optional[torch.Tensor] = None, dt_softplus: bool = False, *,
+                y: Optional[torch.Tensor] = None, final_state: Optional[torch.Tensor] = None,
+                return_final_state: bool = True, head_slice: int = 0,
+                stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Mamba-2 SSD layer forward (include/ssm.h: ssm_ssd_fwd).  x, z: (batch, seqlen, nheads,
+    headdim) bf16; dt: (batch, seqlen, nheads) bf16; B, C: (batch, seqlen, ngroups, dstate) bf16;
+    A, D, dt_bias: (nheads,) fp32.  Returns (y, final_state (batch, nheads, headdim, dstate) fp32
+    or None)."""
+    lib = load_library()
+    if x.dim() != 4 or B.dim() != 4:
+        raise ValueError("x must be (batch, seqlen, nheads, headdim) and B (batch, seqlen, ngroups, dstate)")
+    batch, seqlen, nheads, headdim = x.shape
+    ngroups, dstate = B.shape[2], B.shape[3]
+    dev, ty = x.device, x.dtype
+    code = _dtype_code(x)
+    _need(dt, "dt", (batch, seqlen, nheads), ty, dev)
+    _need(A, "A", (nheads,), torch.float32, dev)
+    _need(B, "B", (batch, seqlen, ngroups, dstate), ty, dev)
+    _need(C, "C", (batch, seqlen, ngroups, dstate), ty, dev)
+    _need(D, "D", (nheads,), torch.float32, dev, optional=True)
+    _need(z, "z", tuple(x.shape), ty, dev, optional=True)
+    _need(dt_bias, "dt_bias", (nheads,), torch.float32, dev, optional=True)
+    if y is None:
+        y = torch.empty_like(x)
+    _need(y, "y", tuple(x.shape), ty, dev)
+    if final_state is None and return_final_state:
+        final_state = torch.empty((batch, nheads, headdim, dstate), dtype=torch.float32, device=dev)
+    _need(final_state, "final_state", (batch, nheads, headdim, dstate), torch.float32, dev, optional=True)
+    opts = SsdOpts(head_slice=int(head_slice))
+    status = lib.ssm_ssd_fwd(batch, seqlen, nheads, headdim, dstate, ngroups, code, _ptr(x), _ptr(dt), _ptr(A),
+                             _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(dt_bias), int(bool(dt_softplus)), _ptr(y),
+                             _ptr(final_state), _stream(dev, stream), ctypes.byref(opts))
+    _check(status)
+    return y, final_state
+
+
 def abi_version() -> int:
     return load_library().ssm_abi_version()
 
 
-__all__ = ["ssm_scan_fwd", "ssm_scan_bwd", "ssm_state_update", "ssm_causal_conv1d_fwd", "ssm_causal_conv1d_update", "abi_version", "load_library", "SsmError", "ScanOpts", "UpdateOpts",
+__all__ = ["ssm_scan_fwd", "ssm_scan_bwd", "ssm_state_update", "ssm_causal_conv1d_fwd", "ssm_causal_conv1d_update",
+           "ssm_ssd_fwd", "SsdOpts", "abi_version", "load_library", "SsmError", "ScanOpts", "UpdateOpts",
            "LIBRARY", "EXPORTED"]

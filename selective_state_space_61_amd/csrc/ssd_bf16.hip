@@ -1,0 +1,20 @@
+// ssd_bf16.hip -- the Mamba-2 SSD chunk kernels, one per (dstate, waves per workgroup).
+#include <hip/hip_runtime.h>
+
+#include "ssd_fwd.hpp"
+
+namespace ssm {
+
+// Instantiated pairs: 4 waves for every dstate, 2 waves up to dstate 128 and 1 wave up to 64
+// (the per-thread staging registers grow as dstate / waves).
+SsdKernel ssd_kernel(int64_t dstate, int waves) {
+#define SSD_CASE(NN, W) \
+  if (dstate == NN && waves == W) return ssd_chunk_kernel<NN, W>;
+  SSD_CASE(32, 4) SSD_CASE(64, 4) SSD_CASE(128, 4) SSD_CASE(256, 4)
+  SSD_CASE(32, 2) SSD_CASE(64, 2) SSD_CASE(128, 2)
+  SSD_CASE(32, 1) SSD_CASE(64, 1)
+#undef SSD_CASE
+  return nullptr;
+}
+
+}  // namespace ssm

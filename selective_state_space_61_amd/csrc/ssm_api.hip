@@ -14,6 +14,7 @@
 #include "state_update.hpp"
 #include "conv1d.hpp"
 #include "scan_bwd.hpp"
+#include "ssd_fwd.hpp"
 
 namespace {
 
@@ -616,6 +617,86 @@ ssm_status_t ssm_causal_conv1d_update(int64_t batch, int64_t dim, int64_t width,
   hipLaunchKernelGGL(k, dim3(static_cast<unsigned>(blocks)), dim3(ssm::kConvThreads), 0,
                      static_cast<hipStream_t>(stream), a);
   return check_launch("causal conv1d update");
+}
+
+
+ssm_status_t ssm_ssd_fwd(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, int64_t dstate,
+                         int64_t ngroups, ssm_dtype_t dtype, const void* x, const void* dt, const float* A,
+                         const void* B, const void* C, const float* D, const void* z, const float* dt_bias,
+                         int dt_softplus, void* y, float* final_state, void* stream, const ssm_ssd_opts_t* opts) {
+  g_err[0] = '\0';
+  if (batch < 0 || seqlen < 0 || nheads < 1 || headdim < 1 || dstate < 1 || ngroups < 1)
+    return fail(SSM_ERR_INVALID_ARG, "bad size (batch=%lld seqlen=%lld nheads=%lld headdim=%lld dstate=%lld "
+                "ngroups=%lld)", (long long)batch, (long long)seqlen, (long long)nheads, (long long)headdim,
+                (long long)dstate, (long long)ngroups);
+  if (nheads % ngroups != 0)
+    return fail(SSM_ERR_INVALID_ARG, "ngroups %lld does not divide nheads %lld", (long long)ngroups,
+                (long long)nheads);
+  if (nheads > 0x7fffffff || headdim > 0x7fffffff)
+    return fail(SSM_ERR_INVALID_ARG, "nheads or headdim exceeds int32");
+  if (dtype != SSM_BF16 && dtype != SSM_F32) return fail(SSM_ERR_UNSUPPORTED, "unknown dtype %d", (int)dtype);
+  if (dtype != SSM_BF16) return fail(SSM_ERR_UNSUPPORTED, "the SSD kernels take bf16 storage only");
+  if (dstate != 32 && dstate != 64 && dstate != 128 && dstate != 256)
+    return fail(SSM_ERR_UNSUPPORTED, "dstate %lld not in {32, 64, 128, 256}", (long long)dstate);
+  if (headdim % 16 != 0) return fail(SSM_ERR_UNSUPPORTED, "headdim %lld is not a multiple of 16", (long long)headdim);
+  int slice = 0;
+  if (opts) {
+    for (int r : opts->reserved)
+      if (r != 0) return fail(SSM_ERR_INVALID_ARG, "reserved option fields must be zero");
+    slice = opts->head_slice;
+    if (slice != 0 && slice != 16 && slice != 32 && slice != 64)
+      return fail(SSM_ERR_INVALID_ARG, "head_slice %d not in {0, 16, 32, 64}", slice);
+    if (slice != 0 && headdim % slice != 0)
+      return fail(SSM_ERR_INVALID_ARG, "head_slice %d does not divide headdim %lld", slice, (long long)headdim);
+  }
+  int64_t nbh, n_tok, n_x, n_bc, n_dt, n_fs;
+  if (!mul_ok(batch, nheads, &nbh) || !mul_ok(batch, seqlen, &n_tok) || !mul_ok(n_tok, nheads * headdim * 2, &n_x) ||
+      !mul_ok(n_tok, ngroups * dstate * 2, &n_bc) || !mul_ok(n_tok, nheads * 2, &n_dt) ||
+      !mul_ok(nbh, headdim * dstate * 4, &n_fs))
+    return fail(SSM_ERR_INVALID_ARG, "tensor size overflows int64");
+  if (nbh == 0 || (seqlen == 0 && !final_state)) return SSM_OK;
+  if (!A || (seqlen > 0 && (!x || !dt || !B || !C || !y)))
+    return fail(SSM_ERR_INVALID_ARG, "NULL required pointer (A, and x, dt, B, C, y when seqlen > 0)");
+  const Arg args[] = {{x, 16, "x"}, {z, 16, "z"}, {y, 16, "y"}, {B, 16, "B"}, {C, 16, "C"}, {dt, 2, "dt"},
+                      {A, 4, "A"}, {D, 4, "D"}, {dt_bias, 4, "dt_bias"}, {final_state, 16, "final_state"}};
+  if (const Arg* bad = misaligned(args, sizeof args / sizeof args[0]))
+    return fail(SSM_ERR_MISALIGNED, "%s (%p) is not aligned to %lld bytes", bad->name, bad->p, (long long)bad->align);
+  const Range ry{seqlen > 0 ? y : nullptr, n_x}, rf{final_state, n_fs};
+  const Range ins[] = {{x, n_x}, {z, n_x}, {dt, n_dt}, {B, n_bc}, {C, n_bc}, {A, nheads * 4}, {D, nheads * 4},
+                       {dt_bias, nheads * 4}};
+  for (Range in : ins)
+    if (overlap(ry, in) || overlap(rf, in)) return fail(SSM_ERR_INVALID_ARG, "an output overlaps an input");
+  if (overlap(ry, rf)) return fail(SSM_ERR_INVALID_ARG, "y overlaps final_state");
+
+  // waves per workgroup (16 head channels each): the largest instantiated count whose grid still
+  // gives every compute unit a workgroup, else the smallest
+  int waves = slice / 16;
+  if (waves == 0) {
+    const int64_t cus = device_cus();
+    for (int w : {4, 2, 1}) {
+      if (headdim % (16 * w) != 0 || !ssm::ssd_kernel(dstate, w)) continue;
+      waves = w;
+      if (nbh * (headdim / (16 * w)) >= cus) break;
+    }
+  }
+  const ssm::SsdKernel k = ssm::ssd_kernel(dstate, waves);
+  if (!k)
+    return fail(SSM_ERR_UNSUPPORTED, "no SSD kernel for dstate %lld with %d head channels per workgroup",
+                (long long)dstate, 16 * waves);
+  const int64_t nslices = headdim / (16 * waves);
+  int64_t blocks;
+  if (!mul_ok(nbh, nslices, &blocks) || blocks > 0x7fffffff) return fail(SSM_ERR_UNSUPPORTED, "grid too large");
+  ssm::SsdArgs a{};
+  a.x = static_cast<const uint16_t*>(x); a.dt = static_cast<const uint16_t*>(dt); a.A = A;
+  a.B = static_cast<const uint16_t*>(B); a.C = static_cast<const uint16_t*>(C); a.D = D;
+  a.z = static_cast<const uint16_t*>(z); a.dt_bias = dt_bias; a.y = static_cast<uint16_t*>(y);
+  a.final_state = final_state;
+  a.batch = batch; a.seqlen = seqlen;
+  a.nheads = static_cast<int32_t>(nheads); a.headdim = static_cast<int32_t>(headdim);
+  a.ngroups = static_cast<int32_t>(ngroups); a.nslices = static_cast<int32_t>(nslices);
+  a.softplus = dt_softplus ? 1 : 0;
+  hipLaunchKernelGGL(k, dim3(static_cast<unsigned>(blocks)), dim3(64 * waves), 0, static_cast<hipStream_t>(stream), a);
+  return check_launch("SSD chunk kernel");
 }
 
 }  // extern "C"

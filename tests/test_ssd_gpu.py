@@ -1,0 +1,125 @@
+"""Parity of the HIP Mamba-2 SSD layer (through the C ABI) with the fp64 oracle.
+
+y and the final state are compared element by element under the bf16 tolerance rule
+(max |v - v_ref| <= 2e-2 * max |v_ref| per tensor): storage is bf16 and the chunk's products
+take bf16 operands with fp32 accumulation.  At the full 8 x 2048 size, sampled (batch row, head)
+pairs are compared with the oracle run on those heads alone, which is exact for them because
+heads do not interact."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from gpu_util import TOL, assert_close, say, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+TOL_SSD = TOL["bf16"]
+
+
+@pytest.fixture(scope="module")
+def o():
+    return oracle.load()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import selective_state_space_61_amd as ssm
+    ssm.load_library()
+    say(f"\n[gpu] {torch.cuda.get_device_name(0)}; library {ssm.LIBRARY}")
+
+
+def ssd_gpu(t, softplus=True, **kw):
+    import selective_state_space_61_amd as ssm
+    d = {k: to_dev(v) for k, v in t.items()}
+    y, fin = ssm.ssm_ssd_fwd(d["x"], d["dt"], d["A"], d["B"], d["C"], D=d["D"], z=d["z"], dt_bias=d["dt_bias"],
+                             dt_softplus=softplus, **kw)
+    torch.cuda.synchronize()
+    return y, fin
+
+
+def compare(o, t, what, softplus=True, nthreads=8, **kw):
+    say(f"[case] {what}")
+    y, fin = ssd_gpu(t, softplus, **kw)
+    y_ref, fin_ref = o.ssd(t["x"], t["dt"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"], dt_bias=t["dt_bias"],
+                           dt_softplus=softplus, nthreads=nthreads)
+    assert_close(to_host(y), y_ref, TOL_SSD, f"{what} y")
+    assert_close(to_host(fin), fin_ref, TOL_SSD, f"{what} final_state")
+    return y, fin
+
+
+# (dstate, head channels per workgroup) pairs the library instantiates
+PAIRS = [(32, 64), (64, 64), (128, 64), (256, 64), (32, 32), (64, 32), (128, 32), (32, 16), (64, 16)]
+
+
+@pytest.mark.parametrize("N,slice_", PAIRS)
+def test_kernel_variants(o, N, slice_):
+    t = W.ssd_inputs(2, 150, 4, 64, N, 2, seed=N + slice_)
+    compare(o, t, f"ssd N={N} slice={slice_}", head_slice=slice_)
+
+
+@pytest.mark.parametrize("L", [1, 5, 63, 64, 65, 128, 191])
+def test_ragged_lengths(o, L):
+    t = W.ssd_inputs(2, L, 3, 32, 64, 1, seed=L + 400)
+    compare(o, t, f"ssd L={L}")
+
+
+@pytest.mark.parametrize("shape", [(1, 70, 8, 16, 64, 8), (3, 90, 6, 48, 32, 3), (1, 100, 2, 128, 128, 1),
+                                   (2, 77, 4, 64, 256, 4)])
+def test_shapes(o, shape):
+    batch, L, H, P, N, G = shape
+    t = W.ssd_inputs(batch, L, H, P, N, G, seed=sum(shape))
+    compare(o, t, f"ssd shape {shape}")
+
+
+@pytest.mark.parametrize("variant", ["no_z", "no_D", "no_bias", "softplus_off", "bare"])
+def test_variants(o, variant):
+    softplus = variant not in ("softplus_off", "bare")
+    t = W.ssd_inputs(2, 130, 4, 32, 64, 2, seed=88, has_z=variant not in ("no_z", "bare"),
+                     has_D=variant not in ("no_D", "bare"), has_bias=softplus and variant != "no_bias")
+    if not softplus:
+        # raw dt is then the step itself: keep it positive and small, as softplus would
+        t["dt"] = W.f32_to_bf16_bits(np.abs(W.bf16_bits_to_f32(t["dt"])) * 0.1)
+    compare(o, t, f"ssd variant {variant}", softplus=softplus)
+
+
+def test_empty_and_deterministic(o):
+    import selective_state_space_61_amd as ssm
+    t = W.ssd_inputs(2, 0, 4, 64, 128, 1, seed=3)
+    y, fin = ssd_gpu(t)
+    assert y.numel() == 0 and torch.count_nonzero(fin).item() == 0
+    t = W.ssd_inputs(2, 200, 8, 64, 128, 1, seed=4)
+    y1, f1 = ssd_gpu(t)
+    y2, f2 = ssd_gpu(t)
+    assert torch.equal(y1, y2) and torch.equal(f1, f2), "two runs differ"
+    # every head-slice choice computes the same thing (different rounding only through the order
+    # of nothing: a channel's arithmetic does not depend on its workgroup)
+    y3, f3 = ssd_gpu(t, head_slice=32)
+    assert torch.equal(y1, y3) and torch.equal(f1, f3), "head slice changed the result"
+    del ssm
+
+
+def test_pages_layer_example(o):
+    """The Mamba2 layer example of the pages (d_model 2048, expand 2, headdim 64, d_state 128,
+    input (1, 1024, 2048)): 64 heads of 64 channels over 1024 steps, every element against the
+    oracle, in the launch configuration the benchmark times."""
+    w = W.SSD_WORKLOADS["mamba2_layer"]
+    compare(o, W.ssd_workload_inputs(w), "mamba2_layer (1, 1024, 64 x 64, N 128)", nthreads=16)
+
+
+def test_full_b8_sampled_heads(o):
+    """8 sequences of 2048 steps, 64 heads: sampled (batch row, head) pairs against the oracle run
+    on those heads alone (ngroups 1, so every head reads the same B and C)."""
+    w = W.SSD_WORKLOADS["mamba2_layer_b8"]
+    t = W.ssd_workload_inputs(w)
+    y, fin = ssd_gpu(t)
+    rows, heads = np.array([0, 7]), np.array([0, 1, 31, 63])
+    sub = {"x": t["x"][rows][:, :, heads], "dt": t["dt"][rows][:, :, heads], "B": t["B"][rows], "C": t["C"][rows],
+           "z": t["z"][rows][:, :, heads], "A": t["A"][heads], "D": t["D"][heads], "dt_bias": t["dt_bias"][heads]}
+    sub = {k: np.ascontiguousarray(v) for k, v in sub.items()}
+    y_ref, fin_ref = o.ssd(sub["x"], sub["dt"], sub["A"], sub["B"], sub["C"], D=sub["D"], z=sub["z"],
+                           dt_bias=sub["dt_bias"], dt_softplus=True, nthreads=16)
+    assert_close(to_host(y)[rows][:, :, heads], y_ref, TOL_SSD, "mamba2_layer_b8 y sampled")
+    assert_close(to_host(fin)[rows][:, heads], fin_ref, TOL_SSD, "mamba2_layer_b8 final_state sampled")

@@ -22,6 +22,11 @@ these tensors stand in for them):
 * ``conv`` (the depthwise convolution before the scan) -- x ~ N(0, 1) as above; weight and bias
   ~ U(-1/sqrt(K), 1/sqrt(K)), the default initialisation range of a depthwise Conv1d whose
   fan-in is the kernel width K; an initial state, when asked for, ~ N(0, 1).
+* ``ssd`` (the Mamba-2 SSD layer: heads of headdim channels, one scalar A per head, B and C per
+  group of heads) -- x, B, C, z ~ N(0, 1); raw dt = 0.5 * N(0, 1) per (step, head); dt bias as
+  in ``default``, per head; A_h = -U(1, 16) per head; D = 1 per head.  The pages give the layer's
+  shapes (headdim 64, d_state 128, expand 2) but no initialisation, so these ranges are a choice:
+  decays exp(dt A) between about 0.2 and 1 per step.
 * ``genomics`` -- a one-hot 4-symbol alphabet (s_t ~ U{0..3}) projected by a
   seeded (4, dim) matrix W ~ N(0, 0.5^2), so x[b, t, :] = W[s_t, :]; delta is
   passed directly (no softplus, no bias) and is log-uniform in [1e-4, 1e-1];
@@ -36,7 +41,7 @@ import numpy as np
 
 # Stream ids: one Philox key per (seed, tensor).
 _TENSOR_IDS = {"x": 1, "delta": 2, "B": 3, "C": 4, "z": 5, "bias": 6, "symbols": 7, "W": 8, "conv_w": 9,
-               "conv_b": 10, "conv_state": 11}
+               "conv_b": 10, "conv_state": 11, "A": 12}
 
 _CHUNK = 1 << 24  # elements per draw; bounds temporary memory for the 1M-step workload
 
@@ -172,6 +177,53 @@ def conv_inputs(batch: int, seqlen: int, dim: int, width: int, dtype: str = "f32
     b = _uniform(seed, "conv_b", (dim,), -bound, bound) if has_bias else None
     init = _normal(seed, "conv_state", (batch, dim, width - 1)) if has_init else None
     return {"x": _store(x, dtype), "weight": w, "bias": b, "init": None if init is None else _store(init, dtype)}
+
+
+@dataclass(frozen=True)
+class SsdWorkload:
+    name: str
+    batch: int
+    seqlen: int
+    nheads: int
+    headdim: int
+    dstate: int
+    ngroups: int
+    seed: int
+    note: str = field(default="", compare=False)
+
+
+SSD_WORKLOADS: Dict[str, SsdWorkload] = {
+    "mamba2_layer": SsdWorkload("mamba2_layer", batch=1, seqlen=1024, nheads=64, headdim=64, dstate=128, ngroups=1,
+                                seed=61010, note="the Mamba2 layer example: d_model 2048, expand 2, headdim 64, "
+                                "d_state 128, input (1, 1024, 2048)"),
+    "mamba2_layer_b8": SsdWorkload("mamba2_layer_b8", batch=8, seqlen=2048, nheads=64, headdim=64, dstate=128,
+                                   ngroups=1, seed=61011, note="the same layer on 8 sequences of 2048 steps"),
+}
+
+
+def ssd_inputs(batch: int, seqlen: int, nheads: int, headdim: int, dstate: int, ngroups: int = 1, seed: int = 0,
+               has_z: bool = True, has_D: bool = True, has_bias: bool = True) -> Dict[str, Optional[np.ndarray]]:
+    """Inputs of one SSD layer call (bf16 storage): x, z (batch, seqlen, nheads, headdim); dt
+    (batch, seqlen, nheads); B, C (batch, seqlen, ngroups, dstate) as uint16 bf16 bits; A, D,
+    dt_bias (nheads,) fp32."""
+    shx = (batch, seqlen, nheads, headdim)
+    x = _normal(seed, "x", shx)
+    dt = _normal(seed, "delta", (batch, seqlen, nheads), 0.5)
+    B = _normal(seed, "B", (batch, seqlen, ngroups, dstate))
+    C = _normal(seed, "C", (batch, seqlen, ngroups, dstate))
+    z = _normal(seed, "z", shx) if has_z else None
+    A = -_uniform(seed, "A", (nheads,), 1.0, 16.0)
+    D = np.ones(nheads, np.float32) if has_D else None
+    bias = None
+    if has_bias:
+        v = _log_uniform(seed, "bias", (nheads,), -3.0, -1.0).astype(np.float64)
+        bias = np.log(np.expm1(v)).astype(np.float32)
+    return {"x": _store(x, "bf16"), "dt": _store(dt, "bf16"), "B": _store(B, "bf16"), "C": _store(C, "bf16"),
+            "z": None if z is None else _store(z, "bf16"), "A": A, "D": D, "dt_bias": bias}
+
+
+def ssd_workload_inputs(w: SsdWorkload) -> Dict[str, Optional[np.ndarray]]:
+    return ssd_inputs(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups, w.seed)
 
 
 def workload_inputs(w: Workload) -> Dict[str, Optional[np.ndarray]]:
