@@ -36,6 +36,7 @@ _CSRC = "selective_state_space_61_amd/csrc/"
 KERNEL_SOURCES = {
     "scan": [_CSRC + f for f in ("scan_fwd.hpp", "scan_table.hpp", "scan_bf16.hip", "scan_f32.hip", "ssm_device.hpp")],
     "conv": [_CSRC + f for f in ("conv1d.hpp", "ssm_device.hpp")],
+    "ssd": [_CSRC + f for f in ("ssd_fwd.hpp", "ssd_bf16.hip", "ssm_device.hpp")],
 }
 
 
@@ -249,6 +250,82 @@ def bench_conv(steps, warmup, torch, np, W, ssm, device):
     return res
 
 
+def time_graph(torch, call, steps, warmup, device):
+    """Captures `steps` calls as one HIP graph (after `warmup` eager calls) and times one replay:
+    short kernels are then timed without the host launch path between them.  Returns ms per call."""
+    for i in range(warmup):
+        call(i)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream(device)
+    side.wait_stream(torch.cuda.current_stream(device))
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            for i in range(steps):
+                call(i)
+    torch.cuda.synchronize()
+    graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    del graph
+    return e0.elapsed_time(e1) / steps
+
+
+def ssd_bytes(w):
+    """Algorithmic bytes of one SSD layer call: x and z read and y written once (bf16), dt, B and
+    C read once, the per-head parameters, and the fp32 final state written."""
+    tok = w.batch * w.seqlen
+    return (3 * tok * w.nheads * w.headdim * 2 + tok * w.nheads * 2 + 2 * tok * w.ngroups * w.dstate * 2
+            + 3 * w.nheads * 4 + w.batch * w.nheads * w.headdim * w.dstate * 4)
+
+
+def ssd_flops(w):
+    """Matrix-core flops of the chunked form per call (64-step chunks, per head): C B^T over the
+    causal lower triangle of each chunk, the masked product with X, the read-out C S and the
+    state update B^T X."""
+    q = 64
+    tri = q * (q + 1) // 2
+    per_chunk = 2 * (tri * w.dstate + tri * w.headdim + 2 * q * w.dstate * w.headdim)
+    return per_chunk * w.batch * w.nheads * ((w.seqlen + q - 1) // q)
+
+
+def bench_ssd(name, steps, warmup, torch, np, W, ssm, device):
+    """The Mamba-2 SSD layer (ssm_ssd_fwd) on a named workload, inputs resident in HBM and rotated
+    to defeat the Infinity Cache, timed as a replayed HIP graph."""
+    w = W.SSD_WORKLOADS[name]
+    t = W.ssd_workload_inputs(w)
+    set_bytes = ssd_bytes(w)
+    copies = max(1, min(8, math.ceil(2 * MALL_BYTES / set_bytes)))
+    sets = []
+    for _ in range(copies):
+        d = {k: dev_tensor(v, torch, np, device) for k, v in t.items()}
+        d["y"] = torch.empty_like(d["x"])
+        d["fin"] = torch.empty(w.batch, w.nheads, w.headdim, w.dstate, device=device)
+        sets.append(d)
+    del t
+
+    def call(i):
+        d = sets[i % copies]
+        ssm.ssm_ssd_fwd(d["x"], d["dt"], d["A"], d["B"], d["C"], D=d["D"], z=d["z"], dt_bias=d["dt_bias"],
+                        dt_softplus=True, y=d["y"], final_state=d["fin"])
+
+    ms = time_graph(torch, call, steps, warmup, device)
+    del sets
+    torch.cuda.empty_cache()
+    flops = ssd_flops(w)
+    tokens = w.batch * w.seqlen
+    return {"workload": name, "batch": w.batch, "seqlen": w.seqlen, "nheads": w.nheads, "headdim": w.headdim,
+            "dstate": w.dstate, "ngroups": w.ngroups, "io_dtype": "bf16", "rotated_input_sets": copies,
+            "kernel_ms": ms, "tokens_per_s": tokens / (ms * 1e-3),
+            "elems_per_s": tokens * w.nheads * w.headdim / (ms * 1e-3), "alg_bytes": set_bytes,
+            "hbm_gbps": set_bytes / (ms * 1e-3) / 1e9, "hbm_frac": set_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+            "mfma_flops": flops, "mfma_tflops": flops / (ms * 1e-3) / 1e12}
+
+
 def bench_scan_bwd(steps, warmup, torch, np, W, ssm, device):
     """The backward scan on the 130M-shaped layer (inputs, dy and gradients resident in HBM;
     two input sets rotated).  Reports the time per call of the whole backward (both kernels)."""
@@ -380,6 +457,8 @@ def profile_mode(args):
     elif args.workload == "bwd":
         res = bench_scan_bwd(args.steps, args.warmup, torch, np, W, ssm, torch.device("cuda:0"))
         res["kernel_ms"] = res["ms_per_call"]
+    elif args.workload in W.SSD_WORKLOADS:
+        res = bench_ssd(args.workload, args.steps, args.warmup, torch, np, W, ssm, torch.device("cuda:0"))
     else:
         res = bench_scan(args.workload, args.steps, args.warmup, torch, np, W, ssm, torch.device("cuda:0"))
     log(f"[profile] {args.workload}: {res['kernel_ms'] * 1e3:.1f} us/launch over {args.steps} launches")
@@ -400,9 +479,10 @@ def summarize_traffic(fetch_csv, write_csv, workload):
         return vals
 
     fetch, write = per_kernel(fetch_csv, "FETCH_SIZE"), per_kernel(write_csv, "WRITE_SIZE")
-    family = "conv" if workload == "conv" else "scan"
+    family = "conv" if workload == "conv" else "ssd" if workload in W.SSD_WORKLOADS else "scan"
     calib = [k for k in fetch if "copy" in k.lower()]
-    scan = [k for k in fetch if ("causal_conv1d_kernel" if family == "conv" else "scan_chunk_kernel") in k]
+    marker = {"conv": "causal_conv1d_kernel", "ssd": "ssd_chunk_kernel", "scan": "scan_chunk_kernel"}[family]
+    scan = [k for k in fetch if marker in k]
     if not calib or not scan:
         raise SystemExit(f"calibration or measured kernel missing in {fetch_csv}: {list(fetch)}")
     ck, sk = calib[0], scan[0]
@@ -413,6 +493,8 @@ def summarize_traffic(fetch_csv, write_csv, workload):
     if family == "conv":
         c = CONV_SHAPE
         alg = conv_bytes(c["batch"], c["seqlen"], c["dim"], c["width"], 2)
+    elif family == "ssd":
+        alg = ssd_bytes(W.SSD_WORKLOADS[workload])
     else:
         w = W.WORKLOADS[workload]
         es = 2 if w.dtype == "bf16" else 4
@@ -436,7 +518,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="mamba130m",
-                    choices=["mamba130m", "mamba2p8b", "genomics", "decode", "conv", "bwd"])
+                    choices=["mamba130m", "mamba2p8b", "genomics", "decode", "conv", "bwd", "mamba2_layer",
+                             "mamba2_layer_b8"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the context measurements (2.8B scan, decode)")
     ap.add_argument("--profile-mode", action="store_true",
@@ -464,7 +547,7 @@ def main():
     import selective_state_space_61_amd as ssm
     from selective_state_space_61_amd import build as hip_build
 
-    if args.workload in ("decode", "conv", "bwd"):
+    if args.workload in ("decode", "conv", "bwd", "mamba2_layer", "mamba2_layer_b8"):
         raise SystemExit(f"{args.workload} is measured as context next to a scan workload; use --profile-mode for it alone")
     if not os.path.exists(ssm.LIBRARY):
         hip_build.build(verbose=True)
@@ -499,6 +582,12 @@ def main():
             f"{extra['causal_conv1d']['hbm_gbps']:.0f} GB/s")
         extra["causal_conv1d_update"] = bench_conv_update(256, torch, np, W, ssm, device)
         log(f"[bench] conv update: {extra['causal_conv1d_update']['ms_per_step'] * 1e3:.2f} us/step")
+        for sname in ("mamba2_layer", "mamba2_layer_b8"):
+            r = bench_ssd(sname, max(10, args.steps // 2), 3, torch, np, W, ssm, device)
+            r["traffic"] = traffic_from_profiles(sname, r["alg_bytes"])[0]
+            extra["ssd_" + sname] = r
+            log(f"[bench] SSD {sname}: {r['kernel_ms'] * 1e3:.1f} us/call, {r['hbm_gbps']:.0f} GB/s, "
+                f"{r['mfma_tflops']:.1f} TFLOP/s on matrix cores")
 
     hbm_frac = main_res["hbm_frac"]
     alu_frac = main_res["valu_slot_frac"]

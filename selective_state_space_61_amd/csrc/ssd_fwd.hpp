@@ -90,13 +90,36 @@ __device__ __forceinline__ float bf16_elem(ssd_u32x4_t v) {
   return (E & 1) ? bf16_hi(v[E / 2]) : bf16_lo(v[E / 2]);
 }
 
+// Workgroups of 4 waves (dstate <= 128) keep two workgroups per compute unit: their LDS fits
+// twice in 160 KB and the registers are held to 256 per lane.
+// Inclusive prefix sum over the 64 lanes of a wave with DPP (gfx9): shifts by 1, 2, 4, 8 within
+// each row of 16 (lanes shifted in from outside the row read 0), then lane 15 of each row is
+// added to rows 1 and 3 and lane 31 to rows 2 and 3.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_or_zero(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROW_MASK, 0xF, true));
+}
+__device__ __forceinline__ float wave_inclusive_sum(float v) {
+  v += dpp_or_zero<0x111, 0xF>(v);  // row_shr:1
+  v += dpp_or_zero<0x112, 0xF>(v);  // row_shr:2
+  v += dpp_or_zero<0x114, 0xF>(v);  // row_shr:4
+  v += dpp_or_zero<0x118, 0xF>(v);  // row_shr:8
+  v += dpp_or_zero<0x142, 0xA>(v);  // row_bcast:15 into rows 1, 3
+  v += dpp_or_zero<0x143, 0xC>(v);  // row_bcast:31 into rows 2, 3
+  return v;
+}
+
 template <int N, int NW>
-__global__ __launch_bounds__(64 * NW) void ssd_chunk_kernel(const SsdArgs p) {
+constexpr int kSsdWavesPerEu = (NW == 4 && N <= 128) ? 2 : 1;
+
+template <int N, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(kSsdWavesPerEu<N, NW>)))
+void ssd_chunk_kernel(const SsdArgs p) {
   constexpr int Q = kSsdChunk;
   constexpr int PS = 16 * NW;  // head channels per workgroup
   constexpr int T = 64 * NW;   // threads
   constexpr int LDB = N + 8;   // row stride (elements) of the row-major B and C tiles
-  constexpr int LDT = Q + 8;   // row stride of the transposed tiles (B^T, X^T, weighted X^T)
+  constexpr int LDT = Q + 8;   // row stride of the step-indexed tiles (B^T, X^T, weighted X^T, M)
   constexpr int NKS = N / 32;  // K = 32 steps over dstate
   constexpr int NT = N / 16;   // 16-row tiles of S per wave
   constexpr int kBTasks = 4 * N;  // (row pair, 8-column group) pieces of B
@@ -111,6 +134,7 @@ __global__ __launch_bounds__(64 * NW) void ssd_chunk_kernel(const SsdArgs p) {
   __shared__ __align__(16) uint16_t s_bt[N * LDT];   // B^T[n][j]
   __shared__ __align__(16) uint16_t s_xt[PS * LDT];  // X^T[p][j]
   __shared__ __align__(16) uint16_t s_xw[PS * LDT];  // X^T[p][j] * exp(cum_last - cum_j) dt_j
+  __shared__ __align__(16) uint16_t s_m[Q * LDT];    // M[i][j] = (C_i . B_j) exp(cum_i - cum_j) dt_j, j <= i
   __shared__ __align__(16) float s_cum[Q];           // cum_j in log2 units
   __shared__ __align__(16) float s_dt[Q];            // dt_j (0 past the end of the sequence)
 
@@ -128,11 +152,12 @@ __global__ __launch_bounds__(64 * NW) void ssd_chunk_kernel(const SsdArgs p) {
   const float A2 = p.A[h] * kLog2e;
   const float bias = p.dt_bias ? p.dt_bias[h] : 0.0f;
   const float Dh = p.D ? p.D[h] : 0.0f;
-  const int pw = 16 * wave + l16;  // this lane's channel within the slice
+  const int pw = 16 * wave + l16;     // this lane's S column (A-operand row of the products)
+  const int pe = 16 * wave + 4 * q;   // first of the 4 channels this lane writes
 
   const uint16_t* xg = p.x + (b * L * H + h) * P + p0;  // step t at xg + t * H * P
-  const uint16_t* zg = p.z ? p.z + (b * L * H + h) * P + p0 + pw : nullptr;
-  uint16_t* yg = p.y + (b * L * H + h) * P + p0 + pw;
+  const uint16_t* zg = p.z ? p.z + (b * L * H + h) * P + p0 + pe : nullptr;
+  uint16_t* yg = p.y + (b * L * H + h) * P + p0 + pe;
   const uint16_t* bg = p.B + (b * L * G + g) * N;  // step t at bg + t * G * N
   const uint16_t* cg = p.C + (b * L * G + g) * N;
   const uint16_t* dtg = p.dt + b * L * H + h;       // step t at dtg + t * H
@@ -140,10 +165,14 @@ __global__ __launch_bounds__(64 * NW) void ssd_chunk_kernel(const SsdArgs p) {
 
   // Registers that carry the next chunk's inputs while the current one is computed.
   ssd_u32x4_t rb[kBPer][2], rc[kCPer], rx[2];
+  ssd_u32x2_t rz[4];
   uint32_t rdt = 0u;
-  uint16_t rz[16] = {};
+#pragma unroll
+  for (int k = 0; k < 4; ++k) rz[k] = ssd_u32x2_t{0u, 0u};
 
-  auto load_chunk = [&](int64_t t0) {
+  // FULL: all 64 steps of the chunk are inside the sequence (no bounds checks).
+  auto load_chunk = [&](int64_t t0, auto full) {
+    constexpr bool FULL = decltype(full)::value;
 #pragma unroll
     for (int u = 0; u < kBPer; ++u) {
       const int k = tid + u * T;
@@ -152,7 +181,8 @@ __global__ __launch_bounds__(64 * NW) void ssd_chunk_kernel(const SsdArgs p) {
 #pragma unroll
         for (int hb = 0; hb < 2; ++hb) {
           const int64_t t = t0 + 2 * rp + hb;
-          rb[u][hb] = t < L ? *reinterpret_cast<const ssd_u32x4_t*>(bg + t * bs + 8 * c8) : ssd_u32x4_t{0, 0, 0, 0};
+          rb[u][hb] = (FULL || t < L) ? *reinterpret_cast<const ssd_u32x4_t*>(bg + t * bs + 8 * c8)
+                                      : ssd_u32x4_t{0, 0, 0, 0};
         }
       }
     }
@@ -162,7 +192,7 @@ __global__ __launch_bounds__(64 * NW) void ssd_chunk_kernel(const SsdArgs p) {
       if (kCPer * T == kCTasks || k < kCTasks) {
         const int c8 = k % (N / 8), i = k / (N / 8);
         const int64_t t = t0 + i;
-        rc[u] = t < L ? *reinterpret_cast<const ssd_u32x4_t*>(cg + t * bs + 8 * c8) : ssd_u32x4_t{0, 0, 0, 0};
+        rc[u] = (FULL || t < L) ? *reinterpret_cast<const ssd_u32x4_t*>(cg + t * bs + 8 * c8) : ssd_u32x4_t{0, 0, 0, 0};
       }
     }
     {
@@ -170,20 +200,20 @@ __global__ __launch_bounds__(64 * NW) void ssd_chunk_kernel(const SsdArgs p) {
 #pragma unroll
       for (int hb = 0; hb < 2; ++hb) {
         const int64_t t = t0 + 2 * rp + hb;
-        rx[hb] = t < L ? *reinterpret_cast<const ssd_u32x4_t*>(xg + t * xs + 8 * p8) : ssd_u32x4_t{0, 0, 0, 0};
+        rx[hb] = (FULL || t < L) ? *reinterpret_cast<const ssd_u32x4_t*>(xg + t * xs + 8 * p8) : ssd_u32x4_t{0, 0, 0, 0};
       }
     }
-    rdt = (t0 + lane < L) ? dtg[(t0 + lane) * H] : 0u;
+    rdt = (FULL || t0 + lane < L) ? dtg[(t0 + lane) * H] : 0u;
     if (zg) {
 #pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        const int64_t t = t0 + 16 * (k / 4) + 4 * q + (k % 4);
-        rz[k] = t < L ? zg[t * xs] : uint16_t(0);
+      for (int ib = 0; ib < 4; ++ib) {
+        const int64_t t = t0 + 16 * ib + l16;
+        rz[ib] = (FULL || t < L) ? *reinterpret_cast<const ssd_u32x2_t*>(zg + t * xs) : ssd_u32x2_t{0u, 0u};
       }
     }
   };
 
-  // Writes the chunk held in registers to LDS (z stays in registers for the epilogue).
+  // Writes the chunk held in registers to LDS.
   auto stage_chunk = [&](int64_t t0) {
     // dt and the cumulative decay: lane l of every wave holds step l of the chunk
     float dtv = 0.0f;
@@ -191,13 +221,8 @@ __global__ __launch_bounds__(64 * NW) void ssd_chunk_kernel(const SsdArgs p) {
       const float v = bf16_lo(rdt) + bias;
       dtv = p.softplus ? softplus_f32(v) : v;
     }
-    float cum = dtv * A2;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const float u = __shfl_up(cum, o);
-      if (lane >= o) cum += u;
-    }
-    const float last = __shfl(cum, 63);
+    const float cum = wave_inclusive_sum(dtv * A2);
+    const float last = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, cum), 63));
     const float wgt = hw_exp2(last - cum) * dtv;
     if (wave == 0) {
       s_cum[lane] = cum;
@@ -248,82 +273,92 @@ __global__ __launch_bounds__(64 * NW) void ssd_chunk_kernel(const SsdArgs p) {
   for (int nb = 0; nb < NT; ++nb) S[nb] = ssd_f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
   const int64_t nchunks = (L + Q - 1) / Q;
-  if (nchunks > 0) load_chunk(0);
+  using Full = std::integral_constant<bool, true>;
+  using Ragged = std::integral_constant<bool, false>;
+  if (nchunks > 0) {
+    if (Q <= L) load_chunk(0, Full{});
+    else load_chunk(0, Ragged{});
+  }
   for (int64_t c = 0; c < nchunks; ++c) {
     const int64_t t0 = c * Q;
     __syncthreads();  // every wave is done with the previous chunk's tiles
     stage_chunk(t0);
-    uint16_t zc[16];
+    ssd_u32x2_t zc[4];
 #pragma unroll
-    for (int k = 0; k < 16; ++k) zc[k] = rz[k];
+    for (int k = 0; k < 4; ++k) zc[k] = rz[k];
     __syncthreads();
-    if (c + 1 < nchunks) load_chunk(t0 + Q);
+    if (c + 1 < nchunks) {
+      if (t0 + 2 * Q <= L) load_chunk(t0 + Q, Full{});
+      else load_chunk(t0 + Q, Ragged{});
+    }
+    // M, split over the waves: G^T tile (j-block jb, i-block ib) = B_j . C_i, masked to j <= i,
+    // decayed and stored as M[i][j].  The masked product reads M in K = 32 steps, so besides the
+    // ten tiles jb <= ib it needs the two tiles (ib, jb) = (0, 1), (2, 3) just past the diagonal,
+    // which the mask zeroes.  Twelve tiles, 12 / NW per wave, in one straight-line block.
+#pragma unroll
+    for (int s = 0; s < 12 / NW; ++s) {
+      const int k = wave + NW * s;
+      const int ib = k < 4 ? k / 2 : k / 4 + 1, jb = k < 4 ? k % 2 : k % 4;
+      const int irow = 16 * ib + l16;
+      ssd_f32x4_t gt = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks)
+        gt = mfma16x16x32(*reinterpret_cast<const ssd_u32x4_t*>(&s_b[(16 * jb + l16) * LDB + 32 * ks + 8 * q]),
+                          *reinterpret_cast<const ssd_u32x4_t*>(&s_c[irow * LDB + 32 * ks + 8 * q]), gt);
+      const float cum_i = s_cum[irow];
+      const ssd_f32x4_t cj = *reinterpret_cast<const ssd_f32x4_t*>(&s_cum[16 * jb + 4 * q]);
+      const ssd_f32x4_t dj = *reinterpret_cast<const ssd_f32x4_t*>(&s_dt[16 * jb + 4 * q]);
+      float m[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) m[r] = (16 * jb + 4 * q + r <= irow) ? gt[r] * hw_exp2(cum_i - cj[r]) * dj[r] : 0.0f;
+      *reinterpret_cast<ssd_u32x2_t*>(&s_m[irow * LDT + 16 * jb + 4 * q]) =
+          ssd_u32x2_t{pack_bf16x2(m[0], m[1]), pack_bf16x2(m[2], m[3])};
+    }
 
-    // S entering the chunk as bf16 B operands of the read-out (k permuted as the tiles hold it)
+    // S entering the chunk as bf16 A operands of the read-out, S^T[p][n] with n permuted as the
+    // tiles hold it
     ssd_u32x4_t sf[NKS];
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks)
       sf[ks] = ssd_u32x4_t{pack_bf16x2(S[2 * ks][0], S[2 * ks][1]), pack_bf16x2(S[2 * ks][2], S[2 * ks][3]),
                            pack_bf16x2(S[2 * ks + 1][0], S[2 * ks + 1][1]),
                            pack_bf16x2(S[2 * ks + 1][2], S[2 * ks + 1][3])};
+    __syncthreads();  // M complete
 
+    // Y^T tiles (channels 16 wave .. +15, steps 16 ib .. +15): the read-out exp(cum_i) S^T C_i^T
+    // plus the masked product X^T M^T over the steps j <= i
+    ssd_f32x4_t acc[4];
 #pragma unroll
     for (int ib = 0; ib < 4; ++ib) {
-      const int irow = 16 * ib + l16;  // the output row whose C this lane supplies
-      ssd_f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
-      // read-out of the entering state, exp(cum_i) C_i S
+      const int irow = 16 * ib + l16;  // the output step this lane holds
+      acc[ib] = ssd_f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) acc = mfma16x16x32(load_perm_frag(&s_c[irow * LDB + 32 * ks + 4 * q]), sf[ks], acc);
-      {
-        const ssd_f32x4_t ci = *reinterpret_cast<const ssd_f32x4_t*>(&s_cum[16 * ib + 4 * q]);
+      for (int ks = 0; ks < NKS; ++ks)
+        acc[ib] = mfma16x16x32(sf[ks], load_perm_frag(&s_c[irow * LDB + 32 * ks + 4 * q]), acc[ib]);
+    }
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc[r] *= hw_exp2(ci[r]);
-      }
-      // G^T tiles (j-block jb, i-block ib) = B_j . C_i for jb <= ib, masked and decayed, packed
-      // as the A operand of the masked product (k-step jb / 2, half jb % 2)
-      ssd_u32x4_t cf[NKS];
+    for (int ib = 0; ib < 4; ++ib) {
+      const int irow = 16 * ib + l16;
+      acc[ib] *= hw_exp2(s_cum[irow]);
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) cf[ks] = *reinterpret_cast<const ssd_u32x4_t*>(&s_c[irow * LDB + 32 * ks + 8 * q]);
-      const float cum_i = s_cum[irow];
-      ssd_u32x4_t mf[2];
+      for (int ks = 0; ks <= ib / 2; ++ks)
+        acc[ib] = mfma16x16x32(*reinterpret_cast<const ssd_u32x4_t*>(&s_xt[pw * LDT + 32 * ks + 8 * q]),
+                               *reinterpret_cast<const ssd_u32x4_t*>(&s_m[irow * LDT + 32 * ks + 8 * q]), acc[ib]);
+    }
+    // skip term, gate, store: channels pe .. pe + 3 of step 16 ib + l16
+    const bool full = t0 + Q <= L;
 #pragma unroll
-      for (int jb = 0; jb <= ib; ++jb) {
-        ssd_f32x4_t gt = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks)
-          gt = mfma16x16x32(*reinterpret_cast<const ssd_u32x4_t*>(&s_b[(16 * jb + l16) * LDB + 32 * ks + 8 * q]),
-                            cf[ks], gt);
-        const ssd_f32x4_t cj = *reinterpret_cast<const ssd_f32x4_t*>(&s_cum[16 * jb + 4 * q]);
-        const ssd_f32x4_t dj = *reinterpret_cast<const ssd_f32x4_t*>(&s_dt[16 * jb + 4 * q]);
-        float m[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int j = 16 * jb + 4 * q + r;
-          m[r] = j <= irow ? gt[r] * hw_exp2(cum_i - cj[r]) * dj[r] : 0.0f;
-        }
-        const uint32_t w01 = pack_bf16x2(m[0], m[1]), w23 = pack_bf16x2(m[2], m[3]);
-        if (jb & 1) {
-          mf[jb >> 1][2] = w01;
-          mf[jb >> 1][3] = w23;
-        } else {
-          mf[jb >> 1] = ssd_u32x4_t{w01, w23, 0u, 0u};
-        }
-      }
-      // masked product with X over the steps j <= i
-#pragma unroll
-      for (int ks = 0; ks <= ib / 2; ++ks) acc = mfma16x16x32(mf[ks], load_perm_frag(&s_xt[pw * LDT + 32 * ks + 4 * q]), acc);
-      // skip term, gate, store: rows 16 ib + 4 q + r of channel pw
-      const ssd_u32x2_t xv = *reinterpret_cast<const ssd_u32x2_t*>(&s_xt[pw * LDT + 16 * ib + 4 * q]);
+    for (int ib = 0; ib < 4; ++ib) {
+      const int irow = 16 * ib + l16;
+      float yv[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int64_t t = t0 + 16 * ib + 4 * q + r;
-        if (t < L) {
-          const float xr = (r & 1) ? bf16_hi(xv[r / 2]) : bf16_lo(xv[r / 2]);
-          float yv = fmaf(Dh, xr, acc[r]);
-          if (zg) yv *= silu_f32(bf16_lo(zc[4 * ib + r]));
-          yg[t * xs] = to_bf16(yv);
-        }
+        yv[r] = fmaf(Dh, bf16_lo(s_xt[(pe + r) * LDT + irow]), acc[ib][r]);
+        if (zg) yv[r] *= silu_f32((r & 1) ? bf16_hi(zc[ib][r / 2]) : bf16_lo(zc[ib][r / 2]));
       }
+      const int64_t t = t0 + irow;
+      if (full || t < L)
+        *reinterpret_cast<ssd_u32x2_t*>(yg + t * xs) = ssd_u32x2_t{pack_bf16x2(yv[0], yv[1]), pack_bf16x2(yv[2], yv[3])};
     }
 
     // state update: S = exp(cum_last) S + B^T (weighted X)
