@@ -257,8 +257,8 @@ SSM_API ssm_status_t ssm_state_update_ex(int64_t batch, int64_t dim, int64_t dst
                                          int delta_softplus, void *y, void *stream, const ssm_update_opts_t *opts);
 
 /* Options of ssm_ssd_fwd.  head_slice: head channels per workgroup (16, 32
- * or 64, dividing headdim), or 0 to let the library choose from the grid
- * size; reserved must be zero. */
+ * or 64, dividing headdim), or 0 for the largest one the library has for
+ * this dstate and headdim; reserved must be zero. */
 typedef struct {
   int32_t head_slice;
   int32_t reserved[7];

@@ -668,15 +668,17 @@ ssm_status_t ssm_ssd_fwd(int64_t batch, int64_t seqlen, int64_t nheads, int64_t 
     if (overlap(ry, in) || overlap(rf, in)) return fail(SSM_ERR_INVALID_ARG, "an output overlaps an input");
   if (overlap(ry, rf)) return fail(SSM_ERR_INVALID_ARG, "y overlaps final_state");
 
-  // waves per workgroup (16 head channels each): the largest instantiated count whose grid still
-  // gives every compute unit a workgroup, else the smallest
+  // waves per workgroup (16 head channels each): the largest instantiated count.  Measured on
+  // MI355X (dstate 128, headdim 64): 64 workgroups of 4 waves beat 128 of 2 waves (71 vs 82 us on
+  // 1 x 1024 steps x 64 heads), and 512 of 4 beat 1024 of 2 (209 vs 344 us on 8 x 2048): fewer
+  // waves per head repeat the chunk's C.B^T over fewer channels and hold more registers each.
   int waves = slice / 16;
   if (waves == 0) {
-    const int64_t cus = device_cus();
     for (int w : {4, 2, 1}) {
-      if (headdim % (16 * w) != 0 || !ssm::ssd_kernel(dstate, w)) continue;
-      waves = w;
-      if (nbh * (headdim / (16 * w)) >= cus) break;
+      if (headdim % (16 * w) == 0 && ssm::ssd_kernel(dstate, w)) {
+        waves = w;
+        break;
+      }
     }
   }
   const ssm::SsdKernel k = ssm::ssd_kernel(dstate, waves);
