@@ -251,14 +251,17 @@ def bench_conv(steps, warmup, torch, np, W, ssm, device):
 
 
 def time_graph(torch, call, steps, warmup, device):
-    """Captures `steps` calls as one HIP graph (after `warmup` eager calls) and times one replay:
-    short kernels are then timed without the host launch path between them.  Returns ms per call."""
-    for i in range(warmup):
-        call(i)
-    torch.cuda.synchronize()
+    """Captures `steps` calls as one HIP graph (after `warmup` eager calls on the capture stream,
+    which also let the library set up its per-stream scratch before capture) and times one
+    replay: short kernels are then timed without the host launch path between them.  Returns ms
+    per call."""
     graph = torch.cuda.CUDAGraph()
     side = torch.cuda.Stream(device)
     side.wait_stream(torch.cuda.current_stream(device))
+    with torch.cuda.stream(side):
+        for i in range(max(1, warmup)):
+            call(i)
+    torch.cuda.synchronize()
     with torch.cuda.stream(side):
         with torch.cuda.graph(graph, stream=side):
             for i in range(steps):

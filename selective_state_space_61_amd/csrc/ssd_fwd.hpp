@@ -20,19 +20,24 @@
 //
 // Work split: one workgroup per (batch row, head, slice of PS = 16*NW head channels).  Wave w
 // owns channels [16w, 16w+16) of the slice, so the columns of S it updates are exactly the ones
-// it reads out: S never leaves the wave's accumulators.  Each wave forms all of G itself
-// (redundant across the waves of a workgroup), which saves a barrier and an LDS round trip.
+// it reads out: S never leaves the wave's accumulators.  The twelve 16 x 16 tiles of C B^T a
+// chunk needs are split over the waves and exchanged through LDS as the masked matrix M.
 //
 // Operand layouts of the 16x16x32 product D = A B (lane l, q = l / 16, i = 0..7, r = 0..3):
 //   A: lane l holds A[l % 16][8q + i];  B: lane l holds B[8q + i][l % 16];
 //   D: lane l holds D[4q + r][l % 16].
-// A D tile therefore hands each lane four CONSECUTIVE rows of one column.  Two D tiles over
-// rows k0..k0+15 and k0+16..k0+31 give lane l the k indices {k0 + 4q + r} and {k0 + 16 + 4q + r}:
-// the same eight k values, in a fixed order, that a K = 32 step asks of lane l, up to a
-// permutation of k.  A product sums over k, so it is unchanged when both operands use the same
-// permutation.  That lets G (computed transposed, so its columns are the output rows) become the
-// A operand of the masked product, and S become the B operand of the read-out, with no LDS
-// round trip; the other operand is read from LDS in the same permuted order.
+// Every tile of the chunk (B, C, X, the weighted X, M) sits in LDS row-major, as it comes from
+// memory, written with 16-byte stores.  Operands whose K index is the row (B^T and X^T over the
+// steps) are read with the transposing LDS read ds_read_b64_tr_b16: in each 16-lane group,
+// output lane i receives, for e = 0..3, element i % 4 of the 8 bytes that lane 4e + i/4
+// addresses.  So when lane s of the group addresses row k0 + s/4 at column c(s % 4), lane i gets
+// rows k0..k0+3 of column c(i/4) + i%4: four consecutive K values of one M/N index, from any four
+// 4-column groups.  Two such reads make a K = 32 fragment.
+//
+// The S tiles (16 dstate rows x 16 channels each) are formed with row m of tile nb holding dstate
+// index 32 (nb/2) + 8 (m/4) + m%4 + 4 (nb%2).  Tiles 2ks and 2ks+1 then hand lane l exactly the
+// dstate indices 32 ks + 8q .. +7 that a K = 32 operand asks of it, in order, so the accumulators
+// pack straight into the A operand of the read-out.
 #pragma once
 
 #include "ssm_device.hpp"
@@ -65,24 +70,28 @@ typedef __bf16 ssd_bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float ssd_f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t ssd_u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t ssd_u32x2_t __attribute__((ext_vector_type(2)));
+typedef short ssd_i16x4_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ ssd_f32x4_t mfma16x16x32(ssd_u32x4_t a, ssd_u32x4_t b, ssd_f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(ssd_bf16x8_t, a),
                                                  __builtin_bit_cast(ssd_bf16x8_t, b), c, 0, 0, 0);
 }
 
-// Two 8-byte halves k0..k0+3 and k0+16..k0+19 of a bf16 row: the permuted K = 32 fragment.
-__device__ __forceinline__ ssd_u32x4_t load_perm_frag(const uint16_t* row_k0) {
-  const ssd_u32x2_t lo = *reinterpret_cast<const ssd_u32x2_t*>(row_k0);
-  const ssd_u32x2_t hi = *reinterpret_cast<const ssd_u32x2_t*>(row_k0 + 16);
-  return ssd_u32x4_t{lo.x, lo.y, hi.x, hi.y};
+// ds_read_b64_tr_b16 at an LDS address, as two 32-bit words.
+__device__ __forceinline__ ssd_u32x2_t lds_read_tr(const uint16_t* p) {
+  const ssd_i16x4_t v =
+      __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) ssd_i16x4_t*)(p));
+  return __builtin_bit_cast(ssd_u32x2_t, v);
 }
 
-// Element e of two bf16 rows (low half from `a`, high half from `b`) as one word.
-template <int E>
-__device__ __forceinline__ uint32_t column_pair(ssd_u32x4_t a, ssd_u32x4_t b) {
-  const uint32_t wa = a[E / 2], wb = b[E / 2];
-  return (E & 1) ? ((wa >> 16) | (wb & 0xffff0000u)) : ((wa & 0xffffu) | (wb << 16));
+// A K = 32 fragment over rows k0 .. k0+31 of a row-major LDS tile with row stride ld: this lane
+// (group q, local index s16) addresses rows k0 + 8q + s16/4 and +4 at column col, which the
+// caller chooses as the column group for local source lane s16 % 4.  The receiving lane i of the
+// group gets rows k0 + 8q .. +7 of column col(i / 4) + i % 4.
+__device__ __forceinline__ ssd_u32x4_t lds_frag_tr(const uint16_t* tile, int ld, int k0, int q, int s16, int col) {
+  const uint16_t* ptr = tile + (k0 + 8 * q + s16 / 4) * ld + col;
+  const ssd_u32x2_t lo = lds_read_tr(ptr), hi = lds_read_tr(ptr + 4 * ld);
+  return ssd_u32x4_t{lo.x, lo.y, hi.x, hi.y};
 }
 
 template <int E>
@@ -90,8 +99,6 @@ __device__ __forceinline__ float bf16_elem(ssd_u32x4_t v) {
   return (E & 1) ? bf16_hi(v[E / 2]) : bf16_lo(v[E / 2]);
 }
 
-// Workgroups of 4 waves (dstate <= 128) keep two workgroups per compute unit: their LDS fits
-// twice in 160 KB and the registers are held to 256 per lane.
 // Inclusive prefix sum over the 64 lanes of a wave with DPP (gfx9): shifts by 1, 2, 4, 8 within
 // each row of 16 (lanes shifted in from outside the row read 0), then lane 15 of each row is
 // added to rows 1 and 3 and lane 31 to rows 2 and 3.
@@ -109,6 +116,15 @@ __device__ __forceinline__ float wave_inclusive_sum(float v) {
   return v;
 }
 
+// The twelve 16 x 16 tiles (i-block ib, j-block jb) of C B^T a chunk needs: the ten with
+// jb <= ib and the two just past the diagonal, (0, 1) and (2, 3), that a K = 32 step of the
+// masked product reads (the mask zeroes them).  Tile k is (k/2, k%2) for k < 4, else
+// (k/4 + 1, k%4).
+__device__ __forceinline__ int gram_tile_i(int k) { return k < 4 ? k / 2 : k / 4 + 1; }
+__device__ __forceinline__ int gram_tile_j(int k) { return k < 4 ? k % 2 : k % 4; }
+
+// Workgroups of 4 waves (dstate <= 128) keep two workgroups per compute unit: their LDS fits
+// twice in 160 KB and the registers are held to 256 per lane.
 template <int N, int NW>
 constexpr int kSsdWavesPerEu = (NW == 4 && N <= 128) ? 2 : 1;
 
@@ -116,27 +132,26 @@ template <int N, int NW>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(kSsdWavesPerEu<N, NW>)))
 void ssd_chunk_kernel(const SsdArgs p) {
   constexpr int Q = kSsdChunk;
-  constexpr int PS = 16 * NW;  // head channels per workgroup
-  constexpr int T = 64 * NW;   // threads
-  constexpr int LDB = N + 8;   // row stride (elements) of the row-major B and C tiles
-  constexpr int LDT = Q + 8;   // row stride of the step-indexed tiles (B^T, X^T, weighted X^T, M)
-  constexpr int NKS = N / 32;  // K = 32 steps over dstate
-  constexpr int NT = N / 16;   // 16-row tiles of S per wave
-  constexpr int kBTasks = 4 * N;  // (row pair, 8-column group) pieces of B
-  constexpr int kBPer = (kBTasks + T - 1) / T;
-  constexpr int kCTasks = 8 * N;  // (row, 8-column group) pieces of C
-  constexpr int kCPer = (kCTasks + T - 1) / T;
-  static_assert(N % 32 == 0, "dstate is a multiple of 32");
-  static_assert(4 * PS == T, "one (row pair, 8-column group) piece of X per thread");
+  constexpr int PS = 16 * NW;         // head channels per workgroup
+  constexpr int T = 64 * NW;          // threads
+  constexpr int LDB = N + 8;          // row stride (elements) of the B and C tiles
+  constexpr int LDX = PS + 8;         // row stride of the X and weighted-X tiles
+  constexpr int LDM = Q + 8;          // row stride of M
+  constexpr int NKS = N / 32;         // K = 32 steps over dstate
+  constexpr int NT = N / 16;          // 16-row tiles of S per wave
+  constexpr int kBCPer = 8 * N / T;   // 16-byte pieces of B (and of C) per thread
+  constexpr int kXPer = 8 * PS / T;   // 16-byte pieces of X per thread
+  constexpr int kTiles = 12 / NW;     // tiles of C B^T per wave
+  static_assert(N % 32 == 0 && (8 * N) % T == 0, "dstate is a multiple of 32");
+  static_assert(kXPer == 2, "two 16-byte pieces of X per thread");
 
-  __shared__ __align__(16) uint16_t s_b[Q * LDB];    // B[j][n]
-  __shared__ __align__(16) uint16_t s_c[Q * LDB];    // C[i][n]
-  __shared__ __align__(16) uint16_t s_bt[N * LDT];   // B^T[n][j]
-  __shared__ __align__(16) uint16_t s_xt[PS * LDT];  // X^T[p][j]
-  __shared__ __align__(16) uint16_t s_xw[PS * LDT];  // X^T[p][j] * exp(cum_last - cum_j) dt_j
-  __shared__ __align__(16) uint16_t s_m[Q * LDT];    // M[i][j] = (C_i . B_j) exp(cum_i - cum_j) dt_j, j <= i
-  __shared__ __align__(16) float s_cum[Q];           // cum_j in log2 units
-  __shared__ __align__(16) float s_dt[Q];            // dt_j (0 past the end of the sequence)
+  __shared__ __align__(16) uint16_t s_b[Q * LDB];   // B[j][n]
+  __shared__ __align__(16) uint16_t s_c[Q * LDB];   // C[i][n]
+  __shared__ __align__(16) uint16_t s_x[Q * LDX];   // X[j][p]
+  __shared__ __align__(16) uint16_t s_xw[Q * LDX];  // X[j][p] * exp(cum_last - cum_j) dt_j
+  __shared__ __align__(16) uint16_t s_m[Q * LDM];   // M[i][j] = (C_i . B_j) exp(cum_i - cum_j) dt_j, j <= i
+  __shared__ __align__(16) float s_cum[Q];          // cum_j in log2 units
+  __shared__ __align__(16) float s_dt[Q];           // dt_j (0 past the end of the sequence)
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -152,8 +167,9 @@ void ssd_chunk_kernel(const SsdArgs p) {
   const float A2 = p.A[h] * kLog2e;
   const float bias = p.dt_bias ? p.dt_bias[h] : 0.0f;
   const float Dh = p.D ? p.D[h] : 0.0f;
-  const int pw = 16 * wave + l16;     // this lane's S column (A-operand row of the products)
-  const int pe = 16 * wave + 4 * q;   // first of the 4 channels this lane writes
+  const int pw = 16 * wave + l16;            // this lane's S column (and output channel of its D rows)
+  const int pe = 16 * wave + 4 * q;          // first of the 4 channels this lane writes
+  const int cx = 16 * wave + 4 * (l16 & 3);  // column group this lane addresses in transposing reads of X
 
   const uint16_t* xg = p.x + (b * L * H + h) * P + p0;  // step t at xg + t * H * P
   const uint16_t* zg = p.z ? p.z + (b * L * H + h) * P + p0 + pe : nullptr;
@@ -163,8 +179,9 @@ void ssd_chunk_kernel(const SsdArgs p) {
   const uint16_t* dtg = p.dt + b * L * H + h;       // step t at dtg + t * H
   const int64_t xs = H * P, bs = G * N;
 
-  // Registers that carry the next chunk's inputs while the current one is computed.
-  ssd_u32x4_t rb[kBPer][2], rc[kCPer], rx[2];
+  // Registers that carry the next chunk's inputs while the current one is computed.  A piece is
+  // 16 bytes of one row; consecutive threads take consecutive pieces of a row (coalesced).
+  ssd_u32x4_t rb[kBCPer], rc[kBCPer], rx[kXPer];
   ssd_u32x2_t rz[4];
   uint32_t rdt = 0u;
 #pragma unroll
@@ -174,34 +191,21 @@ void ssd_chunk_kernel(const SsdArgs p) {
   auto load_chunk = [&](int64_t t0, auto full) {
     constexpr bool FULL = decltype(full)::value;
 #pragma unroll
-    for (int u = 0; u < kBPer; ++u) {
+    for (int u = 0; u < kBCPer; ++u) {
       const int k = tid + u * T;
-      if (kBPer * T == kBTasks || k < kBTasks) {
-        const int rp = k % 32, c8 = k / 32;
-#pragma unroll
-        for (int hb = 0; hb < 2; ++hb) {
-          const int64_t t = t0 + 2 * rp + hb;
-          rb[u][hb] = (FULL || t < L) ? *reinterpret_cast<const ssd_u32x4_t*>(bg + t * bs + 8 * c8)
-                                      : ssd_u32x4_t{0, 0, 0, 0};
-        }
-      }
+      const int c8 = k % (N / 8), j = k / (N / 8);
+      const int64_t t = t0 + j;
+      const bool ok = FULL || t < L;
+      rb[u] = ok ? *reinterpret_cast<const ssd_u32x4_t*>(bg + t * bs + 8 * c8) : ssd_u32x4_t{0u, 0u, 0u, 0u};
+      rc[u] = ok ? *reinterpret_cast<const ssd_u32x4_t*>(cg + t * bs + 8 * c8) : ssd_u32x4_t{0u, 0u, 0u, 0u};
     }
 #pragma unroll
-    for (int u = 0; u < kCPer; ++u) {
+    for (int u = 0; u < kXPer; ++u) {
       const int k = tid + u * T;
-      if (kCPer * T == kCTasks || k < kCTasks) {
-        const int c8 = k % (N / 8), i = k / (N / 8);
-        const int64_t t = t0 + i;
-        rc[u] = (FULL || t < L) ? *reinterpret_cast<const ssd_u32x4_t*>(cg + t * bs + 8 * c8) : ssd_u32x4_t{0, 0, 0, 0};
-      }
-    }
-    {
-      const int rp = tid % 32, p8 = tid / 32;
-#pragma unroll
-      for (int hb = 0; hb < 2; ++hb) {
-        const int64_t t = t0 + 2 * rp + hb;
-        rx[hb] = (FULL || t < L) ? *reinterpret_cast<const ssd_u32x4_t*>(xg + t * xs + 8 * p8) : ssd_u32x4_t{0, 0, 0, 0};
-      }
+      const int p8 = k % (PS / 8), j = k / (PS / 8);
+      const int64_t t = t0 + j;
+      rx[u] = (FULL || t < L) ? *reinterpret_cast<const ssd_u32x4_t*>(xg + t * xs + 8 * p8)
+                              : ssd_u32x4_t{0u, 0u, 0u, 0u};
     }
     rdt = (FULL || t0 + lane < L) ? dtg[(t0 + lane) * H] : 0u;
     if (zg) {
@@ -229,42 +233,23 @@ void ssd_chunk_kernel(const SsdArgs p) {
       s_dt[lane] = dtv;
     }
 #pragma unroll
-    for (int u = 0; u < kBPer; ++u) {
+    for (int u = 0; u < kBCPer; ++u) {
       const int k = tid + u * T;
-      if (kBPer * T == kBTasks || k < kBTasks) {
-        const int rp = k % 32, c8 = k / 32;
-        *reinterpret_cast<ssd_u32x4_t*>(&s_b[(2 * rp) * LDB + 8 * c8]) = rb[u][0];
-        *reinterpret_cast<ssd_u32x4_t*>(&s_b[(2 * rp + 1) * LDB + 8 * c8]) = rb[u][1];
-        uint32_t* bt = reinterpret_cast<uint32_t*>(&s_bt[(8 * c8) * LDT + 2 * rp]);
-        bt[0 * LDT / 2] = column_pair<0>(rb[u][0], rb[u][1]);
-        bt[1 * LDT / 2] = column_pair<1>(rb[u][0], rb[u][1]);
-        bt[2 * LDT / 2] = column_pair<2>(rb[u][0], rb[u][1]);
-        bt[3 * LDT / 2] = column_pair<3>(rb[u][0], rb[u][1]);
-        bt[4 * LDT / 2] = column_pair<4>(rb[u][0], rb[u][1]);
-        bt[5 * LDT / 2] = column_pair<5>(rb[u][0], rb[u][1]);
-        bt[6 * LDT / 2] = column_pair<6>(rb[u][0], rb[u][1]);
-        bt[7 * LDT / 2] = column_pair<7>(rb[u][0], rb[u][1]);
-      }
+      const int c8 = k % (N / 8), j = k / (N / 8);
+      *reinterpret_cast<ssd_u32x4_t*>(&s_b[j * LDB + 8 * c8]) = rb[u];
+      *reinterpret_cast<ssd_u32x4_t*>(&s_c[j * LDB + 8 * c8]) = rc[u];
     }
 #pragma unroll
-    for (int u = 0; u < kCPer; ++u) {
+    for (int u = 0; u < kXPer; ++u) {
       const int k = tid + u * T;
-      if (kCPer * T == kCTasks || k < kCTasks) {
-        const int c8 = k % (N / 8), i = k / (N / 8);
-        *reinterpret_cast<ssd_u32x4_t*>(&s_c[i * LDB + 8 * c8]) = rc[u];
-      }
-    }
-    {
-      const int rp = tid % 32, p8 = tid / 32;
-      const float w0 = __shfl(wgt, 2 * rp), w1 = __shfl(wgt, 2 * rp + 1);
-      uint32_t* xt = reinterpret_cast<uint32_t*>(&s_xt[(8 * p8) * LDT + 2 * rp]);
-      uint32_t* xw = reinterpret_cast<uint32_t*>(&s_xw[(8 * p8) * LDT + 2 * rp]);
-#define SSD_X_COLUMN(E)                                                                  \
-  xt[(E) * LDT / 2] = column_pair<E>(rx[0], rx[1]);                                      \
-  xw[(E) * LDT / 2] = pack_bf16x2(bf16_elem<E>(rx[0]) * w0, bf16_elem<E>(rx[1]) * w1);
-      SSD_X_COLUMN(0) SSD_X_COLUMN(1) SSD_X_COLUMN(2) SSD_X_COLUMN(3)
-      SSD_X_COLUMN(4) SSD_X_COLUMN(5) SSD_X_COLUMN(6) SSD_X_COLUMN(7)
-#undef SSD_X_COLUMN
+      const int p8 = k % (PS / 8), j = k / (PS / 8);
+      const float w = __shfl(wgt, j);
+      *reinterpret_cast<ssd_u32x4_t*>(&s_x[j * LDX + 8 * p8]) = rx[u];
+      *reinterpret_cast<ssd_u32x4_t*>(&s_xw[j * LDX + 8 * p8]) =
+          ssd_u32x4_t{pack_bf16x2(bf16_elem<0>(rx[u]) * w, bf16_elem<1>(rx[u]) * w),
+                      pack_bf16x2(bf16_elem<2>(rx[u]) * w, bf16_elem<3>(rx[u]) * w),
+                      pack_bf16x2(bf16_elem<4>(rx[u]) * w, bf16_elem<5>(rx[u]) * w),
+                      pack_bf16x2(bf16_elem<6>(rx[u]) * w, bf16_elem<7>(rx[u]) * w)};
     }
   };
 
@@ -291,32 +276,42 @@ void ssd_chunk_kernel(const SsdArgs p) {
       if (t0 + 2 * Q <= L) load_chunk(t0 + Q, Full{});
       else load_chunk(t0 + Q, Ragged{});
     }
-    // M, split over the waves: G^T tile (j-block jb, i-block ib) = B_j . C_i, masked to j <= i,
-    // decayed and stored as M[i][j].  The masked product reads M in K = 32 steps, so besides the
-    // ten tiles jb <= ib it needs the two tiles (ib, jb) = (0, 1), (2, 3) just past the diagonal,
-    // which the mask zeroes.  Twelve tiles, 12 / NW per wave, in one straight-line block.
+
+    // M, split over the waves: G^T tile (j-block jb, i-block ib) = B_j . C_i (both rows are
+    // dstate-contiguous: plain 16-byte reads), masked to j <= i, decayed and stored as M[i][j]
+    {
+      ssd_f32x4_t gt[kTiles];
 #pragma unroll
-    for (int s = 0; s < 12 / NW; ++s) {
-      const int k = wave + NW * s;
-      const int ib = k < 4 ? k / 2 : k / 4 + 1, jb = k < 4 ? k % 2 : k % 4;
-      const int irow = 16 * ib + l16;
-      ssd_f32x4_t gt = {0.0f, 0.0f, 0.0f, 0.0f};
+      for (int s = 0; s < kTiles; ++s) gt[s] = ssd_f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks)
-        gt = mfma16x16x32(*reinterpret_cast<const ssd_u32x4_t*>(&s_b[(16 * jb + l16) * LDB + 32 * ks + 8 * q]),
-                          *reinterpret_cast<const ssd_u32x4_t*>(&s_c[irow * LDB + 32 * ks + 8 * q]), gt);
-      const float cum_i = s_cum[irow];
-      const ssd_f32x4_t cj = *reinterpret_cast<const ssd_f32x4_t*>(&s_cum[16 * jb + 4 * q]);
-      const ssd_f32x4_t dj = *reinterpret_cast<const ssd_f32x4_t*>(&s_dt[16 * jb + 4 * q]);
-      float m[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) m[r] = (16 * jb + 4 * q + r <= irow) ? gt[r] * hw_exp2(cum_i - cj[r]) * dj[r] : 0.0f;
-      *reinterpret_cast<ssd_u32x2_t*>(&s_m[irow * LDT + 16 * jb + 4 * q]) =
-          ssd_u32x2_t{pack_bf16x2(m[0], m[1]), pack_bf16x2(m[2], m[3])};
+        for (int s = 0; s < kTiles; ++s) {
+          const int k = wave + NW * s;
+          const int ib = gram_tile_i(k), jb = gram_tile_j(k);
+          gt[s] = mfma16x16x32(*reinterpret_cast<const ssd_u32x4_t*>(&s_b[(16 * jb + l16) * LDB + 32 * ks + 8 * q]),
+                               *reinterpret_cast<const ssd_u32x4_t*>(&s_c[(16 * ib + l16) * LDB + 32 * ks + 8 * q]),
+                               gt[s]);
+        }
+#pragma unroll
+      for (int s = 0; s < kTiles; ++s) {
+        const int k = wave + NW * s;
+        const int ib = gram_tile_i(k), jb = gram_tile_j(k);
+        const int irow = 16 * ib + l16;
+        const float cum_i = s_cum[irow];
+        const ssd_f32x4_t cj = *reinterpret_cast<const ssd_f32x4_t*>(&s_cum[16 * jb + 4 * q]);
+        const ssd_f32x4_t dj = *reinterpret_cast<const ssd_f32x4_t*>(&s_dt[16 * jb + 4 * q]);
+        float m[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          m[r] = (16 * jb + 4 * q + r <= irow) ? gt[s][r] * hw_exp2(cum_i - cj[r]) * dj[r] : 0.0f;
+        *reinterpret_cast<ssd_u32x2_t*>(&s_m[irow * LDM + 16 * jb + 4 * q]) =
+            ssd_u32x2_t{pack_bf16x2(m[0], m[1]), pack_bf16x2(m[2], m[3])};
+      }
     }
 
-    // S entering the chunk as bf16 A operands of the read-out, S^T[p][n] with n permuted as the
-    // tiles hold it
+    // S entering the chunk as bf16 A operands of the read-out: tiles 2ks, 2ks+1 hold dstate
+    // indices 32 ks + 8q .. +7 of channel pw, in order
     ssd_u32x4_t sf[NKS];
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks)
@@ -325,66 +320,73 @@ void ssd_chunk_kernel(const SsdArgs p) {
                            pack_bf16x2(S[2 * ks + 1][2], S[2 * ks + 1][3])};
     __syncthreads();  // M complete
 
+    // x of the four channels pe .. pe+3 at step 16 ib + l16, for the skip term (read early)
+    ssd_u32x2_t xv[4];
+#pragma unroll
+    for (int ib = 0; ib < 4; ++ib) xv[ib] = *reinterpret_cast<const ssd_u32x2_t*>(&s_x[(16 * ib + l16) * LDX + pe]);
     // Y^T tiles (channels 16 wave .. +15, steps 16 ib .. +15): the read-out exp(cum_i) S^T C_i^T
     // plus the masked product X^T M^T over the steps j <= i
     ssd_f32x4_t acc[4];
 #pragma unroll
-    for (int ib = 0; ib < 4; ++ib) {
-      const int irow = 16 * ib + l16;  // the output step this lane holds
-      acc[ib] = ssd_f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int ib = 0; ib < 4; ++ib) acc[ib] = ssd_f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks)
-        acc[ib] = mfma16x16x32(sf[ks], load_perm_frag(&s_c[irow * LDB + 32 * ks + 4 * q]), acc[ib]);
-    }
+    for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
-    for (int ib = 0; ib < 4; ++ib) {
-      const int irow = 16 * ib + l16;
-      acc[ib] *= hw_exp2(s_cum[irow]);
+      for (int ib = 0; ib < 4; ++ib)
+        acc[ib] = mfma16x16x32(sf[ks], *reinterpret_cast<const ssd_u32x4_t*>(&s_c[(16 * ib + l16) * LDB + 32 * ks + 8 * q]),
+                               acc[ib]);
 #pragma unroll
-      for (int ks = 0; ks <= ib / 2; ++ks)
-        acc[ib] = mfma16x16x32(*reinterpret_cast<const ssd_u32x4_t*>(&s_xt[pw * LDT + 32 * ks + 8 * q]),
-                               *reinterpret_cast<const ssd_u32x4_t*>(&s_m[irow * LDT + 32 * ks + 8 * q]), acc[ib]);
+    for (int ib = 0; ib < 4; ++ib) acc[ib] *= hw_exp2(s_cum[16 * ib + l16]);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const ssd_u32x4_t xa = lds_frag_tr(s_x, LDX, 32 * ks, q, l16, cx);  // X^T[pw][32 ks + 8q ..]
+#pragma unroll
+      for (int ib = 2 * ks; ib < 4; ++ib)
+        acc[ib] = mfma16x16x32(xa, *reinterpret_cast<const ssd_u32x4_t*>(&s_m[(16 * ib + l16) * LDM + 32 * ks + 8 * q]),
+                               acc[ib]);
     }
     // skip term, gate, store: channels pe .. pe + 3 of step 16 ib + l16
     const bool full = t0 + Q <= L;
+    const bool gated = zg != nullptr;
 #pragma unroll
     for (int ib = 0; ib < 4; ++ib) {
-      const int irow = 16 * ib + l16;
       float yv[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        yv[r] = fmaf(Dh, bf16_lo(s_xt[(pe + r) * LDT + irow]), acc[ib][r]);
-        if (zg) yv[r] *= silu_f32((r & 1) ? bf16_hi(zc[ib][r / 2]) : bf16_lo(zc[ib][r / 2]));
+        const float xr = (r & 1) ? bf16_hi(xv[ib][r / 2]) : bf16_lo(xv[ib][r / 2]);
+        const float zr = (r & 1) ? bf16_hi(zc[ib][r / 2]) : bf16_lo(zc[ib][r / 2]);
+        yv[r] = fmaf(Dh, xr, acc[ib][r]) * (gated ? silu_f32(zr) : 1.0f);
       }
-      const int64_t t = t0 + irow;
+      const int64_t t = t0 + 16 * ib + l16;
       if (full || t < L)
         *reinterpret_cast<ssd_u32x2_t*>(yg + t * xs) = ssd_u32x2_t{pack_bf16x2(yv[0], yv[1]), pack_bf16x2(yv[2], yv[3])};
     }
 
-    // state update: S = exp(cum_last) S + B^T (weighted X)
+    // state update: S = exp(cum_last) S + B^T (weighted X).  Row m of tile nb is dstate index
+    // 32 (nb/2) + 8 (m/4) + m%4 + 4 (nb%2): this lane addresses column group 8 (l16 % 4) of that base.
     const float decay = hw_exp2(s_cum[Q - 1]);
-    ssd_u32x4_t xw[2];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) xw[ks] = *reinterpret_cast<const ssd_u32x4_t*>(&s_xw[pw * LDT + 32 * ks + 8 * q]);
+    for (int nb = 0; nb < NT; ++nb) S[nb] *= decay;
 #pragma unroll
-    for (int nb = 0; nb < NT; ++nb) {
-      S[nb] *= decay;
+    for (int ks = 0; ks < 2; ++ks) {
+      const ssd_u32x4_t xw = lds_frag_tr(s_xw, LDX, 32 * ks, q, l16, cx);  // weighted X[32 ks + 8q ..][pw]
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-        S[nb] = mfma16x16x32(*reinterpret_cast<const ssd_u32x4_t*>(&s_bt[(16 * nb + l16) * LDT + 32 * ks + 8 * q]),
-                             xw[ks], S[nb]);
+      for (int nb = 0; nb < NT; ++nb)
+        S[nb] = mfma16x16x32(lds_frag_tr(s_b, LDB, 32 * ks, q, l16, 32 * (nb / 2) + 4 * (nb % 2) + 8 * (l16 & 3)),
+                             xw, S[nb]);
     }
   }
 
   if (p.final_state) {
-    float* fs = p.final_state + ((b * H + h) * P + p0 + pw) * N + 4 * q;
+    // tile nb, lane (q, r): dstate index 32 (nb/2) + 8q + 4 (nb%2) + r of channel pw
+    float* fs = p.final_state + ((b * H + h) * P + p0 + pw) * N + 8 * q;
 #pragma unroll
-    for (int nb = 0; nb < NT; ++nb) *reinterpret_cast<ssd_f32x4_t*>(fs + 16 * nb) = S[nb];
+    for (int nb = 0; nb < NT; ++nb) *reinterpret_cast<ssd_f32x4_t*>(fs + 32 * (nb / 2) + 4 * (nb % 2)) = S[nb];
   }
 }
 
 using SsdKernel = void (*)(const SsdArgs);
-// The kernel for (dstate, waves per workgroup), or NULL when that pair is not instantiated.
+// The chunk kernel for (dstate, waves per workgroup), or NULL when that pair is not instantiated.
 SsdKernel ssd_kernel(int64_t dstate, int waves);
 
 }  // namespace ssm
