@@ -34,10 +34,12 @@
 // rows k0..k0+3 of column c(i/4) + i%4: four consecutive K values of one M/N index, from any four
 // 4-column groups.  Two such reads make a K = 32 fragment.
 //
-// The S tiles (16 dstate rows x 16 channels each) are formed with row m of tile nb holding dstate
-// index 32 (nb/2) + 8 (m/4) + m%4 + 4 (nb%2).  Tiles 2ks and 2ks+1 then hand lane l exactly the
-// dstate indices 32 ks + 8q .. +7 that a K = 32 operand asks of it, in order, so the accumulators
-// pack straight into the A operand of the read-out.
+// The S tiles (16 dstate rows x 16 channels each, tile nb = dstate 16 nb .. +15) hand each lane
+// four CONSECUTIVE rows of one column.  Two tiles 2ks, 2ks+1 give lane l the dstate indices
+// 32 ks + 4q .. +3 and 32 ks + 16 + 4q .. +3: the eight k values a K = 32 step asks of lane l up
+// to a fixed permutation of k.  A product is unchanged when both operands use the same
+// permutation, so the accumulators pack straight into the A operand of the read-out, and C is read
+// in that order (two 8-byte halves per fragment).
 #pragma once
 
 #include "ssm_device.hpp"
@@ -91,6 +93,13 @@ __device__ __forceinline__ ssd_u32x2_t lds_read_tr(const uint16_t* p) {
 __device__ __forceinline__ ssd_u32x4_t lds_frag_tr(const uint16_t* tile, int ld, int k0, int q, int s16, int col) {
   const uint16_t* ptr = tile + (k0 + 8 * q + s16 / 4) * ld + col;
   const ssd_u32x2_t lo = lds_read_tr(ptr), hi = lds_read_tr(ptr + 4 * ld);
+  return ssd_u32x4_t{lo.x, lo.y, hi.x, hi.y};
+}
+
+// Two 8-byte halves k0..k0+3 and k0+16..k0+19 of a bf16 row: the permuted K = 32 fragment.
+__device__ __forceinline__ ssd_u32x4_t load_perm_frag(const uint16_t* row_k0) {
+  const ssd_u32x2_t lo = *reinterpret_cast<const ssd_u32x2_t*>(row_k0);
+  const ssd_u32x2_t hi = *reinterpret_cast<const ssd_u32x2_t*>(row_k0 + 16);
   return ssd_u32x4_t{lo.x, lo.y, hi.x, hi.y};
 }
 
@@ -310,8 +319,8 @@ void ssd_chunk_kernel(const SsdArgs p) {
       }
     }
 
-    // S entering the chunk as bf16 A operands of the read-out: tiles 2ks, 2ks+1 hold dstate
-    // indices 32 ks + 8q .. +7 of channel pw, in order
+    // S entering the chunk as bf16 A operands of the read-out: S^T[pw][n], n permuted as the
+    // tiles hold it
     ssd_u32x4_t sf[NKS];
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks)
@@ -333,8 +342,7 @@ void ssd_chunk_kernel(const SsdArgs p) {
     for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
       for (int ib = 0; ib < 4; ++ib)
-        acc[ib] = mfma16x16x32(sf[ks], *reinterpret_cast<const ssd_u32x4_t*>(&s_c[(16 * ib + l16) * LDB + 32 * ks + 8 * q]),
-                               acc[ib]);
+        acc[ib] = mfma16x16x32(sf[ks], load_perm_frag(&s_c[(16 * ib + l16) * LDB + 32 * ks + 4 * q]), acc[ib]);
 #pragma unroll
     for (int ib = 0; ib < 4; ++ib) acc[ib] *= hw_exp2(s_cum[16 * ib + l16]);
 #pragma unroll
@@ -362,8 +370,8 @@ void ssd_chunk_kernel(const SsdArgs p) {
         *reinterpret_cast<ssd_u32x2_t*>(yg + t * xs) = ssd_u32x2_t{pack_bf16x2(yv[0], yv[1]), pack_bf16x2(yv[2], yv[3])};
     }
 
-    // state update: S = exp(cum_last) S + B^T (weighted X).  Row m of tile nb is dstate index
-    // 32 (nb/2) + 8 (m/4) + m%4 + 4 (nb%2): this lane addresses column group 8 (l16 % 4) of that base.
+    // state update: S = exp(cum_last) S + B^T (weighted X); the B^T operand of tile nb is rows
+    // 16 nb .. +15 of B^T, read transposed from B (this lane addresses column 16 nb + 4 (l16 % 4))
     const float decay = hw_exp2(s_cum[Q - 1]);
 #pragma unroll
     for (int nb = 0; nb < NT; ++nb) S[nb] *= decay;
@@ -372,16 +380,15 @@ void ssd_chunk_kernel(const SsdArgs p) {
       const ssd_u32x4_t xw = lds_frag_tr(s_xw, LDX, 32 * ks, q, l16, cx);  // weighted X[32 ks + 8q ..][pw]
 #pragma unroll
       for (int nb = 0; nb < NT; ++nb)
-        S[nb] = mfma16x16x32(lds_frag_tr(s_b, LDB, 32 * ks, q, l16, 32 * (nb / 2) + 4 * (nb % 2) + 8 * (l16 & 3)),
-                             xw, S[nb]);
+        S[nb] = mfma16x16x32(lds_frag_tr(s_b, LDB, 32 * ks, q, l16, 16 * nb + 4 * (l16 & 3)), xw, S[nb]);
     }
   }
 
   if (p.final_state) {
-    // tile nb, lane (q, r): dstate index 32 (nb/2) + 8q + 4 (nb%2) + r of channel pw
-    float* fs = p.final_state + ((b * H + h) * P + p0 + pw) * N + 8 * q;
+    // tile nb, lane (q, r): dstate index 16 nb + 4q + r of channel pw
+    float* fs = p.final_state + ((b * H + h) * P + p0 + pw) * N + 4 * q;
 #pragma unroll
-    for (int nb = 0; nb < NT; ++nb) *reinterpret_cast<ssd_f32x4_t*>(fs + 32 * (nb / 2) + 4 * (nb % 2)) = S[nb];
+    for (int nb = 0; nb < NT; ++nb) *reinterpret_cast<ssd_f32x4_t*>(fs + 16 * nb) = S[nb];
   }
 }
 
