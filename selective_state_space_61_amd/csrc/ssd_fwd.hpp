@@ -146,6 +146,8 @@ void ssd_chunk_kernel(const SsdArgs p) {
   constexpr int LDB = N + 8;          // row stride (elements) of the B and C tiles
   constexpr int LDX = PS + 8;         // row stride of the X and weighted-X tiles
   constexpr int LDM = Q + 8;          // row stride of M
+  constexpr int LDY = PS + 4;         // row stride of the fp32 output tile
+  constexpr int kDtPer = Q / NW;      // raw dt values each wave loads
   constexpr int NKS = N / 32;         // K = 32 steps over dstate
   constexpr int NT = N / 16;          // 16-row tiles of S per wave
   constexpr int kBCPer = 8 * N / T;   // 16-byte pieces of B (and of C) per thread
@@ -161,6 +163,8 @@ void ssd_chunk_kernel(const SsdArgs p) {
   __shared__ __align__(16) uint16_t s_m[Q * LDM];   // M[i][j] = (C_i . B_j) exp(cum_i - cum_j) dt_j, j <= i
   __shared__ __align__(16) float s_cum[Q];          // cum_j in log2 units
   __shared__ __align__(16) float s_dt[Q];           // dt_j (0 past the end of the sequence)
+  __shared__ __align__(16) float s_y[Q * LDY];      // Y[i][p] of the previous chunk, for the epilogue
+  __shared__ __align__(16) uint16_t s_dtraw[Q];     // raw dt of the chunk being staged
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -177,12 +181,12 @@ void ssd_chunk_kernel(const SsdArgs p) {
   const float bias = p.dt_bias ? p.dt_bias[h] : 0.0f;
   const float Dh = p.D ? p.D[h] : 0.0f;
   const int pw = 16 * wave + l16;            // this lane's S column (and output channel of its D rows)
-  const int pe = 16 * wave + 4 * q;          // first of the 4 channels this lane writes
+  const int pe = 16 * wave + 4 * q;          // first of the 4 output channels this lane's Y tiles hold
   const int cx = 16 * wave + 4 * (l16 & 3);  // column group this lane addresses in transposing reads of X
 
   const uint16_t* xg = p.x + (b * L * H + h) * P + p0;  // step t at xg + t * H * P
-  const uint16_t* zg = p.z ? p.z + (b * L * H + h) * P + p0 + pe : nullptr;
-  uint16_t* yg = p.y + (b * L * H + h) * P + p0 + pe;
+  const uint16_t* zg = p.z ? p.z + (b * L * H + h) * P + p0 : nullptr;
+  uint16_t* yg = p.y + (b * L * H + h) * P + p0;
   const uint16_t* bg = p.B + (b * L * G + g) * N;  // step t at bg + t * G * N
   const uint16_t* cg = p.C + (b * L * G + g) * N;
   const uint16_t* dtg = p.dt + b * L * H + h;       // step t at dtg + t * H
@@ -190,11 +194,11 @@ void ssd_chunk_kernel(const SsdArgs p) {
 
   // Registers that carry the next chunk's inputs while the current one is computed.  A piece is
   // 16 bytes of one row; consecutive threads take consecutive pieces of a row (coalesced).
-  ssd_u32x4_t rb[kBCPer], rc[kBCPer], rx[kXPer];
-  ssd_u32x2_t rz[4];
+  // x and z of the chunk whose epilogue is pending stay in xe, ze (same pieces as rx, rz).
+  ssd_u32x4_t rb[kBCPer], rc[kBCPer], rx[kXPer], rz[kXPer], xe[kXPer], ze[kXPer];
   uint32_t rdt = 0u;
 #pragma unroll
-  for (int k = 0; k < 4; ++k) rz[k] = ssd_u32x2_t{0u, 0u};
+  for (int u = 0; u < kXPer; ++u) rz[u] = ze[u] = xe[u] = ssd_u32x4_t{0u, 0u, 0u, 0u};
 
   // FULL: all 64 steps of the chunk are inside the sequence (no bounds checks).
   auto load_chunk = [&](int64_t t0, auto full) {
@@ -215,13 +219,41 @@ void ssd_chunk_kernel(const SsdArgs p) {
       const int64_t t = t0 + j;
       rx[u] = (FULL || t < L) ? *reinterpret_cast<const ssd_u32x4_t*>(xg + t * xs + 8 * p8)
                               : ssd_u32x4_t{0u, 0u, 0u, 0u};
+      if (zg)
+        rz[u] = (FULL || t < L) ? *reinterpret_cast<const ssd_u32x4_t*>(zg + t * xs + 8 * p8)
+                                : ssd_u32x4_t{0u, 0u, 0u, 0u};
     }
-    rdt = (FULL || t0 + lane < L) ? dtg[(t0 + lane) * H] : 0u;
-    if (zg) {
+    // wave w loads the raw dt of steps kDtPer w .. +kDtPer-1 (lanes below kDtPer)
+    const int64_t td = t0 + kDtPer * wave + lane;
+    rdt = (lane < kDtPer && (FULL || td < L)) ? dtg[td * H] : 0u;
+  };
+  // The raw dt just loaded goes to LDS once it has arrived (read by every wave at the next stage).
+  auto publish_dt = [&]() {
+    if (lane < kDtPer) s_dtraw[kDtPer * wave + lane] = static_cast<uint16_t>(rdt);
+  };
+
+  // Skip term, gate and store of the chunk at step te0 whose Y sits in s_y: each thread takes the
+  // same 16-byte pieces it loaded (x in xe, z in ze), 8 channels of one step.  FULL as in load_chunk.
+  auto epilogue = [&](int64_t te0, auto full) {
+    constexpr bool FULL = decltype(full)::value;
 #pragma unroll
-      for (int ib = 0; ib < 4; ++ib) {
-        const int64_t t = t0 + 16 * ib + l16;
-        rz[ib] = (FULL || t < L) ? *reinterpret_cast<const ssd_u32x2_t*>(zg + t * xs) : ssd_u32x2_t{0u, 0u};
+    for (int u = 0; u < kXPer; ++u) {
+      const int k = tid + u * T;
+      const int p8 = k % (PS / 8), j = k / (PS / 8);
+      const int64_t t = te0 + j;
+      if (FULL || t < L) {
+        const ssd_f32x4_t y0 = *reinterpret_cast<const ssd_f32x4_t*>(&s_y[j * LDY + 8 * p8]);
+        const ssd_f32x4_t y1 = *reinterpret_cast<const ssd_f32x4_t*>(&s_y[j * LDY + 8 * p8 + 4]);
+        float yv[8] = {y0[0], y0[1], y0[2], y0[3], y1[0], y1[1], y1[2], y1[3]};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float xr = (e & 1) ? bf16_hi(xe[u][e / 2]) : bf16_lo(xe[u][e / 2]);
+          const float zr = (e & 1) ? bf16_hi(ze[u][e / 2]) : bf16_lo(ze[u][e / 2]);
+          yv[e] = fmaf(Dh, xr, yv[e]) * (zg ? silu_f32(zr) : 1.0f);
+        }
+        *reinterpret_cast<ssd_u32x4_t*>(yg + t * xs + 8 * p8) =
+            ssd_u32x4_t{pack_bf16x2(yv[0], yv[1]), pack_bf16x2(yv[2], yv[3]), pack_bf16x2(yv[4], yv[5]),
+                        pack_bf16x2(yv[6], yv[7])};
       }
     }
   };
@@ -229,11 +261,8 @@ void ssd_chunk_kernel(const SsdArgs p) {
   // Writes the chunk held in registers to LDS.
   auto stage_chunk = [&](int64_t t0) {
     // dt and the cumulative decay: lane l of every wave holds step l of the chunk
-    float dtv = 0.0f;
-    if (t0 + lane < L) {
-      const float v = bf16_lo(rdt) + bias;
-      dtv = p.softplus ? softplus_f32(v) : v;
-    }
+    const float v = bf16_lo(s_dtraw[lane]) + bias;
+    const float dtv = t0 + lane < L ? (p.softplus ? softplus_f32(v) : v) : 0.0f;
     const float cum = wave_inclusive_sum(dtv * A2);
     const float last = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, cum), 63));
     const float wgt = hw_exp2(last - cum) * dtv;
@@ -254,6 +283,8 @@ void ssd_chunk_kernel(const SsdArgs p) {
       const int p8 = k % (PS / 8), j = k / (PS / 8);
       const float w = __shfl(wgt, j);
       *reinterpret_cast<ssd_u32x4_t*>(&s_x[j * LDX + 8 * p8]) = rx[u];
+      xe[u] = rx[u];
+      ze[u] = rz[u];
       *reinterpret_cast<ssd_u32x4_t*>(&s_xw[j * LDX + 8 * p8]) =
           ssd_u32x4_t{pack_bf16x2(bf16_elem<0>(rx[u]) * w, bf16_elem<1>(rx[u]) * w),
                       pack_bf16x2(bf16_elem<2>(rx[u]) * w, bf16_elem<3>(rx[u]) * w),
@@ -272,14 +303,13 @@ void ssd_chunk_kernel(const SsdArgs p) {
   if (nchunks > 0) {
     if (Q <= L) load_chunk(0, Full{});
     else load_chunk(0, Ragged{});
+    publish_dt();
   }
   for (int64_t c = 0; c < nchunks; ++c) {
     const int64_t t0 = c * Q;
     __syncthreads();  // every wave is done with the previous chunk's tiles
+    if (c > 0) epilogue(t0 - Q, Full{});  // the chunk before this one is whole
     stage_chunk(t0);
-    ssd_u32x2_t zc[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) zc[k] = rz[k];
     __syncthreads();
     if (c + 1 < nchunks) {
       if (t0 + 2 * Q <= L) load_chunk(t0 + Q, Full{});
@@ -329,10 +359,6 @@ void ssd_chunk_kernel(const SsdArgs p) {
                            pack_bf16x2(S[2 * ks + 1][2], S[2 * ks + 1][3])};
     __syncthreads();  // M complete
 
-    // x of the four channels pe .. pe+3 at step 16 ib + l16, for the skip term (read early)
-    ssd_u32x2_t xv[4];
-#pragma unroll
-    for (int ib = 0; ib < 4; ++ib) xv[ib] = *reinterpret_cast<const ssd_u32x2_t*>(&s_x[(16 * ib + l16) * LDX + pe]);
     // Y^T tiles (channels 16 wave .. +15, steps 16 ib .. +15): the read-out exp(cum_i) S^T C_i^T
     // plus the masked product X^T M^T over the steps j <= i
     ssd_f32x4_t acc[4];
@@ -353,22 +379,9 @@ void ssd_chunk_kernel(const SsdArgs p) {
         acc[ib] = mfma16x16x32(xa, *reinterpret_cast<const ssd_u32x4_t*>(&s_m[(16 * ib + l16) * LDM + 32 * ks + 8 * q]),
                                acc[ib]);
     }
-    // skip term, gate, store: channels pe .. pe + 3 of step 16 ib + l16
-    const bool full = t0 + Q <= L;
-    const bool gated = zg != nullptr;
+    // Y^T tiles to LDS as Y[i][p] for the epilogue (run at the next chunk's staging)
 #pragma unroll
-    for (int ib = 0; ib < 4; ++ib) {
-      float yv[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float xr = (r & 1) ? bf16_hi(xv[ib][r / 2]) : bf16_lo(xv[ib][r / 2]);
-        const float zr = (r & 1) ? bf16_hi(zc[ib][r / 2]) : bf16_lo(zc[ib][r / 2]);
-        yv[r] = fmaf(Dh, xr, acc[ib][r]) * (gated ? silu_f32(zr) : 1.0f);
-      }
-      const int64_t t = t0 + 16 * ib + l16;
-      if (full || t < L)
-        *reinterpret_cast<ssd_u32x2_t*>(yg + t * xs) = ssd_u32x2_t{pack_bf16x2(yv[0], yv[1]), pack_bf16x2(yv[2], yv[3])};
-    }
+    for (int ib = 0; ib < 4; ++ib) *reinterpret_cast<ssd_f32x4_t*>(&s_y[(16 * ib + l16) * LDY + pe]) = acc[ib];
 
     // state update: S = exp(cum_last) S + B^T (weighted X); the B^T operand of tile nb is rows
     // 16 nb .. +15 of B^T, read transposed from B (this lane addresses column 16 nb + 4 (l16 % 4))
@@ -382,6 +395,11 @@ void ssd_chunk_kernel(const SsdArgs p) {
       for (int nb = 0; nb < NT; ++nb)
         S[nb] = mfma16x16x32(lds_frag_tr(s_b, LDB, 32 * ks, q, l16, 16 * nb + 4 * (l16 & 3)), xw, S[nb]);
     }
+    if (c + 1 < nchunks) publish_dt();
+  }
+  if (nchunks > 0) {
+    __syncthreads();
+    epilogue((nchunks - 1) * Q, Ragged{});
   }
 
   if (p.final_state) {
