@@ -258,10 +258,14 @@ SSM_API ssm_status_t ssm_state_update_ex(int64_t batch, int64_t dim, int64_t dst
 
 /* Options of ssm_ssd_fwd.  head_slice: head channels per workgroup (16, 32
  * or 64, dividing headdim), or 0 for the largest one the library has for
- * this dstate and headdim; reserved must be zero. */
+ * this dstate and headdim.  segments: pieces the sequence is cut into (each
+ * a whole number of 64-step chunks; 1 = none, 0 = chosen by the library:
+ * enough to give every compute unit two workgroups when the batch rows and
+ * heads alone cannot).  reserved must be zero. */
 typedef struct {
   int32_t head_slice;
-  int32_t reserved[7];
+  int32_t segments;
+  int32_t reserved[6];
 } ssm_ssd_opts_t;
 
 /*
@@ -287,6 +291,9 @@ typedef struct {
  * The sequence is taken in chunks of 64 steps whose products run on bf16
  * matrix cores with fp32 accumulation; the state carried between chunks is
  * fp32 and is rounded to bf16 only as an operand of the chunk's read-out.
+ * With a sequence split the segments' states go to the same per-(device,
+ * stream) scratch as the split-sequence scan: (segments-1)*batch*nheads*
+ * headdim*dstate + segments*batch*nheads fp32 (same rules as ssm_scan_fwd).
  * Storage must be bf16 (SSM_F32 gives SSM_ERR_UNSUPPORTED).  dstate must be
  * 32, 64, 128 or 256 and headdim a multiple of 16 (else SSM_ERR_UNSUPPORTED).
  * x, z, y, B, C and final_state must be 16-byte aligned (else

@@ -49,7 +49,7 @@ class UpdateOpts(ctypes.Structure):
 
 
 class SsdOpts(ctypes.Structure):
-    _fields_ = [("head_slice", ctypes.c_int32), ("reserved", ctypes.c_int32 * 7)]
+    _fields_ = [("head_slice", ctypes.c_int32), ("segments", ctypes.c_int32), ("reserved", ctypes.c_int32 * 6)]
 
 
 SSM_BBAR_DELTA_B, SSM_BBAR_ZOH = 0, 1
@@ -303,7 +303,7 @@ def ssm_ssd_fwd(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, B: torch.Ten
                 D: Optional[torch.Tensor] = None, z: Optional[torch.Tensor] = None,
                 dt_bias: Optional[torch.Tensor] = None, dt_softplus: bool = False, *,
                 y: Optional[torch.Tensor] = None, final_state: Optional[torch.Tensor] = None,
-                return_final_state: bool = True, head_slice: int = 0,
+                return_final_state: bool = True, head_slice: int = 0, segments: int = 0,
                 stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Mamba-2 SSD layer forward (include/ssm.h: ssm_ssd_fwd).  x, z: (batch, seqlen, nheads,
     headdim) bf16; dt: (batch, seqlen, nheads) bf16; B, C: (batch, seqlen, ngroups, dstate) bf16;
@@ -329,7 +329,7 @@ def ssm_ssd_fwd(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, B: torch.Ten
     if final_state is None and return_final_state:
         final_state = torch.empty((batch, nheads, headdim, dstate), dtype=torch.float32, device=dev)
     _need(final_state, "final_state", (batch, nheads, headdim, dstate), torch.float32, dev, optional=True)
-    opts = SsdOpts(head_slice=int(head_slice))
+    opts = SsdOpts(head_slice=int(head_slice), segments=int(segments))
     status = lib.ssm_ssd_fwd(batch, seqlen, nheads, headdim, dstate, ngroups, code, _ptr(x), _ptr(dt), _ptr(A),
                              _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(dt_bias), int(bool(dt_softplus)), _ptr(y),
                              _ptr(final_state), _stream(dev, stream), ctypes.byref(opts))

@@ -7,9 +7,10 @@ namespace ssm {
 
 // Instantiated pairs: 4 waves for every dstate, 2 waves up to dstate 128 and 1 wave up to 64
 // (the per-thread staging registers grow as dstate / waves).
-SsdKernel ssd_kernel(int64_t dstate, int waves) {
-#define SSD_CASE(NN, W) \
-  if (dstate == NN && waves == W) return ssd_chunk_kernel<NN, W>;
+SsdKernel ssd_kernel(int64_t dstate, int waves, int mode) {
+#define SSD_CASE(NN, W)                                                                            \
+  if (dstate == NN && waves == W)                                                                  \
+    return mode == kSsdStateOnly ? ssd_chunk_kernel<NN, W, kSsdStateOnly> : ssd_chunk_kernel<NN, W, kSsdOutputs>;
   SSD_CASE(32, 4) SSD_CASE(64, 4) SSD_CASE(128, 4) SSD_CASE(256, 4)
   SSD_CASE(32, 2) SSD_CASE(64, 2) SSD_CASE(128, 2)
   SSD_CASE(32, 1) SSD_CASE(64, 1)

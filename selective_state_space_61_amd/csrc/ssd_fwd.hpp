@@ -18,6 +18,12 @@
 // (Q x Q, over dstate), the masked product with X (over the chunk's steps), C S (over dstate)
 // and B^T X (over the steps).
 //
+// Sequence split (for grids too small to fill the chip): the chunks are cut into segments.  The
+// recurrence is linear, so a segment's true end state is e^{sum dt A over it} S_in + S_end, with
+// S_end its end state from zero.  Pass 1 (MODE kSsdStateOnly) runs segments 0..k-2 from zero
+// through the state update only and records S_end and sum dt A; ssd_carry_kernel composes the
+// entering states in order; pass 2 (kSsdOutputs) runs every segment from its entering state.
+//
 // Work split: one workgroup per (batch row, head, slice of PS = 16*NW head channels).  Wave w
 // owns channels [16w, 16w+16) of the slice, so the columns of S it updates are exactly the ones
 // it reads out: S never leaves the wave's accumulators.  The twelve 16 x 16 tiles of C B^T a
@@ -57,6 +63,10 @@ struct SsdArgs {
   const float* dt_bias;  // (nheads) or NULL
   uint16_t* y;           // like x
   float* final_state;    // (batch, nheads, headdim, dstate) or NULL
+  const float* seg_init;  // (nseg-1, batch, nheads, headdim, dstate): state entering segment s >= 1 at
+                          // [s-1], or NULL (every segment starts from zero)
+  float* seg_state;       // same layout: end state of segment s from zero at [s] (state-only pass)
+  float* seg_dsum;        // (nseg, batch, nheads): sum over segment s of dt A log2(e) (state-only pass)
   int64_t batch;
   int64_t seqlen;
   int32_t nheads;
@@ -64,7 +74,12 @@ struct SsdArgs {
   int32_t ngroups;
   int32_t nslices;  // headdim / PS
   int32_t softplus;
+  int32_t nseg;        // segments the chunks are cut into
+  int32_t seg_chunks;  // chunks per segment (the last may hold fewer)
 };
+
+constexpr int kSsdOutputs = 0;    // full chunk work: y, and the final state from the last segment
+constexpr int kSsdStateOnly = 1;  // state update only: the segment's end state and summed decay
 
 constexpr int kSsdChunk = 64;  // steps per chunk: one per lane of a wave
 
@@ -137,9 +152,10 @@ __device__ __forceinline__ int gram_tile_j(int k) { return k < 4 ? k % 2 : k % 4
 template <int N, int NW>
 constexpr int kSsdWavesPerEu = (NW == 4 && N <= 128) ? 2 : 1;
 
-template <int N, int NW>
+template <int N, int NW, int MODE>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(kSsdWavesPerEu<N, NW>)))
 void ssd_chunk_kernel(const SsdArgs p) {
+  constexpr bool OUT = MODE == kSsdOutputs;
   constexpr int Q = kSsdChunk;
   constexpr int PS = 16 * NW;         // head channels per workgroup
   constexpr int T = 64 * NW;          // threads
@@ -171,7 +187,10 @@ void ssd_chunk_kernel(const SsdArgs p) {
   const int l16 = lane & 15, q = lane >> 4;
   const int64_t blk = blockIdx.x;
   const int slice = static_cast<int>(blk % p.nslices);
-  const int64_t bh = blk / p.nslices;
+  const int64_t bhs = blk / p.nslices;
+  const int64_t nbh = p.batch * p.nheads;
+  const int64_t bh = bhs % nbh;
+  const int seg = static_cast<int>(bhs / nbh);
   const int h = static_cast<int>(bh % p.nheads);
   const int64_t b = bh / p.nheads;
   const int g = h / (p.nheads / p.ngroups);
@@ -200,6 +219,8 @@ void ssd_chunk_kernel(const SsdArgs p) {
 #pragma unroll
   for (int u = 0; u < kXPer; ++u) rz[u] = ze[u] = xe[u] = ssd_u32x4_t{0u, 0u, 0u, 0u};
 
+  float dsum = 0.0f;  // sum of dt A log2(e) over the chunks run
+
   // FULL: all 64 steps of the chunk are inside the sequence (no bounds checks).
   auto load_chunk = [&](int64_t t0, auto full) {
     constexpr bool FULL = decltype(full)::value;
@@ -210,7 +231,8 @@ void ssd_chunk_kernel(const SsdArgs p) {
       const int64_t t = t0 + j;
       const bool ok = FULL || t < L;
       rb[u] = ok ? *reinterpret_cast<const ssd_u32x4_t*>(bg + t * bs + 8 * c8) : ssd_u32x4_t{0u, 0u, 0u, 0u};
-      rc[u] = ok ? *reinterpret_cast<const ssd_u32x4_t*>(cg + t * bs + 8 * c8) : ssd_u32x4_t{0u, 0u, 0u, 0u};
+      if constexpr (OUT)
+        rc[u] = ok ? *reinterpret_cast<const ssd_u32x4_t*>(cg + t * bs + 8 * c8) : ssd_u32x4_t{0u, 0u, 0u, 0u};
     }
 #pragma unroll
     for (int u = 0; u < kXPer; ++u) {
@@ -219,7 +241,7 @@ void ssd_chunk_kernel(const SsdArgs p) {
       const int64_t t = t0 + j;
       rx[u] = (FULL || t < L) ? *reinterpret_cast<const ssd_u32x4_t*>(xg + t * xs + 8 * p8)
                               : ssd_u32x4_t{0u, 0u, 0u, 0u};
-      if (zg)
+      if (OUT && zg)
         rz[u] = (FULL || t < L) ? *reinterpret_cast<const ssd_u32x4_t*>(zg + t * xs + 8 * p8)
                                 : ssd_u32x4_t{0u, 0u, 0u, 0u};
     }
@@ -266,6 +288,7 @@ void ssd_chunk_kernel(const SsdArgs p) {
     const float cum = wave_inclusive_sum(dtv * A2);
     const float last = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, cum), 63));
     const float wgt = hw_exp2(last - cum) * dtv;
+    dsum += last;
     if (wave == 0) {
       s_cum[lane] = cum;
       s_dt[lane] = dtv;
@@ -275,16 +298,18 @@ void ssd_chunk_kernel(const SsdArgs p) {
       const int k = tid + u * T;
       const int c8 = k % (N / 8), j = k / (N / 8);
       *reinterpret_cast<ssd_u32x4_t*>(&s_b[j * LDB + 8 * c8]) = rb[u];
-      *reinterpret_cast<ssd_u32x4_t*>(&s_c[j * LDB + 8 * c8]) = rc[u];
+      if constexpr (OUT) *reinterpret_cast<ssd_u32x4_t*>(&s_c[j * LDB + 8 * c8]) = rc[u];
     }
 #pragma unroll
     for (int u = 0; u < kXPer; ++u) {
       const int k = tid + u * T;
       const int p8 = k % (PS / 8), j = k / (PS / 8);
       const float w = __shfl(wgt, j);
-      *reinterpret_cast<ssd_u32x4_t*>(&s_x[j * LDX + 8 * p8]) = rx[u];
-      xe[u] = rx[u];
-      ze[u] = rz[u];
+      if constexpr (OUT) {
+        *reinterpret_cast<ssd_u32x4_t*>(&s_x[j * LDX + 8 * p8]) = rx[u];
+        xe[u] = rx[u];
+        ze[u] = rz[u];
+      }
       *reinterpret_cast<ssd_u32x4_t*>(&s_xw[j * LDX + 8 * p8]) =
           ssd_u32x4_t{pack_bf16x2(bf16_elem<0>(rx[u]) * w, bf16_elem<1>(rx[u]) * w),
                       pack_bf16x2(bf16_elem<2>(rx[u]) * w, bf16_elem<3>(rx[u]) * w),
@@ -293,29 +318,41 @@ void ssd_chunk_kernel(const SsdArgs p) {
     }
   };
 
+  // S tile nb, lane (q, r): dstate index 16 nb + 4q + r of channel pw (the final-state layout)
+  const int64_t state_off = ((b * H + h) * P + p0 + pw) * N + 4 * q;
+  const int64_t state_seg = nbh * P * N;  // elements per segment in the segment buffers
   ssd_f32x4_t S[NT];
+  if (p.seg_init && seg > 0) {
+    const float* si = p.seg_init + (seg - 1) * state_seg + state_off;
 #pragma unroll
-  for (int nb = 0; nb < NT; ++nb) S[nb] = ssd_f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int nb = 0; nb < NT; ++nb) S[nb] = *reinterpret_cast<const ssd_f32x4_t*>(si + 16 * nb);
+  } else {
+#pragma unroll
+    for (int nb = 0; nb < NT; ++nb) S[nb] = ssd_f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  }
 
-  const int64_t nchunks = (L + Q - 1) / Q;
+  const int64_t nch = (L + Q - 1) / Q;
+  const int64_t cbeg = static_cast<int64_t>(seg) * p.seg_chunks;
+  const int64_t cend = cbeg + p.seg_chunks < nch ? cbeg + p.seg_chunks : nch;
   using Full = std::integral_constant<bool, true>;
   using Ragged = std::integral_constant<bool, false>;
-  if (nchunks > 0) {
-    if (Q <= L) load_chunk(0, Full{});
-    else load_chunk(0, Ragged{});
+  if (cbeg < cend) {
+    if ((cbeg + 1) * Q <= L) load_chunk(cbeg * Q, Full{});
+    else load_chunk(cbeg * Q, Ragged{});
     publish_dt();
   }
-  for (int64_t c = 0; c < nchunks; ++c) {
+  for (int64_t c = cbeg; c < cend; ++c) {
     const int64_t t0 = c * Q;
     __syncthreads();  // every wave is done with the previous chunk's tiles
-    if (c > 0) epilogue(t0 - Q, Full{});  // the chunk before this one is whole
+    if (OUT && c > cbeg) epilogue(t0 - Q, Full{});  // the chunk before this one is whole
     stage_chunk(t0);
     __syncthreads();
-    if (c + 1 < nchunks) {
+    if (c + 1 < cend) {
       if (t0 + 2 * Q <= L) load_chunk(t0 + Q, Full{});
       else load_chunk(t0 + Q, Ragged{});
     }
 
+    if constexpr (OUT) {
     // M, split over the waves: G^T tile (j-block jb, i-block ib) = B_j . C_i (both rows are
     // dstate-contiguous: plain 16-byte reads), masked to j <= i, decayed and stored as M[i][j]
     {
@@ -382,6 +419,7 @@ void ssd_chunk_kernel(const SsdArgs p) {
     // Y^T tiles to LDS as Y[i][p] for the epilogue (run at the next chunk's staging)
 #pragma unroll
     for (int ib = 0; ib < 4; ++ib) *reinterpret_cast<ssd_f32x4_t*>(&s_y[(16 * ib + l16) * LDY + pe]) = acc[ib];
+    }  // OUT
 
     // state update: S = exp(cum_last) S + B^T (weighted X); the B^T operand of tile nb is rows
     // 16 nb .. +15 of B^T, read transposed from B (this lane addresses column 16 nb + 4 (l16 % 4))
@@ -395,23 +433,47 @@ void ssd_chunk_kernel(const SsdArgs p) {
       for (int nb = 0; nb < NT; ++nb)
         S[nb] = mfma16x16x32(lds_frag_tr(s_b, LDB, 32 * ks, q, l16, 16 * nb + 4 * (l16 & 3)), xw, S[nb]);
     }
-    if (c + 1 < nchunks) publish_dt();
+    if (c + 1 < cend) publish_dt();
   }
-  if (nchunks > 0) {
+  if (OUT && cbeg < cend) {
     __syncthreads();
-    epilogue((nchunks - 1) * Q, Ragged{});
+    epilogue((cend - 1) * Q, Ragged{});
+  }
+  if constexpr (!OUT) {
+    float* so = p.seg_state + seg * state_seg + state_off;
+#pragma unroll
+    for (int nb = 0; nb < NT; ++nb) *reinterpret_cast<ssd_f32x4_t*>(so + 16 * nb) = S[nb];
+    if (slice == 0 && tid == 0) p.seg_dsum[seg * nbh + bh] = dsum;
+    return;
   }
 
-  if (p.final_state) {
-    // tile nb, lane (q, r): dstate index 16 nb + 4q + r of channel pw
-    float* fs = p.final_state + ((b * H + h) * P + p0 + pw) * N + 4 * q;
+  if (p.final_state && seg == p.nseg - 1) {
+    float* fs = p.final_state + state_off;
 #pragma unroll
     for (int nb = 0; nb < NT; ++nb) *reinterpret_cast<ssd_f32x4_t*>(fs + 16 * nb) = S[nb];
   }
 }
 
+// Composes the segment states in order, one thread per (batch row, head, channel, dstate index):
+// S <- e^{sum dt A of segment s} S + S_end(s) for s = 0 .. nseg-2, leaving in seg_state[s] the state
+// that enters segment s + 1.
+template <int UNUSED = 0>
+__global__ __launch_bounds__(256) void ssd_carry_kernel(const SsdArgs p, int32_t dstate) {
+  const int64_t per_seg = p.batch * p.nheads * p.headdim * dstate;
+  const int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (e >= per_seg) return;
+  const int64_t bh = e / (static_cast<int64_t>(p.headdim) * dstate);
+  const int64_t nbh = p.batch * p.nheads;
+  float st = 0.0f;
+  for (int s = 0; s + 1 < p.nseg; ++s) {
+    st = fmaf(hw_exp2(p.seg_dsum[s * nbh + bh]), st, p.seg_state[s * per_seg + e]);
+    p.seg_state[s * per_seg + e] = st;
+  }
+}
+
 using SsdKernel = void (*)(const SsdArgs);
-// The chunk kernel for (dstate, waves per workgroup), or NULL when that pair is not instantiated.
-SsdKernel ssd_kernel(int64_t dstate, int waves);
+// The chunk kernel for (dstate, waves per workgroup, MODE), or NULL when that pair is not
+// instantiated.
+SsdKernel ssd_kernel(int64_t dstate, int waves, int mode);
 
 }  // namespace ssm

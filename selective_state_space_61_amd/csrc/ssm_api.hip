@@ -639,11 +639,13 @@ ssm_status_t ssm_ssd_fwd(int64_t batch, int64_t seqlen, int64_t nheads, int64_t 
   if (dstate != 32 && dstate != 64 && dstate != 128 && dstate != 256)
     return fail(SSM_ERR_UNSUPPORTED, "dstate %lld not in {32, 64, 128, 256}", (long long)dstate);
   if (headdim % 16 != 0) return fail(SSM_ERR_UNSUPPORTED, "headdim %lld is not a multiple of 16", (long long)headdim);
-  int slice = 0;
+  int slice = 0, segments = 0;
   if (opts) {
     for (int r : opts->reserved)
       if (r != 0) return fail(SSM_ERR_INVALID_ARG, "reserved option fields must be zero");
     slice = opts->head_slice;
+    segments = opts->segments;
+    if (segments < 0) return fail(SSM_ERR_INVALID_ARG, "segments %d is negative", segments);
     if (slice != 0 && slice != 16 && slice != 32 && slice != 64)
       return fail(SSM_ERR_INVALID_ARG, "head_slice %d not in {0, 16, 32, 64}", slice);
     if (slice != 0 && headdim % slice != 0)
@@ -675,13 +677,13 @@ ssm_status_t ssm_ssd_fwd(int64_t batch, int64_t seqlen, int64_t nheads, int64_t 
   int waves = slice / 16;
   if (waves == 0) {
     for (int w : {4, 2, 1}) {
-      if (headdim % (16 * w) == 0 && ssm::ssd_kernel(dstate, w)) {
+      if (headdim % (16 * w) == 0 && ssm::ssd_kernel(dstate, w, ssm::kSsdOutputs)) {
         waves = w;
         break;
       }
     }
   }
-  const ssm::SsdKernel k = ssm::ssd_kernel(dstate, waves);
+  const ssm::SsdKernel k = ssm::ssd_kernel(dstate, waves, ssm::kSsdOutputs);
   if (!k)
     return fail(SSM_ERR_UNSUPPORTED, "no SSD kernel for dstate %lld with %d head channels per workgroup",
                 (long long)dstate, 16 * waves);
@@ -697,7 +699,41 @@ ssm_status_t ssm_ssd_fwd(int64_t batch, int64_t seqlen, int64_t nheads, int64_t 
   a.nheads = static_cast<int32_t>(nheads); a.headdim = static_cast<int32_t>(headdim);
   a.ngroups = static_cast<int32_t>(ngroups); a.nslices = static_cast<int32_t>(nslices);
   a.softplus = dt_softplus ? 1 : 0;
-  hipLaunchKernelGGL(k, dim3(static_cast<unsigned>(blocks)), dim3(64 * waves), 0, static_cast<hipStream_t>(stream), a);
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+
+  // Sequence split: when the (batch row, head, slice) workgroups cannot fill the chip, cut the
+  // 64-step chunks into segments, up to two workgroups per compute unit
+  const int64_t nch = (seqlen + ssm::kSsdChunk - 1) / ssm::kSsdChunk;
+  int64_t nseg = segments;
+  if (nseg == 0) nseg = blocks < device_cus() ? (2 * device_cus()) / blocks : 1;
+  if (nseg > nch) nseg = nch;
+  if (nseg < 1) nseg = 1;
+  const int64_t seg_chunks = (nch + nseg - 1) / nseg;
+  if (nch > 0) nseg = (nch + seg_chunks - 1) / seg_chunks;  // no empty segment
+  a.nseg = static_cast<int32_t>(nseg);
+  a.seg_chunks = static_cast<int32_t>(seg_chunks > 0 ? seg_chunks : 1);
+  int64_t grid = blocks;
+  if (nseg > 1) {
+    // scratch: (nseg-1) segment states of batch*nheads*headdim*dstate fp32, then nseg*batch*nheads sums
+    int64_t per_seg, n_state, n_total, g1;
+    if (!mul_ok(nbh, headdim * dstate, &per_seg) || !mul_ok(per_seg, nseg - 1, &n_state) ||
+        __builtin_add_overflow(n_state, nseg * nbh, &n_total) || !mul_ok(blocks, nseg, &grid) || grid > 0x7fffffff ||
+        !mul_ok(blocks, nseg - 1, &g1))
+      return fail(SSM_ERR_UNSUPPORTED, "sequence split too large");
+    float* scratch = nullptr;
+    ssm_status_t s = get_scratch(st, n_total, &scratch);
+    if (s != SSM_OK) return s;
+    a.seg_state = scratch;
+    a.seg_dsum = scratch + n_state;
+    hipLaunchKernelGGL(ssm::ssd_kernel(dstate, waves, ssm::kSsdStateOnly), dim3(static_cast<unsigned>(g1)),
+                       dim3(64 * waves), 0, st, a);
+    if ((s = check_launch("SSD segment states")) != SSM_OK) return s;
+    hipLaunchKernelGGL(ssm::ssd_carry_kernel<0>, dim3(static_cast<unsigned>((per_seg + 255) / 256)), dim3(256), 0, st,
+                       a, static_cast<int32_t>(dstate));
+    if ((s = check_launch("SSD segment carry")) != SSM_OK) return s;
+    a.seg_init = a.seg_state;
+  }
+  hipLaunchKernelGGL(k, dim3(static_cast<unsigned>(grid)), dim3(64 * waves), 0, st, a);
   return check_launch("SSD chunk kernel");
 }
 

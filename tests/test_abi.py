@@ -236,8 +236,8 @@ def ssd(lib, batch=2, seqlen=8, nheads=4, headdim=64, dstate=128, ngroups=2, dty
                            fin, None, opts)
 
 
-def ssd_opts(slice_=0, reserved=0):
-    o = ssm.SsdOpts(head_slice=slice_)
+def ssd_opts(slice_=0, reserved=0, segments=0):
+    o = ssm.SsdOpts(head_slice=slice_, segments=segments)
     o.reserved[3] = reserved
     return ctypes.byref(o)
 
@@ -254,7 +254,7 @@ def ssd_opts(slice_=0, reserved=0):
     (dict(A=fake(2, 2)), MISALIGNED), (dict(fin=fake(9, 4)), MISALIGNED),
     (dict(y=fake(0)), INVALID), (dict(y=fake(3)), INVALID), (dict(fin=fake(4)), INVALID), (dict(fin=fake(8)), INVALID),
     (dict(opts=ssd_opts(8)), INVALID), (dict(opts=ssd_opts(48)), INVALID), (dict(headdim=32, opts=ssd_opts(64)), INVALID),
-    (dict(opts=ssd_opts(0, reserved=1)), INVALID),
+    (dict(opts=ssd_opts(0, reserved=1)), INVALID), (dict(opts=ssd_opts(0, segments=-2)), INVALID),
     # instantiated (dstate, waves) pairs: one wave only up to dstate 64, two up to 128
     (dict(opts=ssd_opts(16)), UNSUPPORTED), (dict(dstate=256, opts=ssd_opts(32)), UNSUPPORTED)])
 def test_ssd_validation(lib, kw, code):

@@ -60,6 +60,19 @@ def test_kernel_variants(o, N, slice_):
     compare(o, t, f"ssd N={N} slice={slice_}", head_slice=slice_)
 
 
+@pytest.mark.parametrize("segments,L", [(2, 128), (2, 200), (3, 200), (5, 333), (7, 130), (16, 1024), (4, 1)])
+def test_sequence_split(o, segments, L):
+    """The chunks cut into segments (states carried between them), whole and ragged."""
+    t = W.ssd_inputs(2, L, 4, 64, 128, 1, seed=segments * 1000 + L)
+    compare(o, t, f"ssd segments={segments} L={L}", segments=segments)
+
+
+@pytest.mark.parametrize("N,slice_", [(64, 64), (256, 64), (128, 32), (64, 16)])
+def test_sequence_split_variants(o, N, slice_):
+    t = W.ssd_inputs(1, 300, 2, 64, N, 1, seed=N + slice_ + 5)
+    compare(o, t, f"ssd segments=3 N={N} slice={slice_}", segments=3, head_slice=slice_)
+
+
 @pytest.mark.parametrize("L", [1, 5, 63, 64, 65, 128, 191])
 def test_ragged_lengths(o, L):
     t = W.ssd_inputs(2, L, 3, 32, 64, 1, seed=L + 400)
@@ -98,6 +111,9 @@ def test_empty_and_deterministic(o):
     # of nothing: a channel's arithmetic does not depend on its workgroup)
     y3, f3 = ssd_gpu(t, head_slice=32)
     assert torch.equal(y1, y3) and torch.equal(f1, f3), "head slice changed the result"
+    # a split sequence reorders the state sums, so it agrees to the tolerance, not bit for bit
+    y4, f4 = ssd_gpu(t, segments=3)
+    assert np.max(np.abs(to_host(y4) - to_host(y1))) <= TOL_SSD * np.max(np.abs(to_host(y1)))
     del ssm
 
 
