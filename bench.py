@@ -488,11 +488,14 @@ def summarize_traffic(fetch_csv, write_csv, workload):
     scan = [k for k in fetch if marker in k]
     if not calib or not scan:
         raise SystemExit(f"calibration or measured kernel missing in {fetch_csv}: {list(fetch)}")
-    ck, sk = calib[0], scan[0]
+    ck = calib[0]
+    # the SSD call may be several kernels (segment states, carry, outputs): sum them per call
+    kernels = [k for k in fetch if "ssd_" in k] if family == "ssd" else [scan[0]]
+    sk = " + ".join(kernels)
     kib = CALIB_BYTES / 1024
     f_scale = kib / max(fetch[ck]), kib / max(write[ck])  # the copy reads and writes CALIB_BYTES
-    f_kib = sorted(fetch[sk])[len(fetch[sk]) // 2]
-    w_kib = sorted(write[sk])[len(write[sk]) // 2]
+    f_kib = sum(sorted(fetch[k])[len(fetch[k]) // 2] for k in kernels)
+    w_kib = sum(sorted(write[k])[len(write[k]) // 2] for k in kernels)
     if family == "conv":
         c = CONV_SHAPE
         alg = conv_bytes(c["batch"], c["seqlen"], c["dim"], c["width"], 2)

@@ -260,7 +260,7 @@ SSM_API ssm_status_t ssm_state_update_ex(int64_t batch, int64_t dim, int64_t dst
  * or 64, dividing headdim), or 0 for the largest one the library has for
  * this dstate and headdim.  segments: pieces the sequence is cut into (each
  * a whole number of 64-step chunks; 1 = none, 0 = chosen by the library:
- * enough to give every compute unit two workgroups when the batch rows and
+ * enough to give every compute unit a workgroup when the batch rows and
  * heads alone cannot).  reserved must be zero. */
 typedef struct {
   int32_t head_slice;
