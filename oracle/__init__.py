@@ -89,7 +89,8 @@ class Oracle:
         lib.oracle_scan_bwd.argtypes = [i64, i64, i64, i64, i32, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp,
                                         vp, vp, vp, vp, vp, vp]
         lib.oracle_scan_bwd.restype = i32
-        lib.oracle_ssd.argtypes = [i64, i64, i64, i64, i64, i64, i32, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, i32]
+        lib.oracle_ssd.argtypes = [i64, i64, i64, i64, i64, i64, i32, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp,
+                                   i32]
         lib.oracle_ssd.restype = i32
         lib.oracle_causal_conv1d.argtypes = [i64, i64, i64, i64, i32, vp, vp, vp, vp, i32, vp, vp]
         lib.oracle_causal_conv1d.restype = i32
@@ -219,12 +220,14 @@ class Oracle:
             raise ValueError("oracle_scan_bwd rejected its arguments")
         return out
 
-    def ssd(self, x, dt, A, B, C, D=None, z=None, dt_bias=None, dt_softplus=False,
+    def ssd(self, x, dt, A, B, C, D=None, z=None, dt_bias=None, dt_softplus=False, h0=None,
             nthreads: int = 1) -> Tuple[np.ndarray, np.ndarray]:
         """Mamba-2 SSD layer.  x, z: (batch, L, nheads, headdim); dt: (batch, L, nheads); B, C:
-        (batch, L, ngroups, dstate); A, D, dt_bias: (nheads,) fp32.  Returns y (like x) and
-        final_state (batch, nheads, headdim, dstate), float64."""
+        (batch, L, ngroups, dstate); A, D, dt_bias: (nheads,) fp32; h0: the entering state
+        (batch, nheads, headdim, dstate) or None (zero).  Returns y (like x) and final_state
+        (batch, nheads, headdim, dstate), float64."""
         x, dt, B, C, z = _c(x), _c(dt), _c(B), _c(C), _c(z)
+        h0 = _c(h0, np.float64)
         code = _dtype_code(x)
         A, D, dt_bias = _c(A, np.float32), _c(D, np.float32), _c(dt_bias, np.float32)
         batch, L, H, P = x.shape
@@ -232,8 +235,10 @@ class Oracle:
         assert dt.shape == (batch, L, H) and B.shape == C.shape == (batch, L, G, N) and A.shape == (H,)
         y = np.empty((batch, L, H, P))
         fin = np.empty((batch, H, P, N))
+        if h0 is not None:
+            assert h0.shape == (batch, H, P, N)
         rc = self._lib.oracle_ssd(batch, L, H, P, N, G, code, _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
-                                  _ptr(z), _ptr(dt_bias), int(bool(dt_softplus)), _ptr(y), _ptr(fin),
+                                  _ptr(z), _ptr(dt_bias), int(bool(dt_softplus)), _ptr(h0), _ptr(y), _ptr(fin),
                                   int(nthreads))
         if rc != 0:
             raise ValueError("oracle_ssd rejected its arguments")

@@ -326,7 +326,8 @@ int oracle_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, 
  * matrix; sec. 4.2: multi-head; sec. 5.2: the Mamba2 layer with headdim and
  * d_state).  A is one scalar per head, B and C are shared by the heads of a
  * group, and Bbar = dt B as in the selective scan.  For batch b, head h
- * (group g = h / (nheads / ngroups)) and head channel p, from S = 0:
+ * (group g = h / (nheads / ngroups)) and head channel p, from S = h0[b,h,p,:]
+ * (zero when h0 is NULL):
  *   dt = softplus(dt[b,t,h] + dt_bias[h])  (or without softplus)
  *   S[p,n] = exp(dt A[h]) S[p,n] + dt x[b,t,h,p] B[b,t,g,n]
  *   y[b,t,h,p] = sum_n C[b,t,g,n] S[p,n] + D[h] x[b,t,h,p];  y *= silu(z[b,t,h,p]) if z
@@ -336,8 +337,8 @@ int oracle_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, 
  * ------------------------------------------------------------------------- */
 int oracle_ssd(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, int64_t dstate, int64_t ngroups,
                int dtype, const void *x, const void *dt, const float *A, const void *B, const void *C,
-               const float *Dskip, const void *z, const float *dt_bias, int dt_softplus, double *y,
-               double *final_state, int nthreads) {
+               const float *Dskip, const void *z, const float *dt_bias, int dt_softplus, const double *h0,
+               double *y, double *final_state, int nthreads) {
   if (batch < 0 || seqlen < 0 || nheads < 1 || headdim < 1 || dstate < 1 || ngroups < 1) return -1;
   if (nheads % ngroups != 0 || !x || !dt || !A || !B || !C || !y) return -1;
   const int64_t H = nheads, P = headdim, N = dstate, G = ngroups, hpg = H / G;
@@ -349,6 +350,8 @@ int oracle_ssd(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, i
     const int64_t b = bh / H, h = bh % H, g = h / hpg;
     double *S = (double *)calloc((size_t)(P * N), sizeof(double));
     if (!S) continue;
+    if (h0)
+      for (int64_t i = 0; i < P * N; ++i) S[i] = h0[bh * P * N + i];
     for (int64_t t = 0; t < seqlen; ++t) {
       const double v = load_elem(dt, dtype, (b * seqlen + t) * H + h) + (dt_bias ? (double)dt_bias[h] : 0.0);
       const double d = dt_softplus ? softplus(v) : v;

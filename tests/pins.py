@@ -617,10 +617,35 @@ def pin_ssd_dual_matrix_form(o):
             _close(y[b, :, h, :], ref, 1e-12, f"SSD dual form b={b} h={h}")
 
 
+def pin_ssd_resume_from_state(o):
+    """Running the layer over L steps equals running it over the first k steps and then over the
+    rest from the state it left (the state is the whole memory of the recurrence), for y and the
+    final state; also with a nonzero entering state for the first part."""
+    c = _ssd_case(53, L=13)
+    g = np.random.default_rng(54)
+    batch, L, H, P = c["x"].shape
+    N = c["B"].shape[3]
+    h0 = g.normal(size=(batch, H, P, N))
+    kw = dict(D=c["D"], z=c["z"], dt_bias=c["dt_bias"], dt_softplus=True)
+    y, fin = o.ssd(c["x"], c["dt"], c["A"], c["B"], c["C"], h0=h0, **kw)
+    for k in (1, 6, 12):
+        cut = lambda a, lo, hi: np.ascontiguousarray(a[:, lo:hi])
+        y1, f1 = o.ssd(cut(c["x"], 0, k), cut(c["dt"], 0, k), c["A"], cut(c["B"], 0, k), cut(c["C"], 0, k), h0=h0,
+                       D=c["D"], z=cut(c["z"], 0, k), dt_bias=c["dt_bias"], dt_softplus=True)
+        y2, f2 = o.ssd(cut(c["x"], k, L), cut(c["dt"], k, L), c["A"], cut(c["B"], k, L), cut(c["C"], k, L), h0=f1,
+                       D=c["D"], z=cut(c["z"], k, L), dt_bias=c["dt_bias"], dt_softplus=True)
+        _close(np.concatenate([y1, y2], axis=1), y, 1e-13, f"SSD resumed at {k}: y")
+        _close(f2, fin, 1e-13, f"SSD resumed at {k}: final state")
+    # and the entering state matters: a zero one gives a different result
+    y0, _ = o.ssd(c["x"], c["dt"], c["A"], c["B"], c["C"], **kw)
+    assert np.max(np.abs(y0 - y)) > 1e-3 * np.max(np.abs(y)), "the entering state had no effect"
+
+
 ALL_PINS = [pin_worked_examples, pin_unrolled_sum, pin_lti_convolution, pin_linearity,
             pin_channel_independence, pin_causality, pin_zero_step, pin_impulse_long_carry,
             pin_decode_equals_scan, pin_associative_scan, pin_special_values, pin_storage_widening,
             pin_channel_selection, pin_conv_library_convolution, pin_conv_impulse, pin_conv_silu,
             pin_conv_chaining, pin_conv_decode_equals_fwd, pin_conv_causality, pin_backward_finite_differences,
             pin_backward_linear_in_dy, pin_zoh_steady_state, pin_zoh_semigroup, pin_zoh_small_step_limit,
-            pin_zoh_decode_equals_scan, pin_ssd_equals_selective_scan, pin_ssd_dual_matrix_form]
+            pin_zoh_decode_equals_scan, pin_ssd_equals_selective_scan, pin_ssd_dual_matrix_form,
+            pin_ssd_resume_from_state]

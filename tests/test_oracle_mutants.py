@@ -63,6 +63,8 @@ MUTANTS = [
     ("ssd_no_dt_on_input", "S[p * N + n] = a * S[p * N + n] + d * xv * load_elem(B, dtype, ibc + n);",
      "S[p * N + n] = a * S[p * N + n] + xv * load_elem(B, dtype, ibc + n);"),
     ("ssd_readout_uses_B", "acc += load_elem(C, dtype, ibc + n) * S[p * N + n];", "acc += load_elem(B, dtype, ibc + n) * S[p * N + n];"),
+    ("ssd_initial_state_ignored", "      for (int64_t i = 0; i < P * N; ++i) S[i] = h0[bh * P * N + i];",
+     "      for (int64_t i = 0; i < P * N; ++i) S[i] = 0.0 * h0[bh * P * N + i];"),
     ("conv_silu_skipped", "out[(b * seqlen + t) * dim + d] = apply_silu ? silu(acc) : acc;",
      "out[(b * seqlen + t) * dim + d] = acc;"),
 ]
