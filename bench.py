@@ -329,6 +329,45 @@ def bench_ssd(name, steps, warmup, torch, np, W, ssm, device):
             "mfma_flops": flops, "mfma_tflops": flops / (ms * 1e-3) / 1e12}
 
 
+SSD_DECODE = dict(batch=64, nheads=64, headdim=64, dstate=128, ngroups=1, steps=64, ring=4, seed=61022)
+
+
+def ssd_decode_bytes_per_step(c):
+    """State read and written once (fp32), x and z read and y written (bf16), dt, B, C read, the
+    per-head parameters."""
+    bhp = c["batch"] * c["nheads"] * c["headdim"]
+    return (2 * 4 * bhp * c["dstate"] + 3 * 2 * bhp + 2 * c["batch"] * c["nheads"]
+            + 2 * 2 * c["batch"] * c["ngroups"] * c["dstate"] + 3 * 4 * c["nheads"])
+
+
+def bench_ssd_decode(torch, np, W, ssm, device):
+    """One token of the Mamba-2 layer (ssm_ssd_state_update) for a 64-row decode batch at the layer
+    shape (64 heads x 64, dstate 128): a ring of 4 states (537 MB, twice the Infinity Cache), one
+    state per step, 64 steps captured as a HIP graph and replayed."""
+    c = SSD_DECODE
+    t = W.ssd_inputs(c["batch"], c["steps"], c["nheads"], c["headdim"], c["dstate"], c["ngroups"], c["seed"])
+    sm = {k: (np.ascontiguousarray(np.swapaxes(v, 0, 1)) if k in ("x", "dt", "B", "C", "z") else v)
+          for k, v in t.items()}
+    d = {k: dev_tensor(v, torch, np, device) for k, v in sm.items()}
+    states = [torch.zeros(c["batch"], c["nheads"], c["headdim"], c["dstate"], device=device) for _ in range(c["ring"])]
+    ys = torch.empty_like(d["x"])
+
+    def call(i):
+        s = i % c["steps"]
+        ssm.ssm_ssd_state_update(states[i % c["ring"]], d["x"][s], d["dt"][s], d["A"], d["B"][s], d["C"][s], D=d["D"],
+                                 z=d["z"][s], dt_bias=d["dt_bias"], dt_softplus=True, y=ys[s])
+
+    ms = time_graph(torch, call, c["steps"], 4, device)
+    step_bytes = ssd_decode_bytes_per_step(c)
+    del states
+    torch.cuda.empty_cache()
+    return {**{k: c[k] for k in ("batch", "nheads", "headdim", "dstate", "ngroups", "ring")}, "io_dtype": "bf16",
+            "ms_per_step": ms, "tokens_per_s": c["batch"] / (ms * 1e-3),
+            "updates_per_s": c["batch"] * c["nheads"] * c["headdim"] * c["dstate"] / (ms * 1e-3),
+            "alg_bytes_per_step": step_bytes, "hbm_gbps": step_bytes / (ms * 1e-3) / 1e9,
+            "hbm_frac": step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS}
+
+
 def bench_scan_bwd(steps, warmup, torch, np, W, ssm, device):
     """The backward scan on the 130M-shaped layer (inputs, dy and gradients resident in HBM;
     two input sets rotated).  Reports the time per call of the whole backward (both kernels)."""
@@ -594,6 +633,9 @@ def main():
             extra["ssd_" + sname] = r
             log(f"[bench] SSD {sname}: {r['kernel_ms'] * 1e3:.1f} us/call, {r['hbm_gbps']:.0f} GB/s, "
                 f"{r['mfma_tflops']:.1f} TFLOP/s on matrix cores")
+        extra["ssd_decode"] = bench_ssd_decode(torch, np, W, ssm, device)
+        log(f"[bench] SSD decode step (64 x 64 heads x 64 x 128): {extra['ssd_decode']['ms_per_step'] * 1e3:.1f} us, "
+            f"{extra['ssd_decode']['hbm_gbps']:.0f} GB/s")
 
     hbm_frac = main_res["hbm_frac"]
     alu_frac = main_res["valu_slot_frac"]

@@ -275,7 +275,8 @@ typedef struct {
  * larger states; sec. 5.2: the Mamba2 layer with headdim and d_state).  A is
  * one scalar per head, Bbar = dt B as in ssm_scan_fwd, and the heads of a
  * group (nheads / ngroups consecutive heads) share B and C.  For batch row
- * b, head h in group g and head channel p, from a zero state S (dstate):
+ * b, head h in group g and head channel p, from S = initial_state[b,h,p,:]
+ * (zero when NULL):
  *
  *   dt_t = softplus(dt[b,t,h] + dt_bias[h])   (no softplus when dt_softplus == 0)
  *   S    = exp(dt_t A[h]) S + dt_t x[b,t,h,p] B[b,t,g,:]
@@ -286,6 +287,9 @@ typedef struct {
  *   dt             (batch, seqlen, nheads)           bf16
  *   B, C           (batch, seqlen, ngroups, dstate)  bf16
  *   A              (nheads) fp32;  D, dt_bias (nheads) fp32 or NULL
+ *   initial_state  (batch, nheads, headdim, dstate)  fp32 state entering the
+ *                  sequence, or NULL (zero): the final state of an earlier call
+ *                  continues it
  *   final_state    (batch, nheads, headdim, dstate)  fp32, or NULL
  *
  * The sequence is taken in chunks of 64 steps whose products run on bf16
@@ -295,16 +299,45 @@ typedef struct {
  * stream) scratch as the split-sequence scan: (segments-1)*batch*nheads*
  * headdim*dstate + segments*batch*nheads fp32 (same rules as ssm_scan_fwd).
  * Storage must be bf16 (SSM_F32 gives SSM_ERR_UNSUPPORTED).  dstate must be
- * 32, 64, 128 or 256 and headdim a multiple of 16 (else SSM_ERR_UNSUPPORTED).
- * x, z, y, B, C and final_state must be 16-byte aligned (else
- * SSM_ERR_MISALIGNED).  Outputs must not overlap an input or each other.
- * opts may be NULL.
+ * 32, 64, 128 or 256 and headdim a multiple of 16; workgroups take 16-, 32-
+ * or 64-channel slices of a head, dstate 128 only 32 or 64 and dstate 256
+ * only 64, so dstate 256 needs headdim a multiple of 64 and dstate 128 one of
+ * 32 (else SSM_ERR_UNSUPPORTED).
+ * x, z, y, B, C, initial_state and final_state must be 16-byte aligned
+ * (else SSM_ERR_MISALIGNED).  Outputs must not overlap an input or each
+ * other.  opts may be NULL.
  */
 SSM_API ssm_status_t ssm_ssd_fwd(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, int64_t dstate,
                                  int64_t ngroups, ssm_dtype_t dtype, const void *x, const void *dt, const float *A,
                                  const void *B, const void *C, const float *D, const void *z,
-                                 const float *dt_bias, int dt_softplus, void *y, float *final_state, void *stream,
-                                 const ssm_ssd_opts_t *opts);
+                                 const float *dt_bias, int dt_softplus, const float *initial_state, void *y,
+                                 float *final_state, void *stream, const ssm_ssd_opts_t *opts);
+
+/*
+ * One token of the same layer, the recurrent view of "Mamba 论文精读" sec.
+ * 4.1 (O(1) work per token): for batch row b, head h in group g, channel p,
+ *
+ *   dt = softplus(dt[b,h] + dt_bias[h])   (no softplus when dt_softplus == 0)
+ *   state[b,h,p,:] = exp(dt A[h]) state[b,h,p,:] + dt x[b,h,p] B[b,g,:]
+ *   y[b,h,p] = (C[b,g,:] . state[b,h,p,:] + D[h] x[b,h,p]) * silu(z[b,h,p])
+ *
+ *   state      (batch, nheads, headdim, dstate) fp32, updated in place
+ *              (16-byte aligned)
+ *   x, z, y    (batch, nheads, headdim) bf16; z may be NULL
+ *   dt         (batch, nheads) bf16
+ *   B, C       (batch, ngroups, dstate) bf16 (8-byte aligned)
+ *   A, D, dt_bias (nheads) fp32; D and dt_bias may be NULL
+ *
+ * Running it over the tokens of a sequence from an initial state gives
+ * ssm_ssd_fwd's outputs and final state for that initial state (up to the
+ * rounding of the chunked products).  dstate must be 32, 64, 128 or 256;
+ * storage bf16.
+ */
+SSM_API ssm_status_t ssm_ssd_state_update(int64_t batch, int64_t nheads, int64_t headdim, int64_t dstate,
+                                          int64_t ngroups, ssm_dtype_t dtype, float *state, const void *x,
+                                          const void *dt, const float *A, const void *B, const void *C,
+                                          const float *D, const void *z, const float *dt_bias, int dt_softplus,
+                                          void *y, void *stream);
 
 /* Static string naming a status code ("SSM_OK", ...); never NULL. */
 SSM_API const char *ssm_status_string(ssm_status_t status);

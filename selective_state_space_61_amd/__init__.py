@@ -30,7 +30,7 @@ STATUS_NAMES = {0: "SSM_OK", 1: "SSM_ERR_INVALID_ARG", 2: "SSM_ERR_UNSUPPORTED",
                 4: "SSM_ERR_HIP"}
 EXPORTED = ("ssm_scan_fwd", "ssm_scan_fwd_ex", "ssm_scan_bwd", "ssm_state_update", "ssm_state_update_ex",
             "ssm_causal_conv1d_fwd",
-            "ssm_causal_conv1d_update", "ssm_ssd_fwd", "ssm_status_string", "ssm_last_error", "ssm_abi_version")
+            "ssm_causal_conv1d_update", "ssm_ssd_fwd", "ssm_ssd_state_update", "ssm_status_string", "ssm_last_error", "ssm_abi_version")
 
 
 class SsmError(RuntimeError):
@@ -82,9 +82,11 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
     lib.ssm_causal_conv1d_fwd.restype = i32
     lib.ssm_causal_conv1d_update.argtypes = [i64, i64, i64, i32, vp, vp, vp, vp, i32, vp, vp]
     lib.ssm_causal_conv1d_update.restype = i32
-    lib.ssm_ssd_fwd.argtypes = [i64, i64, i64, i64, i64, i64, i32, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp,
+    lib.ssm_ssd_fwd.argtypes = [i64, i64, i64, i64, i64, i64, i32, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp,
                                 ctypes.POINTER(SsdOpts)]
     lib.ssm_ssd_fwd.restype = i32
+    lib.ssm_ssd_state_update.argtypes = [i64, i64, i64, i64, i64, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp]
+    lib.ssm_ssd_state_update.restype = i32
     lib.ssm_status_string.argtypes = [i32]
     lib.ssm_status_string.restype = ctypes.c_char_p
     lib.ssm_last_error.argtypes = []
@@ -302,6 +304,7 @@ def ssm_causal_conv1d_update(conv_state: Optional[torch.Tensor], x: torch.Tensor
 def ssm_ssd_fwd(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, B: torch.Tensor, C: torch.Tensor,
                 D: Optional[torch.Tensor] = None, z: Optional[torch.Tensor] = None,
                 dt_bias: Optional[torch.Tensor] = None, dt_softplus: bool = False, *,
+                initial_state: Optional[torch.Tensor] = None,
                 y: Optional[torch.Tensor] = None, final_state: Optional[torch.Tensor] = None,
                 return_final_state: bool = True, head_slice: int = 0, segments: int = 0,
                 stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
@@ -323,6 +326,7 @@ def ssm_ssd_fwd(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, B: torch.Ten
     _need(D, "D", (nheads,), torch.float32, dev, optional=True)
     _need(z, "z", tuple(x.shape), ty, dev, optional=True)
     _need(dt_bias, "dt_bias", (nheads,), torch.float32, dev, optional=True)
+    _need(initial_state, "initial_state", (batch, nheads, headdim, dstate), torch.float32, dev, optional=True)
     if y is None:
         y = torch.empty_like(x)
     _need(y, "y", tuple(x.shape), ty, dev)
@@ -331,10 +335,42 @@ def ssm_ssd_fwd(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, B: torch.Ten
     _need(final_state, "final_state", (batch, nheads, headdim, dstate), torch.float32, dev, optional=True)
     opts = SsdOpts(head_slice=int(head_slice), segments=int(segments))
     status = lib.ssm_ssd_fwd(batch, seqlen, nheads, headdim, dstate, ngroups, code, _ptr(x), _ptr(dt), _ptr(A),
-                             _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(dt_bias), int(bool(dt_softplus)), _ptr(y),
-                             _ptr(final_state), _stream(dev, stream), ctypes.byref(opts))
+                             _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(dt_bias), int(bool(dt_softplus)),
+                             _ptr(initial_state), _ptr(y), _ptr(final_state), _stream(dev, stream), ctypes.byref(opts))
     _check(status)
     return y, final_state
+
+
+def ssm_ssd_state_update(state: torch.Tensor, x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, B: torch.Tensor,
+                         C: torch.Tensor, D: Optional[torch.Tensor] = None, z: Optional[torch.Tensor] = None,
+                         dt_bias: Optional[torch.Tensor] = None, dt_softplus: bool = False, *,
+                         y: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """One token of the Mamba-2 SSD layer (include/ssm.h: ssm_ssd_state_update).  state: (batch,
+    nheads, headdim, dstate) fp32, updated in place; x, z: (batch, nheads, headdim) bf16; dt:
+    (batch, nheads) bf16; B, C: (batch, ngroups, dstate) bf16.  Returns y (batch, nheads, headdim)."""
+    lib = load_library()
+    if x.dim() != 3 or B.dim() != 3:
+        raise ValueError("x must be (batch, nheads, headdim) and B (batch, ngroups, dstate)")
+    batch, nheads, headdim = x.shape
+    ngroups, dstate = B.shape[1], B.shape[2]
+    dev, ty = x.device, x.dtype
+    code = _dtype_code(x)
+    _need(state, "state", (batch, nheads, headdim, dstate), torch.float32, dev)
+    _need(dt, "dt", (batch, nheads), ty, dev)
+    _need(A, "A", (nheads,), torch.float32, dev)
+    _need(B, "B", (batch, ngroups, dstate), ty, dev)
+    _need(C, "C", (batch, ngroups, dstate), ty, dev)
+    _need(D, "D", (nheads,), torch.float32, dev, optional=True)
+    _need(z, "z", tuple(x.shape), ty, dev, optional=True)
+    _need(dt_bias, "dt_bias", (nheads,), torch.float32, dev, optional=True)
+    if y is None:
+        y = torch.empty_like(x)
+    _need(y, "y", tuple(x.shape), ty, dev)
+    status = lib.ssm_ssd_state_update(batch, nheads, headdim, dstate, ngroups, code, _ptr(state), _ptr(x), _ptr(dt),
+                                      _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(dt_bias),
+                                      int(bool(dt_softplus)), _ptr(y), _stream(dev, stream))
+    _check(status)
+    return y
 
 
 def abi_version() -> int:
@@ -342,5 +378,5 @@ def abi_version() -> int:
 
 
 __all__ = ["ssm_scan_fwd", "ssm_scan_bwd", "ssm_state_update", "ssm_causal_conv1d_fwd", "ssm_causal_conv1d_update",
-           "ssm_ssd_fwd", "SsdOpts", "abi_version", "load_library", "SsmError", "ScanOpts", "UpdateOpts",
+           "ssm_ssd_fwd", "ssm_ssd_state_update", "SsdOpts", "abi_version", "load_library", "SsmError", "ScanOpts", "UpdateOpts",
            "LIBRARY", "EXPORTED"]

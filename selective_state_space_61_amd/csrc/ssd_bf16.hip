@@ -18,4 +18,14 @@ SsdKernel ssd_kernel(int64_t dstate, int waves, int mode) {
   return nullptr;
 }
 
+SsdUpdateKernel ssd_update_kernel(int64_t dstate) {
+  switch (dstate) {
+    case 32: return ssd_state_update_kernel<32>;
+    case 64: return ssd_state_update_kernel<64>;
+    case 128: return ssd_state_update_kernel<128>;
+    case 256: return ssd_state_update_kernel<256>;
+    default: return nullptr;
+  }
+}
+
 }  // namespace ssm

@@ -63,6 +63,7 @@ struct SsdArgs {
   const float* dt_bias;  // (nheads) or NULL
   uint16_t* y;           // like x
   float* final_state;    // (batch, nheads, headdim, dstate) or NULL
+  const float* init_state;  // (batch, nheads, headdim, dstate) state entering the sequence, or NULL (zero)
   const float* seg_init;  // (nseg-1, batch, nheads, headdim, dstate): state entering segment s >= 1 at
                           // [s-1], or NULL (every segment starts from zero)
   float* seg_state;       // same layout: end state of segment s from zero at [s] (state-only pass)
@@ -322,8 +323,12 @@ void ssd_chunk_kernel(const SsdArgs p) {
   const int64_t state_off = ((b * H + h) * P + p0 + pw) * N + 4 * q;
   const int64_t state_seg = nbh * P * N;  // elements per segment in the segment buffers
   ssd_f32x4_t S[NT];
-  if (p.seg_init && seg > 0) {
-    const float* si = p.seg_init + (seg - 1) * state_seg + state_off;
+  // the entering state: the carried one for a later segment, the caller's for the first (the
+  // state-only pass starts every segment from zero; the carry adds the caller's state)
+  const float* si = (p.seg_init && seg > 0) ? p.seg_init + (seg - 1) * state_seg + state_off
+                    : (OUT && p.init_state && seg == 0) ? p.init_state + state_off
+                                                        : nullptr;
+  if (si) {
 #pragma unroll
     for (int nb = 0; nb < NT; ++nb) S[nb] = *reinterpret_cast<const ssd_f32x4_t*>(si + 16 * nb);
   } else {
@@ -455,8 +460,8 @@ void ssd_chunk_kernel(const SsdArgs p) {
 }
 
 // Composes the segment states in order, one thread per (batch row, head, channel, dstate index):
-// S <- e^{sum dt A of segment s} S + S_end(s) for s = 0 .. nseg-2, leaving in seg_state[s] the state
-// that enters segment s + 1.
+// from the caller's entering state (zero without one), S <- e^{sum dt A of segment s} S + S_end(s)
+// for s = 0 .. nseg-2, leaving in seg_state[s] the state that enters segment s + 1.
 template <int UNUSED = 0>
 __global__ __launch_bounds__(256) void ssd_carry_kernel(const SsdArgs p, int32_t dstate) {
   const int64_t per_seg = p.batch * p.nheads * p.headdim * dstate;
@@ -464,12 +469,87 @@ __global__ __launch_bounds__(256) void ssd_carry_kernel(const SsdArgs p, int32_t
   if (e >= per_seg) return;
   const int64_t bh = e / (static_cast<int64_t>(p.headdim) * dstate);
   const int64_t nbh = p.batch * p.nheads;
-  float st = 0.0f;
+  float st = p.init_state ? p.init_state[e] : 0.0f;
   for (int s = 0; s + 1 < p.nseg; ++s) {
     st = fmaf(hw_exp2(p.seg_dsum[s * nbh + bh]), st, p.seg_state[s * per_seg + e]);
     p.seg_state[s * per_seg + e] = st;
   }
 }
+
+// ---------------------------------------------------------------------------------------------
+// One token of the layer, the recurrent view of "Mamba 论文精读" sec. 4.1 (O(1) work per token):
+// for each (batch row b, head h, channel p) and its group g,
+//   dt = softplus(dt[b,h] + dt_bias[h]);  S[b,h,p,:] = exp(dt A[h]) S[b,h,p,:] + dt x[b,h,p] B[b,g,:]
+//   y[b,h,p] = (C[b,g,:] . S[b,h,p,:] + D[h] x[b,h,p]) * silu(z[b,h,p])
+// The state is read and written once: a streaming kernel.  A thread owns 4 consecutive dstate
+// entries of one channel (16-byte state access, 8-byte B and C); the N/4 lanes of a channel add
+// their partial read-outs with cross-lane shuffles.  The decay is one exp per channel.
+// ---------------------------------------------------------------------------------------------
+struct SsdUpdateArgs {
+  float* state;          // (batch, nheads, headdim, dstate) fp32, in place
+  const uint16_t* x;     // (batch, nheads, headdim) bf16
+  const uint16_t* dt;    // (batch, nheads) bf16
+  const float* A;        // (nheads)
+  const uint16_t* B;     // (batch, ngroups, dstate) bf16
+  const uint16_t* C;
+  const float* D;        // (nheads) or NULL
+  const uint16_t* z;     // like x, or NULL
+  const float* dt_bias;  // (nheads) or NULL
+  uint16_t* y;           // like x
+  int64_t batch;
+  int32_t nheads;
+  int32_t headdim;
+  int32_t ngroups;
+  int32_t softplus;
+};
+
+constexpr int kSsdUpdateThreads = 256;
+
+template <int N>
+__global__ __launch_bounds__(kSsdUpdateThreads) void ssd_state_update_kernel(const SsdUpdateArgs p) {
+  constexpr int TPC = N / 4;  // lanes per channel
+  static_assert(N % 4 == 0 && TPC <= 64 && 64 % TPC == 0, "a channel's lanes share one wave");
+  const int64_t H = p.nheads, P = p.headdim, G = p.ngroups;
+  const int64_t nquads = p.batch * H * P * TPC;
+  const int64_t q = static_cast<int64_t>(blockIdx.x) * kSsdUpdateThreads + threadIdx.x;
+  const bool ok = q < nquads;
+  // a thread past the end works on quad 0 (in bounds) and stores nothing, so every lane of a
+  // channel takes part in the shuffles
+  const int64_t qq = ok ? q : 0;
+  const int64_t ch = qq / TPC;  // (b * H + h) * P + p
+  const int n0 = static_cast<int>(qq % TPC) * 4;
+  const int64_t bh = ch / P;
+  const int64_t h = bh % H, b = bh / H;
+  const int64_t g = h / (H / G);
+  const float xv = bf16_lo(p.x[ch]);
+  const float v = bf16_lo(p.dt[bh]) + (p.dt_bias ? p.dt_bias[h] : 0.0f);
+  const float dtv = p.softplus ? softplus_f32(v) : v;
+  const float a = hw_exp2(dtv * (p.A[h] * kLog2e));
+  const float w = dtv * xv;
+  float* st = p.state + ch * N + n0;
+  float4 s4 = *reinterpret_cast<const float4*>(st);
+  const uint2 b2 = *reinterpret_cast<const uint2*>(p.B + (b * G + g) * N + n0);
+  const uint2 c2 = *reinterpret_cast<const uint2*>(p.C + (b * G + g) * N + n0);
+  s4.x = fmaf(a, s4.x, w * bf16_lo(b2.x));
+  s4.y = fmaf(a, s4.y, w * bf16_hi(b2.x));
+  s4.z = fmaf(a, s4.z, w * bf16_lo(b2.y));
+  s4.w = fmaf(a, s4.w, w * bf16_hi(b2.y));
+  float yp = bf16_lo(c2.x) * s4.x;
+  yp = fmaf(bf16_hi(c2.x), s4.y, yp);
+  yp = fmaf(bf16_lo(c2.y), s4.z, yp);
+  yp = fmaf(bf16_hi(c2.y), s4.w, yp);
+  if (ok) *reinterpret_cast<float4*>(st) = s4;
+#pragma unroll
+  for (int off = 1; off < TPC; off <<= 1) yp += __shfl_xor(yp, off, 64);
+  if (ok && n0 == 0) {
+    float yv = fmaf(p.D ? p.D[h] : 0.0f, xv, yp);
+    if (p.z) yv *= silu_f32(bf16_lo(p.z[ch]));
+    p.y[ch] = to_bf16(yv);
+  }
+}
+
+using SsdUpdateKernel = void (*)(const SsdUpdateArgs);
+SsdUpdateKernel ssd_update_kernel(int64_t dstate);
 
 using SsdKernel = void (*)(const SsdArgs);
 // The chunk kernel for (dstate, waves per workgroup, MODE), or NULL when that pair is not

@@ -623,7 +623,8 @@ ssm_status_t ssm_causal_conv1d_update(int64_t batch, int64_t dim, int64_t width,
 ssm_status_t ssm_ssd_fwd(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, int64_t dstate,
                          int64_t ngroups, ssm_dtype_t dtype, const void* x, const void* dt, const float* A,
                          const void* B, const void* C, const float* D, const void* z, const float* dt_bias,
-                         int dt_softplus, void* y, float* final_state, void* stream, const ssm_ssd_opts_t* opts) {
+                         int dt_softplus, const float* initial_state, void* y, float* final_state, void* stream,
+                         const ssm_ssd_opts_t* opts) {
   g_err[0] = '\0';
   if (batch < 0 || seqlen < 0 || nheads < 1 || headdim < 1 || dstate < 1 || ngroups < 1)
     return fail(SSM_ERR_INVALID_ARG, "bad size (batch=%lld seqlen=%lld nheads=%lld headdim=%lld dstate=%lld "
@@ -657,15 +658,23 @@ ssm_status_t ssm_ssd_fwd(int64_t batch, int64_t seqlen, int64_t nheads, int64_t 
       !mul_ok(nbh, headdim * dstate * 4, &n_fs))
     return fail(SSM_ERR_INVALID_ARG, "tensor size overflows int64");
   if (nbh == 0 || (seqlen == 0 && !final_state)) return SSM_OK;
+  if (seqlen == 0 && initial_state) {
+    // nothing to run: the final state is the entering state
+    const hipError_t e = hipMemcpyAsync(final_state, initial_state, static_cast<size_t>(n_fs),
+                                        hipMemcpyDeviceToDevice, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(SSM_ERR_HIP, "hipMemcpyAsync: %s", hipGetErrorString(e));
+    return SSM_OK;
+  }
   if (!A || (seqlen > 0 && (!x || !dt || !B || !C || !y)))
     return fail(SSM_ERR_INVALID_ARG, "NULL required pointer (A, and x, dt, B, C, y when seqlen > 0)");
   const Arg args[] = {{x, 16, "x"}, {z, 16, "z"}, {y, 16, "y"}, {B, 16, "B"}, {C, 16, "C"}, {dt, 2, "dt"},
-                      {A, 4, "A"}, {D, 4, "D"}, {dt_bias, 4, "dt_bias"}, {final_state, 16, "final_state"}};
+                      {A, 4, "A"}, {D, 4, "D"}, {dt_bias, 4, "dt_bias"}, {final_state, 16, "final_state"},
+                      {initial_state, 16, "initial_state"}};
   if (const Arg* bad = misaligned(args, sizeof args / sizeof args[0]))
     return fail(SSM_ERR_MISALIGNED, "%s (%p) is not aligned to %lld bytes", bad->name, bad->p, (long long)bad->align);
   const Range ry{seqlen > 0 ? y : nullptr, n_x}, rf{final_state, n_fs};
   const Range ins[] = {{x, n_x}, {z, n_x}, {dt, n_dt}, {B, n_bc}, {C, n_bc}, {A, nheads * 4}, {D, nheads * 4},
-                       {dt_bias, nheads * 4}};
+                       {dt_bias, nheads * 4}, {initial_state, n_fs}};
   for (Range in : ins)
     if (overlap(ry, in) || overlap(rf, in)) return fail(SSM_ERR_INVALID_ARG, "an output overlaps an input");
   if (overlap(ry, rf)) return fail(SSM_ERR_INVALID_ARG, "y overlaps final_state");
@@ -685,8 +694,10 @@ ssm_status_t ssm_ssd_fwd(int64_t batch, int64_t seqlen, int64_t nheads, int64_t 
   }
   const ssm::SsdKernel k = ssm::ssd_kernel(dstate, waves, ssm::kSsdOutputs);
   if (!k)
-    return fail(SSM_ERR_UNSUPPORTED, "no SSD kernel for dstate %lld with %d head channels per workgroup",
-                (long long)dstate, 16 * waves);
+    return fail(SSM_ERR_UNSUPPORTED,
+                "no SSD kernel for dstate %lld with headdim %lld (head_slice %d): dstate 256 takes 64-channel "
+                "slices, 128 takes 32 or 64",
+                (long long)dstate, (long long)headdim, 16 * waves);
   const int64_t nslices = headdim / (16 * waves);
   int64_t blocks;
   if (!mul_ok(nbh, nslices, &blocks) || blocks > 0x7fffffff) return fail(SSM_ERR_UNSUPPORTED, "grid too large");
@@ -695,6 +706,7 @@ ssm_status_t ssm_ssd_fwd(int64_t batch, int64_t seqlen, int64_t nheads, int64_t 
   a.B = static_cast<const uint16_t*>(B); a.C = static_cast<const uint16_t*>(C); a.D = D;
   a.z = static_cast<const uint16_t*>(z); a.dt_bias = dt_bias; a.y = static_cast<uint16_t*>(y);
   a.final_state = final_state;
+  a.init_state = initial_state;
   a.batch = batch; a.seqlen = seqlen;
   a.nheads = static_cast<int32_t>(nheads); a.headdim = static_cast<int32_t>(headdim);
   a.ngroups = static_cast<int32_t>(ngroups); a.nslices = static_cast<int32_t>(nslices);
@@ -737,6 +749,53 @@ ssm_status_t ssm_ssd_fwd(int64_t batch, int64_t seqlen, int64_t nheads, int64_t 
   }
   hipLaunchKernelGGL(k, dim3(static_cast<unsigned>(grid)), dim3(64 * waves), 0, st, a);
   return check_launch("SSD chunk kernel");
+}
+
+ssm_status_t ssm_ssd_state_update(int64_t batch, int64_t nheads, int64_t headdim, int64_t dstate, int64_t ngroups,
+                                  ssm_dtype_t dtype, float* state, const void* x, const void* dt, const float* A,
+                                  const void* B, const void* C, const float* D, const void* z, const float* dt_bias,
+                                  int dt_softplus, void* y, void* stream) {
+  g_err[0] = '\0';
+  if (batch < 0 || nheads < 1 || headdim < 1 || dstate < 1 || ngroups < 1)
+    return fail(SSM_ERR_INVALID_ARG, "bad size (batch=%lld nheads=%lld headdim=%lld dstate=%lld ngroups=%lld)",
+                (long long)batch, (long long)nheads, (long long)headdim, (long long)dstate, (long long)ngroups);
+  if (nheads % ngroups != 0)
+    return fail(SSM_ERR_INVALID_ARG, "ngroups %lld does not divide nheads %lld", (long long)ngroups,
+                (long long)nheads);
+  if (nheads > 0x7fffffff || headdim > 0x7fffffff)
+    return fail(SSM_ERR_INVALID_ARG, "nheads or headdim exceeds int32");
+  if (dtype != SSM_BF16 && dtype != SSM_F32) return fail(SSM_ERR_UNSUPPORTED, "unknown dtype %d", (int)dtype);
+  if (dtype != SSM_BF16) return fail(SSM_ERR_UNSUPPORTED, "the SSD kernels take bf16 storage only");
+  const ssm::SsdUpdateKernel k = ssm::ssd_update_kernel(dstate);
+  if (!k) return fail(SSM_ERR_UNSUPPORTED, "dstate %lld not in {32, 64, 128, 256}", (long long)dstate);
+  int64_t nbh, nch, n_st, n_x, n_bc, quads;
+  if (!mul_ok(batch, nheads, &nbh) || !mul_ok(nbh, headdim, &nch) || !mul_ok(nch, dstate * 4, &n_st) ||
+      !mul_ok(nch, 2, &n_x) || !mul_ok(batch * ngroups, dstate * 2, &n_bc) || !mul_ok(nch, dstate / 4, &quads))
+    return fail(SSM_ERR_INVALID_ARG, "tensor size overflows int64");
+  if (nch == 0) return SSM_OK;
+  if (!state || !x || !dt || !A || !B || !C || !y)
+    return fail(SSM_ERR_INVALID_ARG, "NULL required pointer (state, x, dt, A, B, C, y)");
+  const Arg args[] = {{state, 16, "state"}, {x, 2, "x"}, {dt, 2, "dt"}, {A, 4, "A"}, {B, 8, "B"}, {C, 8, "C"},
+                      {D, 4, "D"}, {z, 2, "z"}, {dt_bias, 4, "dt_bias"}, {y, 2, "y"}};
+  if (const Arg* bad = misaligned(args, sizeof args / sizeof args[0]))
+    return fail(SSM_ERR_MISALIGNED, "%s (%p) is not aligned to %lld bytes", bad->name, bad->p, (long long)bad->align);
+  const Range rs{state, n_st}, ry{y, n_x};
+  const Range ins[] = {{x, n_x}, {z, n_x}, {dt, nbh * 2}, {B, n_bc}, {C, n_bc}, {A, nheads * 4}, {D, nheads * 4},
+                       {dt_bias, nheads * 4}};
+  for (Range in : ins)
+    if (overlap(ry, in) || overlap(rs, in)) return fail(SSM_ERR_INVALID_ARG, "an output overlaps an input");
+  if (overlap(ry, rs)) return fail(SSM_ERR_INVALID_ARG, "y overlaps state");
+  const int64_t blocks = (quads + ssm::kSsdUpdateThreads - 1) / ssm::kSsdUpdateThreads;
+  if (blocks > 0x7fffffff) return fail(SSM_ERR_UNSUPPORTED, "grid too large");
+  ssm::SsdUpdateArgs a{};
+  a.state = state; a.x = static_cast<const uint16_t*>(x); a.dt = static_cast<const uint16_t*>(dt); a.A = A;
+  a.B = static_cast<const uint16_t*>(B); a.C = static_cast<const uint16_t*>(C); a.D = D;
+  a.z = static_cast<const uint16_t*>(z); a.dt_bias = dt_bias; a.y = static_cast<uint16_t*>(y);
+  a.batch = batch; a.nheads = static_cast<int32_t>(nheads); a.headdim = static_cast<int32_t>(headdim);
+  a.ngroups = static_cast<int32_t>(ngroups); a.softplus = dt_softplus ? 1 : 0;
+  hipLaunchKernelGGL(k, dim3(static_cast<unsigned>(blocks)), dim3(ssm::kSsdUpdateThreads), 0,
+                     static_cast<hipStream_t>(stream), a);
+  return check_launch("SSD state update");
 }
 
 }  // extern "C"

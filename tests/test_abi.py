@@ -231,9 +231,10 @@ def test_conv_update_validation(lib, kw, code):
 
 
 def ssd(lib, batch=2, seqlen=8, nheads=4, headdim=64, dstate=128, ngroups=2, dtype=BF16, x=fake(0), dt=fake(1),
-        A=fake(2), B=fake(3), C=fake(4), D=fake(5), z=fake(6), bias=fake(7), y=fake(8), fin=fake(9), opts=None):
-    return lib.ssm_ssd_fwd(batch, seqlen, nheads, headdim, dstate, ngroups, dtype, x, dt, A, B, C, D, z, bias, 1, y,
-                           fin, None, opts)
+        A=fake(2), B=fake(3), C=fake(4), D=fake(5), z=fake(6), bias=fake(7), y=fake(8), fin=fake(9), init=None,
+        opts=None):
+    return lib.ssm_ssd_fwd(batch, seqlen, nheads, headdim, dstate, ngroups, dtype, x, dt, A, B, C, D, z, bias, 1, init,
+                           y, fin, None, opts)
 
 
 def ssd_opts(slice_=0, reserved=0, segments=0):
@@ -253,10 +254,12 @@ def ssd_opts(slice_=0, reserved=0, segments=0):
     (dict(B=fake(3, 8)), MISALIGNED), (dict(C=fake(4, 2)), MISALIGNED), (dict(dt=fake(1, 1)), MISALIGNED),
     (dict(A=fake(2, 2)), MISALIGNED), (dict(fin=fake(9, 4)), MISALIGNED),
     (dict(y=fake(0)), INVALID), (dict(y=fake(3)), INVALID), (dict(fin=fake(4)), INVALID), (dict(fin=fake(8)), INVALID),
+    (dict(init=fake(10, 8)), MISALIGNED), (dict(init=fake(9)), INVALID), (dict(init=fake(8)), INVALID),
     (dict(opts=ssd_opts(8)), INVALID), (dict(opts=ssd_opts(48)), INVALID), (dict(headdim=32, opts=ssd_opts(64)), INVALID),
     (dict(opts=ssd_opts(0, reserved=1)), INVALID), (dict(opts=ssd_opts(0, segments=-2)), INVALID),
     # instantiated (dstate, waves) pairs: one wave only up to dstate 64, two up to 128
-    (dict(opts=ssd_opts(16)), UNSUPPORTED), (dict(dstate=256, opts=ssd_opts(32)), UNSUPPORTED)])
+    (dict(opts=ssd_opts(16)), UNSUPPORTED), (dict(dstate=256, opts=ssd_opts(32)), UNSUPPORTED),
+    (dict(dstate=256, headdim=32), UNSUPPORTED), (dict(dstate=128, headdim=16), UNSUPPORTED)])
 def test_ssd_validation(lib, kw, code):
     assert ssd(lib, **kw) == code
     assert err(lib)
@@ -266,3 +269,25 @@ def test_ssd_nothing_to_do(lib):
     assert ssd(lib, batch=0, x=None, dt=None, B=None, C=None, y=None) == OK
     # seqlen == 0 without a final state: nothing to write
     assert ssd(lib, seqlen=0, x=None, dt=None, B=None, C=None, y=None, fin=None) == OK
+
+
+def ssd_update(lib, batch=2, nheads=4, headdim=64, dstate=128, ngroups=2, dtype=BF16, state=fake(0), x=fake(1),
+               dt=fake(2), A=fake(3), B=fake(4), C=fake(5), D=fake(6), z=fake(7), bias=fake(8), y=fake(9)):
+    return lib.ssm_ssd_state_update(batch, nheads, headdim, dstate, ngroups, dtype, state, x, dt, A, B, C, D, z, bias,
+                                    1, y, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(batch=-1), INVALID), (dict(nheads=0), INVALID), (dict(ngroups=3), INVALID), (dict(dtype=F32), UNSUPPORTED),
+    (dict(dstate=16), UNSUPPORTED), (dict(dstate=100), UNSUPPORTED), (dict(state=None), INVALID),
+    (dict(x=None), INVALID), (dict(dt=None), INVALID), (dict(B=None), INVALID), (dict(y=None), INVALID),
+    (dict(state=fake(0, 8)), MISALIGNED), (dict(B=fake(4, 4)), MISALIGNED), (dict(C=fake(5, 2)), MISALIGNED),
+    (dict(x=fake(1, 1)), MISALIGNED), (dict(y=fake(1)), INVALID), (dict(state=fake(4)), INVALID),
+    (dict(y=fake(0)), INVALID)])
+def test_ssd_update_validation(lib, kw, code):
+    assert ssd_update(lib, **kw) == code
+    assert err(lib)
+
+
+def test_ssd_update_nothing_to_do(lib):
+    assert ssd_update(lib, batch=0, state=None, x=None, dt=None, B=None, C=None, y=None) == OK

@@ -139,3 +139,92 @@ def test_full_b8_sampled_heads(o):
                            dt_bias=sub["dt_bias"], dt_softplus=True, nthreads=16)
     assert_close(to_host(y)[rows][:, :, heads], y_ref, TOL_SSD, "mamba2_layer_b8 y sampled")
     assert_close(to_host(fin)[rows][:, heads], fin_ref, TOL_SSD, "mamba2_layer_b8 final_state sampled")
+
+
+def _cut(t, lo, hi):
+    return {k: (np.ascontiguousarray(v[:, lo:hi]) if k in ("x", "dt", "B", "C", "z") and v is not None else v)
+            for k, v in t.items()}
+
+
+@pytest.mark.parametrize("segments", [1, 3])
+def test_initial_state_and_resume(o, segments):
+    """A nonzero entering state against the oracle, with and without a sequence split; and a run
+    resumed from the final state it left equals one run over the whole sequence."""
+    t = W.ssd_inputs(2, 230, 4, 64, 128, 2, seed=71 + segments)
+    g = np.random.default_rng(72)
+    h0 = g.normal(size=(2, 4, 64, 128)).astype(np.float32)
+    say(f"[case] ssd initial state, segments={segments}")
+    y, fin = ssd_gpu(t, initial_state=to_dev(h0), segments=segments)
+    y_ref, fin_ref = o.ssd(t["x"], t["dt"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"], dt_bias=t["dt_bias"],
+                           dt_softplus=True, h0=h0.astype(np.float64), nthreads=8)
+    assert_close(to_host(y), y_ref, TOL_SSD, "initial state y")
+    assert_close(to_host(fin), fin_ref, TOL_SSD, "initial state final_state")
+    # resume: the first 100 steps, then the rest from the state they left
+    y1, f1 = ssd_gpu(_cut(t, 0, 100), initial_state=to_dev(h0), segments=segments)
+    y2, f2 = ssd_gpu(_cut(t, 100, 230), initial_state=f1, segments=segments)
+    assert_close(np.concatenate([to_host(y1), to_host(y2)], axis=1), y_ref, TOL_SSD, "resumed y")
+    assert_close(to_host(f2), fin_ref, TOL_SSD, "resumed final_state")
+
+
+def test_initial_state_empty_sequence():
+    import selective_state_space_61_amd as ssm
+    t = W.ssd_inputs(2, 0, 4, 64, 64, 1, seed=9)
+    h0 = torch.randn(2, 4, 64, 64, device="cuda")
+    d = {k: to_dev(v) for k, v in t.items()}
+    _, fin = ssm.ssm_ssd_fwd(d["x"], d["dt"], d["A"], d["B"], d["C"], D=d["D"], z=d["z"], dt_bias=d["dt_bias"],
+                             dt_softplus=True, initial_state=h0)
+    torch.cuda.synchronize()
+    assert torch.equal(fin, h0), "with no steps the final state is the entering state"
+
+
+def _step_major(t):
+    """Per-step slabs for token-by-token updates: (L, batch, ...) contiguous."""
+    return {k: (np.ascontiguousarray(np.swapaxes(v, 0, 1)) if k in ("x", "dt", "B", "C", "z") and v is not None
+                else v) for k, v in t.items()}
+
+
+@pytest.mark.parametrize("N,G", [(32, 1), (64, 2), (128, 1), (256, 4)])
+def test_state_update_matches_oracle_and_chunked(o, N, G):
+    """Tokens one at a time from an entering state reproduce the oracle's sequence and the chunked
+    forward (to the tolerance: the chunked form rounds its products to bf16)."""
+    import selective_state_space_61_amd as ssm
+    batch, L, H = 3, 20, 4
+    P = 64 if N == 256 else 32  # dstate 256 takes 64-channel head slices
+    t = W.ssd_inputs(batch, L, H, P, N, G, seed=N + G)
+    h0 = np.random.default_rng(N).normal(size=(batch, H, P, N)).astype(np.float32)
+    say(f"[case] ssd state update N={N} G={G}")
+    sm = _step_major(t)
+    d = {k: to_dev(v) for k, v in sm.items()}
+    state = to_dev(h0).clone()
+    ys = []
+    for s in range(L):
+        ys.append(ssm.ssm_ssd_state_update(state, d["x"][s], d["dt"][s], d["A"], d["B"][s], d["C"][s], D=d["D"],
+                                           z=d["z"][s], dt_bias=d["dt_bias"], dt_softplus=True))
+    torch.cuda.synchronize()
+    y_dec = torch.stack(ys, dim=1)
+    y_ref, fin_ref = o.ssd(t["x"], t["dt"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"], dt_bias=t["dt_bias"],
+                           dt_softplus=True, h0=h0.astype(np.float64), nthreads=8)
+    assert_close(to_host(y_dec), y_ref, TOL_SSD, f"decode N={N} y")
+    assert_close(to_host(state), fin_ref, TOL_SSD, f"decode N={N} state")
+    y_fwd, f_fwd = ssd_gpu(t, initial_state=to_dev(h0))
+    assert_close(to_host(y_dec), to_host(y_fwd), TOL_SSD, f"decode vs chunked N={N} y")
+    assert_close(to_host(state), to_host(f_fwd), TOL_SSD, f"decode vs chunked N={N} state")
+
+
+def test_state_update_layer_shape_sampled(o):
+    """One token of the 64-row decode batch of the layer shape (64 heads x 64, dstate 128): every
+    output and the sampled heads' states against the oracle's one-step run from the same state."""
+    import selective_state_space_61_amd as ssm
+    batch, H, P, N = 64, 64, 64, 128
+    t = W.ssd_inputs(batch, 1, H, P, N, 1, seed=61020)
+    h0 = np.random.default_rng(61021).normal(size=(batch, H, P, N)).astype(np.float32) * 0.5
+    d = {k: to_dev(v) for k, v in t.items()}
+    state = to_dev(h0).clone()
+    y = ssm.ssm_ssd_state_update(state, d["x"][:, 0].contiguous(), d["dt"][:, 0].contiguous(), d["A"],
+                                 d["B"][:, 0].contiguous(), d["C"][:, 0].contiguous(), D=d["D"],
+                                 z=d["z"][:, 0].contiguous(), dt_bias=d["dt_bias"], dt_softplus=True)
+    torch.cuda.synchronize()
+    y_ref, fin_ref = o.ssd(t["x"], t["dt"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"], dt_bias=t["dt_bias"],
+                           dt_softplus=True, h0=h0.astype(np.float64), nthreads=16)
+    assert_close(to_host(y), y_ref[:, 0], TOL_SSD, "layer-shape decode y")
+    assert_close(to_host(state), fin_ref, 1e-4, "layer-shape decode state")
