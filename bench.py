@@ -657,7 +657,7 @@ def main():
     roof["kernel_ms"] = main_res["kernel_ms"]
 
     line = {
-        "metric": "scan fwd B*L*D elems/s + achieved HBM GB/s (% of peak); decode updates/s",
+        "metric": "scan fwd B·L·D elems/s + achieved HBM GB/s (% of peak); decode updates/s",
         "value": main_res["elems_per_s"], "unit": "elem/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": main_res["ms_per_step"], "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
