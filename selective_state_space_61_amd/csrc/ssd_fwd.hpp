@@ -358,73 +358,73 @@ void ssd_chunk_kernel(const SsdArgs p) {
     }
 
     if constexpr (OUT) {
-    // M, split over the waves: G^T tile (j-block jb, i-block ib) = B_j . C_i (both rows are
-    // dstate-contiguous: plain 16-byte reads), masked to j <= i, decayed and stored as M[i][j]
-    {
-      ssd_f32x4_t gt[kTiles];
+      // M, split over the waves: G^T tile (j-block jb, i-block ib) = B_j . C_i (both rows are
+      // dstate-contiguous: plain 16-byte reads), masked to j <= i, decayed and stored as M[i][j]
+      {
+        ssd_f32x4_t gt[kTiles];
 #pragma unroll
-      for (int s = 0; s < kTiles; ++s) gt[s] = ssd_f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int s = 0; s < kTiles; ++s) gt[s] = ssd_f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks)
+        for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+          for (int s = 0; s < kTiles; ++s) {
+            const int k = wave + NW * s;
+            const int ib = gram_tile_i(k), jb = gram_tile_j(k);
+            gt[s] = mfma16x16x32(*reinterpret_cast<const ssd_u32x4_t*>(&s_b[(16 * jb + l16) * LDB + 32 * ks + 8 * q]),
+                                 *reinterpret_cast<const ssd_u32x4_t*>(&s_c[(16 * ib + l16) * LDB + 32 * ks + 8 * q]),
+                                 gt[s]);
+          }
 #pragma unroll
         for (int s = 0; s < kTiles; ++s) {
           const int k = wave + NW * s;
           const int ib = gram_tile_i(k), jb = gram_tile_j(k);
-          gt[s] = mfma16x16x32(*reinterpret_cast<const ssd_u32x4_t*>(&s_b[(16 * jb + l16) * LDB + 32 * ks + 8 * q]),
-                               *reinterpret_cast<const ssd_u32x4_t*>(&s_c[(16 * ib + l16) * LDB + 32 * ks + 8 * q]),
-                               gt[s]);
+          const int irow = 16 * ib + l16;
+          const float cum_i = s_cum[irow];
+          const ssd_f32x4_t cj = *reinterpret_cast<const ssd_f32x4_t*>(&s_cum[16 * jb + 4 * q]);
+          const ssd_f32x4_t dj = *reinterpret_cast<const ssd_f32x4_t*>(&s_dt[16 * jb + 4 * q]);
+          float m[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            m[r] = (16 * jb + 4 * q + r <= irow) ? gt[s][r] * hw_exp2(cum_i - cj[r]) * dj[r] : 0.0f;
+          *reinterpret_cast<ssd_u32x2_t*>(&s_m[irow * LDM + 16 * jb + 4 * q]) =
+              ssd_u32x2_t{pack_bf16x2(m[0], m[1]), pack_bf16x2(m[2], m[3])};
         }
-#pragma unroll
-      for (int s = 0; s < kTiles; ++s) {
-        const int k = wave + NW * s;
-        const int ib = gram_tile_i(k), jb = gram_tile_j(k);
-        const int irow = 16 * ib + l16;
-        const float cum_i = s_cum[irow];
-        const ssd_f32x4_t cj = *reinterpret_cast<const ssd_f32x4_t*>(&s_cum[16 * jb + 4 * q]);
-        const ssd_f32x4_t dj = *reinterpret_cast<const ssd_f32x4_t*>(&s_dt[16 * jb + 4 * q]);
-        float m[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          m[r] = (16 * jb + 4 * q + r <= irow) ? gt[s][r] * hw_exp2(cum_i - cj[r]) * dj[r] : 0.0f;
-        *reinterpret_cast<ssd_u32x2_t*>(&s_m[irow * LDM + 16 * jb + 4 * q]) =
-            ssd_u32x2_t{pack_bf16x2(m[0], m[1]), pack_bf16x2(m[2], m[3])};
       }
-    }
 
-    // S entering the chunk as bf16 A operands of the read-out: S^T[pw][n], n permuted as the
-    // tiles hold it
-    ssd_u32x4_t sf[NKS];
+      // S entering the chunk as bf16 A operands of the read-out: S^T[pw][n], n permuted as the
+      // tiles hold it
+      ssd_u32x4_t sf[NKS];
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks)
-      sf[ks] = ssd_u32x4_t{pack_bf16x2(S[2 * ks][0], S[2 * ks][1]), pack_bf16x2(S[2 * ks][2], S[2 * ks][3]),
-                           pack_bf16x2(S[2 * ks + 1][0], S[2 * ks + 1][1]),
-                           pack_bf16x2(S[2 * ks + 1][2], S[2 * ks + 1][3])};
-    __syncthreads();  // M complete
+      for (int ks = 0; ks < NKS; ++ks)
+        sf[ks] = ssd_u32x4_t{pack_bf16x2(S[2 * ks][0], S[2 * ks][1]), pack_bf16x2(S[2 * ks][2], S[2 * ks][3]),
+                             pack_bf16x2(S[2 * ks + 1][0], S[2 * ks + 1][1]),
+                             pack_bf16x2(S[2 * ks + 1][2], S[2 * ks + 1][3])};
+      __syncthreads();  // M complete
 
-    // Y^T tiles (channels 16 wave .. +15, steps 16 ib .. +15): the read-out exp(cum_i) S^T C_i^T
-    // plus the masked product X^T M^T over the steps j <= i
-    ssd_f32x4_t acc[4];
+      // Y^T tiles (channels 16 wave .. +15, steps 16 ib .. +15): the read-out exp(cum_i) S^T C_i^T
+      // plus the masked product X^T M^T over the steps j <= i
+      ssd_f32x4_t acc[4];
 #pragma unroll
-    for (int ib = 0; ib < 4; ++ib) acc[ib] = ssd_f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+      for (int ib = 0; ib < 4; ++ib) acc[ib] = ssd_f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks)
+      for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
-      for (int ib = 0; ib < 4; ++ib)
-        acc[ib] = mfma16x16x32(sf[ks], load_perm_frag(&s_c[(16 * ib + l16) * LDB + 32 * ks + 4 * q]), acc[ib]);
+        for (int ib = 0; ib < 4; ++ib)
+          acc[ib] = mfma16x16x32(sf[ks], load_perm_frag(&s_c[(16 * ib + l16) * LDB + 32 * ks + 4 * q]), acc[ib]);
 #pragma unroll
-    for (int ib = 0; ib < 4; ++ib) acc[ib] *= hw_exp2(s_cum[16 * ib + l16]);
+      for (int ib = 0; ib < 4; ++ib) acc[ib] *= hw_exp2(s_cum[16 * ib + l16]);
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const ssd_u32x4_t xa = lds_frag_tr(s_x, LDX, 32 * ks, q, l16, cx);  // X^T[pw][32 ks + 8q ..]
+      for (int ks = 0; ks < 2; ++ks) {
+        const ssd_u32x4_t xa = lds_frag_tr(s_x, LDX, 32 * ks, q, l16, cx);  // X^T[pw][32 ks + 8q ..]
 #pragma unroll
-      for (int ib = 2 * ks; ib < 4; ++ib)
-        acc[ib] = mfma16x16x32(xa, *reinterpret_cast<const ssd_u32x4_t*>(&s_m[(16 * ib + l16) * LDM + 32 * ks + 8 * q]),
-                               acc[ib]);
+        for (int ib = 2 * ks; ib < 4; ++ib)
+          acc[ib] = mfma16x16x32(xa, *reinterpret_cast<const ssd_u32x4_t*>(&s_m[(16 * ib + l16) * LDM + 32 * ks + 8 * q]),
+                                 acc[ib]);
+      }
+      // Y^T tiles to LDS as Y[i][p] for the epilogue (run at the next chunk's staging)
+#pragma unroll
+      for (int ib = 0; ib < 4; ++ib) *reinterpret_cast<ssd_f32x4_t*>(&s_y[(16 * ib + l16) * LDY + pe]) = acc[ib];
     }
-    // Y^T tiles to LDS as Y[i][p] for the epilogue (run at the next chunk's staging)
-#pragma unroll
-    for (int ib = 0; ib < 4; ++ib) *reinterpret_cast<ssd_f32x4_t*>(&s_y[(16 * ib + l16) * LDY + pe]) = acc[ib];
-    }  // OUT
 
     // state update: S = exp(cum_last) S + B^T (weighted X); the B^T operand of tile nb is rows
     // 16 nb .. +15 of B^T, read transposed from B (this lane addresses column 16 nb + 4 (l16 % 4))
