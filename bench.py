@@ -368,6 +368,26 @@ def bench_ssd_decode(torch, np, W, ssm, device):
             "hbm_frac": step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS}
 
 
+def copy_ceiling_gbps(torch, device, nbytes=1 << 30, reps=10):
+    """Device-to-device copy of `nbytes` (read + written, 4x the 256 MB Infinity Cache): the HBM
+    rate this GPU reaches on a plain stream, the practical ceiling next to the 8 TB/s spec."""
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device=device).fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del src, dst
+    torch.cuda.empty_cache()
+    return 2 * nbytes / (ms * 1e-3) / 1e9
+
+
 def bench_scan_bwd(steps, warmup, torch, np, W, ssm, device):
     """The backward scan on the 130M-shaped layer (inputs, dy and gradients resident in HBM;
     two input sets rotated).  Reports the time per call of the whole backward (both kernels)."""
@@ -655,6 +675,8 @@ def main():
     roof["hbm_frac"] = hbm_frac
     roof["alg_bytes_per_launch"] = main_res["alg_bytes"]
     roof["kernel_ms"] = main_res["kernel_ms"]
+    roof["copy_ceiling_gbps"] = copy_ceiling_gbps(torch, device)
+    roof["hbm_frac_of_copy_ceiling"] = main_res["hbm_gbps"] / roof["copy_ceiling_gbps"]
 
     line = {
         "metric": "scan fwd B·L·D elems/s + achieved HBM GB/s (% of peak); decode updates/s",
