@@ -243,6 +243,9 @@ __global__ __launch_bounds__(64 * (N / NPL + kIoWaves)) void scan_chunk_kernel(c
     dsk[v] = (p.Dskip && v < nvalid_col) ? p.Dskip[d_col + v] : 0.0f;
   }
   const bool has_z = kFull && p.z != nullptr;
+  // without a gate the z tile is read from x (always valid) and never used: a load that runs on
+  // every path keeps the tile registers free of merges, whose copies would wait for the load
+  const void* zsrc = has_z ? p.z : p.x;
 
   RawVec<BF16, VEC> nx[ITEMS], nd[ITEMS], nz[ITEMS];  // tile of the next chunk to enter the prologue
   // loads the x / delta / z tile of chunk c into registers
@@ -254,7 +257,7 @@ __global__ __launch_bounds__(64 * (N / NPL + kIoWaves)) void scan_chunk_kernel(c
         const int64_t idx = (row_base + t0 + row0 + i * RSTEP) * p.dim + d_col;
         nx[i].load(p.x, idx, VEC, true);
         nd[i].load(p.delta, idx, VEC, true);
-        if (has_z) nz[i].load(p.z, idx, VEC, true);
+        nz[i].load(zsrc, idx, VEC, true);
       }
       return;
     }
@@ -265,7 +268,7 @@ __global__ __launch_bounds__(64 * (N / NPL + kIoWaves)) void scan_chunk_kernel(c
       const int64_t idx = (row_base + t) * p.dim + d_col;
       nx[i].load(p.x, idx, nv, vec_ok);
       nd[i].load(p.delta, idx, nv, vec_ok);
-      if (has_z) nz[i].load(p.z, idx, nv, vec_ok);
+      nz[i].load(zsrc, idx, nv, vec_ok);
     }
   };
   if (nchunks > 0) load_tile(0);
@@ -273,14 +276,19 @@ __global__ __launch_bounds__(64 * (N / NPL + kIoWaves)) void scan_chunk_kernel(c
   // x and z of the chunks between prologue and epilogue: at the top of iteration j, [0] holds
   // chunk j (prologued in iteration j-1) and [1] chunk j-1 (its epilogue runs now)
   RawVec<BF16, VEC> ex[2][ITEMS], ez[2][ITEMS];
+  // Order inside an iteration: epilogue arithmetic, prologue, the loads of the next tile, and
+  // last the y stores.  Vector-memory completions are counted in issue order, so any wait for a
+  // load also waits for every store issued before it; in this order no wait in the loop covers a
+  // store issued in the same iteration (only those of the previous one, long complete), where
+  // storing first cost a full write round trip on every chunk.
   for (int64_t j = -1; j <= nchunks; ++j) {
-    // ---- epilogue of chunk j-1: y = sum of partials + D x, gated, stored with vector stores ----
+    // ---- epilogue of chunk j-1, arithmetic: y = sum of partials + D x, gated ------------------
+    const int64_t e = j - 1;
+    const bool epi = kFull && e >= 0;
+    [[maybe_unused]] float out[ITEMS][VEC];
     if constexpr (kFull) {
-      const int64_t e = j - 1;
-      if (e >= 0) {
+      if (epi) {
         const int eb = static_cast<int>(e & 1);
-        const int64_t t0 = t_begin + e * CH;
-        float out[ITEMS][VEC];
 #pragma unroll
         for (int i = 0; i < ITEMS; ++i) {
           const int row = row0 + i * RSTEP;
@@ -297,18 +305,6 @@ __global__ __launch_bounds__(64 * (N / NPL + kIoWaves)) void scan_chunk_kernel(c
           for (int i = 0; i < ITEMS; ++i)
 #pragma unroll
             for (int v = 0; v < VEC; ++v) out[i][v] *= silu_f32(ez[1][i].get(v));
-        }
-        const bool full = chunk_full(e);
-#pragma unroll
-        for (int i = 0; i < ITEMS; ++i) {
-          const int64_t t = t0 + row0 + i * RSTEP;
-          const int64_t idx = (row_base + t) * p.dim + d_col;
-          if (full) {
-            store_vec<BF16, VEC>(p.y, idx, out[i], VEC, true);
-          } else {
-            const int nv = (t < t_end) ? nvalid_col : 0;
-            if (nv > 0) store_vec<BF16, VEC>(p.y, idx, out[i], nv, vec_ok);
-          }
         }
       }
     }
@@ -351,17 +347,34 @@ __global__ __launch_bounds__(64 * (N / NPL + kIoWaves)) void scan_chunk_kernel(c
           s_dw[pb][row][col + v] = make_float2(dts[i][v], dts[i][v] * (ZOH ? xs[i][v] * kLog2e : xs[i][v]));
         ex[1][i] = ex[0][i];
         ex[0][i] = nx[i];
-        if (has_z) {
-          ez[1][i] = ez[0][i];
-          ez[0][i] = nz[i];
-        }
+        ez[1][i] = ez[0][i];
+        ez[0][i] = nz[i];
       }
-      if (c + 1 < nchunks) load_tile(c + 1);
     } else {
 #pragma unroll
       for (int i = 0; i < ITEMS; ++i) {
         ex[1][i] = ex[0][i];
-        if (has_z) ez[1][i] = ez[0][i];
+        ez[1][i] = ez[0][i];
+      }
+    }
+    // ---- tile of chunk j+2 --------------------------------------------------------------------
+    if (c + 1 < nchunks) load_tile(c + 1);
+    // ---- epilogue of chunk j-1, stores --------------------------------------------------------
+    if constexpr (kFull) {
+      if (epi) {
+        const int64_t t0 = t_begin + e * CH;
+        const bool full = chunk_full(e);
+#pragma unroll
+        for (int i = 0; i < ITEMS; ++i) {
+          const int64_t t = t0 + row0 + i * RSTEP;
+          const int64_t idx = (row_base + t) * p.dim + d_col;
+          if (full) {
+            store_vec<BF16, VEC>(p.y, idx, out[i], VEC, true);
+          } else {
+            const int nv = (t < t_end) ? nvalid_col : 0;
+            if (nv > 0) store_vec<BF16, VEC>(p.y, idx, out[i], nv, vec_ok);
+          }
+        }
       }
     }
 
