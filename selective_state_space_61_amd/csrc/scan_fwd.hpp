@@ -247,17 +247,20 @@ __global__ __launch_bounds__(64 * (N / NPL + kIoWaves)) void scan_chunk_kernel(c
   // every path keeps the tile registers free of merges, whose copies would wait for the load
   const void* zsrc = has_z ? p.z : p.x;
 
-  RawVec<BF16, VEC> nx[ITEMS], nd[ITEMS], nz[ITEMS];  // tile of the next chunk to enter the prologue
-  // loads the x / delta / z tile of chunk c into registers
-  auto load_tile = [&](int64_t c) {
+  // tiles of the next two chunks to enter the prologue: chunk c sits in slot c & 1, loaded two
+  // iterations before its prologue, so two tile loads per thread are in flight at any time
+  RawVec<BF16, VEC> nx[2][ITEMS], nd[2][ITEMS], nz[2][ITEMS];
+  // loads the x / delta / z tile of chunk c into slot S
+  auto load_tile = [&](int64_t c, auto S) {
+    constexpr int sl = decltype(S)::value;
     const int64_t t0 = t_begin + c * CH;
     if (chunk_full(c)) {
 #pragma unroll
       for (int i = 0; i < ITEMS; ++i) {
         const int64_t idx = (row_base + t0 + row0 + i * RSTEP) * p.dim + d_col;
-        nx[i].load(p.x, idx, VEC, true);
-        nd[i].load(p.delta, idx, VEC, true);
-        nz[i].load(zsrc, idx, VEC, true);
+        nx[sl][i].load(p.x, idx, VEC, true);
+        nd[sl][i].load(p.delta, idx, VEC, true);
+        nz[sl][i].load(zsrc, idx, VEC, true);
       }
       return;
     }
@@ -266,22 +269,26 @@ __global__ __launch_bounds__(64 * (N / NPL + kIoWaves)) void scan_chunk_kernel(c
       const int64_t t = t0 + row0 + i * RSTEP;
       const int nv = (t < t_end) ? nvalid_col : 0;
       const int64_t idx = (row_base + t) * p.dim + d_col;
-      nx[i].load(p.x, idx, nv, vec_ok);
-      nd[i].load(p.delta, idx, nv, vec_ok);
-      nz[i].load(zsrc, idx, nv, vec_ok);
+      nx[sl][i].load(p.x, idx, nv, vec_ok);
+      nd[sl][i].load(p.delta, idx, nv, vec_ok);
+      nz[sl][i].load(zsrc, idx, nv, vec_ok);
     }
   };
-  if (nchunks > 0) load_tile(0);
+  using Slot0 = std::integral_constant<int, 0>;
+  using Slot1 = std::integral_constant<int, 1>;
+  if (nchunks > 0) load_tile(0, Slot0{});
+  if (nchunks > 1) load_tile(1, Slot1{});
 
   // x and z of the chunks between prologue and epilogue: at the top of iteration j, [0] holds
   // chunk j (prologued in iteration j-1) and [1] chunk j-1 (its epilogue runs now)
   RawVec<BF16, VEC> ex[2][ITEMS], ez[2][ITEMS];
-  // Order inside an iteration: epilogue arithmetic, prologue, the loads of the next tile, and
+  // Order inside an iteration: epilogue arithmetic, prologue, the loads of a later tile, and
   // last the y stores.  Vector-memory completions are counted in issue order, so any wait for a
   // load also waits for every store issued before it; in this order no wait in the loop covers a
-  // store issued in the same iteration (only those of the previous one, long complete), where
-  // storing first cost a full write round trip on every chunk.
-  for (int64_t j = -1; j <= nchunks; ++j) {
+  // store issued in the same iteration, where storing first cost a full write round trip on
+  // every chunk.  Iteration j works on slot (j + 1) & 1, so the loop is unrolled by two.
+  auto iteration = [&](int64_t j, auto S) {
+    constexpr int sl = decltype(S)::value;
     // ---- epilogue of chunk j-1, arithmetic: y = sum of partials + D x, gated ------------------
     const int64_t e = j - 1;
     const bool epi = kFull && e >= 0;
@@ -318,8 +325,8 @@ __global__ __launch_bounds__(64 * (N / NPL + kIoWaves)) void scan_chunk_kernel(c
       for (int i = 0; i < ITEMS; ++i)
 #pragma unroll
         for (int v = 0; v < VEC; ++v) {
-          dts[i][v] = nd[i].get(v) + bias[v];
-          xs[i][v] = nx[i].get(v);
+          dts[i][v] = nd[sl][i].get(v) + bias[v];
+          xs[i][v] = nx[sl][i].get(v);
         }
       if (p.softplus) {
 #pragma unroll
@@ -346,9 +353,9 @@ __global__ __launch_bounds__(64 * (N / NPL + kIoWaves)) void scan_chunk_kernel(c
         for (int v = 0; v < VEC; ++v)  // ZOH: the scan multiplies by ln2 phi, so w carries log2(e)
           s_dw[pb][row][col + v] = make_float2(dts[i][v], dts[i][v] * (ZOH ? xs[i][v] * kLog2e : xs[i][v]));
         ex[1][i] = ex[0][i];
-        ex[0][i] = nx[i];
+        ex[0][i] = nx[sl][i];
         ez[1][i] = ez[0][i];
-        ez[0][i] = nz[i];
+        ez[0][i] = nz[sl][i];
       }
     } else {
 #pragma unroll
@@ -357,8 +364,8 @@ __global__ __launch_bounds__(64 * (N / NPL + kIoWaves)) void scan_chunk_kernel(c
         ez[1][i] = ez[0][i];
       }
     }
-    // ---- tile of chunk j+2 --------------------------------------------------------------------
-    if (c + 1 < nchunks) load_tile(c + 1);
+    // ---- tile of chunk j+3, into the slot the prologue just freed -----------------------------
+    if (c + 2 < nchunks) load_tile(c + 2, S);
     // ---- epilogue of chunk j-1, stores --------------------------------------------------------
     if constexpr (kFull) {
       if (epi) {
@@ -379,6 +386,10 @@ __global__ __launch_bounds__(64 * (N / NPL + kIoWaves)) void scan_chunk_kernel(c
     }
 
     __syncthreads();
+  };
+  for (int64_t j = -1; j <= nchunks; j += 2) {
+    iteration(j, Slot0{});
+    if (j + 1 <= nchunks) iteration(j + 1, Slot1{});
   }
 }
 
