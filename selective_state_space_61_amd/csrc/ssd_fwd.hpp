@@ -481,8 +481,8 @@ __global__ __launch_bounds__(256) void ssd_carry_kernel(const SsdArgs p, int32_t
 // for each (batch row b, head h, channel p) and its group g,
 //   dt = softplus(dt[b,h] + dt_bias[h]);  S[b,h,p,:] = exp(dt A[h]) S[b,h,p,:] + dt x[b,h,p] B[b,g,:]
 //   y[b,h,p] = (C[b,g,:] . S[b,h,p,:] + D[h] x[b,h,p]) * silu(z[b,h,p])
-// The state is read and written once: a streaming kernel.  A thread owns 4 consecutive dstate
-// entries of one channel (16-byte state access, 8-byte B and C); the N/4 lanes of a channel add
+// The state is read and written once: a streaming kernel, with non-temporal state accesses.  A
+// thread owns 4 consecutive dstate entries of one channel (16-byte state access, 8-byte B and C); the N/4 lanes of a channel add
 // their partial read-outs with cross-lane shuffles.  The decay is one exp per channel.
 // ---------------------------------------------------------------------------------------------
 struct SsdUpdateArgs {
@@ -527,7 +527,7 @@ __global__ __launch_bounds__(kSsdUpdateThreads) void ssd_state_update_kernel(con
   const float a = hw_exp2(dtv * (p.A[h] * kLog2e));
   const float w = dtv * xv;
   float* st = p.state + ch * N + n0;
-  float4 s4 = *reinterpret_cast<const float4*>(st);
+  float4 s4 = load_stream(st);
   const uint2 b2 = *reinterpret_cast<const uint2*>(p.B + (b * G + g) * N + n0);
   const uint2 c2 = *reinterpret_cast<const uint2*>(p.C + (b * G + g) * N + n0);
   s4.x = fmaf(a, s4.x, w * bf16_lo(b2.x));
@@ -538,7 +538,7 @@ __global__ __launch_bounds__(kSsdUpdateThreads) void ssd_state_update_kernel(con
   yp = fmaf(bf16_hi(c2.x), s4.y, yp);
   yp = fmaf(bf16_lo(c2.y), s4.z, yp);
   yp = fmaf(bf16_hi(c2.y), s4.w, yp);
-  if (ok) *reinterpret_cast<float4*>(st) = s4;
+  if (ok) store_stream(st, s4);
 #pragma unroll
   for (int off = 1; off < TPC; off <<= 1) yp += __shfl_xor(yp, off, 64);
   if (ok && n0 == 0) {

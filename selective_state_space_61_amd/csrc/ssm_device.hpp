@@ -33,6 +33,19 @@ __device__ __forceinline__ float hw_exp2(float x) { return __builtin_amdgcn_exp2
 __device__ __forceinline__ float hw_log2(float x) { return __builtin_amdgcn_logf(x); }
 __device__ __forceinline__ float hw_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
 
+// 16-byte state accesses marked non-temporal: a decode step reads and writes each state once, and
+// the next touch of that state is a whole model step later (every other layer's state in
+// between), so keeping it in the caches only displaces other lines.
+typedef float StreamF4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ float4 load_stream(const float* p) {
+  const StreamF4 v = __builtin_nontemporal_load(reinterpret_cast<const StreamF4*>(p));
+  return make_float4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void store_stream(float* p, float4 v) {
+  const StreamF4 w = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(w, reinterpret_cast<StreamF4*>(p));
+}
+
 // softplus(v) = log(1 + e^v).  Above 20 the correction log1p(e^-v) < 2.1e-9 is below the fp32
 // resolution of v and v is returned.  Otherwise u = e^v, w = fl(1 + u) and
 //   log1p(u) = log(w) + log(1 + e / w),  e = u - (w - 1)  (the exact rounding error of 1 + u;

@@ -6,7 +6,7 @@
 //   y = sum_n C[n] h[n] + D x;  y *= silu(z).
 //
 // The state (batch, dim, N) fp32 is read and written once per step: that traffic is the whole
-// cost, so the kernel is a streaming one.  A thread owns SPT = min(N, 4) consecutive states of
+// cost, so the kernel is a streaming one, with non-temporal state accesses.  A thread owns SPT = min(N, 4) consecutive states of
 // one channel (one 16-byte load and store), TPC = N / SPT neighbouring lanes share a channel
 // and combine their partial read-outs with cross-lane adds.  The per-channel prologue (softplus)
 // is recomputed by each of those lanes; it is cheap next to the state traffic.
@@ -78,7 +78,7 @@ __global__ __launch_bounds__(kUpdateThreads) void state_update_kernel(const Upda
     const float* st = p.state + ch * N + n0;
     if constexpr (SPT == 4) {
       if (p.state_vec_ok) {
-        const float4 v = *reinterpret_cast<const float4*>(st);
+        const float4 v = load_stream(st);
         hs[k][0] = v.x; hs[k][1] = v.y; hs[k][2] = v.z; hs[k][3] = v.w;
       } else {
 #pragma unroll
@@ -136,7 +136,7 @@ __global__ __launch_bounds__(kUpdateThreads) void state_update_kernel(const Upda
     if (ok[k]) {
       if constexpr (SPT == 4) {
         if (p.state_vec_ok) {
-          *reinterpret_cast<float4*>(st) = make_float4(hs[k][0], hs[k][1], hs[k][2], hs[k][3]);
+          store_stream(st, make_float4(hs[k][0], hs[k][1], hs[k][2], hs[k][3]));
         } else {
 #pragma unroll
           for (int j = 0; j < SPT; ++j) st[j] = hs[k][j];
