@@ -10,7 +10,8 @@
 // next call, or of the one-token update.
 //
 // Both kernels stream: every input element is read once (plus a K-1 row halo per time tile,
-// which the L2 serves) and every output written once, so HBM bandwidth is the bound.  A thread
+// which the L2 serves) and every output written once (non-temporally), so HBM bandwidth is the
+// bound.  A thread
 // owns VEC consecutive channels (one 16-byte access per row) and kConvTile consecutive steps,
 // keeps the K-1 previous inputs in registers, and issues kConvUnroll row loads before using
 // any of them.
@@ -65,6 +66,18 @@ template <bool BF16>
 __device__ __forceinline__ void store_one(void* base, int64_t i, float v) {
   if constexpr (BF16) static_cast<uint16_t*>(base)[i] = to_bf16(v);
   else static_cast<float*>(base)[i] = v;
+}
+
+// One thread's output vector of a row (kConvVecBytes, aligned), stored non-temporally: the
+// output is written once and read by the next kernel, not by this one, so it need not displace
+// the x rows that the neighbouring time tile still reads as its halo.
+template <bool BF16>
+__device__ __forceinline__ void store_row_stream(void* base, int64_t idx, const float (&val)[kConvVec<BF16>]) {
+  static_assert(kConvVecBytes == 4, "one 32-bit word per thread and row");
+  uint32_t word;
+  if constexpr (BF16) word = pack_bf16x2(val[0], val[1]);
+  else word = __builtin_bit_cast(uint32_t, val[0]);
+  __builtin_nontemporal_store(word, reinterpret_cast<uint32_t*>(static_cast<char*>(base) + idx * (BF16 ? 2 : 4)));
 }
 
 template <bool BF16, int K, bool FAST>
@@ -122,7 +135,8 @@ __device__ __forceinline__ void conv_tile(const ConvArgs& p, int64_t b, int64_t 
         for (int j = 0; j + 1 < K - 1; ++j) win[j][v] = win[j + 1][v];
         if constexpr (K > 1) win[K - 2][v] = xv;
       }
-      store_vec<BF16, VEC>(p.y, (b * p.seqlen + t) * p.dim + d0, out, FAST ? VEC : nv, vec);
+      if constexpr (FAST) store_row_stream<BF16>(p.y, (b * p.seqlen + t) * p.dim + d0, out);
+      else store_vec<BF16, VEC>(p.y, (b * p.seqlen + t) * p.dim + d0, out, nv, vec);
     }
   }
   // the tile that holds the last step leaves the last K-1 inputs behind
