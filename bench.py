@@ -250,11 +250,12 @@ def bench_conv(steps, warmup, torch, np, W, ssm, device):
     return res
 
 
-def time_graph(torch, call, steps, warmup, device):
+def time_graph(torch, call, steps, warmup, device, replays=5):
     """Captures `steps` calls as one HIP graph (after `warmup` eager calls on the capture stream,
-    which also let the library set up its per-stream scratch before capture) and times one
-    replay: short kernels are then timed without the host launch path between them.  Returns ms
-    per call."""
+    which also let the library set up its per-stream scratch before capture), replays it twice
+    untimed, then times `replays` replays one by one: short kernels are then timed without the
+    host launch path between them.  Returns the median ms per call (the first replays of a
+    freshly filled working set run up to 15% slower than the steady state)."""
     graph = torch.cuda.CUDAGraph()
     side = torch.cuda.Stream(device)
     side.wait_stream(torch.cuda.current_stream(device))
@@ -267,15 +268,19 @@ def time_graph(torch, call, steps, warmup, device):
             for i in range(steps):
                 call(i)
     torch.cuda.synchronize()
-    graph.replay()
+    for _ in range(2):
+        graph.replay()
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    graph.replay()
-    e1.record()
-    torch.cuda.synchronize()
+    times = []
+    for _ in range(replays):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) / steps)
     del graph
-    return e0.elapsed_time(e1) / steps
+    return sorted(times)[len(times) // 2]
 
 
 def ssd_bytes(w):

@@ -274,9 +274,12 @@ void ssd_chunk_kernel(const SsdArgs p) {
           const float zr = (e & 1) ? bf16_hi(ze[u][e / 2]) : bf16_lo(ze[u][e / 2]);
           yv[e] = fmaf(Dh, xr, yv[e]) * (zg ? silu_f32(zr) : 1.0f);
         }
-        *reinterpret_cast<ssd_u32x4_t*>(yg + t * xs + 8 * p8) =
+        // y is written once and read by the next layer, not here: a non-temporal store keeps the
+        // caches for the B and C rows that every head of the group reads
+        __builtin_nontemporal_store(
             ssd_u32x4_t{pack_bf16x2(yv[0], yv[1]), pack_bf16x2(yv[2], yv[3]), pack_bf16x2(yv[4], yv[5]),
-                        pack_bf16x2(yv[6], yv[7])};
+                        pack_bf16x2(yv[6], yv[7])},
+            reinterpret_cast<ssd_u32x4_t*>(yg + t * xs + 8 * p8));
       }
     }
   };
