@@ -247,8 +247,10 @@ __global__ __launch_bounds__(64 * (N / NPL + kIoWaves)) void scan_chunk_kernel(c
   // every path keeps the tile registers free of merges, whose copies would wait for the load
   const void* zsrc = has_z ? p.z : p.x;
 
-  // tiles of the next two chunks to enter the prologue: chunk c sits in slot c & 1, loaded two
-  // iterations before its prologue, so two tile loads per thread are in flight at any time
+  // tiles of the next two chunks to enter the prologue: chunk c sits in slot c & 1 and is loaded
+  // two iterations before its prologue (the compiler's wait before a prologue counts every
+  // outstanding load, so it also covers the newer tile; the two slots still measured faster than
+  // one, with fixed registers instead of a rotation per iteration)
   RawVec<BF16, VEC> nx[2][ITEMS], nd[2][ITEMS], nz[2][ITEMS];
   // loads the x / delta / z tile of chunk c into slot S
   auto load_tile = [&](int64_t c, auto S) {
