@@ -219,7 +219,7 @@ __device__ __forceinline__ float step_readout2(float dt, float w, const float* a
 template <int KB, int KC>
 __device__ __forceinline__ float step_readout4(float dt, float w, const float* a2, const float* b, const float* c,
                                                float* h) {
-  float t0, t1, t2, t3, u0, u1, u2, u3, ya, yb, yp;
+  float t0, t1, t2, t3, u0, u1, u2, u3, yp;
   asm("v_mul_f32 %[t0], %[dt], %[a0]\n\t"
       "v_mul_f32 %[t1], %[dt], %[a1]\n\t"
       "v_mul_f32 %[t2], %[dt], %[a2]\n\t"
@@ -229,21 +229,20 @@ __device__ __forceinline__ float step_readout4(float dt, float w, const float* a
       "v_exp_f32 %[t2], %[t2]\n\t"
       "v_exp_f32 %[t3], %[t3]\n\t"
       "v_mul_f32_dpp %[u0], %[b0], %[w] " SSM_DPP_KB "\n\t"
-      "v_mul_f32_dpp %[ya], %[c0], %[h0] " SSM_DPP_KC "\n\t"
+      "v_mul_f32_dpp %[yp], %[c0], %[h0] " SSM_DPP_KC "\n\t"
       "v_mul_f32_dpp %[u1], %[b1], %[w] " SSM_DPP_KB "\n\t"
-      "v_mul_f32_dpp %[yb], %[c1], %[h1] " SSM_DPP_KC "\n\t"
+      "v_fmac_f32_dpp %[yp], %[c1], %[h1] " SSM_DPP_KC "\n\t"
       "v_fma_f32 %[h0], %[t0], %[h0], %[u0]\n\t"
-      "v_fmac_f32_dpp %[ya], %[c2], %[h2] " SSM_DPP_KC "\n\t"
       "v_mul_f32_dpp %[u2], %[b2], %[w] " SSM_DPP_KB "\n\t"
+      "v_fmac_f32_dpp %[yp], %[c2], %[h2] " SSM_DPP_KC "\n\t"
       "v_fma_f32 %[h1], %[t1], %[h1], %[u1]\n\t"
-      "v_fmac_f32_dpp %[yb], %[c3], %[h3] " SSM_DPP_KC "\n\t"
       "v_mul_f32_dpp %[u3], %[b3], %[w] " SSM_DPP_KB "\n\t"
+      "v_fmac_f32_dpp %[yp], %[c3], %[h3] " SSM_DPP_KC "\n\t"
       "v_fma_f32 %[h2], %[t2], %[h2], %[u2]\n\t"
-      "v_fma_f32 %[h3], %[t3], %[h3], %[u3]\n\t"
-      "v_add_f32 %[yp], %[ya], %[yb]"
+      "v_fma_f32 %[h3], %[t3], %[h3], %[u3]"
       : [t0] "=&v"(t0), [t1] "=&v"(t1), [t2] "=&v"(t2), [t3] "=&v"(t3), [u0] "=&v"(u0), [u1] "=&v"(u1),
-        [u2] "=&v"(u2), [u3] "=&v"(u3), [ya] "=&v"(ya), [yb] "=&v"(yb), [yp] "=&v"(yp), [h0] "+v"(h[0]),
-        [h1] "+v"(h[1]), [h2] "+v"(h[2]), [h3] "+v"(h[3])
+        [u2] "=&v"(u2), [u3] "=&v"(u3), [yp] "=&v"(yp), [h0] "+v"(h[0]), [h1] "+v"(h[1]), [h2] "+v"(h[2]),
+        [h3] "+v"(h[3])
       : [dt] "v"(dt), [w] "v"(w), [a0] "v"(a2[0]), [a1] "v"(a2[1]), [a2] "v"(a2[2]), [a3] "v"(a2[3]),
         [b0] "v"(b[0]), [b1] "v"(b[1]), [b2] "v"(b[2]), [b3] "v"(b[3]), [c0] "v"(c[0]), [c1] "v"(c[1]),
         [c2] "v"(c[2]), [c3] "v"(c[3]), [kb] "i"(KB), [kc] "i"(KC));
