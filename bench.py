@@ -639,6 +639,10 @@ def main():
         if args.workload != "mamba2p8b":
             extra["mamba2p8b"] = bench_scan("mamba2p8b", max(10, args.steps // 2), 3, torch, np, W, ssm, device)
             log(f"[bench] mamba2p8b: {extra['mamba2p8b']['kernel_ms'] * 1e3:.1f} us/launch")
+        if args.workload != "genomics":
+            extra["genomics"] = bench_scan("genomics", 8, 4, torch, np, W, ssm, device)
+            log(f"[bench] genomics (1 x 2^20 x 256, fp32, split sequence): "
+                f"{extra['genomics']['kernel_ms'] * 1e3:.1f} us/call, {extra['genomics']['hbm_gbps']:.0f} GB/s")
         extra["decode_mall_resident"] = bench_decode(256, torch, np, W, ssm, device, ring=1)
         extra["decode_hbm_ring26"] = bench_decode(256, torch, np, W, ssm, device, ring=26)
         log(f"[bench] decode: {extra['decode_hbm_ring26']['updates_per_s']:.3e} updates/s (ring of 26 states)")
