@@ -92,6 +92,15 @@ def test_chunk_lengths(o, chunk, dtype, shape, segments):
                     segments=segments)
 
 
+@pytest.mark.parametrize("chunk", [16, 32])
+@pytest.mark.parametrize("L", [16, 17, 32, 33, 48, 96, 97])
+def test_whole_and_odd_chunk_counts(o, chunk, L):
+    # the IO waves keep the tiles of the next two chunks in two register slots and run their loop
+    # two iterations at a time: whole chunk counts of both parities, with and without a tail
+    t = W.scan_inputs(2, L, 64, 16, "bf16", seed=L * 7 + chunk)
+    run_and_compare(o, t, "bf16", True, f"L={L} chunk={chunk}", chunk_steps=chunk, segments=1)
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("segments", [2, 3, 7, 16])
 def test_split_sequence(o, dtype, segments):
