@@ -22,7 +22,8 @@
 // recurrence is linear, so a segment's true end state is e^{sum dt A over it} S_in + S_end, with
 // S_end its end state from zero.  Pass 1 (MODE kSsdStateOnly) runs segments 0..k-2 from zero
 // through the state update only and records S_end and sum dt A; ssd_carry_kernel composes the
-// entering states in order; pass 2 (kSsdOutputs) runs every segment from its entering state.
+// entering states in order (with few segments each workgroup of pass 2 composes its own instead);
+// pass 2 (kSsdOutputs) runs every segment from its entering state.
 //
 // Work split: one workgroup per (batch row, head, slice of PS = 16*NW head channels).  Wave w
 // owns channels [16w, 16w+16) of the slice, so the columns of S it updates are exactly the ones
@@ -77,6 +78,8 @@ struct SsdArgs {
   int32_t softplus;
   int32_t nseg;        // segments the chunks are cut into
   int32_t seg_chunks;  // chunks per segment (the last may hold fewer)
+  int32_t compose;     // 1: a later segment composes its entering state itself from seg_state and
+                       // seg_dsum (few segments; no carry kernel); 0: it reads seg_init
 };
 
 constexpr int kSsdOutputs = 0;    // full chunk work: y, and the final state from the last segment
@@ -328,15 +331,34 @@ void ssd_chunk_kernel(const SsdArgs p) {
   ssd_f32x4_t S[NT];
   // the entering state: the carried one for a later segment, the caller's for the first (the
   // state-only pass starts every segment from zero; the carry adds the caller's state)
-  const float* si = (p.seg_init && seg > 0) ? p.seg_init + (seg - 1) * state_seg + state_off
-                    : (OUT && p.init_state && seg == 0) ? p.init_state + state_off
-                                                        : nullptr;
-  if (si) {
+  if (OUT && p.compose && seg > 0) {
+    // composed here, with the carry kernel's arithmetic in its order: from the caller's state
+    // (zero without one), S <- e^{sum dt A of segment r} S + S_end(r) for r = 0 .. seg-1
 #pragma unroll
-    for (int nb = 0; nb < NT; ++nb) S[nb] = *reinterpret_cast<const ssd_f32x4_t*>(si + 16 * nb);
+    for (int nb = 0; nb < NT; ++nb)
+      S[nb] = p.init_state ? *reinterpret_cast<const ssd_f32x4_t*>(p.init_state + state_off + 16 * nb)
+                           : ssd_f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int r = 0; r < seg; ++r) {
+      const float decay = hw_exp2(p.seg_dsum[r * nbh + bh]);
+      const float* sr = p.seg_state + r * state_seg + state_off;
+#pragma unroll
+      for (int nb = 0; nb < NT; ++nb) {
+        const ssd_f32x4_t e = *reinterpret_cast<const ssd_f32x4_t*>(sr + 16 * nb);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) S[nb][i] = fmaf(decay, S[nb][i], e[i]);
+      }
+    }
   } else {
+    const float* si = (p.seg_init && seg > 0) ? p.seg_init + (seg - 1) * state_seg + state_off
+                      : (OUT && p.init_state && seg == 0) ? p.init_state + state_off
+                                                          : nullptr;
+    if (si) {
 #pragma unroll
-    for (int nb = 0; nb < NT; ++nb) S[nb] = ssd_f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+      for (int nb = 0; nb < NT; ++nb) S[nb] = *reinterpret_cast<const ssd_f32x4_t*>(si + 16 * nb);
+    } else {
+#pragma unroll
+      for (int nb = 0; nb < NT; ++nb) S[nb] = ssd_f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    }
   }
 
   const int64_t nch = (L + Q - 1) / Q;

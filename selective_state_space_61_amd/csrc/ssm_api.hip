@@ -713,6 +713,7 @@ ssm_status_t ssm_ssd_fwd(int64_t batch, int64_t seqlen, int64_t nheads, int64_t 
   a.softplus = dt_softplus ? 1 : 0;
   const hipStream_t st = static_cast<hipStream_t>(stream);
 
+  constexpr int64_t kSsdComposeMax = 8;
   // Sequence split: when the (batch row, head, slice) workgroups cannot fill the chip, cut the
   // 64-step chunks into segments, one workgroup per compute unit.  Measured on MI355X (1 x 1024
   // steps x 64 heads, dstate 128): 60 us unsplit, 50 us with 2 segments, 34 us with 4 or 8, 44 us
@@ -742,10 +743,17 @@ ssm_status_t ssm_ssd_fwd(int64_t batch, int64_t seqlen, int64_t nheads, int64_t 
     hipLaunchKernelGGL(ssm::ssd_kernel(dstate, waves, ssm::kSsdStateOnly), dim3(static_cast<unsigned>(g1)),
                        dim3(64 * waves), 0, st, a);
     if ((s = check_launch("SSD segment states")) != SSM_OK) return s;
-    hipLaunchKernelGGL(ssm::ssd_carry_kernel<0>, dim3(static_cast<unsigned>((per_seg + 255) / 256)), dim3(256), 0, st,
-                       a, static_cast<int32_t>(dstate));
-    if ((s = check_launch("SSD segment carry")) != SSM_OK) return s;
-    a.seg_init = a.seg_state;
+    // With few segments every workgroup of the outputs pass composes its own entering state (it
+    // reads at most kSsdComposeMax - 1 segment states), which saves the carry kernel and its
+    // launch; with many, the carry kernel composes them once.
+    if (nseg <= kSsdComposeMax) {
+      a.compose = 1;
+    } else {
+      hipLaunchKernelGGL(ssm::ssd_carry_kernel<0>, dim3(static_cast<unsigned>((per_seg + 255) / 256)), dim3(256), 0,
+                         st, a, static_cast<int32_t>(dstate));
+      if ((s = check_launch("SSD segment carry")) != SSM_OK) return s;
+      a.seg_init = a.seg_state;
+    }
   }
   hipLaunchKernelGGL(k, dim3(static_cast<unsigned>(grid)), dim3(64 * waves), 0, st, a);
   return check_launch("SSD chunk kernel");
