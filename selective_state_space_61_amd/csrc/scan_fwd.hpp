@@ -407,13 +407,32 @@ __global__ __launch_bounds__(256) void scan_carry_kernel(const ScanArgs p) {
   const int n = static_cast<int>(i % N);
   const int64_t d = bd % p.dim;
   const float a2 = p.A[d * N + n] * kLog2e;
+  const int64_t per_sum = p.batch * p.dim;
+  const int last = p.nseg - 1;  // segments 0 .. nseg-2 have summaries
   float h = 0.0f;
-  for (int s = 0; s + 1 < p.nseg; ++s) {
+  // the summaries of kCarryBatch segments are loaded before any of them is composed, so their
+  // loads overlap instead of costing one memory round trip per segment
+  constexpr int kCarryBatch = 8;
+  int s = 0;
+  for (; s + kCarryBatch <= last; s += kCarryBatch) {
+    float hs[kCarryBatch], ds[kCarryBatch];
+#pragma unroll
+    for (int u = 0; u < kCarryBatch; ++u) {
+      hs[u] = p.seg_state[(s + u) * per_seg + i];
+      ds[u] = p.seg_dsum[(s + u) * per_sum + bd];
+    }
+#pragma unroll
+    for (int u = 0; u < kCarryBatch; ++u) {
+      p.seg_state[(s + u) * per_seg + i] = h;
+      h = fmaf(hw_exp2(a2 * ds[u]), h, hs[u]);
+    }
+  }
+  for (; s < last; ++s) {
     const float hs = p.seg_state[s * per_seg + i];
     p.seg_state[s * per_seg + i] = h;
-    h = fmaf(hw_exp2(a2 * p.seg_dsum[s * p.batch * p.dim + bd]), h, hs);
+    h = fmaf(hw_exp2(a2 * p.seg_dsum[s * per_sum + bd]), h, hs);
   }
-  p.seg_state[static_cast<int64_t>(p.nseg - 1) * per_seg + i] = h;
+  p.seg_state[static_cast<int64_t>(last) * per_seg + i] = h;
 }
 
 }  // namespace ssm
