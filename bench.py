@@ -609,7 +609,7 @@ def main():
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(f"bench.py: this build measures one GPU only (--gpus {args.gpus}, WORLD_SIZE {world}); "
+        print(f"bench.py measures one GPU only (--gpus {args.gpus}, WORLD_SIZE {world}); "
               "every (batch, channel) is independent, so N GPUs would each run 1/N of the channels "
               "with no communication. Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
