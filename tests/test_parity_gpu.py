@@ -101,6 +101,28 @@ def test_whole_and_odd_chunk_counts(o, chunk, L):
     run_and_compare(o, t, "bf16", True, f"L={L} chunk={chunk}", chunk_steps=chunk, segments=1)
 
 
+@pytest.mark.parametrize("segments", [1, 3])
+def test_channel_independence_bitwise(o, segments):
+    # changing the inputs of one channel changes that channel's outputs and nothing else, bit for
+    # bit: no lane, tile or segment mixes channels (B and C are shared, x / delta / z are not)
+    t = W.scan_inputs(2, 150, 136, 16, "bf16", seed=17)
+    y0, s0, _ = scan_on_gpu(t, True, segments=segments)
+    t2 = dict(t)
+    d0 = 70
+    for k in ("x", "delta", "z"):
+        if t[k] is None:
+            continue
+        v = t[k].copy()
+        v[:, :, d0] = v[:, :, d0] ^ np.uint16(0x0040)
+        t2[k] = v
+    y1, s1, _ = scan_on_gpu(t2, True, segments=segments)
+    say(f"[case] channel independence, segments={segments}")
+    keep = [d for d in range(136) if d != d0]
+    assert torch.equal(y0[:, :, keep], y1[:, :, keep]), "another channel's y changed"
+    assert torch.equal(s0[:, keep], s1[:, keep]), "another channel's state changed"
+    assert not torch.equal(y0[:, :, d0], y1[:, :, d0]), "the perturbed channel did not change"
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("segments", [2, 3, 7, 16])
 def test_split_sequence(o, dtype, segments):

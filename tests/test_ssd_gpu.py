@@ -181,6 +181,28 @@ def test_initial_state_composed_and_carried(o, segments):
     assert_close(to_host(fin), fin_ref, TOL_SSD, f"segments={segments} final_state")
 
 
+@pytest.mark.parametrize("segments", [1, 3])
+def test_head_independence_bitwise(o, segments):
+    """Changing the x, z and dt of one head changes that head's outputs and nothing else, bit for
+    bit, although all heads of the group share B and C."""
+    t = W.ssd_inputs(2, 200, 4, 64, 128, 1, seed=33)
+    y0, f0 = ssd_gpu(t, segments=segments)
+    t2 = dict(t)
+    h0 = 2
+    for k in ("x", "z", "dt"):
+        if t[k] is None:
+            continue
+        v = t[k].copy()
+        v[:, :, h0] = v[:, :, h0] ^ np.uint16(0x0040)
+        t2[k] = v
+    y1, f1 = ssd_gpu(t2, segments=segments)
+    say(f"[case] ssd head independence, segments={segments}")
+    keep = [h for h in range(4) if h != h0]
+    assert torch.equal(y0[:, :, keep], y1[:, :, keep]), "another head's y changed"
+    assert torch.equal(f0[:, keep], f1[:, keep]), "another head's final state changed"
+    assert not torch.equal(y0[:, :, h0], y1[:, :, h0]), "the perturbed head did not change"
+
+
 def test_initial_state_empty_sequence():
     import selective_state_space_61_amd as ssm
     t = W.ssd_inputs(2, 0, 4, 64, 64, 1, seed=9)
