@@ -123,6 +123,23 @@ def test_channel_independence_bitwise(o, segments):
     assert not torch.equal(y0[:, :, d0], y1[:, :, d0]), "the perturbed channel did not change"
 
 
+@pytest.mark.parametrize("t0", [0, 31, 77, 149])
+def test_causality_bitwise(o, t0):
+    # changing every input at step t0 leaves all outputs before t0 unchanged, bit for bit (tiles
+    # are loaded chunks ahead; none of that may reach an earlier step)
+    t = W.scan_inputs(2, 150, 72, 16, "bf16", seed=23)
+    y0, _, _ = scan_on_gpu(t, True)
+    t2 = dict(t)
+    for k in ("x", "delta", "z", "B", "C"):
+        v = t[k].copy()
+        v[:, t0] = v[:, t0] ^ np.uint16(0x0040)
+        t2[k] = v
+    y1, _, _ = scan_on_gpu(t2, True)
+    say(f"[case] causality, t0={t0}")
+    assert torch.equal(y0[:, :t0], y1[:, :t0]), "an output before the perturbed step changed"
+    assert not torch.equal(y0[:, t0], y1[:, t0]), "the perturbed step did not change"
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("segments", [2, 3, 7, 16])
 def test_split_sequence(o, dtype, segments):

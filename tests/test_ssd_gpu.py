@@ -181,6 +181,23 @@ def test_initial_state_composed_and_carried(o, segments):
     assert_close(to_host(fin), fin_ref, TOL_SSD, f"segments={segments} final_state")
 
 
+@pytest.mark.parametrize("t0", [0, 5, 63, 64, 130, 199])
+def test_causality_bitwise(o, t0):
+    """Changing every input at step t0 leaves all outputs before t0 unchanged, bit for bit: inside
+    a 64-step chunk the masked product must drop every j > i."""
+    t = W.ssd_inputs(1, 200, 4, 64, 128, 1, seed=44)
+    y0, _ = ssd_gpu(t)
+    t2 = dict(t)
+    for k in ("x", "z", "dt", "B", "C"):
+        v = t[k].copy()
+        v[:, t0] = v[:, t0] ^ np.uint16(0x0040)
+        t2[k] = v
+    y1, _ = ssd_gpu(t2)
+    say(f"[case] ssd causality, t0={t0}")
+    assert torch.equal(y0[:, :t0], y1[:, :t0]), "an output before the perturbed step changed"
+    assert not torch.equal(y0[:, t0], y1[:, t0]), "the perturbed step did not change"
+
+
 @pytest.mark.parametrize("segments", [1, 3])
 def test_head_independence_bitwise(o, segments):
     """Changing the x, z and dt of one head changes that head's outputs and nothing else, bit for
