@@ -74,6 +74,26 @@ def test_variants(o, variant):
     compare(o, t, "bf16", variant != "no_silu", f"variant {variant}")
 
 
+@pytest.mark.parametrize("t0,d0", [(0, 5), (31, 64), (32, 130), (95, 199)])
+def test_causality_and_channel_independence_bitwise(o, t0, d0):
+    # changing x at (t0, d0) changes y only at channel d0 and steps t0 .. t0+K-1, bit for bit:
+    # the halo a time tile reads is the K-1 steps before it, never after
+    K = 4
+    t = W.conv_inputs(2, 128, 200, K, "bf16", seed=t0 + d0, has_init=True)
+    y0, _ = conv_gpu(t, True)
+    t2 = dict(t)
+    x = t["x"].copy()
+    x[:, t0, d0] = x[:, t0, d0] ^ np.uint16(0x0040)
+    t2["x"] = x
+    y1, _ = conv_gpu(t2, True)
+    say(f"[case] conv causality and channel independence, t0={t0} d0={d0}")
+    changed = (y0 != y1).cpu().numpy()
+    allowed = np.zeros_like(changed)
+    allowed[:, t0:t0 + K, d0] = True
+    assert not np.any(changed & ~allowed), "an output outside the perturbed step's reach changed"
+    assert np.any(changed[:, t0:t0 + K, d0]), "no output in the perturbed step's reach changed"
+
+
 def test_empty_sequence_passes_state_through(o):
     import selective_state_space_61_amd as ssm
     t = W.conv_inputs(2, 0, 24, 4, "f32", seed=3, has_init=True)
