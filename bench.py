@@ -528,6 +528,9 @@ def profile_mode(args):
     elif args.workload == "bwd":
         res = bench_scan_bwd(args.steps, args.warmup, torch, np, W, ssm, torch.device("cuda:0"))
         res["kernel_ms"] = res["ms_per_call"]
+    elif args.workload == "ssd_decode":
+        res = bench_ssd_decode(torch, np, W, ssm, torch.device("cuda:0"))
+        res["kernel_ms"] = res["ms_per_step"]
     elif args.workload in W.SSD_WORKLOADS:
         res = bench_ssd(args.workload, args.steps, args.warmup, torch, np, W, ssm, torch.device("cuda:0"))
     else:
@@ -592,7 +595,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="mamba130m",
-                    choices=["mamba130m", "mamba2p8b", "genomics", "decode", "conv", "bwd", "mamba2_layer",
+                    choices=["mamba130m", "mamba2p8b", "genomics", "decode", "ssd_decode", "conv", "bwd", "mamba2_layer",
                              "mamba2_layer_b8"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the context measurements (2.8B scan, decode)")
@@ -621,7 +624,7 @@ def main():
     import selective_state_space_61_amd as ssm
     from selective_state_space_61_amd import build as hip_build
 
-    if args.workload in ("decode", "conv", "bwd", "mamba2_layer", "mamba2_layer_b8"):
+    if args.workload in ("decode", "ssd_decode", "conv", "bwd", "mamba2_layer", "mamba2_layer_b8"):
         raise SystemExit(f"{args.workload} is measured as context next to a scan workload; use --profile-mode for it alone")
     if not os.path.exists(ssm.LIBRARY):
         hip_build.build(verbose=True)
