@@ -180,6 +180,7 @@ def bench_decode(steps_per_rep, torch, np, W, ssm, device, ring):
     out = {"batch": w.batch, "dim": w.dim, "dstate": w.dstate, "steps": steps_per_rep, "state_ring": ring,
            "ms_per_step": graph_ms, "ms_per_step_eager_python": eager_ms,
            "updates_per_s": upd / (graph_ms * 1e-3), "tokens_per_s": w.batch / (graph_ms * 1e-3),
+           "calls_per_s": 1.0 / (graph_ms * 1e-3),
            "alg_bytes_per_step": bpstep, "hbm_gbps": bpstep / (graph_ms * 1e-3) / 1e9,
            "same_size_inplace_pass_gbps": 2 * states[0].numel() * 4 / (copy_ms * 1e-3) / 1e9,
            "kernel_ms": graph_ms}
@@ -468,6 +469,17 @@ def bench_conv_update(steps, torch, np, W, ssm, device):
             "hbm_gbps": step_bytes / (ms * 1e-3) / 1e9}
 
 
+def host_cpu_name():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(name, np, W):
     import oracle
     w = W.WORKLOADS[name]
@@ -486,10 +498,19 @@ def cpu_baseline(name, np, W):
         walls.append(time.perf_counter() - t0)
     dt = sorted(walls)[1]
     elems = w.batch * w.seqlen * w.dim
+    # the same oracle on one thread, over the first batch row (a bounded sample)
+    one = {k: (v[:1] if k in ("x", "delta", "B", "C", "z") and v is not None else v) for k, v in t.items()}
+    t0 = time.perf_counter()
+    o.scan(one["x"], one["delta"], one["A"], one["B"], one["C"], D=one["D"], z=one["z"], delta_bias=one["delta_bias"],
+           delta_softplus=w.delta_softplus, nthreads=1)
+    dt1 = time.perf_counter() - t0
     return {"value": elems / dt, "unit": "elem/s", "cores": cores, "kind": "oracle",
             "sample": f"the whole {name} workload ({w.batch}x{w.seqlen}x{w.dim}, N={w.dstate}), three runs, "
                       f"fp64 sequential recurrence, OpenMP over channels; median {dt:.2f} s wall "
-                      f"(runs {', '.join(f'{x:.2f}' for x in walls)} s)"}
+                      f"(runs {', '.join(f'{x:.2f}' for x in walls)} s)",
+            "one_core_value": (w.seqlen * w.dim) / dt1,
+            "one_core_sample": f"batch row 0 of the same workload on one thread, {dt1:.2f} s wall",
+            "host_cpu": host_cpu_name()}
 
 
 def traffic_from_profiles(name, alg_bytes):
@@ -707,7 +728,9 @@ def main():
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(args.workload, np, W)
-        log(f"[bench] cpu oracle: {line['cpu_baseline']['value']:.3e} elem/s on {line['cpu_baseline']['cores']} cores")
+        cb = line["cpu_baseline"]
+        log(f"[bench] cpu oracle: {cb['value']:.3e} elem/s on {cb['cores']} cores, "
+            f"{cb['one_core_value']:.3e} elem/s on one ({cb['host_cpu']})")
     if extra:
         line["extra"] = extra
     print(json.dumps(line), flush=True)
