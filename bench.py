@@ -113,6 +113,7 @@ def bench_scan(name, steps, warmup, torch, np, W, ssm, device, zoh=False):
     res = {
         "workload": name, "batch": w.batch, "seqlen": w.seqlen, "dim": w.dim, "dstate": w.dstate,
         "io_dtype": w.dtype, "rotated_input_sets": copies, "ms_per_step": ms_step, "kernel_ms": kern_ms,
+        "kernel_ms_median": sorted(per)[len(per) // 2], "kernel_ms_min": min(per),
         "elems_per_s": elems / (ms_step * 1e-3), "alg_bytes": set_bytes,
         "hbm_gbps": set_bytes / (kern_ms * 1e-3) / 1e9,
         "valu_slot_frac": SLOTS_PER_UPDATE * updates / (kern_ms * 1e-3) / VALU_LANE_SLOTS,
@@ -712,6 +713,8 @@ def main():
     roof["hbm_frac"] = hbm_frac
     roof["alg_bytes_per_launch"] = main_res["alg_bytes"]
     roof["kernel_ms"] = main_res["kernel_ms"]
+    roof["kernel_ms_median"] = main_res["kernel_ms_median"]
+    roof["kernel_ms_min"] = main_res["kernel_ms_min"]
     roof["copy_ceiling_gbps"] = copy_ceiling_gbps(torch, device)
     roof["hbm_frac_of_copy_ceiling"] = main_res["hbm_gbps"] / roof["copy_ceiling_gbps"]
 
