@@ -173,10 +173,12 @@ __device__ __forceinline__ float row_bcast(float v) {
 // compiler does not fold a broadcast into a multiply-accumulate, so the step is written as one
 // instruction sequence.  Its order obeys the gfx9 VALU hazards, which the compiler cannot enforce
 // inside an asm statement:
-//   * a DPP instruction reads each VGPR operand at least two instructions after the VALU write
-//     of it (inside the block), and its first DPP instruction comes late enough that any write
-//     made just before the block is two or more instructions old;
-//   * no instruction reads a v_exp_f32 result sooner than two instructions after it.
+//   * a DPP instruction reads each VGPR operand (the broadcast source, the other source and a
+//     multiply-accumulate's accumulator) at least two instructions after the VALU write of it
+//     (inside the block), and its first DPP instruction comes late enough that any write made
+//     just before the block is two or more instructions old;
+//   * no instruction reads a v_exp_f32 result sooner than two instructions after it;
+//   * a chain's h is read by its read-out before the update overwrites it.
 // The block has only VALU instructions: no memory access, no EXEC change.
 // ---------------------------------------------------------------------------------------------
 #define SSM_DPP_KB "row_newbcast:%[kb] row_mask:0xf bank_mask:0xf"
@@ -231,14 +233,14 @@ __device__ __forceinline__ float step_readout4(float dt, float w, const float* a
       "v_mul_f32_dpp %[u0], %[b0], %[w] " SSM_DPP_KB "\n\t"
       "v_mul_f32_dpp %[yp], %[c0], %[h0] " SSM_DPP_KC "\n\t"
       "v_mul_f32_dpp %[u1], %[b1], %[w] " SSM_DPP_KB "\n\t"
-      "v_fmac_f32_dpp %[yp], %[c1], %[h1] " SSM_DPP_KC "\n\t"
       "v_fma_f32 %[h0], %[t0], %[h0], %[u0]\n\t"
+      "v_fmac_f32_dpp %[yp], %[c1], %[h1] " SSM_DPP_KC "\n\t"
       "v_mul_f32_dpp %[u2], %[b2], %[w] " SSM_DPP_KB "\n\t"
-      "v_fmac_f32_dpp %[yp], %[c2], %[h2] " SSM_DPP_KC "\n\t"
       "v_fma_f32 %[h1], %[t1], %[h1], %[u1]\n\t"
+      "v_fmac_f32_dpp %[yp], %[c2], %[h2] " SSM_DPP_KC "\n\t"
       "v_mul_f32_dpp %[u3], %[b3], %[w] " SSM_DPP_KB "\n\t"
-      "v_fmac_f32_dpp %[yp], %[c3], %[h3] " SSM_DPP_KC "\n\t"
       "v_fma_f32 %[h2], %[t2], %[h2], %[u2]\n\t"
+      "v_fmac_f32_dpp %[yp], %[c3], %[h3] " SSM_DPP_KC "\n\t"
       "v_fma_f32 %[h3], %[t3], %[h3], %[u3]"
       : [t0] "=&v"(t0), [t1] "=&v"(t1), [t2] "=&v"(t2), [t3] "=&v"(t3), [u0] "=&v"(u0), [u1] "=&v"(u1),
         [u2] "=&v"(u2), [u3] "=&v"(u3), [yp] "=&v"(yp), [h0] "+v"(h[0]), [h1] "+v"(h[1]), [h2] "+v"(h[2]),
