@@ -140,12 +140,13 @@ def test_chaining_equals_one_call(o):
     assert torch.equal(f2, fin_all)
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("width", [1, 2, 4])
-def test_update_matches_oracle_and_fwd(o, dtype, width):
-    """Token-by-token updates reproduce the oracle's convolution and the GPU's full call."""
+@pytest.mark.parametrize("dtype,width,dim", [("f32", 1, 40), ("f32", 2, 40), ("f32", 4, 40), ("bf16", 1, 40),
+                                             ("bf16", 2, 40), ("bf16", 4, 40), ("bf16", 4, 41), ("bf16", 3, 40)])
+def test_update_matches_oracle_and_fwd(o, dtype, width, dim):
+    """Token-by-token updates reproduce the oracle's convolution and the GPU's full call (even and
+    odd dim, every width)."""
     import selective_state_space_61_amd as ssm
-    batch, L, dim = 3, 12, 40
+    batch, L = 3, 12
     t = W.conv_inputs(batch, L, dim, width, dtype, seed=width + 30, has_init=width > 1)
     d = {k: to_dev(v) for k, v in t.items()}
     y_ref, fin_ref = o.causal_conv1d(t["x"], t["weight"], t["bias"], t["init"], silu=True)
