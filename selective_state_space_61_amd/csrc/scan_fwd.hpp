@@ -6,20 +6,21 @@
 //   y_t *= silu(z_t).
 //
 // Work decomposition (one workgroup = 64 channels of one batch row x all N state indices,
-// optionally x one segment of the sequence):
-//   * wave g of the workgroup owns state indices n in [g*NPL, (g+1)*NPL) of all 64 channels;
-//     lane = channel.  Its NPL states live in VGPRs for the whole sequence (never in HBM).
+// optionally x one segment of the sequence), with two kinds of waves:
+//   * scan wave g (G = N / NPL of them) owns state indices n in [g*NPL, (g+1)*NPL) of all 64
+//     channels; lane = channel.  Its NPL states live in VGPRs for the whole sequence (never in
+//     HBM), and it does nothing but the recurrence and the read-out.
 //     B_t[n] and C_t[n] are the same for all 64 lanes: lane k of every 16-lane row loads step
 //     k of each 16-step half of the chunk, and each step takes its values with DPP row
 //     broadcasts that are operands of the multiply (B_t * w) and of the read-out multiply-adds
 //     (C_t * h) -- no memory access and no LDS traffic for B and C.  Each step is one fused,
 //     hazard-ordered instruction block that also reads out the previous step.
-//   * per chunk of CHUNK time steps, all threads of the workgroup load the x / delta / z tile
-//     with coalesced vector loads (a chunk ahead, into registers), compute the per-(t, d)
-//     prologue once (softplus, dt * x) into LDS, every wave runs its CHUNK steps of the
-//     recurrence reading (dt, w) from LDS, writes its partial read-out sum_{n in group} C h
-//     to LDS, and the same threads that loaded the tile sum the G partials, add D x, apply
-//     the gate and store y with vector stores.
+//   * kIoWaves IO waves, per chunk of CH time steps: they load the x / delta / z tile with
+//     coalesced 16-byte loads (two chunks ahead, into registers), compute the per-(t, d)
+//     prologue once (softplus, dt * x) into LDS for the scan waves, and, for the chunk the scan
+//     waves finished one iteration earlier, sum the G partial read-outs sum_{n in group} C h
+//     that those left in LDS, add D x, apply the gate and store y with 16-byte stores.  One
+//     barrier per chunk separates the roles; every LDS buffer is double-buffered across it.
 //   * rows past the end of the sequence and channels past `dim` are carried with
 //     dt = w = B = C = 0, which makes those steps exact identities on the state (A is clamped
 //     to a finite value, so exp2(0 * A) = 1); their outputs are never stored.  Every chunk
