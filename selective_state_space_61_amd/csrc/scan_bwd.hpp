@@ -15,15 +15,17 @@
 //   phase 0 (forward, chunks 0 .. nc-1): IO waves stage (dt, dt x) in LDS, scan waves run the
 //     recurrence and store the state at the start of every kBwdChunk-step chunk in scratch
 //     (B, nc, N, D) fp32 -- the only O(B L D N / kBwdChunk) memory the pass uses;
-//   phase 1 (reverse, chunks nc-1 .. 0), per chunk:
-//     A  IO:   load x, delta, z, dy; stage (dt, dt x) in LDS
+//   phase 1 (reverse, chunks nc-1 .. 0), per chunk, with two barriers:
+//     A  IO:   stage (dt, dt x) and dy0 = dy silu(z) in LDS from the x, delta, z, dy tile fetched
+//              a chunk earlier (dy0 needs no read-out, so it is staged up front); dD partial;
+//              fetch the next chunk's tile                                      -- barrier (1)
 //     B  scan: recompute the chunk's states from the stored chunk start, keep them in VGPRs, and
 //              write the read-out partials C_t.h_t
-//     C  IO:   y0 = sum of partials + D x; dz; dy0 = dy silu(z) into LDS; dD partial
 //     D  scan: reverse the chunk: adjoint g, dA in registers, per-lane dx / ddt partials into
 //              LDS, and the channel sums of dB / dC through an LDS transpose, written per channel
-//              block to scratch
-//     E  IO:   dx, ddelta from the partials; store dx, ddelta, dz; dbias partial
+//              block to scratch                                               -- barrier (2)
+//     E  IO:   y0 = sum of partials + D x, dz, and dx, ddelta from the partials; store dx,
+//              ddelta, dz; dbias partial
 // A second kernel adds the channel-block partials of dB and dC, and the per-batch-row partials
 // of dA, dD and dbias, in a fixed order (deterministic).
 #pragma once
