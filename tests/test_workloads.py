@@ -81,3 +81,16 @@ def test_named_workloads_shapes():
     s = W.scan_inputs(3, 5, 7, 4, "bf16", seed=1)
     assert d["x"].shape == (5, 3, 7) and d["B"].shape == (5, 3, 4)
     assert np.array_equal(d["x"][2], s["x"][:, 2]) and np.array_equal(d["C"][4], s["C"][:, 4])
+
+
+def test_long_inputs_repeat_a_block_in_time():
+    t = W.long_scan_inputs(2, 1000, 40, 16, 37, "bf16", seed=5)
+    assert t["x"].shape == (2, 37, 40) and t["B"].shape == (2, 1000, 16) and t["C"].shape == (2, 1000, 16)
+    r = W.repeat_in_time(t["x"][:, :, 3:4], 1000)
+    assert r.shape == (2, 1000, 1) and r.flags["C_CONTIGUOUS"]
+    for step in (0, 36, 37, 500, 999):
+        assert np.array_equal(r[:, step], t["x"][:, step % 37, 3:4])
+    s = W.long_ssd_inputs(1, 500, 4, 8, 32, 31, seed=6)
+    assert s["x"].shape == (1, 31, 4, 8) and s["dt"].shape == (1, 500, 4) and s["B"].shape == (1, 500, 1, 32)
+    # B and C vary over the whole sequence, not with the block's period
+    assert not np.array_equal(s["B"][:, 31:62], s["B"][:, 0:31])

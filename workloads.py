@@ -222,6 +222,35 @@ def ssd_inputs(batch: int, seqlen: int, nheads: int, headdim: int, dstate: int, 
             "z": None if z is None else _store(z, "bf16"), "A": A, "D": D, "dt_bias": bias}
 
 
+def long_scan_inputs(batch: int, seqlen: int, dim: int, dstate: int, period: int, dtype: str = "bf16",
+                     seed: int = 0) -> Dict[str, Optional[np.ndarray]]:
+    """A scan too long to draw element by element on the host: x, delta and z are one
+    (batch, period, dim) block that the sequence repeats along time (see repeat_in_time); B and C
+    are drawn for every one of the seqlen steps; A, D and the bias as scan_inputs draws them."""
+    t = scan_inputs(batch, period, dim, dstate, dtype, seed)
+    t["B"] = _store(_normal(seed, "B", (batch, seqlen, dstate)), dtype)
+    t["C"] = _store(_normal(seed, "C", (batch, seqlen, dstate)), dtype)
+    return t
+
+
+def long_ssd_inputs(batch: int, seqlen: int, nheads: int, headdim: int, dstate: int, period: int,
+                    seed: int = 0) -> Dict[str, Optional[np.ndarray]]:
+    """An SSD layer call too long to draw element by element on the host: x and z are one
+    (batch, period, nheads, headdim) block repeated along time; dt, B and C (one group) are drawn
+    for every step; A, D and dt_bias as ssd_inputs draws them."""
+    t = ssd_inputs(batch, period, nheads, headdim, dstate, 1, seed)
+    t["dt"] = _store(_normal(seed, "delta", (batch, seqlen, nheads), 0.5), "bf16")
+    t["B"] = _store(_normal(seed, "B", (batch, seqlen, 1, dstate)), "bf16")
+    t["C"] = _store(_normal(seed, "C", (batch, seqlen, 1, dstate)), "bf16")
+    return t
+
+
+def repeat_in_time(block: np.ndarray, seqlen: int) -> np.ndarray:
+    """block (batch, period, ...) repeated along axis 1 and cut to seqlen steps."""
+    reps = -(-seqlen // block.shape[1])
+    return np.ascontiguousarray(np.concatenate([block] * reps, axis=1)[:, :seqlen])
+
+
 def ssd_workload_inputs(w: SsdWorkload) -> Dict[str, Optional[np.ndarray]]:
     return ssd_inputs(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups, w.seed)
 
