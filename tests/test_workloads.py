@@ -94,3 +94,7 @@ def test_long_inputs_repeat_a_block_in_time():
     assert s["x"].shape == (1, 31, 4, 8) and s["dt"].shape == (1, 500, 4) and s["B"].shape == (1, 500, 1, 32)
     # B and C vary over the whole sequence, not with the block's period
     assert not np.array_equal(s["B"][:, 31:62], s["B"][:, 0:31])
+    d = W.long_decode_inputs(20, 96, 16, 7, seed=3)
+    assert d["state_block"].shape == (7, 96, 16) and d["x"].shape == (20, 96) and d["B"].shape == (20, 16)
+    e = W.long_ssd_decode_inputs(12, 4, 8, 32, 5, seed=4)
+    assert e["state_block"].shape == (5, 4, 8, 32) and e["x"].shape == (12, 4, 8) and e["B"].shape == (12, 1, 32)

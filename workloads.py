@@ -41,7 +41,7 @@ import numpy as np
 
 # Stream ids: one Philox key per (seed, tensor).
 _TENSOR_IDS = {"x": 1, "delta": 2, "B": 3, "C": 4, "z": 5, "bias": 6, "symbols": 7, "W": 8, "conv_w": 9,
-               "conv_b": 10, "conv_state": 11, "A": 12}
+               "conv_b": 10, "conv_state": 11, "A": 12, "state": 13}
 
 _CHUNK = 1 << 24  # elements per draw; bounds temporary memory for the 1M-step workload
 
@@ -243,6 +243,30 @@ def long_ssd_inputs(batch: int, seqlen: int, nheads: int, headdim: int, dstate: 
     t["B"] = _store(_normal(seed, "B", (batch, seqlen, 1, dstate)), "bf16")
     t["C"] = _store(_normal(seed, "C", (batch, seqlen, 1, dstate)), "bf16")
     return t
+
+
+def long_decode_inputs(batch: int, dim: int, dstate: int, period: int,
+                       seed: int = 0) -> Dict[str, Optional[np.ndarray]]:
+    """One decode step over a state too large to draw element by element on the host: the state
+    is one (period, dim, dstate) fp32 block repeated along the batch (state_block); x, delta, z
+    (batch, dim) and B, C (batch, dstate) are drawn in full, bf16; A, D and the bias as
+    scan_inputs draws them."""
+    t = scan_inputs(batch, 1, dim, dstate, "bf16", seed)
+    out = {k: (v[:, 0] if k in ("x", "delta", "z", "B", "C") else v) for k, v in t.items()}
+    out["state_block"] = _normal(seed, "state", (period, dim, dstate), 0.5)
+    return out
+
+
+def long_ssd_decode_inputs(batch: int, nheads: int, headdim: int, dstate: int, period: int,
+                           seed: int = 0) -> Dict[str, Optional[np.ndarray]]:
+    """One SSD decode step over a state too large to draw element by element on the host: the
+    state is one (period, nheads, headdim, dstate) fp32 block repeated along the batch
+    (state_block); x, z (batch, nheads, headdim), dt (batch, nheads) and B, C (batch, 1, dstate)
+    are drawn in full, bf16; A, D and dt_bias as ssd_inputs draws them."""
+    t = ssd_inputs(batch, 1, nheads, headdim, dstate, 1, seed)
+    out = {k: (v[:, 0] if k in ("x", "z", "dt", "B", "C") else v) for k, v in t.items()}
+    out["state_block"] = _normal(seed, "state", (period, nheads, headdim, dstate), 0.5)
+    return out
 
 
 def repeat_in_time(block: np.ndarray, seqlen: int) -> np.ndarray:
