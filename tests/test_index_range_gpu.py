@@ -8,8 +8,8 @@ past 2^31).
 x, delta and z repeat a block of a few thousand steps along time (period 4099 or 1031, prime to
 the tile sizes and to the row length); B, C and the SSD's dt are drawn for every step.  An
 offset that wrapped at 2^31 or 2^32 would land on another channel or step, not on an equal
-value; the decode states repeat a block of 7 (5) batch rows.  The largest case takes about 18 GB
-of device memory."""
+value; the decode states repeat a block of 7 (5) batch rows.  The largest case, the backward,
+takes about 44 GB of device memory."""
 import os
 
 import numpy as np
@@ -158,3 +158,30 @@ def test_ssd_decode_state_beyond_2_31_elements(o):
         assert_close(to_host(y[b]), y_ref[0, 0], TOL["bf16"], f"SSD decode y (row {b})")
         assert_close(to_host(state[b]), fin_ref[0], TOL["bf16"], f"SSD decode state (row {b})")
     del state
+
+
+def test_scan_bwd_beyond_2_31_elements(o):
+    """The backward over the scan shape above: dx, ddelta and dz (past 2^31 elements each) and
+    the per-channel dA, dD and ddelta_bias on sampled channels, from a single-channel oracle run
+    over both batch rows.  dB and dC sum over every channel (their buffers stay below 2^31
+    elements) and are covered by the full-width cases of test_bwd_gpu.py."""
+    import selective_state_space_61_amd as ssm
+    t = W.long_scan_inputs(BATCH, L, DIM, 16, PERIOD, "bf16", seed=61105)
+    dy = W.f32_to_bf16_bits(np.random.default_rng(61105).standard_normal((BATCH, PERIOD, DIM)).astype(np.float32))
+    say(f"[case] scan backward of {BATCH}x{L}x{DIM} bf16")
+    x, delta, z, dyd = tiled(t["x"], L), tiled(t["delta"], L), tiled(t["z"], L), tiled(dy, L)
+    g = ssm.ssm_scan_bwd(x, delta, to_dev(t["A"]), to_dev(t["B"]), to_dev(t["C"]), dyd, D=to_dev(t["D"]), z=z,
+                         delta_bias=to_dev(t["delta_bias"]), delta_softplus=True)
+    torch.cuda.synchronize()
+    del x, delta, z, dyd
+    for d in (0, 517, DIM - 1):
+        cols = {k: W.repeat_in_time(src[:, :, d:d + 1], L)
+                for k, src in (("x", t["x"]), ("delta", t["delta"]), ("z", t["z"]), ("dy", dy))}
+        ref = o.scan_bwd(cols["x"], cols["delta"], t["A"][d:d + 1], t["B"], t["C"],
+                         W.bf16_bits_to_f32(cols["dy"]).astype(np.float64), D=t["D"][d:d + 1], z=cols["z"],
+                         delta_bias=t["delta_bias"][d:d + 1], delta_softplus=True)
+        for k in ("dx", "ddelta", "dz"):
+            assert_close(to_host(g[k][:, :, d]), ref[k][:, :, 0], TOL["bf16"], f"bwd {k} (d={d})")
+        assert_close(to_host(g["dA"][d]), ref["dA"][0], 1e-3, f"bwd dA (d={d})")
+        assert_close(to_host(g["dD"][d:d + 1]), ref["dD"], 1e-3, f"bwd dD (d={d})")
+        assert_close(to_host(g["ddelta_bias"][d:d + 1]), ref["ddelta_bias"], 1e-3, f"bwd ddelta_bias (d={d})")
