@@ -66,8 +66,12 @@ struct ScanArgs {
 
 constexpr int kChunk = 32;  // segment lengths are multiples of this (and so of every chunk size)
 constexpr int kIoWaves = 4; // waves per workgroup that load, prologue, epilogue and store
-constexpr int kDwPad = 2;   // float2 padding per LDS row of (dt, w)
-constexpr int kYpPad = 4;   // float padding per LDS row of partial read-outs
+// LDS rows are unpadded: every access to them is a whole 64-lane row (a scan wave's step) or a
+// contiguous run of one row (an IO thread's 16-byte pieces), so padding buys no bank spread.
+// Rows 512 bytes apart let a scan wave read two steps' (dt, dt x) with one ds_read2st64_b64
+// whose immediate offsets reach every step of a chunk (no per-pair address arithmetic).
+constexpr int kDwPad = 0;   // float2 padding per LDS row of (dt, w)
+constexpr int kYpPad = 0;   // float padding per LDS row of partial read-outs
 
 // LDS bytes of one workgroup: double-buffered (dt, dt x) tiles, plus (full scan only) the
 // double-buffered partial read-outs of the G scan waves.

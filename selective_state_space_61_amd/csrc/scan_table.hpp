@@ -34,8 +34,11 @@ void register_scan(ScanTable& m) {
   ScanVariants v{};
   v.full[0] = scan_chunk_kernel<BF16, N, NPL, MODE_FULL, 16>;
   v.agg[0] = scan_chunk_kernel<BF16, N, NPL, MODE_AGG, 16>;
-  if constexpr (scan_lds_bytes(G, true, 32) <= kLdsBudget) v.full[1] = scan_chunk_kernel<BF16, N, NPL, MODE_FULL, 32>;
-  if constexpr (scan_lds_bytes(G, false, 32) <= kLdsBudget) v.agg[1] = scan_chunk_kernel<BF16, N, NPL, MODE_AGG, 32>;
+  // 32-step tiles for at most 4 scan waves (8 would fill all 160 KB of LDS)
+  if constexpr (G <= 4 && scan_lds_bytes(G, true, 32) <= kLdsBudget)
+    v.full[1] = scan_chunk_kernel<BF16, N, NPL, MODE_FULL, 32>;
+  if constexpr (G <= 4 && scan_lds_bytes(G, false, 32) <= kLdsBudget)
+    v.agg[1] = scan_chunk_kernel<BF16, N, NPL, MODE_AGG, 32>;
   m[{N, NPL}] = v;
 }
 
