@@ -560,10 +560,10 @@ def profile_mode(args):
     log(f"[profile] {args.workload}: {res['kernel_ms'] * 1e3:.1f} us/launch over {args.steps} launches")
 
 
-def summarize_traffic(fetch_csv, write_csv, workload):
+def summarize_traffic(fetch_csv, write_csv, workload, out_dir=None):
     """Turns the two rocprofv3 --pmc CSVs (FETCH_SIZE, WRITE_SIZE; KiB per dispatch) into HBM bytes
     per scan launch, scaled by what the counters read for the calibration copy, and writes
-    profiles/traffic_<workload>.json."""
+    traffic_<workload>.json into out_dir (default: profiles/).  Returns the record."""
     import csv
     import workloads as W
 
@@ -606,9 +606,10 @@ def summarize_traffic(fetch_csv, write_csv, workload):
            "calibration_fetch_kib": max(fetch[ck]), "calibration_write_kib": max(write[ck]),
            "fetch_scale": f_scale[0], "write_scale": f_scale[1],
            "hbm_bytes_per_launch": hbm, "alg_bytes_per_launch": alg, "ratio_to_algorithmic": hbm / alg}
-    out = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    out = os.path.join(out_dir or os.path.join(ROOT, "profiles"), f"traffic_{workload}.json")
     json.dump(rec, open(out, "w"), indent=2)
     print(json.dumps(rec, indent=2))
+    return rec
 
 
 def main():
