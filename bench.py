@@ -28,7 +28,10 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0                       # MI355X HBM3E, published
 VALU_LANE_SLOTS = 256 * 4 * 16 * 2.4e9        # CUs x SIMDs x lanes x clock: fp32 VALU issue slots/s (non-packed)
-SLOTS_PER_UPDATE = 6                          # per (t,d,n): 2 mul + 2 fma + v_exp_f32 at half rate (2 slots)
+# The method's own fp32 VALU work, in issue slots (an FMA counts once; v_exp_f32 issues at half rate,
+# measured on MI355X, so it takes 2 slots):
+SLOTS_PER_UPDATE = 6   # per (t,d,n): dt*A, v_exp_f32 (2), B*(dt x), the state FMA, the read-out FMA
+SLOTS_PER_TD = 14      # per (t,d): softplus and SiLU (2 transcendentals each, 2 slots apiece) + ~6 ops
 MALL_BYTES = 256 << 20
 _CSRC = "selective_state_space_61_amd/csrc/"
 # the sources each measured kernel is compiled from; a traffic record is used only while they are
@@ -54,6 +57,11 @@ def source_hash(family: str = "scan") -> str:
 def scan_bytes(batch, L, dim, N, es, has_z=True):
     per_td = (4 if has_z else 3) * es          # x, delta, (z), y
     return batch * L * dim * per_td + 2 * batch * L * N * es + 4 * dim * N + 8 * dim + 4 * batch * dim * N
+
+
+def method_slots(elems, N):
+    """fp32 VALU issue slots the method itself needs for `elems` (b,t,d) elements of state size N."""
+    return elems * (SLOTS_PER_UPDATE * N + SLOTS_PER_TD)
 
 
 def decode_bytes_per_step(batch, dim, N, es):
@@ -116,7 +124,8 @@ def bench_scan(name, steps, warmup, torch, np, W, ssm, device, zoh=False):
         "kernel_ms_median": sorted(per)[len(per) // 2], "kernel_ms_min": min(per),
         "elems_per_s": elems / (ms_step * 1e-3), "alg_bytes": set_bytes,
         "hbm_gbps": set_bytes / (kern_ms * 1e-3) / 1e9,
-        "valu_slot_frac": SLOTS_PER_UPDATE * updates / (kern_ms * 1e-3) / VALU_LANE_SLOTS,
+        "valu_slot_frac": method_slots(elems, w.dstate) / (kern_ms * 1e-3) / VALU_LANE_SLOTS,
+        "delta_softplus": bool(w.delta_softplus), "gate": bool(w.has_z),
     }
     res["hbm_frac"] = res["hbm_gbps"] / HBM_PEAK_GBPS
     del sets
@@ -526,6 +535,16 @@ def traffic_from_profiles(name, alg_bytes):
     return rec["hbm_bytes_per_launch"], rec
 
 
+def valu_from_profiles(name):
+    """VALU instructions per update counted by rocprofv3 (profiles/valu_<workload>.json), if the
+    scan kernel's sources have not changed since."""
+    p = os.path.join(ROOT, "profiles", f"valu_{name}.json")
+    if not os.path.exists(p):
+        return None
+    rec = json.load(open(p))
+    return rec if rec.get("source_hash") == source_hash("scan") else None
+
+
 CALIB_BYTES = 512 << 20
 
 
@@ -697,18 +716,26 @@ def main():
             f"{extra['ssd_decode']['hbm_gbps']:.0f} GB/s")
 
     hbm_frac = main_res["hbm_frac"]
-    alu_frac = main_res["valu_slot_frac"]
     traffic, trec = traffic_from_profiles(args.workload, main_res["alg_bytes"])
-    if alu_frac >= hbm_frac:
-        roof = {"bound": "alu", "achieved": SLOTS_PER_UPDATE * main_res["batch"] * main_res["seqlen"] * main_res["dim"]
-                * main_res["dstate"] / (main_res["kernel_ms"] * 1e-3) / 1e12,
-                "peak": VALU_LANE_SLOTS / 1e12, "unit": "TFLOP/s", "frac": alu_frac}
-        roof["note"] = ("fp32 VALU issue slots: 6 per (t,d,n) update (2 mul + 2 fma + v_exp_f32 at half rate); "
-                        "peak = 256 CU x 64 lanes x 2.4 GHz (packed fp32 disabled); HBM side: "
-                        f"{main_res['hbm_gbps']:.0f} GB/s = {hbm_frac:.3f} of 8 TB/s")
-    else:
-        roof = {"bound": "hbm", "achieved": main_res["hbm_gbps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": hbm_frac}
+    # The binding roofline is HBM (the method's IO argument: every input read once, every output
+    # written once).  The fp32 VALU is a co-bound, reported beside it: the method's own slots per
+    # update, and, while the kernel is unchanged since they were counted, the VALU instructions
+    # rocprofv3 counted per update (SQ_INSTS_VALU x 64 lanes / updates).
+    roof = {"bound": "hbm", "achieved": main_res["hbm_gbps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": hbm_frac}
+    n_upd = main_res["batch"] * main_res["seqlen"] * main_res["dim"] * main_res["dstate"]
+    slots = method_slots(main_res["batch"] * main_res["seqlen"] * main_res["dim"], main_res["dstate"])
+    valu = {"method_slots_per_update": slots / n_upd,
+            "achieved_tslots_per_s": slots / (main_res["kernel_ms"] * 1e-3) / 1e12,
+            "peak_tslots_per_s": VALU_LANE_SLOTS / 1e12, "frac": main_res["valu_slot_frac"],
+            "floor_us": slots / VALU_LANE_SLOTS * 1e6,
+            "note": (f"per (t,d,n) {SLOTS_PER_UPDATE} slots (v_exp_f32 at half rate = 2), per (t,d) {SLOTS_PER_TD}; "
+                     "peak = 256 CU x 4 SIMD x 16 lanes x 2.4 GHz (packed fp32 off); an FMA counts once")}
+    vrec = valu_from_profiles(args.workload)
+    if vrec:
+        valu["measured_valu_insts_per_update"] = vrec["valu_insts_per_update"]
+        valu["measured_source_hash"] = vrec["source_hash"]
+    roof["valu_cobound"] = valu
     roof["traffic"] = traffic
     roof["hbm_gbps"] = main_res["hbm_gbps"]
     roof["hbm_frac"] = hbm_frac
@@ -726,7 +753,8 @@ def main():
         "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": args.workload, "batch": main_res["batch"], "seqlen": main_res["seqlen"],
                    "dim": main_res["dim"], "dstate": main_res["dstate"], "io_dtype": main_res["io_dtype"],
-                   "state_dtype": "f32", "delta_softplus": True, "gate": True,
+                   "state_dtype": "f32", "delta_softplus": main_res["delta_softplus"],
+                   "gate": main_res["gate"],
                    "rotated_input_sets": main_res["rotated_input_sets"]},
         "roofline": roof,
     }

@@ -100,11 +100,13 @@ typedef enum {
  * For small batch*dim the sequence is split into segments scanned in
  * parallel and joined by a carry pass; that needs (segments * batch * dim *
  * (dstate + 1)) fp32 of device scratch.  The library keeps one such buffer
- * per (device, stream), allocated with hipMalloc on first need, grown when a
- * larger call needs it (after synchronising that stream) and kept until the
- * process ends.  A call that would allocate must not be captured into a HIP
- * graph; calls on one stream reuse its buffer in stream order, and calls on
- * different streams never share one.
+ * per (device, stream), allocated with hipMalloc on first need and replaced
+ * by a larger one when a larger call needs it.  A replaced buffer is never
+ * freed (work already enqueued, or a graph captured earlier, may still hold
+ * its address); it stays allocated until the process ends.  A call that
+ * would allocate must not be captured into a HIP graph; calls on one stream
+ * reuse its buffer in stream order, and calls on different streams never
+ * share one.
  */
 SSM_API ssm_status_t ssm_scan_fwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, ssm_dtype_t dtype,
                           const void *x, const void *delta, const float *A, const void *B, const void *C,

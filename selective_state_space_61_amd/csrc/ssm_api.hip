@@ -8,6 +8,7 @@
 #include <map>
 #include <mutex>
 #include <utility>
+#include <vector>
 
 #include "../../include/ssm.h"
 #include "scan_table.hpp"
@@ -169,12 +170,17 @@ __global__ void fill_zero_kernel(float* p, int64_t n) {
 }
 
 // ---- segment scratch: one growable device buffer per (device, stream) ----------------------------
+// A buffer that a larger call outgrows is retired, never freed: work already enqueued, or a graph
+// captured earlier on that stream, may still hold its address, so freeing it could let a later
+// replay write to memory that belongs to someone else.  Retired buffers live until the process
+// ends (each is at most the size of the largest call before it).
 struct Scratch {
   float* ptr = nullptr;
   int64_t floats = 0;
 };
 std::mutex g_scratch_mu;
 std::map<std::pair<int, uintptr_t>, Scratch> g_scratch;
+std::vector<void*> g_retired;
 
 ssm_status_t get_scratch(hipStream_t stream, int64_t floats, float** out) {
   int dev = 0;
@@ -183,18 +189,10 @@ ssm_status_t get_scratch(hipStream_t stream, int64_t floats, float** out) {
   std::lock_guard<std::mutex> lock(g_scratch_mu);
   Scratch& s = g_scratch[{dev, reinterpret_cast<uintptr_t>(stream)}];
   if (s.floats < floats) {
-    if (s.ptr) {
-      // earlier work on this stream may still read the old buffer
-      e = hipStreamSynchronize(stream);
-      if (e != hipSuccess) return fail(SSM_ERR_HIP, "hipStreamSynchronize: %s", hipGetErrorString(e));
-      e = hipFree(s.ptr);
-      s.ptr = nullptr;
-      s.floats = 0;
-      if (e != hipSuccess) return fail(SSM_ERR_HIP, "hipFree: %s", hipGetErrorString(e));
-    }
     void* p = nullptr;
     e = hipMalloc(&p, static_cast<size_t>(floats) * sizeof(float));
     if (e != hipSuccess) return fail(SSM_ERR_HIP, "hipMalloc(%lld floats): %s", (long long)floats, hipGetErrorString(e));
+    if (s.ptr) g_retired.push_back(s.ptr);
     s.ptr = static_cast<float*>(p);
     s.floats = floats;
   }

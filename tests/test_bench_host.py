@@ -84,3 +84,13 @@ def test_traffic_summary_scales_by_the_calibration_copy(tmp_path):
     assert rec["alg_bytes_per_launch"] == 203_272_192
     assert rec["source_hash"] == bench.source_hash("scan")
     assert json.load(open(tmp_path / "traffic_mamba130m.json")) == rec
+
+
+def test_method_slots_term_by_term():
+    """The VALU co-bound's method work: 6 slots per (t,d,n) update (dt*A, v_exp_f32 at half rate,
+    B*(dt x), the state FMA, the read-out FMA) and 14 per (t,d) (softplus and SiLU)."""
+    elems, n = 8 * 2048 * 1536, 16
+    per_update = 1 + 2 + 1 + 1 + 1
+    assert bench.SLOTS_PER_UPDATE == per_update
+    assert bench.method_slots(elems, n) == elems * n * per_update + elems * bench.SLOTS_PER_TD
+    assert abs(bench.method_slots(elems, n) / (elems * n) - 6.875) < 1e-12

@@ -51,3 +51,47 @@ def test_decode_graph_replays_match_eager():
         run(tmp, torch.empty_like(ys_e))
         torch.cuda.synchronize()
         say(f"  replay {rep} matches eager")
+
+
+def test_split_scan_graph_survives_scratch_growth():
+    """A split-sequence scan captured in a graph keeps working after a larger eager call on the
+    same stream has replaced the stream's scratch buffer (the old buffer is retired, not freed)."""
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import selective_state_space_61_amd as ssm
+    small = {k: to_dev(v) for k, v in W.scan_inputs(1, 900, 96, 16, "f32", seed=31).items()}
+    large = {k: to_dev(v) for k, v in W.scan_inputs(2, 1500, 200, 16, "f32", seed=32).items()}
+
+    def call(d, y, st):
+        ssm.ssm_scan_fwd(d["x"], d["delta"], d["A"], d["B"], d["C"], D=d["D"], z=d["z"],
+                         delta_bias=d["delta_bias"], delta_softplus=True, y=y, last_state=st, segments=4)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    ys, ss = torch.empty_like(small["x"]), torch.empty(1, 96, 16, device="cuda")
+    yl, sl = torch.empty_like(large["x"]), torch.empty(2, 200, 16, device="cuda")
+    with torch.cuda.stream(side):
+        call(small, ys, ss)                       # allocates the side stream's scratch
+    torch.cuda.synchronize()
+    ys_e, ss_e = ys.clone(), ss.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            call(small, ys, ss)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(side):
+        call(large, yl, sl)                       # needs more scratch: the buffer is replaced
+    torch.cuda.synchronize()
+    yl_e, sl_e = yl.clone(), sl.clone()
+    for rep in range(3):
+        ys.fill_(0)
+        ss.fill_(0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(ys, ys_e) and torch.equal(ss, ss_e), f"replay {rep} differs from eager"
+        with torch.cuda.stream(side):
+            call(large, yl, sl)
+        torch.cuda.synchronize()
+        assert torch.equal(yl, yl_e) and torch.equal(sl, sl_e), f"eager call after replay {rep} differs"
+        say(f"  replay {rep} after scratch growth matches eager")
