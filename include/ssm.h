@@ -157,6 +157,35 @@ SSM_API ssm_status_t ssm_scan_fwd_ex(int64_t batch, int64_t seqlen, int64_t dim,
                              void *y, float *last_state, void *stream, const ssm_scan_opts_t *opts);
 
 /*
+ * ssm_scan_fwd_ex for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, layouts, validation and results as ssm_scan_fwd_ex (the
+ * same kernels run, so the outputs are bit-identical); it calls no hipMalloc,
+ * hipFree or other allocating routine.
+ *
+ * The split-sequence path's segment summaries (segments * batch * dim *
+ * (dstate + 1) fp32, see ssm_scan_fwd) go to a file-scope device array of
+ * 2^22 fp32 (16 MiB) that each GPU the library runs on holds until the
+ * process ends.  A call that needs more gives SSM_ERR_UNSUPPORTED before any
+ * launch; the automatic launch shape needs at most about 2.8 M fp32 for every
+ * supported dstate, so only forced segment counts (opts->segments) on large
+ * batch * dim can exceed it.  Nothing in the array needs to start at zero:
+ * every call writes each summary before reading it.
+ *
+ * Every call on one GPU shares that GPU's array, which keeps the last call's
+ * contents: calls that may overlap on one GPU (different streams, or
+ * different host threads, without ordering between them) race on it and
+ * give wrong results.  Order them on one stream, or use ssm_scan_fwd_ex.
+ * The first call on a device looks the array's address up
+ * (hipGetSymbolAddress) and caches it; an error there gives SSM_ERR_HIP.
+ */
+SSM_API ssm_status_t ssm_scan_fwd_noalloc(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
+                                  ssm_dtype_t dtype, const void *x, const void *delta, const float *A,
+                                  const void *B, const void *C, const float *D, const void *z,
+                                  const float *delta_bias, int delta_softplus, void *y, float *last_state,
+                                  void *stream, const ssm_scan_opts_t *opts);
+
+/*
  * One single-token decode step ("Mamba 论文精读" sec. 6: O(1) work per token
  * with a fixed-size state; sec. 2.2: the recurrence).
  *

@@ -28,7 +28,7 @@ LIBRARY = os.path.join(_HERE, "libssm61.so")
 SSM_F32, SSM_BF16 = 0, 1
 STATUS_NAMES = {0: "SSM_OK", 1: "SSM_ERR_INVALID_ARG", 2: "SSM_ERR_UNSUPPORTED", 3: "SSM_ERR_MISALIGNED",
                 4: "SSM_ERR_HIP"}
-EXPORTED = ("ssm_scan_fwd", "ssm_scan_fwd_ex", "ssm_scan_bwd", "ssm_state_update", "ssm_state_update_ex",
+EXPORTED = ("ssm_scan_fwd", "ssm_scan_fwd_ex", "ssm_scan_fwd_noalloc", "ssm_scan_bwd", "ssm_state_update", "ssm_state_update_ex",
             "ssm_causal_conv1d_fwd",
             "ssm_causal_conv1d_update", "ssm_ssd_fwd", "ssm_ssd_state_update", "ssm_status_string", "ssm_last_error", "ssm_abi_version")
 
@@ -71,6 +71,8 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
     lib.ssm_scan_fwd.restype = i32
     lib.ssm_scan_fwd_ex.argtypes = lib.ssm_scan_fwd.argtypes + [ctypes.POINTER(ScanOpts)]
     lib.ssm_scan_fwd_ex.restype = i32
+    lib.ssm_scan_fwd_noalloc.argtypes = lib.ssm_scan_fwd_ex.argtypes
+    lib.ssm_scan_fwd_noalloc.restype = i32
     lib.ssm_state_update.argtypes = [i64, i64, i64, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp]
     lib.ssm_state_update.restype = i32
     lib.ssm_state_update_ex.argtypes = lib.ssm_state_update.argtypes + [ctypes.POINTER(UpdateOpts)]
@@ -141,7 +143,8 @@ def ssm_scan_fwd(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch
                  delta_bias: Optional[torch.Tensor] = None, delta_softplus: bool = False, *,
                  y: Optional[torch.Tensor] = None, last_state: Optional[torch.Tensor] = None,
                  return_last_state: bool = True, chains_per_lane: int = 0, segments: int = 0,
-                 chunk_steps: int = 0, zoh: bool = False, stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+                 chunk_steps: int = 0, zoh: bool = False, stream=None,
+                 _noalloc: bool = False) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Selective scan forward (include/ssm.h: ssm_scan_fwd).  Returns (y, last_state); last_state
     is None when return_last_state is False and none was passed in.  chains_per_lane, segments
     and chunk_steps override the launch shape (0 = automatic); zoh selects the exact
@@ -169,11 +172,27 @@ def ssm_scan_fwd(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch
     _need(last_state, "last_state", (batch, dim, dstate), torch.float32, dev, optional=True)
     opts = ScanOpts(int(chains_per_lane), int(segments), int(chunk_steps),
                     SSM_BBAR_ZOH if zoh else SSM_BBAR_DELTA_B)
-    status = lib.ssm_scan_fwd_ex(batch, seqlen, dim, dstate, code, _ptr(x), _ptr(delta), _ptr(A), _ptr(B),
-                                 _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias), int(bool(delta_softplus)), _ptr(y),
-                                 _ptr(last_state), _stream(dev, stream), ctypes.byref(opts))
+    entry = lib.ssm_scan_fwd_noalloc if _noalloc else lib.ssm_scan_fwd_ex
+    status = entry(batch, seqlen, dim, dstate, code, _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+                   _ptr(z), _ptr(delta_bias), int(bool(delta_softplus)), _ptr(y), _ptr(last_state),
+                   _stream(dev, stream), ctypes.byref(opts))
     _check(status)
     return y, last_state
+
+
+def ssm_scan_fwd_noalloc(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Tensor,
+                         C: torch.Tensor, D: Optional[torch.Tensor] = None, z: Optional[torch.Tensor] = None,
+                         delta_bias: Optional[torch.Tensor] = None, delta_softplus: bool = False, *,
+                         y: torch.Tensor, last_state: Optional[torch.Tensor] = None, chains_per_lane: int = 0,
+                         segments: int = 0, chunk_steps: int = 0, zoh: bool = False,
+                         stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """The allocation-free scan (include/ssm.h: ssm_scan_fwd_noalloc): the caller passes y (and
+    last_state, or None) and nothing is allocated, by this binding or by the library."""
+    if y is None:
+        raise ValueError("y is required: the allocation-free scan allocates no output")
+    return ssm_scan_fwd(x, delta, A, B, C, D=D, z=z, delta_bias=delta_bias, delta_softplus=delta_softplus, y=y,
+                        last_state=last_state, return_last_state=False, chains_per_lane=chains_per_lane,
+                        segments=segments, chunk_steps=chunk_steps, zoh=zoh, stream=stream, _noalloc=True)
 
 
 def ssm_state_update(state: torch.Tensor, x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor,

@@ -225,11 +225,23 @@ const char* ssm_last_error(void) { return g_err; }
 
 int ssm_abi_version(void) { return SSM_ABI_VERSION; }
 
-ssm_status_t ssm_scan_fwd_ex(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, ssm_dtype_t dtype,
-                             const void* x, const void* delta, const float* A, const void* B, const void* C,
-                             const float* D, const void* z, const float* delta_bias, int delta_softplus,
-                             void* y, float* last_state, void* stream, const ssm_scan_opts_t* opts) {
-  g_err[0] = '\0';
+}  // extern "C"
+
+namespace {
+
+// Where the split-sequence scan's segment summaries go: the per-(device, stream) buffer of
+// get_scratch (fixed == nullptr), or a caller-provided buffer of fixed_floats fp32 (the
+// allocation-free entry point), in which case nothing is allocated and a call needing more is
+// rejected before any launch.
+struct ScratchSource {
+  float* fixed;
+  int64_t fixed_floats;
+};
+
+ssm_status_t scan_fwd_impl(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, ssm_dtype_t dtype,
+                           const void* x, const void* delta, const float* A, const void* B, const void* C,
+                           const float* D, const void* z, const float* delta_bias, int delta_softplus, void* y,
+                           float* last_state, void* stream, const ssm_scan_opts_t* opts, ScratchSource src) {
   if (batch < 0 || seqlen < 0 || dim < 0 || dstate < 0)
     return fail(SSM_ERR_INVALID_ARG, "negative size (batch=%lld seqlen=%lld dim=%lld dstate=%lld)",
                 (long long)batch, (long long)seqlen, (long long)dim, (long long)dstate);
@@ -356,8 +368,17 @@ ssm_status_t ssm_scan_fwd_ex(int64_t batch, int64_t seqlen, int64_t dim, int64_t
   if (nseg > 1) {
     float* scratch = nullptr;
     const int64_t floats = nseg * nch * (dstate + 1);
-    ssm_status_t s = get_scratch(st, floats, &scratch);
-    if (s != SSM_OK) return s;
+    ssm_status_t s;
+    if (src.fixed) {
+      if (floats > src.fixed_floats)
+        return fail(SSM_ERR_UNSUPPORTED,
+                    "the split scan needs %lld fp32 of scratch (%lld segments x %lld channels x (dstate + 1)); "
+                    "the allocation-free entry point has %lld",
+                    (long long)floats, (long long)nseg, (long long)nch, (long long)src.fixed_floats);
+      scratch = src.fixed;
+    } else if ((s = get_scratch(st, floats, &scratch)) != SSM_OK) {
+      return s;
+    }
     a.seg_state = scratch;
     a.seg_dsum = scratch + nseg * nch * dstate;
     hipLaunchKernelGGL(k_agg, dim3(static_cast<unsigned>(base_wgs * (nseg - 1))), dim3(threads), 0, st, a);
@@ -368,6 +389,63 @@ ssm_status_t ssm_scan_fwd_ex(int64_t batch, int64_t seqlen, int64_t dim, int64_t
   }
   hipLaunchKernelGGL(k_full, dim3(static_cast<unsigned>(grid)), dim3(threads), 0, st, a);
   return check_launch("scan");
+}
+
+}  // namespace
+
+// ---- the allocation-free scan: scratch in a file-scope device array ------------------------------
+// Each GPU the library runs on holds its own copy for the life of the process.  Host code must not
+// use the array's name as an address (on the host it is only a stand-in for the symbol): the
+// device address comes from hipGetSymbolAddress, taken once per device with that device current.
+constexpr int64_t kNoAllocScratchFloats = int64_t{1} << 22;  // 16 MiB
+static __device__ __align__(256) float scratch[kNoAllocScratchFloats];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_noalloc_mu;
+float* g_noalloc_ptr[kMaxDevices] = {};
+
+ssm_status_t noalloc_scratch(float** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(SSM_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(SSM_ERR_UNSUPPORTED, "device %d beyond %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_noalloc_mu);
+  if (!g_noalloc_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(SSM_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+    g_noalloc_ptr[dev] = static_cast<float*>(p);
+  }
+  *out = g_noalloc_ptr[dev];
+  return SSM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+ssm_status_t ssm_scan_fwd_ex(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, ssm_dtype_t dtype,
+                             const void* x, const void* delta, const float* A, const void* B, const void* C,
+                             const float* D, const void* z, const float* delta_bias, int delta_softplus,
+                             void* y, float* last_state, void* stream, const ssm_scan_opts_t* opts) {
+  g_err[0] = '\0';
+  return scan_fwd_impl(batch, seqlen, dim, dstate, dtype, x, delta, A, B, C, D, z, delta_bias, delta_softplus, y,
+                       last_state, stream, opts, ScratchSource{nullptr, 0});
+}
+
+ssm_status_t ssm_scan_fwd_noalloc(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, ssm_dtype_t dtype,
+                                  const void* x, const void* delta, const float* A, const void* B, const void* C,
+                                  const float* D, const void* z, const float* delta_bias, int delta_softplus,
+                                  void* y, float* last_state, void* stream, const ssm_scan_opts_t* opts) {
+  g_err[0] = '\0';
+  float* ptr = nullptr;
+  const ssm_status_t s = noalloc_scratch(&ptr);
+  if (s != SSM_OK) return s;
+  return scan_fwd_impl(batch, seqlen, dim, dstate, dtype, x, delta, A, B, C, D, z, delta_bias, delta_softplus, y,
+                       last_state, stream, opts, ScratchSource{ptr, kNoAllocScratchFloats});
 }
 
 ssm_status_t ssm_scan_fwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, ssm_dtype_t dtype,
