@@ -11,10 +11,9 @@
 //
 // Both kernels stream: every input element is read once (plus a K-1 row halo per time tile,
 // which the L2 serves) and every output written once (non-temporally), so HBM bandwidth is the
-// bound.  A thread
-// owns VEC consecutive channels (one 16-byte access per row) and kConvTile consecutive steps,
-// keeps the K-1 previous inputs in registers, and issues kConvUnroll row loads before using
-// any of them.
+// bound.  A thread owns VEC consecutive channels, one kConvVecBytes-byte (4-byte) access per
+// row, and kConvTile consecutive steps; it keeps the K-1 previous inputs in registers and issues
+// kConvUnroll row loads before using any of them.
 #pragma once
 
 #include "ssm_device.hpp"
@@ -34,7 +33,7 @@ struct ConvArgs {
   int64_t ncv;     // channel vectors per row: ceil(dim / VEC)
   int64_t ntiles;  // time tiles per batch row (at least 1)
   int32_t silu;
-  int32_t vec_ok;  // x / y rows allow aligned 16-byte access
+  int32_t vec_ok;  // x / y rows allow the aligned kConvVecBytes-byte access
 };
 
 struct ConvUpdateArgs {
@@ -82,7 +81,8 @@ __device__ __forceinline__ void store_row_stream(void* base, int64_t idx, const 
 
 template <bool BF16, int K, bool FAST>
 __device__ __forceinline__ void conv_tile(const ConvArgs& p, int64_t b, int64_t d0, int nv, int64_t t0, int64_t t1) {
-  // FAST: all VEC channels valid, rows allow 16-byte access, and the tile is whole (no checks)
+  // FAST: all VEC channels valid, rows allow the aligned vector access, and the tile is whole
+  // (no checks)
   constexpr int VEC = kConvVec<BF16>;
   constexpr int W = K > 1 ? K - 1 : 1;  // window slots (unused when K == 1)
   const bool vec = FAST || (p.vec_ok != 0 && nv == VEC);
