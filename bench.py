@@ -37,7 +37,8 @@ _CSRC = "selective_state_space_61_amd/csrc/"
 # the sources each measured kernel is compiled from; a traffic record is used only while they are
 # unchanged (launch shapes live in ssm_api.hip and are re-measured whenever they change)
 KERNEL_SOURCES = {
-    "scan": [_CSRC + f for f in ("scan_fwd.hpp", "scan_table.hpp", "scan_bf16.hip", "scan_f32.hip", "ssm_device.hpp")],
+    "scan": [_CSRC + f for f in ("scan_fwd.hpp", "scan_table.hpp", "scan_bf16.hip", "scan_f32.hip", "ssm_device.hpp",
+                                 "scan_rows.hpp", "scan_rows.hip")],
     "conv": [_CSRC + f for f in ("conv1d.hpp", "ssm_device.hpp")],
     "ssd": [_CSRC + f for f in ("ssd_fwd.hpp", "ssd_bf16.hip", "ssm_device.hpp")],
 }
@@ -92,20 +93,27 @@ def time_calls(torch, fn, n_calls, warmup):
     return ev[0].elapsed_time(ev[-1]), per
 
 
-def bench_scan(name, steps, warmup, torch, np, W, ssm, device, zoh=False):
+def prepare_scan(name, torch, np, W, device):
+    """The workload's input sets, resident in HBM: as many copies as it takes to exceed twice the
+    256 MB Infinity Cache, so that consecutive calls cannot be served from it."""
     w = W.WORKLOADS[name]
     es = 2 if w.dtype == "bf16" else 4
     t = W.workload_inputs(w)
-    one = dev_tensor
     set_bytes = scan_bytes(w.batch, w.seqlen, w.dim, w.dstate, es)
     copies = max(1, min(4, math.ceil(2 * MALL_BYTES / set_bytes)))
     sets = []
     for c in range(copies):
-        d = {k: one(v, torch, np, device) for k, v in t.items()}
+        d = {k: dev_tensor(v, torch, np, device) for k, v in t.items()}
         d["y"] = torch.empty_like(d["x"])
         d["st"] = torch.empty(w.batch, w.dim, w.dstate, device=device)
         sets.append(d)
-    del t
+    return {"name": name, "w": w, "sets": sets, "set_bytes": set_bytes}
+
+
+def bench_scan(name, steps, warmup, torch, np, W, ssm, device, zoh=False, prepared=None):
+    prep = prepared or prepare_scan(name, torch, np, W, device)
+    w, sets, set_bytes = prep["w"], prep["sets"], prep["set_bytes"]
+    copies = len(sets)
 
     def call(i):
         d = sets[i % copies]
@@ -117,7 +125,6 @@ def bench_scan(name, steps, warmup, torch, np, W, ssm, device, zoh=False):
     ms_step = total_ms / steps
     kern_ms = sum(per) / len(per)
     elems = w.batch * w.seqlen * w.dim
-    updates = elems * w.dstate
     res = {
         "workload": name, "batch": w.batch, "seqlen": w.seqlen, "dim": w.dim, "dstate": w.dstate,
         "io_dtype": w.dtype, "rotated_input_sets": copies, "ms_per_step": ms_step, "kernel_ms": kern_ms,
@@ -128,8 +135,9 @@ def bench_scan(name, steps, warmup, torch, np, W, ssm, device, zoh=False):
         "delta_softplus": bool(w.delta_softplus), "gate": bool(w.has_z),
     }
     res["hbm_frac"] = res["hbm_gbps"] / HBM_PEAK_GBPS
-    del sets
-    torch.cuda.empty_cache()
+    if prepared is None:
+        del sets, prep
+        torch.cuda.empty_cache()
     return res
 
 
@@ -596,8 +604,9 @@ def summarize_traffic(fetch_csv, write_csv, workload, out_dir=None):
     fetch, write = per_kernel(fetch_csv, "FETCH_SIZE"), per_kernel(write_csv, "WRITE_SIZE")
     family = "conv" if workload == "conv" else "ssd" if workload in W.SSD_WORKLOADS else "scan"
     calib = [k for k in fetch if "copy" in k.lower()]
-    marker = {"conv": "causal_conv1d_kernel", "ssd": "ssd_chunk_kernel", "scan": "scan_chunk_kernel"}[family]
-    scan = [k for k in fetch if marker in k]
+    markers = {"conv": ("causal_conv1d_kernel",), "ssd": ("ssd_chunk_kernel",),
+               "scan": ("scan_chunk_kernel", "scan_rows_kernel")}[family]
+    scan = [k for k in fetch if any(m in k for m in markers)]
     if not calib or not scan:
         raise SystemExit(f"calibration or measured kernel missing in {fetch_csv}: {list(fetch)}")
     ck = calib[0]
@@ -675,30 +684,31 @@ def main():
     torch.cuda.set_device(device)
     log(f"[bench] {torch.cuda.get_device_name(0)}; workload {args.workload}; steps {args.steps}; warmup {args.warmup}")
 
-    main_res = bench_scan(args.workload, args.steps, args.warmup, torch, np, W, ssm, device)
-    log(f"[bench] {args.workload}: {main_res['kernel_ms'] * 1e3:.1f} us/launch, {main_res['hbm_gbps']:.0f} GB/s, "
-        f"VALU slots {main_res['valu_slot_frac']:.3f}")
-
+    # The GPU's clocks ramp over the first ~15 ms of sustained load and drop again within about a
+    # second of idling (measured: 5 warmup calls after idling give the 130M shape ~155 us, 100 give
+    # ~143 us).  So the headline workload's inputs are generated and moved to HBM first, the context
+    # measurements run next, and the headline's W warmup and K timed steps follow them directly, at
+    # the steady clocks that a model's back-to-back layers see.  The context measurements take
+    # warmups of about 20 ms of their own.
+    main_prep = prepare_scan(args.workload, torch, np, W, device)
     extra = {}
     if not args.no_extra:
-        if args.workload != "mamba2p8b":
-            extra["mamba2p8b"] = bench_scan("mamba2p8b", max(10, args.steps // 2), 3, torch, np, W, ssm, device)
-            log(f"[bench] mamba2p8b: {extra['mamba2p8b']['kernel_ms'] * 1e3:.1f} us/launch")
         if args.workload != "genomics":
-            extra["genomics"] = bench_scan("genomics", 8, 4, torch, np, W, ssm, device)
+            extra["genomics"] = bench_scan("genomics", 8, 12, torch, np, W, ssm, device)
             log(f"[bench] genomics (1 x 2^20 x 256, fp32, split sequence): "
                 f"{extra['genomics']['kernel_ms'] * 1e3:.1f} us/call, {extra['genomics']['hbm_gbps']:.0f} GB/s")
+        if args.workload != "mamba2p8b":
+            extra["mamba2p8b"] = bench_scan("mamba2p8b", max(10, args.steps // 2), 100, torch, np, W, ssm, device)
+            log(f"[bench] mamba2p8b: {extra['mamba2p8b']['kernel_ms'] * 1e3:.1f} us/launch")
         extra["decode_mall_resident"] = bench_decode(256, torch, np, W, ssm, device, ring=1)
         extra["decode_hbm_ring26"] = bench_decode(256, torch, np, W, ssm, device, ring=26)
         log(f"[bench] decode: {extra['decode_hbm_ring26']['updates_per_s']:.3e} updates/s (ring of 26 states)")
-        zres = bench_scan(args.workload, max(10, args.steps // 2), 3, torch, np, W, ssm, device, zoh=True)
-        extra["scan_fwd_exact_zoh"] = {"kernel_ms": zres["kernel_ms"], "elems_per_s": zres["elems_per_s"],
-                                       "vs_delta_b": zres["kernel_ms"] / main_res["kernel_ms"]}
+        zres = bench_scan(args.workload, max(10, args.steps // 2), 50, torch, np, W, ssm, device, zoh=True,
+                          prepared=main_prep)
+        extra["scan_fwd_exact_zoh"] = {"kernel_ms": zres["kernel_ms"], "elems_per_s": zres["elems_per_s"]}
         log(f"[bench] {args.workload} with exact ZOH Bbar: {zres['kernel_ms'] * 1e3:.1f} us/launch")
-        extra["scan_bwd"] = bench_scan_bwd(max(6, args.steps // 5), 2, torch, np, W, ssm, device)
-        extra["scan_bwd"]["fwd_equiv"] = extra["scan_bwd"]["ms_per_call"] / main_res["kernel_ms"]
-        log(f"[bench] scan backward (130M shape): {extra['scan_bwd']['ms_per_call'] * 1e3:.1f} us/call "
-            f"({extra['scan_bwd']['fwd_equiv']:.2f}x the forward)")
+        extra["scan_bwd"] = bench_scan_bwd(max(6, args.steps // 5), 20, torch, np, W, ssm, device)
+        log(f"[bench] scan backward (130M shape): {extra['scan_bwd']['ms_per_call'] * 1e3:.1f} us/call")
         extra["causal_conv1d"] = bench_conv(max(10, args.steps // 2), 3, torch, np, W, ssm, device)
         extra["causal_conv1d"]["traffic"] = traffic_from_profiles("conv", extra["causal_conv1d"]["alg_bytes"])[0]
         log(f"[bench] causal conv1d: {extra['causal_conv1d']['kernel_ms'] * 1e3:.1f} us/launch, "
@@ -715,6 +725,14 @@ def main():
         log(f"[bench] SSD decode step (64 x 64 heads x 64 x 128): {extra['ssd_decode']['ms_per_step'] * 1e3:.1f} us, "
             f"{extra['ssd_decode']['hbm_gbps']:.0f} GB/s")
 
+    main_res = bench_scan(args.workload, args.steps, args.warmup, torch, np, W, ssm, device, prepared=main_prep)
+    log(f"[bench] {args.workload}: {main_res['kernel_ms'] * 1e3:.1f} us/launch, {main_res['hbm_gbps']:.0f} GB/s, "
+        f"VALU slots {main_res['valu_slot_frac']:.3f}")
+
+    if "scan_fwd_exact_zoh" in extra:
+        extra["scan_fwd_exact_zoh"]["vs_delta_b"] = extra["scan_fwd_exact_zoh"]["kernel_ms"] / main_res["kernel_ms"]
+    if "scan_bwd" in extra:
+        extra["scan_bwd"]["fwd_equiv"] = extra["scan_bwd"]["ms_per_call"] / main_res["kernel_ms"]
     hbm_frac = main_res["hbm_frac"]
     traffic, trec = traffic_from_profiles(args.workload, main_res["alg_bytes"])
     # The binding roofline is HBM (the method's IO argument: every input read once, every output

@@ -68,7 +68,7 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 1
+#define SSM_ABI_VERSION 2
 
 #if defined(__GNUC__)
 #define SSM_API __attribute__((visibility("default")))
@@ -127,6 +127,23 @@ SSM_API ssm_status_t ssm_scan_fwd(int64_t batch, int64_t seqlen, int64_t dim, in
 typedef enum { SSM_BBAR_DELTA_B = 0, SSM_BBAR_ZOH = 1 } ssm_bbar_mode_t;
 
 /*
+ * How the scan's work is laid out over a workgroup (the result is the same
+ * bits either way: both compute each step in the same order).
+ *   SSM_LAYOUT_AUTO           the library chooses;
+ *   SSM_LAYOUT_CHANNEL_LANES  lane = channel, each scan wave one range of
+ *                             state indices of 64 channels, the per-(t, d)
+ *                             work on waves next to every scan wave; every
+ *                             dstate, both Bbar modes, the sequence split;
+ *   SSM_LAYOUT_STATE_ROWS     a scan wave holds 16 channels x 16 state
+ *                             indices (one 16-lane row per 4 states), the
+ *                             per-(t, d) work on a SIMD of its own, and
+ *                             16 x channel_groups channels per workgroup:
+ *                             dstate 16, SSM_BBAR_DELTA_B and one segment
+ *                             only (else SSM_ERR_UNSUPPORTED).
+ */
+typedef enum { SSM_LAYOUT_AUTO = 0, SSM_LAYOUT_CHANNEL_LANES = 1, SSM_LAYOUT_STATE_ROWS = 2 } ssm_scan_layout_t;
+
+/*
  * Launch-shape overrides for ssm_scan_fwd.  Every field 0 means "choose
  * automatically".  The result does not depend on these choices beyond fp32
  * rounding of the re-associated cross-segment carry; they exist for tuning
@@ -139,14 +156,20 @@ typedef enum { SSM_BBAR_DELTA_B = 0, SSM_BBAR_ZOH = 1 } ssm_bbar_mode_t;
  *                    bbar_mode SSM_BBAR_DELTA_B).
  *   bbar_mode        the discretised input term (not a launch-shape choice:
  *                    it changes the result), see ssm_bbar_mode_t.
- * reserved must be zero.
+ *   layout           ssm_scan_layout_t;
+ *   channel_groups   with SSM_LAYOUT_STATE_ROWS: scan waves (groups of 16
+ *                    channels) per workgroup, 1 to 6.
+ * chains_per_lane applies to SSM_LAYOUT_CHANNEL_LANES only (the state rows
+ * always hold 4 chains per lane).  reserved must be zero.
  */
 typedef struct {
   int32_t chains_per_lane;
   int32_t segments;
   int32_t chunk_steps;
   int32_t bbar_mode;
-  int32_t reserved[4];
+  int32_t layout;
+  int32_t channel_groups;
+  int32_t reserved[2];
 } ssm_scan_opts_t;
 
 /* ssm_scan_fwd with launch-shape overrides (opts may be NULL). An override

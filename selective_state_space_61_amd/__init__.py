@@ -41,7 +41,8 @@ class SsmError(RuntimeError):
 
 class ScanOpts(ctypes.Structure):
     _fields_ = [("chains_per_lane", ctypes.c_int32), ("segments", ctypes.c_int32),
-                ("chunk_steps", ctypes.c_int32), ("bbar_mode", ctypes.c_int32), ("reserved", ctypes.c_int32 * 4)]
+                ("chunk_steps", ctypes.c_int32), ("bbar_mode", ctypes.c_int32), ("layout", ctypes.c_int32),
+                ("channel_groups", ctypes.c_int32), ("reserved", ctypes.c_int32 * 2)]
 
 
 class UpdateOpts(ctypes.Structure):
@@ -53,6 +54,8 @@ class SsdOpts(ctypes.Structure):
 
 
 SSM_BBAR_DELTA_B, SSM_BBAR_ZOH = 0, 1
+SSM_LAYOUT_AUTO, SSM_LAYOUT_CHANNEL_LANES, SSM_LAYOUT_STATE_ROWS = 0, 1, 2
+LAYOUTS = {"auto": SSM_LAYOUT_AUTO, "channel_lanes": SSM_LAYOUT_CHANNEL_LANES, "state_rows": SSM_LAYOUT_STATE_ROWS}
 
 
 _lib_handle = None
@@ -143,11 +146,12 @@ def ssm_scan_fwd(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch
                  delta_bias: Optional[torch.Tensor] = None, delta_softplus: bool = False, *,
                  y: Optional[torch.Tensor] = None, last_state: Optional[torch.Tensor] = None,
                  return_last_state: bool = True, chains_per_lane: int = 0, segments: int = 0,
-                 chunk_steps: int = 0, zoh: bool = False, stream=None,
-                 _noalloc: bool = False) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+                 chunk_steps: int = 0, zoh: bool = False, layout: str = "auto", channel_groups: int = 0,
+                 stream=None, _noalloc: bool = False) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Selective scan forward (include/ssm.h: ssm_scan_fwd).  Returns (y, last_state); last_state
-    is None when return_last_state is False and none was passed in.  chains_per_lane, segments
-    and chunk_steps override the launch shape (0 = automatic); zoh selects the exact
+    is None when return_last_state is False and none was passed in.  chains_per_lane, segments,
+    chunk_steps, layout ("auto", "channel_lanes", "state_rows") and channel_groups override the
+    launch shape (0 / "auto" = automatic); zoh selects the exact
     zero-order-hold input term (SSM_BBAR_ZOH) instead of Delta B."""
     lib = load_library()
     if x.dim() != 3 or A.dim() != 2:
@@ -171,7 +175,7 @@ def ssm_scan_fwd(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch
         last_state = torch.empty((batch, dim, dstate), dtype=torch.float32, device=dev)
     _need(last_state, "last_state", (batch, dim, dstate), torch.float32, dev, optional=True)
     opts = ScanOpts(int(chains_per_lane), int(segments), int(chunk_steps),
-                    SSM_BBAR_ZOH if zoh else SSM_BBAR_DELTA_B)
+                    SSM_BBAR_ZOH if zoh else SSM_BBAR_DELTA_B, LAYOUTS[layout], int(channel_groups))
     entry = lib.ssm_scan_fwd_noalloc if _noalloc else lib.ssm_scan_fwd_ex
     status = entry(batch, seqlen, dim, dstate, code, _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
                    _ptr(z), _ptr(delta_bias), int(bool(delta_softplus)), _ptr(y), _ptr(last_state),
@@ -184,15 +188,16 @@ def ssm_scan_fwd_noalloc(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, 
                          C: torch.Tensor, D: Optional[torch.Tensor] = None, z: Optional[torch.Tensor] = None,
                          delta_bias: Optional[torch.Tensor] = None, delta_softplus: bool = False, *,
                          y: torch.Tensor, last_state: Optional[torch.Tensor] = None, chains_per_lane: int = 0,
-                         segments: int = 0, chunk_steps: int = 0, zoh: bool = False,
-                         stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+                         segments: int = 0, chunk_steps: int = 0, zoh: bool = False, layout: str = "auto",
+                         channel_groups: int = 0, stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """The allocation-free scan (include/ssm.h: ssm_scan_fwd_noalloc): the caller passes y (and
     last_state, or None) and nothing is allocated, by this binding or by the library."""
     if y is None:
         raise ValueError("y is required: the allocation-free scan allocates no output")
     return ssm_scan_fwd(x, delta, A, B, C, D=D, z=z, delta_bias=delta_bias, delta_softplus=delta_softplus, y=y,
                         last_state=last_state, return_last_state=False, chains_per_lane=chains_per_lane,
-                        segments=segments, chunk_steps=chunk_steps, zoh=zoh, stream=stream, _noalloc=True)
+                        segments=segments, chunk_steps=chunk_steps, zoh=zoh, layout=layout,
+                        channel_groups=channel_groups, stream=stream, _noalloc=True)
 
 
 def ssm_state_update(state: torch.Tensor, x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor,

@@ -12,6 +12,7 @@
 
 #include "../../include/ssm.h"
 #include "scan_table.hpp"
+#include "scan_rows_table.hpp"
 #include "state_update.hpp"
 #include "conv1d.hpp"
 #include "scan_bwd.hpp"
@@ -294,8 +295,73 @@ ssm_status_t scan_fwd_impl(int64_t batch, int64_t seqlen, int64_t dim, int64_t d
       return fail(SSM_ERR_UNSUPPORTED, "bbar_mode %d is not SSM_BBAR_DELTA_B or SSM_BBAR_ZOH", (int)opts->bbar_mode);
     for (int32_t r : opts->reserved)
       if (r != 0) return fail(SSM_ERR_INVALID_ARG, "ssm_scan_opts_t.reserved must be zero");
+    if (opts->layout != SSM_LAYOUT_AUTO && opts->layout != SSM_LAYOUT_CHANNEL_LANES &&
+        opts->layout != SSM_LAYOUT_STATE_ROWS)
+      return fail(SSM_ERR_UNSUPPORTED, "layout %d is not an ssm_scan_layout_t", (int)opts->layout);
+    if (opts->channel_groups < 0 || opts->channel_groups > ssm::kRowsMaxScanWaves)
+      return fail(SSM_ERR_UNSUPPORTED, "channel_groups %d not in 0..%d", (int)opts->channel_groups,
+                  ssm::kRowsMaxScanWaves);
   }
   const bool split_auto = !(opts && opts->segments > 0) && base_wgs < 160;
+
+  // The state-row layout: dstate 16, Delta B, whole sequences (no split).  The automatic choice
+  // takes it whenever it applies.
+  {
+    const int layout = opts ? opts->layout : SSM_LAYOUT_AUTO;
+    const bool zoh_mode = opts && opts->bbar_mode == SSM_BBAR_ZOH;
+    const bool rows_fit = dstate == 16 && !zoh_mode && !(opts && opts->segments > 1) &&
+                          !(opts && opts->chains_per_lane != 0 && opts->chains_per_lane != 4);
+    if (layout == SSM_LAYOUT_STATE_ROWS && !rows_fit)
+      return fail(SSM_ERR_UNSUPPORTED,
+                  "SSM_LAYOUT_STATE_ROWS needs dstate 16, SSM_BBAR_DELTA_B, one segment and 4 chains per lane");
+    if (layout == SSM_LAYOUT_CHANNEL_LANES && opts && opts->channel_groups != 0)
+      return fail(SSM_ERR_UNSUPPORTED, "channel_groups applies to SSM_LAYOUT_STATE_ROWS only");
+    const bool use_rows = rows_fit && (layout == SSM_LAYOUT_STATE_ROWS || (layout == SSM_LAYOUT_AUTO && !split_auto));
+    if (use_rows) {
+      const int cus = device_cus();
+      int S = opts ? opts->channel_groups : 0;
+      if (S == 0) {
+        // cost = rounds of one workgroup per CU x scan waves on the busiest SIMD (three SIMDs take
+        // scan waves); among equal costs, the one whose rounds leave the fewest CUs idle, then
+        // the larger workgroup.  Measured on MI355X: 3 groups (256 workgroups) for the 130M
+        // shape, 5 groups (256 workgroups) for the 2.8B shape.
+        int64_t best = -1, best_idle = 0;
+        for (int c = 1; c <= ssm::kRowsMaxScanWaves; ++c) {
+          const int64_t wgs = batch * ((dim + 16 * c - 1) / (16 * c));
+          const int64_t rounds = (wgs + cus - 1) / cus;
+          const int64_t cost = rounds * ((c + 2) / 3);
+          const int64_t idle = rounds * cus - wgs;
+          if (best < 0 || cost < best || (cost == best && idle <= best_idle)) {
+            best = cost;
+            best_idle = idle;
+            S = c;
+          }
+        }
+      }
+      const int64_t rncb = (dim + 16 * S - 1) / (16 * S);
+      int64_t rgrid;
+      if (!mul_ok(rncb, batch, &rgrid) || rgrid > 0x7fffffff)
+        return fail(SSM_ERR_UNSUPPORTED, "grid of %lld workgroups is too large", (long long)rncb * batch);
+      const ssm::RowsVariants& rv = ssm::rows_table(dtype == SSM_BF16).v[S];
+      const int chunk_opt = opts ? opts->chunk_steps : 0;
+      if (chunk_opt != 0 && chunk_opt != 16 && chunk_opt != 32)
+        return fail(SSM_ERR_UNSUPPORTED, "chunk_steps %d is not 16 or 32", chunk_opt);
+      if (chunk_opt == 32 && !rv.k[1])
+        return fail(SSM_ERR_UNSUPPORTED, "chunk_steps 32 does not fit LDS with %d channel groups", S);
+      const bool ch32 = chunk_opt == 32 || (chunk_opt == 0 && rv.k[1] && rgrid <= cus);
+      ssm::ScanArgs a{};
+      a.x = x; a.delta = delta; a.A = A; a.B = B; a.C = C; a.Dskip = D; a.z = z; a.delta_bias = delta_bias;
+      a.y = y; a.last_state = last_state;
+      a.batch = batch; a.seqlen = seqlen; a.dim = dim; a.seg_len = seqlen;
+      a.nseg = 1;
+      a.ncb = static_cast<int32_t>(rncb);
+      a.softplus = delta_softplus ? 1 : 0;
+      const int64_t vmax = 16 / es;
+      a.vec_ok = (dim % vmax == 0) && aligned(x, 16) && aligned(delta, 16) && aligned(y, 16) && (!z || aligned(z, 16));
+      hipLaunchKernelGGL(rv.k[ch32 ? 1 : 0], dim3(static_cast<unsigned>(rgrid)), dim3(64 * ssm::kRowsWaves), 0, st, a);
+      return check_launch("scan (state rows)");
+    }
+  }
   int npl = default_npl(dstate, split_auto ? 1024 : base_wgs);
   if (opts && opts->chains_per_lane) {
     if (!npl_supported(dstate, opts->chains_per_lane))

@@ -133,8 +133,20 @@ def test_scan_opts_validation(lib):
     assert scan(lib, dstate=16, opts=ssm.ScanOpts(2, 0, 32)) == UNSUPPORTED  # 8 scan waves: 32-step tiles too big
     assert scan(lib, dstate=16, opts=ssm.ScanOpts(0, -1, 0)) == INVALID
     bad = ssm.ScanOpts(0, 0, 0)
-    bad.reserved[2] = 1
+    bad.reserved[1] = 1
     assert scan(lib, dstate=16, opts=bad) == INVALID and "reserved" in err(lib)
+    # the layout override: unknown values, the state-row layout's limits, channel groups with the
+    # channel-lane layout
+    rows, lanes = ssm.SSM_LAYOUT_STATE_ROWS, ssm.SSM_LAYOUT_CHANNEL_LANES
+    assert scan(lib, dstate=16, opts=ssm.ScanOpts(0, 0, 0, 0, 3)) == UNSUPPORTED and "layout" in err(lib)
+    assert scan(lib, dstate=16, opts=ssm.ScanOpts(0, 0, 0, 0, rows, 7)) == UNSUPPORTED and "channel_groups" in err(lib)
+    assert scan(lib, dstate=16, opts=ssm.ScanOpts(0, 0, 0, 0, rows, -1)) == UNSUPPORTED
+    assert scan(lib, dstate=8, opts=ssm.ScanOpts(0, 0, 0, 0, rows)) == UNSUPPORTED and "STATE_ROWS" in err(lib)
+    assert scan(lib, dstate=16, opts=ssm.ScanOpts(0, 0, 0, ssm.SSM_BBAR_ZOH, rows)) == UNSUPPORTED
+    assert scan(lib, dstate=16, opts=ssm.ScanOpts(2, 0, 0, 0, rows)) == UNSUPPORTED
+    assert scan(lib, dstate=16, opts=ssm.ScanOpts(0, 3, 0, 0, rows)) == UNSUPPORTED
+    assert scan(lib, dstate=16, opts=ssm.ScanOpts(0, 0, 0, 0, lanes, 3)) == UNSUPPORTED and "channel_groups" in err(lib)
+    assert scan(lib, dstate=16, opts=ssm.ScanOpts(0, 0, 32, 0, rows, 5)) == UNSUPPORTED and "chunk_steps" in err(lib)
     assert scan(lib, dstate=16, opts=ssm.ScanOpts(0, 0, 0, 2)) == UNSUPPORTED and "bbar_mode" in err(lib)
     assert scan(lib, dstate=16, opts=ssm.ScanOpts(4, 0, 32, ssm.SSM_BBAR_ZOH)) == UNSUPPORTED  # ZOH: 16-step tiles
 

@@ -300,3 +300,67 @@ def test_decode_full_workload(o):
     # (steps, batch, dim) -> (batch, steps, dim), the scan layout the oracle compares against
     scan_whole(o, sc, ys.transpose(0, 1), state, True, TOL[w.dtype], "decode over 256 steps", block=1024,
                threads=THREADS)
+
+
+# ---------------------------------------------------------------------------------------------------
+# the state-row layout (SSM_LAYOUT_STATE_ROWS): the same arithmetic in the same order as the
+# channel-lane layout, so the same bits; and the oracle
+# ---------------------------------------------------------------------------------------------------
+ROW_SHAPES = [(2, 96, 48, 16), (1, 33, 16, 16), (3, 70, 200, 16), (2, 257, 97, 16), (1, 1, 5, 16), (2, 64, 384, 16)]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("groups", [1, 2, 3, 4, 5, 6])
+@pytest.mark.parametrize("chunk", [16, 32])
+def test_state_rows_equal_channel_lanes(o, dtype, groups, chunk):
+    if chunk == 32 and groups > 4:
+        pytest.skip("32-step tiles do not fit LDS beyond 4 channel groups")
+    for k, (batch, L, dim, N) in enumerate(ROW_SHAPES):
+        say(f"[case] state rows {dtype} groups={groups} chunk={chunk} shape={(batch, L, dim, N)}")
+        t = W.scan_inputs(batch, L, dim, N, dtype, seed=500 + 13 * groups + k)
+        yr, sr, _ = scan_on_gpu(t, True, layout="state_rows", channel_groups=groups, chunk_steps=chunk)
+        yl, sl, _ = scan_on_gpu(t, True, layout="channel_lanes", chains_per_lane=4, chunk_steps=chunk, segments=1)
+        assert torch.equal(yr, yl), "y differs between the layouts"
+        assert torch.equal(sr, sl), "last_state differs between the layouts"
+        if k < 3:
+            y_ref, st_ref = o.scan(t["x"], t["delta"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"],
+                                   delta_bias=t["delta_bias"], delta_softplus=True, nthreads=THREADS)
+            assert_close(to_host(yr), y_ref, TOL[dtype], "state rows y")
+            assert_close(to_host(sr), st_ref, TOL[dtype], "state rows last_state")
+
+
+@pytest.mark.parametrize("variant", ["no_z", "no_D", "no_bias", "softplus_off", "bare"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_state_rows_variants(o, variant, dtype):
+    softplus = variant not in ("softplus_off", "bare")
+    t = W.scan_inputs(2, 90, 120, 16, dtype, seed=61 + len(variant), has_z=variant not in ("no_z", "bare"),
+                      has_D=variant not in ("no_D", "bare"), has_bias=softplus and variant != "no_bias")
+    if not softplus:
+        t["delta"] = np.abs(t["delta"]) if dtype == "f32" else t["delta"] & np.uint16(0x7FFF)
+    say(f"[case] state rows variant {variant} {dtype}")
+    yr, sr, _ = scan_on_gpu(t, softplus, layout="state_rows", channel_groups=3)
+    yl, sl, _ = scan_on_gpu(t, softplus, layout="channel_lanes", chains_per_lane=4, segments=1)
+    assert torch.equal(yr, yl) and torch.equal(sr, sl), "the layouts differ"
+    y_ref, st_ref = o.scan(t["x"], t["delta"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"], delta_bias=t["delta_bias"],
+                           delta_softplus=softplus, nthreads=THREADS)
+    assert_close(to_host(yr), y_ref, TOL[dtype], f"state rows {variant} y")
+    assert_close(to_host(sr), st_ref, TOL[dtype], f"state rows {variant} last_state")
+
+
+def test_state_rows_unaligned_views_and_empty(o):
+    """Views whose rows are not 16-byte aligned take the element-wise path; L = 0 gives a zero
+    state; dim not a multiple of the 16-byte vector."""
+    import selective_state_space_61_amd as ssm
+    t = W.scan_inputs(2, 77, 51, 16, "bf16", seed=8)
+    yr, sr, _ = scan_on_gpu(t, True, layout="state_rows", channel_groups=2)
+    yl, sl, _ = scan_on_gpu(t, True, layout="channel_lanes", chains_per_lane=4, segments=1)
+    assert torch.equal(yr, yl) and torch.equal(sr, sl)
+    d = {k: to_dev(v) for k, v in t.items()}
+    y = torch.empty(2 * 77 * 51 + 1, dtype=torch.bfloat16, device="cuda")[1:].view(2, 77, 51)
+    ssm.ssm_scan_fwd(d["x"], d["delta"], d["A"], d["B"], d["C"], D=d["D"], z=d["z"], delta_bias=d["delta_bias"],
+                     delta_softplus=True, y=y, layout="state_rows", channel_groups=2)
+    torch.cuda.synchronize()
+    assert torch.equal(y, yl), "unaligned y differs"
+    t0 = W.scan_inputs(2, 0, 64, 16, "f32", seed=9)
+    _, s0, _ = scan_on_gpu(t0, True, layout="state_rows", channel_groups=4)
+    assert torch.count_nonzero(s0).item() == 0
