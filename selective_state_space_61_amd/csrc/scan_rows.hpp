@@ -47,6 +47,17 @@ constexpr int rows_lds_bytes(int S, int ch) {
          + 3 * ch * 16 * S * 8;          // (x, silu z), triple-buffered
 }
 
+constexpr int kXcds = 8;  // MI355X: 8 accelerator complex dies, workgroups dealt round robin
+
+// Logical workgroup index for hardware index i of n: the first n - n % 8 workgroups are regrouped
+// so that the hardware indices i with i % 8 == x (one XCD) take logical indices x * (n / 8) ..
+// (x + 1) * (n / 8) - 1; the last n % 8 keep their index.  A bijection on [0, n).
+__device__ __forceinline__ int64_t xcd_local(int64_t i, int64_t n) {
+  const int64_t per = n / kXcds;
+  if (i >= per * kXcds) return i;
+  return (i % kXcds) * per + i / kXcds;
+}
+
 template <bool BF16, int S, int CH>
 __global__ __launch_bounds__(64 * kRowsWaves) void scan_rows_kernel(const ScanArgs p) {
   constexpr int N = 16, NPL = 4;
@@ -72,7 +83,11 @@ __global__ __launch_bounds__(64 * kRowsWaves) void scan_rows_kernel(const ScanAr
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-  const int64_t blk = blockIdx.x;
+  // Workgroups are dispatched to the 8 XCDs (each with its own L2) round robin.  A 16 S-channel
+  // block's rows are not whole 128-byte lines, so neighbouring channel blocks share lines: the
+  // logical index is permuted so that consecutive logical blocks (neighbours in a batch row)
+  // land on the same XCD and share its L2 instead of fetching each line twice.
+  const int64_t blk = xcd_local(blockIdx.x, gridDim.x);
   const int cb = static_cast<int>(blk % p.ncb);
   const int64_t b = blk / p.ncb;
   const int64_t t_end = p.seqlen;
