@@ -89,6 +89,9 @@ class Oracle:
         lib.oracle_scan_bwd.argtypes = [i64, i64, i64, i64, i32, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp,
                                         vp, vp, vp, vp, vp, vp]
         lib.oracle_scan_bwd.restype = i32
+        lib.oracle_scan_bwd_ex.argtypes = [i64, i64, i64, i64, i32, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, vp, vp,
+                                           vp, vp, vp, vp, vp, vp, vp]
+        lib.oracle_scan_bwd_ex.restype = i32
         lib.oracle_ssd.argtypes = [i64, i64, i64, i64, i64, i64, i32, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp,
                                    i32]
         lib.oracle_ssd.restype = i32
@@ -193,8 +196,10 @@ class Oracle:
         return y, st
 
 
-    def scan_bwd(self, x, delta, A, B, C, dy, D=None, z=None, delta_bias=None, delta_softplus=False):
-        """Gradients of sum(dy * y) for the scan from a zero state.  Returns a dict of float64
+    def scan_bwd(self, x, delta, A, B, C, dy, D=None, z=None, delta_bias=None, delta_softplus=False,
+                 zoh: bool = False):
+        """Gradients of sum(dy * y) for the scan from a zero state (zoh: the exact zero-order-hold
+        input term of the forward).  Returns a dict of float64
         arrays: dx, ddelta (batch, L, dim); dA (dim, N); dB, dC (batch, L, N); dD, ddelta_bias
         (dim,) when D / delta_bias are given; dz (batch, L, dim) when z is given."""
         x, delta, B, C, z = _c(x), _c(delta), _c(B), _c(C), _c(z)
@@ -211,8 +216,9 @@ class Oracle:
         out["dD"] = np.empty(dim) if D is not None else None
         out["ddelta_bias"] = np.empty(dim) if delta_bias is not None else None
         out["dz"] = np.empty((batch, L, dim)) if z is not None else None
-        rc = self._lib.oracle_scan_bwd(batch, L, dim, N, code, _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C),
-                                       _ptr(D), _ptr(z), _ptr(delta_bias), int(bool(delta_softplus)), _ptr(dy),
+        rc = self._lib.oracle_scan_bwd_ex(batch, L, dim, N, code, _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C),
+                                       _ptr(D), _ptr(z), _ptr(delta_bias), int(bool(delta_softplus)),
+                                       int(bool(zoh)), _ptr(dy),
                                        _ptr(out["dx"]), _ptr(out["ddelta"]), _ptr(out["dA"]), _ptr(out["dB"]),
                                        _ptr(out["dC"]), _ptr(out["dD"]), _ptr(out["dz"]),
                                        _ptr(out["ddelta_bias"]))

@@ -250,11 +250,38 @@ int oracle_state_update_ex(int64_t batch, int64_t dim, int64_t dstate, int dtype
  * ------------------------------------------------------------------------- */
 static double sigmoid(double v) { return 1.0 / (1.0 + exp(-v)); }
 
+/* Exact zero-order hold ("Mamba 论文精读" sec. 2.2), per (d, n) with z = dt A:
+ *   u_t = phi B_t x_t,  phi = expm1(z) / A  (dt when A = 0),  dphi/ddt = exp(z) = abar,
+ *   dphi/dA = (dt abar - phi) / A = (z expm1(z) + (z - expm1(z))) / A^2  (dt^2 / 2 when A = 0),
+ * so the adjoint differs from the Delta B form in these terms only:
+ *   dB_t += g phi x_t;  dx_t += g phi B_t;  ddt_t += g abar (B_t x_t + A h_{t-1});
+ *   dA += g (dt abar h_{t-1} + B_t x_t dphi/dA). */
+int oracle_scan_bwd_ex(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dtype, const void *x,
+                       const void *delta, const float *A, const void *B, const void *C, const float *Dskip,
+                       const void *z, const float *delta_bias, int delta_softplus, int zoh, const double *dy,
+                       double *dx, double *ddelta, double *dA, double *dB, double *dC, double *dD, double *dz,
+                       double *ddelta_bias);
+static double zoh_phi(double dt, double a) { return a == 0.0 ? dt : expm1(dt * a) / a; }
+static double zoh_dphi_da(double dt, double a) {
+  if (a == 0.0) return 0.5 * dt * dt;
+  const double zz = dt * a, em = expm1(zz);
+  return (zz * em + (zz - em)) / (a * a);
+}
+
 int oracle_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dtype, const void *x,
                     const void *delta, const float *A, const void *B, const void *C, const float *Dskip,
                     const void *z, const float *delta_bias, int delta_softplus, const double *dy, double *dx,
                     double *ddelta, double *dA, double *dB, double *dC, double *dD, double *dz,
                     double *ddelta_bias) {
+  return oracle_scan_bwd_ex(batch, seqlen, dim, dstate, dtype, x, delta, A, B, C, Dskip, z, delta_bias,
+                            delta_softplus, 0, dy, dx, ddelta, dA, dB, dC, dD, dz, ddelta_bias);
+}
+
+int oracle_scan_bwd_ex(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dtype, const void *x,
+                       const void *delta, const float *A, const void *B, const void *C, const float *Dskip,
+                       const void *z, const float *delta_bias, int delta_softplus, int zoh, const double *dy,
+                       double *dx, double *ddelta, double *dA, double *dB, double *dC, double *dD, double *dz,
+                       double *ddelta_bias) {
   if (batch < 0 || seqlen < 0 || dim < 0 || dstate < 1 || dstate > 1024) return -1;
   if (!x || !delta || !A || !B || !C || !dy || !dx || !ddelta || !dA || !dB || !dC) return -1;
   const int64_t L = seqlen, N = dstate;
@@ -276,7 +303,7 @@ int oracle_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, 
         double xt = load_elem(x, dtype, i_td);
         for (int64_t n = 0; n < N; ++n)
           hs[(t + 1) * N + n] = exp(dt * (double)A[d * N + n]) * hs[t * N + n] +
-                                dt * load_elem(B, dtype, i_tn + n) * xt;
+                                bbar_x(zoh, dt, (double)A[d * N + n], load_elem(B, dtype, i_tn + n), xt);
       }
       /* backward */
       for (int64_t n = 0; n < N; ++n) g[n] = 0.0;
@@ -302,10 +329,18 @@ int oracle_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, 
           const double an = (double)A[d * N + n], abar = exp(dt * an);
           g[n] += dy0 * Cn;
           dC[i_tn + n] += dy0 * h[n];
-          dB[i_tn + n] += g[n] * dt * xt;
-          dxt += g[n] * dt * Bn;
-          ddt += g[n] * (Bn * xt + an * abar * hp[n]);
-          dA[d * N + n] += g[n] * dt * abar * hp[n];
+          if (zoh) {
+            const double phi = zoh_phi(dt, an);
+            dB[i_tn + n] += g[n] * phi * xt;
+            dxt += g[n] * phi * Bn;
+            ddt += g[n] * abar * (Bn * xt + an * hp[n]);
+            dA[d * N + n] += g[n] * (dt * abar * hp[n] + Bn * xt * zoh_dphi_da(dt, an));
+          } else {
+            dB[i_tn + n] += g[n] * dt * xt;
+            dxt += g[n] * dt * Bn;
+            ddt += g[n] * (Bn * xt + an * abar * hp[n]);
+            dA[d * N + n] += g[n] * dt * abar * hp[n];
+          }
           g[n] *= abar; /* carried to step t-1 */
         }
         dx[i_td] = dxt;

@@ -57,7 +57,7 @@ def _scan(o, c, **over):
     kw.update(over)
     return o.scan(kw["x"], kw["delta"], kw["A"], kw["B"], kw["C"], D=kw.get("D"), z=kw.get("z"),
                   delta_bias=kw.get("delta_bias"), delta_softplus=kw.get("delta_softplus", False),
-                  h0=kw.get("h0"))
+                  h0=kw.get("h0"), zoh=kw.get("zoh", False))
 
 
 def unrolled(c):
@@ -482,6 +482,37 @@ def pin_backward_finite_differences(o):
             _close(g[gname], fd, rtol, f"d{name} (seed {seed})")
 
 
+def pin_backward_zoh_finite_differences(o):
+    """The adjoint of the exact zero-order-hold forward ("Mamba 论文精读" sec. 2.2) matches central
+    finite differences of that (pinned) forward: ordinary steps, steps small enough that
+    dt * A is ~1e-3 (where (dt abar - phi) / A cancels), and a state with A = 0 exactly."""
+    cases = [(41, True, True, True, True, None), (42, False, True, True, False, "small"),
+             (43, True, False, False, True, "zero_a")]
+    for seed, softplus, z, D, bias, kind in cases:
+        c = _rand_case(seed, batch=2, L=5, dim=3, N=3, softplus=softplus, bias=bias, z=z, D=D)
+        if kind == "small":
+            c["delta"] = c["delta"] * 0.004
+        if kind == "zero_a":
+            c["A"][1, 2] = 0.0
+        c["zoh"] = True
+        dy = np.random.default_rng(seed + 100).normal(size=c["x"].shape)
+        g = o.scan_bwd(c["x"], c["delta"], c["A"], c["B"], c["C"], dy, D=c["D"], z=c["z"],
+                       delta_bias=c["delta_bias"], delta_softplus=softplus, zoh=True)
+        checks = [("x", "dx", 1e-6, 1e-6), ("delta", "ddelta", 1e-7 if kind == "small" else 1e-6, 1e-6),
+                  ("B", "dB", 1e-6, 1e-6), ("C", "dC", 1e-6, 1e-6), ("A", "dA", 1e-3, 1e-5)]
+        if z:
+            checks.append(("z", "dz", 1e-6, 1e-6))
+        if bias:
+            checks.append(("delta_bias", "ddelta_bias", 1e-3, 1e-5))
+        for name, gname, eps, rtol in checks:
+            fd = _fd_grad(o, c, dy, name, eps)
+            _close(g[gname], fd, rtol, f"ZOH d{name} (seed {seed}, {kind or 'ordinary'})")
+        # and the ZOH adjoint is not the Delta B one
+        g0 = o.scan_bwd(c["x"], c["delta"], c["A"], c["B"], c["C"], dy, D=c["D"], z=c["z"],
+                        delta_bias=c["delta_bias"], delta_softplus=softplus)
+        assert np.max(np.abs(g0["dA"] - g["dA"])) > 1e-6 * np.max(np.abs(g["dA"])), "ZOH dA equals the Delta B dA"
+
+
 def pin_backward_linear_in_dy(o):
     """The gradients are linear in dy."""
     c = _rand_case(31, batch=1, L=6, dim=2, N=3)
@@ -646,6 +677,6 @@ ALL_PINS = [pin_worked_examples, pin_unrolled_sum, pin_lti_convolution, pin_line
             pin_decode_equals_scan, pin_associative_scan, pin_special_values, pin_storage_widening,
             pin_channel_selection, pin_conv_library_convolution, pin_conv_impulse, pin_conv_silu,
             pin_conv_chaining, pin_conv_decode_equals_fwd, pin_conv_causality, pin_backward_finite_differences,
-            pin_backward_linear_in_dy, pin_zoh_steady_state, pin_zoh_semigroup, pin_zoh_small_step_limit,
+            pin_backward_zoh_finite_differences, pin_backward_linear_in_dy, pin_zoh_steady_state, pin_zoh_semigroup, pin_zoh_small_step_limit,
             pin_zoh_decode_equals_scan, pin_ssd_equals_selective_scan, pin_ssd_dual_matrix_form,
             pin_ssd_resume_from_state]

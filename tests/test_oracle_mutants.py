@@ -59,6 +59,15 @@ MUTANTS = [
     ("zoh_missing_division", "return expm1(dt * a) / a * bv * xt;", "return expm1(dt * a) * bv * xt;"),
     ("zoh_plain_exp", "return expm1(dt * a) / a * bv * xt;", "return exp(dt * a) / a * bv * xt;"),
     ("zoh_keeps_delta", "return expm1(dt * a) / a * bv * xt;", "return dt * expm1(dt * a) / a * bv * xt;"),
+    ("bwd_zoh_dB_uses_dt", "dB[i_tn + n] += g[n] * phi * xt;", "dB[i_tn + n] += g[n] * dt * xt;"),
+    ("bwd_zoh_dx_uses_dt", "dxt += g[n] * phi * Bn;", "dxt += g[n] * dt * Bn;"),
+    ("bwd_zoh_ddt_delta_b_form", "ddt += g[n] * abar * (Bn * xt + an * hp[n]);",
+     "ddt += g[n] * (Bn * xt + an * abar * hp[n]);"),
+    ("bwd_zoh_dA_without_input_term", "dA[d * N + n] += g[n] * (dt * abar * hp[n] + Bn * xt * zoh_dphi_da(dt, an));",
+     "dA[d * N + n] += g[n] * dt * abar * hp[n];"),
+    ("bwd_zoh_dphi_sign", "return (zz * em + (zz - em)) / (a * a);", "return (zz * em - (zz - em)) / (a * a);"),
+    ("bwd_zoh_forward_delta_b", "bbar_x(zoh, dt, (double)A[d * N + n], load_elem(B, dtype, i_tn + n), xt);",
+     "bbar_x(0, dt, (double)A[d * N + n], load_elem(B, dtype, i_tn + n), xt);"),
     ("ssd_group_ignored", "const int64_t b = bh / H, h = bh % H, g = h / hpg;", "const int64_t b = bh / H, h = bh % H, g = 0;"),
     ("ssd_no_dt_on_input", "S[p * N + n] = a * S[p * N + n] + d * xv * load_elem(B, dtype, ibc + n);",
      "S[p * N + n] = a * S[p * N + n] + xv * load_elem(B, dtype, ibc + n);"),
