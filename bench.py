@@ -412,9 +412,10 @@ def copy_ceiling_gbps(torch, device, nbytes=1 << 30, reps=10):
     return 2 * nbytes / (ms * 1e-3) / 1e9
 
 
-def bench_scan_bwd(steps, warmup, torch, np, W, ssm, device):
+def bench_scan_bwd(steps, warmup, torch, np, W, ssm, device, zoh=False):
     """The backward scan on the 130M-shaped layer (inputs, dy and gradients resident in HBM;
-    two input sets rotated).  Reports the time per call of the whole backward (both kernels)."""
+    two input sets rotated).  Reports the time per call of the whole backward (both kernels);
+    zoh differentiates the exact zero-order-hold forward."""
     w = W.WORKLOADS["mamba130m"]
     t = W.workload_inputs(w)
     g = np.random.default_rng(61)
@@ -428,7 +429,7 @@ def bench_scan_bwd(steps, warmup, torch, np, W, ssm, device):
     def call(i):
         d = sets[i % 2]
         ssm.ssm_scan_bwd(d["x"], d["delta"], d["A"], d["B"], d["C"], d["dy"], D=d["D"], z=d["z"],
-                         delta_bias=d["delta_bias"], delta_softplus=True)
+                         delta_bias=d["delta_bias"], delta_softplus=True, zoh=zoh)
 
     total_ms, per = time_calls(torch, call, steps, warmup)
     ms = sum(per) / len(per)
@@ -709,6 +710,9 @@ def main():
         log(f"[bench] {args.workload} with exact ZOH Bbar: {zres['kernel_ms'] * 1e3:.1f} us/launch")
         extra["scan_bwd"] = bench_scan_bwd(max(6, args.steps // 5), 20, torch, np, W, ssm, device)
         log(f"[bench] scan backward (130M shape): {extra['scan_bwd']['ms_per_call'] * 1e3:.1f} us/call")
+        extra["scan_bwd_exact_zoh"] = bench_scan_bwd(max(4, args.steps // 5), 3, torch, np, W, ssm, device, zoh=True)
+        log(f"[bench] scan backward, exact ZOH (130M shape): "
+            f"{extra['scan_bwd_exact_zoh']['ms_per_call'] * 1e3:.1f} us/call")
         extra["causal_conv1d"] = bench_conv(max(10, args.steps // 2), 3, torch, np, W, ssm, device)
         extra["causal_conv1d"]["traffic"] = traffic_from_profiles("conv", extra["causal_conv1d"]["alg_bytes"])[0]
         log(f"[bench] causal conv1d: {extra['causal_conv1d']['kernel_ms'] * 1e3:.1f} us/launch, "

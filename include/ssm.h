@@ -240,18 +240,40 @@ SSM_API ssm_status_t ssm_state_update(int64_t batch, int64_t dim, int64_t dstate
  *   ddelta_bias when delta_bias is given; ddelta is the gradient with respect
  *   to the raw delta (before bias and softplus).
  *
- * dstate must be 1, 2, 4, 8 or 16.  last_state is not differentiated.  The
- * channel sums of dB / dC and the batch sums of dA / dD / ddelta_bias are
- * taken in a fixed order, so the result does not vary from run to run.
- * Scratch: batch*ceil(seqlen/16)*dstate*dim + 2*ceil(dim/64)*batch*seqlen*dstate
- * + batch*dstate*dim + 32*batch*dim fp32, in the same per-(device, stream)
- * buffer as the split-sequence scan (same rules as ssm_scan_fwd).
+ * dstate must be 1, 2, 4, 8, 16, 32 or 64.  last_state is not
+ * differentiated.  The channel sums of dB / dC and the batch sums of dA / dD
+ * / ddelta_bias are taken in a fixed order, so the result does not vary from
+ * run to run.  With T = 16 (dstate <= 16), 8 (dstate 32) or 4 (dstate 64),
+ * halved for SSM_BBAR_ZOH but at least 4 (ssm_scan_bwd_ex), the scratch is batch*ceil(seqlen/T)*dstate*dim +
+ * 2*ceil(dim/64)*batch*seqlen*dstate + batch*dstate*dim + 2*T*batch*dim fp32,
+ * in the same per-(device, stream) buffer as the split-sequence scan (same
+ * rules as ssm_scan_fwd).
  */
 SSM_API ssm_status_t ssm_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, ssm_dtype_t dtype,
                                   const void *x, const void *delta, const float *A, const void *B, const void *C,
                                   const float *D, const void *z, const float *delta_bias, int delta_softplus,
                                   const void *dy, void *dx, void *ddelta, float *dA, void *dB, void *dC, float *dD,
                                   void *dz, float *ddelta_bias, void *stream);
+
+/* Options of ssm_scan_bwd_ex: bbar_mode as in ssm_scan_opts_t (the forward
+ * being differentiated); reserved must be zero. */
+typedef struct {
+  int32_t bbar_mode;
+  int32_t reserved[7];
+} ssm_bwd_opts_t;
+
+/*
+ * ssm_scan_bwd for either input term (opts may be NULL: SSM_BBAR_DELTA_B).
+ * With SSM_BBAR_ZOH it differentiates the exact zero-order-hold forward of
+ * "Mamba 论文精读" sec. 2.2: with phi = expm1(Delta A) / A the input term is
+ * phi B x, dphi/dDelta = exp(Delta A) and dphi/dA = (Delta exp(Delta A) -
+ * phi) / A.  Same arguments, layouts, scratch and errors as ssm_scan_bwd.
+ */
+SSM_API ssm_status_t ssm_scan_bwd_ex(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, ssm_dtype_t dtype,
+                             const void *x, const void *delta, const float *A, const void *B, const void *C,
+                             const float *D, const void *z, const float *delta_bias, int delta_softplus,
+                             const void *dy, void *dx, void *ddelta, float *dA, void *dB, void *dC, float *dD,
+                             void *dz, float *ddelta_bias, void *stream, const ssm_bwd_opts_t *opts);
 
 /*
  * Depthwise causal convolution that feeds the scan in the Mamba block

@@ -28,7 +28,7 @@ LIBRARY = os.path.join(_HERE, "libssm61.so")
 SSM_F32, SSM_BF16 = 0, 1
 STATUS_NAMES = {0: "SSM_OK", 1: "SSM_ERR_INVALID_ARG", 2: "SSM_ERR_UNSUPPORTED", 3: "SSM_ERR_MISALIGNED",
                 4: "SSM_ERR_HIP"}
-EXPORTED = ("ssm_scan_fwd", "ssm_scan_fwd_ex", "ssm_scan_fwd_noalloc", "ssm_scan_bwd", "ssm_state_update", "ssm_state_update_ex",
+EXPORTED = ("ssm_scan_fwd", "ssm_scan_fwd_ex", "ssm_scan_fwd_noalloc", "ssm_scan_bwd", "ssm_scan_bwd_ex", "ssm_state_update", "ssm_state_update_ex",
             "ssm_causal_conv1d_fwd",
             "ssm_causal_conv1d_update", "ssm_ssd_fwd", "ssm_ssd_state_update", "ssm_status_string", "ssm_last_error", "ssm_abi_version")
 
@@ -46,6 +46,10 @@ class ScanOpts(ctypes.Structure):
 
 
 class UpdateOpts(ctypes.Structure):
+    _fields_ = [("bbar_mode", ctypes.c_int32), ("reserved", ctypes.c_int32 * 7)]
+
+
+class BwdOpts(ctypes.Structure):
     _fields_ = [("bbar_mode", ctypes.c_int32), ("reserved", ctypes.c_int32 * 7)]
 
 
@@ -83,6 +87,8 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
     lib.ssm_scan_bwd.argtypes = [i64, i64, i64, i64, i32, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp,
                                  vp, vp, vp, vp]
     lib.ssm_scan_bwd.restype = i32
+    lib.ssm_scan_bwd_ex.argtypes = lib.ssm_scan_bwd.argtypes + [ctypes.POINTER(BwdOpts)]
+    lib.ssm_scan_bwd_ex.restype = i32
     lib.ssm_causal_conv1d_fwd.argtypes = [i64, i64, i64, i64, i32, vp, vp, vp, vp, i32, vp, vp, vp]
     lib.ssm_causal_conv1d_fwd.restype = i32
     lib.ssm_causal_conv1d_update.argtypes = [i64, i64, i64, i32, vp, vp, vp, vp, i32, vp, vp]
@@ -235,11 +241,12 @@ def ssm_state_update(state: torch.Tensor, x: torch.Tensor, delta: torch.Tensor, 
 
 def ssm_scan_bwd(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Tensor, C: torch.Tensor,
                  dy: torch.Tensor, D: Optional[torch.Tensor] = None, z: Optional[torch.Tensor] = None,
-                 delta_bias: Optional[torch.Tensor] = None, delta_softplus: bool = False,
+                 delta_bias: Optional[torch.Tensor] = None, delta_softplus: bool = False, zoh: bool = False,
                  stream=None) -> dict:
-    """Backward of ssm_scan_fwd (include/ssm.h: ssm_scan_bwd): gradients of sum(dy * y).
-    Returns a dict with dx, ddelta, dB, dC (x's dtype), dA (fp32), and dz / dD / ddelta_bias
-    (None unless z / D / delta_bias were given)."""
+    """Backward of ssm_scan_fwd (include/ssm.h: ssm_scan_bwd_ex): gradients of sum(dy * y); zoh
+    differentiates the exact zero-order-hold forward.  Returns a dict with dx, ddelta, dB, dC
+    (x's dtype), dA (fp32), and dz / dD / ddelta_bias (None unless z / D / delta_bias were
+    given)."""
     lib = load_library()
     if x.dim() != 3 or A.dim() != 2:
         raise ValueError("x must be (batch, seqlen, dim) and A (dim, dstate)")
@@ -260,11 +267,12 @@ def ssm_scan_bwd(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch
            "dz": torch.empty_like(x) if z is not None else None,
            "dD": torch.empty((dim,), dtype=torch.float32, device=dev) if D is not None else None,
            "ddelta_bias": torch.empty((dim,), dtype=torch.float32, device=dev) if delta_bias is not None else None}
-    status = lib.ssm_scan_bwd(batch, seqlen, dim, dstate, code, _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C),
-                              _ptr(D), _ptr(z), _ptr(delta_bias), int(bool(delta_softplus)), _ptr(dy),
-                              _ptr(out["dx"]), _ptr(out["ddelta"]), _ptr(out["dA"]), _ptr(out["dB"]),
-                              _ptr(out["dC"]), _ptr(out["dD"]), _ptr(out["dz"]), _ptr(out["ddelta_bias"]),
-                              _stream(dev, stream))
+    opts = BwdOpts(SSM_BBAR_ZOH if zoh else SSM_BBAR_DELTA_B)
+    status = lib.ssm_scan_bwd_ex(batch, seqlen, dim, dstate, code, _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C),
+                                 _ptr(D), _ptr(z), _ptr(delta_bias), int(bool(delta_softplus)), _ptr(dy),
+                                 _ptr(out["dx"]), _ptr(out["ddelta"]), _ptr(out["dA"]), _ptr(out["dB"]),
+                                 _ptr(out["dC"]), _ptr(out["dD"]), _ptr(out["dz"]), _ptr(out["ddelta_bias"]),
+                                 _stream(dev, stream), ctypes.byref(opts))
     _check(status)
     return out
 
@@ -402,5 +410,5 @@ def abi_version() -> int:
 
 
 __all__ = ["ssm_scan_fwd", "ssm_scan_bwd", "ssm_state_update", "ssm_causal_conv1d_fwd", "ssm_causal_conv1d_update",
-           "ssm_ssd_fwd", "ssm_ssd_state_update", "SsdOpts", "abi_version", "load_library", "SsmError", "ScanOpts", "UpdateOpts",
+           "ssm_ssd_fwd", "ssm_ssd_state_update", "SsdOpts", "BwdOpts", "abi_version", "load_library", "SsmError", "ScanOpts", "UpdateOpts",
            "LIBRARY", "EXPORTED"]

@@ -13,8 +13,8 @@
 //
 // One workgroup per (batch row, 64-channel block), with the wave roles of the forward kernel:
 //   phase 0 (forward, chunks 0 .. nc-1): IO waves stage (dt, dt x) in LDS, scan waves run the
-//     recurrence and store the state at the start of every kBwdChunk-step chunk in scratch
-//     (B, nc, N, D) fp32 -- the only O(B L D N / kBwdChunk) memory the pass uses;
+//     recurrence and store the state at the start of every T-step chunk in scratch
+//     (B, nc, N, D) fp32 -- the only O(B L D N / T) memory the pass uses;
 //   phase 1 (reverse, chunks nc-1 .. 0), per chunk, with two barriers:
 //     A  IO:   stage (dt, dt x) and dy0 = dy silu(z) in LDS from the x, delta, z, dy tile fetched
 //              a chunk earlier (dy0 needs no read-out, so it is staged up front); dD partial;
@@ -28,6 +28,14 @@
 //              ddelta, dz; dbias partial
 // A second kernel adds the channel-block partials of dB and dC, and the per-batch-row partials
 // of dA, dD and dbias, in a fixed order (deterministic).
+//
+// Exact zero-order hold (ZOH, "Mamba 论文精读" sec. 2.2): the input term is phi B x with
+// phi = expm1(dt A) / A = dt fz, fz = log2(e) m, m = zoh_factor.  Its adjoint differs in
+//   dB_t += g dt x fz;  dx_t += dt sum_n g fz B;  ddt_t = x sum_n g abar B + sum_n g A abar h_{t-1};
+//   dA += g dt (abar h_{t-1} + B dt x psi(dt A)),  psi(z) = ((z - 1) e^z + 1) / z^2
+// (the derivative of phi in A over dt^2), so the scan waves hand the IO waves one more sum.
+// Wider states (N 32, 64) keep four scan waves with 8 or 16 chains per lane and shorter chunks
+// (8 or 4 steps), which keeps a chunk's recomputed states in VGPRs.
 #pragma once
 
 #include "ssm_device.hpp"
@@ -50,22 +58,38 @@ struct BwdArgs {
   float* hstart;     // (batch, nc, N, dim) chunk-start states
   float* part_bc;    // (2, ncb, batch, L, N): dB then dC partial sums over one channel block
   float* part_a;     // (batch, N, dim)
-  float* part_d;     // (batch, kBwdChunk, dim)
-  float* part_bias;  // (batch, kBwdChunk, dim)
+  float* part_d;     // (batch, T, dim), T the chunk length
+  float* part_bias;  // (batch, T, dim)
   int64_t batch;
   int64_t seqlen;
   int64_t dim;
-  int64_t nc;        // chunks of kBwdChunk steps
+  int64_t nc;        // chunks of T steps
   int32_t ncb;
   int32_t softplus;
   int32_t vec_ok;
 };
 
-constexpr int kBwdChunk = 16;
+constexpr int kBwdChunk = 16;  // chunk length for dstate <= 16
 constexpr int kBwdIoWaves = 4;
+// chunk length of an instantiation: 16 steps up to 4 chains per lane, 8 for 8, 4 for 16; the
+// exact-ZOH step keeps more values live, so it takes half that (at least 4: one tile row per IO
+// thread)
+constexpr int bwd_chunk(int npl, bool zoh) {
+  const int t = npl <= 4 ? 16 : (npl == 8 ? 8 : 4);
+  return zoh ? (t / 2 < 4 ? 4 : t / 2) : t;
+}
 // steps per dB / dC reduction round: 2 NPL values per step and lane, at most 64 rows per round
-template <int NPL>
-constexpr int kBwdHalf = 32 / NPL < kBwdChunk ? 32 / NPL : kBwdChunk;
+template <int NPL, int T>
+constexpr int kBwdHalf = 32 / NPL < T ? 32 / NPL : T;
+
+// psi(z) = ((z - 1) e^z + 1) / z^2 = 1/2 + z/3 + z^2/8 + z^3/30 + z^4/144 + ..., with a = e^z
+// given.  The closed form cancels for small |z|, where the series (error below 2e-9 relative for
+// |z| < 1/8) is used.
+__device__ __forceinline__ float zoh_psi(float zz, float a) {
+  const float series = fmaf(zz, fmaf(zz, fmaf(zz, fmaf(zz, 1.0f / 144.0f, 1.0f / 30.0f), 0.125f), 1.0f / 3.0f), 0.5f);
+  const float closed = fmaf(zz - 1.0f, a, 1.0f) * hw_rcp(zz * zz);
+  return fabsf(zz) < 0.125f ? series : closed;
+}
 
 // LDS written by some lanes of a wave is visible to all lanes of that wave afterwards
 __device__ __forceinline__ void wave_sync() {
@@ -74,23 +98,25 @@ __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-template <bool BF16, int N, int NPL>
+template <bool BF16, int N, int NPL, bool ZOH = false>
 __global__ __launch_bounds__(64 * (N / NPL + kBwdIoWaves)) void scan_bwd_kernel(const BwdArgs p) {
   constexpr int G = N / NPL;
-  constexpr int T = kBwdChunk;
+  constexpr int T = bwd_chunk(NPL, ZOH);
   constexpr int IOT = 64 * kBwdIoWaves;
   constexpr int EPT = T * 64 / IOT;  // tile elements per IO thread
   constexpr int VEC = EPT;           // one vector per IO thread: a row segment of EPT channels
   constexpr int TPR = 64 / VEC;      // IO threads per tile row
   static_assert(TPR * T == IOT, "IO threads cover the chunk tile exactly once");
-  constexpr int H = kBwdHalf<NPL>;
+  constexpr int H = kBwdHalf<NPL, T>;
   constexpr int RED = 2 * NPL * H;  // dB and dC values per lane per reduction round
   static_assert(RED <= 64 && T % H == 0, "one reduction row per lane, whole rounds per chunk");
 
   __shared__ float2 s_dw[2][T][64 + 2];               // (dt, dt x); phase 0 double-buffers
   __shared__ float s_dy0[T][64 + 2];                  // dy * silu(z)
   __shared__ float s_yp[G][T][64 + 4];                // read-out partials C_t.h_t
-  __shared__ float2 s_part[G][T][64 + 2];             // (sum_j g_j B_j, sum_j g_j A_j abar_j h_{t-1,j})
+  // (sum_j g_j B_j fz_j, sum_j g_j A_j abar_j h_{t-1,j}); with ZOH also sum_j g_j abar_j B_j
+  __shared__ float2 s_part[G][T][64 + 2];
+  __shared__ float s_part_z[ZOH ? G : 1][ZOH ? T : 1][64 + 4];
   __shared__ __align__(16) float s_red[G][RED][64 + 4];  // per-wave transpose for dB / dC sums
 
   const int tid = threadIdx.x;
@@ -150,8 +176,12 @@ __global__ __launch_bounds__(64 * (N / NPL + kBwdIoWaves)) void scan_bwd_kernel(
           constexpr int k = decltype(K)::value;
           const float2 dw = s_dw[sb][k][lane];
 #pragma unroll
-          for (int q = 0; q < NPL; ++q)
-            h[q] = fmaf(hw_exp2(dw.x * A2[q]), h[q], row_bcast<k>(Bv[q]) * dw.y);
+          for (int q = 0; q < NPL; ++q) {
+            const float tt = dw.x * A2[q];
+            const float a = hw_exp2(tt);
+            const float u = ZOH ? dw.y * (kLog2e * zoh_factor(tt, a)) : dw.y;
+            h[q] = fmaf(a, h[q], row_bcast<k>(Bv[q]) * u);
+          }
         });
       }
       __syncthreads();
@@ -186,7 +216,10 @@ __global__ __launch_bounds__(64 * (N / NPL + kBwdIoWaves)) void scan_bwd_kernel(
         float yp = 0.0f;
 #pragma unroll
         for (int q = 0; q < NPL; ++q) {
-          hs[k + 1][q] = fmaf(hw_exp2(dw.x * A2[q]), hs[k][q], row_bcast<k>(Bv[q]) * dw.y);
+          const float tt = dw.x * A2[q];
+          const float a = hw_exp2(tt);
+          const float u = ZOH ? dw.y * (kLog2e * zoh_factor(tt, a)) : dw.y;
+          hs[k + 1][q] = fmaf(a, hs[k][q], row_bcast<k>(Bv[q]) * u);
           yp = fmaf(row_bcast<k>(Cv[q]), hs[k + 1][q], yp);
         }
         s_yp[wave][k][lane] = yp;
@@ -200,21 +233,37 @@ __global__ __launch_bounds__(64 * (N / NPL + kBwdIoWaves)) void scan_bwd_kernel(
           const float2 dw = s_dw[0][k][lane];
           const float dt = dw.x, w = dw.y;
           const float dy0 = s_dy0[k][lane];
-          float gB = 0.0f, pdt = 0.0f;
+          float gB = 0.0f, pdt = 0.0f, gBa = 0.0f;
 #pragma unroll
           for (int q = 0; q < NPL; ++q) {
             g[q] = fmaf(an[q], g[q], dy0 * row_bcast<k>(Cv[q]));  // g_t = dy0 C_t + abar_{t+1} g_{t+1}
-            const float a = hw_exp2(dt * A2[q]);                   // abar_t (recomputed)
+            const float tt = dt * A2[q];
+            const float a = hw_exp2(tt);                           // abar_t (recomputed)
             const float ah = a * hs[k][q];                         // abar_t h_{t-1}
-            red[(r * 2 * NPL + q) * (64 + 4) + lane] = g[q] * w;                   // dB: g dt x
+            const float b = row_bcast<k>(Bv[q]);
+            if constexpr (ZOH) {
+              const float fz = kLog2e * zoh_factor(tt, a);         // phi / dt
+              const float gfz = g[q] * fz;
+              red[(r * 2 * NPL + q) * (64 + 4) + lane] = gfz * w;  // dB: g phi x
+              gB = fmaf(gfz, b, gB);                                // sum g phi B / dt
+              gBa = fmaf(g[q] * a, b, gBa);                         // sum g abar B
+              const float gah = g[q] * ah;
+              pdt = fmaf(gah, Araw[q], pdt);
+              // dA += g dt (abar h_{t-1} + B dt x psi(dt A))
+              const float psi = zoh_psi(tt * kLn2, a);
+              dA[q] = fmaf(g[q] * dt, fmaf(b * w, psi, ah), dA[q]);
+            } else {
+              red[(r * 2 * NPL + q) * (64 + 4) + lane] = g[q] * w;  // dB: g dt x
+              gB = fmaf(g[q], b, gB);
+              const float gah = g[q] * ah;
+              pdt = fmaf(gah, Araw[q], pdt);
+              dA[q] = fmaf(gah, dt, dA[q]);
+            }
             red[(r * 2 * NPL + NPL + q) * (64 + 4) + lane] = dy0 * hs[k + 1][q];  // dC: dy0 h_t
-            gB = fmaf(g[q], row_bcast<k>(Bv[q]), gB);
-            const float gah = g[q] * ah;
-            pdt = fmaf(gah, Araw[q], pdt);
-            dA[q] = fmaf(gah, dt, dA[q]);
             an[q] = a;
           }
           s_part[wave][k][lane] = make_float2(gB, pdt);
+          if constexpr (ZOH) s_part_z[wave][k][lane] = gBa;
         });
         // channel sums of this round's dB / dC values: lane q adds row q of the transpose
         wave_sync();
@@ -334,18 +383,19 @@ __global__ __launch_bounds__(64 * (N / NPL + kBwdIoWaves)) void scan_bwd_kernel(
     float dxo[VEC], ddo[VEC], dzo[VEC];
 #pragma unroll
     for (int v = 0; v < VEC; ++v) {
-      float y0 = dsk[v] * xs[v], gB = 0.0f, pdt = 0.0f;
+      float y0 = dsk[v] * xs[v], gB = 0.0f, pdt = 0.0f, gBa = 0.0f;
 #pragma unroll
       for (int gw = 0; gw < G; ++gw) {
         y0 += s_yp[gw][row][col + v];
         const float2 pr = s_part[gw][row][col + v];
         gB += pr.x;
         pdt += pr.y;
+        if constexpr (ZOH) gBa += s_part_z[gw][row][col + v];
       }
       const float dt = s_dw[0][row][col + v].x;
       dzo[v] = has_z ? dyv[v] * y0 * fmaf(zv[v] * sg[v], 1.0f - sg[v], sg[v]) : 0.0f;
       dxo[v] = fmaf(dy0[v], dsk[v], dt * gB);
-      const float ddt = fmaf(gB, xs[v], pdt);
+      const float ddt = fmaf(ZOH ? gBa : gB, xs[v], pdt);
       ddo[v] = p.softplus ? ddt * hw_rcp(1.0f + hw_exp2(-vs[v] * kLog2e)) : ddt;
       if (v < nv) accBias[v] += ddo[v];
     }
@@ -385,6 +435,7 @@ struct BwdReduceArgs {
   int64_t dim;
   int32_t N;
   int32_t ncb;
+  int32_t T;  // chunk length of the main kernel (rows of the dD / dbias partials)
 };
 
 // Sum of n values base[i * stride], i = 0 .. n-1, with 8 independent accumulators so that the
@@ -422,8 +473,8 @@ __global__ __launch_bounds__(256) void scan_bwd_reduce_kernel(const BwdReduceArg
   }
   const int64_t k = j - ndn;
   if (k < p.dim) {
-    const float sd = strided_sum(p.part_d + k, p.batch * kBwdChunk, p.dim);
-    const float sb = strided_sum(p.part_bias + k, p.batch * kBwdChunk, p.dim);
+    const float sd = strided_sum(p.part_d + k, p.batch * p.T, p.dim);
+    const float sb = strided_sum(p.part_bias + k, p.batch * p.T, p.dim);
     if (p.dD) p.dD[k] = sd;
     if (p.dbias) p.dbias[k] = sb;
   }

@@ -112,19 +112,24 @@ CarryKernel carry_kernel(int64_t n) {
 using BwdKernel = void (*)(const ssm::BwdArgs);
 using BwdReduceKernel = void (*)(const ssm::BwdReduceArgs);
 
-// backward instantiations: chains per lane min(N, 4), so at most 4 scan waves for N <= 16
-// (measured on MI355X: 2 chains per lane with 8 scan waves was 13% slower on the 130M shape)
-template <bool BF16>
+// backward instantiations: chains per lane min(N, 4) up to N 16, so at most 4 scan waves
+// (measured on MI355X: 2 chains per lane with 8 scan waves was 13% slower on the 130M shape);
+// N 32 and 64 keep 4 scan waves with 8 and 16 chains per lane on 8- and 4-step chunks
+template <bool BF16, bool ZOH>
 BwdKernel bwd_kernel(int64_t n) {
   switch (n) {
-    case 1: return ssm::scan_bwd_kernel<BF16, 1, 1>;
-    case 2: return ssm::scan_bwd_kernel<BF16, 2, 2>;
-    case 4: return ssm::scan_bwd_kernel<BF16, 4, 4>;
-    case 8: return ssm::scan_bwd_kernel<BF16, 8, 4>;
-    case 16: return ssm::scan_bwd_kernel<BF16, 16, 4>;
+    case 1: return ssm::scan_bwd_kernel<BF16, 1, 1, ZOH>;
+    case 2: return ssm::scan_bwd_kernel<BF16, 2, 2, ZOH>;
+    case 4: return ssm::scan_bwd_kernel<BF16, 4, 4, ZOH>;
+    case 8: return ssm::scan_bwd_kernel<BF16, 8, 4, ZOH>;
+    case 16: return ssm::scan_bwd_kernel<BF16, 16, 4, ZOH>;
+    case 32: return ssm::scan_bwd_kernel<BF16, 32, 8, ZOH>;
+    case 64: return ssm::scan_bwd_kernel<BF16, 64, 16, ZOH>;
     default: return nullptr;
   }
 }
+
+int bwd_npl(int64_t n) { return n <= 4 ? static_cast<int>(n) : (n <= 16 ? 4 : static_cast<int>(n / 4)); }
 
 using ConvKernel = void (*)(const ssm::ConvArgs);
 using ConvUpdateKernel = void (*)(const ssm::ConvUpdateArgs);
@@ -589,13 +594,29 @@ ssm_status_t ssm_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t ds
                           const float* D, const void* z, const float* delta_bias, int delta_softplus,
                           const void* dy, void* dx, void* ddelta, float* dA, void* dB, void* dC, float* dD,
                           void* dz, float* ddelta_bias, void* stream) {
+  return ssm_scan_bwd_ex(batch, seqlen, dim, dstate, dtype, x, delta, A, B, C, D, z, delta_bias, delta_softplus, dy,
+                         dx, ddelta, dA, dB, dC, dD, dz, ddelta_bias, stream, nullptr);
+}
+
+ssm_status_t ssm_scan_bwd_ex(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, ssm_dtype_t dtype,
+                             const void* x, const void* delta, const float* A, const void* B, const void* C,
+                             const float* D, const void* z, const float* delta_bias, int delta_softplus,
+                             const void* dy, void* dx, void* ddelta, float* dA, void* dB, void* dC, float* dD,
+                             void* dz, float* ddelta_bias, void* stream, const ssm_bwd_opts_t* opts) {
   g_err[0] = '\0';
+  if (opts) {
+    if (opts->bbar_mode != SSM_BBAR_DELTA_B && opts->bbar_mode != SSM_BBAR_ZOH)
+      return fail(SSM_ERR_UNSUPPORTED, "bbar_mode %d is not SSM_BBAR_DELTA_B or SSM_BBAR_ZOH", (int)opts->bbar_mode);
+    for (int32_t r : opts->reserved)
+      if (r != 0) return fail(SSM_ERR_INVALID_ARG, "ssm_bwd_opts_t.reserved must be zero");
+  }
+  const bool zoh = opts && opts->bbar_mode == SSM_BBAR_ZOH;
   if (batch < 0 || seqlen < 0 || dim < 0 || dstate < 0)
     return fail(SSM_ERR_INVALID_ARG, "negative size (batch=%lld seqlen=%lld dim=%lld dstate=%lld)",
                 (long long)batch, (long long)seqlen, (long long)dim, (long long)dstate);
   if (dtype != SSM_F32 && dtype != SSM_BF16) return fail(SSM_ERR_UNSUPPORTED, "unknown dtype %d", (int)dtype);
-  if (dstate != 1 && dstate != 2 && dstate != 4 && dstate != 8 && dstate != 16)
-    return fail(SSM_ERR_UNSUPPORTED, "dstate %lld not in {1,2,4,8,16} for the backward pass", (long long)dstate);
+  if (!dstate_supported(dstate))
+    return fail(SSM_ERR_UNSUPPORTED, "dstate %lld not in {1,2,4,8,16,32,64}", (long long)dstate);
   const int64_t es = dtype == SSM_BF16 ? 2 : 4;
   int64_t nch, n_bl, n_bld, n_bln;
   if (!mul_ok(batch, dim, &nch) || !mul_ok(batch, seqlen, &n_bl) || !mul_ok(n_bl, dim * es, &n_bld) ||
@@ -627,7 +648,8 @@ ssm_status_t ssm_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t ds
   }
 
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const int64_t T = ssm::kBwdChunk;
+  const int npl = bwd_npl(dstate);
+  const int64_t T = ssm::bwd_chunk(npl, zoh);
   const int64_t nc = empty ? 0 : (seqlen + T - 1) / T;
   const int64_t ncb = (dim + 63) / 64;
   // scratch: chunk-start states, dB/dC channel-block partials, dA / dD / dbias batch partials
@@ -652,11 +674,11 @@ ssm_status_t ssm_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t ds
   const int64_t vbytes = 4 * es;  // the IO waves move 4 channels per access
   a.vec_ok = (dim % 4 == 0) && aligned(x, vbytes) && aligned(delta, vbytes) && aligned(dy, vbytes) &&
              aligned(dx, vbytes) && aligned(ddelta, vbytes) && (!z || (aligned(z, vbytes) && aligned(dz, vbytes)));
-  const int npl = dstate < 4 ? static_cast<int>(dstate) : 4;
   const unsigned threads = static_cast<unsigned>(64 * (dstate / npl + ssm::kBwdIoWaves));
   if (!empty) {
     if (batch * ncb > 0x7fffffff) return fail(SSM_ERR_UNSUPPORTED, "grid too large");
-    const BwdKernel k = dtype == SSM_BF16 ? bwd_kernel<true>(dstate) : bwd_kernel<false>(dstate);
+    const BwdKernel k = dtype == SSM_BF16 ? (zoh ? bwd_kernel<true, true>(dstate) : bwd_kernel<true, false>(dstate))
+                                          : (zoh ? bwd_kernel<false, true>(dstate) : bwd_kernel<false, false>(dstate));
     hipLaunchKernelGGL(k, dim3(static_cast<unsigned>(batch * ncb)), dim3(threads), 0, st, a);
     if ((s = check_launch("scan backward")) != SSM_OK) return s;
   } else if (n_a + 2 * n_d > 0) {
@@ -670,6 +692,7 @@ ssm_status_t ssm_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t ds
   r.dB = dB; r.dC = dC; r.dA = dA; r.dD = dD; r.dbias = ddelta_bias;
   r.batch = batch; r.seqlen = seqlen; r.dim = dim; r.N = static_cast<int32_t>(dstate);
   r.ncb = static_cast<int32_t>(ncb);
+  r.T = static_cast<int32_t>(T);
   const int64_t nred = 2 * batch * seqlen * dstate + dim * dstate + dim;
   const BwdReduceKernel rk =
       dtype == SSM_BF16 ? ssm::scan_bwd_reduce_kernel<true> : ssm::scan_bwd_reduce_kernel<false>;

@@ -303,3 +303,14 @@ def test_ssd_update_validation(lib, kw, code):
 
 def test_ssd_update_nothing_to_do(lib):
     assert ssd_update(lib, batch=0, state=None, x=None, dt=None, B=None, C=None, y=None) == OK
+
+
+def test_bwd_opts_validation(lib):
+    def bwd(opts, dstate=16):
+        args = [2, 8, 16, dstate, F32] + [fake(i) for i in range(8)] + [1] + [fake(8 + i) for i in range(9)] + [None]
+        return lib.ssm_scan_bwd_ex(*args, ctypes.byref(opts))
+    assert bwd(ssm.BwdOpts(2)) == UNSUPPORTED and "bbar_mode" in err(lib)
+    bad = ssm.BwdOpts(0)
+    bad.reserved[6] = 1
+    assert bwd(bad) == INVALID and "reserved" in err(lib)
+    assert bwd(ssm.BwdOpts(0), dstate=128) == UNSUPPORTED and "dstate" in err(lib)

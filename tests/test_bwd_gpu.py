@@ -37,21 +37,21 @@ def dy_for(shape, dtype, seed):
     return W.f32_to_bf16_bits(dy) if dtype == "bf16" else dy
 
 
-def bwd_gpu(t, dy, softplus):
+def bwd_gpu(t, dy, softplus, zoh=False):
     import selective_state_space_61_amd as ssm
     d = {k: to_dev(v) for k, v in t.items()}
     g = ssm.ssm_scan_bwd(d["x"], d["delta"], d["A"], d["B"], d["C"], to_dev(dy), D=d["D"], z=d["z"],
-                         delta_bias=d["delta_bias"], delta_softplus=softplus)
+                         delta_bias=d["delta_bias"], delta_softplus=softplus, zoh=zoh)
     torch.cuda.synchronize()
     return g
 
 
-def compare(o, t, dy, dtype, softplus, what):
+def compare(o, t, dy, dtype, softplus, what, zoh=False):
     say(f"[case] {what}")
-    g = bwd_gpu(t, dy, softplus)
+    g = bwd_gpu(t, dy, softplus, zoh)
     dy64 = W.bf16_bits_to_f32(dy).astype(np.float64) if dy.dtype == np.uint16 else dy.astype(np.float64)
     ref = o.scan_bwd(t["x"], t["delta"], t["A"], t["B"], t["C"], dy64, D=t["D"], z=t["z"],
-                     delta_bias=t["delta_bias"], delta_softplus=softplus)
+                     delta_bias=t["delta_bias"], delta_softplus=softplus, zoh=zoh)
     for k, r in ref.items():
         if r is None:
             assert g[k] is None
@@ -61,11 +61,36 @@ def compare(o, t, dy, dtype, softplus, what):
     return g
 
 
+@pytest.mark.parametrize("zoh", [False, True], ids=["delta_b", "zoh"])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("N", [1, 2, 4, 8, 16])
-def test_dstates(o, dtype, N):
+@pytest.mark.parametrize("N", [1, 2, 4, 8, 16, 32, 64])
+def test_dstates(o, dtype, N, zoh):
     t = W.scan_inputs(2, 70, 96, N, dtype, seed=N + 300)
-    compare(o, t, dy_for((2, 70, 96), dtype, N), dtype, True, f"bwd N={N} {dtype}")
+    compare(o, t, dy_for((2, 70, 96), dtype, N), dtype, True, f"bwd N={N} {dtype} zoh={zoh}", zoh=zoh)
+
+
+@pytest.mark.parametrize("N", [16, 32, 64])
+@pytest.mark.parametrize("shape", [(1, 17, 13), (2, 45, 130), (1, 3, 64)])
+def test_zoh_ragged(o, N, shape):
+    """Exact-ZOH backward on ragged shapes (L not a multiple of the chunk, dim not of 64)."""
+    batch, L, dim = shape
+    t = W.scan_inputs(batch, L, dim, N, "f32", seed=L * 7 + dim + N)
+    compare(o, t, dy_for((batch, L, dim), "f32", L + N), "f32", True, f"bwd zoh ragged {shape} N={N}", zoh=True)
+
+
+@pytest.mark.parametrize("variant", ["genomics_steps", "softplus_off_no_bias", "bare"])
+def test_zoh_variants(o, variant):
+    """Exact-ZOH backward: small steps (dt A down to ~1e-4, where phi's derivative in A takes the
+    series), softplus off without a bias, and no z / D / bias."""
+    if variant == "genomics_steps":
+        t = W.scan_inputs(1, 200, 64, 16, "f32", seed=91, recipe="genomics", has_bias=False)
+        softplus = False
+    else:
+        softplus = False
+        t = W.scan_inputs(2, 60, 72, 16, "f32", seed=92, has_bias=False, has_z=variant != "bare",
+                          has_D=variant != "bare")
+        t["delta"] = np.abs(t["delta"])
+    compare(o, t, dy_for(t["x"].shape, "f32", 93), "f32", softplus, f"bwd zoh {variant}", zoh=True)
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
