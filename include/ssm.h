@@ -139,9 +139,23 @@ typedef enum { SSM_BBAR_DELTA_B = 0, SSM_BBAR_ZOH = 1 } ssm_bbar_mode_t;
  *                             per-(t, d) work on a SIMD of its own, and
  *                             16 x channel_groups channels per workgroup:
  *                             dstate 16, SSM_BBAR_DELTA_B and one segment
- *                             only (else SSM_ERR_UNSUPPORTED).
+ *                             only (else SSM_ERR_UNSUPPORTED);
+ *   SSM_LAYOUT_TIME_SCAN      time parallel inside a chunk: one workgroup per
+ *                             (batch row, channel), each lane a block of 4 or
+ *                             8 steps (chunk_steps 256 or 512), the blocks
+ *                             joined by a wave64 associative scan of
+ *                             (abar, state) pairs ("mamba->jamba" sec. 2.3)
+ *                             and a carry across chunks; for few channels and
+ *                             long sequences.  Never chosen automatically:
+ *                             measured slower than the sequence split.  Same
+ *                             limits as SSM_LAYOUT_STATE_ROWS.
  */
-typedef enum { SSM_LAYOUT_AUTO = 0, SSM_LAYOUT_CHANNEL_LANES = 1, SSM_LAYOUT_STATE_ROWS = 2 } ssm_scan_layout_t;
+typedef enum {
+  SSM_LAYOUT_AUTO = 0,
+  SSM_LAYOUT_CHANNEL_LANES = 1,
+  SSM_LAYOUT_STATE_ROWS = 2,
+  SSM_LAYOUT_TIME_SCAN = 3
+} ssm_scan_layout_t;
 
 /*
  * Launch-shape overrides for ssm_scan_fwd.  Every field 0 means "choose

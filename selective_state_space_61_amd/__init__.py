@@ -58,8 +58,9 @@ class SsdOpts(ctypes.Structure):
 
 
 SSM_BBAR_DELTA_B, SSM_BBAR_ZOH = 0, 1
-SSM_LAYOUT_AUTO, SSM_LAYOUT_CHANNEL_LANES, SSM_LAYOUT_STATE_ROWS = 0, 1, 2
-LAYOUTS = {"auto": SSM_LAYOUT_AUTO, "channel_lanes": SSM_LAYOUT_CHANNEL_LANES, "state_rows": SSM_LAYOUT_STATE_ROWS}
+SSM_LAYOUT_AUTO, SSM_LAYOUT_CHANNEL_LANES, SSM_LAYOUT_STATE_ROWS, SSM_LAYOUT_TIME_SCAN = 0, 1, 2, 3
+LAYOUTS = {"auto": SSM_LAYOUT_AUTO, "channel_lanes": SSM_LAYOUT_CHANNEL_LANES, "state_rows": SSM_LAYOUT_STATE_ROWS,
+           "time_scan": SSM_LAYOUT_TIME_SCAN}
 
 
 _lib_handle = None
@@ -156,7 +157,7 @@ def ssm_scan_fwd(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch
                  stream=None, _noalloc: bool = False) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Selective scan forward (include/ssm.h: ssm_scan_fwd).  Returns (y, last_state); last_state
     is None when return_last_state is False and none was passed in.  chains_per_lane, segments,
-    chunk_steps, layout ("auto", "channel_lanes", "state_rows") and channel_groups override the
+    chunk_steps, layout ("auto", "channel_lanes", "state_rows", "time_scan") and channel_groups override the
     launch shape (0 / "auto" = automatic); zoh selects the exact
     zero-order-hold input term (SSM_BBAR_ZOH) instead of Delta B."""
     lib = load_library()

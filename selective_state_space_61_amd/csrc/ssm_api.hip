@@ -13,6 +13,7 @@
 #include "../../include/ssm.h"
 #include "scan_table.hpp"
 #include "scan_rows_table.hpp"
+#include "scan_time_table.hpp"
 #include "state_update.hpp"
 #include "conv1d.hpp"
 #include "scan_bwd.hpp"
@@ -301,13 +302,35 @@ ssm_status_t scan_fwd_impl(int64_t batch, int64_t seqlen, int64_t dim, int64_t d
     for (int32_t r : opts->reserved)
       if (r != 0) return fail(SSM_ERR_INVALID_ARG, "ssm_scan_opts_t.reserved must be zero");
     if (opts->layout != SSM_LAYOUT_AUTO && opts->layout != SSM_LAYOUT_CHANNEL_LANES &&
-        opts->layout != SSM_LAYOUT_STATE_ROWS)
+        opts->layout != SSM_LAYOUT_STATE_ROWS && opts->layout != SSM_LAYOUT_TIME_SCAN)
       return fail(SSM_ERR_UNSUPPORTED, "layout %d is not an ssm_scan_layout_t", (int)opts->layout);
     if (opts->channel_groups < 0 || opts->channel_groups > ssm::kRowsMaxScanWaves)
       return fail(SSM_ERR_UNSUPPORTED, "channel_groups %d not in 0..%d", (int)opts->channel_groups,
                   ssm::kRowsMaxScanWaves);
   }
   const bool split_auto = !(opts && opts->segments > 0) && base_wgs < 160;
+
+  // The time-parallel layout (on request only: measured slower than the split sequence on the
+  // genomics shape, which is the case it targets).
+  if (opts && opts->layout == SSM_LAYOUT_TIME_SCAN) {
+    if (dstate != 16 || opts->bbar_mode != SSM_BBAR_DELTA_B || opts->segments > 1 || opts->channel_groups != 0 ||
+        (opts->chains_per_lane != 0 && opts->chains_per_lane != 4))
+      return fail(SSM_ERR_UNSUPPORTED,
+                  "SSM_LAYOUT_TIME_SCAN needs dstate 16, SSM_BBAR_DELTA_B, one segment and no channel groups");
+    if (opts->chunk_steps != 0 && opts->chunk_steps != 256 && opts->chunk_steps != 512)
+      return fail(SSM_ERR_UNSUPPORTED, "chunk_steps %d is not 256 or 512 for SSM_LAYOUT_TIME_SCAN",
+                  (int)opts->chunk_steps);
+    if (nch > 0x7fffffff) return fail(SSM_ERR_UNSUPPORTED, "grid of %lld workgroups is too large", (long long)nch);
+    const ssm::TimeKernel tk = ssm::time_kernel(dtype == SSM_BF16, opts->chunk_steps == 256 ? 4 : 8);
+    ssm::ScanArgs a{};
+    a.x = x; a.delta = delta; a.A = A; a.B = B; a.C = C; a.Dskip = D; a.z = z; a.delta_bias = delta_bias;
+    a.y = y; a.last_state = last_state;
+    a.batch = batch; a.seqlen = seqlen; a.dim = dim; a.seg_len = seqlen;
+    a.nseg = 1;
+    a.softplus = delta_softplus ? 1 : 0;
+    hipLaunchKernelGGL(tk, dim3(static_cast<unsigned>(nch)), dim3(ssm::kTimeThreads), 0, st, a);
+    return check_launch("scan (time parallel)");
+  }
 
   // The state-row layout: dstate 16, Delta B, whole sequences (no split).  The automatic choice
   // takes it whenever it applies.

@@ -138,7 +138,7 @@ def test_scan_opts_validation(lib):
     # the layout override: unknown values, the state-row layout's limits, channel groups with the
     # channel-lane layout
     rows, lanes = ssm.SSM_LAYOUT_STATE_ROWS, ssm.SSM_LAYOUT_CHANNEL_LANES
-    assert scan(lib, dstate=16, opts=ssm.ScanOpts(0, 0, 0, 0, 3)) == UNSUPPORTED and "layout" in err(lib)
+    assert scan(lib, dstate=16, opts=ssm.ScanOpts(0, 0, 0, 0, 4)) == UNSUPPORTED and "layout" in err(lib)
     assert scan(lib, dstate=16, opts=ssm.ScanOpts(0, 0, 0, 0, rows, 7)) == UNSUPPORTED and "channel_groups" in err(lib)
     assert scan(lib, dstate=16, opts=ssm.ScanOpts(0, 0, 0, 0, rows, -1)) == UNSUPPORTED
     assert scan(lib, dstate=8, opts=ssm.ScanOpts(0, 0, 0, 0, rows)) == UNSUPPORTED and "STATE_ROWS" in err(lib)
@@ -314,3 +314,12 @@ def test_bwd_opts_validation(lib):
     bad.reserved[6] = 1
     assert bwd(bad) == INVALID and "reserved" in err(lib)
     assert bwd(ssm.BwdOpts(0), dstate=128) == UNSUPPORTED and "dstate" in err(lib)
+
+
+def test_time_scan_opts_validation(lib):
+    ts = ssm.SSM_LAYOUT_TIME_SCAN
+    assert scan(lib, dstate=8, opts=ssm.ScanOpts(0, 0, 0, 0, ts)) == UNSUPPORTED and "TIME_SCAN" in err(lib)
+    assert scan(lib, dstate=16, opts=ssm.ScanOpts(0, 0, 0, ssm.SSM_BBAR_ZOH, ts)) == UNSUPPORTED
+    assert scan(lib, dstate=16, opts=ssm.ScanOpts(0, 2, 0, 0, ts)) == UNSUPPORTED
+    assert scan(lib, dstate=16, opts=ssm.ScanOpts(0, 0, 0, 0, ts, 2)) == UNSUPPORTED
+    assert scan(lib, dstate=16, opts=ssm.ScanOpts(0, 0, 128, 0, ts)) == UNSUPPORTED and "chunk_steps" in err(lib)

@@ -364,3 +364,36 @@ def test_state_rows_unaligned_views_and_empty(o):
     t0 = W.scan_inputs(2, 0, 64, 16, "f32", seed=9)
     _, s0, _ = scan_on_gpu(t0, True, layout="state_rows", channel_groups=4)
     assert torch.count_nonzero(s0).item() == 0
+
+
+# ---------------------------------------------------------------------------------------------------
+# the time-parallel layout (SSM_LAYOUT_TIME_SCAN): wave64 associative scan of (abar, state) pairs
+# ---------------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("chunk", [256, 512])
+def test_time_scan_layout(o, dtype, chunk):
+    for k, (batch, L, dim) in enumerate([(1, 1000, 8), (2, 513, 3), (1, 1, 5), (1, 4096, 16), (3, 37, 2)]):
+        say(f"[case] time scan {dtype} chunk={chunk} shape={(batch, L, dim)}")
+        t = W.scan_inputs(batch, L, dim, 16, dtype, seed=700 + k + chunk)
+        y, st, _ = scan_on_gpu(t, True, layout="time_scan", chunk_steps=chunk)
+        y_ref, st_ref = o.scan(t["x"], t["delta"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"],
+                               delta_bias=t["delta_bias"], delta_softplus=True, nthreads=THREADS)
+        assert_close(to_host(y), y_ref, TOL[dtype], "time scan y")
+        assert_close(to_host(st), st_ref, TOL[dtype], "time scan last_state")
+
+
+@pytest.mark.parametrize("variant", ["genomics", "impulse", "no_z_no_D"])
+def test_time_scan_long(o, variant):
+    """The genomics recipe over 2^17 steps (256 chunks of 512 carried), its impulse-carry form, and
+    a bare variant."""
+    L, dim = 1 << 17, 24
+    if variant == "no_z_no_D":
+        t = W.scan_inputs(1, L, dim, 16, "f32", seed=81, recipe="genomics", has_bias=False, has_z=False, has_D=False)
+    else:
+        t = W.scan_inputs(1, L, dim, 16, "f32", seed=80, recipe="genomics", has_bias=False)
+    if variant == "impulse":
+        t["delta"] = np.zeros_like(t["delta"])
+        t["delta"][:, 0, :] = 1.0
+    say(f"[case] time scan long {variant} (1, {L}, {dim})")
+    y, st, _ = scan_on_gpu(t, False, layout="time_scan")
+    scan_whole(o, t, y, st, False, TOL["f32"], f"time scan {variant}", block=dim, threads=THREADS)
