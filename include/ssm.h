@@ -167,7 +167,8 @@ typedef enum {
  *   segments         number of sequence segments scanned in parallel (>= 1);
  *   chunk_steps      time steps staged per LDS tile: 16 or 32 (32 needs at most
  *                    4 scan waves, i.e. dstate / chains_per_lane <= 4, and
- *                    bbar_mode SSM_BBAR_DELTA_B).
+ *                    bbar_mode SSM_BBAR_DELTA_B; with SSM_LAYOUT_STATE_ROWS it
+ *                    needs channel_groups <= 3).
  *   bbar_mode        the discretised input term (not a launch-shape choice:
  *                    it changes the result), see ssm_bbar_mode_t.
  *   layout           ssm_scan_layout_t;

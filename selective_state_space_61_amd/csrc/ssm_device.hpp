@@ -112,6 +112,12 @@ struct RawVec {
     if constexpr (BF16) return (v & 1) ? bf16_hi(w[v >> 1]) : bf16_lo(w[v >> 1]);
     else return __builtin_bit_cast(float, w[v]);
   }
+
+  // an (empty) use of the words: the compiler waits for their load here, on every path through it
+  __device__ __forceinline__ void consume() const {
+#pragma unroll
+    for (int i = 0; i < kWords; ++i) asm volatile("" ::"v"(w[i]));
+  }
 };
 
 // Stores VEC fp32 values as (bf16 | fp32) at base[idx ...]; only the first `nvalid` when the
@@ -284,6 +290,22 @@ struct BcRow {
 #pragma unroll
     for (int i = 0; i < kWords; ++i) w[i] = 0u;
     if (!valid) return;
+    if constexpr (BF16 && NPL == 1) {
+      w[0] = static_cast<const uint16_t*>(tensor)[e];
+    } else if constexpr (BF16) {
+      const uint32_t* p = reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(tensor) + e);
+#pragma unroll
+      for (int i = 0; i < kWords; ++i) w[i] = p[i];
+    } else {
+      const uint32_t* p = static_cast<const uint32_t*>(tensor) + e;
+#pragma unroll
+      for (int i = 0; i < kWords; ++i) w[i] = p[i];
+    }
+  }
+
+  // the same words loaded on every path (e must be in range): no merge with a zero fill, so the
+  // compiler never copies the destination registers, which would wait for the load at once
+  __device__ __forceinline__ void load_in_range(const void* __restrict__ tensor, int64_t e) {
     if constexpr (BF16 && NPL == 1) {
       w[0] = static_cast<const uint16_t*>(tensor)[e];
     } else if constexpr (BF16) {
