@@ -63,17 +63,6 @@ constexpr int rows_lds_bytes(int S, int ch) {
          + 16 * S * 4;                             // D
 }
 
-constexpr int kXcds = 8;  // MI355X: 8 accelerator complex dies, workgroups dealt round robin
-
-// Logical workgroup index for hardware index i of n: the first n - n % 8 workgroups are regrouped
-// so that the hardware indices i with i % 8 == x (one XCD) take logical indices x * (n / 8) ..
-// (x + 1) * (n / 8) - 1; the last n % 8 keep their index.  A bijection on [0, n).
-__device__ __forceinline__ int64_t xcd_local(int64_t i, int64_t n) {
-  const int64_t per = n / kXcds;
-  if (i >= per * kXcds) return i;
-  return (i % kXcds) * per + i / kXcds;
-}
-
 template <bool BF16, int S, int CH>
 __global__ __launch_bounds__(64 * kRowsWaves) void scan_rows_kernel(const ScanArgs p) {
   constexpr int N = 16, NPL = 4;

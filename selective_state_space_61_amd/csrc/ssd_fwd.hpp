@@ -189,7 +189,9 @@ void ssd_chunk_kernel(const SsdArgs p) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, q = lane >> 4;
-  const int64_t blk = blockIdx.x;
+  // The heads of a group read the same B and C rows: the logical index is permuted so that
+  // consecutive heads (and slices) share an XCD and its L2, which then fetches those rows once.
+  const int64_t blk = xcd_local(blockIdx.x, gridDim.x);
   const int slice = static_cast<int>(blk % p.nslices);
   const int64_t bhs = blk / p.nslices;
   const int64_t nbh = p.batch * p.nheads;
@@ -216,42 +218,44 @@ void ssd_chunk_kernel(const SsdArgs p) {
   const int64_t xs = H * P, bs = G * N;
 
   // Registers that carry the next chunk's inputs while the current one is computed.  A piece is
-  // 16 bytes of one row; consecutive threads take consecutive pieces of a row (coalesced).
-  // x and z of the chunk whose epilogue is pending stay in xe, ze (same pieces as rx, rz).
-  ssd_u32x4_t rb[kBCPer], rc[kBCPer], rx[kXPer], rz[kXPer], xe[kXPer], ze[kXPer];
+  // 16 bytes of one row; consecutive threads take consecutive pieces of a row (coalesced).  x and
+  // z come in two register sets, alternating between chunks: the set of the chunk whose epilogue
+  // is pending takes the next chunk's loads once that epilogue has run (no copies between sets).
+  ssd_u32x4_t rb[kBCPer], rc[kBCPer], rx[2][kXPer], rz[2][kXPer];
   uint32_t rdt = 0u;
 #pragma unroll
-  for (int u = 0; u < kXPer; ++u) rz[u] = ze[u] = xe[u] = ssd_u32x4_t{0u, 0u, 0u, 0u};
+  for (int u = 0; u < kXPer; ++u) rz[0][u] = rz[1][u] = rx[1][u] = ssd_u32x4_t{0u, 0u, 0u, 0u};
+  using Set0 = std::integral_constant<int, 0>;
+  using Set1 = std::integral_constant<int, 1>;
 
   float dsum = 0.0f;  // sum of dt A log2(e) over the chunks run
 
-  // FULL: all 64 steps of the chunk are inside the sequence (no bounds checks).
-  auto load_chunk = [&](int64_t t0, auto full) {
-    constexpr bool FULL = decltype(full)::value;
+  // Steps past the end of the sequence load the last step's rows (always in range, so every
+  // lane loads on every path and no register merge makes the compiler wait right after a load):
+  // their dt is staged as 0, which zeroes their weighted X, their columns of M and their share of
+  // the state, and their output rows are not stored.  Without a gate the z pieces are x's.
+  const uint16_t* zsrc = zg ? zg : xg;
+  auto load_chunk = [&](int64_t t0, auto SET) {
+    constexpr int st = decltype(SET)::value;
 #pragma unroll
     for (int u = 0; u < kBCPer; ++u) {
       const int k = tid + u * T;
       const int c8 = k % (N / 8), j = k / (N / 8);
-      const int64_t t = t0 + j;
-      const bool ok = FULL || t < L;
-      rb[u] = ok ? *reinterpret_cast<const ssd_u32x4_t*>(bg + t * bs + 8 * c8) : ssd_u32x4_t{0u, 0u, 0u, 0u};
-      if constexpr (OUT)
-        rc[u] = ok ? *reinterpret_cast<const ssd_u32x4_t*>(cg + t * bs + 8 * c8) : ssd_u32x4_t{0u, 0u, 0u, 0u};
+      const int64_t t = t0 + j < L ? t0 + j : L - 1;
+      rb[u] = *reinterpret_cast<const ssd_u32x4_t*>(bg + t * bs + 8 * c8);
+      if constexpr (OUT) rc[u] = *reinterpret_cast<const ssd_u32x4_t*>(cg + t * bs + 8 * c8);
     }
 #pragma unroll
     for (int u = 0; u < kXPer; ++u) {
       const int k = tid + u * T;
       const int p8 = k % (PS / 8), j = k / (PS / 8);
-      const int64_t t = t0 + j;
-      rx[u] = (FULL || t < L) ? *reinterpret_cast<const ssd_u32x4_t*>(xg + t * xs + 8 * p8)
-                              : ssd_u32x4_t{0u, 0u, 0u, 0u};
-      if (OUT && zg)
-        rz[u] = (FULL || t < L) ? *reinterpret_cast<const ssd_u32x4_t*>(zg + t * xs + 8 * p8)
-                                : ssd_u32x4_t{0u, 0u, 0u, 0u};
+      const int64_t t = t0 + j < L ? t0 + j : L - 1;
+      rx[st][u] = *reinterpret_cast<const ssd_u32x4_t*>(xg + t * xs + 8 * p8);
+      if constexpr (OUT) rz[st][u] = *reinterpret_cast<const ssd_u32x4_t*>(zsrc + t * xs + 8 * p8);
     }
     // wave w loads the raw dt of steps kDtPer w .. +kDtPer-1 (lanes below kDtPer)
     const int64_t td = t0 + kDtPer * wave + lane;
-    rdt = (lane < kDtPer && (FULL || td < L)) ? dtg[td * H] : 0u;
+    rdt = lane < kDtPer ? dtg[(td < L ? td : L - 1) * H] : 0u;
   };
   // The raw dt just loaded goes to LDS once it has arrived (read by every wave at the next stage).
   auto publish_dt = [&]() {
@@ -259,9 +263,11 @@ void ssd_chunk_kernel(const SsdArgs p) {
   };
 
   // Skip term, gate and store of the chunk at step te0 whose Y sits in s_y: each thread takes the
-  // same 16-byte pieces it loaded (x in xe, z in ze), 8 channels of one step.  FULL as in load_chunk.
-  auto epilogue = [&](int64_t te0, auto full) {
+  // same 16-byte pieces it loaded (x and z in register set SET), 8 channels of one step.  FULL:
+  // all 64 steps of the chunk are inside the sequence (no bounds checks).
+  auto epilogue = [&](int64_t te0, auto full, auto SET) {
     constexpr bool FULL = decltype(full)::value;
+    constexpr int st = decltype(SET)::value;
 #pragma unroll
     for (int u = 0; u < kXPer; ++u) {
       const int k = tid + u * T;
@@ -273,8 +279,8 @@ void ssd_chunk_kernel(const SsdArgs p) {
         float yv[8] = {y0[0], y0[1], y0[2], y0[3], y1[0], y1[1], y1[2], y1[3]};
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float xr = (e & 1) ? bf16_hi(xe[u][e / 2]) : bf16_lo(xe[u][e / 2]);
-          const float zr = (e & 1) ? bf16_hi(ze[u][e / 2]) : bf16_lo(ze[u][e / 2]);
+          const float xr = (e & 1) ? bf16_hi(rx[st][u][e / 2]) : bf16_lo(rx[st][u][e / 2]);
+          const float zr = (e & 1) ? bf16_hi(rz[st][u][e / 2]) : bf16_lo(rz[st][u][e / 2]);
           yv[e] = fmaf(Dh, xr, yv[e]) * (zg ? silu_f32(zr) : 1.0f);
         }
         // y is written once and read by the next layer, not here: a non-temporal store keeps the
@@ -288,7 +294,8 @@ void ssd_chunk_kernel(const SsdArgs p) {
   };
 
   // Writes the chunk held in registers to LDS.
-  auto stage_chunk = [&](int64_t t0) {
+  auto stage_chunk = [&](int64_t t0, auto SET) {
+    constexpr int st = decltype(SET)::value;
     // dt and the cumulative decay: lane l of every wave holds step l of the chunk
     const float v = bf16_lo(s_dtraw[lane]) + bias;
     const float dtv = t0 + lane < L ? (p.softplus ? softplus_f32(v) : v) : 0.0f;
@@ -313,15 +320,13 @@ void ssd_chunk_kernel(const SsdArgs p) {
       const int p8 = k % (PS / 8), j = k / (PS / 8);
       const float w = __shfl(wgt, j);
       if constexpr (OUT) {
-        *reinterpret_cast<ssd_u32x4_t*>(&s_x[j * LDX + 8 * p8]) = rx[u];
-        xe[u] = rx[u];
-        ze[u] = rz[u];
+        *reinterpret_cast<ssd_u32x4_t*>(&s_x[j * LDX + 8 * p8]) = rx[st][u];
       }
       *reinterpret_cast<ssd_u32x4_t*>(&s_xw[j * LDX + 8 * p8]) =
-          ssd_u32x4_t{pack_bf16x2(bf16_elem<0>(rx[u]) * w, bf16_elem<1>(rx[u]) * w),
-                      pack_bf16x2(bf16_elem<2>(rx[u]) * w, bf16_elem<3>(rx[u]) * w),
-                      pack_bf16x2(bf16_elem<4>(rx[u]) * w, bf16_elem<5>(rx[u]) * w),
-                      pack_bf16x2(bf16_elem<6>(rx[u]) * w, bf16_elem<7>(rx[u]) * w)};
+          ssd_u32x4_t{pack_bf16x2(bf16_elem<0>(rx[st][u]) * w, bf16_elem<1>(rx[st][u]) * w),
+                      pack_bf16x2(bf16_elem<2>(rx[st][u]) * w, bf16_elem<3>(rx[st][u]) * w),
+                      pack_bf16x2(bf16_elem<4>(rx[st][u]) * w, bf16_elem<5>(rx[st][u]) * w),
+                      pack_bf16x2(bf16_elem<6>(rx[st][u]) * w, bf16_elem<7>(rx[st][u]) * w)};
     }
   };
 
@@ -367,20 +372,18 @@ void ssd_chunk_kernel(const SsdArgs p) {
   using Full = std::integral_constant<bool, true>;
   using Ragged = std::integral_constant<bool, false>;
   if (cbeg < cend) {
-    if ((cbeg + 1) * Q <= L) load_chunk(cbeg * Q, Full{});
-    else load_chunk(cbeg * Q, Ragged{});
+    load_chunk(cbeg * Q, Set0{});
     publish_dt();
   }
-  for (int64_t c = cbeg; c < cend; ++c) {
+  // chunk c, whose x and z sit in register set SET (chunk cbeg in set 0, then alternating)
+  auto chunk = [&](int64_t c, auto SET) {
+    using Prev = std::integral_constant<int, 1 - decltype(SET)::value>;
     const int64_t t0 = c * Q;
     __syncthreads();  // every wave is done with the previous chunk's tiles
-    if (OUT && c > cbeg) epilogue(t0 - Q, Full{});  // the chunk before this one is whole
-    stage_chunk(t0);
+    if (OUT && c > cbeg) epilogue(t0 - Q, Full{}, Prev{});  // the chunk before this one is whole
+    stage_chunk(t0, SET);
     __syncthreads();
-    if (c + 1 < cend) {
-      if (t0 + 2 * Q <= L) load_chunk(t0 + Q, Full{});
-      else load_chunk(t0 + Q, Ragged{});
-    }
+    load_chunk(t0 + Q, Prev{});  // past the segment's last chunk: in-range loads whose values go unused
 
     if constexpr (OUT) {
       // M, split over the waves: G^T tile (j-block jb, i-block ib) = B_j . C_i (both rows are
@@ -463,11 +466,18 @@ void ssd_chunk_kernel(const SsdArgs p) {
       for (int nb = 0; nb < NT; ++nb)
         S[nb] = mfma16x16x32(lds_frag_tr(s_b, LDB, 32 * ks, q, l16, 16 * nb + 4 * (l16 & 3)), xw, S[nb]);
     }
-    if (c + 1 < cend) publish_dt();
+    publish_dt();
+  };
+  int64_t c = cbeg;
+  for (; c + 1 < cend; c += 2) {
+    chunk(c, Set0{});
+    chunk(c + 1, Set1{});
   }
+  if (c < cend) chunk(c, Set0{});
   if (OUT && cbeg < cend) {
     __syncthreads();
-    epilogue((cend - 1) * Q, Ragged{});
+    if ((cend - cbeg) & 1) epilogue((cend - 1) * Q, Ragged{}, Set0{});
+    else epilogue((cend - 1) * Q, Ragged{}, Set1{});
   }
   if constexpr (!OUT) {
     float* so = p.seg_state + seg * state_seg + state_off;

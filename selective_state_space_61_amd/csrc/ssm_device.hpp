@@ -337,6 +337,18 @@ __device__ __forceinline__ float zoh_factor(float tt, float a) {
   return a == 1.0f ? kLn2 : (a - 1.0f) * hw_rcp(l);
 }
 
+constexpr int kXcds = 8;  // MI355X: 8 accelerator complex dies, workgroups dealt round robin
+
+// Logical workgroup index for hardware index i of n: the first n - n % 8 workgroups are regrouped
+// so that the hardware indices i with i % 8 == x (one XCD, with its own L2) take logical indices
+// x * (n / 8) .. (x + 1) * (n / 8) - 1; the last n % 8 keep their index.  A bijection on [0, n):
+// workgroups with neighbouring logical indices share an XCD and its L2.
+__device__ __forceinline__ int64_t xcd_local(int64_t i, int64_t n) {
+  const int64_t per = n / kXcds;
+  if (i >= per * kXcds) return i;
+  return (i % kXcds) * per + i / kXcds;
+}
+
 // compile-time loop: f(std::integral_constant<int, I>) for I = 0 .. N-1
 template <typename F, int... Is>
 __device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, Is...>) {
