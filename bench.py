@@ -412,10 +412,10 @@ def copy_ceiling_gbps(torch, device, nbytes=1 << 30, reps=10):
     return 2 * nbytes / (ms * 1e-3) / 1e9
 
 
-def bench_scan_bwd(steps, warmup, torch, np, W, ssm, device, zoh=False):
+def bench_scan_bwd(steps, warmup, torch, np, W, ssm, device, zoh=False, layout="auto"):
     """The backward scan on the 130M-shaped layer (inputs, dy and gradients resident in HBM;
-    two input sets rotated).  Reports the time per call of the whole backward (both kernels);
-    zoh differentiates the exact zero-order-hold forward."""
+    two input sets rotated).  Reports the time per call of the whole backward (every kernel of
+    the call); zoh differentiates the exact zero-order-hold forward; layout as ssm_scan_bwd's."""
     w = W.WORKLOADS["mamba130m"]
     t = W.workload_inputs(w)
     g = np.random.default_rng(61)
@@ -429,7 +429,7 @@ def bench_scan_bwd(steps, warmup, torch, np, W, ssm, device, zoh=False):
     def call(i):
         d = sets[i % 2]
         ssm.ssm_scan_bwd(d["x"], d["delta"], d["A"], d["B"], d["C"], d["dy"], D=d["D"], z=d["z"],
-                         delta_bias=d["delta_bias"], delta_softplus=True, zoh=zoh)
+                         delta_bias=d["delta_bias"], delta_softplus=True, zoh=zoh, layout=layout)
 
     total_ms, per = time_calls(torch, call, steps, warmup)
     ms = sum(per) / len(per)
@@ -439,7 +439,7 @@ def bench_scan_bwd(steps, warmup, torch, np, W, ssm, device, zoh=False):
     alg = elems * 2 * 7 + 4 * w.batch * w.seqlen * w.dstate * 2 + 4 * w.dim * w.dstate * 2
     del sets
     torch.cuda.empty_cache()
-    return {"workload": "mamba130m", "ms_per_call": ms, "elems_per_s": elems / (ms * 1e-3),
+    return {"workload": "mamba130m", "layout": layout, "ms_per_call": ms, "elems_per_s": elems / (ms * 1e-3),
             "updates_per_s": updates / (ms * 1e-3), "alg_bytes": alg, "hbm_gbps": alg / (ms * 1e-3) / 1e9,
             "fwd_equiv": None}
 
@@ -575,8 +575,9 @@ def profile_mode(args):
         res = bench_decode(args.steps, torch, np, W, ssm, torch.device("cuda:0"), ring=26)
     elif args.workload == "conv":
         res = bench_conv(args.steps, args.warmup, torch, np, W, ssm, torch.device("cuda:0"))
-    elif args.workload == "bwd":
-        res = bench_scan_bwd(args.steps, args.warmup, torch, np, W, ssm, torch.device("cuda:0"))
+    elif args.workload in ("bwd", "bwd_lanes"):
+        res = bench_scan_bwd(args.steps, args.warmup, torch, np, W, ssm, torch.device("cuda:0"),
+                             layout="channel_lanes" if args.workload == "bwd_lanes" else "auto")
         res["kernel_ms"] = res["ms_per_call"]
     elif args.workload == "ssd_decode":
         res = bench_ssd_decode(torch, np, W, ssm, torch.device("cuda:0"))
@@ -647,8 +648,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="mamba130m",
-                    choices=["mamba130m", "mamba2p8b", "genomics", "decode", "ssd_decode", "conv", "bwd", "mamba2_layer",
-                             "mamba2_layer_b8"])
+                    choices=["mamba130m", "mamba2p8b", "genomics", "decode", "ssd_decode", "conv", "bwd", "bwd_lanes",
+                             "mamba2_layer", "mamba2_layer_b8"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the context measurements (2.8B scan, decode)")
     ap.add_argument("--profile-mode", action="store_true",
@@ -676,7 +677,7 @@ def main():
     import selective_state_space_61_amd as ssm
     from selective_state_space_61_amd import build as hip_build
 
-    if args.workload in ("decode", "ssd_decode", "conv", "bwd", "mamba2_layer", "mamba2_layer_b8"):
+    if args.workload in ("decode", "ssd_decode", "conv", "bwd", "bwd_lanes", "mamba2_layer", "mamba2_layer_b8"):
         raise SystemExit(f"{args.workload} is measured as context next to a scan workload; use --profile-mode for it alone")
     if not os.path.exists(ssm.LIBRARY):
         hip_build.build(verbose=True)
@@ -710,6 +711,10 @@ def main():
         log(f"[bench] {args.workload} with exact ZOH Bbar: {zres['kernel_ms'] * 1e3:.1f} us/launch")
         extra["scan_bwd"] = bench_scan_bwd(max(6, args.steps // 5), 20, torch, np, W, ssm, device)
         log(f"[bench] scan backward (130M shape): {extra['scan_bwd']['ms_per_call'] * 1e3:.1f} us/call")
+        extra["scan_bwd_channel_lanes"] = bench_scan_bwd(max(6, args.steps // 5), 5, torch, np, W, ssm, device,
+                                                         layout="channel_lanes")
+        log(f"[bench] scan backward, channel lanes (130M shape): "
+            f"{extra['scan_bwd_channel_lanes']['ms_per_call'] * 1e3:.1f} us/call")
         extra["scan_bwd_exact_zoh"] = bench_scan_bwd(max(4, args.steps // 5), 3, torch, np, W, ssm, device, zoh=True)
         log(f"[bench] scan backward, exact ZOH (130M shape): "
             f"{extra['scan_bwd_exact_zoh']['ms_per_call'] * 1e3:.1f} us/call")

@@ -256,13 +256,17 @@ SSM_API ssm_status_t ssm_state_update(int64_t batch, int64_t dim, int64_t dstate
  *   to the raw delta (before bias and softplus).
  *
  * dstate must be 1, 2, 4, 8, 16, 32 or 64.  last_state is not
- * differentiated.  The channel sums of dB / dC and the batch sums of dA / dD
- * / ddelta_bias are taken in a fixed order, so the result does not vary from
- * run to run.  With T = 16 (dstate <= 16), 8 (dstate 32) or 4 (dstate 64),
- * halved for SSM_BBAR_ZOH but at least 4 (ssm_scan_bwd_ex), the scratch is batch*ceil(seqlen/T)*dstate*dim +
- * 2*ceil(dim/64)*batch*seqlen*dstate + batch*dstate*dim + 2*T*batch*dim fp32,
- * in the same per-(device, stream) buffer as the split-sequence scan (same
- * rules as ssm_scan_fwd).
+ * differentiated.  The batch sums of dA / dD / ddelta_bias are taken in a
+ * fixed order.  With the channel-lane layout the channel sums of dB / dC are
+ * too, so the result does not vary from run to run; the state-row layout
+ * (ssm_bwd_opts_t, chosen automatically for bf16 dstate 16) adds them with
+ * atomics.  Scratch, in the same per-(device, stream) buffer as the
+ * split-sequence scan (same rules as ssm_scan_fwd), in fp32 values:
+ *   channel lanes, with T = 16 (dstate <= 16), 8 (dstate 32) or 4 (dstate
+ *   64), halved for SSM_BBAR_ZOH but at least 4: batch*ceil(seqlen/T)*dstate*dim
+ *   + 2*ceil(dim/64)*batch*seqlen*dstate + batch*dstate*dim + 2*T*batch*dim;
+ *   state rows, with T = 32: batch*ceil(seqlen/T)*16*dim + 2*batch*seqlen*16
+ *   + batch*16*dim + 2*T*batch*dim.
  */
 SSM_API ssm_status_t ssm_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, ssm_dtype_t dtype,
                                   const void *x, const void *delta, const float *A, const void *B, const void *C,
@@ -271,10 +275,26 @@ SSM_API ssm_status_t ssm_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, in
                                   void *dz, float *ddelta_bias, void *stream);
 
 /* Options of ssm_scan_bwd_ex: bbar_mode as in ssm_scan_opts_t (the forward
- * being differentiated); reserved must be zero. */
+ * being differentiated); layout (ssm_scan_layout_t) picks the work
+ * decomposition:
+ *   SSM_LAYOUT_AUTO           state rows where they apply, else channel lanes;
+ *   SSM_LAYOUT_CHANNEL_LANES  one channel per lane, 64 channels per workgroup,
+ *                             every dtype / dstate / bbar_mode;
+ *   SSM_LAYOUT_STATE_ROWS     16 channels x 16 states per wave, 48 channels
+ *                             per workgroup, 32-step chunks: bf16 only,
+ *                             dstate 16, SSM_BBAR_DELTA_B, dim a multiple of 8
+ *                             and x, delta, z, dy, dx, ddelta, dz, B, C
+ *                             16-byte aligned (else SSM_ERR_UNSUPPORTED).
+ *                             Its dB / dC channel sums are added with
+ *                             atomics, so their last bits may vary from run
+ *                             to run; every other gradient is summed in a
+ *                             fixed order.
+ * SSM_LAYOUT_TIME_SCAN is a forward-only layout (SSM_ERR_UNSUPPORTED).
+ * reserved must be zero. */
 typedef struct {
   int32_t bbar_mode;
-  int32_t reserved[7];
+  int32_t layout;
+  int32_t reserved[6];
 } ssm_bwd_opts_t;
 
 /*

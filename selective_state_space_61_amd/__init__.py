@@ -50,7 +50,7 @@ class UpdateOpts(ctypes.Structure):
 
 
 class BwdOpts(ctypes.Structure):
-    _fields_ = [("bbar_mode", ctypes.c_int32), ("reserved", ctypes.c_int32 * 7)]
+    _fields_ = [("bbar_mode", ctypes.c_int32), ("layout", ctypes.c_int32), ("reserved", ctypes.c_int32 * 6)]
 
 
 class SsdOpts(ctypes.Structure):
@@ -243,11 +243,11 @@ def ssm_state_update(state: torch.Tensor, x: torch.Tensor, delta: torch.Tensor, 
 def ssm_scan_bwd(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Tensor, C: torch.Tensor,
                  dy: torch.Tensor, D: Optional[torch.Tensor] = None, z: Optional[torch.Tensor] = None,
                  delta_bias: Optional[torch.Tensor] = None, delta_softplus: bool = False, zoh: bool = False,
-                 stream=None) -> dict:
+                 layout: str = "auto", stream=None) -> dict:
     """Backward of ssm_scan_fwd (include/ssm.h: ssm_scan_bwd_ex): gradients of sum(dy * y); zoh
-    differentiates the exact zero-order-hold forward.  Returns a dict with dx, ddelta, dB, dC
-    (x's dtype), dA (fp32), and dz / dD / ddelta_bias (None unless z / D / delta_bias were
-    given)."""
+    differentiates the exact zero-order-hold forward; layout is "auto", "channel_lanes" or
+    "state_rows" (ssm_bwd_opts_t).  Returns a dict with dx, ddelta, dB, dC (x's dtype), dA
+    (fp32), and dz / dD / ddelta_bias (None unless z / D / delta_bias were given)."""
     lib = load_library()
     if x.dim() != 3 or A.dim() != 2:
         raise ValueError("x must be (batch, seqlen, dim) and A (dim, dstate)")
@@ -268,7 +268,9 @@ def ssm_scan_bwd(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch
            "dz": torch.empty_like(x) if z is not None else None,
            "dD": torch.empty((dim,), dtype=torch.float32, device=dev) if D is not None else None,
            "ddelta_bias": torch.empty((dim,), dtype=torch.float32, device=dev) if delta_bias is not None else None}
-    opts = BwdOpts(SSM_BBAR_ZOH if zoh else SSM_BBAR_DELTA_B)
+    if layout not in LAYOUTS:
+        raise ValueError(f"layout must be one of {sorted(LAYOUTS)}")
+    opts = BwdOpts(SSM_BBAR_ZOH if zoh else SSM_BBAR_DELTA_B, LAYOUTS[layout])
     status = lib.ssm_scan_bwd_ex(batch, seqlen, dim, dstate, code, _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C),
                                  _ptr(D), _ptr(z), _ptr(delta_bias), int(bool(delta_softplus)), _ptr(dy),
                                  _ptr(out["dx"]), _ptr(out["ddelta"]), _ptr(out["dA"]), _ptr(out["dB"]),

@@ -10,9 +10,10 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIBRARY = os.path.join(HERE, "libssm61.so")
 SOURCES = [os.path.join(CSRC, f) for f in ("ssm_api.hip", "scan_f32.hip", "scan_bf16.hip", "scan_zoh_f32.hip",
-                                            "scan_zoh_bf16.hip", "ssd_bf16.hip", "scan_rows.hip", "scan_time.hip")]
+                                            "scan_zoh_bf16.hip", "ssd_bf16.hip", "scan_rows.hip", "scan_time.hip",
+                                            "scan_bwd_rows.hip")]
 HEADERS = [os.path.join(CSRC, f) for f in ("ssm_device.hpp", "scan_fwd.hpp", "scan_table.hpp", "scan_rows.hpp", "scan_rows_table.hpp", "scan_time.hpp", "scan_time_table.hpp", "state_update.hpp",
-                                                  "conv1d.hpp", "scan_bwd.hpp", "ssd_fwd.hpp")] + [
+                                                  "conv1d.hpp", "scan_bwd.hpp", "scan_bwd_rows.hpp", "ssd_fwd.hpp")] + [
     os.path.join(os.path.dirname(HERE), "include", "ssm.h")]
 OBJDIR = os.path.join(HERE, "_build")
 ARCH = "gfx950"

@@ -383,7 +383,9 @@ void ssd_chunk_kernel(const SsdArgs p) {
     if (OUT && c > cbeg) epilogue(t0 - Q, Full{}, Prev{});  // the chunk before this one is whole
     stage_chunk(t0, SET);
     __syncthreads();
-    load_chunk(t0 + Q, Prev{});  // past the segment's last chunk: in-range loads whose values go unused
+    // the next chunk; after the segment's last one the loads still run (one path, no merge) but
+    // read this chunk's rows again, which its L2 holds, and their values go unused
+    load_chunk(c + 1 < cend ? t0 + Q : t0, Prev{});
 
     if constexpr (OUT) {
       // M, split over the waves: G^T tile (j-block jb, i-block ib) = B_j . C_i (both rows are

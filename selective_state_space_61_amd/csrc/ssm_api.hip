@@ -18,6 +18,7 @@
 #include "conv1d.hpp"
 #include "scan_bwd.hpp"
 #include "ssd_fwd.hpp"
+#include "scan_bwd_rows.hpp"
 
 namespace {
 
@@ -632,8 +633,13 @@ ssm_status_t ssm_scan_bwd_ex(int64_t batch, int64_t seqlen, int64_t dim, int64_t
       return fail(SSM_ERR_UNSUPPORTED, "bbar_mode %d is not SSM_BBAR_DELTA_B or SSM_BBAR_ZOH", (int)opts->bbar_mode);
     for (int32_t r : opts->reserved)
       if (r != 0) return fail(SSM_ERR_INVALID_ARG, "ssm_bwd_opts_t.reserved must be zero");
+    if (opts->layout < SSM_LAYOUT_AUTO || opts->layout > SSM_LAYOUT_TIME_SCAN)
+      return fail(SSM_ERR_INVALID_ARG, "unknown layout %d", (int)opts->layout);
+    if (opts->layout == SSM_LAYOUT_TIME_SCAN)
+      return fail(SSM_ERR_UNSUPPORTED, "SSM_LAYOUT_TIME_SCAN is a forward layout");
   }
   const bool zoh = opts && opts->bbar_mode == SSM_BBAR_ZOH;
+  const int layout = opts ? opts->layout : SSM_LAYOUT_AUTO;
   if (batch < 0 || seqlen < 0 || dim < 0 || dstate < 0)
     return fail(SSM_ERR_INVALID_ARG, "negative size (batch=%lld seqlen=%lld dim=%lld dstate=%lld)",
                 (long long)batch, (long long)seqlen, (long long)dim, (long long)dstate);
@@ -671,6 +677,69 @@ ssm_status_t ssm_scan_bwd_ex(int64_t batch, int64_t seqlen, int64_t dim, int64_t
   }
 
   hipStream_t st = static_cast<hipStream_t>(stream);
+  // state rows: bf16, dstate 16, Delta B, 16-byte rows of every per-step tensor
+  const bool rows_fit = !empty && dtype == SSM_BF16 && dstate == 16 && !zoh && dim % 8 == 0 && aligned(x, 16) &&
+                        aligned(delta, 16) && aligned(dy, 16) && aligned(dx, 16) && aligned(ddelta, 16) &&
+                        (!z || (aligned(z, 16) && aligned(dz, 16))) && aligned(B, 16) && aligned(C, 16);
+  if (layout == SSM_LAYOUT_STATE_ROWS && !rows_fit)
+    return fail(SSM_ERR_UNSUPPORTED,
+                "SSM_LAYOUT_STATE_ROWS backward needs bf16, dstate 16, SSM_BBAR_DELTA_B, dim a multiple of 8 and "
+                "16-byte aligned x, delta, z, dy, dx, ddelta, dz, B, C");
+  if (rows_fit && layout != SSM_LAYOUT_CHANNEL_LANES) {
+    // scan waves per workgroup: the fewest rounds of one workgroup per CU, then the larger
+    // workgroup (a workgroup's time does not depend on its scan waves, one per SIMD)
+    const int cus = device_cus();
+    int S = 1;
+    int64_t best = -1;
+    for (int c = 1; c <= ssm::kBwdRowsMaxS; ++c) {
+      const int64_t rounds = (batch * ((dim + 16 * c - 1) / (16 * c)) + cus - 1) / cus;
+      if (best < 0 || rounds <= best) {
+        best = rounds;
+        S = c;
+      }
+    }
+    constexpr int64_t T = ssm::kBwdRowsT;
+    const int64_t nc = (seqlen + T - 1) / T;
+    const int64_t ncb = (dim + 16 * S - 1) / (16 * S);
+    int64_t grid;
+    if (!mul_ok(batch, ncb, &grid) || grid > 0x7fffffff) return fail(SSM_ERR_UNSUPPORTED, "grid too large");
+    // scratch: chunk-start states, the dB / dC accumulator, dA / dD / dbias batch partials
+    const int64_t n_h = batch * nc * 16 * dim;
+    const int64_t n_bc = 2 * batch * seqlen * 16;
+    const int64_t n_a = batch * 16 * dim;
+    const int64_t n_d = batch * T * dim;
+    float* scratch = nullptr;
+    ssm_status_t s = get_scratch(st, n_h + n_bc + n_a + 2 * n_d + 1, &scratch);
+    if (s != SSM_OK) return s;
+    ssm::BwdArgs a{};
+    a.x = x; a.delta = delta; a.A = A; a.B = B; a.C = C; a.Dskip = D; a.z = z; a.delta_bias = delta_bias; a.dy = dy;
+    a.dx = dx; a.ddelta = ddelta; a.dz = dz;
+    a.hstart = scratch;
+    a.part_bc = scratch + n_h;
+    a.part_a = a.part_bc + n_bc;
+    a.part_d = a.part_a + n_a;
+    a.part_bias = a.part_d + n_d;
+    a.batch = batch; a.seqlen = seqlen; a.dim = dim; a.nc = nc;
+    a.ncb = static_cast<int32_t>(ncb);
+    a.softplus = delta_softplus ? 1 : 0;
+    a.vec_ok = 1;
+    hipLaunchKernelGGL(fill_zero_kernel, dim3(static_cast<unsigned>((n_bc + 255) / 256)), dim3(256), 0, st,
+                       a.part_bc, n_bc);
+    if ((s = check_launch("fill_zero_kernel")) != SSM_OK) return s;
+    hipLaunchKernelGGL(ssm::bwd_rows_kernel(S), dim3(static_cast<unsigned>(grid)), dim3(64 * ssm::kBwdRowsWaves), 0,
+                       st, a);
+    if ((s = check_launch("scan backward (state rows)")) != SSM_OK) return s;
+    ssm::BwdReduceArgs r{};
+    r.part_bc = a.part_bc; r.part_a = a.part_a; r.part_d = a.part_d; r.part_bias = a.part_bias;
+    r.dB = dB; r.dC = dC; r.dA = dA; r.dD = dD; r.dbias = ddelta_bias;
+    r.batch = batch; r.seqlen = seqlen; r.dim = dim; r.N = 16;
+    r.ncb = 1;  // the accumulator already holds the channel sums
+    r.T = static_cast<int32_t>(T);
+    const int64_t nred = 2 * batch * seqlen * 16 + dim * 16 + dim;
+    hipLaunchKernelGGL(ssm::scan_bwd_reduce_kernel<true>, dim3(static_cast<unsigned>((nred + 255) / 256)), dim3(256),
+                       0, st, r);
+    return check_launch("scan backward reduce");
+  }
   const int npl = bwd_npl(dstate);
   const int64_t T = ssm::bwd_chunk(npl, zoh);
   const int64_t nc = empty ? 0 : (seqlen + T - 1) / T;

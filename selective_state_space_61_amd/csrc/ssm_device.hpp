@@ -164,11 +164,12 @@ __device__ __forceinline__ void store_vec(void* __restrict__ base, int64_t idx, 
 // of that row.  A register whose lane (row r, k) holds the value for step k (the same in every
 // row) hands step K's value to all 64 lanes without a memory access.
 // ---------------------------------------------------------------------------------------------
+// (Every lane has a source in its row, so bound_ctrl changes nothing; it spares the compiler a
+// register for the unused "old" value, one v_mov per broadcast that it cannot fold.)
 template <int K>
 __device__ __forceinline__ float row_bcast(float v) {
   static_assert(K >= 0 && K < 16, "row_newbcast selects one of 16 lanes");
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x150 + K, 0xF, 0xF,
-                                                               false));
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x150 + K, 0xF, 0xF, true));
 }
 
 // ---------------------------------------------------------------------------------------------

@@ -311,9 +311,14 @@ def test_bwd_opts_validation(lib):
         return lib.ssm_scan_bwd_ex(*args, ctypes.byref(opts))
     assert bwd(ssm.BwdOpts(2)) == UNSUPPORTED and "bbar_mode" in err(lib)
     bad = ssm.BwdOpts(0)
-    bad.reserved[6] = 1
+    bad.reserved[5] = 1
     assert bwd(bad) == INVALID and "reserved" in err(lib)
     assert bwd(ssm.BwdOpts(0), dstate=128) == UNSUPPORTED and "dstate" in err(lib)
+    assert bwd(ssm.BwdOpts(0, 9)) == INVALID and "layout" in err(lib)
+    assert bwd(ssm.BwdOpts(0, ssm.SSM_LAYOUT_TIME_SCAN)) == UNSUPPORTED and "TIME_SCAN" in err(lib)
+    # the state-row backward takes bf16 only: fp32 is refused before any launch
+    assert bwd(ssm.BwdOpts(0, ssm.SSM_LAYOUT_STATE_ROWS)) == UNSUPPORTED and "STATE_ROWS" in err(lib)
+    assert bwd(ssm.BwdOpts(1, ssm.SSM_LAYOUT_STATE_ROWS)) == UNSUPPORTED and "STATE_ROWS" in err(lib)
 
 
 def test_time_scan_opts_validation(lib):

@@ -37,18 +37,18 @@ def dy_for(shape, dtype, seed):
     return W.f32_to_bf16_bits(dy) if dtype == "bf16" else dy
 
 
-def bwd_gpu(t, dy, softplus, zoh=False):
+def bwd_gpu(t, dy, softplus, zoh=False, layout="auto"):
     import selective_state_space_61_amd as ssm
     d = {k: to_dev(v) for k, v in t.items()}
     g = ssm.ssm_scan_bwd(d["x"], d["delta"], d["A"], d["B"], d["C"], to_dev(dy), D=d["D"], z=d["z"],
-                         delta_bias=d["delta_bias"], delta_softplus=softplus, zoh=zoh)
+                         delta_bias=d["delta_bias"], delta_softplus=softplus, zoh=zoh, layout=layout)
     torch.cuda.synchronize()
     return g
 
 
-def compare(o, t, dy, dtype, softplus, what, zoh=False):
-    say(f"[case] {what}")
-    g = bwd_gpu(t, dy, softplus, zoh)
+def compare(o, t, dy, dtype, softplus, what, zoh=False, layout="auto"):
+    say(f"[case] {what} ({layout})")
+    g = bwd_gpu(t, dy, softplus, zoh, layout)
     dy64 = W.bf16_bits_to_f32(dy).astype(np.float64) if dy.dtype == np.uint16 else dy.astype(np.float64)
     ref = o.scan_bwd(t["x"], t["delta"], t["A"], t["B"], t["C"], dy64, D=t["D"], z=t["z"],
                      delta_bias=t["delta_bias"], delta_softplus=softplus, zoh=zoh)
@@ -112,19 +112,56 @@ def test_variants(o, variant):
     compare(o, t, dy_for((2, 50, 72), "f32", 78), "f32", softplus, f"bwd variant {variant}")
 
 
-def test_deterministic_and_empty(o):
+@pytest.mark.parametrize("layout", ["channel_lanes", "state_rows"])
+def test_deterministic_and_empty(o, layout):
+    """Channel lanes: every gradient is bit-identical between runs.  State rows: all but dB and dC
+    (whose channel sums are added with atomics in a run-dependent order)."""
     import selective_state_space_61_amd as ssm
     t = W.scan_inputs(2, 64, 128, 16, "bf16", seed=5)
     dy = dy_for((2, 64, 128), "bf16", 6)
-    g1, g2 = bwd_gpu(t, dy, True), bwd_gpu(t, dy, True)
+    g1, g2 = bwd_gpu(t, dy, True, layout=layout), bwd_gpu(t, dy, True, layout=layout)
     for k in g1:
-        if g1[k] is not None:
+        if g1[k] is not None and not (layout == "state_rows" and k in ("dB", "dC")):
             assert torch.equal(g1[k], g2[k]), f"{k} differs between runs"
     # seqlen 0: nothing flows back and the parameter gradients are zero
     t0 = W.scan_inputs(2, 0, 32, 16, "f32", seed=1)
     g0 = bwd_gpu(t0, np.zeros((2, 0, 32), np.float32), True)
     assert torch.count_nonzero(g0["dA"]).item() == 0 and torch.count_nonzero(g0["dD"]).item() == 0
     assert torch.count_nonzero(g0["ddelta_bias"]).item() == 0
+
+
+@pytest.mark.parametrize("shape", [(1, 1, 8), (1, 31, 40), (2, 33, 56), (3, 100, 200), (2, 64, 144), (1, 96, 48),
+                                   (2, 65, 16)])
+def test_state_rows_shapes(o, shape):
+    """The state-row backward (bf16, dstate 16): sequences that are not whole 32-step chunks, channel
+    counts that are not whole 48-channel workgroups (1, 2 or 3 scan waves), several batch rows."""
+    batch, L, dim = shape
+    t = W.scan_inputs(batch, L, dim, 16, "bf16", seed=L * 5 + dim)
+    compare(o, t, dy_for((batch, L, dim), "bf16", L + 2 * dim), "bf16", True, f"bwd state rows {shape}",
+            layout="state_rows")
+
+
+@pytest.mark.parametrize("variant", ["no_z", "no_D", "no_bias", "softplus_off", "bare"])
+def test_state_rows_variants(o, variant):
+    softplus = variant not in ("softplus_off", "bare")
+    t = W.scan_inputs(2, 70, 96, 16, "bf16", seed=79, has_z=variant not in ("no_z", "bare"),
+                      has_D=variant not in ("no_D", "bare"), has_bias=softplus and variant != "no_bias")
+    if not softplus:
+        t["delta"] = t["delta"] & np.uint16(0x7FFF)
+    compare(o, t, dy_for((2, 70, 96), "bf16", 80), "bf16", softplus, f"bwd state rows {variant}",
+            layout="state_rows")
+
+
+def test_state_rows_refusals():
+    """Where the state rows do not apply, asking for them is an error before any launch (auto
+    takes the channel lanes there, which the other tests cover)."""
+    import selective_state_space_61_amd as ssm
+    cases = [("f32", 2, 40, 48, 16, False), ("bf16", 2, 40, 44, 16, False), ("bf16", 2, 40, 48, 8, False),
+             ("bf16", 2, 40, 48, 16, True)]
+    for dtype, batch, L, dim, N, zoh in cases:
+        t = W.scan_inputs(batch, L, dim, N, dtype, seed=3)
+        with pytest.raises(ssm.SsmError, match="STATE_ROWS"):
+            bwd_gpu(t, dy_for((batch, L, dim), dtype, 4), True, zoh=zoh, layout="state_rows")
 
 
 def test_mid_size_every_gradient(o):
