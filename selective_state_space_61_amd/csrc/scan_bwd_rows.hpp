@@ -21,8 +21,10 @@
 //   2. sweeps the chunk in reverse: g_t = dy0_t C_t + abar_{t+1} g_{t+1}, dA in registers, and per
 //      step the row partials sum_j g B_j (for dx) and sum_j g A_j abar_j h_{t-1,j} (for ddelta);
 //   3. hands the channel sums of dB_t = sum_d g dt x and dC_t = sum_d dy0 h_t over its 16
-//      channels to LDS (a transpose through LDS, one output per lane every two steps, added into
-//      the workgroup's sums with ds_add_f32).
+//      channels to LDS (a transpose through LDS, one output per lane every two steps, stored in
+//      the wave's own slot; the stager adds the S slots).  LDS float atomics are avoided: on this
+//      chip a ds_add_f32 keeps the LDS busy many times longer than a store, and the scan's own
+//      LDS reads queue behind it.
 // The four row partials of a channel (read-out, gB, pdt) are summed inside the scan wave, four
 // steps at a time, with v_permlane16_swap / v_permlane32_swap (gfx950): after the swaps lane
 // 16 q + k holds step q's sum for channel k, one LDS write per four steps.
@@ -53,7 +55,7 @@ constexpr int bwd_rows_lds_bytes(int S) {
          + 3 * kBwdRowsT * 16 * S * 8         // raw x, delta, z, dy (bf16), triple-buffered
          + 2 * 3 * (kBwdRowsT / 4) * S * 64 * 4  // row sums: read-out, gB, pdt
          + S * 16 * 68 * 4                    // per-wave dB / dC transposes
-         + 2 * kBwdRowsT * 32 * 4;            // the workgroup's dB / dC sums
+         + 2 * S * kBwdRowsT * 32 * 4;        // each scan wave's dB / dC sums
 }
 
 // v_permlane16_swap (gfx950) on two registers: afterwards a holds rows (a0, b0, a2, b2) and b rows
@@ -106,7 +108,7 @@ __global__ __launch_bounds__(64 * kBwdRowsWaves) void scan_bwd_rows_kernel(const
   __shared__ uint2 s_ep[3][T][CW];                 // {x | delta << 16, z | dy << 16}
   __shared__ float s_part[2][3][T / 4][S][64];     // row sums: read-out, gB, pdt
   __shared__ __align__(16) float s_red[S][16][68]; // dB / dC transpose rows of a scan wave
-  __shared__ float s_bsum[2][T][2 * N];            // the workgroup's dB (0..15), dC (16..31)
+  __shared__ float s_bsum[2][S][T][2 * N];         // each scan wave's dB (0..15), dC (16..31)
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -259,8 +261,7 @@ __global__ __launch_bounds__(64 * kBwdRowsWaves) void scan_bwd_rows_kernel(const
                           ((pend[1].x + pend[1].y) + (pend[1].z + pend[1].w)) +
                           (((pend[2].x + pend[2].y) + (pend[2].z + pend[2].w)) +
                            ((pend[3].x + pend[3].y) + (pend[3].z + pend[3].w)));
-        __hip_atomic_fetch_add(&s_bsum[buf][t_even + sub][kind * N + 4 * rr + qrow], sum, __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_WORKGROUP);
+        s_bsum[buf][s][t_even + sub][kind * N + 4 * rr + qrow] = sum;
       };
       static_for<T>([&](auto K) {
         constexpr int t = T - 1 - decltype(K)::value;
@@ -478,7 +479,6 @@ __global__ __launch_bounds__(64 * kBwdRowsWaves) void scan_bwd_rows_kernel(const
     const uint16_t* Bg = static_cast<const uint16_t*>(p.B);
     const uint16_t* Cg = static_cast<const uint16_t*>(p.C);
     const uint4 zero4 = make_uint4(0u, 0u, 0u, 0u);
-    for (int e = lane; e < 2 * T * 2 * N; e += 64) (&s_bsum[0][0][0])[e] = 0.0f;
     using Slot0 = std::integral_constant<int, 0>;
     using Slot1 = std::integral_constant<int, 1>;
     // ---- phase 0: B of chunk j in iteration j ------------------------------------------------
@@ -525,16 +525,18 @@ __global__ __launch_bounds__(64 * kBwdRowsWaves) void scan_bwd_rows_kernel(const
         widen(ok ? ncr[sl] : zero4, &s_bc[cp & 1][1][srow][8 * shalf]);
       }
       if (ce < nc) {
-        float* sums = &s_bsum[ce & 1][0][0];
+        const float* sums = &s_bsum[ce & 1][0][0][0];
 #pragma unroll
         for (int e0 = 0; e0 < T * 2 * N; e0 += 64) {
           const int e = e0 + lane;
           const int tt = e / (2 * N), q = e % (2 * N);
           const int64_t t = ce * T + tt;
+          float sum = sums[e];
+#pragma unroll
+          for (int sw = 1; sw < S; ++sw) sum += sums[sw * T * 2 * N + e];
           // every lane adds on every path (0 to the last row past the sequence): one wait count
           const int64_t tc = t < L ? t : L - 1;
-          atomicAdd((q < N ? acc_b : acc_c) + (row_base + tc) * N + (q % N), t < L ? sums[e] : 0.0f);
-          sums[e] = 0.0f;
+          atomicAdd((q < N ? acc_b : acc_c) + (row_base + tc) * N + (q % N), t < L ? sum : 0.0f);
         }
       }
       load(cp - 2, SL);
