@@ -444,6 +444,56 @@ def bench_scan_bwd(steps, warmup, torch, np, W, ssm, device, zoh=False, layout="
             "fwd_equiv": None}
 
 
+def bench_train_pair(steps, warmup, torch, np, W, ssm, device, which="both"):
+    """The checkpoint pair on the 130M-shaped layer: the forward that also stores the state before
+    every 32nd step (ssm_scan_fwd_ckpt), and the backward that starts from those states
+    (ssm_scan_bwd_ckpt) instead of running the forward recurrence again.  Two input sets rotated;
+    which = "fwd", "bwd" or "both" (each timed on its own)."""
+    w = W.WORKLOADS["mamba130m"]
+    t = W.workload_inputs(w)
+    g = np.random.default_rng(61)
+    dy = W.f32_to_bf16_bits(g.standard_normal((w.batch, w.seqlen, w.dim)).astype(np.float32))
+    sets = []
+    for _ in range(2):
+        d = {k: dev_tensor(v, torch, np, device) for k, v in t.items()}
+        d["dy"] = dev_tensor(dy, torch, np, device)
+        d["y"] = torch.empty_like(d["x"])
+        d["ck"] = torch.empty(ssm.checkpoint_shape(w.batch, w.seqlen, w.dim, w.dstate), dtype=torch.float32,
+                              device=device)
+        sets.append(d)
+
+    def fwd(i):
+        d = sets[i % 2]
+        ssm.ssm_scan_fwd_ckpt(d["x"], d["delta"], d["A"], d["B"], d["C"], D=d["D"], z=d["z"],
+                              delta_bias=d["delta_bias"], delta_softplus=True, y=d["y"], return_last_state=False,
+                              checkpoints=d["ck"])
+
+    def bwd(i):
+        d = sets[i % 2]
+        ssm.ssm_scan_bwd_ckpt(d["x"], d["delta"], d["A"], d["B"], d["C"], d["dy"], d["ck"], D=d["D"], z=d["z"],
+                              delta_bias=d["delta_bias"], delta_softplus=True)
+
+    elems = w.batch * w.seqlen * w.dim
+    ck_bytes = 4 * w.batch * ((w.seqlen + 31) // 32) * w.dstate * w.dim
+    out = {"workload": "mamba130m", "checkpoint_bytes": ck_bytes}
+    fwd(0)
+    fwd(1)
+    torch.cuda.synchronize()
+    # about 20 ms of warmup each: the input generation above left the GPU idle, and its clocks take
+    # that long to ramp back (a short warmup times the forward ~15% slow)
+    if which in ("fwd", "both"):
+        _, per = time_calls(torch, fwd, steps, max(warmup, 160))
+        out["fwd_ms_per_call"] = sum(per) / len(per)
+    if which in ("bwd", "both"):
+        _, per = time_calls(torch, bwd, steps, max(warmup, 40))
+        ms = sum(per) / len(per)
+        out["bwd_ms_per_call"] = ms
+        out["bwd_elems_per_s"] = elems / (ms * 1e-3)
+    del sets
+    torch.cuda.empty_cache()
+    return out
+
+
 def bench_conv_update(steps, torch, np, W, ssm, device):
     """The one-token convolution on the decode shape (64 x 5120, width 4, bf16), one call per
     step on a ring of 26 conv states, captured as one HIP graph and replayed."""
@@ -579,6 +629,10 @@ def profile_mode(args):
         res = bench_scan_bwd(args.steps, args.warmup, torch, np, W, ssm, torch.device("cuda:0"),
                              layout="channel_lanes" if args.workload == "bwd_lanes" else "auto")
         res["kernel_ms"] = res["ms_per_call"]
+    elif args.workload in ("fwd_ckpt", "bwd_ckpt"):
+        which = args.workload.split("_")[0]
+        res = bench_train_pair(args.steps, args.warmup, torch, np, W, ssm, torch.device("cuda:0"), which=which)
+        res["kernel_ms"] = res[f"{which}_ms_per_call"]
     elif args.workload == "ssd_decode":
         res = bench_ssd_decode(torch, np, W, ssm, torch.device("cuda:0"))
         res["kernel_ms"] = res["ms_per_step"]
@@ -649,7 +703,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="mamba130m",
                     choices=["mamba130m", "mamba2p8b", "genomics", "decode", "ssd_decode", "conv", "bwd", "bwd_lanes",
-                             "mamba2_layer", "mamba2_layer_b8"])
+                             "fwd_ckpt", "bwd_ckpt", "mamba2_layer", "mamba2_layer_b8"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the context measurements (2.8B scan, decode)")
     ap.add_argument("--profile-mode", action="store_true",
@@ -677,7 +731,8 @@ def main():
     import selective_state_space_61_amd as ssm
     from selective_state_space_61_amd import build as hip_build
 
-    if args.workload in ("decode", "ssd_decode", "conv", "bwd", "bwd_lanes", "mamba2_layer", "mamba2_layer_b8"):
+    if args.workload in ("decode", "ssd_decode", "conv", "bwd", "bwd_lanes", "fwd_ckpt", "bwd_ckpt", "mamba2_layer",
+                         "mamba2_layer_b8"):
         raise SystemExit(f"{args.workload} is measured as context next to a scan workload; use --profile-mode for it alone")
     if not os.path.exists(ssm.LIBRARY):
         hip_build.build(verbose=True)
@@ -715,6 +770,9 @@ def main():
                                                          layout="channel_lanes")
         log(f"[bench] scan backward, channel lanes (130M shape): "
             f"{extra['scan_bwd_channel_lanes']['ms_per_call'] * 1e3:.1f} us/call")
+        extra["train_pair_checkpoints"] = bench_train_pair(max(10, args.steps // 2), 10, torch, np, W, ssm, device)
+        log(f"[bench] forward storing checkpoints: {extra['train_pair_checkpoints']['fwd_ms_per_call'] * 1e3:.1f} "
+            f"us/call; backward from them: {extra['train_pair_checkpoints']['bwd_ms_per_call'] * 1e3:.1f} us/call")
         extra["scan_bwd_exact_zoh"] = bench_scan_bwd(max(4, args.steps // 5), 3, torch, np, W, ssm, device, zoh=True)
         log(f"[bench] scan backward, exact ZOH (130M shape): "
             f"{extra['scan_bwd_exact_zoh']['ms_per_call'] * 1e3:.1f} us/call")

@@ -311,6 +311,44 @@ SSM_API ssm_status_t ssm_scan_bwd_ex(int64_t batch, int64_t seqlen, int64_t dim,
                              void *dz, float *ddelta_bias, void *stream, const ssm_bwd_opts_t *opts);
 
 /*
+ * A training pair that hands the forward's states to the backward.  The
+ * backward recomputes the states of each 32-step chunk from the state that
+ * enters it ("mamba->jamba" sec. 2.3: recompute instead of storing every
+ * step); with these two calls the forward stores those entering states, so
+ * the backward does not run the forward recurrence again (and reads x and
+ * delta once instead of twice).
+ *
+ *   checkpoints  (batch, ceil(seqlen / 32), dim, dstate) fp32: entry [b][c]
+ *                is the state before step 32 c in last_state's layout (entry
+ *                0 is zero).  Written by ssm_scan_fwd_ckpt, read by
+ *                ssm_scan_bwd_ckpt; owned by the caller; must not overlap any
+ *                other argument (else SSM_ERR_INVALID_ARG), 16-byte aligned
+ *                (else SSM_ERR_MISALIGNED), and not NULL when there is work.
+ *
+ * ssm_scan_fwd_ckpt: ssm_scan_fwd plus the checkpoints.  It runs the
+ * state-row layout, so dstate must be 16 (else SSM_ERR_UNSUPPORTED); y and
+ * last_state are bit-identical to ssm_scan_fwd_ex with SSM_LAYOUT_STATE_ROWS.
+ * ssm_scan_bwd_ckpt: ssm_scan_bwd (SSM_BBAR_DELTA_B) from the checkpoints of
+ * ssm_scan_fwd_ckpt on the same inputs.  It runs the state-row backward, so
+ * it needs bf16, dstate 16, dim a multiple of 8 and 16-byte aligned x, delta,
+ * z, dy, dx, ddelta, dz, B, C (else SSM_ERR_UNSUPPORTED).  Scratch as the
+ * state-row backward of ssm_scan_bwd without its first term.  Nothing checks
+ * that the checkpoints come from the same inputs: others give the gradients
+ * of a different forward.
+ */
+SSM_API ssm_status_t ssm_scan_fwd_ckpt(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, ssm_dtype_t dtype,
+                                       const void *x, const void *delta, const float *A, const void *B,
+                                       const void *C, const float *D, const void *z, const float *delta_bias,
+                                       int delta_softplus, void *y, float *last_state, float *checkpoints,
+                                       void *stream);
+SSM_API ssm_status_t ssm_scan_bwd_ckpt(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, ssm_dtype_t dtype,
+                                       const void *x, const void *delta, const float *A, const void *B,
+                                       const void *C, const float *D, const void *z, const float *delta_bias,
+                                       int delta_softplus, const void *dy, void *dx, void *ddelta, float *dA,
+                                       void *dB, void *dC, float *dD, void *dz, float *ddelta_bias,
+                                       const float *checkpoints, void *stream);
+
+/*
  * Depthwise causal convolution that feeds the scan in the Mamba block
  * ("Mamba 论文精读" sec. 3.4, MambaBlock: Conv1d with one group per channel,
  * kernel width K and K-1 zeros of padding, the first L outputs kept, then

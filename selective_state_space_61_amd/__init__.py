@@ -28,7 +28,8 @@ LIBRARY = os.path.join(_HERE, "libssm61.so")
 SSM_F32, SSM_BF16 = 0, 1
 STATUS_NAMES = {0: "SSM_OK", 1: "SSM_ERR_INVALID_ARG", 2: "SSM_ERR_UNSUPPORTED", 3: "SSM_ERR_MISALIGNED",
                 4: "SSM_ERR_HIP"}
-EXPORTED = ("ssm_scan_fwd", "ssm_scan_fwd_ex", "ssm_scan_fwd_noalloc", "ssm_scan_bwd", "ssm_scan_bwd_ex", "ssm_state_update", "ssm_state_update_ex",
+EXPORTED = ("ssm_scan_fwd", "ssm_scan_fwd_ex", "ssm_scan_fwd_noalloc", "ssm_scan_fwd_ckpt", "ssm_scan_bwd",
+            "ssm_scan_bwd_ex", "ssm_scan_bwd_ckpt", "ssm_state_update", "ssm_state_update_ex",
             "ssm_causal_conv1d_fwd",
             "ssm_causal_conv1d_update", "ssm_ssd_fwd", "ssm_ssd_state_update", "ssm_status_string", "ssm_last_error", "ssm_abi_version")
 
@@ -90,6 +91,11 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
     lib.ssm_scan_bwd.restype = i32
     lib.ssm_scan_bwd_ex.argtypes = lib.ssm_scan_bwd.argtypes + [ctypes.POINTER(BwdOpts)]
     lib.ssm_scan_bwd_ex.restype = i32
+    # the checkpoint pair: the checkpoints pointer comes right before the stream
+    lib.ssm_scan_fwd_ckpt.argtypes = lib.ssm_scan_fwd.argtypes[:-1] + [vp, vp]
+    lib.ssm_scan_fwd_ckpt.restype = i32
+    lib.ssm_scan_bwd_ckpt.argtypes = lib.ssm_scan_bwd.argtypes[:-1] + [vp, vp]
+    lib.ssm_scan_bwd_ckpt.restype = i32
     lib.ssm_causal_conv1d_fwd.argtypes = [i64, i64, i64, i64, i32, vp, vp, vp, vp, i32, vp, vp, vp]
     lib.ssm_causal_conv1d_fwd.restype = i32
     lib.ssm_causal_conv1d_update.argtypes = [i64, i64, i64, i32, vp, vp, vp, vp, i32, vp, vp]
@@ -240,6 +246,37 @@ def ssm_state_update(state: torch.Tensor, x: torch.Tensor, delta: torch.Tensor, 
     return y
 
 
+def _bwd_prepare(x, delta, A, B, C, dy, D, z, delta_bias) -> dict:
+    """Shape checks and the gradient buffers of a backward call."""
+    if x.dim() != 3 or A.dim() != 2:
+        raise ValueError("x must be (batch, seqlen, dim) and A (dim, dstate)")
+    batch, seqlen, dim = x.shape
+    dstate = A.shape[1]
+    dev, dt = x.device, x.dtype
+    _need(x, "x", (batch, seqlen, dim), dt, dev)
+    _need(delta, "delta", (batch, seqlen, dim), dt, dev)
+    _need(A, "A", (dim, dstate), torch.float32, dev)
+    _need(B, "B", (batch, seqlen, dstate), dt, dev)
+    _need(C, "C", (batch, seqlen, dstate), dt, dev)
+    _need(dy, "dy", (batch, seqlen, dim), dt, dev)
+    _need(D, "D", (dim,), torch.float32, dev, optional=True)
+    _need(z, "z", (batch, seqlen, dim), dt, dev, optional=True)
+    _need(delta_bias, "delta_bias", (dim,), torch.float32, dev, optional=True)
+    return {"dx": torch.empty_like(x), "ddelta": torch.empty_like(x), "dB": torch.empty_like(B),
+            "dC": torch.empty_like(C), "dA": torch.empty((dim, dstate), dtype=torch.float32, device=dev),
+            "dz": torch.empty_like(x) if z is not None else None,
+            "dD": torch.empty((dim,), dtype=torch.float32, device=dev) if D is not None else None,
+            "ddelta_bias": torch.empty((dim,), dtype=torch.float32, device=dev) if delta_bias is not None else None}
+
+
+def _bwd_args(x, delta, A, B, C, dy, D, z, delta_bias, delta_softplus, out) -> list:
+    batch, seqlen, dim = x.shape
+    return [batch, seqlen, dim, A.shape[1], _dtype_code(x), _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C),
+            _ptr(D), _ptr(z), _ptr(delta_bias), int(bool(delta_softplus)), _ptr(dy), _ptr(out["dx"]),
+            _ptr(out["ddelta"]), _ptr(out["dA"]), _ptr(out["dB"]), _ptr(out["dC"]), _ptr(out["dD"]),
+            _ptr(out["dz"]), _ptr(out["ddelta_bias"])]
+
+
 def ssm_scan_bwd(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Tensor, C: torch.Tensor,
                  dy: torch.Tensor, D: Optional[torch.Tensor] = None, z: Optional[torch.Tensor] = None,
                  delta_bias: Optional[torch.Tensor] = None, delta_softplus: bool = False, zoh: bool = False,
@@ -249,33 +286,71 @@ def ssm_scan_bwd(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch
     "state_rows" (ssm_bwd_opts_t).  Returns a dict with dx, ddelta, dB, dC (x's dtype), dA
     (fp32), and dz / dD / ddelta_bias (None unless z / D / delta_bias were given)."""
     lib = load_library()
+    out = _bwd_prepare(x, delta, A, B, C, dy, D, z, delta_bias)
+    if layout not in LAYOUTS:
+        raise ValueError(f"layout must be one of {sorted(LAYOUTS)}")
+    opts = BwdOpts(SSM_BBAR_ZOH if zoh else SSM_BBAR_DELTA_B, LAYOUTS[layout])
+    status = lib.ssm_scan_bwd_ex(*_bwd_args(x, delta, A, B, C, dy, D, z, delta_bias, delta_softplus, out),
+                                 _stream(x.device, stream), ctypes.byref(opts))
+    _check(status)
+    return out
+
+
+def checkpoint_shape(batch: int, seqlen: int, dim: int, dstate: int) -> Tuple[int, int, int, int]:
+    """Shape of the checkpoints of ssm_scan_fwd_ckpt: the state before every 32nd step."""
+    return (batch, (seqlen + 31) // 32, dim, dstate)
+
+
+def ssm_scan_fwd_ckpt(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Tensor, C: torch.Tensor,
+                      D: Optional[torch.Tensor] = None, z: Optional[torch.Tensor] = None,
+                      delta_bias: Optional[torch.Tensor] = None, delta_softplus: bool = False, *,
+                      y: Optional[torch.Tensor] = None, last_state: Optional[torch.Tensor] = None,
+                      return_last_state: bool = True, checkpoints: Optional[torch.Tensor] = None,
+                      stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor], torch.Tensor]:
+    """Forward that also stores the state before every 32nd step (include/ssm.h:
+    ssm_scan_fwd_ckpt), for ssm_scan_bwd_ckpt.  Returns (y, last_state, checkpoints)."""
+    lib = load_library()
     if x.dim() != 3 or A.dim() != 2:
         raise ValueError("x must be (batch, seqlen, dim) and A (dim, dstate)")
     batch, seqlen, dim = x.shape
     dstate = A.shape[1]
     dev, dt = x.device, x.dtype
-    code = _dtype_code(x)
-    _need(delta, "delta", (batch, seqlen, dim), dt, dev)
-    _need(A, "A", (dim, dstate), torch.float32, dev)
-    _need(B, "B", (batch, seqlen, dstate), dt, dev)
-    _need(C, "C", (batch, seqlen, dstate), dt, dev)
-    _need(dy, "dy", (batch, seqlen, dim), dt, dev)
-    _need(D, "D", (dim,), torch.float32, dev, optional=True)
-    _need(z, "z", (batch, seqlen, dim), dt, dev, optional=True)
-    _need(delta_bias, "delta_bias", (dim,), torch.float32, dev, optional=True)
-    out = {"dx": torch.empty_like(x), "ddelta": torch.empty_like(x), "dB": torch.empty_like(B),
-           "dC": torch.empty_like(C), "dA": torch.empty((dim, dstate), dtype=torch.float32, device=dev),
-           "dz": torch.empty_like(x) if z is not None else None,
-           "dD": torch.empty((dim,), dtype=torch.float32, device=dev) if D is not None else None,
-           "ddelta_bias": torch.empty((dim,), dtype=torch.float32, device=dev) if delta_bias is not None else None}
-    if layout not in LAYOUTS:
-        raise ValueError(f"layout must be one of {sorted(LAYOUTS)}")
-    opts = BwdOpts(SSM_BBAR_ZOH if zoh else SSM_BBAR_DELTA_B, LAYOUTS[layout])
-    status = lib.ssm_scan_bwd_ex(batch, seqlen, dim, dstate, code, _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C),
-                                 _ptr(D), _ptr(z), _ptr(delta_bias), int(bool(delta_softplus)), _ptr(dy),
-                                 _ptr(out["dx"]), _ptr(out["ddelta"]), _ptr(out["dA"]), _ptr(out["dB"]),
-                                 _ptr(out["dC"]), _ptr(out["dD"]), _ptr(out["dz"]), _ptr(out["ddelta_bias"]),
-                                 _stream(dev, stream), ctypes.byref(opts))
+    for t, name, shape, tdt, opt in ((x, "x", (batch, seqlen, dim), dt, False),
+                                     (delta, "delta", (batch, seqlen, dim), dt, False),
+                                     (A, "A", (dim, dstate), torch.float32, False),
+                                     (B, "B", (batch, seqlen, dstate), dt, False),
+                                     (C, "C", (batch, seqlen, dstate), dt, False),
+                                     (D, "D", (dim,), torch.float32, True), (z, "z", (batch, seqlen, dim), dt, True),
+                                     (delta_bias, "delta_bias", (dim,), torch.float32, True)):
+        _need(t, name, shape, tdt, dev, optional=opt)
+    if y is None:
+        y = torch.empty_like(x)
+    _need(y, "y", (batch, seqlen, dim), dt, dev)
+    if last_state is None and return_last_state:
+        last_state = torch.empty((batch, dim, dstate), dtype=torch.float32, device=dev)
+    _need(last_state, "last_state", (batch, dim, dstate), torch.float32, dev, optional=True)
+    if checkpoints is None:
+        checkpoints = torch.empty(checkpoint_shape(batch, seqlen, dim, dstate), dtype=torch.float32, device=dev)
+    _need(checkpoints, "checkpoints", checkpoint_shape(batch, seqlen, dim, dstate), torch.float32, dev)
+    status = lib.ssm_scan_fwd_ckpt(batch, seqlen, dim, dstate, _dtype_code(x), _ptr(x), _ptr(delta), _ptr(A),
+                                   _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias), int(bool(delta_softplus)),
+                                   _ptr(y), _ptr(last_state), _ptr(checkpoints), _stream(dev, stream))
+    _check(status)
+    return y, last_state, checkpoints
+
+
+def ssm_scan_bwd_ckpt(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Tensor, C: torch.Tensor,
+                      dy: torch.Tensor, checkpoints: torch.Tensor, D: Optional[torch.Tensor] = None,
+                      z: Optional[torch.Tensor] = None, delta_bias: Optional[torch.Tensor] = None,
+                      delta_softplus: bool = False, stream=None) -> dict:
+    """Backward from the checkpoints of ssm_scan_fwd_ckpt on the same inputs (include/ssm.h:
+    ssm_scan_bwd_ckpt); returns the same dict as ssm_scan_bwd."""
+    lib = load_library()
+    out = _bwd_prepare(x, delta, A, B, C, dy, D, z, delta_bias)
+    batch, seqlen, dim = x.shape
+    _need(checkpoints, "checkpoints", checkpoint_shape(batch, seqlen, dim, A.shape[1]), torch.float32, x.device)
+    status = lib.ssm_scan_bwd_ckpt(*_bwd_args(x, delta, A, B, C, dy, D, z, delta_bias, delta_softplus, out),
+                                   _ptr(checkpoints), _stream(x.device, stream))
     _check(status)
     return out
 
@@ -414,4 +489,5 @@ def abi_version() -> int:
 
 __all__ = ["ssm_scan_fwd", "ssm_scan_bwd", "ssm_state_update", "ssm_causal_conv1d_fwd", "ssm_causal_conv1d_update",
            "ssm_ssd_fwd", "ssm_ssd_state_update", "SsdOpts", "BwdOpts", "abi_version", "load_library", "SsmError", "ScanOpts", "UpdateOpts",
+           "ssm_scan_fwd_ckpt", "ssm_scan_bwd_ckpt", "checkpoint_shape",
            "LIBRARY", "EXPORTED"]

@@ -55,7 +55,8 @@ struct BwdArgs {
   void* dx;
   void* ddelta;
   void* dz;
-  float* hstart;     // (batch, nc, N, dim) chunk-start states
+  float* hstart;     // chunk-start states: (batch, nc, N, dim) channel lanes, (batch, nc, dim, N) state rows
+  int32_t have_hstart;  // state rows: hstart holds the forward's checkpoints, so there is no phase 0
   float* part_bc;    // (2, ncb, batch, L, N): dB then dC partial sums over one channel block
   float* part_a;     // (batch, N, dim)
   float* part_d;     // (batch, T, dim), T the chunk length

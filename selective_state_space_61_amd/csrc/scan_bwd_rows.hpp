@@ -16,7 +16,8 @@
 //   * 512 threads, so a wave has 256 VGPRs: the 33 states of a 32-step chunk stay in registers
 //     between the recompute and the reverse sweep.
 // Phase 0 runs the recurrence forward and stores the state at the start of every 32-step chunk
-// (fp32, (batch, nc, 16, dim)).  Phase 1 walks the chunks backwards; per chunk a scan wave
+// (fp32, (batch, nc, dim, 16): each chunk's states in last_state's layout); when the forward pass stored these states (scan_rows.hpp, the
+// same layout), every role skips phase 0.  Phase 1 walks the chunks backwards; per chunk a scan wave
 //   1. recomputes the chunk's states from the stored one, with the read-outs C_t.h_t;
 //   2. sweeps the chunk in reverse: g_t = dy0_t C_t + abar_{t+1} g_{t+1}, dA in registers, and per
 //      step the row partials sum_j g B_j (for dx) and sum_j g A_j abar_j h_{t-1,j} (for ddelta);
@@ -135,7 +136,11 @@ __global__ __launch_bounds__(64 * kBwdRowsWaves) void scan_bwd_rows_kernel(const
       Araw[j] = lane_ok ? p.A[d * N + n0 + j] : 0.0f;
       A2[j] = fmaxf(Araw[j] * kLog2e, -3.0e38f);
     }
-    auto hstart = [&](int64_t c, int j) -> float* { return p.hstart + ((b * nc + c) * N + n0 + j) * p.dim + d; };
+    // the state before chunk c, (batch, nc, dim, 16) as last_state: the lane's 4 states are 16
+    // contiguous bytes, a wave's 16 channels 1 KB
+    auto hstart = [&](int64_t c) -> float4* {
+      return reinterpret_cast<float4*>(p.hstart + ((b * nc + c) * p.dim + d) * N + n0);
+    };
     float Bv[2][NPL], Cv[2][NPL];
     auto read_b = [&](int buf) {
 #pragma unroll
@@ -153,16 +158,14 @@ __global__ __launch_bounds__(64 * kBwdRowsWaves) void scan_bwd_rows_kernel(const
     };
 
     // ---- phase 0: forward over chunk j - 1 in iteration j, storing its starting state ----------
-    {
+    // (skipped by every role when the forward pass stored the states)
+    if (!p.have_hstart) {
       float h[NPL] = {0.0f, 0.0f, 0.0f, 0.0f};
       for (int64_t j = 0; j <= nc; ++j) {
         if (j >= 1) {
           const int64_t c = j - 1;
           const int buf = static_cast<int>(c & 1);
-          if (lane_ok) {
-#pragma unroll
-            for (int q = 0; q < NPL; ++q) *hstart(c, q) = h[q];
-          }
+          if (lane_ok) *hstart(c) = make_float4(h[0], h[1], h[2], h[3]);
           read_b(buf);
           // (dt, dt x) in batches of 8 steps, each read while the batch before it runs
           float2 rq[2][8];
@@ -191,8 +194,8 @@ __global__ __launch_bounds__(64 * kBwdRowsWaves) void scan_bwd_rows_kernel(const
     float hn[NPL];
     auto load_hn = [&](int64_t c) {
       const int64_t cc = c < 0 ? 0 : c;
-#pragma unroll
-      for (int q = 0; q < NPL; ++q) hn[q] = lane_ok ? *hstart(cc, q) : 0.0f;
+      const float4 v = lane_ok ? *hstart(cc) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      hn[0] = v.x; hn[1] = v.y; hn[2] = v.z; hn[3] = v.w;
     };
     load_hn(nc - 1);
     __syncthreads();  // iteration -1: the prologue stages chunk nc - 1
@@ -345,7 +348,7 @@ __global__ __launch_bounds__(64 * kBwdRowsWaves) void scan_bwd_rows_kernel(const
     using Slot1 = std::integral_constant<int, 1>;
 
     // ---- phase 0: (dt, dt x) of chunk j in iteration j, tiles loaded two iterations ahead ------
-    {
+    if (!p.have_hstart) {
       RawVec<true, VEC> nx[2][ITEMS], nd[2][ITEMS];
       auto load = [&](int64_t c, auto SL) {
         constexpr int sl = decltype(SL)::value;
@@ -482,7 +485,7 @@ __global__ __launch_bounds__(64 * kBwdRowsWaves) void scan_bwd_rows_kernel(const
     using Slot0 = std::integral_constant<int, 0>;
     using Slot1 = std::integral_constant<int, 1>;
     // ---- phase 0: B of chunk j in iteration j ------------------------------------------------
-    {
+    if (!p.have_hstart) {
       uint4 nb[2];
       auto load = [&](int64_t c, auto SL) {
         nb[decltype(SL)::value] = *reinterpret_cast<const uint4*>(Bg + piece_off(c));
@@ -573,7 +576,8 @@ __global__ __launch_bounds__(64 * kBwdRowsWaves) void scan_bwd_rows_kernel(const
         ebias[i][v] = (ok && p.delta_bias) ? p.delta_bias[dc + v] : 0.0f;
       }
     }
-    for (int64_t j = 0; j <= nc; ++j) __syncthreads();  // phase 0
+    if (!p.have_hstart)
+      for (int64_t j = 0; j <= nc; ++j) __syncthreads();  // phase 0
     for (int64_t i = -1; i <= nc; ++i) {
       const int64_t ce = nc - i;
       if (ce < nc) {
@@ -645,7 +649,8 @@ __global__ __launch_bounds__(64 * kBwdRowsWaves) void scan_bwd_rows_kernel(const
   }
 
   // ===================================== the other waves: barriers only =========================
-  for (int64_t j = 0; j <= nc; ++j) __syncthreads();
+  if (!p.have_hstart)
+    for (int64_t j = 0; j <= nc; ++j) __syncthreads();
   for (int64_t i = -1; i <= nc; ++i) __syncthreads();
 }
 

@@ -54,6 +54,8 @@ struct ScanArgs {
   float* last_state;
   float* seg_state;  // (nseg, batch, dim, N): end state of a segment (AGG) / incoming state (FULL)
   float* seg_dsum;   // (nseg, batch, dim): summed step of a segment (AGG)
+  float* ckpt;       // (batch, ceil(seqlen / 32), dim, N): the state entering every 32nd step, or NULL
+                     // (state rows only)
   int64_t batch;
   int64_t seqlen;
   int64_t dim;

@@ -149,7 +149,14 @@ __global__ __launch_bounds__(64 * kRowsWaves) void scan_rows_kernel(const ScanAr
     __syncthreads();  // iteration -1: the prologue stages chunk 1
     int sbuf = 0;     // (dt, dt x) and B / C buffer of chunk j
     int pbuf = 1;     // the same of chunk j + 1
+    // the state entering every 32nd step, for a backward pass that starts from it: (batch,
+    // ceil(L / 32), dim, 16) as last_state, so a lane's 4 states are one 16-byte store and a
+    // wave's 16 channels 1 KB
+    const int64_t nck = (t_end + 31) / 32;
+    float* const ck = (p.ckpt && lane_ok) ? p.ckpt + (b * nck * p.dim + d) * N + n0 : nullptr;
     for (int64_t j = 0; j < nchunks; ++j) {
+      if (ck != nullptr && (CH == 32 || (j & 1) == 0))
+        *reinterpret_cast<float4*>(ck + ((j * CH) / 32) * p.dim * N) = make_float4(h[0], h[1], h[2], h[3]);
       if constexpr (kHalves == 2) read_bc(1, sbuf);
       const int yb = static_cast<int>(j & 1);
       float ypp = 0.0f;  // read-out of the even step, written with the odd one

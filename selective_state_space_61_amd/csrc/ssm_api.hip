@@ -249,7 +249,8 @@ struct ScratchSource {
 ssm_status_t scan_fwd_impl(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, ssm_dtype_t dtype,
                            const void* x, const void* delta, const float* A, const void* B, const void* C,
                            const float* D, const void* z, const float* delta_bias, int delta_softplus, void* y,
-                           float* last_state, void* stream, const ssm_scan_opts_t* opts, ScratchSource src) {
+                           float* last_state, void* stream, const ssm_scan_opts_t* opts, ScratchSource src,
+                           float* ckpt = nullptr) {
   if (batch < 0 || seqlen < 0 || dim < 0 || dstate < 0)
     return fail(SSM_ERR_INVALID_ARG, "negative size (batch=%lld seqlen=%lld dim=%lld dstate=%lld)",
                 (long long)batch, (long long)seqlen, (long long)dim, (long long)dstate);
@@ -270,16 +271,31 @@ ssm_status_t scan_fwd_impl(int64_t batch, int64_t seqlen, int64_t dim, int64_t d
   }
   const Arg args[] = {{x, es, "x"}, {delta, es, "delta"}, {A, 4, "A"}, {B, es, "B"}, {C, es, "C"},
                       {D, 4, "D"}, {z, es, "z"}, {delta_bias, 4, "delta_bias"}, {y, es, "y"},
-                      {last_state, 4, "last_state"}};
+                      {last_state, 4, "last_state"}, {ckpt, 4, "checkpoints"}};
   if (const Arg* bad = misaligned(args, sizeof args / sizeof args[0]))
     return fail(SSM_ERR_MISALIGNED, "%s (%p) is not aligned to its element size", bad->name, bad->p);
   if (dtype == SSM_BF16 && (dstate % 2) == 0 && seqlen > 0 && !(aligned(B, 4) && aligned(C, 4)))
     return fail(SSM_ERR_MISALIGNED, "bf16 B and C must be 4-byte aligned when dstate is even");
+  if (!aligned(ckpt, 16)) return fail(SSM_ERR_MISALIGNED, "checkpoints (%p) is not 16-byte aligned", ckpt);
+  // checkpoints: (batch, ceil(seqlen / 32), dim, dstate) fp32
+  int64_t n_ck = 0;
+  if (ckpt && (!mul_ok(batch, (seqlen + 31) / 32, &n_ck) || !mul_ok(n_ck, dstate * 4, &n_ck) ||
+               !mul_ok(n_ck, dim, &n_ck)))
+    return fail(SSM_ERR_INVALID_ARG, "tensor size overflows int64");
   const Range rx{x, n_bld}, rd{delta, n_bld}, rz{z, n_bld}, rB{B, n_bln}, rC{C, n_bln}, rA{A, n_dn},
-      rD{D, dim * 4}, rb{delta_bias, dim * 4}, ry{seqlen > 0 ? y : nullptr, n_bld}, rs{last_state, n_bdn};
+      rD{D, dim * 4}, rb{delta_bias, dim * 4}, ry{seqlen > 0 ? y : nullptr, n_bld}, rs{last_state, n_bdn},
+      rk{seqlen > 0 ? ckpt : nullptr, n_ck};
   for (Range in : {rx, rd, rz, rB, rC, rA, rD, rb})
-    if (overlap(ry, in) || overlap(rs, in)) return fail(SSM_ERR_INVALID_ARG, "an output overlaps an input");
+    if (overlap(ry, in) || overlap(rs, in) || overlap(rk, in))
+      return fail(SSM_ERR_INVALID_ARG, "an output overlaps an input");
   if (overlap(ry, rs)) return fail(SSM_ERR_INVALID_ARG, "y overlaps last_state");
+  if (overlap(rk, ry) || overlap(rk, rs)) return fail(SSM_ERR_INVALID_ARG, "checkpoints overlap y or last_state");
+
+  if (ckpt && (dstate != 16 || (opts && (opts->bbar_mode != SSM_BBAR_DELTA_B || opts->segments > 1 ||
+                                          (opts->layout != SSM_LAYOUT_AUTO && opts->layout != SSM_LAYOUT_STATE_ROWS) ||
+                                          (opts->chains_per_lane != 0 && opts->chains_per_lane != 4)))))
+    return fail(SSM_ERR_UNSUPPORTED,
+                "checkpoints need the state-row layout: dstate 16, SSM_BBAR_DELTA_B, one segment");
 
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (seqlen == 0) {
@@ -345,7 +361,8 @@ ssm_status_t scan_fwd_impl(int64_t batch, int64_t seqlen, int64_t dim, int64_t d
                   "SSM_LAYOUT_STATE_ROWS needs dstate 16, SSM_BBAR_DELTA_B, one segment and 4 chains per lane");
     if (layout == SSM_LAYOUT_CHANNEL_LANES && opts && opts->channel_groups != 0)
       return fail(SSM_ERR_UNSUPPORTED, "channel_groups applies to SSM_LAYOUT_STATE_ROWS only");
-    const bool use_rows = rows_fit && (layout == SSM_LAYOUT_STATE_ROWS || (layout == SSM_LAYOUT_AUTO && !split_auto));
+    const bool use_rows =
+        rows_fit && (layout == SSM_LAYOUT_STATE_ROWS || (layout == SSM_LAYOUT_AUTO && (!split_auto || ckpt)));
     if (use_rows) {
       const int cus = device_cus();
       int S = opts ? opts->channel_groups : 0;
@@ -380,7 +397,7 @@ ssm_status_t scan_fwd_impl(int64_t batch, int64_t seqlen, int64_t dim, int64_t d
       const bool ch32 = chunk_opt == 32 || (chunk_opt == 0 && rv.k[1] && rgrid <= cus);
       ssm::ScanArgs a{};
       a.x = x; a.delta = delta; a.A = A; a.B = B; a.C = C; a.Dskip = D; a.z = z; a.delta_bias = delta_bias;
-      a.y = y; a.last_state = last_state;
+      a.y = y; a.last_state = last_state; a.ckpt = ckpt;
       a.batch = batch; a.seqlen = seqlen; a.dim = dim; a.seg_len = seqlen;
       a.nseg = 1;
       a.ncb = static_cast<int32_t>(rncb);
@@ -391,6 +408,7 @@ ssm_status_t scan_fwd_impl(int64_t batch, int64_t seqlen, int64_t dim, int64_t d
       return check_launch("scan (state rows)");
     }
   }
+  if (ckpt) return fail(SSM_ERR_UNSUPPORTED, "checkpoints need the state-row layout");
   int npl = default_npl(dstate, split_auto ? 1024 : base_wgs);
   if (opts && opts->chains_per_lane) {
     if (!npl_supported(dstate, opts->chains_per_lane))
@@ -543,6 +561,17 @@ ssm_status_t ssm_scan_fwd_noalloc(int64_t batch, int64_t seqlen, int64_t dim, in
                        last_state, stream, opts, ScratchSource{ptr, kNoAllocScratchFloats});
 }
 
+ssm_status_t ssm_scan_fwd_ckpt(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, ssm_dtype_t dtype,
+                               const void* x, const void* delta, const float* A, const void* B, const void* C,
+                               const float* D, const void* z, const float* delta_bias, int delta_softplus, void* y,
+                               float* last_state, float* checkpoints, void* stream) {
+  g_err[0] = '\0';
+  if (!checkpoints && batch > 0 && seqlen > 0 && dim > 0 && dstate > 0)
+    return fail(SSM_ERR_INVALID_ARG, "NULL checkpoints");
+  return scan_fwd_impl(batch, seqlen, dim, dstate, dtype, x, delta, A, B, C, D, z, delta_bias, delta_softplus, y,
+                       last_state, stream, nullptr, ScratchSource{nullptr, 0}, checkpoints);
+}
+
 ssm_status_t ssm_scan_fwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, ssm_dtype_t dtype,
                           const void* x, const void* delta, const float* A, const void* B, const void* C,
                           const float* D, const void* z, const float* delta_bias, int delta_softplus, void* y,
@@ -622,12 +651,18 @@ ssm_status_t ssm_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t ds
                          dx, ddelta, dA, dB, dC, dD, dz, ddelta_bias, stream, nullptr);
 }
 
-ssm_status_t ssm_scan_bwd_ex(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, ssm_dtype_t dtype,
-                             const void* x, const void* delta, const float* A, const void* B, const void* C,
-                             const float* D, const void* z, const float* delta_bias, int delta_softplus,
-                             const void* dy, void* dx, void* ddelta, float* dA, void* dB, void* dC, float* dD,
-                             void* dz, float* ddelta_bias, void* stream, const ssm_bwd_opts_t* opts) {
-  g_err[0] = '\0';
+}  // extern "C"
+
+namespace {
+
+// The backward; ckpt (batch, ceil(seqlen / 32), dim, 16) fp32, when given, holds the forward's
+// chunk-start states and replaces the state-row kernel's phase 0.
+ssm_status_t scan_bwd_impl(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, ssm_dtype_t dtype,
+                           const void* x, const void* delta, const float* A, const void* B, const void* C,
+                           const float* D, const void* z, const float* delta_bias, int delta_softplus,
+                           const void* dy, void* dx, void* ddelta, float* dA, void* dB, void* dC, float* dD,
+                           void* dz, float* ddelta_bias, void* stream, const ssm_bwd_opts_t* opts,
+                           const float* ckpt) {
   if (opts) {
     if (opts->bbar_mode != SSM_BBAR_DELTA_B && opts->bbar_mode != SSM_BBAR_ZOH)
       return fail(SSM_ERR_UNSUPPORTED, "bbar_mode %d is not SSM_BBAR_DELTA_B or SSM_BBAR_ZOH", (int)opts->bbar_mode);
@@ -665,8 +700,14 @@ ssm_status_t ssm_scan_bwd_ex(int64_t batch, int64_t seqlen, int64_t dim, int64_t
     return fail(SSM_ERR_MISALIGNED, "%s (%p) is not aligned to its element size", bad->name, bad->p);
   if (dtype == SSM_BF16 && !empty && !(aligned(B, 4) && aligned(C, 4)))
     return fail(SSM_ERR_MISALIGNED, "bf16 B and C must be 4-byte aligned");
+  int64_t n_ck = 0;
+  if (ckpt && (!mul_ok(batch, (seqlen + 31) / 32, &n_ck) || !mul_ok(n_ck, dstate * 4, &n_ck) ||
+               !mul_ok(n_ck, dim, &n_ck)))
+    return fail(SSM_ERR_INVALID_ARG, "tensor size overflows int64");
+  if (!aligned(ckpt, 16)) return fail(SSM_ERR_MISALIGNED, "checkpoints (%p) is not 16-byte aligned", ckpt);
   const Range ins[] = {{x, n_bld}, {delta, n_bld}, {z, n_bld}, {dy, n_bld}, {B, n_bln}, {C, n_bln},
-                       {A, dim * dstate * 4}, {D, dim * 4}, {delta_bias, dim * 4}};
+                       {A, dim * dstate * 4}, {D, dim * 4}, {delta_bias, dim * 4},
+                       {empty ? nullptr : ckpt, n_ck}};
   const Range outs[] = {{dx, n_bld}, {ddelta, n_bld}, {dz, n_bld}, {dB, n_bln}, {dC, n_bln},
                         {dA, dim * dstate * 4}, {dD, dim * 4}, {ddelta_bias, dim * 4}};
   for (const Range& o : outs) {
@@ -685,6 +726,10 @@ ssm_status_t ssm_scan_bwd_ex(int64_t batch, int64_t seqlen, int64_t dim, int64_t
     return fail(SSM_ERR_UNSUPPORTED,
                 "SSM_LAYOUT_STATE_ROWS backward needs bf16, dstate 16, SSM_BBAR_DELTA_B, dim a multiple of 8 and "
                 "16-byte aligned x, delta, z, dy, dx, ddelta, dz, B, C");
+  if (ckpt && !empty && (!rows_fit || layout == SSM_LAYOUT_CHANNEL_LANES))
+    return fail(SSM_ERR_UNSUPPORTED,
+                "a backward from checkpoints needs the state-row layout: bf16, dstate 16, SSM_BBAR_DELTA_B, dim a "
+                "multiple of 8 and 16-byte aligned x, delta, z, dy, dx, ddelta, dz, B, C");
   if (rows_fit && layout != SSM_LAYOUT_CHANNEL_LANES) {
     // scan waves per workgroup: the fewest rounds of one workgroup per CU, then the larger
     // workgroup (a workgroup's time does not depend on its scan waves, one per SIMD)
@@ -704,7 +749,7 @@ ssm_status_t ssm_scan_bwd_ex(int64_t batch, int64_t seqlen, int64_t dim, int64_t
     int64_t grid;
     if (!mul_ok(batch, ncb, &grid) || grid > 0x7fffffff) return fail(SSM_ERR_UNSUPPORTED, "grid too large");
     // scratch: chunk-start states, the dB / dC accumulator, dA / dD / dbias batch partials
-    const int64_t n_h = batch * nc * 16 * dim;
+    const int64_t n_h = ckpt ? 0 : batch * nc * 16 * dim;
     const int64_t n_bc = 2 * batch * seqlen * 16;
     const int64_t n_a = batch * 16 * dim;
     const int64_t n_d = batch * T * dim;
@@ -714,7 +759,8 @@ ssm_status_t ssm_scan_bwd_ex(int64_t batch, int64_t seqlen, int64_t dim, int64_t
     ssm::BwdArgs a{};
     a.x = x; a.delta = delta; a.A = A; a.B = B; a.C = C; a.Dskip = D; a.z = z; a.delta_bias = delta_bias; a.dy = dy;
     a.dx = dx; a.ddelta = ddelta; a.dz = dz;
-    a.hstart = scratch;
+    a.hstart = ckpt ? const_cast<float*>(ckpt) : scratch;  // read only when given
+    a.have_hstart = ckpt ? 1 : 0;
     a.part_bc = scratch + n_h;
     a.part_a = a.part_bc + n_bc;
     a.part_d = a.part_a + n_a;
@@ -790,6 +836,32 @@ ssm_status_t ssm_scan_bwd_ex(int64_t batch, int64_t seqlen, int64_t dim, int64_t
       dtype == SSM_BF16 ? ssm::scan_bwd_reduce_kernel<true> : ssm::scan_bwd_reduce_kernel<false>;
   hipLaunchKernelGGL(rk, dim3(static_cast<unsigned>((nred + 255) / 256)), dim3(256), 0, st, r);
   return check_launch("scan backward reduce");
+}
+
+}  // namespace
+
+extern "C" {
+
+ssm_status_t ssm_scan_bwd_ex(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, ssm_dtype_t dtype,
+                             const void* x, const void* delta, const float* A, const void* B, const void* C,
+                             const float* D, const void* z, const float* delta_bias, int delta_softplus,
+                             const void* dy, void* dx, void* ddelta, float* dA, void* dB, void* dC, float* dD,
+                             void* dz, float* ddelta_bias, void* stream, const ssm_bwd_opts_t* opts) {
+  g_err[0] = '\0';
+  return scan_bwd_impl(batch, seqlen, dim, dstate, dtype, x, delta, A, B, C, D, z, delta_bias, delta_softplus, dy,
+                       dx, ddelta, dA, dB, dC, dD, dz, ddelta_bias, stream, opts, nullptr);
+}
+
+ssm_status_t ssm_scan_bwd_ckpt(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, ssm_dtype_t dtype,
+                               const void* x, const void* delta, const float* A, const void* B, const void* C,
+                               const float* D, const void* z, const float* delta_bias, int delta_softplus,
+                               const void* dy, void* dx, void* ddelta, float* dA, void* dB, void* dC, float* dD,
+                               void* dz, float* ddelta_bias, const float* checkpoints, void* stream) {
+  g_err[0] = '\0';
+  if (!checkpoints && batch > 0 && seqlen > 0 && dim > 0 && dstate > 0)
+    return fail(SSM_ERR_INVALID_ARG, "NULL checkpoints");
+  return scan_bwd_impl(batch, seqlen, dim, dstate, dtype, x, delta, A, B, C, D, z, delta_bias, delta_softplus, dy,
+                       dx, ddelta, dA, dB, dC, dD, dz, ddelta_bias, stream, nullptr, checkpoints);
 }
 
 ssm_status_t ssm_causal_conv1d_fwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t width, ssm_dtype_t dtype,

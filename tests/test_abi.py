@@ -328,3 +328,32 @@ def test_time_scan_opts_validation(lib):
     assert scan(lib, dstate=16, opts=ssm.ScanOpts(0, 2, 0, 0, ts)) == UNSUPPORTED
     assert scan(lib, dstate=16, opts=ssm.ScanOpts(0, 0, 0, 0, ts, 2)) == UNSUPPORTED
     assert scan(lib, dstate=16, opts=ssm.ScanOpts(0, 0, 128, 0, ts)) == UNSUPPORTED and "chunk_steps" in err(lib)
+
+
+def test_checkpoint_pair_validation(lib):
+    """ssm_scan_fwd_ckpt / ssm_scan_bwd_ckpt: the checkpoints are required when there is work,
+    must be 16-byte aligned and must not overlap another argument; both need the state rows."""
+    def fwd(ck=fake(10), dstate=16, dtype=BF16, batch=2, seqlen=8, dim=16, y=fake(8)):
+        return lib.ssm_scan_fwd_ckpt(batch, seqlen, dim, dstate, dtype, fake(0), fake(1), fake(2), fake(3),
+                                     fake(4), fake(5), fake(6), fake(7), 1, y, fake(9), ck, None)
+
+    def bwd(ck=fake(20), dstate=16, dtype=BF16, batch=2, seqlen=8, dim=16):
+        args = [batch, seqlen, dim, dstate, dtype] + [fake(i) for i in range(8)] + [1] + \
+               [fake(8 + i) for i in range(9)]
+        return lib.ssm_scan_bwd_ckpt(*args, ck, None)
+
+    assert fwd(ck=None) == INVALID and "checkpoints" in err(lib)
+    assert bwd(ck=None) == INVALID and "checkpoints" in err(lib)
+    assert fwd(ck=None, batch=0) == OK  # nothing to compute
+    assert bwd(ck=None, dim=0) == OK
+    assert fwd(ck=fake(10, 2)) == MISALIGNED and "checkpoints" in err(lib)
+    assert bwd(ck=fake(20, 2)) == MISALIGNED and "checkpoints" in err(lib)
+    assert fwd(ck=fake(10, 8)) == MISALIGNED and "16-byte" in err(lib)
+    assert bwd(ck=fake(20, 8)) == MISALIGNED and "16-byte" in err(lib)
+    assert fwd(ck=fake(8)) == INVALID and "overlap" in err(lib)   # on y
+    assert fwd(ck=fake(0)) == INVALID and "overlap" in err(lib)   # on x
+    assert bwd(ck=fake(9)) == INVALID and "overlap" in err(lib)   # on dx (an output)
+    assert fwd(dstate=8) == UNSUPPORTED and "state-row" in err(lib)
+    assert bwd(dstate=8) == UNSUPPORTED
+    assert bwd(dtype=F32) == UNSUPPORTED and "state-row" in err(lib)
+    assert bwd(dim=12) == UNSUPPORTED and "state-row" in err(lib)
