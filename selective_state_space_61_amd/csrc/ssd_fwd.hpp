@@ -394,16 +394,35 @@ void ssd_chunk_kernel(const SsdArgs p) {
         ssd_f32x4_t gt[kTiles];
 #pragma unroll
         for (int s = 0; s < kTiles; ++s) gt[s] = ssd_f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        if constexpr (NW == 4) {
+          // wave w's tiles are (w / 2, w % 2), (2, w) and (3, w): the last two share their B rows,
+          // and for w < 2 the first does too, so a K step reads 4 or 5 fragments instead of 6
+          const bool b0_shared = wave < 2;
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks)
-#pragma unroll
-          for (int s = 0; s < kTiles; ++s) {
-            const int k = wave + NW * s;
-            const int ib = gram_tile_i(k), jb = gram_tile_j(k);
-            gt[s] = mfma16x16x32(*reinterpret_cast<const ssd_u32x4_t*>(&s_b[(16 * jb + l16) * LDB + 32 * ks + 8 * q]),
-                                 *reinterpret_cast<const ssd_u32x4_t*>(&s_c[(16 * ib + l16) * LDB + 32 * ks + 8 * q]),
-                                 gt[s]);
+          for (int ks = 0; ks < NKS; ++ks) {
+            const int col = 32 * ks + 8 * q;
+            const ssd_u32x4_t bw = *reinterpret_cast<const ssd_u32x4_t*>(&s_b[(16 * wave + l16) * LDB + col]);
+            const ssd_u32x4_t c2 = *reinterpret_cast<const ssd_u32x4_t*>(&s_c[(32 + l16) * LDB + col]);
+            const ssd_u32x4_t c3 = *reinterpret_cast<const ssd_u32x4_t*>(&s_c[(48 + l16) * LDB + col]);
+            const ssd_u32x4_t c0 = *reinterpret_cast<const ssd_u32x4_t*>(&s_c[(16 * (wave >> 1) + l16) * LDB + col]);
+            const ssd_u32x4_t b0 =
+                b0_shared ? bw : *reinterpret_cast<const ssd_u32x4_t*>(&s_b[(16 * (wave & 1) + l16) * LDB + col]);
+            gt[0] = mfma16x16x32(b0, c0, gt[0]);
+            gt[1] = mfma16x16x32(bw, c2, gt[1]);
+            gt[2] = mfma16x16x32(bw, c3, gt[2]);
           }
+        } else {
+#pragma unroll
+          for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+            for (int s = 0; s < kTiles; ++s) {
+              const int k = wave + NW * s;
+              const int ib = gram_tile_i(k), jb = gram_tile_j(k);
+              gt[s] = mfma16x16x32(*reinterpret_cast<const ssd_u32x4_t*>(&s_b[(16 * jb + l16) * LDB + 32 * ks + 8 * q]),
+                                   *reinterpret_cast<const ssd_u32x4_t*>(&s_c[(16 * ib + l16) * LDB + 32 * ks + 8 * q]),
+                                   gt[s]);
+            }
+        }
 #pragma unroll
         for (int s = 0; s < kTiles; ++s) {
           const int k = wave + NW * s;
