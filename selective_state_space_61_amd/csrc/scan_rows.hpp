@@ -12,7 +12,8 @@
 // So a workgroup has 16 waves in four groups of one SIMD each.  Waves 3, 7, 11 (the prologue) and
 // 15 (the epilogue) share one SIMD; the scan waves take the slots of the other three SIMDs (slot
 // k = wave (k / 3) * 4 + k % 3: waves 0, 1, 2, then 4, 5, 6, ...); slot S holds the B / C
-// stager; the other slots only take part in the barriers.
+// stager (with three scan waves, slots 3 and 4: B on one, C on the other); the other slots only
+// take part in the barriers.
 //
 //   * scan wave s (S per workgroup) covers channels 16 s .. 16 s + 15 of the workgroup's 16 S:
 //     lane = 16 r + k is channel k with state indices 4 r .. 4 r + 3 in VGPRs for the whole
@@ -338,7 +339,11 @@ __global__ __launch_bounds__(64 * kRowsWaves) void scan_rows_kernel(const ScanAr
     return;
   }
 
-  if (group != 3 && slot == S) {
+  // With three scan waves (one per scan SIMD) B and C are staged by two waves, slots 3 and 4
+  // (SIMDs 0 and 1), so that each scan wave loses less issue to the staging; otherwise one wave in
+  // slot S stages both (on a SIMD with the fewest scan waves for S = 2, 4, 5).
+  constexpr bool kSplitStager = S == 3;
+  if (group != 3 && (slot == S || (kSplitStager && slot == S + 1))) {
     // =============================== B / C stager ================================================
     // B and C rows of a chunk, staged as fp32 for the scan waves two chunks ahead of them, from
     // 32-bit words loaded one iteration earlier: word w = lane + 64 i of a tile is step w / WPR,
@@ -348,48 +353,57 @@ __global__ __launch_bounds__(64 * kRowsWaves) void scan_rows_kernel(const ScanAr
     constexpr int WPR = BF16 ? 8 : 16;  // 32-bit words per row of 16 states
     constexpr int WPT = CH * WPR;       // words per tile
     constexpr int BI = WPT / 64;
-    uint32_t nbw[BI], ncw[BI];
-    auto load_bc_tile = [&](int64_t c) {
-      const int64_t lim = t_end - 1 - c * CH;  // last step of the sequence, relative to the chunk
-      const uint32_t* bsrc = static_cast<const uint32_t*>(p.B) + (row_base + c * CH) * WPR;
-      const uint32_t* csrc = static_cast<const uint32_t*>(p.C) + (row_base + c * CH) * WPR;
+    // NT tensors from tensor t0 (0 = B, 1 = C)
+    auto run = [&](auto NT_, int t0) {
+      constexpr int NT = decltype(NT_)::value;
+      const uint32_t* src[NT];
 #pragma unroll
-      for (int i = 0; i < BI; ++i) {
-        const int w = lane + 64 * i;
-        const int row = w / WPR;
-        const int64_t off = (row <= lim ? static_cast<int64_t>(row) : lim) * WPR + w % WPR;
-        nbw[i] = bsrc[off];
-        ncw[i] = csrc[off];
-      }
-    };
-    auto stage_bc = [&](int64_t c) {
-      const int pb = static_cast<int>(c % kRowsDwBufs);
+      for (int tt = 0; tt < NT; ++tt) src[tt] = static_cast<const uint32_t*>(t0 + tt == 0 ? p.B : p.C);
+      uint32_t nw[NT][BI];
+      auto load_bc_tile = [&](int64_t c) {
+        const int64_t lim = t_end - 1 - c * CH;  // last step of the sequence, relative to the chunk
 #pragma unroll
-      for (int i = 0; i < BI; ++i) {
-        const int w = lane + 64 * i;
-        const int row = w / WPR, wc = w % WPR;
-        const bool ok = c * CH + row < t_end;
-        const uint32_t bw = ok ? nbw[i] : 0u, cw = ok ? ncw[i] : 0u;
-        if constexpr (BF16) {
-          *reinterpret_cast<float2*>(&s_bc[pb][0][row][2 * wc]) = make_float2(bf16_lo(bw), bf16_hi(bw));
-          *reinterpret_cast<float2*>(&s_bc[pb][1][row][2 * wc]) = make_float2(bf16_lo(cw), bf16_hi(cw));
-        } else {
-          s_bc[pb][0][row][wc] = __builtin_bit_cast(float, bw);
-          s_bc[pb][1][row][wc] = __builtin_bit_cast(float, cw);
+        for (int i = 0; i < BI; ++i) {
+          const int w = lane + 64 * i;
+          const int row = w / WPR;
+          const int64_t off = (row_base + c * CH + (row <= lim ? static_cast<int64_t>(row) : lim)) * WPR + w % WPR;
+#pragma unroll
+          for (int tt = 0; tt < NT; ++tt) nw[tt][i] = src[tt][off];
         }
+      };
+      auto stage_bc = [&](int64_t c) {
+        const int pb = static_cast<int>(c % kRowsDwBufs);
+#pragma unroll
+        for (int i = 0; i < BI; ++i) {
+          const int w = lane + 64 * i;
+          const int row = w / WPR, wc = w % WPR;
+          const bool ok = c * CH + row < t_end;
+#pragma unroll
+          for (int tt = 0; tt < NT; ++tt) {
+            const uint32_t word = ok ? nw[tt][i] : 0u;
+            if constexpr (BF16)
+              *reinterpret_cast<float2*>(&s_bc[pb][t0 + tt][row][2 * wc]) = make_float2(bf16_lo(word), bf16_hi(word));
+            else
+              s_bc[pb][t0 + tt][row][wc] = __builtin_bit_cast(float, word);
+          }
+        }
+      };
+      // iteration j: B / C of chunk j + 2, then the loads of chunk j + 3's rows (past the last
+      // chunk: in-range loads whose values go unused)
+      load_bc_tile(0);
+      for (int64_t j = -2; j <= nchunks; ++j) {
+        // the words are taken in on every path, so that no path leaves their loads outstanding
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+          for (int i = 0; i < BI; ++i) asm volatile("" ::"v"(nw[tt][i]));
+        if (j + 2 < nchunks) stage_bc(j + 2);
+        load_bc_tile(j + 3);
+        __syncthreads();
       }
     };
-    // iteration j: B / C of chunk j + 2, then the loads of chunk j + 3's rows (past the last
-    // chunk: in-range loads whose values go unused)
-    load_bc_tile(0);
-    for (int64_t j = -2; j <= nchunks; ++j) {
-      // the words are taken in on every path, so that no path leaves their loads outstanding
-#pragma unroll
-      for (int i = 0; i < BI; ++i) asm volatile("" ::"v"(nbw[i]), "v"(ncw[i]));
-      if (j + 2 < nchunks) stage_bc(j + 2);
-      load_bc_tile(j + 3);
-      __syncthreads();
-    }
+    if constexpr (kSplitStager) run(std::integral_constant<int, 1>{}, slot - S);
+    else run(std::integral_constant<int, 2>{}, 0);
     return;
   }
 
