@@ -80,6 +80,53 @@ __device__ __forceinline__ void permlane32_swap(float& a, float& b) {
   b = __builtin_bit_cast(float, y);
 }
 
+// One step of the four state chains of a lane with separate input and output state registers
+// (the recompute keeps all 33 states of a chunk): out_j = exp2(dt a2_j) in_j + B_j w with B
+// broadcast from lane KB of each row, and the read-out of the input states, sum_j C_j in_j with C
+// broadcast from lane KC (the previous step's read-out).  The instructions and their order are
+// those of step_readout4 (the forward's block), so the states are the forward's bits.
+#define SSM_BWD_DPP_KB "row_newbcast:%[kb] row_mask:0xf bank_mask:0xf"
+#define SSM_BWD_DPP_KC "row_newbcast:%[kc] row_mask:0xf bank_mask:0xf"
+template <int KB, int KC>
+__device__ __forceinline__ float step_readout4_io(float dt, float w, const float* a2, const float* b, const float* c,
+                                                  const float* hin, float* hout) {
+  float t0, t1, t2, t3, u0, u1, u2, u3, yp, o0, o1, o2, o3;
+  asm("v_mul_f32 %[t0], %[dt], %[a0]\n\t"
+      "v_mul_f32 %[t1], %[dt], %[a1]\n\t"
+      "v_mul_f32 %[t2], %[dt], %[a2]\n\t"
+      "v_mul_f32 %[t3], %[dt], %[a3]\n\t"
+      "v_exp_f32 %[t0], %[t0]\n\t"
+      "v_exp_f32 %[t1], %[t1]\n\t"
+      "v_exp_f32 %[t2], %[t2]\n\t"
+      "v_exp_f32 %[t3], %[t3]\n\t"
+      "v_mul_f32_dpp %[u0], %[b0], %[w] " SSM_BWD_DPP_KB "\n\t"
+      "v_mul_f32_dpp %[yp], %[c0], %[i0] " SSM_BWD_DPP_KC "\n\t"
+      "v_mul_f32_dpp %[u1], %[b1], %[w] " SSM_BWD_DPP_KB "\n\t"
+      "v_fma_f32 %[o0], %[t0], %[i0], %[u0]\n\t"
+      "v_fmac_f32_dpp %[yp], %[c1], %[i1] " SSM_BWD_DPP_KC "\n\t"
+      "v_mul_f32_dpp %[u2], %[b2], %[w] " SSM_BWD_DPP_KB "\n\t"
+      "v_fma_f32 %[o1], %[t1], %[i1], %[u1]\n\t"
+      "v_fmac_f32_dpp %[yp], %[c2], %[i2] " SSM_BWD_DPP_KC "\n\t"
+      "v_mul_f32_dpp %[u3], %[b3], %[w] " SSM_BWD_DPP_KB "\n\t"
+      "v_fma_f32 %[o2], %[t2], %[i2], %[u2]\n\t"
+      "v_fmac_f32_dpp %[yp], %[c3], %[i3] " SSM_BWD_DPP_KC "\n\t"
+      "v_fma_f32 %[o3], %[t3], %[i3], %[u3]"
+      : [t0] "=&v"(t0), [t1] "=&v"(t1), [t2] "=&v"(t2), [t3] "=&v"(t3), [u0] "=&v"(u0), [u1] "=&v"(u1),
+        [u2] "=&v"(u2), [u3] "=&v"(u3), [yp] "=&v"(yp), [o0] "=&v"(o0), [o1] "=&v"(o1), [o2] "=&v"(o2),
+        [o3] "=&v"(o3)
+      : [dt] "v"(dt), [w] "v"(w), [a0] "v"(a2[0]), [a1] "v"(a2[1]), [a2] "v"(a2[2]), [a3] "v"(a2[3]),
+        [b0] "v"(b[0]), [b1] "v"(b[1]), [b2] "v"(b[2]), [b3] "v"(b[3]), [c0] "v"(c[0]), [c1] "v"(c[1]),
+        [c2] "v"(c[2]), [c3] "v"(c[3]), [i0] "v"(hin[0]), [i1] "v"(hin[1]), [i2] "v"(hin[2]), [i3] "v"(hin[3]),
+        [kb] "i"(KB), [kc] "i"(KC));
+  hout[0] = o0;
+  hout[1] = o1;
+  hout[2] = o2;
+  hout[3] = o3;
+  return yp;
+}
+#undef SSM_BWD_DPP_KB
+#undef SSM_BWD_DPP_KC
+
 // The four 16-lane rows of y0 .. y3 summed per lane column: lane 16 q + k of the result holds
 // (y_q[k] + y_q[16 + k]) + (y_q[32 + k] + y_q[48 + k]).
 __device__ __forceinline__ float rows4_transpose_sum(float y0, float y1, float y2, float y3) {
@@ -213,21 +260,31 @@ __global__ __launch_bounds__(64 * kBwdRowsWaves) void scan_bwd_rows_kernel(const
       float yq[4];
       float2 rq[2][8];
       static_for<8>([&](auto J) { rq[0][decltype(J)::value] = s_dw[buf][decltype(J)::value][col]; });
-      static_for<T>([&](auto K) {
+      // step t's block also reads out step t - 1 (its input states); one more read-out after the
+      // last step
+      static_for<T + 1>([&](auto K) {
         constexpr int t = decltype(K)::value;
-        if constexpr (t % 8 == 0 && t + 8 < T)
-          static_for<8>([&](auto J) {
-            rq[(t / 8 + 1) & 1][decltype(J)::value] = s_dw[buf][t + 8 + decltype(J)::value][col];
-          });
-        const float2 dw = rq[(t / 8) & 1][t % 8];
-        float yp = 0.0f;
+        float yp;
+        if constexpr (t < T) {
+          if constexpr (t % 8 == 0 && t + 8 < T)
+            static_for<8>([&](auto J) {
+              rq[(t / 8 + 1) & 1][decltype(J)::value] = s_dw[buf][t + 8 + decltype(J)::value][col];
+            });
+          const float2 dw = rq[(t / 8) & 1][t % 8];
+          // (for t = 0 the read-out uses step 31's C and goes unused)
+          yp = step_readout4_io<t % 16, (t + 15) % 16>(dw.x, dw.y, A2, Bv[t / 16], Cv[((t + T - 1) % T) / 16], hs[t],
+                                                       hs[t + 1]);
+        } else {
+          yp = 0.0f;
 #pragma unroll
-        for (int q = 0; q < NPL; ++q) {
-          hs[t + 1][q] = fmaf(hw_exp2(dw.x * A2[q]), hs[t][q], row_bcast<t % 16>(Bv[t / 16][q]) * dw.y);
-          yp = fmaf(row_bcast<t % 16>(Cv[t / 16][q]), hs[t + 1][q], yp);
+          for (int q = 0; q < NPL; ++q) yp = fmaf(row_bcast<(T - 1) % 16>(Cv[(T - 1) / 16][q]), hs[T][q], yp);
         }
-        yq[t % 4] = yp;
-        if constexpr (t % 4 == 3) s_part[buf][0][t / 4][s][lane] = rows4_transpose_sum(yq[0], yq[1], yq[2], yq[3]);
+        if constexpr (t >= 1) {
+          constexpr int tp = t - 1;  // the step this read-out belongs to
+          yq[tp % 4] = yp;
+          if constexpr (tp % 4 == 3)
+            s_part[buf][0][tp / 4][s][lane] = rows4_transpose_sum(yq[0], yq[1], yq[2], yq[3]);
+        }
       });
       // reverse sweep.  The compiler barrier makes the sweep read (dt, dt x) from LDS again and
       // recompute abar, and the opaque B / C registers make it broadcast them again: reusing the
