@@ -124,8 +124,104 @@ __device__ __forceinline__ float step_readout4_io(float dt, float w, const float
   hout[3] = o3;
   return yp;
 }
+
+// One reverse step of the four state chains of a lane, B_t and C_t broadcast from lane KB of each
+// row.  With abar_{t+1} in an and the adjoint of the step after in g:
+//   g  <- abar_{t+1} g + dy0 C_t               (the adjoint of h_t)
+//   an <- abar_t = exp2(dt a2)
+//   gB  = sum_j g_j B_t,j                       (this row's share of d/d(dt x))
+//   pdt = sum_j a_j abar_t h_{t-1},j g_j        (this row's share of d/d(dt) through abar)
+//   dA += dt abar_t h_{t-1} g
+// The products and their rounding are those of the plain expressions: (abar h) g, fma chains.
+template <int KB>
+__device__ __forceinline__ void bwd_step4(float dt, float dy0, const float* a2, const float* araw, const float* b,
+                                          const float* c, const float* hin, float* g, float* an, float* dA,
+                                          float& gB, float& pdt) {
+  float t0, t1, t2, t3, u0, u1, u2, u3, gb, pd;
+  asm("v_mul_f32 %[t0], %[dt], %[a0]\n\t"
+      "v_mul_f32 %[t1], %[dt], %[a1]\n\t"
+      "v_mul_f32 %[t2], %[dt], %[a2]\n\t"
+      "v_mul_f32 %[t3], %[dt], %[a3]\n\t"
+      "v_mul_f32_dpp %[u0], %[c0], %[dy] " SSM_BWD_DPP_KB "\n\t"
+      "v_mul_f32_dpp %[u1], %[c1], %[dy] " SSM_BWD_DPP_KB "\n\t"
+      "v_mul_f32_dpp %[u2], %[c2], %[dy] " SSM_BWD_DPP_KB "\n\t"
+      "v_mul_f32_dpp %[u3], %[c3], %[dy] " SSM_BWD_DPP_KB "\n\t"
+      "v_fmac_f32 %[u0], %[n0], %[g0]\n\t"
+      "v_fmac_f32 %[u1], %[n1], %[g1]\n\t"
+      "v_fmac_f32 %[u2], %[n2], %[g2]\n\t"
+      "v_fmac_f32 %[u3], %[n3], %[g3]\n\t"
+      "v_exp_f32 %[n0], %[t0]\n\t"
+      "v_exp_f32 %[n1], %[t1]\n\t"
+      "v_exp_f32 %[n2], %[t2]\n\t"
+      "v_exp_f32 %[n3], %[t3]\n\t"
+      "v_mul_f32_dpp %[gb], %[b0], %[u0] " SSM_BWD_DPP_KB "\n\t"
+      "v_fmac_f32_dpp %[gb], %[b1], %[u1] " SSM_BWD_DPP_KB "\n\t"
+      "v_fmac_f32_dpp %[gb], %[b2], %[u2] " SSM_BWD_DPP_KB "\n\t"
+      "v_fmac_f32_dpp %[gb], %[b3], %[u3] " SSM_BWD_DPP_KB "\n\t"
+      "v_mul_f32 %[t0], %[n0], %[h0]\n\t"
+      "v_mul_f32 %[t1], %[n1], %[h1]\n\t"
+      "v_mul_f32 %[t2], %[n2], %[h2]\n\t"
+      "v_mul_f32 %[t3], %[n3], %[h3]\n\t"
+      "v_mul_f32 %[t0], %[t0], %[u0]\n\t"
+      "v_mul_f32 %[t1], %[t1], %[u1]\n\t"
+      "v_mul_f32 %[t2], %[t2], %[u2]\n\t"
+      "v_mul_f32 %[t3], %[t3], %[u3]\n\t"
+      "v_mul_f32 %[pd], %[t0], %[r0]\n\t"
+      "v_fmac_f32 %[d0], %[t0], %[dt]\n\t"
+      "v_fmac_f32 %[pd], %[t1], %[r1]\n\t"
+      "v_fmac_f32 %[d1], %[t1], %[dt]\n\t"
+      "v_fmac_f32 %[pd], %[t2], %[r2]\n\t"
+      "v_fmac_f32 %[d2], %[t2], %[dt]\n\t"
+      "v_fmac_f32 %[pd], %[t3], %[r3]\n\t"
+      "v_fmac_f32 %[d3], %[t3], %[dt]"
+      : [t0] "=&v"(t0), [t1] "=&v"(t1), [t2] "=&v"(t2), [t3] "=&v"(t3), [u0] "=&v"(u0), [u1] "=&v"(u1),
+        [u2] "=&v"(u2), [u3] "=&v"(u3), [gb] "=&v"(gb), [pd] "=&v"(pd), [n0] "+v"(an[0]), [n1] "+v"(an[1]),
+        [n2] "+v"(an[2]), [n3] "+v"(an[3]), [d0] "+v"(dA[0]), [d1] "+v"(dA[1]), [d2] "+v"(dA[2]), [d3] "+v"(dA[3])
+      : [dt] "v"(dt), [dy] "v"(dy0), [a0] "v"(a2[0]), [a1] "v"(a2[1]), [a2] "v"(a2[2]), [a3] "v"(a2[3]),
+        [r0] "v"(araw[0]), [r1] "v"(araw[1]), [r2] "v"(araw[2]), [r3] "v"(araw[3]), [b0] "v"(b[0]),
+        [b1] "v"(b[1]), [b2] "v"(b[2]), [b3] "v"(b[3]), [c0] "v"(c[0]), [c1] "v"(c[1]), [c2] "v"(c[2]),
+        [c3] "v"(c[3]), [h0] "v"(hin[0]), [h1] "v"(hin[1]), [h2] "v"(hin[2]), [h3] "v"(hin[3]), [g0] "v"(g[0]),
+        [g1] "v"(g[1]), [g2] "v"(g[2]), [g3] "v"(g[3]), [kb] "i"(KB));
+  g[0] = u0;
+  g[1] = u1;
+  g[2] = u2;
+  g[3] = u3;
+  gB = gb;
+  pdt = pd;
+}
 #undef SSM_BWD_DPP_KB
 #undef SSM_BWD_DPP_KC
+
+// sum_k p_k w_k over the 16 lanes k of a row, w_k taken from lane k of the lane's own row; two
+// fma chains of eight.  (The leading wait covers a VALU write of w just before: a DPP source.)
+__device__ __forceinline__ float dot16_row_bcast(const float4* p, float w) {
+  float s0, s1;
+#define SSM_BC(k) "row_newbcast:" #k " row_mask:0xf bank_mask:0xf"
+  asm("s_nop 1\n\t"
+      "v_mul_f32_dpp %[s0], %[w], %[p0] " SSM_BC(0) "\n\t"
+      "v_mul_f32_dpp %[s1], %[w], %[p8] " SSM_BC(8) "\n\t"
+      "v_fmac_f32_dpp %[s0], %[w], %[p1] " SSM_BC(1) "\n\t"
+      "v_fmac_f32_dpp %[s1], %[w], %[p9] " SSM_BC(9) "\n\t"
+      "v_fmac_f32_dpp %[s0], %[w], %[p2] " SSM_BC(2) "\n\t"
+      "v_fmac_f32_dpp %[s1], %[w], %[p10] " SSM_BC(10) "\n\t"
+      "v_fmac_f32_dpp %[s0], %[w], %[p3] " SSM_BC(3) "\n\t"
+      "v_fmac_f32_dpp %[s1], %[w], %[p11] " SSM_BC(11) "\n\t"
+      "v_fmac_f32_dpp %[s0], %[w], %[p4] " SSM_BC(4) "\n\t"
+      "v_fmac_f32_dpp %[s1], %[w], %[p12] " SSM_BC(12) "\n\t"
+      "v_fmac_f32_dpp %[s0], %[w], %[p5] " SSM_BC(5) "\n\t"
+      "v_fmac_f32_dpp %[s1], %[w], %[p13] " SSM_BC(13) "\n\t"
+      "v_fmac_f32_dpp %[s0], %[w], %[p6] " SSM_BC(6) "\n\t"
+      "v_fmac_f32_dpp %[s1], %[w], %[p14] " SSM_BC(14) "\n\t"
+      "v_fmac_f32_dpp %[s0], %[w], %[p7] " SSM_BC(7) "\n\t"
+      "v_fmac_f32_dpp %[s1], %[w], %[p15] " SSM_BC(15)
+      : [s0] "=&v"(s0), [s1] "=&v"(s1)
+      : [w] "v"(w), [p0] "v"(p[0].x), [p1] "v"(p[0].y), [p2] "v"(p[0].z), [p3] "v"(p[0].w), [p4] "v"(p[1].x),
+        [p5] "v"(p[1].y), [p6] "v"(p[1].z), [p7] "v"(p[1].w), [p8] "v"(p[2].x), [p9] "v"(p[2].y),
+        [p10] "v"(p[2].z), [p11] "v"(p[2].w), [p12] "v"(p[3].x), [p13] "v"(p[3].y), [p14] "v"(p[3].z),
+        [p15] "v"(p[3].w));
+#undef SSM_BC
+  return s0 + s1;
+}
 
 // The four 16-lane rows of y0 .. y3 summed per lane column: lane 16 q + k of the result holds
 // (y_q[k] + y_q[16 + k]) + (y_q[32 + k] + y_q[48 + k]).
@@ -309,19 +405,19 @@ __global__ __launch_bounds__(64 * kBwdRowsWaves) void scan_bwd_rows_kernel(const
       };
       read_batch(std::integral_constant<int, T / 4 - 1>{});
       float gq[4], pq[4];
-      // the transposed dB / dC rows of a round are read at its end and summed at the end of the
-      // next round, when the reads have arrived (a wave's LDS instructions run in order, so they
-      // return the round's values although the next round rewrites the rows)
+      // dB_t = sum over channels of g_t dt x, dC_t = sum over channels of dy0 h_t: a round (two
+      // steps) writes g_t and h_t of its steps as rows of a transpose; at the end of the next
+      // round lane (row, rr) takes the 16 channels of its row and state group, which arrived in
+      // the meantime (a wave's LDS instructions run in order, so they return the round's values
+      // although the next round rewrites the rows), and multiplies them by the channels' dt x or
+      // dy0 broadcast from the lanes of its own 16-lane row (that row's (sub, kind) is fixed)
       const int row = lane >> 2, rr = lane & 3;
       const int sub = row >> 3, kind = (row >> 2) & 1, qrow = row & 3;
       const float4* const src = reinterpret_cast<const float4*>(red + row * 68 + 16 * rr);
       float4 pend[4];
+      float wpend;  // lane 16 R + k: channel k's dt x (R even) or dy0 (R odd) of step t_even + R / 2
       auto add_round = [&](int t_even) {
-        const float sum = ((pend[0].x + pend[0].y) + (pend[0].z + pend[0].w)) +
-                          ((pend[1].x + pend[1].y) + (pend[1].z + pend[1].w)) +
-                          (((pend[2].x + pend[2].y) + (pend[2].z + pend[2].w)) +
-                           ((pend[3].x + pend[3].y) + (pend[3].z + pend[3].w)));
-        s_bsum[buf][s][t_even + sub][kind * N + 4 * rr + qrow] = sum;
+        s_bsum[buf][s][t_even + sub][kind * N + 4 * rr + qrow] = dot16_row_bcast(pend, wpend);
       };
       static_for<T>([&](auto K) {
         constexpr int t = T - 1 - decltype(K)::value;
@@ -329,39 +425,30 @@ __global__ __launch_bounds__(64 * kBwdRowsWaves) void scan_bwd_rows_kernel(const
         if constexpr (t % 4 == 3 && m > 0) read_batch(std::integral_constant<int, m - 1>{});
         const float2 dw = wq[m & 1][t % 4];
         const float dy0 = dq[m & 1][t % 4];
-        float gB = 0.0f, pdt = 0.0f;
-        float vb[NPL], vc[NPL];
-#pragma unroll
-        for (int q = 0; q < NPL; ++q) {
-          g[q] = fmaf(an[q], g[q], dy0 * row_bcast<t % 16>(Cv[t / 16][q]));  // g_t
-          const float a = hw_exp2(dw.x * A2[q]);                               // abar_t
-          const float ah = a * hs[t][q];                                       // abar_t h_{t-1}
-          gB = fmaf(g[q], row_bcast<t % 16>(Bv[t / 16][q]), gB);
-          const float gah = g[q] * ah;
-          pdt = fmaf(gah, Araw[q], pdt);
-          dA[q] = fmaf(gah, dw.x, dA[q]);
-          vb[q] = g[q] * dw.y;         // dB_t: g dt x
-          vc[q] = dy0 * hs[t + 1][q];  // dC_t: dy0 h_t
-          an[q] = a;
-        }
+        float gB, pdt;
+        bwd_step4<t % 16>(dw.x, dy0, A2, Araw, Bv[t / 16], Cv[t / 16], hs[t], g, an, dA, gB, pdt);
         gq[t % 4] = gB;
         pq[t % 4] = pdt;
         if constexpr (t % 4 == 0) {
           s_part[buf][1][t / 4][s][lane] = rows4_transpose_sum(gq[0], gq[1], gq[2], gq[3]);
           s_part[buf][2][t / 4][s][lane] = rows4_transpose_sum(pq[0], pq[1], pq[2], pq[3]);
         }
-        // dB / dC: row (sub, kind, q) of the transpose, sub = t % 2
+        // row (sub, kind, q) of the transpose, sub = t % 2
         asm volatile("" ::: "memory");  // after the previous round's reads
 #pragma unroll
         for (int q = 0; q < NPL; ++q) {
-          red[((t % 2) * 8 + q) * 68 + lane] = vb[q];
-          red[((t % 2) * 8 + 4 + q) * 68 + lane] = vc[q];
+          red[((t % 2) * 8 + q) * 68 + lane] = g[q];
+          red[((t % 2) * 8 + 4 + q) * 68 + lane] = hs[t + 1][q];
         }
         if constexpr (t % 2 == 0) {
-          // steps t, t + 1 written: lane (row, rr) will sum the 16 channels of state row rr
+          // steps t, t + 1 written
           if constexpr (t + 2 < T) add_round(t + 2);  // the previous round's reads have arrived
           asm volatile("" ::: "memory");
           pend[0] = src[0]; pend[1] = src[1]; pend[2] = src[2]; pend[3] = src[3];
+          const float2 dw1 = wq[m & 1][t % 4 + 1];
+          const float dy1 = dq[m & 1][t % 4 + 1];
+          const float w0 = (r & 1) ? dy0 : dw.y, w1 = (r & 1) ? dy1 : dw1.y;
+          wpend = (r & 2) ? w1 : w0;
         }
       });
       add_round(0);
