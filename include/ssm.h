@@ -410,11 +410,19 @@ SSM_API ssm_status_t ssm_state_update_ex(int64_t batch, int64_t dim, int64_t dst
  * this dstate and headdim.  segments: pieces the sequence is cut into (each
  * a whole number of 64-step chunks; 1 = none, 0 = chosen by the library:
  * enough to give every compute unit a workgroup when the batch rows and
- * heads alone cannot).  reserved must be zero. */
+ * heads alone cannot).  gram: where each chunk's C B^T (the Gram matrix the
+ * heads of a group share, "Mamba 论文精读" sec. 4.2) is computed: 1 = once
+ * per (batch row, group, chunk) by a separate pass whose tiles every head's
+ * workgroup then reads (64-channel slices only, else SSM_ERR_UNSUPPORTED),
+ * -1 = inside every head's workgroup, 0 = chosen by the library (the
+ * separate pass when at least 4 workgroups share a group's B and C and each
+ * runs at least 8 chunks).  The outputs are the same bits either way.
+ * reserved must be zero. */
 typedef struct {
   int32_t head_slice;
   int32_t segments;
-  int32_t reserved[6];
+  int32_t gram;
+  int32_t reserved[5];
 } ssm_ssd_opts_t;
 
 /*
@@ -446,7 +454,9 @@ typedef struct {
  * fp32 and is rounded to bf16 only as an operand of the chunk's read-out.
  * With a sequence split the segments' states go to the same per-(device,
  * stream) scratch as the split-sequence scan: (segments-1)*batch*nheads*
- * headdim*dstate + segments*batch*nheads fp32 (same rules as ssm_scan_fwd).
+ * headdim*dstate + segments*batch*nheads fp32 (same rules as ssm_scan_fwd);
+ * the separate C B^T pass adds batch*ngroups*ceil(seqlen/64)*3072 fp32 to it
+ * (12 KB per chunk).
  * Storage must be bf16 (SSM_F32 gives SSM_ERR_UNSUPPORTED).  dstate must be
  * 32, 64, 128 or 256 and headdim a multiple of 16; workgroups take 16-, 32-
  * or 64-channel slices of a head, dstate 128 only 32 or 64 and dstate 256

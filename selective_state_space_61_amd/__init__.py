@@ -55,7 +55,8 @@ class BwdOpts(ctypes.Structure):
 
 
 class SsdOpts(ctypes.Structure):
-    _fields_ = [("head_slice", ctypes.c_int32), ("segments", ctypes.c_int32), ("reserved", ctypes.c_int32 * 6)]
+    _fields_ = [("head_slice", ctypes.c_int32), ("segments", ctypes.c_int32), ("gram", ctypes.c_int32),
+                ("reserved", ctypes.c_int32 * 5)]
 
 
 SSM_BBAR_DELTA_B, SSM_BBAR_ZOH = 0, 1
@@ -416,12 +417,13 @@ def ssm_ssd_fwd(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, B: torch.Ten
                 dt_bias: Optional[torch.Tensor] = None, dt_softplus: bool = False, *,
                 initial_state: Optional[torch.Tensor] = None,
                 y: Optional[torch.Tensor] = None, final_state: Optional[torch.Tensor] = None,
-                return_final_state: bool = True, head_slice: int = 0, segments: int = 0,
+                return_final_state: bool = True, head_slice: int = 0, segments: int = 0, gram: int = 0,
                 stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Mamba-2 SSD layer forward (include/ssm.h: ssm_ssd_fwd).  x, z: (batch, seqlen, nheads,
     headdim) bf16; dt: (batch, seqlen, nheads) bf16; B, C: (batch, seqlen, ngroups, dstate) bf16;
-    A, D, dt_bias: (nheads,) fp32.  Returns (y, final_state (batch, nheads, headdim, dstate) fp32
-    or None)."""
+    A, D, dt_bias: (nheads,) fp32.  gram: 1 computes each chunk's C B^T once per (batch row, group)
+    in a separate pass, -1 inside every head's workgroup, 0 lets the library choose.  Returns (y,
+    final_state (batch, nheads, headdim, dstate) fp32 or None)."""
     lib = load_library()
     if x.dim() != 4 or B.dim() != 4:
         raise ValueError("x must be (batch, seqlen, nheads, headdim) and B (batch, seqlen, ngroups, dstate)")
@@ -443,7 +445,7 @@ def ssm_ssd_fwd(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, B: torch.Ten
     if final_state is None and return_final_state:
         final_state = torch.empty((batch, nheads, headdim, dstate), dtype=torch.float32, device=dev)
     _need(final_state, "final_state", (batch, nheads, headdim, dstate), torch.float32, dev, optional=True)
-    opts = SsdOpts(head_slice=int(head_slice), segments=int(segments))
+    opts = SsdOpts(head_slice=int(head_slice), segments=int(segments), gram=int(gram))
     status = lib.ssm_ssd_fwd(batch, seqlen, nheads, headdim, dstate, ngroups, code, _ptr(x), _ptr(dt), _ptr(A),
                              _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(dt_bias), int(bool(dt_softplus)),
                              _ptr(initial_state), _ptr(y), _ptr(final_state), _stream(dev, stream), ctypes.byref(opts))

@@ -41,12 +41,13 @@
 // rows k0..k0+3 of column c(i/4) + i%4: four consecutive K values of one M/N index, from any four
 // 4-column groups.  Two such reads make a K = 32 fragment.
 //
-// The S tiles (16 dstate rows x 16 channels each, tile nb = dstate 16 nb .. +15) hand each lane
-// four CONSECUTIVE rows of one column.  Two tiles 2ks, 2ks+1 give lane l the dstate indices
-// 32 ks + 4q .. +3 and 32 ks + 16 + 4q .. +3: the eight k values a K = 32 step asks of lane l up
-// to a fixed permutation of k.  A product is unchanged when both operands use the same
-// permutation, so the accumulators pack straight into the A operand of the read-out, and C is read
-// in that order (two 8-byte halves per fragment).
+// The S tiles (16 dstate rows x 16 channels each) interleave the dstate index in pairs: row
+// 4j + r of tile nb is dstate 32 (nb / 2) + 8 j + 4 (nb % 2) + r.  A lane holds rows 4q .. 4q+3
+// of a tile, so tiles 2ks and 2ks+1 give lane l the eight consecutive dstate indices
+// 32 ks + 8q .. +7: exactly the K values a K = 32 step asks of lane l.  The accumulators pack
+// straight into the A operand of the read-out, C is read with one 16-byte load per fragment, and
+// the state update's transposing reads of B address those rows (column group 8 (s % 4) + 4 (nb % 2)
+// of the 32-column block for source lane s).
 #pragma once
 
 #include "ssm_device.hpp"
@@ -69,6 +70,9 @@ struct SsdArgs {
                           // [s-1], or NULL (every segment starts from zero)
   float* seg_state;       // same layout: end state of segment s from zero at [s] (state-only pass)
   float* seg_dsum;        // (nseg, batch, nheads): sum over segment s of dt A log2(e) (state-only pass)
+  const float* gram;      // (batch, ngroups, chunks, 12, 64, 4): the tiles of C B^T per chunk, as
+                          // ssd_gram_kernel leaves them (the precomputed-Gram outputs pass), or NULL
+  float* gram_out;        // the same buffer, written by ssd_gram_kernel
   int64_t batch;
   int64_t seqlen;
   int32_t nheads;
@@ -84,6 +88,7 @@ struct SsdArgs {
 
 constexpr int kSsdOutputs = 0;    // full chunk work: y, and the final state from the last segment
 constexpr int kSsdStateOnly = 1;  // state update only: the segment's end state and summed decay
+constexpr int kSsdOutputsGram = 2;  // kSsdOutputs with the tiles of C B^T read from SsdArgs::gram
 
 constexpr int kSsdChunk = 64;  // steps per chunk: one per lane of a wave
 
@@ -112,13 +117,6 @@ __device__ __forceinline__ ssd_u32x2_t lds_read_tr(const uint16_t* p) {
 __device__ __forceinline__ ssd_u32x4_t lds_frag_tr(const uint16_t* tile, int ld, int k0, int q, int s16, int col) {
   const uint16_t* ptr = tile + (k0 + 8 * q + s16 / 4) * ld + col;
   const ssd_u32x2_t lo = lds_read_tr(ptr), hi = lds_read_tr(ptr + 4 * ld);
-  return ssd_u32x4_t{lo.x, lo.y, hi.x, hi.y};
-}
-
-// Two 8-byte halves k0..k0+3 and k0+16..k0+19 of a bf16 row: the permuted K = 32 fragment.
-__device__ __forceinline__ ssd_u32x4_t load_perm_frag(const uint16_t* row_k0) {
-  const ssd_u32x2_t lo = *reinterpret_cast<const ssd_u32x2_t*>(row_k0);
-  const ssd_u32x2_t hi = *reinterpret_cast<const ssd_u32x2_t*>(row_k0 + 16);
   return ssd_u32x4_t{lo.x, lo.y, hi.x, hi.y};
 }
 
@@ -151,6 +149,30 @@ __device__ __forceinline__ float wave_inclusive_sum(float v) {
 __device__ __forceinline__ int gram_tile_i(int k) { return k < 4 ? k / 2 : k / 4 + 1; }
 __device__ __forceinline__ int gram_tile_j(int k) { return k < 4 ? k % 2 : k % 4; }
 
+// The three 16 x 16 tiles of G^T = B C^T (over dstate) that wave w of four computes, from the
+// chunk's B and C rows in LDS (row stride N + 8): (w / 2, w % 2), (2, w) and (3, w) in (i-block,
+// j-block) terms, i.e. tiles k = w, w + 4, w + 8.  The last two share their B rows, and for w < 2
+// the first does too, so a K step reads 4 or 5 fragments instead of 6.  gt must hold zeros.
+template <int N>
+__device__ __forceinline__ void gram_tiles_nw4(const uint16_t* s_b, const uint16_t* s_c, int wave, int l16, int q,
+                                               ssd_f32x4_t* gt) {
+  constexpr int LDB = N + 8, NKS = N / 32;
+  const bool b0_shared = wave < 2;
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) {
+    const int col = 32 * ks + 8 * q;
+    const ssd_u32x4_t bw = *reinterpret_cast<const ssd_u32x4_t*>(&s_b[(16 * wave + l16) * LDB + col]);
+    const ssd_u32x4_t c2 = *reinterpret_cast<const ssd_u32x4_t*>(&s_c[(32 + l16) * LDB + col]);
+    const ssd_u32x4_t c3 = *reinterpret_cast<const ssd_u32x4_t*>(&s_c[(48 + l16) * LDB + col]);
+    const ssd_u32x4_t c0 = *reinterpret_cast<const ssd_u32x4_t*>(&s_c[(16 * (wave >> 1) + l16) * LDB + col]);
+    const ssd_u32x4_t b0 =
+        b0_shared ? bw : *reinterpret_cast<const ssd_u32x4_t*>(&s_b[(16 * (wave & 1) + l16) * LDB + col]);
+    gt[0] = mfma16x16x32(b0, c0, gt[0]);
+    gt[1] = mfma16x16x32(bw, c2, gt[1]);
+    gt[2] = mfma16x16x32(bw, c3, gt[2]);
+  }
+}
+
 // Workgroups of 4 waves (dstate <= 128) keep two workgroups per compute unit: their LDS fits
 // twice in 160 KB and the registers are held to 256 per lane.
 template <int N, int NW>
@@ -159,7 +181,8 @@ constexpr int kSsdWavesPerEu = (NW == 4 && N <= 128) ? 2 : 1;
 template <int N, int NW, int MODE>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(kSsdWavesPerEu<N, NW>)))
 void ssd_chunk_kernel(const SsdArgs p) {
-  constexpr bool OUT = MODE == kSsdOutputs;
+  constexpr bool OUT = MODE != kSsdStateOnly;
+  constexpr bool PRE = MODE == kSsdOutputsGram;  // C B^T tiles from the buffer, not computed here
   constexpr int Q = kSsdChunk;
   constexpr int PS = 16 * NW;         // head channels per workgroup
   constexpr int T = 64 * NW;          // threads
@@ -175,6 +198,7 @@ void ssd_chunk_kernel(const SsdArgs p) {
   constexpr int kTiles = 12 / NW;     // tiles of C B^T per wave
   static_assert(N % 32 == 0 && (8 * N) % T == 0, "dstate is a multiple of 32");
   static_assert(kXPer == 2, "two 16-byte pieces of X per thread");
+  static_assert(!PRE || NW == 4, "the precomputed C B^T tiles are laid out for four waves");
 
   __shared__ __align__(16) uint16_t s_b[Q * LDB];   // B[j][n]
   __shared__ __align__(16) uint16_t s_c[Q * LDB];   // C[i][n]
@@ -330,8 +354,10 @@ void ssd_chunk_kernel(const SsdArgs p) {
     }
   };
 
-  // S tile nb, lane (q, r): dstate index 16 nb + 4q + r of channel pw (the final-state layout)
-  const int64_t state_off = ((b * H + h) * P + p0 + pw) * N + 4 * q;
+  // S tile nb, lane (q, r): dstate index 32 (nb / 2) + 8q + 4 (nb % 2) + r of channel pw (the
+  // final-state layout), at state_off + toff(nb) + r
+  const int64_t state_off = ((b * H + h) * P + p0 + pw) * N + 8 * q;
+  auto toff = [](int nb) { return 32 * (nb >> 1) + 4 * (nb & 1); };
   const int64_t state_seg = nbh * P * N;  // elements per segment in the segment buffers
   ssd_f32x4_t S[NT];
   // the entering state: the carried one for a later segment, the caller's for the first (the
@@ -341,14 +367,14 @@ void ssd_chunk_kernel(const SsdArgs p) {
     // (zero without one), S <- e^{sum dt A of segment r} S + S_end(r) for r = 0 .. seg-1
 #pragma unroll
     for (int nb = 0; nb < NT; ++nb)
-      S[nb] = p.init_state ? *reinterpret_cast<const ssd_f32x4_t*>(p.init_state + state_off + 16 * nb)
+      S[nb] = p.init_state ? *reinterpret_cast<const ssd_f32x4_t*>(p.init_state + state_off + toff(nb))
                            : ssd_f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
     for (int r = 0; r < seg; ++r) {
       const float decay = hw_exp2(p.seg_dsum[r * nbh + bh]);
       const float* sr = p.seg_state + r * state_seg + state_off;
 #pragma unroll
       for (int nb = 0; nb < NT; ++nb) {
-        const ssd_f32x4_t e = *reinterpret_cast<const ssd_f32x4_t*>(sr + 16 * nb);
+        const ssd_f32x4_t e = *reinterpret_cast<const ssd_f32x4_t*>(sr + toff(nb));
 #pragma unroll
         for (int i = 0; i < 4; ++i) S[nb][i] = fmaf(decay, S[nb][i], e[i]);
       }
@@ -359,7 +385,7 @@ void ssd_chunk_kernel(const SsdArgs p) {
                                                           : nullptr;
     if (si) {
 #pragma unroll
-      for (int nb = 0; nb < NT; ++nb) S[nb] = *reinterpret_cast<const ssd_f32x4_t*>(si + 16 * nb);
+      for (int nb = 0; nb < NT; ++nb) S[nb] = *reinterpret_cast<const ssd_f32x4_t*>(si + toff(nb));
     } else {
 #pragma unroll
       for (int nb = 0; nb < NT; ++nb) S[nb] = ssd_f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
@@ -379,6 +405,14 @@ void ssd_chunk_kernel(const SsdArgs p) {
   auto chunk = [&](int64_t c, auto SET) {
     using Prev = std::integral_constant<int, 1 - decltype(SET)::value>;
     const int64_t t0 = c * Q;
+    // this wave's three tiles of C B^T (k = wave, wave + 4, wave + 8), issued here so that they
+    // arrive during the epilogue and the staging
+    ssd_f32x4_t gpre[3];
+    if constexpr (PRE) {
+      const float* gsrc = p.gram + (((b * G + g) * nch + c) * 12 + wave) * 256 + 4 * lane;
+#pragma unroll
+      for (int s = 0; s < 3; ++s) gpre[s] = *reinterpret_cast<const ssd_f32x4_t*>(gsrc + 4 * 256 * s);
+    }
     __syncthreads();  // every wave is done with the previous chunk's tiles
     if (OUT && c > cbeg) epilogue(t0 - Q, Full{}, Prev{});  // the chunk before this one is whole
     stage_chunk(t0, SET);
@@ -394,23 +428,11 @@ void ssd_chunk_kernel(const SsdArgs p) {
         ssd_f32x4_t gt[kTiles];
 #pragma unroll
         for (int s = 0; s < kTiles; ++s) gt[s] = ssd_f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-        if constexpr (NW == 4) {
-          // wave w's tiles are (w / 2, w % 2), (2, w) and (3, w): the last two share their B rows,
-          // and for w < 2 the first does too, so a K step reads 4 or 5 fragments instead of 6
-          const bool b0_shared = wave < 2;
+        if constexpr (PRE) {
 #pragma unroll
-          for (int ks = 0; ks < NKS; ++ks) {
-            const int col = 32 * ks + 8 * q;
-            const ssd_u32x4_t bw = *reinterpret_cast<const ssd_u32x4_t*>(&s_b[(16 * wave + l16) * LDB + col]);
-            const ssd_u32x4_t c2 = *reinterpret_cast<const ssd_u32x4_t*>(&s_c[(32 + l16) * LDB + col]);
-            const ssd_u32x4_t c3 = *reinterpret_cast<const ssd_u32x4_t*>(&s_c[(48 + l16) * LDB + col]);
-            const ssd_u32x4_t c0 = *reinterpret_cast<const ssd_u32x4_t*>(&s_c[(16 * (wave >> 1) + l16) * LDB + col]);
-            const ssd_u32x4_t b0 =
-                b0_shared ? bw : *reinterpret_cast<const ssd_u32x4_t*>(&s_b[(16 * (wave & 1) + l16) * LDB + col]);
-            gt[0] = mfma16x16x32(b0, c0, gt[0]);
-            gt[1] = mfma16x16x32(bw, c2, gt[1]);
-            gt[2] = mfma16x16x32(bw, c3, gt[2]);
-          }
+          for (int s = 0; s < kTiles; ++s) gt[s] = gpre[s];
+        } else if constexpr (NW == 4) {
+          gram_tiles_nw4<N>(s_b, s_c, wave, l16, q, gt);
         } else {
 #pragma unroll
           for (int ks = 0; ks < NKS; ++ks)
@@ -459,7 +481,8 @@ void ssd_chunk_kernel(const SsdArgs p) {
       for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
         for (int ib = 0; ib < 4; ++ib)
-          acc[ib] = mfma16x16x32(sf[ks], load_perm_frag(&s_c[(16 * ib + l16) * LDB + 32 * ks + 4 * q]), acc[ib]);
+          acc[ib] = mfma16x16x32(sf[ks], *reinterpret_cast<const ssd_u32x4_t*>(&s_c[(16 * ib + l16) * LDB + 32 * ks + 8 * q]),
+                                 acc[ib]);
 #pragma unroll
       for (int ib = 0; ib < 4; ++ib) acc[ib] *= hw_exp2(s_cum[16 * ib + l16]);
 #pragma unroll
@@ -475,8 +498,9 @@ void ssd_chunk_kernel(const SsdArgs p) {
       for (int ib = 0; ib < 4; ++ib) *reinterpret_cast<ssd_f32x4_t*>(&s_y[(16 * ib + l16) * LDY + pe]) = acc[ib];
     }
 
-    // state update: S = exp(cum_last) S + B^T (weighted X); the B^T operand of tile nb is rows
-    // 16 nb .. +15 of B^T, read transposed from B (this lane addresses column 16 nb + 4 (l16 % 4))
+    // state update: S = exp(cum_last) S + B^T (weighted X); the B^T operand of tile nb is its 16
+    // dstate rows of B^T, read transposed from B (this lane addresses column
+    // 32 (nb / 2) + 8 (l16 % 4) + 4 (nb % 2))
     const float decay = hw_exp2(s_cum[Q - 1]);
 #pragma unroll
     for (int nb = 0; nb < NT; ++nb) S[nb] *= decay;
@@ -485,7 +509,8 @@ void ssd_chunk_kernel(const SsdArgs p) {
       const ssd_u32x4_t xw = lds_frag_tr(s_xw, LDX, 32 * ks, q, l16, cx);  // weighted X[32 ks + 8q ..][pw]
 #pragma unroll
       for (int nb = 0; nb < NT; ++nb)
-        S[nb] = mfma16x16x32(lds_frag_tr(s_b, LDB, 32 * ks, q, l16, 16 * nb + 4 * (l16 & 3)), xw, S[nb]);
+        S[nb] = mfma16x16x32(lds_frag_tr(s_b, LDB, 32 * ks, q, l16, 32 * (nb >> 1) + 8 * (l16 & 3) + 4 * (nb & 1)),
+                             xw, S[nb]);
     }
     publish_dt();
   };
@@ -503,7 +528,7 @@ void ssd_chunk_kernel(const SsdArgs p) {
   if constexpr (!OUT) {
     float* so = p.seg_state + seg * state_seg + state_off;
 #pragma unroll
-    for (int nb = 0; nb < NT; ++nb) *reinterpret_cast<ssd_f32x4_t*>(so + 16 * nb) = S[nb];
+    for (int nb = 0; nb < NT; ++nb) *reinterpret_cast<ssd_f32x4_t*>(so + toff(nb)) = S[nb];
     if (slice == 0 && tid == 0) p.seg_dsum[seg * nbh + bh] = dsum;
     return;
   }
@@ -511,8 +536,58 @@ void ssd_chunk_kernel(const SsdArgs p) {
   if (p.final_state && seg == p.nseg - 1) {
     float* fs = p.final_state + state_off;
 #pragma unroll
-    for (int nb = 0; nb < NT; ++nb) *reinterpret_cast<ssd_f32x4_t*>(fs + 16 * nb) = S[nb];
+    for (int nb = 0; nb < NT; ++nb) *reinterpret_cast<ssd_f32x4_t*>(fs + toff(nb)) = S[nb];
   }
+}
+
+// The tiles of C B^T of one 64-step chunk of one (batch row, group), computed once for every head
+// of the group and every slice of its channels (the twelve tiles gram_tile_i / gram_tile_j name,
+// "Mamba 论文精读" sec. 4.2: the heads of a group share B and C).  Workgroup (b, g, c) of 4
+// waves stages the chunk's B and C rows as the chunk kernel does (steps past the sequence take the
+// last step's rows) and runs the same product, gram_tiles_nw4, so each tile holds the bits the
+// chunk kernel would compute; tile k goes to gram[((b G + g) nch + c) 12 + k] as 64 lanes x 4 fp32
+// in the product's output layout.
+template <int N>
+__global__ __launch_bounds__(256) void ssd_gram_kernel(const SsdArgs p) {
+  constexpr int Q = kSsdChunk, LDB = N + 8, T = 256, kBCPer = 8 * N / T;
+  static_assert(N % 32 == 0 && (8 * N) % T == 0, "dstate is a multiple of 32");
+  __shared__ __align__(16) uint16_t s_b[Q * LDB];
+  __shared__ __align__(16) uint16_t s_c[Q * LDB];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, q = lane >> 4;
+  const int64_t L = p.seqlen, G = p.ngroups;
+  const int64_t nch = (L + Q - 1) / Q;
+  const int64_t blk = blockIdx.x;  // (batch row, group, chunk)
+  const int64_t c = blk % nch, bg_i = blk / nch;
+  const int64_t g = bg_i % G, b = bg_i / G;
+  const uint16_t* bg = p.B + (b * L * G + g) * N;
+  const uint16_t* cg = p.C + (b * L * G + g) * N;
+  const int64_t bs = G * N, t0 = c * Q;
+  ssd_u32x4_t rb[kBCPer], rc[kBCPer];
+#pragma unroll
+  for (int u = 0; u < kBCPer; ++u) {
+    const int k = tid + u * T;
+    const int c8 = k % (N / 8), j = k / (N / 8);
+    const int64_t t = t0 + j < L ? t0 + j : L - 1;
+    rb[u] = *reinterpret_cast<const ssd_u32x4_t*>(bg + t * bs + 8 * c8);
+    rc[u] = *reinterpret_cast<const ssd_u32x4_t*>(cg + t * bs + 8 * c8);
+  }
+#pragma unroll
+  for (int u = 0; u < kBCPer; ++u) {
+    const int k = tid + u * T;
+    const int c8 = k % (N / 8), j = k / (N / 8);
+    *reinterpret_cast<ssd_u32x4_t*>(&s_b[j * LDB + 8 * c8]) = rb[u];
+    *reinterpret_cast<ssd_u32x4_t*>(&s_c[j * LDB + 8 * c8]) = rc[u];
+  }
+  __syncthreads();
+  ssd_f32x4_t gt[3];
+#pragma unroll
+  for (int s = 0; s < 3; ++s) gt[s] = ssd_f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  gram_tiles_nw4<N>(s_b, s_c, wave, l16, q, gt);
+  float* dst = p.gram_out + (blk * 12 + wave) * 256 + 4 * lane;
+#pragma unroll
+  for (int s = 0; s < 3; ++s) *reinterpret_cast<ssd_f32x4_t*>(dst + 4 * 256 * s) = gt[s];
 }
 
 // Composes the segment states in order, one thread per (batch row, head, channel, dstate index):
@@ -608,6 +683,9 @@ using SsdUpdateKernel = void (*)(const SsdUpdateArgs);
 SsdUpdateKernel ssd_update_kernel(int64_t dstate);
 
 using SsdKernel = void (*)(const SsdArgs);
+// The C B^T tile kernel for dstate (256 threads per workgroup, one workgroup per (batch row,
+// group, chunk)), or NULL when dstate is not instantiated.
+SsdKernel ssd_gram_kernel_for(int64_t dstate);
 // The chunk kernel for (dstate, waves per workgroup, MODE), or NULL when that pair is not
 // instantiated.
 SsdKernel ssd_kernel(int64_t dstate, int waves, int mode);

@@ -969,12 +969,14 @@ ssm_status_t ssm_ssd_fwd(int64_t batch, int64_t seqlen, int64_t nheads, int64_t 
   if (dstate != 32 && dstate != 64 && dstate != 128 && dstate != 256)
     return fail(SSM_ERR_UNSUPPORTED, "dstate %lld not in {32, 64, 128, 256}", (long long)dstate);
   if (headdim % 16 != 0) return fail(SSM_ERR_UNSUPPORTED, "headdim %lld is not a multiple of 16", (long long)headdim);
-  int slice = 0, segments = 0;
+  int slice = 0, segments = 0, gram = 0;
   if (opts) {
     for (int r : opts->reserved)
       if (r != 0) return fail(SSM_ERR_INVALID_ARG, "reserved option fields must be zero");
     slice = opts->head_slice;
     segments = opts->segments;
+    gram = opts->gram;
+    if (gram < -1 || gram > 1) return fail(SSM_ERR_INVALID_ARG, "gram %d not in {-1, 0, 1}", gram);
     if (segments < 0) return fail(SSM_ERR_INVALID_ARG, "segments %d is negative", segments);
     if (slice != 0 && slice != 16 && slice != 32 && slice != 64)
       return fail(SSM_ERR_INVALID_ARG, "head_slice %d not in {0, 16, 32, 64}", slice);
@@ -1021,8 +1023,8 @@ ssm_status_t ssm_ssd_fwd(int64_t batch, int64_t seqlen, int64_t nheads, int64_t 
       }
     }
   }
-  const ssm::SsdKernel k = ssm::ssd_kernel(dstate, waves, ssm::kSsdOutputs);
-  if (!k)
+  const ssm::SsdKernel k0 = ssm::ssd_kernel(dstate, waves, ssm::kSsdOutputs);
+  if (!k0)
     return fail(SSM_ERR_UNSUPPORTED,
                 "no SSD kernel for dstate %lld with headdim %lld (head_slice %d): dstate 256 takes 64-channel "
                 "slices, 128 takes 32 or 64",
@@ -1056,19 +1058,47 @@ ssm_status_t ssm_ssd_fwd(int64_t batch, int64_t seqlen, int64_t nheads, int64_t 
   if (nch > 0) nseg = (nch + seg_chunks - 1) / seg_chunks;  // no empty segment
   a.nseg = static_cast<int32_t>(nseg);
   a.seg_chunks = static_cast<int32_t>(seg_chunks > 0 ? seg_chunks : 1);
-  int64_t grid = blocks;
-  if (nseg > 1) {
-    // scratch: (nseg-1) segment states of batch*nheads*headdim*dstate fp32, then nseg*batch*nheads sums
-    int64_t per_seg, n_state, n_total, g1;
-    if (!mul_ok(nbh, headdim * dstate, &per_seg) || !mul_ok(per_seg, nseg - 1, &n_state) ||
-        __builtin_add_overflow(n_state, nseg * nbh, &n_total) || !mul_ok(blocks, nseg, &grid) || grid > 0x7fffffff ||
-        !mul_ok(blocks, nseg - 1, &g1))
-      return fail(SSM_ERR_UNSUPPORTED, "sequence split too large");
-    float* scratch = nullptr;
-    ssm_status_t s = get_scratch(st, n_total, &scratch);
+  // The Gram matrix C B^T of a chunk is the same for every head of a group and every slice of a
+  // head: with 4-wave workgroups (the tiles' layout), at least kSsdGramShare workgroups per (batch
+  // row, group) and at least kSsdGramChunks chunks per workgroup, a separate pass computes each
+  // chunk's tiles once and the chunk kernels read them (the same bits as computing them in place).
+  // Measured on MI355X (64 heads x 64 channels, dstate 128): 8 x 2048 steps 142 us against 153;
+  // 1 x 1024 steps in 4 segments of 4 chunks 33.8 us against 32.6 (the pass's ~5 us is not
+  // repaid by 4 chunks).
+  constexpr int64_t kSsdGramShare = 4, kSsdGramChunks = 8;
+  const int64_t share = (nheads / ngroups) * nslices;
+  if (gram == 1 && waves != 4)
+    return fail(SSM_ERR_UNSUPPORTED, "the separate C B^T pass needs 64-channel slices (head_slice %d)", 16 * waves);
+  const bool use_gram = nch > 0 && waves == 4 &&
+                        (gram == 1 || (gram == 0 && share >= kSsdGramShare && seg_chunks >= kSsdGramChunks));
+  int64_t n_gram = 0, g_gram = 0;
+  if (use_gram && (!mul_ok(batch * ngroups, nch, &g_gram) || g_gram > 0x7fffffff || !mul_ok(g_gram, 3072, &n_gram)))
+    return fail(SSM_ERR_UNSUPPORTED, "C B^T buffer too large");
+  // scratch: the C B^T tiles (n_gram fp32, a multiple of 4), then with a sequence split (nseg-1)
+  // segment states of batch*nheads*headdim*dstate fp32 and nseg*batch*nheads sums
+  int64_t per_seg = 0, n_state = 0, n_seg = 0, g1 = 0, grid = blocks;
+  if (nseg > 1 && (!mul_ok(nbh, headdim * dstate, &per_seg) || !mul_ok(per_seg, nseg - 1, &n_state) ||
+                   __builtin_add_overflow(n_state, nseg * nbh, &n_seg) || !mul_ok(blocks, nseg, &grid) ||
+                   grid > 0x7fffffff || !mul_ok(blocks, nseg - 1, &g1)))
+    return fail(SSM_ERR_UNSUPPORTED, "sequence split too large");
+  float* scratch = nullptr;
+  if (n_gram + n_seg > 0) {
+    ssm_status_t s = get_scratch(st, n_gram + n_seg, &scratch);
     if (s != SSM_OK) return s;
-    a.seg_state = scratch;
-    a.seg_dsum = scratch + n_state;
+  }
+  if (use_gram) {
+    const ssm::SsdKernel kg = ssm::ssd_gram_kernel_for(dstate);
+    if (!kg) return fail(SSM_ERR_UNSUPPORTED, "no C B^T kernel for dstate %lld", (long long)dstate);
+    a.gram = scratch;
+    a.gram_out = scratch;
+    hipLaunchKernelGGL(kg, dim3(static_cast<unsigned>(g_gram)), dim3(256), 0, st, a);
+    ssm_status_t s = check_launch("SSD C B^T tiles");
+    if (s != SSM_OK) return s;
+  }
+  if (nseg > 1) {
+    a.seg_state = scratch + n_gram;
+    a.seg_dsum = scratch + n_gram + n_state;
+    ssm_status_t s;
     hipLaunchKernelGGL(ssm::ssd_kernel(dstate, waves, ssm::kSsdStateOnly), dim3(static_cast<unsigned>(g1)),
                        dim3(64 * waves), 0, st, a);
     if ((s = check_launch("SSD segment states")) != SSM_OK) return s;
@@ -1084,6 +1114,8 @@ ssm_status_t ssm_ssd_fwd(int64_t batch, int64_t seqlen, int64_t nheads, int64_t 
       a.seg_init = a.seg_state;
     }
   }
+  const ssm::SsdKernel k = use_gram ? ssm::ssd_kernel(dstate, waves, ssm::kSsdOutputsGram) : k0;
+  if (!k) return fail(SSM_ERR_UNSUPPORTED, "no SSD kernel for dstate %lld with read C B^T tiles", (long long)dstate);
   hipLaunchKernelGGL(k, dim3(static_cast<unsigned>(grid)), dim3(64 * waves), 0, st, a);
   return check_launch("SSD chunk kernel");
 }

@@ -249,8 +249,8 @@ def ssd(lib, batch=2, seqlen=8, nheads=4, headdim=64, dstate=128, ngroups=2, dty
                            y, fin, None, opts)
 
 
-def ssd_opts(slice_=0, reserved=0, segments=0):
-    o = ssm.SsdOpts(head_slice=slice_, segments=segments)
+def ssd_opts(slice_=0, reserved=0, segments=0, gram=0):
+    o = ssm.SsdOpts(head_slice=slice_, segments=segments, gram=gram)
     o.reserved[3] = reserved
     return ctypes.byref(o)
 
@@ -269,6 +269,9 @@ def ssd_opts(slice_=0, reserved=0, segments=0):
     (dict(init=fake(10, 8)), MISALIGNED), (dict(init=fake(9)), INVALID), (dict(init=fake(8)), INVALID),
     (dict(opts=ssd_opts(8)), INVALID), (dict(opts=ssd_opts(48)), INVALID), (dict(headdim=32, opts=ssd_opts(64)), INVALID),
     (dict(opts=ssd_opts(0, reserved=1)), INVALID), (dict(opts=ssd_opts(0, segments=-2)), INVALID),
+    (dict(opts=ssd_opts(0, gram=2)), INVALID), (dict(opts=ssd_opts(0, gram=-2)), INVALID),
+    # the separate C B^T pass lays its tiles out for 64-channel slices
+    (dict(opts=ssd_opts(32, gram=1)), UNSUPPORTED),
     # instantiated (dstate, waves) pairs: one wave only up to dstate 64, two up to 128
     (dict(opts=ssd_opts(16)), UNSUPPORTED), (dict(dstate=256, opts=ssd_opts(32)), UNSUPPORTED),
     (dict(dstate=256, headdim=32), UNSUPPORTED), (dict(dstate=128, headdim=16), UNSUPPORTED)])

@@ -132,6 +132,37 @@ def test_full_b8_every_element(o):
     compare(o, W.ssd_workload_inputs(w), "mamba2_layer_b8 (8, 2048, 64 x 64, N 128)", nthreads=16)
 
 
+@pytest.mark.parametrize("shape,segments", [((2, 150, 4, 64, 128, 1), 1), ((2, 333, 8, 64, 64, 2), 3),
+                                            ((1, 65, 4, 64, 256, 1), 1), ((3, 200, 6, 64, 32, 3), 12),
+                                            ((1, 1, 4, 64, 128, 1), 1), ((2, 130, 2, 128, 128, 1), 2)])
+def test_gram_pass_bitwise(o, shape, segments):
+    """C B^T computed once per (batch row, group, chunk) by the separate pass and read by every
+    head's workgroup: against the oracle, and the same bits as computing it in each workgroup
+    (ragged tails, several groups, two slices per head, split sequences, carried segments)."""
+    batch, L, H, P, N, G = shape
+    t = W.ssd_inputs(batch, L, H, P, N, G, seed=7 * L + N + segments)
+    y1, f1 = compare(o, t, f"ssd separate C B^T pass {shape} segments={segments}", gram=1, segments=segments)
+    y0, f0 = ssd_gpu(t, gram=-1, segments=segments)
+    assert torch.equal(y1, y0), "y differs between the separate C B^T pass and the in-workgroup product"
+    assert torch.equal(f1, f0), "final_state differs between the two C B^T paths"
+
+
+def test_gram_pass_initial_state(o):
+    """The separate pass with an entering state and a resumed sequence: the same bits as the
+    in-workgroup product."""
+    import selective_state_space_61_amd as ssm
+    t = W.ssd_inputs(2, 200, 8, 64, 128, 1, seed=41)
+    d = {k: to_dev(v) for k, v in t.items()}
+    init = torch.randn((2, 8, 64, 128), device="cuda", dtype=torch.float32) * 0.5
+    out = []
+    for gram in (1, -1):
+        y, fin = ssm.ssm_ssd_fwd(d["x"], d["dt"], d["A"], d["B"], d["C"], D=d["D"], z=d["z"], dt_bias=d["dt_bias"],
+                                 dt_softplus=True, initial_state=init, gram=gram, segments=3)
+        out.append((y, fin))
+    torch.cuda.synchronize()
+    assert torch.equal(out[0][0], out[1][0]) and torch.equal(out[0][1], out[1][1])
+
+
 def _cut(t, lo, hi):
     return {k: (np.ascontiguousarray(v[:, lo:hi]) if k in ("x", "dt", "B", "C", "z") and v is not None else v)
             for k, v in t.items()}
