@@ -120,6 +120,36 @@ __device__ __forceinline__ ssd_u32x4_t lds_frag_tr(const uint16_t* tile, int ld,
   return ssd_u32x4_t{lo.x, lo.y, hi.x, hi.y};
 }
 
+// The chunk's B rows in LDS.  The state update reads them transposed (ds_read_b64_tr_b16: 16 lanes
+// address rows k0 .. k0+3 at four column groups 8 elements apart), which with rows padded to
+// N + 8 elements puts up to four lanes on one bank.  With SWZ a row is stored unpadded, its
+// 16-byte pieces permuted by the row: piece p of row j sits at p ^ h(j), h(j) = 4 (j % 4) +
+// (j / 4) % 4.  Then those reads hit each bank at most twice (the least for 8-byte reads of one
+// half of each piece), the staging stores meet no conflict, and the tile is 2 KB smaller.  The
+// chunk kernel takes it from dstate 128 when it does not compute C B^T itself (whose register
+// budget the swizzled addressing of its B reads would exceed).
+template <int N, bool SWZ>
+struct SsdBLayout {
+  static constexpr bool kSwizzle = SWZ && N >= 128;
+  static constexpr int LD = kSwizzle ? N : N + 8;  // row stride (elements)
+  // element offset of (row, col); col % 8 is kept, so 8- and 16-byte accesses stay in one piece
+  __device__ static __forceinline__ int off(int row, int col) {
+    if constexpr (kSwizzle)
+      return row * LD + 8 * ((col >> 3) ^ (((row & 3) << 2) | ((row >> 2) & 3))) + (col & 7);
+    else
+      return row * LD + col;
+  }
+};
+
+// lds_frag_tr for the B tile in its SsdBLayout BL.
+template <class BL>
+__device__ __forceinline__ ssd_u32x4_t lds_frag_tr_b(const uint16_t* s_b, int k0, int q, int s16, int col) {
+  const int r = k0 + 8 * q + s16 / 4;
+  const ssd_u32x2_t lo = lds_read_tr(s_b + BL::off(r, col));
+  const ssd_u32x2_t hi = lds_read_tr(s_b + BL::off(r + 4, col));
+  return ssd_u32x4_t{lo.x, lo.y, hi.x, hi.y};
+}
+
 template <int E>
 __device__ __forceinline__ float bf16_elem(ssd_u32x4_t v) {
   return (E & 1) ? bf16_hi(v[E / 2]) : bf16_lo(v[E / 2]);
@@ -149,24 +179,24 @@ __device__ __forceinline__ float wave_inclusive_sum(float v) {
 __device__ __forceinline__ int gram_tile_i(int k) { return k < 4 ? k / 2 : k / 4 + 1; }
 __device__ __forceinline__ int gram_tile_j(int k) { return k < 4 ? k % 2 : k % 4; }
 
-// The three 16 x 16 tiles of G^T = B C^T (over dstate) that wave w of four computes, from the
-// chunk's B and C rows in LDS (row stride N + 8): (w / 2, w % 2), (2, w) and (3, w) in (i-block,
-// j-block) terms, i.e. tiles k = w, w + 4, w + 8.  The last two share their B rows, and for w < 2
-// the first does too, so a K step reads 4 or 5 fragments instead of 6.  gt must hold zeros.
-template <int N>
-__device__ __forceinline__ void gram_tiles_nw4(const uint16_t* s_b, const uint16_t* s_c, int wave, int l16, int q,
+// The three 16 x 16 tiles of G^T = B C^T (over dstate) that wave w of four computes:
+// (w / 2, w % 2), (2, w) and (3, w) in (i-block, j-block) terms, i.e. tiles k = w, w + 4, w + 8.
+// The last two share their B rows, and for w < 2 the first does too, so a K step reads 4 or 5
+// fragments instead of 6.  frag_b(r, col) / frag_c(r, col) return 16 bytes (8 bf16) of row r of the
+// chunk's B / C at dstate column col, wherever the caller keeps them.  gt must hold zeros.
+template <int N, class FragB, class FragC>
+__device__ __forceinline__ void gram_tiles_nw4(FragB frag_b, FragC frag_c, int wave, int l16, int q,
                                                ssd_f32x4_t* gt) {
-  constexpr int LDB = N + 8, NKS = N / 32;
+  constexpr int NKS = N / 32;
   const bool b0_shared = wave < 2;
 #pragma unroll
   for (int ks = 0; ks < NKS; ++ks) {
     const int col = 32 * ks + 8 * q;
-    const ssd_u32x4_t bw = *reinterpret_cast<const ssd_u32x4_t*>(&s_b[(16 * wave + l16) * LDB + col]);
-    const ssd_u32x4_t c2 = *reinterpret_cast<const ssd_u32x4_t*>(&s_c[(32 + l16) * LDB + col]);
-    const ssd_u32x4_t c3 = *reinterpret_cast<const ssd_u32x4_t*>(&s_c[(48 + l16) * LDB + col]);
-    const ssd_u32x4_t c0 = *reinterpret_cast<const ssd_u32x4_t*>(&s_c[(16 * (wave >> 1) + l16) * LDB + col]);
-    const ssd_u32x4_t b0 =
-        b0_shared ? bw : *reinterpret_cast<const ssd_u32x4_t*>(&s_b[(16 * (wave & 1) + l16) * LDB + col]);
+    const ssd_u32x4_t bw = frag_b(16 * wave + l16, col);
+    const ssd_u32x4_t c2 = frag_c(32 + l16, col);
+    const ssd_u32x4_t c3 = frag_c(48 + l16, col);
+    const ssd_u32x4_t c0 = frag_c(16 * (wave >> 1) + l16, col);
+    const ssd_u32x4_t b0 = b0_shared ? bw : frag_b(16 * (wave & 1) + l16, col);
     gt[0] = mfma16x16x32(b0, c0, gt[0]);
     gt[1] = mfma16x16x32(bw, c2, gt[1]);
     gt[2] = mfma16x16x32(bw, c3, gt[2]);
@@ -186,7 +216,7 @@ void ssd_chunk_kernel(const SsdArgs p) {
   constexpr int Q = kSsdChunk;
   constexpr int PS = 16 * NW;         // head channels per workgroup
   constexpr int T = 64 * NW;          // threads
-  constexpr int LDB = N + 8;          // row stride (elements) of the B and C tiles
+  constexpr int LDB = N + 8;          // row stride (elements) of the C tile (B: SsdBLayout)
   constexpr int LDX = PS + 8;         // row stride of the X and weighted-X tiles
   constexpr int LDM = Q + 8;          // row stride of M
   constexpr int LDY = PS + 4;         // row stride of the fp32 output tile
@@ -200,7 +230,8 @@ void ssd_chunk_kernel(const SsdArgs p) {
   static_assert(kXPer == 2, "two 16-byte pieces of X per thread");
   static_assert(!PRE || NW == 4, "the precomputed C B^T tiles are laid out for four waves");
 
-  __shared__ __align__(16) uint16_t s_b[Q * LDB];   // B[j][n]
+  using BL = SsdBLayout<N, MODE != kSsdOutputs>;  // swizzled unless this kernel computes C B^T
+  __shared__ __align__(16) uint16_t s_b[Q * BL::LD];  // B[j][n] at BL::off(j, n)
   __shared__ __align__(16) uint16_t s_c[Q * LDB];   // C[i][n]
   __shared__ __align__(16) uint16_t s_x[Q * LDX];   // X[j][p]
   __shared__ __align__(16) uint16_t s_xw[Q * LDX];  // X[j][p] * exp(cum_last - cum_j) dt_j
@@ -335,7 +366,7 @@ void ssd_chunk_kernel(const SsdArgs p) {
     for (int u = 0; u < kBCPer; ++u) {
       const int k = tid + u * T;
       const int c8 = k % (N / 8), j = k / (N / 8);
-      *reinterpret_cast<ssd_u32x4_t*>(&s_b[j * LDB + 8 * c8]) = rb[u];
+      *reinterpret_cast<ssd_u32x4_t*>(&s_b[BL::off(j, 8 * c8)]) = rb[u];
       if constexpr (OUT) *reinterpret_cast<ssd_u32x4_t*>(&s_c[j * LDB + 8 * c8]) = rc[u];
     }
 #pragma unroll
@@ -432,7 +463,9 @@ void ssd_chunk_kernel(const SsdArgs p) {
 #pragma unroll
           for (int s = 0; s < kTiles; ++s) gt[s] = gpre[s];
         } else if constexpr (NW == 4) {
-          gram_tiles_nw4<N>(s_b, s_c, wave, l16, q, gt);
+          gram_tiles_nw4<N>([&](int r, int col) { return *reinterpret_cast<const ssd_u32x4_t*>(&s_b[BL::off(r, col)]); },
+                            [&](int r, int col) { return *reinterpret_cast<const ssd_u32x4_t*>(&s_c[r * LDB + col]); },
+                            wave, l16, q, gt);
         } else {
 #pragma unroll
           for (int ks = 0; ks < NKS; ++ks)
@@ -440,7 +473,7 @@ void ssd_chunk_kernel(const SsdArgs p) {
             for (int s = 0; s < kTiles; ++s) {
               const int k = wave + NW * s;
               const int ib = gram_tile_i(k), jb = gram_tile_j(k);
-              gt[s] = mfma16x16x32(*reinterpret_cast<const ssd_u32x4_t*>(&s_b[(16 * jb + l16) * LDB + 32 * ks + 8 * q]),
+              gt[s] = mfma16x16x32(*reinterpret_cast<const ssd_u32x4_t*>(&s_b[BL::off(16 * jb + l16, 32 * ks + 8 * q)]),
                                    *reinterpret_cast<const ssd_u32x4_t*>(&s_c[(16 * ib + l16) * LDB + 32 * ks + 8 * q]),
                                    gt[s]);
             }
@@ -509,7 +542,7 @@ void ssd_chunk_kernel(const SsdArgs p) {
       const ssd_u32x4_t xw = lds_frag_tr(s_xw, LDX, 32 * ks, q, l16, cx);  // weighted X[32 ks + 8q ..][pw]
 #pragma unroll
       for (int nb = 0; nb < NT; ++nb)
-        S[nb] = mfma16x16x32(lds_frag_tr(s_b, LDB, 32 * ks, q, l16, 32 * (nb >> 1) + 8 * (l16 & 3) + 4 * (nb & 1)),
+        S[nb] = mfma16x16x32(lds_frag_tr_b<BL>(s_b, 32 * ks, q, l16, 32 * (nb >> 1) + 8 * (l16 & 3) + 4 * (nb & 1)),
                              xw, S[nb]);
     }
     publish_dt();
@@ -584,7 +617,9 @@ __global__ __launch_bounds__(256) void ssd_gram_kernel(const SsdArgs p) {
   ssd_f32x4_t gt[3];
 #pragma unroll
   for (int s = 0; s < 3; ++s) gt[s] = ssd_f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-  gram_tiles_nw4<N>(s_b, s_c, wave, l16, q, gt);
+  gram_tiles_nw4<N>([&](int r, int col) { return *reinterpret_cast<const ssd_u32x4_t*>(&s_b[r * LDB + col]); },
+                    [&](int r, int col) { return *reinterpret_cast<const ssd_u32x4_t*>(&s_c[r * LDB + col]); },
+                    wave, l16, q, gt);
   float* dst = p.gram_out + (blk * 12 + wave) * 256 + 4 * lane;
 #pragma unroll
   for (int s = 0; s < 3; ++s) *reinterpret_cast<ssd_f32x4_t*>(dst + 4 * 256 * s) = gt[s];
