@@ -94,3 +94,15 @@ def test_method_slots_term_by_term():
     assert bench.SLOTS_PER_UPDATE == per_update
     assert bench.method_slots(elems, n) == elems * n * per_update + elems * bench.SLOTS_PER_TD
     assert abs(bench.method_slots(elems, n) / (elems * n) - 6.875) < 1e-12
+
+
+def test_valu_ceiling_against_the_hbm_target():
+    """The bench line's target block: at 100% fp32 issue with zero overhead the 130M-shaped scan
+    takes method_slots / 39.3 T slots/s = 70.4 us, i.e. its 203,272,192 algorithmic bytes at 36% of
+    8 TB/s, so the 60% target lies above what this arithmetic allows without packed fp32."""
+    elems, n = 8 * 2048 * 1536, 16
+    floor_s = bench.method_slots(elems, n) / bench.VALU_LANE_SLOTS
+    assert abs(floor_s * 1e6 - 70.4) < 0.05
+    ceiling = bench.scan_bytes(8, 2048, 1536, 16, 2) / floor_s / 1e9 / bench.HBM_PEAK_GBPS
+    assert 0.36 < ceiling < 0.362
+    assert ceiling < bench.HBM_TARGET_FRAC
