@@ -526,6 +526,67 @@ def pin_backward_linear_in_dy(o):
         _close(r3[k], 2.0 * r1[k] - 3.0 * r2[k], 1e-12, f"linearity of {k}")
 
 
+def pin_backward_euler_identities(o):
+    """Euler's identity for homogeneous functions, on the loss l = sum(dy * y).  For fixed delta,
+    A and z, y is linear in x (the input term and the D skip), and y - D x silu(z) is linear in B
+    and, separately, in C (the state is linear in B; the read-out in C).  So, exactly:
+        sum(x dx) = l,   sum(B dB) = sum(C dC) = l - l_D,   sum(D dD) = l_D,
+    with l_D = sum(dy D x silu(z)).  This checks dx, dB, dC and dD against the forward oracle
+    without finite differences, for both input terms (delta B and the exact zero-order hold)."""
+    for seed, softplus, z, D, bias, zoh in ((51, True, True, True, True, False), (52, False, False, True, False, False),
+                                             (53, True, True, False, True, False), (54, True, True, True, True, True)):
+        c = _rand_case(seed, batch=2, L=6, dim=3, N=4, softplus=softplus, bias=bias, z=z, D=D)
+        c["zoh"] = zoh
+        dy = np.random.default_rng(seed + 200).normal(size=c["x"].shape)
+        y, _ = _scan(o, c)
+        g = o.scan_bwd(c["x"], c["delta"], c["A"], c["B"], c["C"], dy, D=c["D"], z=c["z"],
+                       delta_bias=c["delta_bias"], delta_softplus=softplus, zoh=zoh)
+        gate = c["z"] * expit(c["z"]) if z else 1.0
+        loss = float(np.sum(dy * y))
+        loss_d = float(np.sum(dy * c["D"].astype(np.float64) * c["x"] * gate)) if D else 0.0
+        scale = float(np.sum(np.abs(dy * y))) + abs(loss_d)
+        what = f"seed {seed}{', ZOH' if zoh else ''}"
+        for got, want, name in ((np.sum(c["x"] * g["dx"]), loss, "sum(x dx) = l"),
+                                (np.sum(c["B"] * g["dB"]), loss - loss_d, "sum(B dB) = l - l_D"),
+                                (np.sum(c["C"] * g["dC"]), loss - loss_d, "sum(C dC) = l - l_D")):
+            assert abs(float(got) - want) <= 1e-12 * scale, f"{name} ({what}): {float(got):.15e} vs {want:.15e}"
+        if D:
+            got = float(np.sum(c["D"].astype(np.float64) * g["dD"]))
+            assert abs(got - loss_d) <= 1e-12 * scale, f"sum(D dD) = l_D ({what}): {got:.15e} vs {loss_d:.15e}"
+
+
+def pin_backward_closed_forms(o):
+    """Exact identities for the gradients the homogeneity pin does not reach:
+      * scale invariance: replacing (delta_eff, A, B) by (s delta_eff, A / s, B / s) leaves every
+        decay exp(delta A) and every input term (delta B for "Mamba 论文精读" sec. 3.3; (exp(delta A)
+        - 1) / A B for the exact hold of sec. 2.2) unchanged, so d/ds at s = 1 gives
+        sum(delta_eff g_eff) = sum(A dA) + sum(B dB), g_eff = ddelta / softplus'(v) with softplus
+        (the logistic function, scipy's expit) and ddelta without;
+      * the gate: y = y0 silu(z) with y0 free of z, so dz = dy y (1 + z (1 - sigma(z))) / z;
+      * the skip: dD[d] = sum over (b, t) of dy x silu(z);
+      * the bias enters as delta does: ddelta_bias[d] = sum over (b, t) of ddelta."""
+    for seed, softplus, zoh in ((61, True, False), (62, False, False), (63, True, True), (64, False, True)):
+        c = _rand_case(seed, batch=2, L=6, dim=3, N=4, softplus=softplus, bias=True, z=True, D=True)
+        c["zoh"] = zoh
+        dy = np.random.default_rng(seed + 300).normal(size=c["x"].shape)
+        y, _ = _scan(o, c)
+        g = o.scan_bwd(c["x"], c["delta"], c["A"], c["B"], c["C"], dy, D=c["D"], z=c["z"],
+                       delta_bias=c["delta_bias"], delta_softplus=softplus, zoh=zoh)
+        what = f"seed {seed}{', softplus' if softplus else ''}{', ZOH' if zoh else ''}"
+        v = c["delta"] + c["delta_bias"].astype(np.float64)
+        dt = np.logaddexp(0.0, v) if softplus else v
+        g_eff = g["ddelta"] / expit(v) if softplus else g["ddelta"]
+        A = c["A"].astype(np.float64)
+        lhs = float(np.sum(dt * g_eff))
+        rhs = float(np.sum(A * g["dA"]) + np.sum(c["B"] * g["dB"]))
+        scale = float(np.sum(np.abs(dt * g_eff)) + np.sum(np.abs(A * g["dA"])) + np.sum(np.abs(c["B"] * g["dB"])))
+        assert abs(lhs - rhs) <= 1e-12 * scale, f"scale invariance ({what}): {lhs:.15e} vs {rhs:.15e}"
+        zz = c["z"]
+        _close(g["dz"], dy * y * (1.0 + zz * (1.0 - expit(zz))) / zz, 1e-11, f"dz closed form ({what})")
+        _close(g["dD"], np.sum(dy * c["x"] * zz * expit(zz), axis=(0, 1)), 1e-12, f"dD closed form ({what})")
+        _close(g["ddelta_bias"], np.sum(g["ddelta"], axis=(0, 1)), 1e-12, f"ddelta_bias = sum ddelta ({what})")
+
+
 # ----------------------------------------------------------------------------------------------
 # the exact zero-order hold ("Mamba 论文精读" sec. 2.2: Bbar = (Delta A)^-1 (exp(Delta A) - I) Delta B)
 # ----------------------------------------------------------------------------------------------
@@ -677,6 +738,6 @@ ALL_PINS = [pin_worked_examples, pin_unrolled_sum, pin_lti_convolution, pin_line
             pin_decode_equals_scan, pin_associative_scan, pin_special_values, pin_storage_widening,
             pin_channel_selection, pin_conv_library_convolution, pin_conv_impulse, pin_conv_silu,
             pin_conv_chaining, pin_conv_decode_equals_fwd, pin_conv_causality, pin_backward_finite_differences,
-            pin_backward_zoh_finite_differences, pin_backward_linear_in_dy, pin_zoh_steady_state, pin_zoh_semigroup, pin_zoh_small_step_limit,
+            pin_backward_zoh_finite_differences, pin_backward_linear_in_dy, pin_backward_euler_identities, pin_backward_closed_forms, pin_zoh_steady_state, pin_zoh_semigroup, pin_zoh_small_step_limit,
             pin_zoh_decode_equals_scan, pin_ssd_equals_selective_scan, pin_ssd_dual_matrix_form,
             pin_ssd_resume_from_state]
