@@ -733,6 +733,31 @@ def pin_ssd_resume_from_state(o):
     assert np.max(np.abs(y0 - y)) > 1e-3 * np.max(np.abs(y)), "the entering state had no effect"
 
 
+def pin_discretisation_scale_invariance(o):
+    """The discretisation depends on the step only through delta A (the decay exp(delta A)) and
+    delta B (the input term delta B x of "Mamba 论文精读" sec. 3.3; the exact hold
+    (exp(delta A) - 1) / A B of sec. 2.2 is the same under the map).  So replacing (delta, A, B)
+    by (s delta, A / s, B / s) leaves y and the final state unchanged, for the selective scan with
+    either input term and for the SSD layer (whose A is one scalar per head).  With s a power of
+    two every product is unchanged bit for bit, so the results must be equal exactly.  Scaling
+    delta alone must change them."""
+    for s_ in (2.0, 0.25):
+        for zoh in (False, True):
+            c = _rand_case(71, batch=2, L=7, dim=3, N=4, softplus=False, bias=False, z=True, D=True)
+            c["zoh"] = zoh
+            y0, h0 = _scan(o, c)
+            y1, h1 = _scan(o, c, delta=c["delta"] * s_, A=(c["A"] / np.float32(s_)).astype(np.float32), B=c["B"] / s_)
+            assert np.array_equal(y0, y1) and np.array_equal(h0, h1), f"scan scale invariance (s {s_}, zoh {zoh})"
+            y2, _ = _scan(o, c, delta=c["delta"] * s_)
+            assert not np.allclose(y0, y2), "scaling delta alone left y unchanged"
+        c = _ssd_case(72, softplus=False)
+        c["dt"] = np.abs(c["dt"])
+        kw = dict(D=c["D"], z=c["z"])
+        y0, f0 = o.ssd(c["x"], c["dt"], c["A"], c["B"], c["C"], **kw)
+        y1, f1 = o.ssd(c["x"], c["dt"] * s_, (c["A"] / np.float32(s_)).astype(np.float32), c["B"] / s_, c["C"], **kw)
+        assert np.array_equal(y0, y1) and np.array_equal(f0, f1), f"SSD scale invariance (s {s_})"
+
+
 ALL_PINS = [pin_worked_examples, pin_unrolled_sum, pin_lti_convolution, pin_linearity,
             pin_channel_independence, pin_causality, pin_zero_step, pin_impulse_long_carry,
             pin_decode_equals_scan, pin_associative_scan, pin_special_values, pin_storage_widening,
@@ -740,4 +765,4 @@ ALL_PINS = [pin_worked_examples, pin_unrolled_sum, pin_lti_convolution, pin_line
             pin_conv_chaining, pin_conv_decode_equals_fwd, pin_conv_causality, pin_backward_finite_differences,
             pin_backward_zoh_finite_differences, pin_backward_linear_in_dy, pin_backward_euler_identities, pin_backward_closed_forms, pin_zoh_steady_state, pin_zoh_semigroup, pin_zoh_small_step_limit,
             pin_zoh_decode_equals_scan, pin_ssd_equals_selective_scan, pin_ssd_dual_matrix_form,
-            pin_ssd_resume_from_state]
+            pin_ssd_resume_from_state, pin_discretisation_scale_invariance]
