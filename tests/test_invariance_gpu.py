@@ -1,0 +1,125 @@
+"""A property of the discretisation, checked on the HIP path at full size, bit for bit.
+
+The step enters the method only through delta A (the decay exp(delta A)) and delta B (the input
+term delta B x of "Mamba 论文精读" sec. 3.3, and the exact hold (exp(delta A) - 1) / A B of
+sec. 2.2).  So (delta, A, B) -> (2 delta, A / 2, B / 2) leaves every output unchanged.  Scaling by
+two commutes with every rounding the kernels make (bf16 storage included), so the kernels must
+return the same bits, whatever their order of operations: a kernel that mixed up which tensor
+feeds which product, or dropped a factor of delta, would not.  The step is passed in its final
+form (softplus applied on the host, no bias), since the map acts on the step itself.  These
+tests need no oracle; the oracle side of the property is pinned in tests/pins.py."""
+import pytest
+import torch
+
+import workloads as W
+from gpu_util import say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import selective_state_space_61_amd as ssm
+    ssm.load_library()
+
+
+def final_step(delta, bias):
+    """softplus(delta + bias) in fp32, stored in delta's dtype (bf16 rounded to nearest even)."""
+    v = delta.float() + (0.0 if bias is None else bias)
+    return torch.nn.functional.softplus(v, threshold=20.0).to(delta.dtype)
+
+
+def halved(t):
+    return t / 2 if t.dtype == torch.float32 else (t.float() / 2).to(t.dtype)
+
+
+def doubled(t):
+    return t * 2 if t.dtype == torch.float32 else (t.float() * 2).to(t.dtype)
+
+
+def assert_same_bits(a, b, what):
+    assert a.shape == b.shape, f"{what}: shapes {a.shape} / {b.shape}"
+    assert torch.all(torch.isfinite(a.float())), f"{what}: non-finite values"
+    same = torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a.view(torch.int32),
+                       b.view(torch.int16) if b.dtype == torch.bfloat16 else b.view(torch.int32))
+    if not same:
+        diff = (a.float() - b.float()).abs().max().item()
+        raise AssertionError(f"{what}: outputs differ under (2 delta, A / 2, B / 2), max |diff| {diff:.3e}")
+    say(f"  {what}: {a.numel()} elements bit-identical")
+
+
+def scan_pair(t, softplus=True, **kw):
+    import selective_state_space_61_amd as ssm
+    d = {k: to_dev(v) for k, v in t.items()}
+    dt = final_step(d["delta"], d["delta_bias"]) if softplus else d["delta"]
+    out = []
+    for dtv, A, B in ((dt, d["A"], d["B"]), (doubled(dt), halved(d["A"]), halved(d["B"]))):
+        y, st = ssm.ssm_scan_fwd(d["x"], dtv, A, B, d["C"], D=d["D"], z=d["z"], delta_softplus=False, **kw)
+        out.append((y, st))
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.parametrize("workload,kw", [("mamba130m", {}), ("mamba130m", {"layout": "channel_lanes"}),
+                                         ("mamba130m", {"zoh": True}), ("mamba2p8b", {})],
+                         ids=["130m-auto", "130m-channel-lanes", "130m-zoh", "2p8b-auto"])
+def test_scan_scale_invariance(workload, kw):
+    w = W.WORKLOADS[workload]
+    say(f"[case] scan {workload} {kw}: (2 delta, A / 2, B / 2)")
+    (y0, s0), (y1, s1) = scan_pair(W.workload_inputs(w), **kw)
+    assert_same_bits(y0, y1, f"{workload} {kw} y")
+    assert_same_bits(s0, s1, f"{workload} {kw} last_state")
+
+
+def test_scan_scale_invariance_split_sequence():
+    """The genomics recipe (fp32, 256 channels) over 2^17 steps: few channels, so the sequence is
+    split and the segments' carries composed with exp(A sum delta)."""
+    t = W.scan_inputs(1, 1 << 17, 256, 16, dtype="f32", seed=61003, recipe="genomics", has_bias=False)
+    say("[case] scan split sequence, genomics recipe 1 x 2^17 x 256 (delta passed as the step)")
+    (y0, s0), (y1, s1) = scan_pair(t, softplus=False)
+    assert_same_bits(y0, y1, "split-sequence y")
+    assert_same_bits(s0, s1, "split-sequence last_state")
+
+
+def test_decode_scale_invariance():
+    import selective_state_space_61_amd as ssm
+    w = W.WORKLOADS["decode"]
+    t = W.workload_inputs(w)
+    d = {k: to_dev(v) for k, v in t.items()}
+    steps = 32
+    say(f"[case] decode {w.batch} x {w.dim}, {steps} steps: (2 delta, A / 2, B / 2)")
+    results = []
+    for scale in (False, True):
+        state = torch.zeros(w.batch, w.dim, w.dstate, device="cuda")
+        ys = []
+        for s in range(steps):
+            dt = final_step(d["delta"][s], d["delta_bias"])
+            A, B = d["A"], d["B"][s]
+            if scale:
+                dt, A, B = doubled(dt), halved(A), halved(B)
+            ys.append(ssm.ssm_state_update(state, d["x"][s], dt, A, B, d["C"][s], D=d["D"], z=d["z"][s],
+                                           delta_softplus=False))
+        torch.cuda.synchronize()
+        results.append((torch.stack(ys), state))
+    assert_same_bits(results[0][0], results[1][0], "decode y")
+    assert_same_bits(results[0][1], results[1][1], "decode state")
+
+
+@pytest.mark.parametrize("workload", ["mamba2_layer_b8", "mamba2_layer"])
+def test_ssd_scale_invariance(workload):
+    """The SSD layer: the 8 x 2048 layer (C B^T computed once per group by the separate pass) and
+    the 1 x 1024 example (the sequence split into segments whose states are composed)."""
+    import selective_state_space_61_amd as ssm
+    w = W.SSD_WORKLOADS[workload]
+    t = W.ssd_workload_inputs(w)
+    d = {k: to_dev(v) for k, v in t.items()}
+    dt = final_step(d["dt"], d["dt_bias"])
+    say(f"[case] SSD {workload}: (2 dt, A / 2, B / 2)")
+    out = []
+    for dtv, A, B in ((dt, d["A"], d["B"]), (doubled(dt), halved(d["A"]), halved(d["B"]))):
+        out.append(ssm.ssm_ssd_fwd(d["x"], dtv, A, B, d["C"], D=d["D"], z=d["z"], dt_softplus=False))
+    torch.cuda.synchronize()
+    assert_same_bits(out[0][0], out[1][0], f"{workload} y")
+    assert_same_bits(out[0][1], out[1][1], f"{workload} final_state")
