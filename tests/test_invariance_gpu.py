@@ -123,3 +123,39 @@ def test_ssd_scale_invariance(workload):
     torch.cuda.synchronize()
     assert_same_bits(out[0][0], out[1][0], f"{workload} y")
     assert_same_bits(out[0][1], out[1][1], f"{workload} final_state")
+
+
+# ---------------------------------------------------------------------------------------------------
+# homogeneity in x: x enters only through the input term (delta x) and the skip (D x), and the gate
+# depends on z alone, so y(2 x) = 2 y(x) and the final state doubles; doubling is exact in every
+# rounding the kernels make.
+# ---------------------------------------------------------------------------------------------------
+def assert_doubled(a2, a1, what):
+    assert_same_bits(a2, doubled(a1), what + " (x doubled)")
+
+
+@pytest.mark.parametrize("workload,kw", [("mamba130m", {}), ("mamba130m", {"layout": "channel_lanes"}),
+                                         ("mamba130m", {"zoh": True})],
+                         ids=["130m-auto", "130m-channel-lanes", "130m-zoh"])
+def test_scan_homogeneous_in_x(workload, kw):
+    import selective_state_space_61_amd as ssm
+    t = W.workload_inputs(W.WORKLOADS[workload])
+    d = {k: to_dev(v) for k, v in t.items()}
+    say(f"[case] scan {workload} {kw}: x -> 2 x")
+    out = [ssm.ssm_scan_fwd(x, d["delta"], d["A"], d["B"], d["C"], D=d["D"], z=d["z"], delta_bias=d["delta_bias"],
+                            delta_softplus=True, **kw) for x in (d["x"], doubled(d["x"]))]
+    torch.cuda.synchronize()
+    assert_doubled(out[1][0], out[0][0], f"{workload} {kw} y")
+    assert_doubled(out[1][1], out[0][1], f"{workload} {kw} last_state")
+
+
+def test_ssd_homogeneous_in_x():
+    import selective_state_space_61_amd as ssm
+    t = W.ssd_workload_inputs(W.SSD_WORKLOADS["mamba2_layer_b8"])
+    d = {k: to_dev(v) for k, v in t.items()}
+    say("[case] SSD mamba2_layer_b8: x -> 2 x")
+    out = [ssm.ssm_ssd_fwd(x, d["dt"], d["A"], d["B"], d["C"], D=d["D"], z=d["z"], dt_bias=d["dt_bias"],
+                           dt_softplus=True) for x in (d["x"], doubled(d["x"]))]
+    torch.cuda.synchronize()
+    assert_doubled(out[1][0], out[0][0], "mamba2_layer_b8 y")
+    assert_doubled(out[1][1], out[0][1], "mamba2_layer_b8 final_state")
