@@ -159,3 +159,36 @@ def test_ssd_homogeneous_in_x():
     torch.cuda.synchronize()
     assert_doubled(out[1][0], out[0][0], "mamba2_layer_b8 y")
     assert_doubled(out[1][1], out[0][1], "mamba2_layer_b8 final_state")
+
+
+# ---------------------------------------------------------------------------------------------------
+# the backward under the same map: the loss sum(dy y) is unchanged by (delta, A, B) -> (2 delta,
+# A / 2, B / 2), so at the mapped point dx, dC, dD and dz are unchanged, ddelta (with respect to the
+# step) halves, and dA and dB double, bit for bit (every term of each gradient scales alike).
+# The state-row backward adds dB and dC over channel blocks with atomics, in an order that varies
+# from run to run, so there those two are compared to within their bf16 storage.
+# ---------------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("kw", [{}, {"layout": "channel_lanes"}, {"zoh": True}],
+                         ids=["auto", "channel-lanes", "zoh"])
+def test_backward_scale_covariance(kw):
+    import selective_state_space_61_amd as ssm
+    t = W.workload_inputs(W.WORKLOADS["mamba130m"])
+    d = {k: to_dev(v) for k, v in t.items()}
+    dt = final_step(d["delta"], d["delta_bias"])
+    gen = torch.Generator(device="cuda").manual_seed(61)
+    dy = torch.randn(d["x"].shape, generator=gen, device="cuda").to(torch.bfloat16)
+    say(f"[case] backward mamba130m {kw}: (2 delta, A / 2, B / 2)")
+    g0 = ssm.ssm_scan_bwd(d["x"], dt, d["A"], d["B"], d["C"], dy, D=d["D"], z=d["z"], **kw)
+    g1 = ssm.ssm_scan_bwd(d["x"], doubled(dt), halved(d["A"]), halved(d["B"]), d["C"], dy, D=d["D"], z=d["z"], **kw)
+    torch.cuda.synchronize()
+    atomics = kw.get("layout", "auto") == "auto" and not kw.get("zoh", False)
+    for k, f in (("dx", None), ("dz", None), ("dD", None), ("ddelta", halved), ("dA", doubled),
+                 ("dB", doubled), ("dC", None)):
+        want = g0[k] if f is None else f(g0[k])
+        if atomics and k in ("dB", "dC"):
+            err = (g1[k].float() - want.float()).abs().max().item()
+            scale = want.float().abs().max().item()
+            say(f"  {k}: max |diff| {err:.3e} against max {scale:.3e} (atomic sums)")
+            assert err <= 1e-2 * scale, f"{k}: {err:.3e} > 1e-2 x {scale:.3e}"
+        else:
+            assert_same_bits(g1[k], want, f"{k}{'' if f is None else ' (scaled)'}")
