@@ -192,3 +192,31 @@ def test_backward_scale_covariance(kw):
             assert err <= 1e-2 * scale, f"{k}: {err:.3e} > 1e-2 x {scale:.3e}"
         else:
             assert_same_bits(g1[k], want, f"{k}{'' if f is None else ' (scaled)'}")
+
+
+def test_ssd_decode_scale_invariance():
+    """The SSD layer's single-token step on 64 rows x 64 heads x 64 channels, dstate 128, from a
+    nonzero state over 8 tokens: the same bits under (2 dt, A / 2, B / 2)."""
+    import selective_state_space_61_amd as ssm
+    batch, H, P, N, steps = 64, 64, 64, 128, 8
+    t = W.ssd_inputs(batch, steps, H, P, N, 1, seed=61009)
+    d = {k: (None if v is None else to_dev(v)) for k, v in t.items()}
+    gen = torch.Generator(device="cuda").manual_seed(9)
+    h0 = torch.randn((batch, H, P, N), generator=gen, device="cuda") * 0.5
+    dt = final_step(d["dt"], d["dt_bias"])
+    say(f"[case] SSD decode {batch} x {H} x {P}, N {N}, {steps} tokens: (2 dt, A / 2, B / 2)")
+    results = []
+    for scale in (False, True):
+        state = h0.clone()
+        A = halved(d["A"]) if scale else d["A"]
+        ys = []
+        for s in range(steps):
+            dts, B = dt[:, s].contiguous(), d["B"][:, s].contiguous()
+            if scale:
+                dts, B = doubled(dts), halved(B)
+            ys.append(ssm.ssm_ssd_state_update(state, d["x"][:, s].contiguous(), dts, A, B, d["C"][:, s].contiguous(),
+                                               D=d["D"], z=d["z"][:, s].contiguous()))
+        torch.cuda.synchronize()
+        results.append((torch.stack(ys), state))
+    assert_same_bits(results[0][0], results[1][0], "SSD decode y")
+    assert_same_bits(results[0][1], results[1][1], "SSD decode state")
