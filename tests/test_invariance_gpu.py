@@ -131,7 +131,7 @@ def test_ssd_scale_invariance(workload):
 # rounding the kernels make.
 # ---------------------------------------------------------------------------------------------------
 def assert_doubled(a2, a1, what):
-    assert_same_bits(a2, doubled(a1), what + " (x doubled)")
+    assert_same_bits(a2, doubled(a1), what + ": twice the original")
 
 
 @pytest.mark.parametrize("workload,kw", [("mamba130m", {}), ("mamba130m", {"layout": "channel_lanes"}),
@@ -220,3 +220,54 @@ def test_ssd_decode_scale_invariance():
         results.append((torch.stack(ys), state))
     assert_same_bits(results[0][0], results[1][0], "SSD decode y")
     assert_same_bits(results[0][1], results[1][1], "SSD decode state")
+
+
+def test_conv1d_homogeneous():
+    """The depthwise causal convolution without bias or SiLU is linear in x and in the weights:
+    doubling either (the entering state with x) doubles y and the final state, bit for bit, on
+    the 8 x 2048 x 1536 bf16 shape."""
+    import selective_state_space_61_amd as ssm
+    t = W.conv_inputs(8, 2048, 1536, 4, "bf16", seed=61001, has_bias=False, has_init=True)
+    d = {k: (None if v is None else to_dev(v)) for k, v in t.items()}
+    say("[case] conv1d 8 x 2048 x 1536, width 4: x -> 2 x, weight -> 2 weight")
+
+    def run(x, w, init):
+        return ssm.ssm_causal_conv1d_fwd(x, w, None, initial_state=init, silu=False, return_final_state=True)
+    y0, f0 = run(d["x"], d["weight"], d["init"])
+    y1, f1 = run(doubled(d["x"]), d["weight"], doubled(d["init"]))
+    y2, f2 = run(d["x"], d["weight"] * 2, d["init"])
+    torch.cuda.synchronize()
+    assert_doubled(y1, y0, "conv1d y")
+    assert_doubled(f1, f0, "conv1d final_state")
+    assert_doubled(y2, y0, "conv1d y (weights doubled)")
+    assert_same_bits(f2, f0, "conv1d final_state (weights doubled: the inputs, unchanged)")
+
+
+def test_checkpoint_pair_scale_covariance():
+    """The training pair under (delta, A, B) -> (2 delta, A / 2, B / 2) at the 130M shape: the
+    forward's checkpoints (states) are unchanged, and the backward from them transforms as the
+    plain backward does (dB and dC are atomic sums there: compared within their bf16 storage)."""
+    import selective_state_space_61_amd as ssm
+    t = W.workload_inputs(W.WORKLOADS["mamba130m"])
+    d = {k: to_dev(v) for k, v in t.items()}
+    dt = final_step(d["delta"], d["delta_bias"])
+    gen = torch.Generator(device="cuda").manual_seed(62)
+    dy = torch.randn(d["x"].shape, generator=gen, device="cuda").to(torch.bfloat16)
+    say("[case] checkpoint pair mamba130m: (2 delta, A / 2, B / 2)")
+    res = []
+    for dtv, A, B in ((dt, d["A"], d["B"]), (doubled(dt), halved(d["A"]), halved(d["B"]))):
+        y, st, ck = ssm.ssm_scan_fwd_ckpt(d["x"], dtv, A, B, d["C"], D=d["D"], z=d["z"])
+        g = ssm.ssm_scan_bwd_ckpt(d["x"], dtv, A, B, d["C"], dy, ck, D=d["D"], z=d["z"])
+        res.append((y, st, ck, g))
+    torch.cuda.synchronize()
+    assert_same_bits(res[1][0], res[0][0], "pair forward y")
+    assert_same_bits(res[1][2], res[0][2], "checkpoints")
+    g0, g1 = res[0][3], res[1][3]
+    for k, f in (("dx", None), ("dz", None), ("dD", None), ("ddelta", halved), ("dA", doubled)):
+        assert_same_bits(g1[k], g0[k] if f is None else f(g0[k]), f"pair {k}{'' if f is None else ' (scaled)'}")
+    for k, f in (("dB", doubled), ("dC", None)):
+        want = g0[k] if f is None else f(g0[k])
+        err = (g1[k].float() - want.float()).abs().max().item()
+        scale = want.float().abs().max().item()
+        say(f"  pair {k}: max |diff| {err:.3e} against max {scale:.3e} (atomic sums)")
+        assert err <= 1e-2 * scale, f"pair {k}: {err:.3e} > 1e-2 x {scale:.3e}"
