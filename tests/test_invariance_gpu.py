@@ -271,3 +271,59 @@ def test_checkpoint_pair_scale_covariance():
         scale = want.float().abs().max().item()
         say(f"  pair {k}: max |diff| {err:.3e} against max {scale:.3e} (atomic sums)")
         assert err <= 1e-2 * scale, f"pair {k}: {err:.3e} > 1e-2 x {scale:.3e}"
+
+
+# ---------------------------------------------------------------------------------------------------
+# batch order: every batch row is computed by the same arithmetic whatever its position (and
+# whichever workgroup and XCD the remapped grid gives it), so reversing the batch reverses the
+# outputs bit for bit.  Gradients summed over the batch (dA, dD, the bias) change their order of
+# summation and are left out; so are the state rows' atomically summed dB / dC.
+# ---------------------------------------------------------------------------------------------------
+def flipped(t):
+    return None if t is None else torch.flip(t, dims=[0]).contiguous()
+
+
+def test_scan_batch_reversal():
+    import selective_state_space_61_amd as ssm
+    t = W.workload_inputs(W.WORKLOADS["mamba130m"])
+    d = {k: to_dev(v) for k, v in t.items()}
+    say("[case] scan mamba130m: batch reversed")
+    kw = dict(D=d["D"], delta_bias=d["delta_bias"], delta_softplus=True)
+    y0, s0 = ssm.ssm_scan_fwd(d["x"], d["delta"], d["A"], d["B"], d["C"], z=d["z"], **kw)
+    y1, s1 = ssm.ssm_scan_fwd(flipped(d["x"]), flipped(d["delta"]), d["A"], flipped(d["B"]), flipped(d["C"]),
+                              z=flipped(d["z"]), **kw)
+    torch.cuda.synchronize()
+    assert_same_bits(y1, flipped(y0), "scan y (batch reversed)")
+    assert_same_bits(s1, flipped(s0), "scan last_state (batch reversed)")
+
+
+def test_ssd_batch_reversal():
+    import selective_state_space_61_amd as ssm
+    t = W.ssd_workload_inputs(W.SSD_WORKLOADS["mamba2_layer_b8"])
+    d = {k: to_dev(v) for k, v in t.items()}
+    say("[case] SSD mamba2_layer_b8: batch reversed")
+    kw = dict(D=d["D"], dt_bias=d["dt_bias"], dt_softplus=True)
+    y0, f0 = ssm.ssm_ssd_fwd(d["x"], d["dt"], d["A"], d["B"], d["C"], z=d["z"], **kw)
+    y1, f1 = ssm.ssm_ssd_fwd(flipped(d["x"]), flipped(d["dt"]), d["A"], flipped(d["B"]), flipped(d["C"]),
+                             z=flipped(d["z"]), **kw)
+    torch.cuda.synchronize()
+    assert_same_bits(y1, flipped(y0), "SSD y (batch reversed)")
+    assert_same_bits(f1, flipped(f0), "SSD final_state (batch reversed)")
+
+
+@pytest.mark.parametrize("layout", ["auto", "channel_lanes"])
+def test_backward_batch_reversal(layout):
+    import selective_state_space_61_amd as ssm
+    t = W.workload_inputs(W.WORKLOADS["mamba130m"])
+    d = {k: to_dev(v) for k, v in t.items()}
+    gen = torch.Generator(device="cuda").manual_seed(63)
+    dy = torch.randn(d["x"].shape, generator=gen, device="cuda").to(torch.bfloat16)
+    say(f"[case] backward mamba130m ({layout}): batch reversed")
+    kw = dict(D=d["D"], delta_bias=d["delta_bias"], delta_softplus=True, layout=layout)
+    g0 = ssm.ssm_scan_bwd(d["x"], d["delta"], d["A"], d["B"], d["C"], dy, z=d["z"], **kw)
+    g1 = ssm.ssm_scan_bwd(flipped(d["x"]), flipped(d["delta"]), d["A"], flipped(d["B"]), flipped(d["C"]),
+                          flipped(dy), z=flipped(d["z"]), **kw)
+    torch.cuda.synchronize()
+    keys = ("dx", "ddelta", "dz") + (("dB", "dC") if layout == "channel_lanes" else ())
+    for k in keys:
+        assert_same_bits(g1[k], flipped(g0[k]), f"{k} (batch reversed)")
